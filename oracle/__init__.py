@@ -1,0 +1,153 @@
+"""CPU parity oracle (test infrastructure only).
+
+Thin ctypes wrapper over ``oracle.c`` (plain fp64 C, built with gcc).  Only the
+tests, the smoke check and the benchmark's CPU-baseline leg use this package;
+the product path (the HIP library and its binding) never imports it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from typing import Optional, Tuple
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+OK, NOT_CONVERGED, ERR_ARG, ERR_BREAKDOWN, ERR_NONFINITE, ERR_NOMEM = 0, 1, -1, -3, -4, -6
+
+_lock = threading.Lock()
+_lib = None
+
+
+def build(src: str = SRC, out: str = LIB, extra_flags: Tuple[str, ...] = ()) -> str:
+    """Compile the oracle with gcc (-O2, no FP contraction, OpenMP over rows)."""
+    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC",
+           "-shared", "-std=c11", *extra_flags, "-o", out, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def load(path: Optional[str] = None):
+    global _lib
+    with _lock:
+        if path is not None:
+            return _bind(ctypes.CDLL(path))
+        if _lib is None:
+            if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+                build()
+            _lib = _bind(ctypes.CDLL(LIB))
+        return _lib
+
+
+def _bind(lib):
+    i64, i32, dbl, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_double, ctypes.c_void_p
+    lib.orc_spmv.argtypes = [i64, ctypes.c_int, vp, vp, vp, vp, vp]
+    lib.orc_spmv.restype = None
+    lib.orc_transpose.argtypes = [i64, ctypes.c_int, vp, vp, vp, vp, vp, vp]
+    lib.orc_transpose.restype = ctypes.c_int
+    lib.orc_dot.argtypes = [i64, vp, vp]
+    lib.orc_dot.restype = dbl
+    lib.orc_precond_apply.argtypes = [i64, ctypes.c_int, vp, vp, vp, dbl, vp, vp]
+    lib.orc_precond_apply.restype = ctypes.c_int
+    lib.orc_pcg.argtypes = [i64, ctypes.c_int, vp, vp, vp, vp, vp, vp, dbl, vp, vp, dbl, i32,
+                            ctypes.POINTER(i32), ctypes.POINTER(dbl)]
+    lib.orc_pcg.restype = ctypes.c_int
+    lib.orc_adjoint.argtypes = [i64, ctypes.c_int, vp, vp, vp, vp, vp, vp, dbl, vp, vp, vp, vp,
+                                dbl, i32, ctypes.POINTER(i32), ctypes.POINTER(dbl)]
+    lib.orc_adjoint.restype = ctypes.c_int
+    lib.orc_dot_block.argtypes = []
+    lib.orc_dot_block.restype = ctypes.c_int
+    return lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _mat(M):
+    return (_c(M.row_ptr, np.int32), _c(M.col_idx, np.int32), _c(M.vals, np.float64))
+
+
+def spmv(M, x: np.ndarray, lib=None) -> np.ndarray:
+    """y = M x (M a SparseMatrix from the inputs module)."""
+    lib = lib or load()
+    rp, ci, v = _mat(M)
+    x = _c(x, np.float64)
+    y = np.empty(M.n, dtype=np.float64)
+    lib.orc_spmv(M.n_block_rows, M.block_dim, _p(rp), _p(ci), _p(v), _p(x), _p(y))
+    return y
+
+
+def transpose(M, lib=None):
+    """Explicit transpose (row_ptr, col_idx, vals) of a square CSR/BSR matrix."""
+    lib = lib or load()
+    rp, ci, v = _mat(M)
+    trp = np.empty_like(rp)
+    tci = np.empty_like(ci)
+    tv = np.empty_like(v)
+    st = lib.orc_transpose(M.n_block_rows, M.block_dim, _p(rp), _p(ci), _p(v), _p(trp),
+                           _p(tci), _p(tv))
+    if st != OK:
+        raise MemoryError("oracle transpose failed")
+    return trp, tci, tv
+
+
+def dot(a: np.ndarray, b: np.ndarray, lib=None) -> float:
+    lib = lib or load()
+    a = _c(a, np.float64)
+    b = _c(b, np.float64)
+    return float(lib.orc_dot(a.shape[0], _p(a), _p(b)))
+
+
+def precond_apply(G, eps: float, r: np.ndarray, lib=None) -> np.ndarray:
+    """z = (G G^T + eps I) r."""
+    lib = lib or load()
+    rp, ci, v = _mat(G)
+    r = _c(r, np.float64)
+    z = np.empty(G.n, dtype=np.float64)
+    st = lib.orc_precond_apply(G.n_block_rows, G.block_dim, _p(rp), _p(ci), _p(v), eps, _p(r),
+                               _p(z))
+    if st != OK:
+        raise MemoryError("oracle precond_apply failed")
+    return z
+
+
+def pcg(A, G, eps: float, b: np.ndarray, rtol: float, maxit: int, lib=None):
+    """Returns (x, status, iterations, recursive relative residual)."""
+    lib = lib or load()
+    arp, aci, av = _mat(A)
+    grp, gci, gv = _mat(G)
+    b = _c(b, np.float64)
+    x = np.empty(A.n, dtype=np.float64)
+    it = ctypes.c_int32(0)
+    rr = ctypes.c_double(0.0)
+    st = lib.orc_pcg(A.n_block_rows, A.block_dim, _p(arp), _p(aci), _p(av), _p(grp), _p(gci),
+                     _p(gv), float(eps), _p(b), _p(x), float(rtol), int(maxit),
+                     ctypes.byref(it), ctypes.byref(rr))
+    return x, int(st), int(it.value), float(rr.value)
+
+
+def adjoint(A, G, eps: float, x: np.ndarray, gx: np.ndarray, rtol: float, maxit: int, lib=None):
+    """Returns (lambda = dL/db, dL/dvals in A's storage order, status, iterations, relres)."""
+    lib = lib or load()
+    arp, aci, av = _mat(A)
+    grp, gci, gv = _mat(G)
+    x = _c(x, np.float64)
+    gx = _c(gx, np.float64)
+    lam = np.empty(A.n, dtype=np.float64)
+    gval = np.empty(av.shape[0], dtype=np.float64)
+    it = ctypes.c_int32(0)
+    rr = ctypes.c_double(0.0)
+    st = lib.orc_adjoint(A.n_block_rows, A.block_dim, _p(arp), _p(aci), _p(av), _p(grp),
+                         _p(gci), _p(gv), float(eps), _p(x), _p(gx), _p(lam), _p(gval),
+                         float(rtol), int(maxit), ctypes.byref(it), ctypes.byref(rr))
+    return lam, gval, int(st), int(it.value), float(rr.value)

@@ -1,0 +1,428 @@
+"""Pins that tie the CPU oracle to mathematics independent of it.
+
+Every function takes the loaded oracle library (so the same pins can be run
+against deliberately broken copies of the oracle) and raises AssertionError
+when the oracle disagrees with what the pages and the mathematics fix:
+dense brute force, closed-form Laplacian eigenpairs, dense Cholesky / LU,
+the Galerkin characterisation of CG iterates, finite differences, and the
+edge cases of the stopping rule.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import scipy.linalg as sla
+
+import oracle
+from preconditioned_cg_solver_amd import inputs as I
+
+
+# ---------------------------------------------------------------------------
+# helpers (dense, independent of the oracle)
+# ---------------------------------------------------------------------------
+
+def rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    nb = np.linalg.norm(b)
+    return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
+
+
+def dense_matvec_loops(D, x):
+    """y_i = sum_j D_ij x_j with Python loops (brute force)."""
+    n = D.shape[0]
+    y = [0.0] * n
+    for i in range(n):
+        s = 0.0
+        for j in range(n):
+            if D[i, j] != 0.0:
+                s += float(D[i, j]) * float(x[j])
+        y[i] = s
+    return np.array(y)
+
+
+def small_int_csr(n, rng, density=0.3):
+    """Random CSR with small-integer values (exact products and sums)."""
+    D = np.where(rng.uniform(size=(n, n)) < density, rng.integers(-4, 5, size=(n, n)), 0)
+    np.fill_diagonal(D, rng.integers(1, 6, size=n))
+    rows, cols = np.nonzero(D)
+    rp = np.zeros(n + 1, dtype=np.int32)
+    np.cumsum(np.bincount(rows, minlength=n), out=rp[1:])
+    return I.SparseMatrix(n, 1, rp, cols.astype(np.int32), D[rows, cols].astype(np.float64)), D
+
+
+def galerkin_iterate(A, Minv, b, k):
+    """Exact-arithmetic characterisation of the k-th PCG iterate from x0 = 0:
+    x_k minimises ||x - A^-1 b||_A over the Krylov space
+    K_k = span{M^-1 b, (M^-1 A) M^-1 b, ...}; so x_k = V (V^T A V)^-1 V^T b.
+    An orthonormal basis keeps the small projected system well conditioned."""
+    v = Minv @ b
+    V = []
+    for _ in range(k):
+        V.append(v)
+        v = Minv @ (A @ v)
+    Q, _ = np.linalg.qr(np.stack(V, axis=1))
+    H = Q.T @ A @ Q
+    return Q @ np.linalg.solve(H, Q.T @ b)
+
+
+def lap2d_eig(N, k, l):
+    i = np.arange(1, N + 1)
+    vy = np.sin(math.pi * i * k / (N + 1))
+    vx = np.sin(math.pi * i * l / (N + 1))
+    lam = 4 - 2 * math.cos(math.pi * k / (N + 1)) - 2 * math.cos(math.pi * l / (N + 1))
+    return np.outer(vy, vx).reshape(-1), lam
+
+
+def lap3d_eig(N, k, l, m):
+    i = np.arange(1, N + 1)
+    a = np.sin(math.pi * i * k / (N + 1))
+    b = np.sin(math.pi * i * l / (N + 1))
+    c = np.sin(math.pi * i * m / (N + 1))
+    lam = 6 - 2 * (math.cos(math.pi * k / (N + 1)) + math.cos(math.pi * l / (N + 1))
+                   + math.cos(math.pi * m / (N + 1)))
+    return np.einsum("i,j,k->ijk", a, b, c).reshape(-1), lam
+
+
+def scalar_factor(n, c):
+    """G = c I, so M^-1 = (c^2 + eps) I is a scalar and PCG reduces to CG."""
+    return I.SparseMatrix(n, 1, np.arange(n + 1, dtype=np.int32), np.arange(n, dtype=np.int32),
+                          np.full(n, c, dtype=np.float64))
+
+
+def zero_factor_like(G):
+    return I.SparseMatrix(G.n_block_rows, G.block_dim, G.row_ptr, G.col_idx,
+                          np.zeros_like(G.vals))
+
+
+# ---------------------------------------------------------------------------
+# SpMV
+# ---------------------------------------------------------------------------
+
+def pin_spmv_bruteforce(lib):
+    rng = np.random.default_rng(11)
+    for n in (1, 7, 33, 64):
+        M, D = small_int_csr(n, rng)
+        x = rng.integers(-3, 4, size=n).astype(np.float64)
+        y = oracle.spmv(M, x, lib=lib)
+        assert np.array_equal(y, dense_matvec_loops(D, x)), f"csr spmv n={n}"
+    # real values on a generated problem
+    p = I.make_problem(0, size=8)
+    x = rng.standard_normal(p.A.n)
+    y = oracle.spmv(p.A, x, lib=lib)
+    assert rel(y, dense_matvec_loops(p.A.to_dense(), x)) <= 1e-15
+
+
+def pin_spmv_bsr_dense(lib):
+    rng = np.random.default_rng(12)
+    A = I.elastic_bsr(3, np.random.default_rng(5))
+    x = rng.standard_normal(A.n)
+    y = oracle.spmv(A, x, lib=lib)
+    assert rel(y, dense_matvec_loops(A.to_dense(), x)) <= 1e-14, "bsr spmv"
+    G = I.spai_factor(A, np.random.default_rng(6))
+    y = oracle.spmv(G, x, lib=lib)
+    assert rel(y, G.to_dense() @ x) <= 1e-14, "bsr spmv (lower)"
+
+
+def pin_spmv_eigenpairs(lib):
+    N = 24
+    A = I.poisson2d(N)
+    lmax = 8.0
+    for (k, l) in ((1, 1), (3, 7), (N, N), (5, 1)):
+        v, lam = lap2d_eig(N, k, l)
+        r = oracle.spmv(A, v, lib=lib) - lam * v
+        assert np.linalg.norm(r) <= 1e-14 * lmax * np.linalg.norm(v), f"2d eig {k},{l}"
+    N = 10
+    A = I.poisson3d(N)
+    for (k, l, m) in ((1, 1, 1), (2, 9, 4), (N, 1, N)):
+        v, lam = lap3d_eig(N, k, l, m)
+        r = oracle.spmv(A, v, lib=lib) - lam * v
+        assert np.linalg.norm(r) <= 1e-14 * 12.0 * np.linalg.norm(v), f"3d eig {k},{l},{m}"
+    N = 20
+    A = I.heat2d(N)
+    s = I.heat_scale(N)
+    for (k, l) in ((1, 2), (N, N)):
+        v, lam = lap2d_eig(N, k, l)
+        lam = 1.0 + s * lam
+        r = oracle.spmv(A, v, lib=lib) - lam * v
+        assert np.linalg.norm(r) <= 1e-14 * (1 + 8 * s) * np.linalg.norm(v), "heat eig"
+
+
+# ---------------------------------------------------------------------------
+# transpose and preconditioner
+# ---------------------------------------------------------------------------
+
+def pin_transpose(lib):
+    p = I.make_problem(0, size=6)
+    G = p.G
+    trp, tci, tv = oracle.transpose(G, lib=lib)
+    Gt = I.SparseMatrix(G.n_block_rows, 1, trp, tci, tv)
+    assert np.array_equal(Gt.to_dense(), G.to_dense().T), "csr transpose"
+    # pattern of G^T is the upper triangle of A's pattern
+    Ad = p.A.to_dense()
+    assert np.array_equal(Gt.to_dense() != 0, np.triu(Ad != 0)), "pattern"
+    # rows of the result are column-sorted
+    for i in range(Gt.n_block_rows):
+        seg = tci[trp[i]:trp[i + 1]]
+        assert np.all(np.diff(seg) > 0)
+    # (G^T)^T == G bitwise
+    rp2, ci2, v2 = oracle.transpose(Gt, lib=lib)
+    assert np.array_equal(rp2, G.row_ptr) and np.array_equal(ci2, G.col_idx)
+    assert np.array_equal(v2, G.vals)
+    # BSR: blocks are transposed too
+    A = I.elastic_bsr(3, np.random.default_rng(1))
+    Gb = I.spai_factor(A, np.random.default_rng(2))
+    trp, tci, tv = oracle.transpose(Gb, lib=lib)
+    Gbt = I.SparseMatrix(Gb.n_block_rows, 3, trp, tci, tv)
+    assert np.array_equal(Gbt.to_dense(), Gb.to_dense().T), "bsr transpose"
+
+
+def pin_precond(lib):
+    rng = np.random.default_rng(21)
+    for cfg, size in ((0, 8), (2, 4)):
+        p = I.make_problem(cfg, size=size)
+        r = rng.standard_normal(p.A.n)
+        Gd = p.G.to_dense()
+        z = oracle.precond_apply(p.G, p.eps, r, lib=lib)
+        zd = Gd @ (Gd.T @ r) + p.eps * r
+        assert rel(z, zd) <= 1e-14, "precond dense"
+        assert float(r @ z) > 0
+        z0 = oracle.precond_apply(zero_factor_like(p.G), p.eps, r, lib=lib)
+        assert np.array_equal(z0, p.eps * r), "G = 0 gives eps r"
+    A = I.elastic_bsr(2, np.random.default_rng(3))
+    G = I.spai_factor(A, np.random.default_rng(4))
+    r = rng.standard_normal(A.n)
+    Gd = G.to_dense()
+    assert rel(oracle.precond_apply(G, 3e-3, r, lib=lib), Gd @ (Gd.T @ r) + 3e-3 * r) <= 1e-14
+
+
+# ---------------------------------------------------------------------------
+# PCG
+# ---------------------------------------------------------------------------
+
+def pin_pcg_cholesky(lib):
+    rng = np.random.default_rng(31)
+    p = I.make_problem(0, size=8)                      # n = 64
+    x, st, it, _ = oracle.pcg(p.A, p.G, p.eps, p.b, 1e-14, 500, lib=lib)
+    assert st == oracle.OK
+    xd = sla.cho_solve(sla.cho_factor(p.A.to_dense()), p.b)
+    assert rel(x, xd) <= 1e-11, "pcg vs cholesky (poisson)"
+    A = I.random_spd_csr(50, rng)
+    G = I.spai_factor(A, rng)
+    b = rng.standard_normal(50)
+    x, st, it, _ = oracle.pcg(A, G, 3e-3, b, 1e-14, 500, lib=lib)
+    assert st == oracle.OK
+    assert rel(x, sla.cho_solve(sla.cho_factor(A.to_dense()), b)) <= 1e-11, "pcg vs cholesky"
+    Ab = I.elastic_bsr(2, rng)
+    Gb = I.spai_factor(Ab, rng)
+    b = rng.standard_normal(Ab.n)
+    x, st, it, _ = oracle.pcg(Ab, Gb, 3e-3, b, 1e-14, 500, lib=lib)
+    assert st == oracle.OK
+    assert rel(x, sla.cho_solve(sla.cho_factor(Ab.to_dense()), b)) <= 1e-11, "bsr pcg"
+
+
+def pin_pcg_galerkin(lib):
+    """The first k iterates equal the Krylov-Galerkin projections."""
+    rng = np.random.default_rng(32)
+    p = I.make_problem(0, size=5)                      # n = 25
+    A = p.A.to_dense()
+    Gd = p.G.to_dense()
+    Minv = Gd @ Gd.T + p.eps * np.eye(p.A.n)
+    b = rng.standard_normal(p.A.n)
+    for k in (1, 2, 3, 4):
+        x, st, it, _ = oracle.pcg(p.A, p.G, p.eps, b, 1e-300, k, lib=lib)
+        assert st == oracle.NOT_CONVERGED and it == k
+        assert rel(x, galerkin_iterate(A, Minv, b, k)) <= 1e-10, f"galerkin k={k}"
+
+
+def pin_pcg_eigen(lib):
+    N = 16
+    A = I.poisson2d(N)
+    G = scalar_factor(A.n, 0.7)
+    v, lam = lap2d_eig(N, 3, 5)
+    x, st, it, _ = oracle.pcg(A, G, 3e-3, v, 1e-12, 100, lib=lib)
+    assert st == oracle.OK and it == 1, f"one eigenvector -> 1 iteration (got {it})"
+    assert rel(x, v / lam) <= 1e-14
+    b = np.zeros(A.n)
+    modes = ((1, 1), (2, 3), (7, 7), (12, 4))
+    for (k, l) in modes:
+        b += lap2d_eig(N, k, l)[0] * (1 + k + l)
+    x, st, it, _ = oracle.pcg(A, G, 3e-3, b, 1e-12, 100, lib=lib)
+    assert st == oracle.OK and it <= len(modes) + 1, f"m eigenvectors -> <= m iterations ({it})"
+
+
+def pin_pcg_cg_equivalence(lib):
+    """A scalar preconditioner (G = 0 or G = c I) gives the CG iterates."""
+    import scipy.sparse.linalg as ssl
+    p = I.make_problem(0)
+    z = zero_factor_like(p.G)
+    x0, st0, it0, _ = oracle.pcg(p.A, z, 1.0, p.b, 1e-10, 2000, lib=lib)
+    x1, st1, it1, _ = oracle.pcg(p.A, scalar_factor(p.A.n, 0.5), 3e-3, p.b, 1e-10, 2000, lib=lib)
+    count = [0]
+
+    def cb(_):
+        count[0] += 1
+    xs, info = ssl.cg(p.A.to_scipy(), p.b, rtol=1e-10, atol=0.0, maxiter=2000, callback=cb)
+    assert st0 == st1 == oracle.OK and info == 0
+    assert abs(it0 - count[0]) <= 1 and abs(it1 - count[0]) <= 1, (it0, it1, count[0])
+    assert rel(x0, xs) <= 1e-8 and rel(x1, xs) <= 1e-8
+    # CG convergence bound with kappa of the 2D Laplacian in closed form
+    N = 32
+    lmin = 4 - 4 * math.cos(math.pi / (N + 1))
+    lmax = 4 + 4 * math.cos(math.pi / (N + 1))
+    kappa = lmax / lmin
+    bound = math.ceil(0.5 * math.sqrt(kappa) * math.log(2 / 1e-10))
+    assert it1 <= bound, (it1, bound)
+
+
+def pin_pcg_scipy(lib):
+    import scipy.sparse.linalg as ssl
+    p = I.make_problem(0)
+    x, st, it, _ = oracle.pcg(p.A, p.G, p.eps, p.b, p.rtol, p.maxit, lib=lib)
+    Gs = p.G.to_scipy()
+    Gts = Gs.T.tocsr()
+    M = ssl.LinearOperator((p.A.n, p.A.n), matvec=lambda r: Gs @ (Gts @ r) + p.eps * r)
+    count = [0]
+
+    def cb(_):
+        count[0] += 1
+    xs, info = ssl.cg(p.A.to_scipy(), p.b, rtol=p.rtol, atol=0.0, maxiter=p.maxit, M=M,
+                      callback=cb)
+    assert st == oracle.OK and info == 0
+    assert abs(it - count[0]) <= 1, (it, count[0])
+    assert rel(x, xs) <= 1e-8
+    A = p.A.to_scipy()
+    assert np.linalg.norm(p.b - A @ x) <= 10 * p.rtol * np.linalg.norm(p.b), "true residual"
+
+
+def pin_pcg_edges(lib):
+    p = I.make_problem(0, size=8)
+    x, st, it, rr = oracle.pcg(p.A, p.G, p.eps, np.zeros(p.A.n), 1e-10, 100, lib=lib)
+    assert st == oracle.OK and it == 0 and not np.any(x), "b = 0"
+    x, st, it, rr = oracle.pcg(p.A, p.G, p.eps, p.b, 1e-10, 0, lib=lib)
+    assert st == oracle.NOT_CONVERGED and it == 0 and not np.any(x), "maxit = 0"
+    x, st, it, rr = oracle.pcg(p.A, p.G, p.eps, p.b, 1e-10, 1, lib=lib)
+    assert st == oracle.NOT_CONVERGED and it == 1 and rr < 1.0, "maxit = 1"
+    neg = I.SparseMatrix(p.A.n_block_rows, 1, p.A.row_ptr, p.A.col_idx, -p.A.vals)
+    x, st, it, rr = oracle.pcg(neg, p.G, p.eps, p.b, 1e-10, 100, lib=lib)
+    assert st == oracle.ERR_BREAKDOWN and it == 0, "negative definite -> breakdown"
+    b = p.b.copy()
+    b[3] = np.nan
+    x, st, it, rr = oracle.pcg(p.A, p.G, p.eps, b, 1e-10, 100, lib=lib)
+    assert st == oracle.ERR_NONFINITE, "NaN in b"
+    # n = 1
+    one = I.SparseMatrix(1, 1, np.array([0, 1], np.int32), np.array([0], np.int32),
+                         np.array([4.0]))
+    g1 = I.SparseMatrix(1, 1, np.array([0, 1], np.int32), np.array([0], np.int32),
+                        np.array([0.5]))
+    x, st, it, rr = oracle.pcg(one, g1, 3e-3, np.array([2.0]), 1e-12, 10, lib=lib)
+    assert st == oracle.OK and it == 1 and abs(x[0] - 0.5) <= 1e-16
+
+
+# ---------------------------------------------------------------------------
+# adjoint
+# ---------------------------------------------------------------------------
+
+def pin_adjoint_fd_b(lib):
+    """dL/db = lambda against central differences of a dense solve."""
+    p = I.make_problem(0, size=6)
+    Ad = p.A.to_dense()
+    cf = sla.cho_factor(Ad)
+    x, st, it, _ = oracle.pcg(p.A, p.G, p.eps, p.b, 1e-14, 500, lib=lib)
+    lam, gval, st2, _, _ = oracle.adjoint(p.A, p.G, p.eps, x, 2 * x, 1e-14, 500, lib=lib)
+    assert st == st2 == oracle.OK
+
+    def L(b):
+        xx = sla.cho_solve(cf, b)
+        return float(xx @ xx)
+    h = 1e-3
+    for i in (0, 7, 20, 35):
+        e = np.zeros(p.A.n)
+        e[i] = h
+        fd = (L(p.b + e) - L(p.b - e)) / (2 * h)
+        assert abs(fd - lam[i]) <= 1e-9 * max(1.0, abs(lam[i])), ("dL/db", i, fd, lam[i])
+
+
+def pin_adjoint_fd_entries(lib):
+    """dL/dA_ij = -lambda_i x_j against central differences of single-entry
+    (unsymmetric) perturbations solved with dense LU."""
+    rng = np.random.default_rng(41)
+    p = I.make_problem(0, size=6)
+    w = rng.standard_normal(p.A.n)
+    Ad = p.A.to_dense()
+    x, st, it, _ = oracle.pcg(p.A, p.G, p.eps, p.b, 1e-14, 500, lib=lib)
+    lam, gval, st2, _, _ = oracle.adjoint(p.A, p.G, p.eps, x, w, 1e-14, 500, lib=lib)
+    rows = p.A.row_of_entry()
+    h = 1e-5
+    for k in (0, 3, 10, 50, p.A.nnz - 1, 77):
+        i, j = rows[k], p.A.col_idx[k]
+        E = np.zeros_like(Ad)
+        E[i, j] = h
+        fd = (w @ np.linalg.solve(Ad + E, p.b) - w @ np.linalg.solve(Ad - E, p.b)) / (2 * h)
+        assert abs(fd - gval[k]) <= 1e-6 * max(1e-3, abs(gval[k])), ("dL/dA", k, fd, gval[k])
+    # BSR: one scalar inside an off-diagonal block and one inside a diagonal block
+    Ab = I.elastic_bsr(2, np.random.default_rng(7))
+    Gb = I.spai_factor(Ab, np.random.default_rng(8))
+    b = rng.standard_normal(Ab.n)
+    w = rng.standard_normal(Ab.n)
+    Abd = Ab.to_dense()
+    x, st, it, _ = oracle.pcg(Ab, Gb, 3e-3, b, 1e-14, 500, lib=lib)
+    lam, gval, st2, _, _ = oracle.adjoint(Ab, Gb, 3e-3, x, w, 1e-14, 500, lib=lib)
+    brows = Ab.row_of_entry()
+    for k, r, c in ((1, 0, 2), (0, 1, 1), (Ab.nnzb - 1, 2, 0)):
+        i, j = brows[k] * 3 + r, Ab.col_idx[k] * 3 + c
+        E = np.zeros_like(Abd)
+        E[i, j] = h
+        fd = (w @ np.linalg.solve(Abd + E, b) - w @ np.linalg.solve(Abd - E, b)) / (2 * h)
+        g = gval[k * 9 + r * 3 + c]
+        assert abs(fd - g) <= 1e-6 * max(1e-3, abs(g)), ("bsr dL/dA", k, r, c, fd, g)
+
+
+def pin_adjoint_directional(lib):
+    """Symmetric random direction on the full c0 pattern, oracle solves at
+    rtol 1e-13: <grad, S> against central differences of L = <w, x>."""
+    rng = np.random.default_rng(42)
+    p = I.make_problem(0)
+    w = rng.standard_normal(p.A.n)
+    x, st, it, _ = oracle.pcg(p.A, p.G, p.eps, p.b, 1e-13, 5000, lib=lib)
+    lam, gval, st2, _, _ = oracle.adjoint(p.A, p.G, p.eps, x, w, 1e-13, 5000, lib=lib)
+    S = p.A.to_scipy().copy()
+    S.data = rng.standard_normal(S.nnz)
+    S = (S + S.T) * 0.5
+    S = S.tocsr()
+    S.sort_indices()
+    # S has exactly A's (symmetric) pattern
+    assert np.array_equal(S.indptr, p.A.row_ptr) and np.array_equal(S.indices, p.A.col_idx)
+    h = 1e-6
+
+    def L(sign):
+        Ah = I.SparseMatrix(p.A.n, 1, p.A.row_ptr, p.A.col_idx, p.A.vals + sign * h * S.data)
+        xx, s, _, _ = oracle.pcg(Ah, p.G, p.eps, p.b, 1e-13, 5000, lib=lib)
+        assert s == oracle.OK
+        return float(w @ xx)
+    fd = (L(+1) - L(-1)) / (2 * h)
+    an = float(gval @ S.data)
+    assert abs(fd - an) <= 1e-6 * abs(an), ("directional", fd, an)
+
+
+def pin_adjoint_identities(lib):
+    p = I.make_problem(0)
+    x, st, it, _ = oracle.pcg(p.A, p.G, p.eps, p.b, p.rtol, p.maxit, lib=lib)
+    lam, gval, st2, _, _ = oracle.adjoint(p.A, p.G, p.eps, x, 2 * x, p.rtol, p.maxit, lib=lib)
+    assert abs(lam @ p.b - 2 * (x @ x)) <= 1e-7 * abs(2 * (x @ x)), "<lam,b> = 2||x||^2"
+    rng = np.random.default_rng(43)
+    w = rng.standard_normal(p.A.n)
+    lam, gval, st2, _, _ = oracle.adjoint(p.A, p.G, p.eps, x, w, p.rtol, p.maxit, lib=lib)
+    assert abs(lam @ p.b - w @ x) <= 1e-7 * max(abs(w @ x), 1e-3), "<lam,b> = <w,x>"
+    # gradient entries are -lam_i x_j in storage order
+    rows = p.A.row_of_entry()
+    assert np.array_equal(gval, -(lam[rows] * x[p.A.col_idx]))
+
+
+ALL_PINS = [
+    pin_spmv_bruteforce, pin_spmv_bsr_dense, pin_spmv_eigenpairs, pin_transpose, pin_precond,
+    pin_pcg_cholesky, pin_pcg_galerkin, pin_pcg_eigen, pin_pcg_cg_equivalence, pin_pcg_scipy,
+    pin_pcg_edges, pin_adjoint_fd_b, pin_adjoint_fd_entries, pin_adjoint_directional,
+    pin_adjoint_identities,
+]

@@ -1,0 +1,63 @@
+"""Plants plausible mistakes in copies of the oracle (on the CPU) and checks that
+at least one pin catches each of them.  The shipped oracle is never modified."""
+import os
+
+import pytest
+
+import oracle
+import pins
+
+MUTATIONS = [
+    ("spmv drops the block column offset",
+     "s += blk[c] * x[J * bs + c];", "s += blk[c] * x[J * bs];"),
+    ("spmv reads x at the row instead of the column",
+     "s += blk[c] * x[J * bs + c];", "s += blk[c] * x[I * bs + c];"),
+    ("transpose keeps blocks untransposed",
+     "t_val[dst * bb + (int64_t)c * bs + r]", "t_val[dst * bb + (int64_t)r * bs + c]"),
+    ("dot skips the last element of every block",
+     "for (int64_t i = lo; i < hi; ++i) s += a[i] * b[i];",
+     "for (int64_t i = lo; i + 1 < hi; ++i) s += a[i] * b[i];"),
+    ("preconditioner subtracts the shift",
+     "z[i] = z[i] + eps * r[i];", "z[i] = z[i] - eps * r[i];"),
+    ("preconditioner applies G twice instead of G G^T",
+     "orc_spmv(Gt->nbr, Gt->bs, Gt->row_ptr, Gt->col, Gt->val, r, t);",
+     "orc_spmv(G->nbr, G->bs, G->row_ptr, G->col, G->val, r, t);"),
+    ("residual update with the wrong sign",
+     "r[i] = r[i] - alpha * q[i];", "r[i] = r[i] + alpha * q[i];"),
+    ("beta inverted",
+     "const double beta = rho_new / rho;", "const double beta = rho / rho_new;"),
+    ("search direction from r instead of z",
+     "p[i] = z[i] + beta * p[i];", "p[i] = r[i] + beta * p[i];"),
+    ("absolute instead of relative stopping test",
+     "if (rnorm <= rtol * bnorm)", "if (rnorm <= rtol)"),
+    ("alpha from the wrong inner product",
+     "const double alpha = rho / sigma;", "const double alpha = rho / orc_dot(n, q, q);"),
+    ("iteration counted before the update",
+     "*iters = k;", "*iters = k + 1;"),
+    ("adjoint gradient transposed (lambda_j x_i)",
+     "-(lam[I * bs + r] * x[J * bs + c])", "-(lam[J * bs + c] * x[I * bs + r])"),
+    ("adjoint gradient sign dropped",
+     "-(lam[I * bs + r] * x[J * bs + c])", "(lam[I * bs + r] * x[J * bs + c])"),
+    ("adjoint solves with b instead of dL/dx",
+     "eps, gx, lam,", "eps, x, lam,"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_planted_mistake(tmp_path, name, old, new):
+    src = open(oracle.SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not unique/present: {old!r}"
+    mutant = tmp_path / "mutant.c"
+    mutant.write_text(src.replace(old, new))
+    so = str(tmp_path / "libmutant.so")
+    oracle.build(str(mutant), so)
+    lib = oracle.load(so)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(lib)
+        except AssertionError as e:
+            caught.append(pin.__name__)
+        except Exception as e:  # a crash of the mutant is also a catch
+            caught.append(f"{pin.__name__} ({type(e).__name__})")
+    assert caught, f"no pin caught: {name}"
