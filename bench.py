@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Benchmark of the PCG + factorised-SPAI hot path on one MI355X.
+
+Workload: 3D Poisson 7-point Laplacian on a 128^3 interior grid (n = 2,097,152,
+nnz = 14,581,760), fp64 CSR, b ~ N(0,1), G on tril(A) with seeded random
+values, eps = 3e-3, rtol = 1e-10, adjoint loss L = <w, x> with w ~ N(0,1).
+
+One step = the whole hot path on that input, already resident in HBM:
+handle set-up (row binning of A and G, explicit G^T built on the device),
+the forward PCG solve, and the adjoint solve with dL/db and dL/dA.
+value = PCG iterations (forward + adjoint) per second over the timed steps.
+
+Also reported: the live HIP-event duration of the dominant kernel (the fused
+A-product step) and its algorithmic-byte rate against the 8 TB/s HBM peak,
+the whole-iteration byte rate, a standalone SpMV rate, and the CPU oracle
+timed on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_a_step_poisson3d_128.json")
+KERNEL_SRC = os.path.join(ROOT, "preconditioned_cg_solver_amd", "csrc", "solver.hip")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(n, nnz_a, nnz_g, sv, si=4):
+    """Bytes the method must move (each matrix stream once, each vector once
+    per kernel, gathers counted once), per SpMV and per fused kernel."""
+    def spmv(nnz):
+        return (sv + si) * nnz + si * (n + 1) + 2 * sv * n
+    a_step = spmv(nnz_a) + 3 * sv * n + 3 * sv * n      # SpMV(A) + p update + x update
+    gt_step = spmv(nnz_g) + 3 * sv * n                  # SpMV(G^T) + r update
+    g_step = spmv(nnz_g) + sv * n                       # SpMV(G) + eps r
+    return {"spmv_A": spmv(nnz_a), "a_step": a_step, "gt_step": gt_step, "g_step": g_step,
+            "iteration": a_step + gt_step + g_step}
+
+
+def traffic_if_current():
+    """HBM bytes per A-step launch from the committed rocprofv3 counter runs,
+    if they were taken on the current kernel source; else None."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+        src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+        if rec.get("kernel_source_sha256") != src:
+            return None
+        return rec.get("bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+
+
+def cpu_baseline(p, iters):
+    import oracle
+    log(f"cpu oracle: forward PCG capped at {iters} iterations, {oracle.num_threads()} threads")
+    t0 = time.perf_counter()
+    x, st, it, rr = oracle.pcg(p.A, p.G, p.eps, p.b, p.rtol, iters)
+    dt = time.perf_counter() - t0
+    return {"value": it / dt, "unit": "iters/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"forward PCG on the same 128^3 input capped at {iters} iterations "
+                      f"({it} done, includes the oracle's G^T build), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--size", type=int, default=128, help="grid edge of the 3D Poisson workload")
+    ap.add_argument("--cpu-iters", type=int, default=300)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--spmv-reps", type=int, default=50)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this solver runs on a single MI355X "
+              "(multi-GPU sharding is described in the design notes, not built); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from preconditioned_cg_solver_amd import binding as B
+    from preconditioned_cg_solver_amd import inputs as I
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("generating inputs")
+    p = I.make_problem(2, size=None if args.size == 128 else args.size)
+    n, nnz_a, nnz_g = p.A.n, p.A.nnz, p.G.nnz
+    ab = algorithmic_bytes(n, nnz_a, nnz_g, 8)
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    a_rp, a_ci, a_v = t(p.A.row_ptr), t(p.A.col_idx), t(p.A.vals)
+    g_rp, g_ci, g_v = t(p.G.row_ptr), t(p.G.col_idx), t(p.G.vals)
+    b, w = t(p.b), t(p.w)
+    x = torch.empty_like(b)
+    grad_b = torch.empty_like(b)
+    grad_vals = torch.empty(nnz_a, dtype=torch.float64, device=dev)
+    work = None
+
+    def step():
+        nonlocal work
+        A = B.sla_csr_create(a_rp, a_ci, a_v)
+        G = B.sla_csr_create(g_rp, g_ci, g_v, build_transpose=True)
+        if work is None:
+            work = B.workspace(A)
+        _, fi = B.sla_pcg_solve(A, G, p.eps, b, x=x, rtol=p.rtol, maxit=p.maxit, work=work)
+        _, _, ai = B.sla_pcg_adjoint(A, G, p.eps, x, w, rtol=p.rtol, maxit=p.maxit,
+                                     grad_b=grad_b, grad_vals=grad_vals, work=work)
+        A.destroy()
+        G.destroy()
+        return fi, ai
+
+    log(f"warmup {args.warmup} step(s)")
+    for _ in range(args.warmup):
+        fi, ai = step()
+    log(f"forward iterations {fi.iterations}, adjoint iterations {ai.iterations}")
+
+    B.sla_reset_profile()
+    B.sla_set_profiling(["a_step"])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    total_iters = 0
+    for k in range(args.steps):
+        fi, ai = step()
+        total_iters += fi.iterations + ai.iterations
+        log(f"step {k + 1}/{args.steps} done")
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    B.sla_set_profiling(False)
+    a_launches, a_ms = B.sla_get_profile("a_step")
+    a_avg_s = a_ms / max(a_launches, 1) / 1e3
+
+    # Outside the timed region: the parts of a step on their own.
+    A = B.sla_csr_create(a_rp, a_ci, a_v)
+    G = B.sla_csr_create(g_rp, g_ci, g_v, build_transpose=True)
+    setup = []
+    for _ in range(3):
+        torch.cuda.synchronize()
+        s0 = time.perf_counter()
+        H = B.sla_csr_create(g_rp, g_ci, g_v, build_transpose=True)
+        H2 = B.sla_csr_create(a_rp, a_ci, a_v)
+        torch.cuda.synchronize()
+        setup.append(time.perf_counter() - s0)
+        H.destroy()
+        H2.destroy()
+    solve_t = []
+    for _ in range(3):
+        torch.cuda.synchronize()
+        s0 = time.perf_counter()
+        _, fi = B.sla_pcg_solve(A, G, p.eps, b, x=x, rtol=p.rtol, maxit=p.maxit, work=work)
+        solve_t.append(time.perf_counter() - s0)
+    tts = statistics.median(solve_t)
+    y = torch.empty_like(b)
+    B.sla_spmv(A, b, y)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.spmv_reps):
+        B.sla_spmv(A, b, y)
+    e1.record()
+    torch.cuda.synchronize()
+    spmv_s = e0.elapsed_time(e1) / 1e3 / args.spmv_reps
+
+    achieved = ab["a_step"] / a_avg_s / 1e9
+    traffic = traffic_if_current()
+    iter_gbs = ab["iteration"] * fi.iterations / tts / 1e9
+    spmv_gbs = ab["spmv_A"] / spmv_s / 1e9
+    result = {
+        "metric": "PCG iters/sec + SpMV HBM GB/s (% of peak), 3D Poisson 128^3 fp64, 1 GPU",
+        "value": total_iters / elapsed,
+        "unit": "iters/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": f"poisson3d_{args.size} (3D Poisson 7-point, {args.size}^3 "
+                               "interior, fp64 CSR, PCG + factorised SPAI eps=3e-3, rtol=1e-10, "
+                               "forward + adjoint)",
+                   "n": n, "nnz_A": nnz_a, "nnz_G": nnz_g,
+                   "iterations_forward": fi.iterations, "iterations_adjoint": ai.iterations,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "csr_step<double, A> (q = A p, fused p/x "
+                                               "updates, p.q)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": ab["a_step"],
+                     "avg_launch_us": a_avg_s * 1e6, "launches": a_launches},
+        "iteration": {"bytes": ab["iteration"], "GBps": iter_gbs, "frac": iter_gbs / HBM_PEAK_GBS,
+                      "us_per_iteration": tts / fi.iterations * 1e6,
+                      "time_to_solution_ms": tts * 1e3},
+        "spmv": {"bytes": ab["spmv_A"], "GBps": spmv_gbs, "frac": spmv_gbs / HBM_PEAK_GBS,
+                 "us": spmv_s * 1e6, "note": "warm, back-to-back sla_spmv calls"},
+        "setup_ms": statistics.median(setup) * 1e3,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(p, args.cpu_iters)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

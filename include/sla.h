@@ -1,0 +1,200 @@
+/*
+ * sla.h -- C ABI of the MI355X (gfx950) preconditioned conjugate-gradient
+ * library: CG for sparse symmetric positive-definite A x = b, preconditioned
+ * by the factorised sparse approximate inverse M^-1 = G G^T + eps I, and the
+ * adjoint (backward) solve of that system.
+ *
+ * Method (pages cited by title and section):
+ *  - "Learning Sparse Approximate Inverse Preconditioners for Conjugate
+ *    Gradient Solvers on GPUs", "Approach": M^-1 = G G^T + eps I with G on
+ *    A's sparsity, so a preconditioner apply is two sparse products; "Problem":
+ *    CG for sparse SPD systems on GPUs.  G here has the lower-triangular
+ *    (block-lower) part of A's pattern.
+ *  - "torch-sla: Differentiable Sparse Linear Algebra with Adjoint Solvers...",
+ *    Technical Summary, Methodology 2 (adjoint differentiation, linear
+ *    systems): the backward pass is one solve A^T lambda = dL/dx, and
+ *    dL/dA_ij = -lambda_i x_j on the sparsity pattern only; memory is
+ *    O(n + nnz) and independent of the iteration count.
+ *
+ * Conventions shared by every entry point:
+ *  - All array arguments named d_* are DEVICE pointers (memory of the current
+ *    HIP device, e.g. from hipMalloc or a torch CUDA tensor).  Index arrays
+ *    are int32; value arrays are fp64 (SLA_F64) or fp32 (SLA_F32) as given at
+ *    create time.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *    device work is enqueued on it.  sla_spmv returns without waiting;
+ *    sla_csr_create / sla_bsr_create, sla_pcg_solve and sla_pcg_adjoint
+ *    return after their results are final (they synchronise `stream`).
+ *  - Errors are returned as sla_status, never thrown; sla_last_error() gives
+ *    a thread-local message for the last failing call on that thread.
+ *  - Nothing here falls back to the CPU: every numerical step runs in the
+ *    library's HIP kernels.
+ */
+#ifndef SLA_H
+#define SLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SLA_F64 = 0, SLA_F32 = 1 } sla_dtype;
+
+typedef enum {
+    SLA_OK = 0,
+    SLA_NOT_CONVERGED = 1,       /* > 0: result valid (last iterate), warning   */
+    SLA_ERR_INVALID_ARG = -1,    /* bad size, pointer, dtype, CSR structure     */
+    SLA_ERR_UNSUPPORTED = -2,    /* e.g. block size other than 1 or 3, n>=2^31  */
+    SLA_ERR_BREAKDOWN = -3,      /* p.Ap <= 0, r.z <= 0 or non-finite residual  */
+    SLA_ERR_NONFINITE = -4,      /* right-hand side holds NaN/Inf               */
+    SLA_ERR_HIP = -5,            /* a HIP runtime call failed                   */
+    SLA_ERR_OOM = -6             /* device or pinned host allocation failed     */
+} sla_status;
+
+/* Flags for sla_csr_create / sla_bsr_create. */
+#define SLA_BUILD_TRANSPOSE 1u   /* build and keep the explicit transpose (needed for G) */
+#define SLA_VALIDATE 2u          /* check the structure on the device (O(nnz))          */
+
+typedef struct sla_mat *sla_mat_t;
+
+typedef struct {
+    int32_t iterations;   /* number of products with A (= x updates) performed  */
+    int32_t converged;    /* 1 if ||r_k|| <= rtol ||b|| was reached               */
+    double rel_residual;  /* ||r_k|| / ||b|| of the recursive residual (0 if b=0) */
+    double bnorm;         /* ||b||_2 of the right-hand side actually solved       */
+} sla_solve_info;
+
+/*
+ * Create a handle for a square CSR matrix with n rows and nnz stored entries.
+ * The handle BORROWS d_row_ptr[n+1], d_col_idx[nnz] (columns ascending within
+ * each row, no duplicates, 0 <= col < n) and d_vals[nnz]; they must stay alive
+ * and unchanged until sla_mat_destroy.  The handle OWNS what it derives at
+ * create time: the SpMV tiling of the rows (row binning by nonzeros per row)
+ * and, with SLA_BUILD_TRANSPOSE, an explicit transpose in CSR built once on
+ * the device (a stable sort of the entries by column, so every transposed row
+ * lists its columns ascending and later products need no atomics).
+ * Errors: SLA_ERR_INVALID_ARG (negative sizes, NULL pointers with nnz > 0,
+ * row_ptr[n] != nnz, or -- with SLA_VALIDATE -- a malformed structure),
+ * SLA_ERR_UNSUPPORTED (n or nnz >= 2^31), SLA_ERR_OOM, SLA_ERR_HIP.
+ */
+sla_status sla_csr_create(sla_mat_t *out, int64_t n, int64_t nnz, const int32_t *d_row_ptr,
+                          const int32_t *d_col_idx, const void *d_vals, sla_dtype dtype,
+                          uint32_t flags, void *stream);
+
+/*
+ * Same for a square block-sparse matrix of n_block_rows x n_block_rows blocks
+ * of size block_dim x block_dim (only block_dim 3 and 1 are supported):
+ * d_brow_ptr[n_block_rows+1], d_bcol_idx[nnzb], d_bvals[nnzb*block_dim^2]
+ * with every block stored row-major.  The transpose (SLA_BUILD_TRANSPOSE)
+ * transposes the block pattern and every block.
+ */
+sla_status sla_bsr_create(sla_mat_t *out, int64_t n_block_rows, int64_t nnzb, int32_t block_dim,
+                          const int32_t *d_brow_ptr, const int32_t *d_bcol_idx,
+                          const void *d_bvals, sla_dtype dtype, uint32_t flags, void *stream);
+
+/* Release the handle and everything it owns (the borrowed arrays are untouched). */
+sla_status sla_mat_destroy(sla_mat_t m);
+
+/* Sizes of a handle: scalar rows, stored scalar entries, block size, dtype. */
+sla_status sla_mat_info(sla_mat_t m, int64_t *n, int64_t *nnz, int32_t *block_dim,
+                        int32_t *dtype);
+
+/*
+ * Device arrays of the explicit transpose owned by the handle (built with
+ * SLA_BUILD_TRANSPOSE): row_ptr[n_block_rows+1], col_idx[nnzb], vals.  The
+ * pointers stay valid until sla_mat_destroy; the caller must not free them.
+ * Error: SLA_ERR_INVALID_ARG if the handle has no transpose.
+ */
+sla_status sla_mat_transpose_arrays(sla_mat_t m, const int32_t **d_row_ptr,
+                                    const int32_t **d_col_idx, const void **d_vals);
+
+/* Number of SpMV tiles (row bins) of the handle and how many of them are long
+ * rows processed by row splitting; for tests and reports. */
+sla_status sla_mat_tiling(sla_mat_t m, int32_t transpose, int64_t *n_tiles, int64_t *n_long);
+
+/* y = A x (transpose = 0) or y = A^T x via the explicit transpose (transpose = 1).
+ * d_x[n] and d_y[n] must not overlap.  Asynchronous on `stream`. */
+sla_status sla_spmv(sla_mat_t A, const void *d_x, void *d_y, void *stream);
+sla_status sla_spmv_t(sla_mat_t A, const void *d_x, void *d_y, void *stream);
+
+/*
+ * Bytes of device workspace that sla_pcg_solve / sla_pcg_adjoint /
+ * sla_precond_apply need for a system of A's size: O(n) (seven vectors, the
+ * per-workgroup reduction partials and a small solver state), independent of
+ * maxit.  The caller allocates it (alignment 256 bytes) and passes it in; the
+ * library keeps nothing in it between calls.
+ */
+sla_status sla_pcg_workspace_size(sla_mat_t A, size_t *bytes);
+
+/*
+ * z = (G G^T + eps I) r  (the preconditioner apply), with G^T the handle's
+ * explicit transpose.  d_r[n], d_z[n] device vectors, workspace as above.
+ * Asynchronous on `stream`.
+ */
+sla_status sla_precond_apply(sla_mat_t G, double eps, const void *d_r, void *d_z, void *d_work,
+                             size_t work_bytes, void *stream);
+
+/*
+ * Preconditioned CG for A x = b, M^-1 = G G^T + eps I, x_0 = 0.
+ * A: SPD (assumed, not checked); G: same size, block size and dtype as A,
+ * created with SLA_BUILD_TRANSPOSE.  d_b[n] input, d_x[n] output (must not
+ * alias d_b or the workspace).  Stops when the recursive residual satisfies
+ * ||r_k||_2 <= rtol ||b||_2 (tested after each residual update, before the
+ * preconditioner) or after maxit iterations.  Returns SLA_OK (converged,
+ * including b = 0 with 0 iterations), SLA_NOT_CONVERGED (maxit reached; d_x
+ * holds the last iterate), SLA_ERR_BREAKDOWN (p.Ap <= 0, r.z <= 0 or a
+ * non-finite residual; d_x holds the last complete iterate),
+ * SLA_ERR_NONFINITE (b holds NaN/Inf), SLA_ERR_INVALID_ARG (mismatched
+ * handles, eps < 0, rtol < 0, maxit < 0, workspace too small).  `info` (may
+ * be NULL) receives iterations, convergence and residual.
+ */
+sla_status sla_pcg_solve(sla_mat_t A, sla_mat_t G, double eps, const void *d_b, void *d_x,
+                         double rtol, int32_t maxit, void *d_work, size_t work_bytes, void *stream,
+                         sla_solve_info *info);
+
+/*
+ * Adjoint of x = A^-1 b for a scalar loss L(x) with gradient d_grad_x = dL/dx:
+ * solves A^T lambda = dL/dx with the same preconditioner (A^T = A for the SPD
+ * matrices this solver targets), writes dL/db = lambda to d_grad_b[n], and
+ * dL/dA at every stored scalar entry (i, j) = -lambda_i x_j to
+ * d_grad_vals[nnz] in A's storage order (BSR: block by block, row-major).
+ * d_x is the forward solution.  Statuses as for sla_pcg_solve; the gradient
+ * is written whenever lambda is (SLA_OK or SLA_NOT_CONVERGED).
+ */
+sla_status sla_pcg_adjoint(sla_mat_t A, sla_mat_t G, double eps, const void *d_x,
+                           const void *d_grad_x, void *d_grad_b, void *d_grad_vals, double rtol,
+                           int32_t maxit, void *d_work, size_t work_bytes, void *stream,
+                           sla_solve_info *info);
+
+/*
+ * dL/dA on A's pattern: d_grad_vals[k] = -lambda[row(k)] * x[col(k)] for every
+ * stored scalar k (the last step of the adjoint, on its own).  Asynchronous.
+ */
+sla_status sla_pattern_grad(sla_mat_t A, const void *d_lambda, const void *d_x,
+                            void *d_grad_vals, void *stream);
+
+/* Human-readable name of a status, and the calling thread's last error text. */
+const char *sla_status_string(sla_status st);
+const char *sla_last_error(void);
+
+/*
+ * Kernel timing with HIP events recorded on the caller's stream around each
+ * launch of the solver's kernels.  `enable` is a bit mask of kernel classes
+ * (bit c records class c; 0 = off, the default).  Only launches that did work
+ * are counted (not the no-op launches after convergence).  Classes:
+ * 0 = A product step (q = A p, fused p and x updates, p.q), 1 = G^T product
+ * step (fused residual update, ||r||^2), 2 = G product step (z = G t + eps r,
+ * r.z), 3 = plain sla_spmv.  sla_get_profile returns the launch count and the
+ * summed event time (ms) of a class since the last sla_reset_profile.
+ */
+sla_status sla_set_profiling(int32_t enable);
+sla_status sla_get_profile(int32_t kernel_class, int64_t *launches, double *total_ms);
+sla_status sla_reset_profile(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SLA_H */

@@ -60,6 +60,10 @@ def _bind(lib):
     lib.orc_adjoint.argtypes = [i64, ctypes.c_int, vp, vp, vp, vp, vp, vp, dbl, vp, vp, vp, vp,
                                 dbl, i32, ctypes.POINTER(i32), ctypes.POINTER(dbl)]
     lib.orc_adjoint.restype = ctypes.c_int
+    lib.orc_pattern_grad.argtypes = [i64, ctypes.c_int, vp, vp, vp, vp, vp]
+    lib.orc_pattern_grad.restype = None
+    lib.orc_num_threads.argtypes = []
+    lib.orc_num_threads.restype = ctypes.c_int
     lib.orc_dot_block.argtypes = []
     lib.orc_dot_block.restype = ctypes.c_int
     return lib
@@ -75,6 +79,10 @@ def _c(a, dtype):
 
 def _mat(M):
     return (_c(M.row_ptr, np.int32), _c(M.col_idx, np.int32), _c(M.vals, np.float64))
+
+
+def num_threads(lib=None) -> int:
+    return int((lib or load()).orc_num_threads())
 
 
 def spmv(M, x: np.ndarray, lib=None) -> np.ndarray:
@@ -134,6 +142,17 @@ def pcg(A, G, eps: float, b: np.ndarray, rtol: float, maxit: int, lib=None):
                      _p(gv), float(eps), _p(b), _p(x), float(rtol), int(maxit),
                      ctypes.byref(it), ctypes.byref(rr))
     return x, int(st), int(it.value), float(rr.value)
+
+
+def pattern_grad(A, lam: np.ndarray, x: np.ndarray, lib=None) -> np.ndarray:
+    """dL/dvals[k] = -lam_row(k) * x_col(k) in A's storage order."""
+    lib = lib or load()
+    arp, aci, _ = _mat(A)
+    lam = _c(lam, np.float64)
+    x = _c(x, np.float64)
+    g = np.empty(A.nnz, dtype=np.float64)
+    lib.orc_pattern_grad(A.n_block_rows, A.block_dim, _p(arp), _p(aci), _p(lam), _p(x), _p(g))
+    return g
 
 
 def adjoint(A, G, eps: float, x: np.ndarray, gx: np.ndarray, rtol: float, maxit: int, lib=None):

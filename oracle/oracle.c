@@ -244,19 +244,12 @@ out:
     return st;
 }
 
-/* Adjoint of x = A^-1 b for a loss L(x) with gradient gx = dL/dx:
- * lambda solves A^T lambda = gx (A^T = A here), dL/db = lambda, and
- * dL/dA at every stored scalar (i, j) is -lambda_i x_j, in A's storage order. */
-int orc_adjoint(int64_t nbr, int bs,
-                const int32_t *a_row_ptr, const int32_t *a_col, const double *a_val,
-                const int32_t *g_row_ptr, const int32_t *g_col, const double *g_val,
-                double eps, const double *x, const double *gx, double *lam, double *grad_val,
-                double rtol, int32_t maxit, int32_t *iters, double *relres)
+/* dL/dA on A's pattern: for every stored scalar (i, j), -lambda_i x_j,
+ * written in A's storage order (block by block, row-major inside a block). */
+void orc_pattern_grad(int64_t nbr, int bs, const int32_t *a_row_ptr, const int32_t *a_col,
+                      const double *lam, const double *x, double *grad_val)
 {
     const int64_t bb = (int64_t)bs * bs;
-    int st = orc_pcg(nbr, bs, a_row_ptr, a_col, a_val, g_row_ptr, g_col, g_val, eps, gx, lam,
-                     rtol, maxit, iters, relres);
-    if (st < 0) return st;
 #pragma omp parallel for schedule(static)
     for (int64_t I = 0; I < nbr; ++I) {
         for (int64_t k = a_row_ptr[I]; k < a_row_ptr[I + 1]; ++k) {
@@ -266,7 +259,30 @@ int orc_adjoint(int64_t nbr, int bs,
                     grad_val[k * bb + (int64_t)r * bs + c] = -(lam[I * bs + r] * x[J * bs + c]);
         }
     }
+}
+
+/* Adjoint of x = A^-1 b for a loss L(x) with gradient gx = dL/dx:
+ * lambda solves A^T lambda = gx (A^T = A here), dL/db = lambda, and
+ * dL/dA at every stored scalar (i, j) is -lambda_i x_j, in A's storage order. */
+int orc_adjoint(int64_t nbr, int bs,
+                const int32_t *a_row_ptr, const int32_t *a_col, const double *a_val,
+                const int32_t *g_row_ptr, const int32_t *g_col, const double *g_val,
+                double eps, const double *x, const double *gx, double *lam, double *grad_val,
+                double rtol, int32_t maxit, int32_t *iters, double *relres)
+{
+    int st = orc_pcg(nbr, bs, a_row_ptr, a_col, a_val, g_row_ptr, g_col, g_val, eps, gx, lam,
+                     rtol, maxit, iters, relres);
+    if (st < 0) return st;
+    orc_pattern_grad(nbr, bs, a_row_ptr, a_col, lam, x, grad_val);
     return st;
 }
 
 int orc_dot_block(void) { return ORC_DOT_BLOCK; }
+
+/* Threads the OpenMP row loops use (1 when built without OpenMP). */
+#ifdef _OPENMP
+#include <omp.h>
+int orc_num_threads(void) { return omp_get_max_threads(); }
+#else
+int orc_num_threads(void) { return 1; }
+#endif

@@ -1,0 +1,308 @@
+"""ctypes binding of ``libsla.so`` (the C ABI in ``include/sla.h``).
+
+Argument marshalling only: every numerical step runs in the library's HIP
+kernels.  Torch tensors supply device memory and the current HIP stream.
+torch is imported before the library is loaded so that ``libsla.so`` binds to
+the same HIP runtime instance as torch (both carry the soname
+``libamdhip64.so.7``).  There is no CPU fallback: if the library is missing or
+no GPU is present, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+import threading
+from typing import Optional, Tuple
+
+import torch  # noqa: F401  (must precede loading libsla.so, see above)
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libsla.so")
+
+SLA_F64, SLA_F32 = 0, 1
+SLA_BUILD_TRANSPOSE, SLA_VALIDATE = 1, 2
+STATUS = {0: "SLA_OK", 1: "SLA_NOT_CONVERGED", -1: "SLA_ERR_INVALID_ARG", -2: "SLA_ERR_UNSUPPORTED",
+          -3: "SLA_ERR_BREAKDOWN", -4: "SLA_ERR_NONFINITE", -5: "SLA_ERR_HIP", -6: "SLA_ERR_OOM"}
+OK, NOT_CONVERGED = 0, 1
+ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_BREAKDOWN, ERR_NONFINITE, ERR_HIP, ERR_OOM = -1, -2, -3, -4, -5, -6
+PROFILE_CLASSES = {"a_step": 0, "gt_step": 1, "g_step": 2, "spmv": 3}
+
+
+class SlaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class SolveInfo(ctypes.Structure):
+    _fields_ = [("iterations", ctypes.c_int32), ("converged", ctypes.c_int32),
+                ("rel_residual", ctypes.c_double), ("bnorm", ctypes.c_double)]
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib():
+    """Load libsla.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError(f"{LIB_PATH} is missing: build it with "
+                                  "preconditioned_cg_solver_amd.build.build()")
+            _lib = _declare(ctypes.CDLL(LIB_PATH))
+        return _lib
+
+
+def _declare(L):
+    vp, i32, i64, u32, dbl, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
+                                  ctypes.c_double, ctypes.c_size_t)
+    st = ctypes.c_int
+    sig = {
+        "sla_csr_create": ([ctypes.POINTER(vp), i64, i64, vp, vp, vp, ctypes.c_int, u32, vp], st),
+        "sla_bsr_create": ([ctypes.POINTER(vp), i64, i64, i32, vp, vp, vp, ctypes.c_int, u32, vp], st),
+        "sla_mat_destroy": ([vp], st),
+        "sla_mat_info": ([vp, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i32),
+                          ctypes.POINTER(i32)], st),
+        "sla_mat_transpose_arrays": ([vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                      ctypes.POINTER(vp)], st),
+        "sla_mat_tiling": ([vp, i32, ctypes.POINTER(i64), ctypes.POINTER(i64)], st),
+        "sla_spmv": ([vp, vp, vp, vp], st),
+        "sla_spmv_t": ([vp, vp, vp, vp], st),
+        "sla_pcg_workspace_size": ([vp, ctypes.POINTER(sz)], st),
+        "sla_precond_apply": ([vp, dbl, vp, vp, vp, sz, vp], st),
+        "sla_pcg_solve": ([vp, vp, dbl, vp, vp, dbl, i32, vp, sz, vp, ctypes.POINTER(SolveInfo)],
+                          st),
+        "sla_pcg_adjoint": ([vp, vp, dbl, vp, vp, vp, vp, dbl, i32, vp, sz, vp,
+                             ctypes.POINTER(SolveInfo)], st),
+        "sla_pattern_grad": ([vp, vp, vp, vp, vp], st),
+        "sla_status_string": ([st], ctypes.c_char_p),
+        "sla_last_error": ([], ctypes.c_char_p),
+        "sla_set_profiling": ([i32], st),
+        "sla_get_profile": ([i32, ctypes.POINTER(i64), ctypes.POINTER(dbl)], st),
+        "sla_reset_profile": ([], st),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = res
+    return L
+
+
+def _check(status: int, allow=(OK,)) -> int:
+    if status in allow:
+        return status
+    msg = lib().sla_last_error().decode(errors="replace")
+    raise SlaError(status, msg)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream) if hasattr(stream, "cuda_stream") else stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors passed to the library must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float64:
+        return SLA_F64
+    if dt == torch.float32:
+        return SLA_F32
+    raise ValueError(f"unsupported dtype {dt}")
+
+
+class Mat:
+    """A library matrix handle; keeps the borrowed tensors alive."""
+
+    def __init__(self, handle, keep, n, nnz, block_dim, dtype):
+        self.handle = handle
+        self._keep = keep
+        self.n, self.nnz, self.block_dim, self.dtype = n, nnz, block_dim, dtype
+
+    def destroy(self):
+        if self.handle:
+            lib().sla_mat_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+    @property
+    def device(self):
+        return self._keep[0].device
+
+
+def sla_csr_create(row_ptr: torch.Tensor, col_idx: torch.Tensor, vals: torch.Tensor,
+                   build_transpose: bool = False, validate: bool = False, stream=None) -> Mat:
+    n = row_ptr.numel() - 1
+    nnz = col_idx.numel()
+    for t, want in ((row_ptr, torch.int32), (col_idx, torch.int32)):
+        if t.dtype != want:
+            raise ValueError("index arrays must be int32")
+    h = ctypes.c_void_p()
+    flags = (SLA_BUILD_TRANSPOSE if build_transpose else 0) | (SLA_VALIDATE if validate else 0)
+    _check(lib().sla_csr_create(ctypes.byref(h), n, nnz, _ptr(row_ptr), _ptr(col_idx), _ptr(vals),
+                                _dtype_code(vals.dtype), flags, _stream(stream)))
+    return Mat(h, (row_ptr, col_idx, vals), n, nnz, 1, vals.dtype)
+
+
+def sla_bsr_create(brow_ptr: torch.Tensor, bcol_idx: torch.Tensor, bvals: torch.Tensor,
+                   block_dim: int = 3, build_transpose: bool = False, validate: bool = False,
+                   stream=None) -> Mat:
+    nbr = brow_ptr.numel() - 1
+    nnzb = bcol_idx.numel()
+    if bvals.numel() != nnzb * block_dim * block_dim:
+        raise ValueError("bvals must hold nnzb * block_dim^2 values")
+    h = ctypes.c_void_p()
+    flags = (SLA_BUILD_TRANSPOSE if build_transpose else 0) | (SLA_VALIDATE if validate else 0)
+    _check(lib().sla_bsr_create(ctypes.byref(h), nbr, nnzb, block_dim, _ptr(brow_ptr),
+                                _ptr(bcol_idx), _ptr(bvals), _dtype_code(bvals.dtype), flags,
+                                _stream(stream)))
+    return Mat(h, (brow_ptr, bcol_idx, bvals), nbr * block_dim, nnzb * block_dim ** 2, block_dim,
+               bvals.dtype)
+
+
+def sla_mat_tiling(A: Mat, transpose: bool = False) -> Tuple[int, int]:
+    nt, nl = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().sla_mat_tiling(A.handle, int(transpose), ctypes.byref(nt), ctypes.byref(nl)))
+    return nt.value, nl.value
+
+
+def sla_mat_transpose_arrays(A: Mat):
+    """Raw device pointers (row_ptr, col_idx, vals) of the owned transpose."""
+    rp, ci, v = ctypes.c_void_p(), ctypes.c_void_p(), ctypes.c_void_p()
+    _check(lib().sla_mat_transpose_arrays(A.handle, ctypes.byref(rp), ctypes.byref(ci),
+                                          ctypes.byref(v)))
+    return rp.value, ci.value, v.value
+
+
+def sla_spmv(A: Mat, x: torch.Tensor, y: Optional[torch.Tensor] = None, stream=None,
+             transpose: bool = False) -> torch.Tensor:
+    if y is None:
+        y = torch.empty(A.n, dtype=A.dtype, device=x.device)
+    f = lib().sla_spmv_t if transpose else lib().sla_spmv
+    _check(f(A.handle, _ptr(x), _ptr(y), _stream(stream)))
+    return y
+
+
+def sla_pcg_workspace_size(A: Mat) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().sla_pcg_workspace_size(A.handle, ctypes.byref(b)))
+    return b.value
+
+
+def workspace(A: Mat, device=None) -> torch.Tensor:
+    nbytes = sla_pcg_workspace_size(A)
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device or A.device)
+
+
+def sla_precond_apply(G: Mat, eps: float, r: torch.Tensor, z: Optional[torch.Tensor] = None,
+                      work: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    if z is None:
+        z = torch.empty_like(r)
+    if work is None:
+        work = workspace(G, r.device)
+    _check(lib().sla_precond_apply(G.handle, float(eps), _ptr(r), _ptr(z), _ptr(work),
+                                   work.numel(), _stream(stream)))
+    return z
+
+
+@dataclasses.dataclass
+class Info:
+    status: int
+    iterations: int
+    converged: bool
+    rel_residual: float
+    bnorm: float
+
+
+def _info(status, si: SolveInfo) -> Info:
+    return Info(status, si.iterations, bool(si.converged), si.rel_residual, si.bnorm)
+
+
+def sla_pcg_solve(A: Mat, G: Mat, eps: float, b: torch.Tensor, x: Optional[torch.Tensor] = None,
+                  rtol: float = 1e-10, maxit: int = 1000, work: Optional[torch.Tensor] = None,
+                  stream=None, raise_on_error: bool = True) -> Tuple[torch.Tensor, Info]:
+    if x is None:
+        x = torch.empty_like(b)
+    if work is None:
+        work = workspace(A, b.device)
+    si = SolveInfo()
+    st = lib().sla_pcg_solve(A.handle, G.handle, float(eps), _ptr(b), _ptr(x), float(rtol),
+                             int(maxit), _ptr(work), work.numel(), _stream(stream),
+                             ctypes.byref(si))
+    if raise_on_error:
+        _check(st, allow=(OK, NOT_CONVERGED))
+    return x, _info(st, si)
+
+
+def sla_pcg_adjoint(A: Mat, G: Mat, eps: float, x: torch.Tensor, grad_x: torch.Tensor,
+                    rtol: float = 1e-10, maxit: int = 1000, grad_b: Optional[torch.Tensor] = None,
+                    grad_vals: Optional[torch.Tensor] = None, work: Optional[torch.Tensor] = None,
+                    stream=None, raise_on_error: bool = True):
+    if grad_b is None:
+        grad_b = torch.empty_like(x)
+    if grad_vals is None:
+        grad_vals = torch.empty(A.nnz, dtype=A.dtype, device=x.device)
+    if work is None:
+        work = workspace(A, x.device)
+    si = SolveInfo()
+    st = lib().sla_pcg_adjoint(A.handle, G.handle, float(eps), _ptr(x), _ptr(grad_x),
+                               _ptr(grad_b), _ptr(grad_vals), float(rtol), int(maxit), _ptr(work),
+                               work.numel(), _stream(stream), ctypes.byref(si))
+    if raise_on_error:
+        _check(st, allow=(OK, NOT_CONVERGED))
+    return grad_b, grad_vals, _info(st, si)
+
+
+def sla_pattern_grad(A: Mat, lam: torch.Tensor, x: torch.Tensor,
+                     out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty(A.nnz, dtype=A.dtype, device=x.device)
+    _check(lib().sla_pattern_grad(A.handle, _ptr(lam), _ptr(x), _ptr(out), _stream(stream)))
+    return out
+
+
+def sla_set_profiling(enable) -> None:
+    """enable: True (all classes), False, or a bit mask / iterable of class names."""
+    if enable is True:
+        mask = 15
+    elif enable is False or enable is None:
+        mask = 0
+    elif isinstance(enable, int):
+        mask = enable
+    else:
+        mask = 0
+        for c in enable:
+            mask |= 1 << (PROFILE_CLASSES[c] if isinstance(c, str) else int(c))
+    _check(lib().sla_set_profiling(int(mask)))
+
+
+def sla_reset_profile() -> None:
+    _check(lib().sla_reset_profile())
+
+
+def sla_get_profile(kernel_class) -> Tuple[int, float]:
+    if isinstance(kernel_class, str):
+        kernel_class = PROFILE_CLASSES[kernel_class]
+    n, ms = ctypes.c_int64(), ctypes.c_double()
+    _check(lib().sla_get_profile(int(kernel_class), ctypes.byref(n), ctypes.byref(ms)))
+    return n.value, ms.value
+
+
+def sla_status_string(status: int) -> str:
+    return lib().sla_status_string(int(status)).decode()

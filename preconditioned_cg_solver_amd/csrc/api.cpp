@@ -1,0 +1,379 @@
+// C ABI of the gfx950 PCG library: handle management, argument checks and
+// error reporting around the kernels in setup.hip and solver.hip.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <mutex>
+#include <new>
+#include <string>
+
+#include "internal.h"
+
+namespace sla {
+
+int occupancy_grid(int cus);  // solver.hip
+
+namespace {
+thread_local std::string g_last_error;
+
+enum OwnedSlot {
+  O_TILES_F = 0,
+  O_TILES_T = 1,
+  O_LPART_F = 2,
+  O_LCNT_F = 3,
+  O_LPART_T = 4,
+  O_LCNT_T = 5,
+  O_TRP = 6,
+  O_TCI = 7,
+  O_TV = 8
+};
+
+std::mutex g_dev_mu;
+DeviceInfo g_dev[64];
+bool g_dev_ready[64];
+
+void free_owned(sla_mat* m) {
+  for (void*& p : m->owned) {
+    if (p) (void)hipFree(p);
+    p = nullptr;
+  }
+}
+
+sla_status alloc_long_scratch(sla_mat* m, MatView& v, int part_slot, int cnt_slot,
+                              hipStream_t s) {
+  const size_t np = (size_t)std::max(1, v.n_long_part);
+  const size_t nc = (size_t)std::max(1, v.nlong_rows);
+  SLA_HIP(hipMalloc(&m->owned[part_slot], np * sizeof(double)));
+  SLA_HIP(hipMalloc(&m->owned[cnt_slot], nc * sizeof(int)));
+  SLA_HIP(hipMemsetAsync(m->owned[cnt_slot], 0, nc * sizeof(int), s));
+  return SLA_OK;
+}
+
+bool check(bool ok, const char* msg) {
+  if (!ok) set_error(msg);
+  return ok;
+}
+
+sla_status create_common(sla_mat_t* out, int64_t nbr, int64_t nnzb, int32_t bs, const int32_t* rp,
+                         const int32_t* ci, const void* v, sla_dtype dtype, uint32_t flags,
+                         void* stream) {
+  if (!check(out != nullptr, "out is NULL")) return SLA_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (!check(nbr >= 0 && nnzb >= 0, "negative size")) return SLA_ERR_INVALID_ARG;
+  if (!check(dtype == SLA_F64 || dtype == SLA_F32, "unknown dtype")) return SLA_ERR_INVALID_ARG;
+  if (bs != 1 && bs != 3) {
+    set_error("only block sizes 1 (CSR) and 3 (3x3 BSR) are supported");
+    return SLA_ERR_UNSUPPORTED;
+  }
+  if (nbr * bs >= (int64_t)INT32_MAX || nnzb * bs * bs >= (int64_t)INT32_MAX) {
+    set_error("sizes must fit int32 indices (n and nnz < 2^31)");
+    return SLA_ERR_UNSUPPORTED;
+  }
+  if (!check(rp != nullptr, "row_ptr is NULL")) return SLA_ERR_INVALID_ARG;
+  if (!check(nnzb == 0 || (ci != nullptr && v != nullptr), "col_idx or vals is NULL"))
+    return SLA_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  int hb[2] = {-1, -1};
+  SLA_HIP(hipMemcpyAsync(&hb[0], rp, sizeof(int), hipMemcpyDeviceToHost, s));
+  SLA_HIP(hipMemcpyAsync(&hb[1], rp + nbr, sizeof(int), hipMemcpyDeviceToHost, s));
+  SLA_HIP(hipStreamSynchronize(s));
+  if (hb[0] != 0 || hb[1] != (int)nnzb) {
+    char msg[128];
+    snprintf(msg, sizeof msg, "row_ptr[0] = %d, row_ptr[n] = %d, expected 0 and %lld", hb[0],
+             hb[1], (long long)nnzb);
+    set_error(msg);
+    return SLA_ERR_INVALID_ARG;
+  }
+  sla_mat* m = new (std::nothrow) sla_mat();
+  if (!m) {
+    set_error("host allocation failed");
+    return SLA_ERR_OOM;
+  }
+  m->nbr = nbr;
+  m->bs = bs;
+  m->nnzb = nnzb;
+  m->dtype = dtype;
+  (void)hipGetDevice(&m->device);
+  m->fwd.rp = rp;
+  m->fwd.ci = ci;
+  m->fwd.v = v;
+  sla_status st = SLA_OK;
+  if (flags & SLA_VALIDATE) st = validate_structure(*m, s);
+  if (st == SLA_OK && bs == 1) st = build_tiling(rp, nbr, m->fwd, &m->owned[O_TILES_F], s);
+  if (st == SLA_OK) st = alloc_long_scratch(m, m->fwd, O_LPART_F, O_LCNT_F, s);
+  if (st == SLA_OK && (flags & SLA_BUILD_TRANSPOSE)) {
+    int32_t *trp = nullptr, *tci = nullptr;
+    void* tv = nullptr;
+    st = build_transpose(*m, &trp, &tci, &tv, s);
+    m->owned[O_TRP] = trp;
+    m->owned[O_TCI] = tci;
+    m->owned[O_TV] = tv;
+    if (st == SLA_OK) {
+      m->has_t = true;
+      m->tr.rp = trp;
+      m->tr.ci = tci;
+      m->tr.v = tv;
+      if (bs == 1) st = build_tiling(trp, nbr, m->tr, &m->owned[O_TILES_T], s);
+      if (st == SLA_OK) st = alloc_long_scratch(m, m->tr, O_LPART_T, O_LCNT_T, s);
+    }
+  }
+  if (st == SLA_OK) {
+    hipError_t e = hipStreamSynchronize(s);
+    if (e != hipSuccess) st = hip_fail(e, "hipStreamSynchronize");
+  }
+  if (st != SLA_OK) {
+    (void)hipStreamSynchronize(s);
+    free_owned(m);
+    delete m;
+    return st;
+  }
+  *out = m;
+  return SLA_OK;
+}
+
+sla_status check_solve(sla_mat_t A, sla_mat_t G, double eps, const void* b, const void* x,
+                       double rtol, int32_t maxit, const void* work, size_t work_bytes) {
+  if (!check(A && G, "matrix handle is NULL")) return SLA_ERR_INVALID_ARG;
+  if (!check(A->nbr == G->nbr && A->bs == G->bs && A->dtype == G->dtype,
+             "A and G differ in size, block size or dtype"))
+    return SLA_ERR_INVALID_ARG;
+  if (!check(G->has_t, "G was created without SLA_BUILD_TRANSPOSE")) return SLA_ERR_INVALID_ARG;
+  if (!check(std::isfinite(eps) && eps >= 0.0, "eps must be finite and >= 0"))
+    return SLA_ERR_INVALID_ARG;
+  if (!check(std::isfinite(rtol) && rtol >= 0.0, "rtol must be finite and >= 0"))
+    return SLA_ERR_INVALID_ARG;
+  if (!check(maxit >= 0, "maxit must be >= 0")) return SLA_ERR_INVALID_ARG;
+  if (A->n() == 0) return SLA_OK;
+  if (!check(b && x, "vector pointer is NULL")) return SLA_ERR_INVALID_ARG;
+  if (!check(b != x, "x must not alias b")) return SLA_ERR_INVALID_ARG;
+  if (!check(work != nullptr && work_bytes >= workspace_bytes(*A), "workspace too small"))
+    return SLA_ERR_INVALID_ARG;
+  const int64_t slots = (int64_t)std::max<int64_t>(A->fwd.nlong_rows, A->nnz() / kLdsCap + 1);
+  if (!check(G->fwd.nlong_rows <= slots && G->tr.nlong_rows <= slots,
+             "G has more long rows than the workspace sized for A provides"))
+    return SLA_ERR_INVALID_ARG;
+  return SLA_OK;
+}
+
+}  // namespace
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+sla_status hip_fail(hipError_t e, const char* what) {
+  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  return e == hipErrorOutOfMemory ? SLA_ERR_OOM : SLA_ERR_HIP;
+}
+
+const DeviceInfo& device_info() {
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  if (dev < 0 || dev >= 64) dev = 0;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (!g_dev_ready[dev]) {
+    DeviceInfo d;
+    (void)hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (d.cus <= 0) d.cus = 256;
+    d.max_grid = occupancy_grid(d.cus);
+    if (const char* e = getenv("SLA_GRID")) {
+      const int g = atoi(e);
+      if (g >= 8) d.max_grid = g & ~7;
+    }
+    g_dev[dev] = d;
+    g_dev_ready[dev] = true;
+  }
+  return g_dev[dev];
+}
+
+}  // namespace sla
+
+using namespace sla;
+
+extern "C" {
+
+sla_status sla_csr_create(sla_mat_t* out, int64_t n, int64_t nnz, const int32_t* d_row_ptr,
+                          const int32_t* d_col_idx, const void* d_vals, sla_dtype dtype,
+                          uint32_t flags, void* stream) {
+  return create_common(out, n, nnz, 1, d_row_ptr, d_col_idx, d_vals, dtype, flags, stream);
+}
+
+sla_status sla_bsr_create(sla_mat_t* out, int64_t n_block_rows, int64_t nnzb, int32_t block_dim,
+                          const int32_t* d_brow_ptr, const int32_t* d_bcol_idx,
+                          const void* d_bvals, sla_dtype dtype, uint32_t flags, void* stream) {
+  return create_common(out, n_block_rows, nnzb, block_dim, d_brow_ptr, d_bcol_idx, d_bvals, dtype,
+                       flags, stream);
+}
+
+sla_status sla_mat_destroy(sla_mat_t m) {
+  if (!m) return SLA_OK;
+  (void)hipDeviceSynchronize();
+  free_owned(m);
+  delete m;
+  return SLA_OK;
+}
+
+sla_status sla_mat_info(sla_mat_t m, int64_t* n, int64_t* nnz, int32_t* block_dim,
+                        int32_t* dtype) {
+  if (!m) {
+    set_error("matrix handle is NULL");
+    return SLA_ERR_INVALID_ARG;
+  }
+  if (n) *n = m->n();
+  if (nnz) *nnz = m->nnz();
+  if (block_dim) *block_dim = m->bs;
+  if (dtype) *dtype = m->dtype;
+  return SLA_OK;
+}
+
+sla_status sla_mat_transpose_arrays(sla_mat_t m, const int32_t** d_row_ptr,
+                                    const int32_t** d_col_idx, const void** d_vals) {
+  if (!m || !m->has_t) {
+    set_error("handle has no transpose (create with SLA_BUILD_TRANSPOSE)");
+    return SLA_ERR_INVALID_ARG;
+  }
+  if (d_row_ptr) *d_row_ptr = m->tr.rp;
+  if (d_col_idx) *d_col_idx = m->tr.ci;
+  if (d_vals) *d_vals = m->tr.v;
+  return SLA_OK;
+}
+
+sla_status sla_mat_tiling(sla_mat_t m, int32_t transpose, int64_t* n_tiles, int64_t* n_long) {
+  if (!m || (transpose && !m->has_t)) {
+    set_error("bad handle or no transpose");
+    return SLA_ERR_INVALID_ARG;
+  }
+  const MatView& v = transpose ? m->tr : m->fwd;
+  if (n_tiles) *n_tiles = m->bs == 1 ? v.ntiles : (m->nbr + kBsrTileRows - 1) / kBsrTileRows;
+  if (n_long) *n_long = v.nlong;
+  return SLA_OK;
+}
+
+sla_status sla_spmv(sla_mat_t A, const void* d_x, void* d_y, void* stream) {
+  if (!A) {
+    set_error("matrix handle is NULL");
+    return SLA_ERR_INVALID_ARG;
+  }
+  if (A->n() > 0 && (!d_x || !d_y || d_x == d_y)) {
+    set_error("x and y must be distinct non-NULL device vectors");
+    return SLA_ERR_INVALID_ARG;
+  }
+  return sla::spmv(*A, false, d_x, d_y, (hipStream_t)stream);
+}
+
+sla_status sla_spmv_t(sla_mat_t A, const void* d_x, void* d_y, void* stream) {
+  if (!A || !A->has_t) {
+    set_error("handle has no transpose (create with SLA_BUILD_TRANSPOSE)");
+    return SLA_ERR_INVALID_ARG;
+  }
+  if (A->n() > 0 && (!d_x || !d_y || d_x == d_y)) {
+    set_error("x and y must be distinct non-NULL device vectors");
+    return SLA_ERR_INVALID_ARG;
+  }
+  return sla::spmv(*A, true, d_x, d_y, (hipStream_t)stream);
+}
+
+sla_status sla_pcg_workspace_size(sla_mat_t A, size_t* bytes) {
+  if (!A || !bytes) {
+    set_error("NULL argument");
+    return SLA_ERR_INVALID_ARG;
+  }
+  *bytes = workspace_bytes(*A);
+  return SLA_OK;
+}
+
+sla_status sla_precond_apply(sla_mat_t G, double eps, const void* d_r, void* d_z, void* d_work,
+                             size_t work_bytes, void* stream) {
+  if (!G || !G->has_t) {
+    set_error("G must be created with SLA_BUILD_TRANSPOSE");
+    return SLA_ERR_INVALID_ARG;
+  }
+  if (!(std::isfinite(eps) && eps >= 0.0)) {
+    set_error("eps must be finite and >= 0");
+    return SLA_ERR_INVALID_ARG;
+  }
+  if (G->n() > 0 && (!d_r || !d_z || d_r == d_z || !d_work || work_bytes < workspace_bytes(*G))) {
+    set_error("bad vector or workspace argument");
+    return SLA_ERR_INVALID_ARG;
+  }
+  return sla::precond_apply(*G, eps, d_r, d_z, d_work, work_bytes, (hipStream_t)stream);
+}
+
+sla_status sla_pcg_solve(sla_mat_t A, sla_mat_t G, double eps, const void* d_b, void* d_x,
+                         double rtol, int32_t maxit, void* d_work, size_t work_bytes, void* stream,
+                         sla_solve_info* info) {
+  sla_status st = check_solve(A, G, eps, d_b, d_x, rtol, maxit, d_work, work_bytes);
+  if (st != SLA_OK) return st;
+  return sla::pcg_solve(*A, *G, eps, d_b, d_x, rtol, maxit, d_work, work_bytes,
+                        (hipStream_t)stream, info);
+}
+
+sla_status sla_pcg_adjoint(sla_mat_t A, sla_mat_t G, double eps, const void* d_x,
+                           const void* d_grad_x, void* d_grad_b, void* d_grad_vals, double rtol,
+                           int32_t maxit, void* d_work, size_t work_bytes, void* stream,
+                           sla_solve_info* info) {
+  sla_status st = check_solve(A, G, eps, d_grad_x, d_grad_b, rtol, maxit, d_work, work_bytes);
+  if (st != SLA_OK) return st;
+  if (A->n() > 0 && (!d_x || (A->nnzb > 0 && !d_grad_vals))) {
+    set_error("x or grad_vals is NULL");
+    return SLA_ERR_INVALID_ARG;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  st = sla::pcg_solve(*A, *G, eps, d_grad_x, d_grad_b, rtol, maxit, d_work, work_bytes, s, info);
+  if (st < 0) return st;
+  sla_status gs = sla::pattern_grad(*A, d_grad_b, d_x, d_grad_vals, s);
+  if (gs != SLA_OK) return gs;
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  return st;
+}
+
+sla_status sla_pattern_grad(sla_mat_t A, const void* d_lambda, const void* d_x,
+                            void* d_grad_vals, void* stream) {
+  if (!A) {
+    set_error("matrix handle is NULL");
+    return SLA_ERR_INVALID_ARG;
+  }
+  if (A->nnzb > 0 && (!d_lambda || !d_x || !d_grad_vals)) {
+    set_error("NULL vector");
+    return SLA_ERR_INVALID_ARG;
+  }
+  return sla::pattern_grad(*A, d_lambda, d_x, d_grad_vals, (hipStream_t)stream);
+}
+
+const char* sla_status_string(sla_status st) {
+  switch (st) {
+    case SLA_OK: return "SLA_OK";
+    case SLA_NOT_CONVERGED: return "SLA_NOT_CONVERGED";
+    case SLA_ERR_INVALID_ARG: return "SLA_ERR_INVALID_ARG";
+    case SLA_ERR_UNSUPPORTED: return "SLA_ERR_UNSUPPORTED";
+    case SLA_ERR_BREAKDOWN: return "SLA_ERR_BREAKDOWN";
+    case SLA_ERR_NONFINITE: return "SLA_ERR_NONFINITE";
+    case SLA_ERR_HIP: return "SLA_ERR_HIP";
+    case SLA_ERR_OOM: return "SLA_ERR_OOM";
+  }
+  return "unknown status";
+}
+
+const char* sla_last_error(void) { return g_last_error.c_str(); }
+
+sla_status sla_set_profiling(int32_t enable) {
+  prof_enable(enable);
+  return SLA_OK;
+}
+
+sla_status sla_get_profile(int32_t kernel_class, int64_t* launches, double* total_ms) {
+  if (kernel_class < 0 || kernel_class > 3) {
+    set_error("kernel_class must be 0..3");
+    return SLA_ERR_INVALID_ARG;
+  }
+  prof_get(kernel_class, launches, total_ms);
+  return SLA_OK;
+}
+
+sla_status sla_reset_profile(void) {
+  prof_reset();
+  return SLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,142 @@
+// Internal declarations of the gfx950 PCG library (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "sla.h"
+
+namespace sla {
+
+// Workgroup size of every row-parallel kernel: four wave64 wavefronts.
+constexpr int kWG = 256;
+constexpr int kWaves = kWG / 64;
+// CSR tiles: at most kTileRows consecutive rows whose nonzeros (<= kLdsCap)
+// are staged in LDS; rows with more than kLdsCap nonzeros are split into
+// kLongChunk-sized chunks processed by separate workgroups.
+constexpr int kTileRows = 256;
+constexpr int kLdsCap = 2048;
+constexpr int kLongChunk = 4096;
+// BSR(3x3) engine: kBsrLanes lanes per block row, kWG / kBsrLanes block rows
+// per tile.
+constexpr int kBsrLanes = 32;
+constexpr int kBsrTileRows = kWG / kBsrLanes;
+// Ring sizes of the per-iteration scalars kept on the device.
+constexpr int kRing = 4;
+
+// Tile descriptor (CSR engine).
+//   kind 0: rows [a, b) staged through LDS, 2^c lanes per row.
+//   kind 1: a chunk of one long row: row a, nonzeros [b, c) of the matrix,
+//           its partial sum goes to long_part[d]; pad[0] = long-row index,
+//           pad[1] = chunks of the row, pad[2] = the row's first partial
+//           slot.  The chunk that finishes last (integer ticket) sums the
+//           row's partials in chunk order and runs the row epilogue.
+enum TileKind { kTileLds = 0, kTileLong = 1 };
+struct Tile {
+  int a, b, c, d;
+  int kind;
+  int pad[3];
+};
+
+// Device-resident solver state (lives in the caller's workspace).
+struct SolverState {
+  int done;        // set once an exit condition is met
+  int exit_kind;   // ExitKind
+  int exit_iter;   // iteration index at which the exit was taken
+  int pad0;
+  double rr;       // last ||r||^2
+  double bb;       // ||b||^2
+  double rho[kRing];    // rho_k = r_k . z_k at slot k % kRing
+  double alpha[kRing];  // alpha_k at slot k % kRing
+  double sigma;         // last p.Ap
+  double pad1;
+};
+
+enum ExitKind {
+  EX_NONE = 0,
+  EX_CONV = 1,          // ||r_k|| <= rtol ||b|| at the G step of iteration k
+  EX_MAXIT = 2,         // k == maxit without convergence
+  EX_BREAK_SIGMA = 3,   // p.Ap <= 0 or non-finite at the G^T step of iteration k
+  EX_BREAK_RHO = 4,     // rho_{k-1} <= 0 or non-finite at the A step of iteration k
+  EX_BREAK_RR = 5,      // ||r_k||^2 non-finite
+  EX_NONFINITE_B = 6,   // ||b||^2 non-finite
+  EX_BZERO = 7,         // b == 0
+  EX_MAXIT0 = 8         // maxit == 0, b != 0
+};
+
+// One orientation (A or A^T) of a matrix on the device.
+struct MatView {
+  const int32_t* rp = nullptr;
+  const int32_t* ci = nullptr;
+  const void* v = nullptr;
+  const Tile* tiles = nullptr;   // CSR only
+  int ntiles = 0;                // CSR: descriptor count; BSR: block-row tiles
+  int nlong = 0;                 // long-row chunks among the tiles
+  int nlong_rows = 0;            // rows split into chunks
+  int n_long_part = 0;           // partial slots needed by the long-row chunks
+};
+
+}  // namespace sla
+
+struct sla_mat {
+  int64_t nbr = 0;     // block rows (= rows for CSR)
+  int32_t bs = 1;      // block size
+  int64_t nnzb = 0;    // stored blocks (= nonzeros for CSR)
+  int32_t dtype = SLA_F64;
+  int device = 0;
+  sla::MatView fwd;
+  bool has_t = false;
+  sla::MatView tr;
+  // owned device memory: tiles, long-row scratch and the transpose arrays
+  void* owned[12] = {};
+  int64_t n() const { return nbr * bs; }
+  int64_t nnz() const { return nnzb * bs * bs; }
+};
+
+namespace sla {
+
+// Error plumbing (api.cpp).
+void set_error(const std::string& msg);
+sla_status hip_fail(hipError_t e, const char* what);
+
+#define SLA_HIP(call)                                        \
+  do {                                                       \
+    hipError_t e_ = (call);                                  \
+    if (e_ != hipSuccess) return ::sla::hip_fail(e_, #call); \
+  } while (0)
+
+// Device properties cached per device (api.cpp).
+struct DeviceInfo {
+  int cus = 0;
+  int max_grid = 0;      // resident workgroups of the step kernels
+};
+const DeviceInfo& device_info();
+int occupancy_grid(int cus);
+
+// Setup (setup.hip).
+sla_status build_tiling(const int32_t* d_rp, int64_t n, MatView& view, void** owned_tiles,
+                        hipStream_t s);
+sla_status build_transpose(const sla_mat& m, int32_t** t_rp, int32_t** t_ci, void** t_v,
+                           hipStream_t s);
+sla_status validate_structure(const sla_mat& m, hipStream_t s);
+
+// Solver (solver.hip).
+size_t workspace_bytes(const sla_mat& A);
+sla_status spmv(const sla_mat& A, bool transpose, const void* x, void* y, hipStream_t s);
+sla_status precond_apply(const sla_mat& G, double eps, const void* r, void* z, void* work,
+                         size_t work_bytes, hipStream_t s);
+sla_status pcg_solve(const sla_mat& A, const sla_mat& G, double eps, const void* b, void* x,
+                     double rtol, int32_t maxit, void* work, size_t work_bytes, hipStream_t s,
+                     sla_solve_info* info);
+sla_status pattern_grad(const sla_mat& A, const void* lam, const void* x, void* grad,
+                        hipStream_t s);
+
+// Profiling (solver.hip).
+void prof_enable(int mask);
+void prof_get(int cls, int64_t* launches, double* ms);
+void prof_reset();
+
+}  // namespace sla

@@ -1,0 +1,480 @@
+// Setup kernels of the gfx950 PCG library: run once per matrix handle.
+//
+//  * row binning: consecutive rows are packed into SpMV tiles of at most
+//    kTileRows rows and kLdsCap nonzeros (staged in LDS); rows longer than
+//    kLdsCap are split into kLongChunk-nonzero chunks (row splitting);
+//  * explicit transpose G^T (built once so the G^T product needs no scatter
+//    and no atomics): a stable LSD radix sort of the entries by column, so
+//    every transposed row lists its columns in ascending order and the result
+//    is deterministic; 3x3 blocks are transposed as well;
+//  * optional structure validation.
+//
+// Pages: "Learning Sparse Approximate Inverse Preconditioners for CG Solvers
+// on GPUs", "Approach" (G and G^T products each iteration); the sparse-format
+// guide "Efficient Sparse Matrix Algebra in Python", "SciPy sparse" (convert
+// once, keep conversions out of hot loops).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <vector>
+
+#include "internal.h"
+
+namespace sla {
+namespace {
+
+constexpr int kScanItems = 8;                    // per thread
+constexpr int kScanTile = kWG * kScanItems;      // 2048 per workgroup
+constexpr int kRadixBits = 8;
+constexpr int kRadixDigits = 1 << kRadixBits;
+constexpr int kRadixItems = 8;
+constexpr int kRadixTile = kWG * kRadixItems;    // 2048 keys per workgroup
+
+// ---------------------------------------------------------------------------
+// Exclusive prefix sum of int32 (device-wide, three phases, recursive).
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kWG) void scan_tiles(const int* __restrict__ in, int* __restrict__ out,
+                                                  int* __restrict__ tile_sums, int m) {
+  __shared__ int s_t[kWG];
+  const int base = blockIdx.x * kScanTile + threadIdx.x * kScanItems;
+  int v[kScanItems];
+  int run = 0;
+#pragma unroll
+  for (int j = 0; j < kScanItems; ++j) {
+    const int idx = base + j;
+    v[j] = idx < m ? in[idx] : 0;
+    const int t = v[j];
+    v[j] = run;
+    run += t;
+  }
+  s_t[threadIdx.x] = run;
+  __syncthreads();
+  // Hillis-Steele inclusive scan of the per-thread totals (integers: exact).
+  for (int off = 1; off < kWG; off <<= 1) {
+    const int add = threadIdx.x >= off ? s_t[threadIdx.x - off] : 0;
+    __syncthreads();
+    s_t[threadIdx.x] += add;
+    __syncthreads();
+  }
+  const int excl = s_t[threadIdx.x] - run;
+#pragma unroll
+  for (int j = 0; j < kScanItems; ++j) {
+    const int idx = base + j;
+    if (idx < m) out[idx] = v[j] + excl;
+  }
+  if (threadIdx.x == kWG - 1 && tile_sums) tile_sums[blockIdx.x] = s_t[kWG - 1];
+}
+
+__global__ __launch_bounds__(kWG) void scan_add(int* __restrict__ out, const int* __restrict__ offs,
+                                                int m) {
+  const int add = offs[blockIdx.x];
+  const int base = blockIdx.x * kScanTile;
+  for (int j = threadIdx.x; j < kScanTile; j += kWG) {
+    const int idx = base + j;
+    if (idx < m) out[idx] += add;
+  }
+}
+
+// Exclusive scan of m ints (in may equal out).  Temporary memory is taken
+// stream-ordered and released before returning.
+sla_status exclusive_scan(const int* in, int* out, int m, hipStream_t s) {
+  if (m <= 0) return SLA_OK;
+  const int tiles = (m + kScanTile - 1) / kScanTile;
+  if (tiles == 1) {
+    hipLaunchKernelGGL(scan_tiles, dim3(1), dim3(kWG), 0, s, in, out, (int*)nullptr, m);
+    SLA_HIP(hipGetLastError());
+    return SLA_OK;
+  }
+  int* sums = nullptr;
+  SLA_HIP(hipMallocAsync((void**)&sums, sizeof(int) * (size_t)tiles, s));
+  hipLaunchKernelGGL(scan_tiles, dim3(tiles), dim3(kWG), 0, s, in, out, sums, m);
+  SLA_HIP(hipGetLastError());
+  sla_status st = exclusive_scan(sums, sums, tiles, s);
+  if (st != SLA_OK) return st;
+  hipLaunchKernelGGL(scan_add, dim3(tiles), dim3(kWG), 0, s, out, (const int*)sums, m);
+  SLA_HIP(hipGetLastError());
+  SLA_HIP(hipFreeAsync(sums, s));
+  return SLA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Row binning into tiles.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int floor_pow2(int v) {
+  int p = 1;
+  while (p * 2 <= v) p *= 2;
+  return p;
+}
+__device__ __forceinline__ int ilog2(int p) {
+  int l = 0;
+  while ((1 << l) < p) ++l;
+  return l;
+}
+
+// Greedy packing of the rows [r0, r1) of one 256-row block.  `emit_lds(a, b,
+// nnz)` gets row ranges that fit in LDS; `emit_long(row, kb, ke)` gets rows
+// longer than kLdsCap.
+template <class E>
+__device__ void pack_block(const int* __restrict__ rp, int r0, int r1, E& em) {
+  int cur = r0, cur_nnz = 0;
+  for (int i = r0; i < r1; ++i) {
+    const int kb = rp[i], ke = rp[i + 1];
+    const int len = ke - kb;
+    if (len > kLdsCap) {
+      if (cur < i) em.lds(cur, i, cur_nnz);
+      em.longrow(i, kb, ke);
+      cur = i + 1;
+      cur_nnz = 0;
+    } else if (cur_nnz + len > kLdsCap) {
+      em.lds(cur, i, cur_nnz);
+      cur = i;
+      cur_nnz = len;
+    } else {
+      cur_nnz += len;
+    }
+  }
+  if (cur < r1) em.lds(cur, r1, cur_nnz);
+}
+
+struct CountEmit {
+  int tiles = 0, longrows = 0, chunks = 0;
+  __device__ void lds(int, int, int) { ++tiles; }
+  __device__ void longrow(int, int kb, int ke) {
+    const int nc = (ke - kb + kLongChunk - 1) / kLongChunk;
+    tiles += nc;
+    longrows += 1;
+    chunks += nc;
+  }
+};
+
+struct WriteEmit {
+  Tile* out;
+  int t, lr, ch;
+  __device__ void lds(int a, int b, int nnz) {
+    const int rows = b - a;
+    const int avg = (nnz + rows - 1) / max(rows, 1);
+    int want = 1;
+    while (want < avg && want < 64) want *= 2;
+    const int lanes = min(want, min(64, floor_pow2(kWG / rows)));
+    Tile d;
+    d.a = a;
+    d.b = b;
+    d.c = ilog2(lanes);
+    d.d = 0;
+    d.kind = kTileLds;
+    d.pad[0] = d.pad[1] = d.pad[2] = 0;
+    out[t++] = d;
+  }
+  __device__ void longrow(int row, int kb, int ke) {
+    const int nc = (ke - kb + kLongChunk - 1) / kLongChunk;
+    for (int c = 0; c < nc; ++c) {
+      Tile d;
+      d.a = row;
+      d.b = kb + c * kLongChunk;
+      d.c = min(ke, kb + (c + 1) * kLongChunk);
+      d.d = ch + c;
+      d.kind = kTileLong;
+      d.pad[0] = lr;
+      d.pad[1] = nc;
+      d.pad[2] = ch;
+      out[t++] = d;
+    }
+    lr += 1;
+    ch += nc;
+  }
+};
+
+__global__ void tiling_count(const int* __restrict__ rp, int n, int nblk, int* __restrict__ ct,
+                             int* __restrict__ cl, int* __restrict__ cc) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nblk) return;
+  CountEmit em;
+  pack_block(rp, b * kTileRows, min(n, (b + 1) * kTileRows), em);
+  ct[b] = em.tiles;
+  cl[b] = em.longrows;
+  cc[b] = em.chunks;
+}
+
+__global__ void tiling_write(const int* __restrict__ rp, int n, int nblk, const int* __restrict__ ot,
+                             const int* __restrict__ ol, const int* __restrict__ oc,
+                             Tile* __restrict__ out) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nblk) return;
+  WriteEmit em{out, ot[b], ol[b], oc[b]};
+  pack_block(rp, b * kTileRows, min(n, (b + 1) * kTileRows), em);
+}
+
+// ---------------------------------------------------------------------------
+// Transpose: stable LSD radix sort of (column, entry index) pairs.
+// ---------------------------------------------------------------------------
+
+__global__ void count_cols(const int* __restrict__ ci, int nnzb, int* __restrict__ cnt) {
+  for (int k = blockIdx.x * blockDim.x + threadIdx.x; k < nnzb; k += gridDim.x * blockDim.x)
+    atomicAdd(&cnt[ci[k]], 1);
+}
+
+// Histogram of one digit per tile, stored digit-major: hist[d * ntiles + tile].
+__global__ __launch_bounds__(kWG) void radix_hist(const int* __restrict__ keys, int m, int shift,
+                                                  int ntiles, int* __restrict__ hist) {
+  __shared__ int cnt[kRadixDigits];
+  cnt[threadIdx.x] = 0;
+  __syncthreads();
+  const int base = blockIdx.x * kRadixTile;
+  for (int s = 0; s < kRadixItems; ++s) {
+    const int e = base + s * kWG + threadIdx.x;
+    if (e < m) atomicAdd(&cnt[(keys[e] >> shift) & (kRadixDigits - 1)], 1);
+  }
+  __syncthreads();
+  hist[threadIdx.x * ntiles + blockIdx.x] = cnt[threadIdx.x];
+}
+
+// Stable scatter: element e of the tile goes to offs[d * ntiles + tile] +
+// (number of earlier elements of the tile with the same digit).  Elements
+// are ranked in rounds of 256 consecutive keys, one per thread in thread
+// order; inside a wavefront the same-digit peers are found with ballots.
+// `vals_in == nullptr` means the values are the element indices (first pass).
+__global__ __launch_bounds__(kWG) void radix_scatter(const int* __restrict__ keys_in,
+                                                     const int* __restrict__ vals_in, int m,
+                                                     int shift, int ntiles,
+                                                     const int* __restrict__ offs,
+                                                     int* __restrict__ keys_out,
+                                                     int* __restrict__ vals_out) {
+  __shared__ int running[kRadixDigits];
+  __shared__ int wcount[kWaves][kRadixDigits];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  running[tid] = offs[tid * ntiles + blockIdx.x];
+  for (int q = 0; q < kWaves; ++q) wcount[q][tid] = 0;
+  __syncthreads();
+  const unsigned long long lt = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+  const int base = blockIdx.x * kRadixTile;
+  for (int s = 0; s < kRadixItems; ++s) {
+    const int e = base + s * kWG + tid;
+    const bool valid = e < m;
+    int key = 0, val = 0, d = 0;
+    if (valid) {
+      key = keys_in[e];
+      val = vals_in ? vals_in[e] : e;
+      d = (key >> shift) & (kRadixDigits - 1);
+    }
+    unsigned long long peers = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < kRadixBits; ++bit) {
+      const bool on = (d >> bit) & 1;
+      const unsigned long long bal = __ballot(on);
+      peers &= on ? bal : ~bal;
+    }
+    const int rank = __popcll(peers & lt);
+    if (valid && rank == 0) wcount[w][d] = __popcll(peers);
+    __syncthreads();
+    if (valid) {
+      int pos = running[d] + rank;
+      for (int q = 0; q < w; ++q) pos += wcount[q][d];
+      keys_out[pos] = key;
+      vals_out[pos] = val;
+    }
+    __syncthreads();
+    int tot = 0;
+    for (int q = 0; q < kWaves; ++q) {
+      tot += wcount[q][tid];
+      wcount[q][tid] = 0;
+    }
+    running[tid] += tot;
+    __syncthreads();
+  }
+}
+
+// Row of stored entry k: the last row whose row_ptr <= k.
+__device__ __forceinline__ int row_of(const int* __restrict__ rp, int nbr, int k) {
+  int lo = 0, hi = nbr;  // rp[lo] <= k < rp[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (rp[mid] <= k) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+template <typename T>
+__global__ void transpose_fill(const int* __restrict__ rp, const int* __restrict__ ci,
+                               const T* __restrict__ v, int nbr, int nnzb, int bs,
+                               const int* __restrict__ order, int* __restrict__ t_ci,
+                               T* __restrict__ t_v) {
+  for (int p = blockIdx.x * blockDim.x + threadIdx.x; p < nnzb; p += gridDim.x * blockDim.x) {
+    const int k = order[p];
+    t_ci[p] = row_of(rp, nbr, k);
+    if (bs == 1) {
+      t_v[p] = v[k];
+    } else {
+      const int bb = bs * bs;
+      for (int r = 0; r < bs; ++r)
+        for (int c = 0; c < bs; ++c)
+          t_v[(size_t)p * bb + c * bs + r] = v[(size_t)k * bb + r * bs + c];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Validation.
+// ---------------------------------------------------------------------------
+
+__global__ void validate_rows(const int* __restrict__ rp, const int* __restrict__ ci, int nbr,
+                              int nnzb, int* __restrict__ bad) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < nbr; i += gridDim.x * blockDim.x) {
+    const int kb = rp[i], ke = rp[i + 1];
+    if (ke < kb || kb < 0 || ke > nnzb) {
+      atomicOr(bad, 1);
+      continue;
+    }
+    int prev = -1;
+    for (int k = kb; k < ke; ++k) {
+      const int c = ci[k];
+      if (c < 0 || c >= nbr) atomicOr(bad, 2);
+      if (c <= prev) atomicOr(bad, 4);
+      prev = c;
+    }
+  }
+}
+
+int grid_for(int64_t work, int per_block = kWG) {
+  const int64_t g = (work + per_block - 1) / per_block;
+  return (int)std::max<int64_t>(1, std::min<int64_t>(g, 65536));
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Host entry points.
+// ---------------------------------------------------------------------------
+
+sla_status build_tiling(const int32_t* d_rp, int64_t n, MatView& view, void** owned_tiles,
+                        hipStream_t s) {
+  view.tiles = nullptr;
+  view.ntiles = view.nlong = view.nlong_rows = view.n_long_part = 0;
+  if (n == 0) return SLA_OK;
+  const int nblk = (int)((n + kTileRows - 1) / kTileRows);
+  int* buf = nullptr;
+  SLA_HIP(hipMallocAsync((void**)&buf, sizeof(int) * 6 * (size_t)(nblk + 1), s));
+  int *ct = buf, *cl = buf + (nblk + 1), *cc = buf + 2 * (nblk + 1);
+  int *ot = buf + 3 * (nblk + 1), *ol = buf + 4 * (nblk + 1), *oc = buf + 5 * (nblk + 1);
+  SLA_HIP(hipMemsetAsync(buf, 0, sizeof(int) * 6 * (size_t)(nblk + 1), s));
+  hipLaunchKernelGGL(tiling_count, dim3((nblk + 127) / 128), dim3(128), 0, s, d_rp, (int)n, nblk,
+                     ct, cl, cc);
+  SLA_HIP(hipGetLastError());
+  // scan nblk + 1 entries so the last slot holds the totals
+  sla_status st;
+  if ((st = exclusive_scan(ct, ot, nblk + 1, s)) != SLA_OK) return st;
+  if ((st = exclusive_scan(cl, ol, nblk + 1, s)) != SLA_OK) return st;
+  if ((st = exclusive_scan(cc, oc, nblk + 1, s)) != SLA_OK) return st;
+  int tot[3];
+  SLA_HIP(hipMemcpyAsync(&tot[0], ot + nblk, sizeof(int), hipMemcpyDeviceToHost, s));
+  SLA_HIP(hipMemcpyAsync(&tot[1], ol + nblk, sizeof(int), hipMemcpyDeviceToHost, s));
+  SLA_HIP(hipMemcpyAsync(&tot[2], oc + nblk, sizeof(int), hipMemcpyDeviceToHost, s));
+  SLA_HIP(hipStreamSynchronize(s));
+  Tile* tiles = nullptr;
+  SLA_HIP(hipMalloc((void**)&tiles, sizeof(Tile) * (size_t)std::max(1, tot[0])));
+  hipLaunchKernelGGL(tiling_write, dim3((nblk + 127) / 128), dim3(128), 0, s, d_rp, (int)n, nblk,
+                     (const int*)ot, (const int*)ol, (const int*)oc, tiles);
+  SLA_HIP(hipGetLastError());
+  SLA_HIP(hipFreeAsync(buf, s));
+  SLA_HIP(hipStreamSynchronize(s));
+  *owned_tiles = tiles;
+  view.tiles = tiles;
+  view.ntiles = tot[0];
+  view.nlong_rows = tot[1];
+  view.n_long_part = tot[2];
+  view.nlong = tot[2];
+  return SLA_OK;
+}
+
+sla_status build_transpose(const sla_mat& m, int32_t** t_rp_out, int32_t** t_ci_out, void** t_v_out,
+                           hipStream_t s) {
+  const int nbr = (int)m.nbr, nnzb = (int)m.nnzb, bs = m.bs;
+  const size_t es = m.dtype == SLA_F64 ? 8 : 4;
+  int32_t *t_rp = nullptr, *t_ci = nullptr;
+  void* t_v = nullptr;
+  SLA_HIP(hipMalloc((void**)&t_rp, sizeof(int) * ((size_t)nbr + 1)));
+  SLA_HIP(hipMalloc((void**)&t_ci, sizeof(int) * (size_t)std::max(1, nnzb)));
+  SLA_HIP(hipMalloc(&t_v, es * (size_t)bs * bs * (size_t)std::max(1, nnzb)));
+  *t_rp_out = t_rp;
+  *t_ci_out = t_ci;
+  *t_v_out = t_v;
+  // row pointer of the transpose: column counts, exclusive scan
+  int* cnt = nullptr;
+  SLA_HIP(hipMallocAsync((void**)&cnt, sizeof(int) * ((size_t)nbr + 1), s));
+  SLA_HIP(hipMemsetAsync(cnt, 0, sizeof(int) * ((size_t)nbr + 1), s));
+  if (nnzb > 0) {
+    hipLaunchKernelGGL(count_cols, dim3(grid_for(nnzb)), dim3(kWG), 0, s, m.fwd.ci, nnzb, cnt);
+    SLA_HIP(hipGetLastError());
+  }
+  sla_status st = exclusive_scan(cnt, t_rp, nbr + 1, s);
+  if (st != SLA_OK) return st;
+  SLA_HIP(hipFreeAsync(cnt, s));
+  if (nnzb == 0) {
+    SLA_HIP(hipStreamSynchronize(s));
+    return SLA_OK;
+  }
+  // stable radix sort of the column keys, carrying entry indices
+  int bits = 1;
+  while (bits < 31 && ((int64_t)1 << bits) < (int64_t)nbr) ++bits;
+  const int passes = (bits + kRadixBits - 1) / kRadixBits;
+  const int ntiles = (nnzb + kRadixTile - 1) / kRadixTile;
+  int* work = nullptr;
+  const size_t hist_n = (size_t)kRadixDigits * ntiles;
+  SLA_HIP(hipMallocAsync((void**)&work, sizeof(int) * (4 * (size_t)nnzb + hist_n), s));
+  int *ka = work, *va = work + nnzb, *kb = work + 2 * (size_t)nnzb, *vb = work + 3 * (size_t)nnzb;
+  int* hist = work + 4 * (size_t)nnzb;
+  const int* kin = m.fwd.ci;
+  const int* vin = nullptr;
+  for (int p = 0; p < passes; ++p) {
+    const int shift = p * kRadixBits;
+    int* kout = (p & 1) ? kb : ka;
+    int* vout = (p & 1) ? vb : va;
+    hipLaunchKernelGGL(radix_hist, dim3(ntiles), dim3(kWG), 0, s, kin, nnzb, shift, ntiles, hist);
+    SLA_HIP(hipGetLastError());
+    if ((st = exclusive_scan(hist, hist, (int)hist_n, s)) != SLA_OK) return st;
+    hipLaunchKernelGGL(radix_scatter, dim3(ntiles), dim3(kWG), 0, s, kin, vin, nnzb, shift, ntiles,
+                       (const int*)hist, kout, vout);
+    SLA_HIP(hipGetLastError());
+    kin = kout;
+    vin = vout;
+  }
+  if (m.dtype == SLA_F64)
+    hipLaunchKernelGGL(transpose_fill<double>, dim3(grid_for(nnzb)), dim3(kWG), 0, s, m.fwd.rp,
+                       m.fwd.ci, (const double*)m.fwd.v, nbr, nnzb, bs, vin, t_ci, (double*)t_v);
+  else
+    hipLaunchKernelGGL(transpose_fill<float>, dim3(grid_for(nnzb)), dim3(kWG), 0, s, m.fwd.rp,
+                       m.fwd.ci, (const float*)m.fwd.v, nbr, nnzb, bs, vin, t_ci, (float*)t_v);
+  SLA_HIP(hipGetLastError());
+  SLA_HIP(hipFreeAsync(work, s));
+  SLA_HIP(hipStreamSynchronize(s));
+  return SLA_OK;
+}
+
+sla_status validate_structure(const sla_mat& m, hipStream_t s) {
+  int* bad = nullptr;
+  SLA_HIP(hipMallocAsync((void**)&bad, sizeof(int), s));
+  SLA_HIP(hipMemsetAsync(bad, 0, sizeof(int), s));
+  if (m.nbr > 0) {
+    hipLaunchKernelGGL(validate_rows, dim3(grid_for(m.nbr)), dim3(kWG), 0, s, m.fwd.rp, m.fwd.ci,
+                       (int)m.nbr, (int)m.nnzb, bad);
+    SLA_HIP(hipGetLastError());
+  }
+  int h = 0;
+  SLA_HIP(hipMemcpyAsync(&h, bad, sizeof(int), hipMemcpyDeviceToHost, s));
+  SLA_HIP(hipFreeAsync(bad, s));
+  SLA_HIP(hipStreamSynchronize(s));
+  if (h) {
+    char msg[160];
+    snprintf(msg, sizeof msg, "invalid sparse structure:%s%s%s",
+             (h & 1) ? " row_ptr not monotone within [0, nnz]" : "", (h & 2) ? " column out of range" : "",
+             (h & 4) ? " columns not strictly ascending within a row" : "");
+    set_error(msg);
+    return SLA_ERR_INVALID_ARG;
+  }
+  return SLA_OK;
+}
+
+}  // namespace sla

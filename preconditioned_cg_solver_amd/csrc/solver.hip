@@ -1,0 +1,961 @@
+// Hot path of the gfx950 PCG library: the three fused product kernels of a
+// preconditioned-CG iteration, the finalize step, the adjoint's pattern
+// gradient, and the host driver.
+//
+// Method: CG for sparse SPD A x = b with M^-1 = G G^T + eps I ("Learning
+// Sparse Approximate Inverse Preconditioners for CG Solvers on GPUs",
+// "Approach": G on A's sparsity, each apply is two sparse products); adjoint
+// A^T lambda = dL/dx and dL/dA_ij = -lambda_i x_j on the pattern ("torch-sla",
+// Technical Summary, Methodology 2, linear systems).
+//
+// One iteration k (textbook PCG, stopping on the recursive residual) is
+// three kernels, each one pass over one matrix with its vector work fused:
+//
+//   A step   q = A p_{k-1} with p_{k-1} = z_{k-1} + beta_{k-1} p_{k-2} formed
+//            on the fly for every gathered column (double-buffered p) and
+//            stored for owned rows, the deferred x_{k-1} = x_{k-2} +
+//            alpha_{k-1} p_{k-2}, and partials of sigma = p.q;
+//   G^T step t = G^T r_k with r_k = r_{k-1} - alpha_k q formed on the fly
+//            (double-buffered r) and stored, and partials of ||r_k||^2;
+//   G step   z_k = G t + eps r_k, partials of rho_k = r_k . z_k.
+//
+// Each kernel begins by summing the previous kernel's per-workgroup partials
+// in a fixed order (so every workgroup derives the same scalar) and the
+// convergence / breakdown decisions are taken on the device; the host polls
+// a small state record once per batch of iterations.  No floating-point
+// atomics are used anywhere, so results are bitwise reproducible.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <deque>
+#include <mutex>
+#include <vector>
+
+#include "internal.h"
+
+namespace sla {
+namespace {
+
+enum Mode {
+  M_PLAIN = 0,  // y = M x
+  M_A1 = 1,     // A step of iteration 1 (p_0 = z_0)
+  M_A = 2,      // A step of iteration k >= 2
+  M_GT0 = 3,    // G^T step of the start-up: r_0 = b, x = 0, t = G^T b
+  M_GT = 4,     // G^T step of iteration k >= 1
+  M_G0 = 5,     // G step of the start-up (checks ||b||)
+  M_G = 6,      // G step of iteration k >= 1 (checks convergence)
+  M_GZ = 7      // z = G t + eps r without solver state (precondition apply)
+};
+
+template <typename T>
+struct StepArgs {
+  const int32_t* rp;
+  const int32_t* ci;
+  const T* v;
+  const Tile* tiles;
+  int ntiles;
+  int nbr;
+  double* long_part;
+  int* long_cnt;
+  const T* in0;   // gathered vector (PLAIN: x, A: z, GT0: b, GT: r_{k-1}, G: t)
+  const T* in1;   // second gathered vector (A: p_{k-2}, GT: q)
+  T* y;           // product output (PLAIN: y, A: q, GT: t, G: z)
+  T* own;         // own-row vector output (A: p_{k-1}, GT: r_k)
+  T* xv;          // solution (A: deferred update, GT0: zeroed)
+  const T* rv;    // G: r_k
+  double eps;
+  const double* pin;  // partials summed in the prologue
+  int npin;
+  double* pout;       // partials written: [gridDim.x] workgroups then long rows
+  SolverState* st;
+  int k;
+  int maxit;
+  double rtol;
+};
+
+template <typename T>
+struct Coef {
+  T c;
+  T c2;
+};
+
+// ---------------------------------------------------------------------------
+// Reductions (deterministic: fixed association order)
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Sum over the workgroup; every thread gets lane 0 / wave order's value.
+__device__ __forceinline__ double block_sum(double v, double* red) {
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double s = red[0];
+#pragma unroll
+  for (int q = 1; q < kWaves; ++q) s += red[q];
+  return s;
+}
+
+__device__ __forceinline__ double sum_partials(const double* __restrict__ p, int np, double* red) {
+  double s = 0.0;
+  for (int i = threadIdx.x; i < np; i += kWG) s += p[i];
+  return block_sum(s, red);
+}
+
+__device__ __forceinline__ void take_exit(SolverState* st, int kind, int k) {
+  st->exit_kind = kind;
+  st->exit_iter = k;
+  st->done = 1;
+}
+
+// ---------------------------------------------------------------------------
+// Prologue: scalars of the step and exit decisions.  Returns false when the
+// whole workgroup must return (uniformly).
+// ---------------------------------------------------------------------------
+
+template <typename T, int MODE>
+__device__ __forceinline__ bool prologue(const StepArgs<T>& a, Coef<T>& cf, double* red,
+                                         int* s_flag) {
+  cf.c = T(0);
+  cf.c2 = T(0);
+  if constexpr (MODE == M_PLAIN || MODE == M_GZ) {
+    return true;
+  } else {
+    if (threadIdx.x == 0) *s_flag = __hip_atomic_load(&a.st->done, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (*s_flag) return false;
+    const bool lead = blockIdx.x == 0 && threadIdx.x == 0;
+    const int k = a.k;
+    if constexpr (MODE == M_A1 || MODE == M_A) {
+      const double rho = sum_partials(a.pin, a.npin, red);  // rho_{k-1}
+      const bool bad = !(rho > 0.0) || !isfinite(rho);
+      if (lead) {
+        if (bad) take_exit(a.st, EX_BREAK_RHO, k);
+        else a.st->rho[(k - 1) % kRing] = rho;
+      }
+      if (bad) return false;
+      if constexpr (MODE == M_A) {
+        cf.c = T(rho / a.st->rho[(k - 2) % kRing]);   // beta_{k-1}
+        cf.c2 = T(a.st->alpha[(k - 1) % kRing]);      // alpha_{k-1}
+      }
+      return true;
+    } else if constexpr (MODE == M_GT) {
+      const double sigma = sum_partials(a.pin, a.npin, red);
+      const bool bad = !(sigma > 0.0) || !isfinite(sigma);
+      const double alpha = a.st->rho[(k - 1) % kRing] / sigma;
+      if (lead) {
+        if (bad) {
+          take_exit(a.st, EX_BREAK_SIGMA, k);
+        } else {
+          a.st->alpha[k % kRing] = alpha;
+          a.st->sigma = sigma;
+        }
+      }
+      if (bad) return false;
+      cf.c = T(-alpha);
+      return true;
+    } else if constexpr (MODE == M_GT0) {
+      return true;
+    } else if constexpr (MODE == M_G0) {
+      const double bb = sum_partials(a.pin, a.npin, red);
+      int ex = EX_NONE;
+      if (!isfinite(bb)) ex = EX_NONFINITE_B;
+      else if (bb == 0.0) ex = EX_BZERO;
+      else if (a.maxit == 0) ex = EX_MAXIT0;
+      if (lead) {
+        a.st->bb = bb;
+        a.st->rr = bb;
+        if (ex != EX_NONE) take_exit(a.st, ex, 0);
+      }
+      return ex == EX_NONE;
+    } else {  // M_G
+      const double rr = sum_partials(a.pin, a.npin, red);
+      const double rnorm = sqrt(rr);
+      const double bnorm = sqrt(a.st->bb);
+      int ex = EX_NONE;
+      if (!isfinite(rnorm)) ex = EX_BREAK_RR;
+      else if (rnorm <= a.rtol * bnorm) ex = EX_CONV;
+      else if (k == a.maxit) ex = EX_MAXIT;
+      if (lead) {
+        a.st->rr = rr;
+        if (ex != EX_NONE) take_exit(a.st, ex, k);
+      }
+      return ex == EX_NONE;
+    }
+  }
+}
+
+// Value of the gathered vector at column j.
+template <typename T, int MODE>
+__device__ __forceinline__ T gat(const StepArgs<T>& a, int j, const Coef<T>& cf) {
+  if constexpr (MODE == M_A || MODE == M_GT) return fma(cf.c, a.in1[j], a.in0[j]);
+  else return a.in0[j];
+}
+
+// Row epilogue: stores and the row's contribution to the fused dot product.
+template <typename T, int MODE>
+__device__ __forceinline__ double epi(const StepArgs<T>& a, int i, T acc, const Coef<T>& cf) {
+  if constexpr (MODE == M_PLAIN) {
+    a.y[i] = acc;
+    return 0.0;
+  } else if constexpr (MODE == M_A1) {
+    const T pn = a.in0[i];
+    a.own[i] = pn;
+    a.y[i] = acc;
+    return (double)pn * (double)acc;
+  } else if constexpr (MODE == M_A) {
+    const T po = a.in1[i];
+    const T pn = fma(cf.c, po, a.in0[i]);
+    a.own[i] = pn;
+    a.xv[i] = fma(cf.c2, po, a.xv[i]);
+    a.y[i] = acc;
+    return (double)pn * (double)acc;
+  } else if constexpr (MODE == M_GT0) {
+    const T rn = a.in0[i];
+    a.own[i] = rn;
+    a.xv[i] = T(0);
+    a.y[i] = acc;
+    return (double)rn * (double)rn;
+  } else if constexpr (MODE == M_GT) {
+    const T rn = fma(cf.c, a.in1[i], a.in0[i]);
+    a.own[i] = rn;
+    a.y[i] = acc;
+    return (double)rn * (double)rn;
+  } else {  // G0, G, GZ
+    const T rv = a.rv[i];
+    const T zv = fma(T(a.eps), rv, acc);
+    a.y[i] = zv;
+    return (double)rv * (double)zv;
+  }
+}
+
+// XCD-aware tile assignment: workgroups are dispatched round-robin over the
+// 8 XCDs, so workgroup b runs on XCD b % 8.  Give each XCD a contiguous eighth
+// of the tiles and let its workgroups stride through it, so neighbouring rows
+// (and the vector entries they gather) stay in one XCD's L2.
+__device__ __forceinline__ void tile_range(int ntiles, int& t0, int& t1, int& step) {
+  const int G = gridDim.x, b = blockIdx.x;
+  if (G >= 8 && (G & 7) == 0) {
+    const int x = b & 7, slot = b >> 3;
+    t0 = (int)(((long long)ntiles * x) >> 3) + slot;
+    t1 = (int)(((long long)ntiles * (x + 1)) >> 3);
+    step = G >> 3;
+  } else {
+    t0 = b;
+    t1 = ntiles;
+    step = G;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ T shfl_xor_t(T v, int m) {
+  return __shfl_xor(v, m, 64);
+}
+
+// ---------------------------------------------------------------------------
+// CSR engine: tiles staged through LDS (2^c lanes per row) and long-row
+// chunks combined by the last finishing chunk (integer ticket).
+// ---------------------------------------------------------------------------
+
+template <typename T, int MODE>
+__global__ __launch_bounds__(kWG) void csr_step(StepArgs<T> a) {
+  __shared__ T s_val[kLdsCap];
+  __shared__ int s_col[kLdsCap];
+  __shared__ int s_rp[kTileRows + 1];
+  __shared__ double s_red[kWaves];
+  __shared__ int s_flag;
+  Coef<T> cf;
+  if (!prologue<T, MODE>(a, cf, s_red, &s_flag)) return;
+  const int tid = threadIdx.x;
+  double dot = 0.0;
+  int t0, t1, step;
+  tile_range(a.ntiles, t0, t1, step);
+  for (int t = t0; t < t1; t += step) {
+    const Tile d = a.tiles[t];
+    if (d.kind == kTileLds) {
+      const int r0 = d.a, nr = d.b - d.a, lg = d.c;
+      for (int i = tid; i <= nr; i += kWG) s_rp[i] = a.rp[r0 + i];
+      __syncthreads();
+      const int kb = s_rp[0], ne = s_rp[nr] - kb;
+      for (int e = tid; e < ne; e += kWG) {
+        s_val[e] = a.v[kb + e];
+        s_col[e] = a.ci[kb + e];
+      }
+      __syncthreads();
+      const int L = 1 << lg, g = tid >> lg, sub = tid & (L - 1);
+      T acc = T(0);
+      if (g < nr) {
+        const int e1 = s_rp[g + 1] - kb;
+        for (int e = s_rp[g] - kb + sub; e < e1; e += L)
+          acc = fma(s_val[e], gat<T, MODE>(a, s_col[e], cf), acc);
+      }
+      for (int off = L >> 1; off >= 1; off >>= 1) acc += shfl_xor_t(acc, off);
+      if (g < nr && sub == 0) dot += epi<T, MODE>(a, r0 + g, acc, cf);
+      __syncthreads();
+    } else {
+      // chunk [d.b, d.c) of long row d.a
+      double acc = 0.0;
+      for (int k = d.b + tid; k < d.c; k += kWG)
+        acc += (double)a.v[k] * (double)gat<T, MODE>(a, a.ci[k], cf);
+      const double cs = block_sum(acc, s_red);
+      const int lr = d.pad[0], nch = d.pad[1], first = d.pad[2];
+      bool finish = false;
+      double total = cs;
+      if (nch > 1) {
+        if (tid == 0) {
+          __hip_atomic_store(&a.long_part[d.d], cs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __threadfence();
+          const int ticket = atomicAdd(&a.long_cnt[lr], 1);
+          s_flag = (ticket == nch - 1);
+        }
+        __syncthreads();
+        finish = s_flag;
+        __syncthreads();
+        if (finish && tid == 0) {
+          __threadfence();
+          total = 0.0;
+          for (int c = 0; c < nch; ++c)
+            total += __hip_atomic_load(&a.long_part[first + c], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+          a.long_cnt[lr] = 0;
+        }
+      } else {
+        finish = true;
+      }
+      if (finish && tid == 0) {
+        const double c = epi<T, MODE>(a, d.a, T(total), cf);
+        if (a.pout) a.pout[gridDim.x + lr] = c;
+      }
+    }
+  }
+  if constexpr (MODE != M_PLAIN && MODE != M_GZ) {
+    const double s = block_sum(dot, s_red);
+    if (tid == 0) a.pout[blockIdx.x] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// BSR(3x3) engine: kBsrLanes lanes per block row stream the row's blocks
+// (9 values each, row-major) contiguously and keep three row accumulators.
+// ---------------------------------------------------------------------------
+
+template <typename T, int MODE>
+__global__ __launch_bounds__(kWG) void bsr3_step(StepArgs<T> a) {
+  __shared__ double s_red[kWaves];
+  __shared__ int s_flag;
+  Coef<T> cf;
+  if (!prologue<T, MODE>(a, cf, s_red, &s_flag)) return;
+  const int g = threadIdx.x / kBsrLanes, sub = threadIdx.x % kBsrLanes;
+  double dot = 0.0;
+  int t0, t1, step;
+  tile_range(a.ntiles, t0, t1, step);
+  for (int t = t0; t < t1; t += step) {
+    const int I = t * kBsrTileRows + g;
+    T acc0 = T(0), acc1 = T(0), acc2 = T(0);
+    if (I < a.nbr) {
+      const int e0 = a.rp[I] * 9, e1 = a.rp[I + 1] * 9;
+      for (int e = e0 + sub; e < e1; e += kBsrLanes) {
+        const int kb = e / 9;
+        const int w = e - kb * 9;
+        const int r = w / 3;
+        const int c = w - 3 * r;
+        const T val = a.v[e];
+        const T xv = gat<T, MODE>(a, 3 * a.ci[kb] + c, cf);
+        if (r == 0) acc0 = fma(val, xv, acc0);
+        else if (r == 1) acc1 = fma(val, xv, acc1);
+        else acc2 = fma(val, xv, acc2);
+      }
+    }
+#pragma unroll
+    for (int off = kBsrLanes / 2; off >= 1; off >>= 1) {
+      acc0 += shfl_xor_t(acc0, off);
+      acc1 += shfl_xor_t(acc1, off);
+      acc2 += shfl_xor_t(acc2, off);
+    }
+    if (I < a.nbr && sub < 3) {
+      const T accr = sub == 0 ? acc0 : (sub == 1 ? acc1 : acc2);
+      dot += epi<T, MODE>(a, 3 * I + sub, accr, cf);
+    }
+  }
+  if constexpr (MODE != M_PLAIN && MODE != M_GZ) {
+    const double s = block_sum(dot, s_red);
+    if (threadIdx.x == 0) a.pout[blockIdx.x] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Finalize: apply the pending x update of the last iteration whose alpha was
+// computed (the A step of the next iteration would have applied it).
+// ---------------------------------------------------------------------------
+
+template <typename T>
+__global__ void finalize_x(const SolverState* __restrict__ st, T* __restrict__ x,
+                           const T* __restrict__ p0, const T* __restrict__ p1, int n) {
+  const int kind = st->exit_kind, k = st->exit_iter;
+  int upd = -1;
+  if (kind == EX_CONV || kind == EX_MAXIT || kind == EX_BREAK_RR) upd = k;
+  else if (kind == EX_BREAK_RHO && k >= 2) upd = k - 1;
+  if (upd < 1) return;
+  const T al = T(st->alpha[upd % kRing]);
+  const T* p = (upd & 1) ? p1 : p0;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+    x[i] = fma(al, p[i], x[i]);
+}
+
+// ---------------------------------------------------------------------------
+// Adjoint pattern gradient: g[k] = -lambda_row(k) * x_col(k).
+// ---------------------------------------------------------------------------
+
+template <typename T>
+__global__ __launch_bounds__(kWG) void csr_grad(const int32_t* __restrict__ rp,
+                                                const int32_t* __restrict__ ci,
+                                                const Tile* __restrict__ tiles, int ntiles,
+                                                const T* __restrict__ lam, const T* __restrict__ x,
+                                                T* __restrict__ g) {
+  __shared__ int s_rp[kTileRows + 1];
+  const int tid = threadIdx.x;
+  int t0, t1, step;
+  tile_range(ntiles, t0, t1, step);
+  for (int t = t0; t < t1; t += step) {
+    const Tile d = tiles[t];
+    if (d.kind == kTileLds) {
+      const int r0 = d.a, nr = d.b - d.a;
+      for (int i = tid; i <= nr; i += kWG) s_rp[i] = rp[r0 + i];
+      __syncthreads();
+      const int kb = s_rp[0], ke = s_rp[nr];
+      for (int k = kb + tid; k < ke; k += kWG) {
+        int lo = 0, hi = nr;
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (s_rp[mid] <= k) lo = mid;
+          else hi = mid;
+        }
+        g[k] = -(lam[r0 + lo] * x[ci[k]]);
+      }
+      __syncthreads();
+    } else {
+      const T l = lam[d.a];
+      for (int k = d.b + tid; k < d.c; k += kWG) g[k] = -(l * x[ci[k]]);
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kWG) void bsr3_grad(const int32_t* __restrict__ rp,
+                                                 const int32_t* __restrict__ ci, int nbr,
+                                                 int ntiles, const T* __restrict__ lam,
+                                                 const T* __restrict__ x, T* __restrict__ g) {
+  const int gi = threadIdx.x / kBsrLanes, sub = threadIdx.x % kBsrLanes;
+  int t0, t1, step;
+  tile_range(ntiles, t0, t1, step);
+  for (int t = t0; t < t1; t += step) {
+    const int I = t * kBsrTileRows + gi;
+    if (I >= nbr) continue;
+    const int e0 = rp[I] * 9, e1 = rp[I + 1] * 9;
+    for (int e = e0 + sub; e < e1; e += kBsrLanes) {
+      const int kb = e / 9;
+      const int w = e - kb * 9;
+      const int r = w / 3;
+      const int c = w - 3 * r;
+      g[e] = -(lam[3 * I + r] * x[3 * ci[kb] + c]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int max_grid() {
+  const int g = device_info().max_grid;
+  return g > 0 ? g : 2048;
+}
+
+// Grid of a step kernel over `ntiles` tiles: at most the resident capacity,
+// a multiple of 8 (one share per XCD) when large enough.
+int step_grid(int ntiles) {
+  int g = std::min(std::max(ntiles, 1), max_grid());
+  if (g >= 8) g &= ~7;
+  return std::max(g, 1);
+}
+
+template <typename T>
+void fill_matrix(StepArgs<T>& a, const sla_mat& m, const MatView& v, double* long_part,
+                 int* long_cnt) {
+  a.rp = v.rp;
+  a.ci = v.ci;
+  a.v = (const T*)v.v;
+  a.tiles = v.tiles;
+  a.ntiles = m.bs == 1 ? v.ntiles : (int)((m.nbr + kBsrTileRows - 1) / kBsrTileRows);
+  a.nbr = (int)m.nbr;
+  a.long_part = long_part;
+  a.long_cnt = long_cnt;
+}
+
+template <typename T, int MODE>
+hipError_t launch_step(const sla_mat& m, const StepArgs<T>& a, int grid, hipStream_t s) {
+  if (m.bs == 1)
+    hipLaunchKernelGGL((csr_step<T, MODE>), dim3(grid), dim3(kWG), 0, s, a);
+  else
+    hipLaunchKernelGGL((bsr3_step<T, MODE>), dim3(grid), dim3(kWG), 0, s, a);
+  return hipGetLastError();
+}
+
+// Long-row scratch of a handle orientation lives in the handle (owned[]);
+// slots: see api.cpp (make_long_scratch).
+struct LongScratch {
+  double* part;
+  int* cnt;
+};
+LongScratch long_scratch(const sla_mat& m, bool transpose) {
+  LongScratch ls{nullptr, nullptr};
+  const int base = transpose ? 4 : 2;
+  ls.part = (double*)m.owned[base];
+  ls.cnt = (int*)m.owned[base + 1];
+  return ls;
+}
+
+// ----- profiling -----
+struct ProfClass {
+  int64_t launches = 0;
+  double ms = 0.0;
+};
+std::mutex g_prof_mu;
+std::atomic<int> g_prof_mask{0};
+ProfClass g_prof[4];
+
+struct EventPair {
+  hipEvent_t a, b;
+  int cls;
+  int k;
+};
+
+struct Recorder {
+  int mask = 0;
+  hipStream_t s = nullptr;
+  std::vector<EventPair> ev;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+  hipEvent_t get() {
+    if (used == pool.size()) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      pool.push_back(e);
+    }
+    return pool[used++];
+  }
+  hipEvent_t begin(int cls) {
+    if (!(mask & (1 << cls))) return nullptr;
+    hipEvent_t e = get();
+    if (e) (void)hipEventRecord(e, s);
+    return e;
+  }
+  void end(hipEvent_t a, int cls, int k) {
+    if (!a) return;
+    hipEvent_t e = get();
+    if (!e) return;
+    (void)hipEventRecord(e, s);
+    ev.push_back({a, e, cls, k});
+  }
+  // Accumulate the launches that did work: every launch with k <= last_a for
+  // the A / G^T classes, k < last_g (or the start-up k = 0) for the G class.
+  void flush(int iters_a, int iters_g) {
+    if (ev.empty()) return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    for (auto& p : ev) {
+      bool real = false;
+      if (p.cls == 0 || p.cls == 1) real = p.k <= iters_a;
+      else if (p.cls == 2) real = p.k < iters_g || p.k == 0;
+      else real = true;
+      if (!real) continue;
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, p.a, p.b) == hipSuccess) {
+        g_prof[p.cls].launches += 1;
+        g_prof[p.cls].ms += ms;
+      }
+    }
+    ev.clear();
+  }
+  ~Recorder() {
+    for (auto e : pool) (void)hipEventDestroy(e);
+  }
+};
+
+// ----- pinned host polling slots -----
+std::mutex g_poll_mu;
+SolverState* g_host_state = nullptr;
+hipEvent_t g_poll_ev[3];
+bool g_poll_ready = false;
+
+sla_status poll_init() {
+  if (g_poll_ready) return SLA_OK;
+  if (hipHostMalloc((void**)&g_host_state, 4 * sizeof(SolverState), hipHostMallocDefault) !=
+      hipSuccess) {
+    set_error("hipHostMalloc of the polling slots failed");
+    return SLA_ERR_OOM;
+  }
+  for (auto& e : g_poll_ev) SLA_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+  g_poll_ready = true;
+  return SLA_OK;
+}
+
+int batch_iters() {
+  static int b = [] {
+    const char* e = getenv("SLA_BATCH_ITERS");
+    int v = e ? atoi(e) : 16;
+    return std::max(1, std::min(v, 4096));
+  }();
+  return b;
+}
+
+struct Work {
+  SolverState* st;
+  double* psig;
+  double* prr;
+  double* prho;
+  void* vec[7];  // P0 P1 R0 R1 q t z
+};
+
+size_t partial_slots(const sla_mat& A) {
+  const int64_t lr_bound = std::max<int64_t>(A.fwd.nlong_rows, A.nnz() / kLdsCap + 1);
+  return (size_t)max_grid() + (size_t)lr_bound;
+}
+
+Work carve(const sla_mat& A, void* work) {
+  Work w;
+  char* p = (char*)work;
+  const size_t es = A.dtype == SLA_F64 ? 8 : 4;
+  const size_t n = (size_t)A.n();
+  w.st = (SolverState*)p;
+  p += align_up(sizeof(SolverState));
+  const size_t ps = align_up(partial_slots(A) * sizeof(double));
+  w.psig = (double*)p;
+  p += ps;
+  w.prr = (double*)p;
+  p += ps;
+  w.prho = (double*)p;
+  p += ps;
+  for (int i = 0; i < 7; ++i) {
+    w.vec[i] = p;
+    p += align_up(n * es);
+  }
+  return w;
+}
+
+template <typename T>
+sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, T* x, double rtol,
+                    int maxit, void* work, hipStream_t s, sla_solve_info* info) {
+  const int n = (int)A.n();
+  Work w = carve(A, work);
+  T *P[2] = {(T*)w.vec[0], (T*)w.vec[1]}, *R[2] = {(T*)w.vec[2], (T*)w.vec[3]};
+  T *q = (T*)w.vec[4], *t = (T*)w.vec[5], *z = (T*)w.vec[6];
+  const LongScratch lsA = long_scratch(A, false), lsG = long_scratch(G, false),
+                    lsT = long_scratch(G, true);
+  const int ntA = A.bs == 1 ? A.fwd.ntiles : (int)((A.nbr + kBsrTileRows - 1) / kBsrTileRows);
+  const int ntG = G.bs == 1 ? G.fwd.ntiles : ntA;
+  const int ntT = G.bs == 1 ? G.tr.ntiles : ntA;
+  const int grid = step_grid(std::max(ntA, std::max(ntG, ntT)));
+  const int npA = grid + A.fwd.nlong_rows, npG = grid + G.fwd.nlong_rows,
+            npT = grid + G.tr.nlong_rows;
+
+  SLA_HIP(hipMemsetAsync(w.st, 0, sizeof(SolverState), s));
+
+  StepArgs<T> aA{}, aT{}, aG{};
+  fill_matrix(aA, A, A.fwd, lsA.part, lsA.cnt);
+  fill_matrix(aT, G, G.tr, lsT.part, lsT.cnt);
+  fill_matrix(aG, G, G.fwd, lsG.part, lsG.cnt);
+  for (StepArgs<T>* a : {&aA, &aT, &aG}) {
+    a->st = w.st;
+    a->maxit = maxit;
+    a->rtol = rtol;
+    a->eps = eps;
+  }
+  // A step: pin = rho partials (from G step), pout = sigma partials
+  aA.pin = w.prho;
+  aA.npin = npG;
+  aA.pout = w.psig;
+  aA.in0 = z;
+  aA.y = q;
+  aA.xv = x;
+  // G^T step: pin = sigma partials, pout = rr partials
+  aT.pin = w.psig;
+  aT.npin = npA;
+  aT.pout = w.prr;
+  aT.in1 = q;
+  aT.y = t;
+  aT.xv = x;
+  // G step: pin = rr partials, pout = rho partials
+  aG.pin = w.prr;
+  aG.npin = npT;
+  aG.pout = w.prho;
+  aG.in0 = t;
+  aG.y = z;
+
+  Recorder rec;
+  rec.mask = g_prof_mask.load();
+  rec.s = s;
+
+  // start-up: r_0 = b, x = 0, t = G^T b, ||b||^2; z_0 = G t + eps r_0, rho_0
+  aT.k = 0;
+  aT.in0 = b;
+  aT.own = R[0];
+  hipEvent_t e0 = rec.begin(1);
+  SLA_HIP((launch_step<T, M_GT0>(G, aT, grid, s)));
+  rec.end(e0, 1, 0);
+  aG.k = 0;
+  aG.rv = R[0];
+  e0 = rec.begin(2);
+  SLA_HIP((launch_step<T, M_G0>(G, aG, grid, s)));
+  rec.end(e0, 2, 0);
+
+  std::unique_lock<std::mutex> lk(g_poll_mu);
+  sla_status pst = poll_init();
+  if (pst != SLA_OK) return pst;
+  struct Pending {
+    int slot;
+    int kend;
+  };
+  std::deque<Pending> pend;
+  int next_slot = 0;
+  const int B = batch_iters();
+  int k = 1;
+  bool finished = false;
+  while (!finished) {
+    if (k <= maxit) {
+      const int kend = std::min(maxit, k + B - 1);
+      for (int kk = k; kk <= kend; ++kk) {
+        aA.k = kk;
+        aA.in1 = P[(kk - 1) & 1];
+        aA.own = P[kk & 1];
+        hipEvent_t ea = rec.begin(0);
+        if (kk == 1) SLA_HIP((launch_step<T, M_A1>(A, aA, grid, s)));
+        else SLA_HIP((launch_step<T, M_A>(A, aA, grid, s)));
+        rec.end(ea, 0, kk);
+        aT.k = kk;
+        aT.in0 = R[(kk - 1) & 1];
+        aT.own = R[kk & 1];
+        hipEvent_t et = rec.begin(1);
+        SLA_HIP((launch_step<T, M_GT>(G, aT, grid, s)));
+        rec.end(et, 1, kk);
+        aG.k = kk;
+        aG.rv = R[kk & 1];
+        hipEvent_t eg = rec.begin(2);
+        SLA_HIP((launch_step<T, M_G>(G, aG, grid, s)));
+        rec.end(eg, 2, kk);
+      }
+      const int slot = next_slot;
+      next_slot = (next_slot + 1) % 3;
+      SLA_HIP(hipMemcpyAsync(&g_host_state[slot], w.st, 16, hipMemcpyDeviceToHost, s));
+      SLA_HIP(hipEventRecord(g_poll_ev[slot], s));
+      pend.push_back({slot, kend});
+      k = kend + 1;
+    }
+    if (pend.size() >= 2 || (k > maxit && !pend.empty())) {
+      const Pending p = pend.front();
+      pend.pop_front();
+      SLA_HIP(hipEventSynchronize(g_poll_ev[p.slot]));
+      if (g_host_state[p.slot].done) finished = true;
+    }
+    if (k > maxit && pend.empty()) finished = true;
+  }
+  while (!pend.empty()) {
+    SLA_HIP(hipEventSynchronize(g_poll_ev[pend.front().slot]));
+    pend.pop_front();
+  }
+  hipLaunchKernelGGL(finalize_x<T>, dim3(std::max(1, std::min((n + kWG - 1) / kWG, 4096))),
+                     dim3(kWG), 0, s, (const SolverState*)w.st, x, (const T*)P[0],
+                     (const T*)P[1], n);
+  SLA_HIP(hipGetLastError());
+  SolverState* hs = &g_host_state[3];
+  SLA_HIP(hipMemcpyAsync(hs, w.st, sizeof(SolverState), hipMemcpyDeviceToHost, s));
+  SLA_HIP(hipStreamSynchronize(s));
+  const SolverState fin = *hs;
+  lk.unlock();
+
+  sla_status st = SLA_OK;
+  int iters = 0, conv = 0;
+  switch (fin.exit_kind) {
+    case EX_CONV: st = SLA_OK; iters = fin.exit_iter; conv = 1; break;
+    case EX_BZERO: st = SLA_OK; iters = 0; conv = 1; break;
+    case EX_MAXIT: st = SLA_NOT_CONVERGED; iters = fin.exit_iter; break;
+    case EX_MAXIT0: st = SLA_NOT_CONVERGED; iters = 0; break;
+    case EX_BREAK_SIGMA: st = SLA_ERR_BREAKDOWN; iters = fin.exit_iter - 1; break;
+    case EX_BREAK_RHO: st = SLA_ERR_BREAKDOWN; iters = fin.exit_iter - 1; break;
+    case EX_BREAK_RR: st = SLA_ERR_BREAKDOWN; iters = fin.exit_iter; break;
+    case EX_NONFINITE_B: st = SLA_ERR_NONFINITE; iters = 0; break;
+    default:
+      set_error("solver finished without an exit record");
+      return SLA_ERR_HIP;
+  }
+  if (st == SLA_ERR_BREAKDOWN) set_error("PCG breakdown (p.Ap <= 0, r.z <= 0 or non-finite residual)");
+  if (st == SLA_ERR_NONFINITE) set_error("right-hand side is not finite");
+  if (info) {
+    info->iterations = iters;
+    info->converged = conv;
+    info->bnorm = std::sqrt(fin.bb);
+    info->rel_residual = fin.bb > 0 ? std::sqrt(fin.rr) / std::sqrt(fin.bb)
+                                    : (fin.exit_kind == EX_BZERO ? 0.0 : 1.0);
+    if (fin.exit_kind == EX_MAXIT0) info->rel_residual = 1.0;
+  }
+  // profile: A / G^T launches of iterations 1..iters did work; G launches of
+  // iterations < the exit iteration did work (the exit one returns early)
+  rec.flush(std::max(iters, fin.exit_kind == EX_BREAK_SIGMA ? fin.exit_iter : iters),
+            fin.exit_iter);
+  return st;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Internal API used by api.cpp
+// ---------------------------------------------------------------------------
+
+size_t workspace_bytes(const sla_mat& A) {
+  const size_t es = A.dtype == SLA_F64 ? 8 : 4;
+  return align_up(sizeof(SolverState)) + 3 * align_up(partial_slots(A) * sizeof(double)) +
+         7 * align_up((size_t)A.n() * es);
+}
+
+sla_status spmv(const sla_mat& A, bool transpose, const void* x, void* y, hipStream_t s) {
+  const MatView& v = transpose ? A.tr : A.fwd;
+  if (A.n() == 0) return SLA_OK;
+  hipEvent_t ea = nullptr, eb = nullptr;
+  const bool prof = (g_prof_mask.load() & (1 << 3)) != 0;
+  if (prof) {
+    SLA_HIP(hipEventCreate(&ea));
+    SLA_HIP(hipEventCreate(&eb));
+    SLA_HIP(hipEventRecord(ea, s));
+  }
+  const LongScratch ls = long_scratch(A, transpose);
+  if (A.dtype == SLA_F64) {
+    StepArgs<double> a{};
+    fill_matrix(a, A, v, ls.part, ls.cnt);
+    a.in0 = (const double*)x;
+    a.y = (double*)y;
+    SLA_HIP((launch_step<double, M_PLAIN>(A, a, step_grid(a.ntiles), s)));
+  } else {
+    StepArgs<float> a{};
+    fill_matrix(a, A, v, ls.part, ls.cnt);
+    a.in0 = (const float*)x;
+    a.y = (float*)y;
+    SLA_HIP((launch_step<float, M_PLAIN>(A, a, step_grid(a.ntiles), s)));
+  }
+  if (prof) {
+    SLA_HIP(hipEventRecord(eb, s));
+    SLA_HIP(hipEventSynchronize(eb));
+    float ms = 0.f;
+    SLA_HIP(hipEventElapsedTime(&ms, ea, eb));
+    {
+      std::lock_guard<std::mutex> lk(g_prof_mu);
+      g_prof[3].launches += 1;
+      g_prof[3].ms += ms;
+    }
+    (void)hipEventDestroy(ea);
+    (void)hipEventDestroy(eb);
+  }
+  return SLA_OK;
+}
+
+sla_status precond_apply(const sla_mat& G, double eps, const void* r, void* z, void* work,
+                         size_t, hipStream_t s) {
+  if (G.n() == 0) return SLA_OK;
+  Work w = carve(G, work);
+  void* t = w.vec[5];
+  sla_status st = spmv(G, true, r, t, s);
+  if (st != SLA_OK) return st;
+  const LongScratch ls = long_scratch(G, false);
+  if (G.dtype == SLA_F64) {
+    StepArgs<double> a{};
+    fill_matrix(a, G, G.fwd, ls.part, ls.cnt);
+    a.in0 = (const double*)t;
+    a.rv = (const double*)r;
+    a.y = (double*)z;
+    a.eps = eps;
+    SLA_HIP((launch_step<double, M_GZ>(G, a, step_grid(a.ntiles), s)));
+  } else {
+    StepArgs<float> a{};
+    fill_matrix(a, G, G.fwd, ls.part, ls.cnt);
+    a.in0 = (const float*)t;
+    a.rv = (const float*)r;
+    a.y = (float*)z;
+    a.eps = eps;
+    SLA_HIP((launch_step<float, M_GZ>(G, a, step_grid(a.ntiles), s)));
+  }
+  return SLA_OK;
+}
+
+sla_status pcg_solve(const sla_mat& A, const sla_mat& G, double eps, const void* b, void* x,
+                     double rtol, int32_t maxit, void* work, size_t, hipStream_t s,
+                     sla_solve_info* info) {
+  if (A.n() == 0) {
+    if (info) *info = sla_solve_info{0, 1, 0.0, 0.0};
+    return SLA_OK;
+  }
+  if (A.dtype == SLA_F64)
+    return pcg_impl<double>(A, G, eps, (const double*)b, (double*)x, rtol, maxit, work, s, info);
+  return pcg_impl<float>(A, G, eps, (const float*)b, (float*)x, rtol, maxit, work, s, info);
+}
+
+sla_status pattern_grad(const sla_mat& A, const void* lam, const void* x, void* grad,
+                        hipStream_t s) {
+  if (A.nnzb == 0) return SLA_OK;
+  if (A.bs == 1) {
+    const int grid = step_grid(A.fwd.ntiles);
+    if (A.dtype == SLA_F64)
+      hipLaunchKernelGGL(csr_grad<double>, dim3(grid), dim3(kWG), 0, s, A.fwd.rp, A.fwd.ci,
+                         A.fwd.tiles, A.fwd.ntiles, (const double*)lam, (const double*)x,
+                         (double*)grad);
+    else
+      hipLaunchKernelGGL(csr_grad<float>, dim3(grid), dim3(kWG), 0, s, A.fwd.rp, A.fwd.ci,
+                         A.fwd.tiles, A.fwd.ntiles, (const float*)lam, (const float*)x,
+                         (float*)grad);
+  } else {
+    const int nt = (int)((A.nbr + kBsrTileRows - 1) / kBsrTileRows);
+    const int grid = step_grid(nt);
+    if (A.dtype == SLA_F64)
+      hipLaunchKernelGGL(bsr3_grad<double>, dim3(grid), dim3(kWG), 0, s, A.fwd.rp, A.fwd.ci,
+                         (int)A.nbr, nt, (const double*)lam, (const double*)x, (double*)grad);
+    else
+      hipLaunchKernelGGL(bsr3_grad<float>, dim3(grid), dim3(kWG), 0, s, A.fwd.rp, A.fwd.ci,
+                         (int)A.nbr, nt, (const float*)lam, (const float*)x, (float*)grad);
+  }
+  SLA_HIP(hipGetLastError());
+  return SLA_OK;
+}
+
+void prof_enable(int mask) { g_prof_mask.store(mask & 15); }
+void prof_get(int cls, int64_t* launches, double* ms) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (launches) *launches = g_prof[cls].launches;
+  if (ms) *ms = g_prof[cls].ms;
+}
+void prof_reset() {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto& p : g_prof) p = ProfClass{};
+}
+
+int occupancy_grid(int cus) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, csr_step<double, M_A>, kWG, 0) !=
+          hipSuccess ||
+      per_cu <= 0)
+    per_cu = 4;
+  int g = cus * per_cu;
+  g &= ~7;
+  return std::max(8, g);
+}
+
+}  // namespace sla

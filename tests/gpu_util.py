@@ -1,0 +1,91 @@
+"""Helpers shared by the GPU parity tests (marshalling only)."""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+from preconditioned_cg_solver_amd import binding as B
+from preconditioned_cg_solver_amd import inputs as I
+
+DEV = "cuda:0"
+
+
+def say(*args):
+    """Name the case before a GPU step (and flush), so a failing run names it."""
+    print("[case]", *args, flush=True)
+    sys.stdout.flush()
+
+
+def tdev(a: np.ndarray, dtype=None) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(DEV)
+
+
+def torch_dtype(p_or_dtype):
+    d = p_or_dtype if isinstance(p_or_dtype, str) else p_or_dtype.dtype
+    return torch.float32 if d == "f32" else torch.float64
+
+
+def np_dtype(dt: str):
+    return np.float32 if dt == "f32" else np.float64
+
+
+def create(M: I.SparseMatrix, transpose=False, validate=True, dtype="f64") -> B.Mat:
+    vals = tdev(M.vals.astype(np_dtype(dtype)))
+    rp = tdev(M.row_ptr.astype(np.int32))
+    ci = tdev(M.col_idx.astype(np.int32))
+    if M.block_dim == 1:
+        return B.sla_csr_create(rp, ci, vals, build_transpose=transpose, validate=validate)
+    return B.sla_bsr_create(rp, ci, vals, block_dim=M.block_dim, build_transpose=transpose,
+                            validate=validate)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def rel(a, b) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
+
+
+def iters_close(k_gpu: int, k_ref: int) -> bool:
+    return abs(k_gpu - k_ref) <= max(1, math.ceil(0.02 * k_ref))
+
+
+def copy_device_ints(ptr: int, count: int) -> np.ndarray:
+    """Copy `count` int32 from a raw device pointer owned by the library."""
+    out = torch.empty(count, dtype=torch.int32, device=DEV)
+    _memcpy_d2d(out.data_ptr(), ptr, count * 4)
+    return out.cpu().numpy()
+
+
+def copy_device_vals(ptr: int, count: int, dtype=torch.float64) -> np.ndarray:
+    out = torch.empty(count, dtype=dtype, device=DEV)
+    _memcpy_d2d(out.data_ptr(), ptr, count * out.element_size())
+    return out.cpu().numpy()
+
+
+_hip = None
+
+
+def _memcpy_d2d(dst: int, src: int, nbytes: int):
+    """Device-to-device copy through the HIP runtime torch already loaded."""
+    import ctypes
+    global _hip
+    if _hip is None:
+        import os
+        libdir = os.path.join(os.path.dirname(torch.__file__), "lib")
+        _hip = ctypes.CDLL(os.path.join(libdir, "libamdhip64.so"))
+        _hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+        _hip.hipMemcpy.restype = ctypes.c_int
+    torch.cuda.synchronize()
+    rc = _hip.hipMemcpy(ctypes.c_void_p(dst), ctypes.c_void_p(src), nbytes, 3)
+    assert rc == 0, f"hipMemcpy failed: {rc}"

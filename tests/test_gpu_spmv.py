@@ -1,0 +1,192 @@
+"""GPU parity of the sparse products, the explicit transpose, the
+preconditioner apply and the pattern gradient against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from preconditioned_cg_solver_amd import binding as B
+from preconditioned_cg_solver_amd import inputs as I
+from gpu_util import DEV, copy_device_ints, copy_device_vals, create, host, rel, say, tdev
+
+pytestmark = pytest.mark.gpu
+
+
+def empty_rows_matrix():
+    A = I.poisson2d(12)
+    keep_rows = np.ones(A.n, bool)
+    keep_rows[[0, 5, 6, 7, 143]] = False
+    rows = A.row_of_entry()
+    keep = keep_rows[rows]
+    counts = np.bincount(rows[keep], minlength=A.n)
+    rp = np.zeros(A.n + 1, np.int32)
+    np.cumsum(counts, out=rp[1:])
+    return I.SparseMatrix(A.n, 1, rp, A.col_idx[keep], A.vals[keep])
+
+
+def hub_matrix(n=10000, seed=3):
+    """Every row has an entry in column 0 and a few random ones: the transpose
+    has one row with n entries (a long row split into several chunks)."""
+    rng = np.random.default_rng(seed)
+    rows, cols = [], []
+    for i in range(n):
+        c = set(rng.choice(n, size=rng.integers(0, 5), replace=False).tolist()) | {0, i}
+        c = sorted(c)
+        rows += [i] * len(c)
+        cols += c
+    rows = np.array(rows)
+    rp = np.zeros(n + 1, np.int32)
+    np.cumsum(np.bincount(rows, minlength=n), out=rp[1:])
+    return I.SparseMatrix(n, 1, rp, np.array(cols, np.int32), rng.standard_normal(len(cols)))
+
+
+def one_by_one():
+    return I.SparseMatrix(1, 1, np.array([0, 1], np.int32), np.array([0], np.int32),
+                          np.array([2.5]))
+
+
+MATRICES = {
+    "c0_poisson2d_32": lambda: I.make_problem(0).A,
+    "c1_heat2d_512": lambda: I.make_problem(1).A,
+    "c2_poisson3d_128": lambda: I.make_problem(2).A,
+    "poisson2d_37_ragged": lambda: I.poisson2d(37),
+    "poisson3d_13_ragged": lambda: I.poisson3d(13),
+    "irregular_3001": lambda: I.random_spd_csr(3001, np.random.default_rng(7), max_deg=40),
+    "irregular_long_rows": lambda: I.random_spd_csr(12000, np.random.default_rng(8), max_deg=6,
+                                                    long_rows=5, long_deg=9000),
+    "one_by_one": one_by_one,
+    "empty_rows": empty_rows_matrix,
+    "hub_column": hub_matrix,
+    "bsr_elastic_5": lambda: I.elastic_bsr(5, I.rng_for(3, 0)),
+    "c3_bsr_elastic_64": lambda: I.make_problem(3).A,
+}
+
+
+@pytest.mark.parametrize("name", list(MATRICES))
+def test_spmv_fp64(name):
+    M = MATRICES[name]()
+    x = I.spmv_test_vector(9, M.n)
+    say("spmv fp64", name, M.n, M.nnz)
+    h = create(M)
+    xd = tdev(x)
+    y = B.sla_spmv(h, xd)
+    torch.cuda.synchronize()
+    ref = oracle.spmv(M, x)
+    assert rel(host(y), ref) <= 1e-13
+    # bitwise reproducible
+    y2 = B.sla_spmv(h, xd)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+
+
+@pytest.mark.parametrize("name", ["c1_heat2d_512", "c0_poisson2d_32", "irregular_long_rows",
+                                  "bsr_elastic_5"])
+def test_spmv_fp32(name):
+    M = MATRICES[name]()
+    M32 = M.astype(np.float32)
+    x = I.spmv_test_vector(9, M.n).astype(np.float32)
+    say("spmv fp32", name)
+    h = create(M, dtype="f32")
+    y = B.sla_spmv(h, tdev(x))
+    torch.cuda.synchronize()
+    # reference: the fp64 oracle on the fp32-rounded matrix and vector
+    ref = oracle.spmv(I.SparseMatrix(M.n_block_rows, M.block_dim, M.row_ptr, M.col_idx,
+                                     M32.vals.astype(np.float64)), x.astype(np.float64))
+    assert rel(host(y), ref) <= 1e-5
+
+
+def test_empty_matrix():
+    say("n = 0")
+    rp = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ci = torch.zeros(0, dtype=torch.int32, device=DEV)
+    v = torch.zeros(0, dtype=torch.float64, device=DEV)
+    h = B.sla_csr_create(rp, ci, v, build_transpose=True, validate=True)
+    y = B.sla_spmv(h, torch.zeros(0, dtype=torch.float64, device=DEV))
+    assert y.numel() == 0
+
+
+FACTORS = {
+    "c0_G": lambda: I.make_problem(0).G,
+    "c2_G": lambda: I.make_problem(2).G,
+    "irregular_G": lambda: I.spai_factor(I.random_spd_csr(3001, np.random.default_rng(7),
+                                                          max_deg=40), np.random.default_rng(1)),
+    "hub_column": hub_matrix,
+    "empty_rows": empty_rows_matrix,
+    "bsr_G_5": lambda: I.spai_factor(I.elastic_bsr(5, I.rng_for(3, 0)), I.rng_for(3, 1)),
+    "c3_bsr_G": lambda: I.make_problem(3).G,
+}
+
+
+@pytest.mark.parametrize("name", list(FACTORS))
+def test_transpose_bit_exact(name):
+    M = FACTORS[name]()
+    say("transpose", name, M.n, M.nnzb)
+    h = create(M, transpose=True)
+    rp_p, ci_p, v_p = B.sla_mat_transpose_arrays(h)
+    trp, tci, tv = oracle.transpose(M)
+    assert np.array_equal(copy_device_ints(rp_p, M.n_block_rows + 1), trp)
+    assert np.array_equal(copy_device_ints(ci_p, M.nnzb), tci)
+    assert np.array_equal(copy_device_vals(v_p, M.nnz), tv)
+    # product with the transpose
+    x = I.spmv_test_vector(8, M.n)
+    y = B.sla_spmv(h, tdev(x), transpose=True)
+    torch.cuda.synchronize()
+    Mt = I.SparseMatrix(M.n_block_rows, M.block_dim, trp, tci, tv)
+    assert rel(host(y), oracle.spmv(Mt, x)) <= 1e-13
+
+
+@pytest.mark.parametrize("name", ["c0_G", "c2_G", "irregular_G", "bsr_G_5"])
+def test_precond_apply(name):
+    G = FACTORS[name]()
+    r = I.spmv_test_vector(7, G.n)
+    say("precond apply", name)
+    h = create(G, transpose=True)
+    z = B.sla_precond_apply(h, 3e-3, tdev(r))
+    torch.cuda.synchronize()
+    assert rel(host(z), oracle.precond_apply(G, 3e-3, r)) <= 1e-13
+
+
+@pytest.mark.parametrize("name", ["c0_poisson2d_32", "c2_poisson3d_128", "irregular_long_rows",
+                                  "bsr_elastic_5", "empty_rows"])
+def test_pattern_grad_bit_exact(name):
+    M = MATRICES[name]()
+    lam = I.spmv_test_vector(5, M.n)
+    x = I.spmv_test_vector(6, M.n)
+    say("pattern grad", name)
+    h = create(M)
+    g = B.sla_pattern_grad(h, tdev(lam), tdev(x))
+    torch.cuda.synchronize()
+    assert np.array_equal(g.cpu().numpy(), oracle.pattern_grad(M, lam, x))
+
+
+def test_tiling_classes():
+    """Short rows go to LDS tiles, rows above the LDS capacity to chunks."""
+    h = create(MATRICES["c2_poisson3d_128"]())
+    nt, nl = B.sla_mat_tiling(h)
+    assert nt == 2097152 // 256 and nl == 0
+    h = create(MATRICES["irregular_long_rows"]())
+    nt, nl = B.sla_mat_tiling(h)
+    assert nl >= 5 * 2          # 9000-entry rows: 3 chunks of 4096
+    ht = create(hub_matrix(), transpose=True)
+    nt, nl = B.sla_mat_tiling(ht, transpose=True)
+    assert nl == 3              # transposed row 0 holds 10000 entries
+
+
+def test_validate_rejects_bad_structure():
+    M = I.poisson2d(6)
+    ci = M.col_idx.copy()
+    ci[10] = 999
+    say("validate: column out of range")
+    with pytest.raises(B.SlaError) as e:
+        B.sla_csr_create(tdev(M.row_ptr), tdev(ci), tdev(M.vals), validate=True)
+    assert e.value.status == B.ERR_INVALID_ARG
+    ci = M.col_idx.copy()
+    ci[[3, 4]] = ci[[4, 3]]
+    with pytest.raises(B.SlaError) as e:
+        B.sla_csr_create(tdev(M.row_ptr), tdev(ci), tdev(M.vals), validate=True)
+    assert e.value.status == B.ERR_INVALID_ARG
+    rp = M.row_ptr.copy()
+    rp[-1] -= 1
+    with pytest.raises(B.SlaError) as e:
+        B.sla_csr_create(tdev(rp), tdev(M.col_idx), tdev(M.vals))
+    assert e.value.status == B.ERR_INVALID_ARG

@@ -34,6 +34,8 @@ MUTATIONS = [
      "const double alpha = rho / sigma;", "const double alpha = rho / orc_dot(n, q, q);"),
     ("iteration counted before the update",
      "*iters = k;", "*iters = k + 1;"),
+    ("adjoint gradient drops the block row offset",
+     "-(lam[I * bs + r] * x[J * bs + c])", "-(lam[I * bs] * x[J * bs + c])"),
     ("adjoint gradient transposed (lambda_j x_i)",
      "-(lam[I * bs + r] * x[J * bs + c])", "-(lam[J * bs + c] * x[I * bs + r])"),
     ("adjoint gradient sign dropped",
