@@ -27,7 +27,9 @@ enum OwnedSlot {
   O_LCNT_T = 5,
   O_TRP = 6,
   O_TCI = 7,
-  O_TV = 8
+  O_TV = 8,
+  O_SELL_F = 9,   // 9, 10, 11: values, columns, slice offsets
+  O_SELL_T = 12   // 12, 13, 14
 };
 
 std::mutex g_dev_mu;
@@ -49,6 +51,16 @@ sla_status alloc_long_scratch(sla_mat* m, MatView& v, int part_slot, int cnt_slo
   SLA_HIP(hipMalloc(&m->owned[cnt_slot], nc * sizeof(int)));
   SLA_HIP(hipMemsetAsync(m->owned[cnt_slot], 0, nc * sizeof(int), s));
   return SLA_OK;
+}
+
+// SELL-64 copies are built unless SLA_SELL=0 (then every CSR product uses
+// the LDS-tile engine).
+bool sell_enabled() {
+  static const bool on = [] {
+    const char* e = getenv("SLA_SELL");
+    return !(e && e[0] == '0');
+  }();
+  return on;
 }
 
 bool check(bool ok, const char* msg) {
@@ -102,6 +114,8 @@ sla_status create_common(sla_mat_t* out, int64_t nbr, int64_t nnzb, int32_t bs, 
   sla_status st = SLA_OK;
   if (flags & SLA_VALIDATE) st = validate_structure(*m, s);
   if (st == SLA_OK && bs == 1) st = build_tiling(rp, nbr, m->fwd, &m->owned[O_TILES_F], s);
+  if (st == SLA_OK && bs == 1 && sell_enabled())
+    st = build_sell(m->fwd, nbr, nnzb, dtype, &m->owned[O_SELL_F], s);
   if (st == SLA_OK) st = alloc_long_scratch(m, m->fwd, O_LPART_F, O_LCNT_F, s);
   if (st == SLA_OK && (flags & SLA_BUILD_TRANSPOSE)) {
     int32_t *trp = nullptr, *tci = nullptr;
@@ -116,6 +130,8 @@ sla_status create_common(sla_mat_t* out, int64_t nbr, int64_t nnzb, int32_t bs, 
       m->tr.ci = tci;
       m->tr.v = tv;
       if (bs == 1) st = build_tiling(trp, nbr, m->tr, &m->owned[O_TILES_T], s);
+      if (st == SLA_OK && bs == 1 && sell_enabled())
+        st = build_sell(m->tr, nbr, nnzb, dtype, &m->owned[O_SELL_T], s);
       if (st == SLA_OK) st = alloc_long_scratch(m, m->tr, O_LPART_T, O_LCNT_T, s);
     }
   }

@@ -20,6 +20,17 @@ constexpr int kWaves = kWG / 64;
 constexpr int kTileRows = 256;
 constexpr int kLdsCap = 2048;
 constexpr int kLongChunk = 4096;
+// Sliced ELLPACK with one wavefront per slice (SELL-64): used for a CSR
+// orientation whose rows are short and of even length (at most
+// kSellMaxWidth nonzeros per row, padding at most kSellMaxPadPct percent).
+constexpr int kSlice = 64;
+constexpr int kSellMaxWidth = 32;
+constexpr int kSellMaxPadPct = 25;
+// SELL columns are stored as int16 offsets from the row when every
+// |col - row| fits; kPad16 marks padding slots.
+constexpr int kPad16 = -32768;
+// Padding slots allocated past the last slice (covers the widest batch).
+constexpr int kSellTail = 16 * kSlice;
 // BSR(3x3) engine: kBsrLanes lanes per block row, kWG / kBsrLanes block rows
 // per tile.
 constexpr int kBsrLanes = 32;
@@ -28,7 +39,8 @@ constexpr int kBsrTileRows = kWG / kBsrLanes;
 constexpr int kRing = 4;
 
 // Tile descriptor (CSR engine).
-//   kind 0: rows [a, b) staged through LDS, 2^c lanes per row.
+//   kind 0: rows [a, b) staged through LDS, 2^c lanes per row; their
+//           nonzeros are [d, d + pad[0]).
 //   kind 1: a chunk of one long row: row a, nonzeros [b, c) of the matrix,
 //           its partial sum goes to long_part[d]; pad[0] = long-row index,
 //           pad[1] = chunks of the row, pad[2] = the row's first partial
@@ -77,6 +89,16 @@ struct MatView {
   int nlong = 0;                 // long-row chunks among the tiles
   int nlong_rows = 0;            // rows split into chunks
   int n_long_part = 0;           // partial slots needed by the long-row chunks
+  // SELL-64 copy (owned), built once when the rows qualify: slice s holds
+  // rows [64 s, 64 s + 64); slot j of its row 64 s + l sits at
+  // soff[s] + 64 j + l; padding slots have column -1 and value 0.
+  const void* sv = nullptr;
+  const int32_t* sc = nullptr;   // absolute columns, or
+  const int16_t* sd = nullptr;   // column - row offsets (preferred when they fit)
+  const int32_t* soff = nullptr;
+  int nslices = 0;
+  int sell_w = 0;                // widest slice (slots per row)
+  bool sell = false;
 };
 
 }  // namespace sla
@@ -91,7 +113,7 @@ struct sla_mat {
   bool has_t = false;
   sla::MatView tr;
   // owned device memory: tiles, long-row scratch and the transpose arrays
-  void* owned[12] = {};
+  void* owned[16] = {};
   int64_t n() const { return nbr * bs; }
   int64_t nnz() const { return nnzb * bs * bs; }
 };
@@ -122,6 +144,8 @@ sla_status build_tiling(const int32_t* d_rp, int64_t n, MatView& view, void** ow
 sla_status build_transpose(const sla_mat& m, int32_t** t_rp, int32_t** t_ci, void** t_v,
                            hipStream_t s);
 sla_status validate_structure(const sla_mat& m, hipStream_t s);
+sla_status build_sell(MatView& view, int64_t n, int64_t nnz, int32_t dtype, void** owned3,
+                      hipStream_t s);
 
 // Solver (solver.hip).
 size_t workspace_bytes(const sla_mat& A);

@@ -17,6 +17,7 @@
 
 #include <algorithm>
 #include <cstdio>
+#include <cstdlib>
 #include <vector>
 
 #include "internal.h"
@@ -151,6 +152,7 @@ struct CountEmit {
 };
 
 struct WriteEmit {
+  const int* rp;
   Tile* out;
   int t, lr, ch;
   __device__ void lds(int a, int b, int nnz) {
@@ -163,9 +165,10 @@ struct WriteEmit {
     d.a = a;
     d.b = b;
     d.c = ilog2(lanes);
-    d.d = 0;
+    d.d = rp[a];
     d.kind = kTileLds;
-    d.pad[0] = d.pad[1] = d.pad[2] = 0;
+    d.pad[0] = nnz;
+    d.pad[1] = d.pad[2] = 0;
     out[t++] = d;
   }
   __device__ void longrow(int row, int kb, int ke) {
@@ -203,7 +206,7 @@ __global__ void tiling_write(const int* __restrict__ rp, int n, int nblk, const 
                              Tile* __restrict__ out) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= nblk) return;
-  WriteEmit em{out, ot[b], ol[b], oc[b]};
+  WriteEmit em{rp, out, ot[b], ol[b], oc[b]};
   pack_block(rp, b * kTileRows, min(n, (b + 1) * kTileRows), em);
 }
 
@@ -334,6 +337,55 @@ __global__ void validate_rows(const int* __restrict__ rp, const int* __restrict_
       if (c < 0 || c >= nbr) atomicOr(bad, 2);
       if (c <= prev) atomicOr(bad, 4);
       prev = c;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// SELL-64 conversion.
+// ---------------------------------------------------------------------------
+
+// Per slice: slots (widest row x 64); global: widest row and largest
+// |column - row| (to decide whether int16 offsets can hold the columns).
+__global__ void sell_widths(const int* __restrict__ rp, const int* __restrict__ ci, int n,
+                            int nslices, int* __restrict__ slots, int* __restrict__ maxw,
+                            int* __restrict__ maxd) {
+  const int sl = blockIdx.x * blockDim.x + threadIdx.x;
+  if (sl >= nslices) return;
+  int w = 0, dmax = 0;
+  const int r1 = min(n, (sl + 1) * kSlice);
+  for (int i = sl * kSlice; i < r1; ++i) {
+    const int kb = rp[i], ke = rp[i + 1];
+    w = max(w, ke - kb);
+    if (ke > kb) dmax = max(dmax, max(abs(ci[kb] - i), abs(ci[ke - 1] - i)));
+  }
+  slots[sl] = w * kSlice;
+  atomicMax(maxw, w);
+  atomicMax(maxd, dmax);
+}
+
+// Fill the SELL slots of one row (rows past n only get padding).  C is the
+// column type: int (absolute column, -1 = padding) or short (offset from the
+// row, kPad16 = padding).
+template <typename T, typename C>
+__global__ void sell_fill(const int* __restrict__ rp, const int* __restrict__ ci,
+                          const T* __restrict__ v, int n, int nslices,
+                          const int* __restrict__ soff, T* __restrict__ sv,
+                          C* __restrict__ sc) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;  // row (padded to slices)
+  if (i >= nslices * kSlice) return;
+  const int sl = i / kSlice, lane = i % kSlice;
+  const int off = soff[sl], w = (soff[sl + 1] - off) / kSlice;
+  const int kb = i < n ? rp[i] : 0, len = i < n ? rp[i + 1] - kb : 0;
+  constexpr bool rel = sizeof(C) == 2;
+  for (int j = 0; j < w; ++j) {
+    const int dst = off + j * kSlice + lane;
+    if (j < len) {
+      sv[dst] = v[kb + j];
+      sc[dst] = (C)(rel ? ci[kb + j] - i : ci[kb + j]);
+    } else {
+      sv[dst] = T(0);
+      sc[dst] = (C)(rel ? kPad16 : -1);
     }
   }
 }
@@ -474,6 +526,80 @@ sla_status validate_structure(const sla_mat& m, hipStream_t s) {
     set_error(msg);
     return SLA_ERR_INVALID_ARG;
   }
+  return SLA_OK;
+}
+
+sla_status build_sell(MatView& view, int64_t n, int64_t nnz, int32_t dtype, void** owned3,
+                      hipStream_t s) {
+  view.sell = false;
+  if (n == 0 || nnz == 0) return SLA_OK;
+  const int nslices = (int)((n + kSlice - 1) / kSlice);
+  int* buf = nullptr;
+  SLA_HIP(hipMallocAsync((void**)&buf, sizeof(int) * ((size_t)nslices + 3), s));
+  int* slots = buf;            // nslices + 1 (last one zero)
+  int* maxw = buf + nslices + 1;
+  int* maxd = buf + nslices + 2;
+  SLA_HIP(hipMemsetAsync(buf, 0, sizeof(int) * ((size_t)nslices + 3), s));
+  hipLaunchKernelGGL(sell_widths, dim3((nslices + 255) / 256), dim3(256), 0, s, view.rp, view.ci,
+                     (int)n, nslices, slots, maxw, maxd);
+  SLA_HIP(hipGetLastError());
+  int* soff = nullptr;
+  SLA_HIP(hipMalloc((void**)&soff, sizeof(int) * ((size_t)nslices + 1)));
+  owned3[2] = soff;
+  sla_status st = exclusive_scan(slots, soff, nslices + 1, s);
+  if (st != SLA_OK) return st;
+  int h[3] = {0, 0, 0};
+  SLA_HIP(hipMemcpyAsync(&h[0], maxw, sizeof(int), hipMemcpyDeviceToHost, s));
+  SLA_HIP(hipMemcpyAsync(&h[1], soff + nslices, sizeof(int), hipMemcpyDeviceToHost, s));
+  SLA_HIP(hipMemcpyAsync(&h[2], maxd, sizeof(int), hipMemcpyDeviceToHost, s));
+  SLA_HIP(hipFreeAsync(buf, s));
+  SLA_HIP(hipStreamSynchronize(s));
+  const int64_t total = h[1];
+  if (h[0] > kSellMaxWidth || total * 100 > nnz * (100 + kSellMaxPadPct)) return SLA_OK;
+  const size_t es = dtype == SLA_F64 ? 8 : 4;
+  const char* e16 = getenv("SLA_SELL16");
+  const bool rel16 = h[2] <= 32767 && !(e16 && e16[0] == '0');
+  void* sv = nullptr;
+  void* sc = nullptr;
+  // kSellTail padding slots past the last slice let the products load whole
+  // batches without bounds checks.
+  const size_t alloc = (size_t)total + kSellTail;
+  SLA_HIP(hipMalloc(&sv, es * alloc));
+  owned3[0] = sv;
+  SLA_HIP(hipMalloc(&sc, (rel16 ? 2 : 4) * alloc));
+  owned3[1] = sc;
+  SLA_HIP(hipMemsetAsync((char*)sv + es * (size_t)total, 0, es * kSellTail, s));
+  if (rel16)
+    SLA_HIP(hipMemsetD16Async((hipDeviceptr_t)((short*)sc + total), (unsigned short)kPad16,
+                              kSellTail, s));
+  else
+    SLA_HIP(hipMemsetAsync((int*)sc + total, 0xff, 4 * (size_t)kSellTail, s));
+  const int rows = nslices * kSlice;
+  const dim3 g((rows + 255) / 256), b(256);
+  if (dtype == SLA_F64 && rel16)
+    hipLaunchKernelGGL((sell_fill<double, short>), g, b, 0, s, view.rp, view.ci,
+                       (const double*)view.v, (int)n, nslices, (const int*)soff, (double*)sv,
+                       (short*)sc);
+  else if (dtype == SLA_F64)
+    hipLaunchKernelGGL((sell_fill<double, int>), g, b, 0, s, view.rp, view.ci,
+                       (const double*)view.v, (int)n, nslices, (const int*)soff, (double*)sv,
+                       (int*)sc);
+  else if (rel16)
+    hipLaunchKernelGGL((sell_fill<float, short>), g, b, 0, s, view.rp, view.ci,
+                       (const float*)view.v, (int)n, nslices, (const int*)soff, (float*)sv,
+                       (short*)sc);
+  else
+    hipLaunchKernelGGL((sell_fill<float, int>), g, b, 0, s, view.rp, view.ci,
+                       (const float*)view.v, (int)n, nslices, (const int*)soff, (float*)sv,
+                       (int*)sc);
+  SLA_HIP(hipGetLastError());
+  view.sv = sv;
+  view.sc = rel16 ? nullptr : (const int32_t*)sc;
+  view.sd = rel16 ? (const int16_t*)sc : nullptr;
+  view.soff = soff;
+  view.nslices = nslices;
+  view.sell_w = h[0];
+  view.sell = true;
   return SLA_OK;
 }
 

@@ -31,6 +31,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 #include <deque>
 #include <mutex>
 #include <vector>
@@ -59,6 +60,12 @@ struct StepArgs {
   const Tile* tiles;
   int ntiles;
   int nbr;
+  const T* sv;           // SELL-64 copy (null: use the tiles)
+  const int32_t* sc;     // absolute columns (-1 = padding), or
+  const int16_t* sd;     // column - row offsets (kPad16 = padding)
+  const int32_t* soff;
+  int nslices;
+  int sell_w;            // widest slice (slots per row)
   double* long_part;
   int* long_cnt;
   const T* in0;   // gathered vector (PLAIN: x, A: z, GT0: b, GT: r_{k-1}, G: t)
@@ -202,6 +209,64 @@ __device__ __forceinline__ T gat(const StepArgs<T>& a, int j, const Coef<T>& cf)
   else return a.in0[j];
 }
 
+// Row-owned vector entries a row's epilogue needs; they do not depend on the
+// row sum, so the SELL engine loads them together with the gathers.
+template <typename T>
+struct Own {
+  T a, b, c;
+};
+template <typename T, int MODE>
+__device__ __forceinline__ Own<T> own_load(const StepArgs<T>& a, int i) {
+  Own<T> o{T(0), T(0), T(0)};
+  if constexpr (MODE == M_A1 || MODE == M_GT0) {
+    o.a = a.in0[i];
+  } else if constexpr (MODE == M_A) {
+    o.a = a.in1[i];
+    o.b = a.in0[i];
+    o.c = a.xv[i];
+  } else if constexpr (MODE == M_GT) {
+    o.a = a.in1[i];
+    o.b = a.in0[i];
+  } else if constexpr (MODE == M_G0 || MODE == M_G || MODE == M_GZ) {
+    o.a = a.rv[i];
+  }
+  return o;
+}
+
+// Row epilogue from preloaded row-owned entries (same arithmetic as epi()).
+template <typename T, int MODE>
+__device__ __forceinline__ double epi_own(const StepArgs<T>& a, int i, T acc, const Coef<T>& cf,
+                                          const Own<T>& o) {
+  if constexpr (MODE == M_PLAIN) {
+    a.y[i] = acc;
+    return 0.0;
+  } else if constexpr (MODE == M_A1) {
+    a.own[i] = o.a;
+    a.y[i] = acc;
+    return (double)o.a * (double)acc;
+  } else if constexpr (MODE == M_A) {
+    const T pn = fma(cf.c, o.a, o.b);
+    a.own[i] = pn;
+    a.xv[i] = fma(cf.c2, o.a, o.c);
+    a.y[i] = acc;
+    return (double)pn * (double)acc;
+  } else if constexpr (MODE == M_GT0) {
+    a.own[i] = o.a;
+    a.xv[i] = T(0);
+    a.y[i] = acc;
+    return (double)o.a * (double)o.a;
+  } else if constexpr (MODE == M_GT) {
+    const T rn = fma(cf.c, o.a, o.b);
+    a.own[i] = rn;
+    a.y[i] = acc;
+    return (double)rn * (double)rn;
+  } else {
+    const T zv = fma(T(a.eps), o.a, acc);
+    a.y[i] = zv;
+    return (double)o.a * (double)zv;
+  }
+}
+
 // Row epilogue: stores and the row's contribution to the fused dot product.
 template <typename T, int MODE>
 __device__ __forceinline__ double epi(const StepArgs<T>& a, int i, T acc, const Coef<T>& cf) {
@@ -262,12 +327,103 @@ __device__ __forceinline__ T shfl_xor_t(T v, int m) {
   return __shfl_xor(v, m, 64);
 }
 
+#ifndef SLA_ROW_BATCH
+#define SLA_ROW_BATCH 4
+#endif
+
+
+// Matrix streams (values, column indices, row pointers) are read once per
+// product.  With NT they are loaded non-temporally: they do not displace the
+// gathered vector entries from L2, and they are not allocated in the 256 MB
+// last-level Infinity Cache (MALL), which is then left to the operator the
+// host chose to keep resident there across iterations.
+template <bool NT, typename U>
+__device__ __forceinline__ U ld_stream(const U* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+// Software pipelining of the LDS tiles: the next tile's row pointers,
+// values and columns are loaded into registers (all loads of a thread in
+// flight at once) while the current tile does its gathers, then committed to
+// LDS at the top of the next round.
+constexpr int kPer = kLdsCap / kWG;
+template <typename T>
+struct TileRegs {
+  T v[kPer];
+  int c[kPer];
+  int rp, rp_last;
+};
+
+template <bool NT, typename T>
+__device__ __forceinline__ void tile_load(const StepArgs<T>& a, const Tile& d, TileRegs<T>& R) {
+  const int nr = d.b - d.a, kb = d.d, ne = d.pad[0];
+  const int tid = threadIdx.x;
+  if (tid <= nr) R.rp = ld_stream<NT>(a.rp + d.a + tid);
+  if (tid == 0 && nr == kWG) R.rp_last = ld_stream<NT>(a.rp + d.a + kWG);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = tid + j * kWG;
+    if (e < ne) {
+      R.v[j] = ld_stream<NT>(a.v + kb + e);
+      R.c[j] = ld_stream<NT>(a.ci + kb + e);
+    }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void tile_commit(const Tile& d, const TileRegs<T>& R, T* s_val,
+                                            int* s_col, int* s_rp) {
+  const int nr = d.b - d.a, ne = d.pad[0];
+  const int tid = threadIdx.x;
+  if (tid <= nr) s_rp[tid] = R.rp;
+  if (tid == 0 && nr == kWG) s_rp[kWG] = R.rp_last;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = tid + j * kWG;
+    if (e < ne) {
+      s_val[e] = R.v[j];
+      s_col[e] = R.c[j];
+    }
+  }
+}
+
+// Sum of one row's entries [e0, e1) (stride L) from LDS: batches of
+// SLA_ROW_BATCH entries load their values and columns, then issue all the
+// gathers, then accumulate in entry order (the order is fixed, so results do
+// not depend on the batching).
+template <typename T, int MODE>
+__device__ __forceinline__ T row_sum_lds(const StepArgs<T>& a, const T* s_val, const int* s_col,
+                                         int e0, int e1, int L, const Coef<T>& cf) {
+  constexpr int U = SLA_ROW_BATCH;
+  T acc = T(0);
+  for (int e = e0; e < e1; e += U * L) {
+    T vv[U], xx[U];
+    int cc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ee = e + u * L;
+      const bool in = ee < e1;
+      vv[u] = in ? s_val[ee] : T(0);
+      cc[u] = in ? s_col[ee] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) xx[u] = cc[u] >= 0 ? gat<T, MODE>(a, cc[u], cf) : T(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (cc[u] >= 0) acc = fma(vv[u], xx[u], acc);
+  }
+  return acc;
+}
+
 // ---------------------------------------------------------------------------
 // CSR engine: tiles staged through LDS (2^c lanes per row) and long-row
 // chunks combined by the last finishing chunk (integer ticket).
 // ---------------------------------------------------------------------------
 
-template <typename T, int MODE>
+static_assert(kTileRows == kWG, "one row pointer per thread when staging a tile");
+
+template <typename T, int MODE, bool NT>
 __global__ __launch_bounds__(kWG) void csr_step(StepArgs<T> a) {
   __shared__ T s_val[kLdsCap];
   __shared__ int s_col[kLdsCap];
@@ -280,33 +436,48 @@ __global__ __launch_bounds__(kWG) void csr_step(StepArgs<T> a) {
   double dot = 0.0;
   int t0, t1, step;
   tile_range(a.ntiles, t0, t1, step);
+  TileRegs<T> R;
+  Tile nxt;
+  if (t0 < t1) {
+    nxt = a.tiles[t0];
+    if (nxt.kind == kTileLds) tile_load<NT>(a, nxt, R);
+  }
   for (int t = t0; t < t1; t += step) {
-    const Tile d = a.tiles[t];
+    const Tile d = nxt;
     if (d.kind == kTileLds) {
-      const int r0 = d.a, nr = d.b - d.a, lg = d.c;
-      for (int i = tid; i <= nr; i += kWG) s_rp[i] = a.rp[r0 + i];
-      __syncthreads();
-      const int kb = s_rp[0], ne = s_rp[nr] - kb;
-      for (int e = tid; e < ne; e += kWG) {
-        s_val[e] = a.v[kb + e];
-        s_col[e] = a.ci[kb + e];
+      tile_commit(d, R, s_val, s_col, s_rp);
+      if (t + step < t1) {
+        nxt = a.tiles[t + step];
+        if (nxt.kind == kTileLds) tile_load<NT>(a, nxt, R);
       }
       __syncthreads();
+      const int r0 = d.a, nr = d.b - d.a, lg = d.c, kb = d.d;
       const int L = 1 << lg, g = tid >> lg, sub = tid & (L - 1);
       T acc = T(0);
-      if (g < nr) {
-        const int e1 = s_rp[g + 1] - kb;
-        for (int e = s_rp[g] - kb + sub; e < e1; e += L)
-          acc = fma(s_val[e], gat<T, MODE>(a, s_col[e], cf), acc);
-      }
+      if (g < nr) acc = row_sum_lds<T, MODE>(a, s_val, s_col, s_rp[g] - kb + sub, s_rp[g + 1] - kb,
+                                             L, cf);
       for (int off = L >> 1; off >= 1; off >>= 1) acc += shfl_xor_t(acc, off);
       if (g < nr && sub == 0) dot += epi<T, MODE>(a, r0 + g, acc, cf);
       __syncthreads();
     } else {
-      // chunk [d.b, d.c) of long row d.a
+      // chunk [d.b, d.c) of long row d.a, four loads in flight per thread
       double acc = 0.0;
-      for (int k = d.b + tid; k < d.c; k += kWG)
-        acc += (double)a.v[k] * (double)gat<T, MODE>(a, a.ci[k], cf);
+      for (int k = d.b + tid; k < d.c; k += 4 * kWG) {
+        T vv[4], xx[4];
+        int cc[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int kk = k + u * kWG;
+          const bool in = kk < d.c;
+          vv[u] = in ? ld_stream<NT>(a.v + kk) : T(0);
+          cc[u] = in ? ld_stream<NT>(a.ci + kk) : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) xx[u] = cc[u] >= 0 ? gat<T, MODE>(a, cc[u], cf) : T(0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (cc[u] >= 0) acc += (double)vv[u] * (double)xx[u];
+      }
       const double cs = block_sum(acc, s_red);
       const int lr = d.pad[0], nch = d.pad[1], first = d.pad[2];
       bool finish = false;
@@ -336,6 +507,10 @@ __global__ __launch_bounds__(kWG) void csr_step(StepArgs<T> a) {
         const double c = epi<T, MODE>(a, d.a, T(total), cf);
         if (a.pout) a.pout[gridDim.x + lr] = c;
       }
+      if (t + step < t1) {
+        nxt = a.tiles[t + step];
+        if (nxt.kind == kTileLds) tile_load<NT>(a, nxt, R);
+      }
     }
   }
   if constexpr (MODE != M_PLAIN && MODE != M_GZ) {
@@ -345,11 +520,126 @@ __global__ __launch_bounds__(kWG) void csr_step(StepArgs<T> a) {
 }
 
 // ---------------------------------------------------------------------------
+// SELL-64 engine: one wavefront per slice of 64 rows, lane l owns row
+// 64 s + l and reads its slots at soff[s] + 64 j + l, so every value and
+// column load of a wavefront is one contiguous 512 / 256 byte access.  No
+// LDS and no barrier inside the slice loop: waves advance independently.
+// ---------------------------------------------------------------------------
+
+// Raw column word of a slot and its decoding: absolute int32 columns (-1 =
+// padding) or int16 offsets from the row (kPad16 = padding).  Loads are
+// unconditional (the SELL arrays carry a batch of padding slots past the last
+// slice), so a batch issues all its loads back to back; masking happens after.
+template <bool NT, bool I16, typename T>
+__device__ __forceinline__ int sell_raw(const StepArgs<T>& a, int idx) {
+  if constexpr (I16) return ld_stream<NT>(a.sd + idx);
+  else return ld_stream<NT>(a.sc + idx);
+}
+template <bool I16>
+__device__ __forceinline__ int sell_decode(int raw, int row, bool in) {
+  if constexpr (I16) return (in && raw != kPad16) ? row + raw : -1;
+  else return in ? raw : -1;
+}
+
+// One batch of U slots starting at slot j of a slice: value, column and
+// gathered entry (0 for padding) for every slot.
+template <typename T, int MODE, bool NT, bool I16, int U>
+__device__ __forceinline__ void sell_batch(const StepArgs<T>& a, int off, int lane, int row,
+                                           int j, int w, const Coef<T>& cf, T (&v)[U],
+                                           T (&x)[U]) {
+  int raw[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int idx = off + (j + u) * kSlice + lane;
+    v[u] = ld_stream<NT>(a.sv + idx);
+    raw[u] = sell_raw<NT, I16>(a, idx);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int c = sell_decode<I16>(raw[u], row, j + u < w);
+    const T g = gat<T, MODE>(a, c >= 0 ? c : 0, cf);
+    x[u] = c >= 0 ? g : T(0);
+    if (c < 0) v[u] = T(0);
+  }
+}
+
+template <typename T, int MODE, bool NT, bool I16, int U>
+__global__ __launch_bounds__(kWG) void sell_step(StepArgs<T> a) {
+  __shared__ double s_red[kWaves];
+  __shared__ int s_flag;
+  const int lane = threadIdx.x & (kSlice - 1), wv = threadIdx.x / kSlice;
+  int t0, t1, step;
+  tile_range(a.ntiles, t0, t1, step);
+  // The first batch of slots of the next slice is kept in registers: it is
+  // loaded while the current slice does its gathers (and, for the first
+  // slice, while the prologue sums the partials).
+  T hv[U];
+  int hr[U];
+  int hoff = 0, hw = 0;
+  auto load_head = [&](int sl) {
+    hoff = 0;
+    hw = 0;
+    if (sl < a.nslices) {
+      hoff = a.soff[sl];
+      hw = (a.soff[sl + 1] - hoff) / kSlice;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int idx = hoff + u * kSlice + lane;
+      hv[u] = ld_stream<NT>(a.sv + idx);
+      hr[u] = sell_raw<NT, I16>(a, idx);
+    }
+  };
+  if (t0 < t1) load_head(t0 * kWaves + wv);
+  Coef<T> cf;
+  if (!prologue<T, MODE>(a, cf, s_red, &s_flag)) return;
+  double dot = 0.0;
+  for (int t = t0; t < t1; t += step) {
+    const int sl = t * kWaves + wv;
+    const int off = hoff, w = hw;
+    T cv[U];
+    int cr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      cv[u] = hv[u];
+      cr[u] = hr[u];
+    }
+    if (t + step < t1) load_head((t + step) * kWaves + wv);
+    if (sl >= a.nslices) continue;
+    const int row = sl * kSlice + lane;
+    const bool live = row < a.nbr;
+    T xx[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = sell_decode<I16>(cr[u], row, u < w);
+      const T g = gat<T, MODE>(a, c >= 0 ? c : 0, cf);
+      xx[u] = c >= 0 ? g : T(0);
+      if (c < 0) cv[u] = T(0);
+    }
+    const Own<T> o = own_load<T, MODE>(a, live ? row : 0);
+    T acc = T(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc = fma(cv[u], xx[u], acc);
+    for (int j = U; j < w; j += U) {
+      T vv[U], yy[U];
+      sell_batch<T, MODE, NT, I16, U>(a, off, lane, row, j, w, cf, vv, yy);
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc = fma(vv[u], yy[u], acc);
+    }
+    if (live) dot += epi_own<T, MODE>(a, row, acc, cf, o);
+  }
+  if constexpr (MODE != M_PLAIN && MODE != M_GZ) {
+    const double s = block_sum(dot, s_red);
+    if (threadIdx.x == 0) a.pout[blockIdx.x] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // BSR(3x3) engine: kBsrLanes lanes per block row stream the row's blocks
 // (9 values each, row-major) contiguously and keep three row accumulators.
 // ---------------------------------------------------------------------------
 
-template <typename T, int MODE>
+template <typename T, int MODE, bool NT>
 __global__ __launch_bounds__(kWG) void bsr3_step(StepArgs<T> a) {
   __shared__ double s_red[kWaves];
   __shared__ int s_flag;
@@ -363,17 +653,31 @@ __global__ __launch_bounds__(kWG) void bsr3_step(StepArgs<T> a) {
     const int I = t * kBsrTileRows + g;
     T acc0 = T(0), acc1 = T(0), acc2 = T(0);
     if (I < a.nbr) {
-      const int e0 = a.rp[I] * 9, e1 = a.rp[I + 1] * 9;
-      for (int e = e0 + sub; e < e1; e += kBsrLanes) {
-        const int kb = e / 9;
-        const int w = e - kb * 9;
-        const int r = w / 3;
-        const int c = w - 3 * r;
-        const T val = a.v[e];
-        const T xv = gat<T, MODE>(a, 3 * a.ci[kb] + c, cf);
-        if (r == 0) acc0 = fma(val, xv, acc0);
-        else if (r == 1) acc1 = fma(val, xv, acc1);
-        else acc2 = fma(val, xv, acc2);
+      const int e0 = ld_stream<NT>(a.rp + I) * 9, e1 = ld_stream<NT>(a.rp + I + 1) * 9;
+      // batches of kB values per lane: loads first, then gathers, then the
+      // accumulation in value order
+      constexpr int kB = 8;
+      for (int e = e0 + sub; e < e1; e += kB * kBsrLanes) {
+        T vv[kB], xx[kB];
+        int rr[kB], cc[kB];
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+          const int ee = e + u * kBsrLanes;
+          const bool in = ee < e1;
+          const int kb = ee / 9;
+          const int w = ee - kb * 9;
+          rr[u] = in ? w / 3 : -1;
+          vv[u] = in ? ld_stream<NT>(a.v + ee) : T(0);
+          cc[u] = in ? 3 * ld_stream<NT>(a.ci + kb) + (w - 3 * (w / 3)) : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kB; ++u) xx[u] = rr[u] >= 0 ? gat<T, MODE>(a, cc[u], cf) : T(0);
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+          if (rr[u] == 0) acc0 = fma(vv[u], xx[u], acc0);
+          else if (rr[u] == 1) acc1 = fma(vv[u], xx[u], acc1);
+          else if (rr[u] == 2) acc2 = fma(vv[u], xx[u], acc2);
+        }
       }
     }
 #pragma unroll
@@ -492,6 +796,14 @@ int step_grid(int ntiles) {
   return std::max(g, 1);
 }
 
+// Work items of a product over one orientation: SELL slices grouped by
+// workgroup (one per wavefront), LDS tiles, or BSR block-row tiles.
+int view_tiles(const sla_mat& m, const MatView& v) {
+  if (m.bs != 1) return (int)((m.nbr + kBsrTileRows - 1) / kBsrTileRows);
+  if (v.sell) return (v.nslices + kWaves - 1) / kWaves;
+  return v.ntiles;
+}
+
 template <typename T>
 void fill_matrix(StepArgs<T>& a, const sla_mat& m, const MatView& v, double* long_part,
                  int* long_cnt) {
@@ -499,19 +811,83 @@ void fill_matrix(StepArgs<T>& a, const sla_mat& m, const MatView& v, double* lon
   a.ci = v.ci;
   a.v = (const T*)v.v;
   a.tiles = v.tiles;
-  a.ntiles = m.bs == 1 ? v.ntiles : (int)((m.nbr + kBsrTileRows - 1) / kBsrTileRows);
+  a.ntiles = view_tiles(m, v);
+  if (m.bs == 1 && v.sell) {
+    a.sv = (const T*)v.sv;
+    a.sc = v.sd ? nullptr : v.sc;
+    a.sd = v.sd;
+    a.soff = v.soff;
+    a.nslices = v.nslices;
+    a.sell_w = v.sell_w;
+  }
   a.nbr = (int)m.nbr;
   a.long_part = long_part;
   a.long_cnt = long_cnt;
 }
 
 template <typename T, int MODE>
-hipError_t launch_step(const sla_mat& m, const StepArgs<T>& a, int grid, hipStream_t s) {
-  if (m.bs == 1)
-    hipLaunchKernelGGL((csr_step<T, MODE>), dim3(grid), dim3(kWG), 0, s, a);
-  else
-    hipLaunchKernelGGL((bsr3_step<T, MODE>), dim3(grid), dim3(kWG), 0, s, a);
+hipError_t launch_step(const sla_mat& m, const StepArgs<T>& a, int grid, hipStream_t s,
+                       bool nt) {
+  if (m.bs == 1 && (a.sd || a.sc)) {
+    // batch of slots per load round: the slice width rounded up to 4 or 8
+    const bool wide = a.sell_w > 4;
+    const dim3 g(grid), b(kWG);
+    if (a.sd) {
+      if (nt && wide) hipLaunchKernelGGL((sell_step<T, MODE, true, true, 8>), g, b, 0, s, a);
+      else if (nt) hipLaunchKernelGGL((sell_step<T, MODE, true, true, 4>), g, b, 0, s, a);
+      else if (wide) hipLaunchKernelGGL((sell_step<T, MODE, false, true, 8>), g, b, 0, s, a);
+      else hipLaunchKernelGGL((sell_step<T, MODE, false, true, 4>), g, b, 0, s, a);
+    } else {
+      if (nt && wide) hipLaunchKernelGGL((sell_step<T, MODE, true, false, 8>), g, b, 0, s, a);
+      else if (nt) hipLaunchKernelGGL((sell_step<T, MODE, true, false, 4>), g, b, 0, s, a);
+      else if (wide) hipLaunchKernelGGL((sell_step<T, MODE, false, false, 8>), g, b, 0, s, a);
+      else hipLaunchKernelGGL((sell_step<T, MODE, false, false, 4>), g, b, 0, s, a);
+    }
+  } else if (m.bs == 1) {
+    if (nt) hipLaunchKernelGGL((csr_step<T, MODE, true>), dim3(grid), dim3(kWG), 0, s, a);
+    else hipLaunchKernelGGL((csr_step<T, MODE, false>), dim3(grid), dim3(kWG), 0, s, a);
+  } else {
+    if (nt) hipLaunchKernelGGL((bsr3_step<T, MODE, true>), dim3(grid), dim3(kWG), 0, s, a);
+    else hipLaunchKernelGGL((bsr3_step<T, MODE, false>), dim3(grid), dim3(kWG), 0, s, a);
+  }
   return hipGetLastError();
+}
+
+// Infinity Cache (MALL) residency plan for one solve.  Every iteration
+// streams A, G^T and G once; the MI355X's 256 MB MALL can hold one operator
+// across iterations if the others do not allocate in it.  Keep A resident
+// when its streams (values, columns, row pointers) fit the budget, else keep
+// nothing resident; the remaining operators are streamed non-temporally.
+// When everything fits, nothing is streamed non-temporally.
+struct MallPlan {
+  bool nt_a, nt_g;
+};
+size_t matrix_bytes(const sla_mat& m) {
+  const size_t es = m.dtype == SLA_F64 ? 8 : 4;
+  return (size_t)m.nnz() * es + (size_t)m.nnzb * 4 + (size_t)(m.nbr + 1) * 4;
+}
+size_t mall_budget() {
+  static size_t b = [] {
+    const char* e = getenv("SLA_MALL_BUDGET_MB");
+    const long v = e ? atol(e) : 208;
+    return (size_t)std::max(0L, v) << 20;
+  }();
+  return b;
+}
+MallPlan mall_plan(const sla_mat& A, const sla_mat& G) {
+  const size_t a = matrix_bytes(A), g = matrix_bytes(G);
+  const size_t vecs = 8 * (size_t)A.n() * (A.dtype == SLA_F64 ? 8 : 4);
+  const size_t budget = mall_budget();
+  const char* pol = getenv("SLA_MALL_POLICY");
+  if (pol) {
+    if (!strcmp(pol, "none")) return {true, true};
+    if (!strcmp(pol, "all")) return {false, false};
+    if (!strcmp(pol, "A")) return {false, true};
+    if (!strcmp(pol, "G")) return {true, false};
+  }
+  if (a + 2 * g + vecs <= budget) return {false, false};
+  if (a <= budget) return {false, true};
+  return {true, true};
 }
 
 // Long-row scratch of a handle orientation lives in the handle (owned[]);
@@ -664,14 +1040,13 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
   T *q = (T*)w.vec[4], *t = (T*)w.vec[5], *z = (T*)w.vec[6];
   const LongScratch lsA = long_scratch(A, false), lsG = long_scratch(G, false),
                     lsT = long_scratch(G, true);
-  const int ntA = A.bs == 1 ? A.fwd.ntiles : (int)((A.nbr + kBsrTileRows - 1) / kBsrTileRows);
-  const int ntG = G.bs == 1 ? G.fwd.ntiles : ntA;
-  const int ntT = G.bs == 1 ? G.tr.ntiles : ntA;
+  const int ntA = view_tiles(A, A.fwd), ntG = view_tiles(G, G.fwd), ntT = view_tiles(G, G.tr);
   const int grid = step_grid(std::max(ntA, std::max(ntG, ntT)));
   const int npA = grid + A.fwd.nlong_rows, npG = grid + G.fwd.nlong_rows,
             npT = grid + G.tr.nlong_rows;
 
   SLA_HIP(hipMemsetAsync(w.st, 0, sizeof(SolverState), s));
+  const MallPlan plan = mall_plan(A, G);
 
   StepArgs<T> aA{}, aT{}, aG{};
   fill_matrix(aA, A, A.fwd, lsA.part, lsA.cnt);
@@ -713,12 +1088,12 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
   aT.in0 = b;
   aT.own = R[0];
   hipEvent_t e0 = rec.begin(1);
-  SLA_HIP((launch_step<T, M_GT0>(G, aT, grid, s)));
+  SLA_HIP((launch_step<T, M_GT0>(G, aT, grid, s, plan.nt_g)));
   rec.end(e0, 1, 0);
   aG.k = 0;
   aG.rv = R[0];
   e0 = rec.begin(2);
-  SLA_HIP((launch_step<T, M_G0>(G, aG, grid, s)));
+  SLA_HIP((launch_step<T, M_G0>(G, aG, grid, s, plan.nt_g)));
   rec.end(e0, 2, 0);
 
   std::unique_lock<std::mutex> lk(g_poll_mu);
@@ -741,19 +1116,19 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
         aA.in1 = P[(kk - 1) & 1];
         aA.own = P[kk & 1];
         hipEvent_t ea = rec.begin(0);
-        if (kk == 1) SLA_HIP((launch_step<T, M_A1>(A, aA, grid, s)));
-        else SLA_HIP((launch_step<T, M_A>(A, aA, grid, s)));
+        if (kk == 1) SLA_HIP((launch_step<T, M_A1>(A, aA, grid, s, plan.nt_a)));
+        else SLA_HIP((launch_step<T, M_A>(A, aA, grid, s, plan.nt_a)));
         rec.end(ea, 0, kk);
         aT.k = kk;
         aT.in0 = R[(kk - 1) & 1];
         aT.own = R[kk & 1];
         hipEvent_t et = rec.begin(1);
-        SLA_HIP((launch_step<T, M_GT>(G, aT, grid, s)));
+        SLA_HIP((launch_step<T, M_GT>(G, aT, grid, s, plan.nt_g)));
         rec.end(et, 1, kk);
         aG.k = kk;
         aG.rv = R[kk & 1];
         hipEvent_t eg = rec.begin(2);
-        SLA_HIP((launch_step<T, M_G>(G, aG, grid, s)));
+        SLA_HIP((launch_step<T, M_G>(G, aG, grid, s, plan.nt_g)));
         rec.end(eg, 2, kk);
       }
       const int slot = next_slot;
@@ -840,18 +1215,19 @@ sla_status spmv(const sla_mat& A, bool transpose, const void* x, void* y, hipStr
     SLA_HIP(hipEventRecord(ea, s));
   }
   const LongScratch ls = long_scratch(A, transpose);
+  const bool nt = matrix_bytes(A) > mall_budget();
   if (A.dtype == SLA_F64) {
     StepArgs<double> a{};
     fill_matrix(a, A, v, ls.part, ls.cnt);
     a.in0 = (const double*)x;
     a.y = (double*)y;
-    SLA_HIP((launch_step<double, M_PLAIN>(A, a, step_grid(a.ntiles), s)));
+    SLA_HIP((launch_step<double, M_PLAIN>(A, a, step_grid(a.ntiles), s, nt)));
   } else {
     StepArgs<float> a{};
     fill_matrix(a, A, v, ls.part, ls.cnt);
     a.in0 = (const float*)x;
     a.y = (float*)y;
-    SLA_HIP((launch_step<float, M_PLAIN>(A, a, step_grid(a.ntiles), s)));
+    SLA_HIP((launch_step<float, M_PLAIN>(A, a, step_grid(a.ntiles), s, nt)));
   }
   if (prof) {
     SLA_HIP(hipEventRecord(eb, s));
@@ -877,6 +1253,7 @@ sla_status precond_apply(const sla_mat& G, double eps, const void* r, void* z, v
   sla_status st = spmv(G, true, r, t, s);
   if (st != SLA_OK) return st;
   const LongScratch ls = long_scratch(G, false);
+  const bool nt = matrix_bytes(G) > mall_budget();
   if (G.dtype == SLA_F64) {
     StepArgs<double> a{};
     fill_matrix(a, G, G.fwd, ls.part, ls.cnt);
@@ -884,7 +1261,7 @@ sla_status precond_apply(const sla_mat& G, double eps, const void* r, void* z, v
     a.rv = (const double*)r;
     a.y = (double*)z;
     a.eps = eps;
-    SLA_HIP((launch_step<double, M_GZ>(G, a, step_grid(a.ntiles), s)));
+    SLA_HIP((launch_step<double, M_GZ>(G, a, step_grid(a.ntiles), s, nt)));
   } else {
     StepArgs<float> a{};
     fill_matrix(a, G, G.fwd, ls.part, ls.cnt);
@@ -892,7 +1269,7 @@ sla_status precond_apply(const sla_mat& G, double eps, const void* r, void* z, v
     a.rv = (const float*)r;
     a.y = (float*)z;
     a.eps = eps;
-    SLA_HIP((launch_step<float, M_GZ>(G, a, step_grid(a.ntiles), s)));
+    SLA_HIP((launch_step<float, M_GZ>(G, a, step_grid(a.ntiles), s, nt)));
   }
   return SLA_OK;
 }
@@ -949,7 +1326,8 @@ void prof_reset() {
 
 int occupancy_grid(int cus) {
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, csr_step<double, M_A>, kWG, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, csr_step<double, M_A, true>, kWG,
+                                                   0) !=
           hipSuccess ||
       per_cu <= 0)
     per_cu = 4;
