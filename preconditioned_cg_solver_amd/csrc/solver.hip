@@ -233,36 +233,49 @@ __device__ __forceinline__ Own<T> own_load(const StepArgs<T>& a, int i) {
   return o;
 }
 
+#ifndef SLA_NTS_MASK
+#define SLA_NTS_MASK 3
+#endif
+// Output stores.  Outputs with no reuse before the next iteration (x and p
+// of the A step: bits 1 and 2 of SLA_NTS_MASK; bit 4 would add q) are stored
+// non-temporally, so they do not sit dirty in L2 and need no write-back at
+// the kernel boundary; outputs the next kernel consumes keep normal stores.
+template <int BIT, typename U>
+__device__ __forceinline__ void st_out(U* p, U v) {
+  if constexpr ((SLA_NTS_MASK & BIT) != 0) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
 // Row epilogue from preloaded row-owned entries (same arithmetic as epi()).
 template <typename T, int MODE>
 __device__ __forceinline__ double epi_own(const StepArgs<T>& a, int i, T acc, const Coef<T>& cf,
                                           const Own<T>& o) {
   if constexpr (MODE == M_PLAIN) {
-    a.y[i] = acc;
+    st_out<0>(a.y + i, acc);
     return 0.0;
   } else if constexpr (MODE == M_A1) {
-    a.own[i] = o.a;
-    a.y[i] = acc;
+    st_out<2>(a.own + i, o.a);
+    st_out<4>(a.y + i, acc);
     return (double)o.a * (double)acc;
   } else if constexpr (MODE == M_A) {
     const T pn = fma(cf.c, o.a, o.b);
-    a.own[i] = pn;
-    a.xv[i] = fma(cf.c2, o.a, o.c);
-    a.y[i] = acc;
+    st_out<2>(a.own + i, pn);
+    st_out<1>(a.xv + i, fma(cf.c2, o.a, o.c));
+    st_out<4>(a.y + i, acc);
     return (double)pn * (double)acc;
   } else if constexpr (MODE == M_GT0) {
-    a.own[i] = o.a;
-    a.xv[i] = T(0);
-    a.y[i] = acc;
+    st_out<0>(a.own + i, o.a);
+    st_out<1>(a.xv + i, T(0));
+    st_out<0>(a.y + i, acc);
     return (double)o.a * (double)o.a;
   } else if constexpr (MODE == M_GT) {
     const T rn = fma(cf.c, o.a, o.b);
-    a.own[i] = rn;
-    a.y[i] = acc;
+    st_out<0>(a.own + i, rn);
+    st_out<0>(a.y + i, acc);
     return (double)rn * (double)rn;
   } else {
     const T zv = fma(T(a.eps), o.a, acc);
-    a.y[i] = zv;
+    st_out<0>(a.y + i, zv);
     return (double)o.a * (double)zv;
   }
 }
@@ -913,6 +926,15 @@ std::mutex g_prof_mu;
 std::atomic<int> g_prof_mask{0};
 ProfClass g_prof[4];
 
+// Events used only for timing: no system-scope fence when recorded, so the
+// bracketed kernel is not slowed by cache write-back and invalidation.
+hipEvent_t timing_event() {
+  hipEvent_t e = nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) == hipSuccess) return e;
+  if (hipEventCreate(&e) == hipSuccess) return e;
+  return nullptr;
+}
+
 struct EventPair {
   hipEvent_t a, b;
   int cls;
@@ -927,8 +949,8 @@ struct Recorder {
   size_t used = 0;
   hipEvent_t get() {
     if (used == pool.size()) {
-      hipEvent_t e;
-      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      hipEvent_t e = timing_event();
+      if (!e) return nullptr;
       pool.push_back(e);
     }
     return pool[used++];
@@ -1210,8 +1232,12 @@ sla_status spmv(const sla_mat& A, bool transpose, const void* x, void* y, hipStr
   hipEvent_t ea = nullptr, eb = nullptr;
   const bool prof = (g_prof_mask.load() & (1 << 3)) != 0;
   if (prof) {
-    SLA_HIP(hipEventCreate(&ea));
-    SLA_HIP(hipEventCreate(&eb));
+    ea = timing_event();
+    eb = timing_event();
+    if (!ea || !eb) {
+      set_error("hipEventCreate failed");
+      return SLA_ERR_HIP;
+    }
     SLA_HIP(hipEventRecord(ea, s));
   }
   const LongScratch ls = long_scratch(A, transpose);
