@@ -49,6 +49,25 @@ def algorithmic_bytes(n, nnz_a, nnz_g, sv, si=4):
             "iteration": a_step + gt_step + g_step}
 
 
+def sell_slots(M):
+    """Slots of the SELL-64 copy the library builds for short-row CSR (each
+    64-row slice padded to its longest row)."""
+    import numpy as np
+    lens = np.diff(M.row_ptr.astype(np.int64))
+    ns = (M.n + 63) // 64
+    w = np.zeros(ns, np.int64)
+    np.maximum.at(w, np.arange(M.n) // 64, lens)
+    return int(w.sum() * 64), ns
+
+
+def moved_bytes_a_step(A, n, sv=8, col_bytes=2):
+    """Bytes the fused A step physically streams with the SELL-64 layout and
+    16-bit column offsets: values + column offsets + slice offsets, z, p_old
+    and x read, x, p_new and q written (gathers counted once)."""
+    slots, ns = sell_slots(A)
+    return slots * (sv + col_bytes) + 4 * (ns + 1) + 6 * sv * n
+
+
 def traffic_if_current():
     """HBM bytes per A-step launch from the committed rocprofv3 counter runs,
     if they were taken on the current kernel source; else None."""
@@ -82,6 +101,9 @@ def main():
     ap.add_argument("--cpu-iters", type=int, default=300)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--spmv-reps", type=int, default=50)
+    ap.add_argument("--counters-workload", action="store_true",
+                    help="short run for rocprofv3 --pmc: a 256 MiB copy (calibration) and "
+                         "20 forward + 20 adjoint PCG iterations on the same input")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this solver runs on a single MI355X "
@@ -112,6 +134,22 @@ def main():
     grad_b = torch.empty_like(b)
     grad_vals = torch.empty(nnz_a, dtype=torch.float64, device=dev)
     work = None
+
+    if args.counters_workload:
+        src = torch.ones(32 * 1024 * 1024, dtype=torch.float64, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)                       # 256 MiB read + 256 MiB written
+        torch.cuda.synchronize()
+        A = B.sla_csr_create(a_rp, a_ci, a_v)
+        G = B.sla_csr_create(g_rp, g_ci, g_v, build_transpose=True)
+        work = B.workspace(A)
+        B.sla_pcg_solve(A, G, p.eps, b, x=x, rtol=p.rtol, maxit=20, work=work)
+        B.sla_pcg_adjoint(A, G, p.eps, x, w, rtol=p.rtol, maxit=20, grad_b=grad_b,
+                          grad_vals=grad_vals, work=work)
+        torch.cuda.synchronize()
+        log("counters workload done")
+        return
 
     def step():
         nonlocal work
@@ -176,11 +214,26 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     spmv_s = e0.elapsed_time(e1) / 1e3 / args.spmv_reps
+    # cold: a 1 GiB read-only pass before each call evicts A from L2 and the
+    # 256 MB Infinity Cache without leaving dirty lines behind
+    flush = torch.ones(128 * 1024 * 1024, dtype=torch.float64, device=dev)
+    cold = []
+    for _ in range(10):
+        flush.sum()
+        e0.record()
+        B.sla_spmv(A, b, y)
+        e1.record()
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1) / 1e3)
+    del flush
+    spmv_cold_s = statistics.median(cold)
 
     achieved = ab["a_step"] / a_avg_s / 1e9
     traffic = traffic_if_current()
+    moved = moved_bytes_a_step(p.A, n)
     iter_gbs = ab["iteration"] * fi.iterations / tts / 1e9
     spmv_gbs = ab["spmv_A"] / spmv_s / 1e9
+    spmv_cold_gbs = ab["spmv_A"] / spmv_cold_s / 1e9
     result = {
         "metric": "PCG iters/sec + SpMV HBM GB/s (% of peak), 3D Poisson 128^3 fp64, 1 GPU",
         "value": total_iters / elapsed,
@@ -200,17 +253,26 @@ def main():
                    "n": n, "nnz_A": nnz_a, "nnz_G": nnz_g,
                    "iterations_forward": fi.iterations, "iterations_adjoint": ai.iterations,
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "csr_step<double, A> (q = A p, fused p/x "
-                                               "updates, p.q)",
+        "roofline": {"bound": "hbm",
+                     "kernel": "sell_step<double, A step> (q = A p with p = z + beta p_old "
+                               "formed on the fly, x += alpha_prev p_old, p.q partials)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": ab["a_step"],
+                     "moved_bytes_per_launch": moved,
+                     "moved_GBps": moved / a_avg_s / 1e9,
                      "avg_launch_us": a_avg_s * 1e6, "launches": a_launches},
         "iteration": {"bytes": ab["iteration"], "GBps": iter_gbs, "frac": iter_gbs / HBM_PEAK_GBS,
                       "us_per_iteration": tts / fi.iterations * 1e6,
                       "time_to_solution_ms": tts * 1e3},
-        "spmv": {"bytes": ab["spmv_A"], "GBps": spmv_gbs, "frac": spmv_gbs / HBM_PEAK_GBS,
-                 "us": spmv_s * 1e6, "note": "warm, back-to-back sla_spmv calls"},
+        "spmv": {"bytes": ab["spmv_A"],
+                 "cold": {"GBps": spmv_cold_gbs, "frac": spmv_cold_gbs / HBM_PEAK_GBS,
+                          "us": spmv_cold_s * 1e6},
+                 "warm": {"GBps": spmv_gbs, "frac": spmv_gbs / HBM_PEAK_GBS,
+                          "us": spmv_s * 1e6},
+                 "note": "algorithmic CSR bytes; cold = median of 10 calls after a 1 GiB "
+                         "read-only cache flush, warm = back-to-back calls with A (183 MB) "
+                         "held in the 256 MB Infinity Cache"},
         "setup_ms": statistics.median(setup) * 1e3,
     }
     if not args.no_cpu_baseline:
