@@ -116,6 +116,8 @@ sla_status create_common(sla_mat_t* out, int64_t nbr, int64_t nnzb, int32_t bs, 
   if (st == SLA_OK && bs == 1) st = build_tiling(rp, nbr, m->fwd, &m->owned[O_TILES_F], s);
   if (st == SLA_OK && bs == 1 && sell_enabled())
     st = build_sell(m->fwd, nbr, nnzb, dtype, &m->owned[O_SELL_F], s);
+  if (st == SLA_OK && bs == 3 && sell_enabled())
+    st = build_bsell(m->fwd, nbr, nnzb, dtype, &m->owned[O_SELL_F], s);
   if (st == SLA_OK) st = alloc_long_scratch(m, m->fwd, O_LPART_F, O_LCNT_F, s);
   if (st == SLA_OK && (flags & SLA_BUILD_TRANSPOSE)) {
     int32_t *trp = nullptr, *tci = nullptr;
@@ -132,6 +134,8 @@ sla_status create_common(sla_mat_t* out, int64_t nbr, int64_t nnzb, int32_t bs, 
       if (bs == 1) st = build_tiling(trp, nbr, m->tr, &m->owned[O_TILES_T], s);
       if (st == SLA_OK && bs == 1 && sell_enabled())
         st = build_sell(m->tr, nbr, nnzb, dtype, &m->owned[O_SELL_T], s);
+      if (st == SLA_OK && bs == 3 && sell_enabled())
+        st = build_bsell(m->tr, nbr, nnzb, dtype, &m->owned[O_SELL_T], s);
       if (st == SLA_OK) st = alloc_long_scratch(m, m->tr, O_LPART_T, O_LCNT_T, s);
     }
   }

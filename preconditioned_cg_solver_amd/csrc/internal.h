@@ -31,6 +31,11 @@ constexpr int kSellMaxPadPct = 25;
 constexpr int kPad16 = -32768;
 // Padding slots allocated past the last slice (covers the widest batch).
 constexpr int kSellTail = 16 * kSlice;
+// Sliced ELLPACK for 3x3 BSR: kBSlice block rows per wavefront slice (lane l
+// owns scalar row 3 (kBSlice s + l / 3) + l % 3; lane 63 idles).
+constexpr int kBSlice = 21;
+constexpr int kBSellMaxWidth = 64;
+constexpr int kBSellTail = 16 * kBSlice;
 // BSR(3x3) engine: kBsrLanes lanes per block row, kWG / kBsrLanes block rows
 // per tile.
 constexpr int kBsrLanes = 32;
@@ -92,6 +97,9 @@ struct MatView {
   // SELL-64 copy (owned), built once when the rows qualify: slice s holds
   // rows [64 s, 64 s + 64); slot j of its row 64 s + l sits at
   // soff[s] + 64 j + l; padding slots have column -1 and value 0.
+  // For 3x3 BSR the same fields hold the block form: slice s holds block
+  // rows [21 s, 21 s + 21); block slot j of local block row i sits at
+  // soff[s] + 21 j + i (9 values each, row-major), columns are block columns.
   const void* sv = nullptr;
   const int32_t* sc = nullptr;   // absolute columns, or
   const int16_t* sd = nullptr;   // column - row offsets (preferred when they fit)
@@ -146,6 +154,8 @@ sla_status build_transpose(const sla_mat& m, int32_t** t_rp, int32_t** t_ci, voi
 sla_status validate_structure(const sla_mat& m, hipStream_t s);
 sla_status build_sell(MatView& view, int64_t n, int64_t nnz, int32_t dtype, void** owned3,
                       hipStream_t s);
+sla_status build_bsell(MatView& view, int64_t nbr, int64_t nnzb, int32_t dtype, void** owned3,
+                       hipStream_t s);
 
 // Solver (solver.hip).
 size_t workspace_bytes(const sla_mat& A);

@@ -390,6 +390,41 @@ __global__ void sell_fill(const int* __restrict__ rp, const int* __restrict__ ci
   }
 }
 
+// ---- sliced ELLPACK for 3x3 BSR ----
+
+__global__ void bsell_widths(const int* __restrict__ rp, int nbr, int nslices,
+                             int* __restrict__ slots, int* __restrict__ maxw) {
+  const int sl = blockIdx.x * blockDim.x + threadIdx.x;
+  if (sl >= nslices) return;
+  int w = 0;
+  const int r1 = min(nbr, (sl + 1) * kBSlice);
+  for (int i = sl * kBSlice; i < r1; ++i) w = max(w, rp[i + 1] - rp[i]);
+  slots[sl] = w * kBSlice;
+  atomicMax(maxw, w);
+}
+
+template <typename T>
+__global__ void bsell_fill(const int* __restrict__ rp, const int* __restrict__ ci,
+                           const T* __restrict__ v, int nbr, int nslices,
+                           const int* __restrict__ soff, T* __restrict__ sv,
+                           int* __restrict__ sc) {
+  const int I = blockIdx.x * blockDim.x + threadIdx.x;  // block row (padded)
+  if (I >= nslices * kBSlice) return;
+  const int sl = I / kBSlice, li = I % kBSlice;
+  const int off = soff[sl], w = (soff[sl + 1] - off) / kBSlice;
+  const int kb = I < nbr ? rp[I] : 0, len = I < nbr ? rp[I + 1] - kb : 0;
+  for (int j = 0; j < w; ++j) {
+    const size_t dst = (size_t)off + (size_t)j * kBSlice + li;
+    if (j < len) {
+      for (int e = 0; e < 9; ++e) sv[dst * 9 + e] = v[(size_t)(kb + j) * 9 + e];
+      sc[dst] = ci[kb + j];
+    } else {
+      for (int e = 0; e < 9; ++e) sv[dst * 9 + e] = T(0);
+      sc[dst] = -1;
+    }
+  }
+}
+
 int grid_for(int64_t work, int per_block = kWG) {
   const int64_t g = (work + per_block - 1) / per_block;
   return (int)std::max<int64_t>(1, std::min<int64_t>(g, 65536));
@@ -596,6 +631,62 @@ sla_status build_sell(MatView& view, int64_t n, int64_t nnz, int32_t dtype, void
   view.sv = sv;
   view.sc = rel16 ? nullptr : (const int32_t*)sc;
   view.sd = rel16 ? (const int16_t*)sc : nullptr;
+  view.soff = soff;
+  view.nslices = nslices;
+  view.sell_w = h[0];
+  view.sell = true;
+  return SLA_OK;
+}
+
+sla_status build_bsell(MatView& view, int64_t nbr, int64_t nnzb, int32_t dtype, void** owned3,
+                       hipStream_t s) {
+  view.sell = false;
+  if (nbr == 0 || nnzb == 0) return SLA_OK;
+  const int nslices = (int)((nbr + kBSlice - 1) / kBSlice);
+  int* buf = nullptr;
+  SLA_HIP(hipMallocAsync((void**)&buf, sizeof(int) * ((size_t)nslices + 2), s));
+  int* slots = buf;
+  int* maxw = buf + nslices + 1;
+  SLA_HIP(hipMemsetAsync(buf, 0, sizeof(int) * ((size_t)nslices + 2), s));
+  hipLaunchKernelGGL(bsell_widths, dim3((nslices + 255) / 256), dim3(256), 0, s, view.rp,
+                     (int)nbr, nslices, slots, maxw);
+  SLA_HIP(hipGetLastError());
+  int* soff = nullptr;
+  SLA_HIP(hipMalloc((void**)&soff, sizeof(int) * ((size_t)nslices + 1)));
+  owned3[2] = soff;
+  sla_status st = exclusive_scan(slots, soff, nslices + 1, s);
+  if (st != SLA_OK) return st;
+  int h[2] = {0, 0};
+  SLA_HIP(hipMemcpyAsync(&h[0], maxw, sizeof(int), hipMemcpyDeviceToHost, s));
+  SLA_HIP(hipMemcpyAsync(&h[1], soff + nslices, sizeof(int), hipMemcpyDeviceToHost, s));
+  SLA_HIP(hipFreeAsync(buf, s));
+  SLA_HIP(hipStreamSynchronize(s));
+  const int64_t total = h[1];
+  if (h[0] > kBSellMaxWidth || total * 100 > nnzb * (100 + kSellMaxPadPct)) return SLA_OK;
+  if ((total + kBSellTail) * 9 >= (int64_t)INT32_MAX) return SLA_OK;
+  const size_t es = dtype == SLA_F64 ? 8 : 4;
+  const size_t alloc = (size_t)total + kBSellTail;
+  void* sv = nullptr;
+  int* sc = nullptr;
+  SLA_HIP(hipMalloc(&sv, es * 9 * alloc));
+  owned3[0] = sv;
+  SLA_HIP(hipMalloc((void**)&sc, sizeof(int) * alloc));
+  owned3[1] = sc;
+  SLA_HIP(hipMemsetAsync((char*)sv + es * 9 * (size_t)total, 0, es * 9 * kBSellTail, s));
+  SLA_HIP(hipMemsetAsync(sc + total, 0xff, sizeof(int) * kBSellTail, s));
+  const int rows = nslices * kBSlice;
+  if (dtype == SLA_F64)
+    hipLaunchKernelGGL(bsell_fill<double>, dim3((rows + 255) / 256), dim3(256), 0, s, view.rp,
+                       view.ci, (const double*)view.v, (int)nbr, nslices, (const int*)soff,
+                       (double*)sv, sc);
+  else
+    hipLaunchKernelGGL(bsell_fill<float>, dim3((rows + 255) / 256), dim3(256), 0, s, view.rp,
+                       view.ci, (const float*)view.v, (int)nbr, nslices, (const int*)soff,
+                       (float*)sv, sc);
+  SLA_HIP(hipGetLastError());
+  view.sv = sv;
+  view.sc = sc;
+  view.sd = nullptr;
   view.soff = soff;
   view.nslices = nslices;
   view.sell_w = h[0];

@@ -49,7 +49,9 @@ enum Mode {
   M_GT = 4,     // G^T step of iteration k >= 1
   M_G0 = 5,     // G step of the start-up (checks ||b||)
   M_G = 6,      // G step of iteration k >= 1 (checks convergence)
-  M_GZ = 7      // z = G t + eps r without solver state (precondition apply)
+  M_GZ = 7,     // z = G t + eps r without solver state (precondition apply)
+  M_AU = 8,     // unfused A product: q = A p on a stored p, p.q partials
+  M_GTU = 9     // unfused G^T product: t = G^T r on a stored r
 };
 
 template <typename T>
@@ -60,6 +62,7 @@ struct StepArgs {
   const Tile* tiles;
   int ntiles;
   int nbr;
+  int n;                 // scalar rows (vector length)
   const T* sv;           // SELL-64 copy (null: use the tiles)
   const int32_t* sc;     // absolute columns (-1 = padding), or
   const int16_t* sd;     // column - row offsets (kPad16 = padding)
@@ -141,6 +144,7 @@ __device__ __forceinline__ bool prologue(const StepArgs<T>& a, Coef<T>& cf, doub
                                                       __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (*s_flag) return false;
+    if constexpr (MODE == M_AU || MODE == M_GTU) return true;
     const bool lead = blockIdx.x == 0 && threadIdx.x == 0;
     const int k = a.k;
     if constexpr (MODE == M_A1 || MODE == M_A) {
@@ -218,7 +222,7 @@ struct Own {
 template <typename T, int MODE>
 __device__ __forceinline__ Own<T> own_load(const StepArgs<T>& a, int i) {
   Own<T> o{T(0), T(0), T(0)};
-  if constexpr (MODE == M_A1 || MODE == M_GT0) {
+  if constexpr (MODE == M_A1 || MODE == M_GT0 || MODE == M_AU) {
     o.a = a.in0[i];
   } else if constexpr (MODE == M_A) {
     o.a = a.in1[i];
@@ -250,9 +254,12 @@ __device__ __forceinline__ void st_out(U* p, U v) {
 template <typename T, int MODE>
 __device__ __forceinline__ double epi_own(const StepArgs<T>& a, int i, T acc, const Coef<T>& cf,
                                           const Own<T>& o) {
-  if constexpr (MODE == M_PLAIN) {
+  if constexpr (MODE == M_PLAIN || MODE == M_GTU) {
     st_out<0>(a.y + i, acc);
     return 0.0;
+  } else if constexpr (MODE == M_AU) {
+    st_out<0>(a.y + i, acc);
+    return (double)o.a * (double)acc;
   } else if constexpr (MODE == M_A1) {
     st_out<2>(a.own + i, o.a);
     st_out<4>(a.y + i, acc);
@@ -283,9 +290,12 @@ __device__ __forceinline__ double epi_own(const StepArgs<T>& a, int i, T acc, co
 // Row epilogue: stores and the row's contribution to the fused dot product.
 template <typename T, int MODE>
 __device__ __forceinline__ double epi(const StepArgs<T>& a, int i, T acc, const Coef<T>& cf) {
-  if constexpr (MODE == M_PLAIN) {
+  if constexpr (MODE == M_PLAIN || MODE == M_GTU) {
     a.y[i] = acc;
     return 0.0;
+  } else if constexpr (MODE == M_AU) {
+    a.y[i] = acc;
+    return (double)a.in0[i] * (double)acc;
   } else if constexpr (MODE == M_A1) {
     const T pn = a.in0[i];
     a.own[i] = pn;
@@ -526,7 +536,7 @@ __global__ __launch_bounds__(kWG) void csr_step(StepArgs<T> a) {
       }
     }
   }
-  if constexpr (MODE != M_PLAIN && MODE != M_GZ) {
+  if constexpr (MODE != M_PLAIN && MODE != M_GZ && MODE != M_GTU) {
     const double s = block_sum(dot, s_red);
     if (tid == 0) a.pout[blockIdx.x] = s;
   }
@@ -641,7 +651,105 @@ __global__ __launch_bounds__(kWG) void sell_step(StepArgs<T> a) {
     }
     if (live) dot += epi_own<T, MODE>(a, row, acc, cf, o);
   }
-  if constexpr (MODE != M_PLAIN && MODE != M_GZ) {
+  if constexpr (MODE != M_PLAIN && MODE != M_GZ && MODE != M_GTU) {
+    const double s = block_sum(dot, s_red);
+    if (threadIdx.x == 0) a.pout[blockIdx.x] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Sliced-ELL engine for 3x3 BSR: one wavefront per slice of 21 block rows.
+// Lane l owns scalar row 3 (21 s + l / 3) + l % 3 and, for every block slot,
+// reads that row's three values of the block (the 63 live lanes read 63
+// consecutive 24-byte row thirds) and the three gathered entries of the
+// block column; no cross-lane reduction, accumulation in (block, column)
+// order.  The next slice's first batch is prefetched across slices.
+// ---------------------------------------------------------------------------
+
+template <typename T, int MODE, bool NT, int U>
+__global__ __launch_bounds__(kWG) void bsell_step(StepArgs<T> a) {
+  __shared__ double s_red[kWaves];
+  __shared__ int s_flag;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int li = min(lane / 3, kBSlice - 1), r = lane - 3 * (lane / 3);
+  const bool lane_live = lane < 3 * kBSlice;
+  int t0, t1, step;
+  tile_range(a.ntiles, t0, t1, step);
+  T hv[U][3];
+  int hc[U];
+  int hoff = 0, hw = 0;
+  auto load_head = [&](int sl) {
+    hoff = 0;
+    hw = 0;
+    if (sl < a.nslices) {
+      hoff = a.soff[sl];
+      hw = (a.soff[sl + 1] - hoff) / kBSlice;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int blk = hoff + u * kBSlice + li;
+      hc[u] = ld_stream<NT>(a.sc + blk);
+#pragma unroll
+      for (int c = 0; c < 3; ++c) hv[u][c] = ld_stream<NT>(a.sv + (size_t)blk * 9 + 3 * r + c);
+    }
+  };
+  if (t0 < t1) load_head(t0 * kWaves + wv);
+  Coef<T> cf;
+  if (!prologue<T, MODE>(a, cf, s_red, &s_flag)) return;
+  double dot = 0.0;
+  for (int t = t0; t < t1; t += step) {
+    const int sl = t * kWaves + wv;
+    const int off = hoff, w = hw;
+    T cv[U][3];
+    int cc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      cc[u] = hc[u];
+#pragma unroll
+      for (int c = 0; c < 3; ++c) cv[u][c] = hv[u][c];
+    }
+    if (t + step < t1) load_head((t + step) * kWaves + wv);
+    if (sl >= a.nslices) continue;
+    const int brow = sl * kBSlice + li;
+    const bool live = lane_live && brow < a.nbr;
+    const int row = 3 * brow + r;
+    T acc = T(0);
+    auto consume = [&](T (&v)[U][3], int (&col)[U], int j0) {
+      T g[U][3];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool ok = j0 + u < w && col[u] >= 0;
+        const int base = ok ? 3 * col[u] : 0;
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+          const T x = gat<T, MODE>(a, base + c, cf);
+          g[u][c] = ok ? x : T(0);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool ok = j0 + u < w && col[u] >= 0;
+#pragma unroll
+        for (int c = 0; c < 3; ++c) acc = fma(ok ? v[u][c] : T(0), g[u][c], acc);
+      }
+    };
+    const Own<T> o = own_load<T, MODE>(a, live ? row : 0);
+    consume(cv, cc, 0);
+    for (int j = U; j < w; j += U) {
+      T bv[U][3];
+      int bc[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int blk = off + (j + u) * kBSlice + li;
+        bc[u] = ld_stream<NT>(a.sc + blk);
+#pragma unroll
+        for (int c = 0; c < 3; ++c) bv[u][c] = ld_stream<NT>(a.sv + (size_t)blk * 9 + 3 * r + c);
+      }
+      consume(bv, bc, j);
+    }
+    if (live) dot += epi_own<T, MODE>(a, row, acc, cf, o);
+  }
+  if constexpr (MODE != M_PLAIN && MODE != M_GZ && MODE != M_GTU) {
     const double s = block_sum(dot, s_red);
     if (threadIdx.x == 0) a.pout[blockIdx.x] = s;
   }
@@ -704,10 +812,52 @@ __global__ __launch_bounds__(kWG) void bsr3_step(StepArgs<T> a) {
       dot += epi<T, MODE>(a, 3 * I + sub, accr, cf);
     }
   }
-  if constexpr (MODE != M_PLAIN && MODE != M_GZ) {
+  if constexpr (MODE != M_PLAIN && MODE != M_GZ && MODE != M_GTU) {
     const double s = block_sum(dot, s_red);
     if (threadIdx.x == 0) a.pout[blockIdx.x] = s;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Vector passes of the unfused iteration (matrices whose gathers have no
+// locality: forming p and r on the fly would double the random gathers).
+// ---------------------------------------------------------------------------
+
+// p_{k-1} = z_{k-1} + beta_{k-1} p_{k-2} and the deferred x update; the
+// prologue is the A step's (rho, beta, alpha_{k-1}, breakdown).
+template <typename T, int MODE>
+__global__ __launch_bounds__(kWG) void vec_p_update(StepArgs<T> a) {
+  __shared__ double s_red[kWaves];
+  __shared__ int s_flag;
+  Coef<T> cf;
+  if (!prologue<T, MODE>(a, cf, s_red, &s_flag)) return;
+  for (int i = blockIdx.x * kWG + threadIdx.x; i < a.n; i += gridDim.x * kWG) {
+    if constexpr (MODE == M_A1) {
+      st_out<2>(a.own + i, a.in0[i]);
+    } else {
+      const T po = a.in1[i];
+      st_out<2>(a.own + i, fma(cf.c, po, a.in0[i]));
+      st_out<1>(a.xv + i, fma(cf.c2, po, a.xv[i]));
+    }
+  }
+}
+
+// r_k = r_{k-1} - alpha_k q and ||r_k||^2 partials; the prologue is the G^T
+// step's (sigma, alpha_k, breakdown).
+template <typename T>
+__global__ __launch_bounds__(kWG) void vec_r_update(StepArgs<T> a) {
+  __shared__ double s_red[kWaves];
+  __shared__ int s_flag;
+  Coef<T> cf;
+  if (!prologue<T, M_GT>(a, cf, s_red, &s_flag)) return;
+  double dot = 0.0;
+  for (int i = blockIdx.x * kWG + threadIdx.x; i < a.n; i += gridDim.x * kWG) {
+    const T rn = fma(cf.c, a.in1[i], a.in0[i]);
+    a.own[i] = rn;
+    dot += (double)rn * (double)rn;
+  }
+  const double s = block_sum(dot, s_red);
+  if (threadIdx.x == 0) a.pout[blockIdx.x] = s;
 }
 
 // ---------------------------------------------------------------------------
@@ -812,6 +962,7 @@ int step_grid(int ntiles) {
 // Work items of a product over one orientation: SELL slices grouped by
 // workgroup (one per wavefront), LDS tiles, or BSR block-row tiles.
 int view_tiles(const sla_mat& m, const MatView& v) {
+  if (m.bs != 1 && v.sell) return (v.nslices + kWaves - 1) / kWaves;
   if (m.bs != 1) return (int)((m.nbr + kBsrTileRows - 1) / kBsrTileRows);
   if (v.sell) return (v.nslices + kWaves - 1) / kWaves;
   return v.ntiles;
@@ -825,7 +976,8 @@ void fill_matrix(StepArgs<T>& a, const sla_mat& m, const MatView& v, double* lon
   a.v = (const T*)v.v;
   a.tiles = v.tiles;
   a.ntiles = view_tiles(m, v);
-  if (m.bs == 1 && v.sell) {
+  a.n = (int)m.n();
+  if (v.sell) {
     a.sv = (const T*)v.sv;
     a.sc = v.sd ? nullptr : v.sc;
     a.sd = v.sd;
@@ -859,6 +1011,9 @@ hipError_t launch_step(const sla_mat& m, const StepArgs<T>& a, int grid, hipStre
   } else if (m.bs == 1) {
     if (nt) hipLaunchKernelGGL((csr_step<T, MODE, true>), dim3(grid), dim3(kWG), 0, s, a);
     else hipLaunchKernelGGL((csr_step<T, MODE, false>), dim3(grid), dim3(kWG), 0, s, a);
+  } else if (a.sc) {
+    if (nt) hipLaunchKernelGGL((bsell_step<T, MODE, true, 4>), dim3(grid), dim3(kWG), 0, s, a);
+    else hipLaunchKernelGGL((bsell_step<T, MODE, false, 4>), dim3(grid), dim3(kWG), 0, s, a);
   } else {
     if (nt) hipLaunchKernelGGL((bsr3_step<T, MODE, true>), dim3(grid), dim3(kWG), 0, s, a);
     else hipLaunchKernelGGL((bsr3_step<T, MODE, false>), dim3(grid), dim3(kWG), 0, s, a);
@@ -1053,6 +1208,19 @@ Work carve(const sla_mat& A, void* work) {
   return w;
 }
 
+// Fused iteration (p and r formed inside the products' gathers) when A's
+// gathers have locality -- A qualified for the SELL-64 layout (short, even,
+// banded rows) or is block sparse; otherwise separate streaming passes keep
+// every product at one random gather per nonzero.  SLA_FUSION=fused|unfused
+// overrides the choice.
+bool use_fused(const sla_mat& A) {
+  if (const char* e = getenv("SLA_FUSION")) {
+    if (!strcmp(e, "fused")) return true;
+    if (!strcmp(e, "unfused")) return false;
+  }
+  return A.bs != 1 || A.fwd.sell;
+}
+
 template <typename T>
 sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, T* x, double rtol,
                     int maxit, void* work, hipStream_t s, sla_solve_info* info) {
@@ -1069,6 +1237,7 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
 
   SLA_HIP(hipMemsetAsync(w.st, 0, sizeof(SolverState), s));
   const MallPlan plan = mall_plan(A, G);
+  const bool fused = use_fused(A);
 
   StepArgs<T> aA{}, aT{}, aG{};
   fill_matrix(aA, A, A.fwd, lsA.part, lsA.cnt);
@@ -1101,6 +1270,23 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
   aG.in0 = t;
   aG.y = z;
 
+  // unfused iteration: vector passes (p/x update, r update) around
+  // single-gather products
+  StepArgs<T> aV = aA, aR = aT;
+  aV.in0 = z;
+  aV.xv = x;
+  aV.pin = w.prho;
+  aV.npin = npG;
+  aR.in1 = q;
+  aR.pin = w.psig;
+  aR.npin = npA;
+  aR.pout = w.prr;
+  if (!fused) {
+    aT.pout = nullptr;  // t = G^T r carries no reduction when unfused
+    aA.pin = nullptr;
+    aA.npin = 0;
+  }
+
   Recorder rec;
   rec.mask = g_prof_mask.load();
   rec.s = s;
@@ -1109,9 +1295,11 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
   aT.k = 0;
   aT.in0 = b;
   aT.own = R[0];
+  aT.pout = w.prr;
   hipEvent_t e0 = rec.begin(1);
   SLA_HIP((launch_step<T, M_GT0>(G, aT, grid, s, plan.nt_g)));
   rec.end(e0, 1, 0);
+  if (!fused) aT.pout = nullptr;
   aG.k = 0;
   aG.rv = R[0];
   e0 = rec.begin(2);
@@ -1134,19 +1322,47 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
     if (k <= maxit) {
       const int kend = std::min(maxit, k + B - 1);
       for (int kk = k; kk <= kend; ++kk) {
-        aA.k = kk;
-        aA.in1 = P[(kk - 1) & 1];
-        aA.own = P[kk & 1];
-        hipEvent_t ea = rec.begin(0);
-        if (kk == 1) SLA_HIP((launch_step<T, M_A1>(A, aA, grid, s, plan.nt_a)));
-        else SLA_HIP((launch_step<T, M_A>(A, aA, grid, s, plan.nt_a)));
-        rec.end(ea, 0, kk);
-        aT.k = kk;
-        aT.in0 = R[(kk - 1) & 1];
-        aT.own = R[kk & 1];
-        hipEvent_t et = rec.begin(1);
-        SLA_HIP((launch_step<T, M_GT>(G, aT, grid, s, plan.nt_g)));
-        rec.end(et, 1, kk);
+        if (fused) {
+          aA.k = kk;
+          aA.in1 = P[(kk - 1) & 1];
+          aA.own = P[kk & 1];
+          hipEvent_t ea = rec.begin(0);
+          if (kk == 1) SLA_HIP((launch_step<T, M_A1>(A, aA, grid, s, plan.nt_a)));
+          else SLA_HIP((launch_step<T, M_A>(A, aA, grid, s, plan.nt_a)));
+          rec.end(ea, 0, kk);
+          aT.k = kk;
+          aT.in0 = R[(kk - 1) & 1];
+          aT.own = R[kk & 1];
+          hipEvent_t et = rec.begin(1);
+          SLA_HIP((launch_step<T, M_GT>(G, aT, grid, s, plan.nt_g)));
+          rec.end(et, 1, kk);
+        } else {
+          // p and x update, q = A p, r update, t = G^T r: single gathers
+          aV.k = kk;
+          aV.in1 = P[(kk - 1) & 1];
+          aV.own = P[kk & 1];
+          if (kk == 1)
+            hipLaunchKernelGGL((vec_p_update<T, M_A1>), dim3(grid), dim3(kWG), 0, s, aV);
+          else
+            hipLaunchKernelGGL((vec_p_update<T, M_A>), dim3(grid), dim3(kWG), 0, s, aV);
+          SLA_HIP(hipGetLastError());
+          aA.k = kk;
+          aA.in0 = P[kk & 1];
+          hipEvent_t ea = rec.begin(0);
+          SLA_HIP((launch_step<T, M_AU>(A, aA, grid, s, plan.nt_a)));
+          rec.end(ea, 0, kk);
+          aR.k = kk;
+          aR.in0 = R[(kk - 1) & 1];
+          aR.own = R[kk & 1];
+          hipLaunchKernelGGL((vec_r_update<T>), dim3(grid), dim3(kWG), 0, s, aR);
+          SLA_HIP(hipGetLastError());
+          aT.k = kk;
+          aT.in0 = R[kk & 1];
+          hipEvent_t et = rec.begin(1);
+          SLA_HIP((launch_step<T, M_GTU>(G, aT, grid, s, plan.nt_g)));
+          rec.end(et, 1, kk);
+          aG.npin = grid;  // rr partials now come from vec_r_update
+        }
         aG.k = kk;
         aG.rv = R[kk & 1];
         hipEvent_t eg = rec.begin(2);

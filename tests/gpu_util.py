@@ -60,6 +60,19 @@ def iters_close(k_gpu: int, k_ref: int) -> bool:
     return abs(k_gpu - k_ref) <= max(1, math.ceil(0.02 * k_ref))
 
 
+def oracle_self_sensitivity(A, G, eps, b, rtol, maxit, seed=0):
+    """How far the oracle's own iterate and recursive residual norm move when
+    b is perturbed by about one ulp: CG amplifies rounding on ill-conditioned
+    systems, so this is the yardstick for comparing two implementations'
+    intermediate iterates.  Returns (relative change of x, relative change of
+    ||r_k|| / ||b||)."""
+    import oracle
+    b2 = b * (1.0 + 1e-16 * np.random.default_rng(seed).standard_normal(b.shape))
+    x1, _, _, r1 = oracle.pcg(A, G, eps, b, rtol, maxit)
+    x2, _, _, r2 = oracle.pcg(A, G, eps, b2, rtol, maxit)
+    return rel(x2, x1), abs(r2 - r1) / max(abs(r1), 1e-300)
+
+
 def copy_device_ints(ptr: int, count: int) -> np.ndarray:
     """Copy `count` int32 from a raw device pointer owned by the library."""
     out = torch.empty(count, dtype=torch.int32, device=DEV)

@@ -13,7 +13,7 @@ import oracle
 from preconditioned_cg_solver_amd import autograd as AG
 from preconditioned_cg_solver_amd import binding as B
 from preconditioned_cg_solver_amd import inputs as I
-from gpu_util import DEV, create, host, iters_close, rel, say, tdev
+from gpu_util import DEV, create, host, iters_close, oracle_self_sensitivity, rel, say, tdev
 
 pytestmark = pytest.mark.gpu
 
@@ -59,8 +59,19 @@ FORWARD = ["c0", "poisson2d_37", "poisson3d_13", "irregular_long_rows", "bsr_ela
            "powerlaw_20k", "c1", "c2"]
 
 
+@pytest.fixture(params=["auto", "fused", "unfused"])
+def fusion(request, monkeypatch):
+    """The iteration's two forms: p and r formed inside the products'
+    gathers, or separate vector passes (the library picks per matrix)."""
+    if request.param != "auto":
+        monkeypatch.setenv("SLA_FUSION", request.param)
+    return request.param
+
+
 @pytest.mark.parametrize("key", FORWARD)
-def test_forward_parity(key):
+def test_forward_parity(key, fusion):
+    if fusion != "auto" and key in ("c1", "c2"):
+        pytest.skip("full-size configs run in the library's own choice only")
     p = problem(key)
     x_ref, st_ref, it_ref, rr_ref = oracle.pcg(p.A, p.G, p.eps, p.b, p.rtol, p.maxit)
     assert st_ref == oracle.OK
@@ -75,8 +86,10 @@ def test_forward_parity(key):
 
 
 @pytest.mark.parametrize("key", ["c0", "poisson3d_13", "bsr_elastic_6", "irregular_long_rows",
-                                 "c2"])
-def test_adjoint_parity(key):
+                                 "powerlaw_20k", "c2"])
+def test_adjoint_parity(key, fusion):
+    if fusion != "auto" and key == "c2":
+        pytest.skip("full-size configs run in the library's own choice only")
     p = problem(key)
     x_ref, st, it, _ = oracle.pcg(p.A, p.G, p.eps, p.b, p.rtol, p.maxit)
     gx_ref = I.loss_grad_weights(p, x_ref)
@@ -119,8 +132,9 @@ def test_edge_zero_rhs():
     assert not torch.any(x)
 
 
-def test_edge_maxit_zero_and_small():
-    p = problem("c0")
+@pytest.mark.parametrize("key", ["c0", "powerlaw_20k"])
+def test_edge_maxit_zero_and_small(key, fusion):
+    p = problem(key)
     A, G = handles(p)
     b = tdev(p.b)
     say("maxit = 0")
@@ -132,11 +146,16 @@ def test_edge_maxit_zero_and_small():
         x_ref, st, it, rr = oracle.pcg(p.A, p.G, p.eps, p.b, 1e-10, m)
         assert st == oracle.NOT_CONVERGED and info.status == B.NOT_CONVERGED
         assert info.iterations == it == m
-        assert rel(host(x), x_ref) <= 1e-12
-        assert abs(info.rel_residual - rr) <= 1e-10 * rr
+        # iterates agree to rounding; on an ill-conditioned system CG amplifies
+        # rounding, so the bound is 100x the oracle's own movement under a
+        # one-ulp perturbation of b (about 1e-16 for Poisson, 1.7e-5 at
+        # iteration 17 for the power-law system, kappa ~ 1e8)
+        sx, sr = oracle_self_sensitivity(p.A, p.G, p.eps, p.b, 1e-10, m)
+        assert rel(host(x), x_ref) <= max(1e-12, 100 * sx)
+        assert abs(info.rel_residual - rr) <= max(1e-10, 100 * sr) * rr
 
 
-def test_edge_breakdown_negative_definite():
+def test_edge_breakdown_negative_definite(fusion):
     p = problem("c0")
     neg = I.SparseMatrix(p.A.n_block_rows, 1, p.A.row_ptr, p.A.col_idx, -p.A.vals)
     x_ref, st, it, _ = oracle.pcg(neg, p.G, p.eps, p.b, 1e-10, 100)
@@ -195,8 +214,8 @@ def test_invalid_arguments():
     assert e.value.status == B.ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("key", ["c0", "irregular_long_rows", "bsr_elastic_6"])
-def test_bitwise_deterministic(key):
+@pytest.mark.parametrize("key", ["c0", "irregular_long_rows", "bsr_elastic_6", "powerlaw_20k"])
+def test_bitwise_deterministic(key, fusion):
     p = problem(key)
     A, G = handles(p)
     b = tdev(p.b)
