@@ -155,6 +155,22 @@ sla_status sla_pcg_solve(sla_mat_t A, sla_mat_t G, double eps, const void *d_b, 
                          sla_solve_info *info);
 
 /*
+ * sla_pcg_solve that also records the CG coefficients, for spectral estimates
+ * of the preconditioned operator (the Lanczos tridiagonal of M^-1 A is built
+ * from them: T_jj = 1/alpha_j + beta_{j-1}/alpha_{j-1}, T_j,j+1 =
+ * sqrt(beta_j)/alpha_j).  d_alpha[k-1] = alpha_k (k = 1 .. iterations) and
+ * d_beta[k-1] = beta_k = rho_k / rho_{k-1} (k = 1 .. iterations - 1), for
+ * k <= hist_len; both are caller-owned device arrays of hist_len doubles
+ * (entries past the iterations performed are left untouched).  Other
+ * arguments and statuses as sla_pcg_solve; SLA_ERR_INVALID_ARG if
+ * hist_len < 0 or a buffer is NULL with hist_len > 0.
+ */
+sla_status sla_pcg_solve_history(sla_mat_t A, sla_mat_t G, double eps, const void *d_b,
+                                 void *d_x, double rtol, int32_t maxit, void *d_work,
+                                 size_t work_bytes, double *d_alpha, double *d_beta,
+                                 int32_t hist_len, void *stream, sla_solve_info *info);
+
+/*
  * Adjoint of x = A^-1 b for a scalar loss L(x) with gradient d_grad_x = dL/dx:
  * solves A^T lambda = dL/dx with the same preconditioner (A^T = A for the SPD
  * matrices this solver targets), writes dL/db = lambda to d_grad_b[n], and
@@ -167,6 +183,36 @@ sla_status sla_pcg_adjoint(sla_mat_t A, sla_mat_t G, double eps, const void *d_x
                            const void *d_grad_x, void *d_grad_b, void *d_grad_vals, double rtol,
                            int32_t maxit, void *d_work, size_t work_bytes, void *stream,
                            sla_solve_info *info);
+
+/*
+ * Extreme Ritz values of M^-1 A from k steps of PCG: the smallest and largest
+ * eigenvalues of the Lanczos tridiagonal built from h_alpha[0..k-1] and
+ * h_beta[0..k-2] as recorded by sla_pcg_solve_history (host arrays).  They lie
+ * inside [lambda_min, lambda_max] of M^-1 A and approach its ends as k grows,
+ * so *lmax / *lmin estimates the preconditioned condition number, one of the
+ * metrics of "Learning Sparse Approximate Inverse Preconditioners for
+ * Conjugate Gradient Solvers on GPUs" (Experimental setup).  Host-only and
+ * synchronous.  SLA_ERR_INVALID_ARG if k < 1, a pointer is NULL, an alpha is
+ * not finite and > 0, or a beta is not finite and >= 0.
+ */
+sla_status sla_lanczos_extremes(const double *h_alpha, const double *h_beta, int32_t k,
+                                double *lmin, double *lmax);
+
+/*
+ * Stochastic estimate of the scale-invariant SAI loss || A M^-1 / scale - I ||_F^2
+ * that the learned factor is trained on (same paper, Approach), for a given G:
+ * for each probe w_j, column j of the column-major n x nprobe device array
+ * d_probes (A's dtype), d_out[j] = || A (G G^T w_j + eps w_j) / scale - w_j ||^2
+ * (device double).  For probes with E[w w^T] = I (Rademacher or Gaussian) the
+ * mean of d_out estimates the loss; with the n unit vectors as probes the sum
+ * is the loss exactly.  scale is the caller's matrix norm.  G must carry its
+ * transpose; d_work needs max(sla_pcg_workspace_size(A), ..(G)) bytes.
+ * Asynchronous on `stream`.  SLA_ERR_INVALID_ARG on NULL or mismatched
+ * handles, eps < 0, scale <= 0, nprobe < 0 or a short workspace.
+ */
+sla_status sla_sai_loss(sla_mat_t A, sla_mat_t G, double eps, const void *d_probes,
+                        int32_t nprobe, double scale, void *d_work, size_t work_bytes,
+                        double *d_out, void *stream);
 
 /*
  * dL/dA on A's pattern: d_grad_vals[k] = -lambda[row(k)] * x[col(k)] for every

@@ -62,6 +62,13 @@ def _bind(lib):
     lib.orc_adjoint.restype = ctypes.c_int
     lib.orc_pattern_grad.argtypes = [i64, ctypes.c_int, vp, vp, vp, vp, vp]
     lib.orc_pattern_grad.restype = None
+    lib.orc_pcg_history.argtypes = [i64, ctypes.c_int, vp, vp, vp, vp, vp, vp, dbl, vp, vp, dbl,
+                                    i32, ctypes.POINTER(i32), ctypes.POINTER(dbl), vp, vp, i32]
+    lib.orc_pcg_history.restype = ctypes.c_int
+    lib.orc_lanczos_tridiag.argtypes = [vp, vp, i32, vp, vp]
+    lib.orc_lanczos_tridiag.restype = ctypes.c_int
+    lib.orc_sai_loss.argtypes = [i64, ctypes.c_int, vp, vp, vp, vp, vp, vp, dbl, vp, i32, dbl, vp]
+    lib.orc_sai_loss.restype = ctypes.c_int
     lib.orc_num_threads.argtypes = []
     lib.orc_num_threads.restype = ctypes.c_int
     lib.orc_dot_block.argtypes = []
@@ -142,6 +149,85 @@ def pcg(A, G, eps: float, b: np.ndarray, rtol: float, maxit: int, lib=None):
                      _p(gv), float(eps), _p(b), _p(x), float(rtol), int(maxit),
                      ctypes.byref(it), ctypes.byref(rr))
     return x, int(st), int(it.value), float(rr.value)
+
+
+def pcg_history(A, G, eps: float, b: np.ndarray, rtol: float, maxit: int, lib=None):
+    """pcg that also returns the CG coefficients: (x, status, iterations, relres,
+    alpha[0:iterations], beta[0:iterations-1]) with beta_k = rho_k / rho_{k-1}."""
+    lib = lib or load()
+    arp, aci, av = _mat(A)
+    grp, gci, gv = _mat(G)
+    b = _c(b, np.float64)
+    x = np.empty(A.n, dtype=np.float64)
+    m = max(int(maxit), 1)
+    ha = np.zeros(m, dtype=np.float64)
+    hb = np.zeros(m, dtype=np.float64)
+    it = ctypes.c_int32(0)
+    rr = ctypes.c_double(0.0)
+    st = lib.orc_pcg_history(A.n_block_rows, A.block_dim, _p(arp), _p(aci), _p(av), _p(grp),
+                             _p(gci), _p(gv), float(eps), _p(b), _p(x), float(rtol), int(maxit),
+                             ctypes.byref(it), ctypes.byref(rr), _p(ha), _p(hb), m)
+    k = int(it.value)
+    return x, int(st), k, float(rr.value), ha[:k].copy(), hb[:max(k - 1, 0)].copy()
+
+
+def lanczos_tridiag(alpha: np.ndarray, beta: np.ndarray, lib=None):
+    """(diagonal, off-diagonal) of the Lanczos tridiagonal built from CG's
+    alpha_1..k and beta_1..k-1."""
+    lib = lib or load()
+    a = _c(alpha, np.float64)
+    k = a.shape[0]
+    b = _c(beta, np.float64) if k > 1 else np.zeros(1)
+    d = np.empty(max(k, 1), dtype=np.float64)
+    e = np.empty(max(k - 1, 1), dtype=np.float64)
+    st = lib.orc_lanczos_tridiag(_p(a), _p(b), k, _p(d), _p(e))
+    if st != OK:
+        raise ValueError("lanczos_tridiag: need k >= 1, alpha > 0, beta >= 0")
+    return d[:k], e[:k - 1]
+
+
+def ritz_values(alpha: np.ndarray, beta: np.ndarray, lib=None) -> np.ndarray:
+    """Eigenvalues (ascending) of the Lanczos tridiagonal: Ritz values of M^-1 A
+    (scipy's symmetric tridiagonal eigensolver is the library step)."""
+    from scipy.linalg import eigvalsh_tridiagonal
+    d, e = lanczos_tridiag(alpha, beta, lib)
+    if d.shape[0] == 1:
+        return d.copy()
+    return eigvalsh_tridiagonal(d, e)
+
+
+def sai_loss(A, G, eps: float, W: np.ndarray, scale: float, lib=None) -> np.ndarray:
+    """Per-probe || A M^-1 w_j / scale - w_j ||^2 for the columns w_j of W (n x m)."""
+    lib = lib or load()
+    arp, aci, av = _mat(A)
+    grp, gci, gv = _mat(G)
+    W = np.asarray(W, dtype=np.float64)
+    m = W.shape[1]
+    w = np.ascontiguousarray(W.T)  # probe j contiguous at j * n
+    out = np.empty(max(m, 1), dtype=np.float64)
+    st = lib.orc_sai_loss(A.n_block_rows, A.block_dim, _p(arp), _p(aci), _p(av), _p(grp),
+                          _p(gci), _p(gv), float(eps), _p(w), m, float(scale), _p(out))
+    if st != OK:
+        raise ValueError("sai_loss: bad argument")
+    return out[:m]
+
+
+def dense_spectrum(A, G, eps: float) -> np.ndarray:
+    """All eigenvalues (ascending) of M^-1 A with M^-1 = G G^T + eps I, for small
+    matrices: M^-1 = L L^T (Cholesky) makes M^-1 A similar to L^T A L."""
+    Ad = A.to_dense()
+    Gd = G.to_dense()
+    Minv = Gd @ Gd.T + eps * np.eye(A.n)
+    L = np.linalg.cholesky(Minv)
+    S = L.T @ Ad @ L
+    return np.linalg.eigvalsh(0.5 * (S + S.T))
+
+
+def kaporin_number(eigs: np.ndarray) -> float:
+    """Kaporin's condition number of an SPD operator: the arithmetic mean of its
+    eigenvalues over their geometric mean (1 for a multiple of I)."""
+    e = np.asarray(eigs, dtype=np.float64)
+    return float(np.mean(e) / np.exp(np.mean(np.log(e))))
 
 
 def pattern_grad(A, lam: np.ndarray, x: np.ndarray, lib=None) -> np.ndarray:

@@ -172,12 +172,16 @@ out:
 
 /* Preconditioned CG for A x = b with M^-1 = G G^T + eps I.
  * On return: x = last iterate, *iters = number of A-products, *relres =
- * ||r_k|| / ||b|| of the recursive residual (0 when b = 0). */
-int orc_pcg(int64_t nbr, int bs,
-            const int32_t *a_row_ptr, const int32_t *a_col, const double *a_val,
-            const int32_t *g_row_ptr, const int32_t *g_col, const double *g_val,
-            double eps, const double *b, double *x, double rtol, int32_t maxit,
-            int32_t *iters, double *relres)
+ * ||r_k|| / ||b|| of the recursive residual (0 when b = 0).
+ * When hist_len > 0 the step lengths are recorded as hist_a[k-1] = alpha_k and
+ * the direction coefficients as hist_b[k-1] = beta_k = rho_k / rho_{k-1}, for
+ * every k <= hist_len that the iteration reaches. */
+int orc_pcg_history(int64_t nbr, int bs,
+                    const int32_t *a_row_ptr, const int32_t *a_col, const double *a_val,
+                    const int32_t *g_row_ptr, const int32_t *g_col, const double *g_val,
+                    double eps, const double *b, double *x, double rtol, int32_t maxit,
+                    int32_t *iters, double *relres, double *hist_a, double *hist_b,
+                    int32_t hist_len)
 {
     const int64_t n = nbr * bs;
     const int64_t bb = (int64_t)bs * bs;
@@ -217,6 +221,7 @@ int orc_pcg(int64_t nbr, int bs,
             const double sigma = orc_dot(n, p, q);
             if (!(sigma > 0.0) || !isfinite(sigma)) { *iters = k - 1; st = ORC_ERR_BREAKDOWN; goto out; }
             const double alpha = rho / sigma;
+            if (k <= hist_len) hist_a[k - 1] = alpha;
 #pragma omp parallel for schedule(static)
             for (int64_t i = 0; i < n; ++i) {
                 x[i] = x[i] + alpha * p[i];
@@ -232,6 +237,7 @@ int orc_pcg(int64_t nbr, int bs,
             const double rho_new = orc_dot(n, r, z);
             if (!(rho_new > 0.0) || !isfinite(rho_new)) { st = ORC_ERR_BREAKDOWN; goto out; }
             const double beta = rho_new / rho;
+            if (k <= hist_len) hist_b[k - 1] = beta;
 #pragma omp parallel for schedule(static)
             for (int64_t i = 0; i < n; ++i) p[i] = z[i] + beta * p[i];
             rho = rho_new;
@@ -241,6 +247,70 @@ int orc_pcg(int64_t nbr, int bs,
 out:
     free(trp); free(tci); free(tv);
     free(r); free(z); free(p); free(q); free(t);
+    return st;
+}
+
+int orc_pcg(int64_t nbr, int bs,
+            const int32_t *a_row_ptr, const int32_t *a_col, const double *a_val,
+            const int32_t *g_row_ptr, const int32_t *g_col, const double *g_val,
+            double eps, const double *b, double *x, double rtol, int32_t maxit,
+            int32_t *iters, double *relres)
+{
+    return orc_pcg_history(nbr, bs, a_row_ptr, a_col, a_val, g_row_ptr, g_col, g_val, eps, b,
+                           x, rtol, maxit, iters, relres, NULL, NULL, 0);
+}
+
+/* The Lanczos tridiagonal T_k of the preconditioned operator M^-1 A that k
+ * steps of PCG implicitly build (the CG-Lanczos connection of textbook
+ * iterative-methods theory; its eigenvalues are Ritz values of M^-1 A):
+ *   T_11 = 1 / alpha_1,
+ *   T_jj = 1 / alpha_j + beta_{j-1} / alpha_{j-1}          (j = 2 .. k),
+ *   T_j,j+1 = T_j+1,j = sqrt(beta_j) / alpha_j             (j = 1 .. k-1).
+ * diag gets k entries, off gets k-1. */
+int orc_lanczos_tridiag(const double *alpha, const double *beta, int32_t k, double *diag,
+                        double *off)
+{
+    if (k < 1) return ORC_ERR_ARG;
+    for (int32_t j = 0; j < k; ++j) {
+        if (!(alpha[j] > 0.0) || !isfinite(alpha[j])) return ORC_ERR_ARG;
+        if (j + 1 < k && (!(beta[j] >= 0.0) || !isfinite(beta[j]))) return ORC_ERR_ARG;
+    }
+    for (int32_t j = 0; j < k; ++j) {
+        diag[j] = 1.0 / alpha[j];
+        if (j > 0) diag[j] = diag[j] + beta[j - 1] / alpha[j - 1];
+        if (j + 1 < k) off[j] = sqrt(beta[j]) / alpha[j];
+    }
+    return ORC_OK;
+}
+
+/* Stochastic estimate of the scale-invariant SAI loss || A M^-1 / s - I ||_F^2
+ * ("Learning Sparse Approximate Inverse Preconditioners ...", Approach):
+ * for probe vectors w_j (column j of the n x nprobe column-major array w),
+ * out[j] = || A (M^-1 w_j) / s - w_j ||^2, with M^-1 w = G (G^T w) + eps w.
+ * For probes with E[w w^T] = I the mean of out is an unbiased estimate of the
+ * loss; with the n unit vectors as probes their sum is the loss exactly. */
+int orc_sai_loss(int64_t nbr, int bs,
+                 const int32_t *a_row_ptr, const int32_t *a_col, const double *a_val,
+                 const int32_t *g_row_ptr, const int32_t *g_col, const double *g_val,
+                 double eps, const double *w, int32_t nprobe, double s, double *out)
+{
+    const int64_t n = nbr * bs;
+    if (nbr < 0 || bs < 1 || nprobe < 0 || !(eps >= 0.0) || !(s > 0.0) || !isfinite(s))
+        return ORC_ERR_ARG;
+    const size_t vb = (size_t)(n > 0 ? n : 1) * sizeof(double);
+    double *z = (double *)malloc(vb), *y = (double *)malloc(vb), *d = (double *)malloc(vb);
+    int st = ORC_OK;
+    if (!z || !y || !d) { st = ORC_ERR_NOMEM; goto out; }
+    for (int32_t j = 0; j < nprobe; ++j) {
+        const double *wj = w + (int64_t)j * n;
+        st = orc_precond_apply(nbr, bs, g_row_ptr, g_col, g_val, eps, wj, z);
+        if (st != ORC_OK) goto out;
+        orc_spmv(nbr, bs, a_row_ptr, a_col, a_val, z, y);
+        for (int64_t i = 0; i < n; ++i) d[i] = y[i] / s - wj[i];
+        out[j] = orc_dot(n, d, d);
+    }
+out:
+    free(z); free(y); free(d);
     return st;
 }
 

@@ -77,6 +77,10 @@ def _declare(L):
                           st),
         "sla_pcg_adjoint": ([vp, vp, dbl, vp, vp, vp, vp, dbl, i32, vp, sz, vp,
                              ctypes.POINTER(SolveInfo)], st),
+        "sla_lanczos_extremes": ([vp, vp, i32, ctypes.POINTER(dbl), ctypes.POINTER(dbl)], st),
+        "sla_sai_loss": ([vp, vp, dbl, vp, i32, dbl, vp, sz, vp, vp], st),
+        "sla_pcg_solve_history": ([vp, vp, dbl, vp, vp, dbl, i32, vp, sz, vp, vp, i32, vp,
+                                   ctypes.POINTER(SolveInfo)], st),
         "sla_pattern_grad": ([vp, vp, vp, vp, vp], st),
         "sla_status_string": ([st], ctypes.c_char_p),
         "sla_last_error": ([], ctypes.c_char_p),
@@ -248,6 +252,57 @@ def sla_pcg_solve(A: Mat, G: Mat, eps: float, b: torch.Tensor, x: Optional[torch
     if raise_on_error:
         _check(st, allow=(OK, NOT_CONVERGED))
     return x, _info(st, si)
+
+
+def sla_pcg_solve_history(A: Mat, G: Mat, eps: float, b: torch.Tensor,
+                          x: Optional[torch.Tensor] = None, rtol: float = 1e-10,
+                          maxit: int = 1000, work: Optional[torch.Tensor] = None, stream=None,
+                          raise_on_error: bool = True):
+    """sla_pcg_solve that also returns the CG coefficients alpha_k (k = 1..iters)
+    and beta_k = rho_k / rho_{k-1} (k = 1..iters-1) as CPU float64 tensors."""
+    if x is None:
+        x = torch.empty_like(b)
+    if work is None:
+        work = workspace(A, b.device)
+    hist_a = torch.zeros(max(maxit, 1), dtype=torch.float64, device=b.device)
+    hist_b = torch.zeros(max(maxit, 1), dtype=torch.float64, device=b.device)
+    si = SolveInfo()
+    st = lib().sla_pcg_solve_history(A.handle, G.handle, float(eps), _ptr(b), _ptr(x),
+                                     float(rtol), int(maxit), _ptr(work), work.numel(),
+                                     _ptr(hist_a), _ptr(hist_b), int(maxit), _stream(stream),
+                                     ctypes.byref(si))
+    if raise_on_error:
+        _check(st, allow=(OK, NOT_CONVERGED))
+    k = si.iterations
+    return x, _info(st, si), hist_a[:k].cpu(), hist_b[:max(k - 1, 0)].cpu()
+
+
+def sla_lanczos_extremes(alpha, beta):
+    """(lmin, lmax) of the Lanczos tridiagonal from CG's alpha_1..k, beta_1..k-1."""
+    a = [float(v) for v in alpha]
+    b = [float(v) for v in beta] or [0.0]
+    ha = (ctypes.c_double * max(len(a), 1))(*a)
+    hb = (ctypes.c_double * len(b))(*b)
+    lo, hi = ctypes.c_double(0.0), ctypes.c_double(0.0)
+    st = lib().sla_lanczos_extremes(ha, hb, len(a), ctypes.byref(lo), ctypes.byref(hi))
+    _check(st)
+    return lo.value, hi.value
+
+
+def sla_sai_loss(A: Mat, G: Mat, eps: float, probes: torch.Tensor, scale: float,
+                 work: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Per-probe || A M^-1 w_j / scale - w_j ||^2 for the columns w_j of the
+    (n, m) device tensor `probes` (float64 device tensor of length m)."""
+    n, m = probes.shape
+    pt = probes.t().contiguous()  # probe j contiguous at j * n
+    if work is None:
+        nb = max(sla_pcg_workspace_size(A), sla_pcg_workspace_size(G), 1)
+        work = torch.empty(nb, dtype=torch.uint8, device=probes.device)
+    out = torch.empty(max(m, 1), dtype=torch.float64, device=probes.device)
+    st = lib().sla_sai_loss(A.handle, G.handle, float(eps), _ptr(pt), int(m), float(scale),
+                            _ptr(work), work.numel(), _ptr(out), _stream(stream))
+    _check(st)
+    return out[:m]
 
 
 def sla_pcg_adjoint(A: Mat, G: Mat, eps: float, x: torch.Tensor, grad_x: torch.Tensor,

@@ -328,6 +328,20 @@ sla_status sla_pcg_solve(sla_mat_t A, sla_mat_t G, double eps, const void* d_b, 
                         (hipStream_t)stream, info);
 }
 
+sla_status sla_pcg_solve_history(sla_mat_t A, sla_mat_t G, double eps, const void* d_b, void* d_x,
+                                 double rtol, int32_t maxit, void* d_work, size_t work_bytes,
+                                 double* d_alpha, double* d_beta, int32_t hist_len, void* stream,
+                                 sla_solve_info* info) {
+  sla_status st = check_solve(A, G, eps, d_b, d_x, rtol, maxit, d_work, work_bytes);
+  if (st != SLA_OK) return st;
+  if (hist_len < 0 || (hist_len > 0 && (!d_alpha || !d_beta))) {
+    set_error("history buffers must hold hist_len doubles each");
+    return SLA_ERR_INVALID_ARG;
+  }
+  return sla::pcg_solve(*A, *G, eps, d_b, d_x, rtol, maxit, d_work, work_bytes,
+                        (hipStream_t)stream, info, d_alpha, d_beta, hist_len);
+}
+
 sla_status sla_pcg_adjoint(sla_mat_t A, sla_mat_t G, double eps, const void* d_x,
                            const void* d_grad_x, void* d_grad_b, void* d_grad_vals, double rtol,
                            int32_t maxit, void* d_work, size_t work_bytes, void* stream,
@@ -346,6 +360,39 @@ sla_status sla_pcg_adjoint(sla_mat_t A, sla_mat_t G, double eps, const void* d_x
   hipError_t e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
   return st;
+}
+
+sla_status sla_lanczos_extremes(const double* h_alpha, const double* h_beta, int32_t k,
+                                double* lmin, double* lmax) {
+  if (k < 1 || !h_alpha || (k > 1 && !h_beta) || !lmin || !lmax) {
+    set_error("need k >= 1 and non-NULL alpha[k], beta[k-1], lmin, lmax");
+    return SLA_ERR_INVALID_ARG;
+  }
+  return sla::lanczos_extremes(h_alpha, h_beta, k, lmin, lmax);
+}
+
+sla_status sla_sai_loss(sla_mat_t A, sla_mat_t G, double eps, const void* d_probes,
+                        int32_t nprobe, double scale, void* d_work, size_t work_bytes,
+                        double* d_out, void* stream) {
+  if (!A || !G || !G->has_t) {
+    set_error("A and G must be non-NULL and G created with SLA_BUILD_TRANSPOSE");
+    return SLA_ERR_INVALID_ARG;
+  }
+  if (G->n() != A->n() || G->bs != A->bs || G->dtype != A->dtype) {
+    set_error("A and G must have the same size, block size and dtype");
+    return SLA_ERR_INVALID_ARG;
+  }
+  if (!(std::isfinite(eps) && eps >= 0.0) || !(std::isfinite(scale) && scale > 0.0) ||
+      nprobe < 0) {
+    set_error("need finite eps >= 0, finite scale > 0 and nprobe >= 0");
+    return SLA_ERR_INVALID_ARG;
+  }
+  const size_t need = std::max(sla::workspace_bytes(*A), sla::workspace_bytes(*G));
+  if (nprobe > 0 && (!d_out || (A->n() > 0 && !d_probes) || !d_work || work_bytes < need)) {
+    set_error("bad probe, output or workspace argument");
+    return SLA_ERR_INVALID_ARG;
+  }
+  return sla::sai_loss(*A, *G, eps, d_probes, nprobe, scale, d_work, d_out, (hipStream_t)stream);
 }
 
 sla_status sla_pattern_grad(sla_mat_t A, const void* d_lambda, const void* d_x,

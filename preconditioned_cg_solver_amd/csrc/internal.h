@@ -164,9 +164,16 @@ sla_status precond_apply(const sla_mat& G, double eps, const void* r, void* z, v
                          size_t work_bytes, hipStream_t s);
 sla_status pcg_solve(const sla_mat& A, const sla_mat& G, double eps, const void* b, void* x,
                      double rtol, int32_t maxit, void* work, size_t work_bytes, hipStream_t s,
-                     sla_solve_info* info);
+                     sla_solve_info* info, double* hist_a = nullptr, double* hist_b = nullptr,
+                     int32_t hist_len = 0);
 sla_status pattern_grad(const sla_mat& A, const void* lam, const void* x, void* grad,
                         hipStream_t s);
+sla_status sai_loss(const sla_mat& A, const sla_mat& G, double eps, const void* probes,
+                    int32_t nprobe, double scale, void* work, double* out, hipStream_t s);
+
+// Spectrum of the Lanczos tridiagonal (spectrum.cpp, host only).
+sla_status lanczos_extremes(const double* alpha, const double* beta, int32_t k, double* lmin,
+                            double* lmax);
 
 // Profiling (solver.hip).
 void prof_enable(int mask);

@@ -85,6 +85,9 @@ struct StepArgs {
   int k;
   int maxit;
   double rtol;
+  double* hist_a;  // optional coefficient history: alpha_k at [k-1],
+  double* hist_b;  // beta_k = rho_k / rho_{k-1} at [k-1], for k <= hist_len
+  int hist_len;
 };
 
 template <typename T>
@@ -156,8 +159,10 @@ __device__ __forceinline__ bool prologue(const StepArgs<T>& a, Coef<T>& cf, doub
       }
       if (bad) return false;
       if constexpr (MODE == M_A) {
-        cf.c = T(rho / a.st->rho[(k - 2) % kRing]);   // beta_{k-1}
+        const double beta = rho / a.st->rho[(k - 2) % kRing];
+        cf.c = T(beta);                               // beta_{k-1}
         cf.c2 = T(a.st->alpha[(k - 1) % kRing]);      // alpha_{k-1}
+        if (lead && a.hist_b && k - 1 <= a.hist_len) a.hist_b[k - 2] = beta;
       }
       return true;
     } else if constexpr (MODE == M_GT) {
@@ -170,6 +175,7 @@ __device__ __forceinline__ bool prologue(const StepArgs<T>& a, Coef<T>& cf, doub
         } else {
           a.st->alpha[k % kRing] = alpha;
           a.st->sigma = sigma;
+          if (a.hist_a && k <= a.hist_len) a.hist_a[k - 1] = alpha;
         }
       }
       if (bad) return false;
@@ -880,6 +886,32 @@ __global__ void finalize_x(const SolverState* __restrict__ st, T* __restrict__ x
 }
 
 // ---------------------------------------------------------------------------
+// SAI-loss probe term || y / s - w ||^2 with y = A M^-1 w: workgroup partials,
+// then one workgroup adds them in index order.
+// ---------------------------------------------------------------------------
+
+template <typename T>
+__global__ __launch_bounds__(kWG) void sai_partial(const T* __restrict__ y,
+                                                   const T* __restrict__ w, double s, int n,
+                                                   double* __restrict__ part) {
+  __shared__ double s_red[kWaves];
+  double acc = 0.0;
+  for (int i = blockIdx.x * kWG + threadIdx.x; i < n; i += gridDim.x * kWG) {
+    const double d = (double)y[i] / s - (double)w[i];
+    acc += d * d;
+  }
+  const double t = block_sum(acc, s_red);
+  if (threadIdx.x == 0) part[blockIdx.x] = t;
+}
+
+__global__ __launch_bounds__(kWG) void sai_final(const double* __restrict__ part, int np,
+                                                 double* __restrict__ out) {
+  __shared__ double s_red[kWaves];
+  const double t = sum_partials(part, np, s_red);
+  if (threadIdx.x == 0) *out = t;
+}
+
+// ---------------------------------------------------------------------------
 // Adjoint pattern gradient: g[k] = -lambda_row(k) * x_col(k).
 // ---------------------------------------------------------------------------
 
@@ -1223,7 +1255,8 @@ bool use_fused(const sla_mat& A) {
 
 template <typename T>
 sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, T* x, double rtol,
-                    int maxit, void* work, hipStream_t s, sla_solve_info* info) {
+                    int maxit, void* work, hipStream_t s, sla_solve_info* info, double* hist_a,
+                    double* hist_b, int hist_len) {
   const int n = (int)A.n();
   Work w = carve(A, work);
   T *P[2] = {(T*)w.vec[0], (T*)w.vec[1]}, *R[2] = {(T*)w.vec[2], (T*)w.vec[3]};
@@ -1248,6 +1281,9 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
     a->maxit = maxit;
     a->rtol = rtol;
     a->eps = eps;
+    a->hist_a = hist_a;
+    a->hist_b = hist_b;
+    a->hist_len = hist_len;
   }
   // A step: pin = rho partials (from G step), pout = sigma partials
   aA.pin = w.prho;
@@ -1487,11 +1523,9 @@ sla_status spmv(const sla_mat& A, bool transpose, const void* x, void* y, hipStr
   return SLA_OK;
 }
 
-sla_status precond_apply(const sla_mat& G, double eps, const void* r, void* z, void* work,
-                         size_t, hipStream_t s) {
-  if (G.n() == 0) return SLA_OK;
-  Work w = carve(G, work);
-  void* t = w.vec[5];
+// z = G (G^T r) + eps r with t = G^T r in caller-provided memory.
+static sla_status precond_into(const sla_mat& G, double eps, const void* r, void* t, void* z,
+                               hipStream_t s) {
   sla_status st = spmv(G, true, r, t, s);
   if (st != SLA_OK) return st;
   const LongScratch ls = long_scratch(G, false);
@@ -1516,16 +1550,53 @@ sla_status precond_apply(const sla_mat& G, double eps, const void* r, void* z, v
   return SLA_OK;
 }
 
+sla_status precond_apply(const sla_mat& G, double eps, const void* r, void* z, void* work,
+                         size_t, hipStream_t s) {
+  if (G.n() == 0) return SLA_OK;
+  Work w = carve(G, work);
+  return precond_into(G, eps, r, w.vec[5], z, s);
+}
+
+sla_status sai_loss(const sla_mat& A, const sla_mat& G, double eps, const void* probes,
+                    int32_t nprobe, double scale, void* work, double* out, hipStream_t s) {
+  const int64_t n = A.n();
+  if (nprobe == 0) return SLA_OK;
+  Work w = carve(A, work);
+  const size_t es = A.dtype == SLA_F64 ? 8 : 4;
+  const int grid = (int)std::min<int64_t>(max_grid(), std::max<int64_t>(1, (n + kWG - 1) / kWG));
+  for (int32_t j = 0; j < nprobe; ++j) {
+    const void* wj = (const char*)probes + (size_t)j * (size_t)n * es;
+    if (n > 0) {
+      sla_status st = precond_into(G, eps, wj, w.vec[5], w.vec[0], s);
+      if (st != SLA_OK) return st;
+      st = spmv(A, false, w.vec[0], w.vec[1], s);
+      if (st != SLA_OK) return st;
+    }
+    if (A.dtype == SLA_F64)
+      sai_partial<double><<<grid, kWG, 0, s>>>((const double*)w.vec[1], (const double*)wj,
+                                               scale, (int)n, w.psig);
+    else
+      sai_partial<float><<<grid, kWG, 0, s>>>((const float*)w.vec[1], (const float*)wj, scale,
+                                              (int)n, w.psig);
+    SLA_HIP(hipGetLastError());
+    sai_final<<<1, kWG, 0, s>>>(w.psig, grid, out + j);
+    SLA_HIP(hipGetLastError());
+  }
+  return SLA_OK;
+}
+
 sla_status pcg_solve(const sla_mat& A, const sla_mat& G, double eps, const void* b, void* x,
                      double rtol, int32_t maxit, void* work, size_t, hipStream_t s,
-                     sla_solve_info* info) {
+                     sla_solve_info* info, double* hist_a, double* hist_b, int32_t hist_len) {
   if (A.n() == 0) {
     if (info) *info = sla_solve_info{0, 1, 0.0, 0.0};
     return SLA_OK;
   }
   if (A.dtype == SLA_F64)
-    return pcg_impl<double>(A, G, eps, (const double*)b, (double*)x, rtol, maxit, work, s, info);
-  return pcg_impl<float>(A, G, eps, (const float*)b, (float*)x, rtol, maxit, work, s, info);
+    return pcg_impl<double>(A, G, eps, (const double*)b, (double*)x, rtol, maxit, work, s, info,
+                            hist_a, hist_b, hist_len);
+  return pcg_impl<float>(A, G, eps, (const float*)b, (float*)x, rtol, maxit, work, s, info,
+                         hist_a, hist_b, hist_len);
 }
 
 sla_status pattern_grad(const sla_mat& A, const void* lam, const void* x, void* grad,

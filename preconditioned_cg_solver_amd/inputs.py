@@ -322,13 +322,21 @@ def spai_factor(A: SparseMatrix, rng: np.random.Generator, spread: float = 0.1) 
 
 
 def diagonal_factor(A: SparseMatrix) -> SparseMatrix:
-    """G = diag(a_ii^(-1/2)) (with eps = 0 this is Jacobi preconditioning)."""
-    if A.block_dim != 1:
-        raise ValueError("diagonal factor is defined for CSR here")
+    """G = diag(a_ii^(-1/2)) in A's format (3x3 diagonal blocks for BSR); with
+    eps = 0, M^-1 = G G^T is Jacobi (diagonal) preconditioning."""
+    b = A.block_dim
     rows = A.row_of_entry()
-    d = A.vals[A.col_idx.astype(np.int64) == rows]
-    rp = np.arange(A.n + 1, dtype=np.int32)
-    return SparseMatrix(A.n, 1, rp, np.arange(A.n, dtype=np.int32), 1.0 / np.sqrt(d))
+    dpos = np.nonzero(A.col_idx.astype(np.int64) == rows)[0]
+    if dpos.shape[0] != A.n_block_rows:
+        raise ValueError("every row of A must store its diagonal")
+    blocks = A.vals.reshape(-1, b, b)
+    d = np.stack([blocks[dpos, r, r] for r in range(b)], axis=1)      # (nbr, b)
+    g = np.zeros((A.n_block_rows, b, b), dtype=np.float64)
+    for r in range(b):
+        g[:, r, r] = 1.0 / np.sqrt(d[:, r])
+    rp = np.arange(A.n_block_rows + 1, dtype=np.int32)
+    return SparseMatrix(A.n_block_rows, b, rp, np.arange(A.n_block_rows, dtype=np.int32),
+                        g.reshape(-1))
 
 
 # ----------------------------------------------------------------------------

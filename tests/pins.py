@@ -420,9 +420,100 @@ def pin_adjoint_identities(lib):
     assert np.array_equal(gval, -(lam[rows] * x[p.A.col_idx]))
 
 
+# ---------------------------------------------------------------------------
+# CG coefficients, Lanczos spectrum, SAI loss
+# ---------------------------------------------------------------------------
+
+def diag_matrix(d):
+    n = len(d)
+    return I.SparseMatrix(n, 1, np.arange(n + 1, dtype=np.int32), np.arange(n, dtype=np.int32),
+                          np.asarray(d, dtype=np.float64).copy())
+
+
+def pin_lanczos_diagonal(lib):
+    """For A = diag(d) and G = diag(g), M^-1 A = diag((g^2 + eps) d); n steps of
+    PCG from a b with no zero component make the Lanczos tridiagonal's
+    eigenvalues those n numbers (exact arithmetic; here to rounding).  alpha_1 is
+    rho_0 / sigma_1 in closed form."""
+    rng = np.random.default_rng(51)
+    n = 9
+    d = np.array([1.0, 2.0, 3.5, 5.0, 8.0, 13.0, 21.0, 34.0, 55.0])
+    g = rng.uniform(0.5, 1.5, n)
+    eps = 0.25
+    A, G = diag_matrix(d), diag_matrix(g)
+    b = rng.uniform(0.5, 1.5, n)
+    x, st, it, _, al, be = oracle.pcg_history(A, G, eps, b, 1e-300, n, lib=lib)
+    assert it == n and al.shape == (n,) and be.shape == (n - 1,), ("history length", it)
+    m = g * g + eps
+    z0 = m * b
+    assert abs(al[0] - (b @ z0) / (z0 @ (d * z0))) <= 1e-14 * al[0], "alpha_1 closed form"
+    ritz = oracle.ritz_values(al, be, lib=lib)
+    exact = np.sort(m * d)
+    assert np.max(np.abs(ritz - exact) / exact) <= 1e-9, ("ritz vs diag spectrum", ritz, exact)
+    # a single step: T_1 = 1 / alpha_1 is the Rayleigh quotient of z0
+    _, _, it1, _, al1, be1 = oracle.pcg_history(A, G, eps, b, 1e-300, 1, lib=lib)
+    assert it1 == 1 and be1.shape == (0,)
+    r1 = oracle.ritz_values(al1, be1, lib=lib)
+    assert abs(r1[0] - (z0 @ (d * z0)) / (b @ z0)) <= 1e-14 * r1[0]
+
+
+def pin_lanczos_spectrum(lib):
+    """On a preconditioned Poisson system the Ritz values after n steps match
+    the generalised eigenvalues of (A, M) at both ends (scipy's dense
+    generalised symmetric eigensolver), and the oracle's dense spectrum agrees
+    with that eigensolver; after a few steps every Ritz value lies inside the
+    spectrum and the largest grows monotonically (interlacing)."""
+    p = I.make_problem(0, size=5)                      # n = 25
+    Ad = p.A.to_dense()
+    Gd = p.G.to_dense()
+    M = np.linalg.inv(Gd @ Gd.T + p.eps * np.eye(p.A.n))
+    ev = sla.eigh(Ad, 0.5 * (M + M.T), eigvals_only=True)
+    ds = oracle.dense_spectrum(p.A, p.G, p.eps)
+    assert np.max(np.abs(ds - ev) / ev) <= 1e-9, "dense spectrum vs generalised eigh"
+    rng = np.random.default_rng(52)
+    b = rng.standard_normal(p.A.n)
+    _, _, it, _, al, be = oracle.pcg_history(p.A, p.G, p.eps, b, 1e-300, p.A.n, lib=lib)
+    assert it == p.A.n
+    ritz = oracle.ritz_values(al, be, lib=lib)
+    assert abs(ritz[0] - ev[0]) <= 1e-8 * ev[0] and abs(ritz[-1] - ev[-1]) <= 1e-8 * ev[-1], \
+        ("extreme ritz", ritz[[0, -1]], ev[[0, -1]])
+    prev = 0.0
+    for k in range(1, 7):
+        rk = oracle.ritz_values(al[:k], be[:k - 1], lib=lib)
+        assert rk[0] >= ev[0] * (1 - 1e-12) and rk[-1] <= ev[-1] * (1 + 1e-12), f"inside k={k}"
+        assert rk[-1] >= prev * (1 - 1e-12), f"monotone k={k}"
+        prev = rk[-1]
+
+
+def pin_sai_loss(lib):
+    """|| A M^-1 / s - I ||_F^2: with unit-vector probes the per-probe terms sum
+    to the dense Frobenius norm; for diagonal A and G the loss has a closed
+    form; with the SPAI factor of a Poisson matrix the dense product is formed
+    explicitly."""
+    n = 6
+    d = np.array([1.0, 2.0, 4.0, 8.0, 3.0, 5.0])
+    g = np.array([1.0, 0.5, 0.25, 0.3, 0.6, 0.4])
+    eps, s = 0.1, 2.5
+    out = oracle.sai_loss(diag_matrix(d), diag_matrix(g), eps, np.eye(n), s, lib=lib)
+    closed = (d * (g * g + eps) / s - 1.0) ** 2
+    assert np.allclose(out, closed, rtol=1e-14, atol=1e-15), ("closed form", out, closed)
+    p = I.make_problem(0, size=5)
+    Ad = p.A.to_dense()
+    Gd = p.G.to_dense()
+    s = float(np.mean(np.abs(p.A.vals)))
+    E = Ad @ (Gd @ Gd.T + p.eps * np.eye(p.A.n)) / s - np.eye(p.A.n)
+    tot = oracle.sai_loss(p.A, p.G, p.eps, np.eye(p.A.n), s, lib=lib).sum()
+    fro = float(np.sum(E * E))
+    assert abs(tot - fro) <= 1e-12 * fro, ("frobenius", tot, fro)
+    rng = np.random.default_rng(53)
+    W = rng.choice([-1.0, 1.0], size=(p.A.n, 3))
+    est = oracle.sai_loss(p.A, p.G, p.eps, W, s, lib=lib)
+    assert np.allclose(est, np.sum((E @ W) ** 2, axis=0), rtol=1e-12), "probe terms"
+
+
 ALL_PINS = [
     pin_spmv_bruteforce, pin_spmv_bsr_dense, pin_spmv_eigenpairs, pin_transpose, pin_precond,
     pin_pcg_cholesky, pin_pcg_galerkin, pin_pcg_eigen, pin_pcg_cg_equivalence, pin_pcg_scipy,
     pin_pcg_edges, pin_adjoint_fd_b, pin_adjoint_fd_entries, pin_adjoint_directional,
-    pin_adjoint_identities,
+    pin_adjoint_identities, pin_lanczos_diagonal, pin_lanczos_spectrum, pin_sai_loss,
 ]

@@ -267,3 +267,19 @@ def test_autograd_function_matches_oracle():
     assert rel(host(x), x_ref) <= 1e-8
     assert rel(host(b.grad), lam) <= 1e-7
     assert rel(host(v.grad), gv) <= 1e-7
+
+
+@pytest.mark.parametrize("key", ["c0", "poisson3d_13", "bsr_elastic_6", "powerlaw_20k"])
+def test_jacobi_parity(key):
+    """Diagonal (Jacobi) preconditioning through the same kernels:
+    G = diag(a_ii^-1/2), eps = 0, so M^-1 = D^-1."""
+    p = problem(key)
+    D = I.diagonal_factor(p.A)
+    x_ref, st, it, _ = oracle.pcg(p.A, D, 0.0, p.b, p.rtol, p.maxit)
+    assert st == oracle.OK
+    say("jacobi", key, "oracle iterations", it)
+    A = create(p.A)
+    Dh = create(D, transpose=True)
+    x, info = B.sla_pcg_solve(A, Dh, 0.0, tdev(p.b), rtol=p.rtol, maxit=p.maxit)
+    assert info.status == B.OK and iters_close(info.iterations, it)
+    assert rel(host(x), x_ref) <= 1e-8

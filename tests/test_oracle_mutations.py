@@ -42,6 +42,23 @@ MUTATIONS = [
      "-(lam[I * bs + r] * x[J * bs + c])", "(lam[I * bs + r] * x[J * bs + c])"),
     ("adjoint solves with b instead of dL/dx",
      "eps, gx, lam,", "eps, x, lam,"),
+    ("Lanczos diagonal divides by the current alpha",
+     "diag[j] = diag[j] + beta[j - 1] / alpha[j - 1];",
+     "diag[j] = diag[j] + beta[j - 1] / alpha[j];"),
+    ("Lanczos off-diagonal without the square root",
+     "off[j] = sqrt(beta[j]) / alpha[j];", "off[j] = beta[j] / alpha[j];"),
+    ("history records alpha one step late",
+     "if (k <= hist_len) hist_a[k - 1] = alpha;", "if (k < hist_len) hist_a[k] = alpha;"),
+    ("SAI loss ignores the scale",
+     "d[i] = y[i] / s - wj[i];", "d[i] = y[i] - wj[i];"),
+    ("SAI loss multiplies M^-1 A instead of A M^-1",
+     "orc_precond_apply(nbr, bs, g_row_ptr, g_col, g_val, eps, wj, z);\n"
+     "        if (st != ORC_OK) goto out;\n"
+     "        orc_spmv(nbr, bs, a_row_ptr, a_col, a_val, z, y);",
+     "ORC_OK;\n"
+     "        orc_spmv(nbr, bs, a_row_ptr, a_col, a_val, wj, z);\n"
+     "        st = orc_precond_apply(nbr, bs, g_row_ptr, g_col, g_val, eps, z, y);\n"
+     "        if (st != ORC_OK) goto out;"),
 ]
 
 
