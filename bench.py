@@ -81,15 +81,166 @@ def traffic_if_current():
         return None
 
 
-def cpu_baseline(p, iters):
+STEP_NAMES = {1: "A step, iteration 1", 2: "A step (q = A p, p and x updates)",
+              3: "G^T step, start-up", 4: "G^T step (t = G^T r, r update)",
+              5: "G step, start-up", 6: "G step (z = G t + eps r)"}
+
+
+def _counter_rows(run_dir):
+    import csv
+    import glob
+    import re
+    out = {}
+    for path in sorted(glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"),
+                                 recursive=True)):
+        for r in csv.DictReader(open(path)):
+            nm = r["Kernel_Name"].replace("void ", "").replace("sla::(anonymous namespace)::", "")
+            nm = nm.replace("sla::", "")
+            m = re.match(r"([\w:]+)(<[^>]*>)?", nm)
+            key = (m.group(1) + (m.group(2) or "")) if m else nm[:48]
+            out.setdefault(key, []).append((float(r["Counter_Value"]), int(r.get("Grid_Size", 0))))
+    return out
+
+
+def summarize_counters(fetch_dir, write_dir):
+    """Turn the two rocprofv3 --pmc runs of --counters-workload (FETCH_SIZE, then
+    WRITE_SIZE, KiB per dispatch) into the traffic summary and the A-step record
+    that the benchmark reports; the 256 MiB copy calibrates both counters."""
+    import re
+    fetch, write = _counter_rows(fetch_dir), _counter_rows(write_dir)
+    copy_kib = 256 * 1024.0
+
+    def calib(rows):
+        vals = [v for k, lst in rows.items() if "copyBuffer" in k for v, g in lst]
+        big = [v for v in vals if v > 0.25 * copy_kib]
+        return copy_kib / statistics.median(big)
+    fs, ws = calib(fetch), calib(write)
+    src_sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    lines = ["| kernel | step | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB (scaled) "
+             "| written MB | total MB |", "|---|---|---|---|---|---|---|---|"]
+    a_rec = None
+    for k in sorted(fetch):
+        m = re.match(r"(sell_step|csr_step|bsell_step|bsr3_step)<double, (\d+),", k)
+        if not m or k not in write:
+            continue
+        mode = int(m.group(2))
+        fk = statistics.fmean(v for v, _ in fetch[k])
+        wk = statistics.fmean(v for v, _ in write[k])
+        rb, wb = fk * 1024 * fs, wk * 1024 * ws
+        lines.append(f"| `{k}` | {STEP_NAMES.get(mode, mode)} | {len(fetch[k])} | {fk:,.1f} | "
+                     f"{wk:,.1f} | {rb / 1e6:.1f} | {wb / 1e6:.1f} | {(rb + wb) / 1e6:.1f} |")
+        if mode == 2:
+            a_rec = {"kernel": k, "workload": "poisson3d_128 fp64", "kernel_source_sha256": src_sha,
+                     "fetch_scale": fs, "write_scale": ws, "fetch_kib_raw": fk,
+                     "write_kib_raw": wk, "fetch_bytes": rb, "write_bytes": wb,
+                     "bytes_per_launch": rb + wb, "launches_averaged": len(fetch[k])}
+    cmd = "rocprofv3 --pmc {c} --output-format csv -d {d} -o pmc -- python -u bench.py " \
+          "--counters-workload"
+    md = ["# HBM traffic per launch of the PCG kernels, 3D Poisson 128^3 fp64", "",
+          "Counters from two rocprofv3 runs of the benchmark's counter workload (a 256 MiB",
+          "copy for calibration, then 20 forward and 20 adjoint PCG iterations on the",
+          "128^3 input).  FETCH_SIZE and WRITE_SIZE are KiB per dispatch; the copy of",
+          f"known size (256 MiB read, 256 MiB written) calibrates fetched bytes by {fs:.3f}",
+          f"and written bytes by {ws:.3f}.", "",
+          "Commands (from the repository root, `export TMPDIR=/tmp`):", "",
+          "    " + cmd.format(c="FETCH_SIZE", d=fetch_dir),
+          "    " + cmd.format(c="WRITE_SIZE", d=write_dir),
+          f"    python bench.py --counter-summary {fetch_dir} {write_dir}", "", *lines, "",
+          f"Kernel source: preconditioned_cg_solver_amd/csrc/solver.hip sha256 {src_sha}.", ""]
+    with open(os.path.join(ROOT, "profiles", "traffic_poisson3d_128.md"), "w") as f:
+        f.write("\n".join(md))
+    if a_rec is not None:
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(a_rec, f, indent=1)
+    print("\n".join(lines))
+
+
+def _short_kernel(nm):
+    import re
+    nm = nm.replace("void ", "").replace("sla::(anonymous namespace)::", "").replace("sla::", "")
+    m = re.match(r"([\w:]+)(<[^>]*>)?", nm)
+    nm = (m.group(1) + (m.group(2) or "")) if m else nm
+    return nm if len(nm) <= 48 else nm[:45] + "..."
+
+
+def summarize_trace(trace_dir, bench_json=None):
+    """Per-kernel table of a rocprofv3 --kernel-trace --stats run of this benchmark
+    (profiles/kernel_trace_poisson3d_128.md); launches under 10 us are the
+    early-out launches of a batch that ends after convergence."""
+    import csv
+    import glob
+    recs = []
+    for path in sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"),
+                                 recursive=True)):
+        for r in csv.DictReader(open(path)):
+            t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+            recs.append((t0, t1, _short_kernel(r["Kernel_Name"])))
+    recs.sort()
+    total = sum(t1 - t0 for t0, t1, _ in recs)
+    by = {}
+    for t0, t1, k in recs:
+        by.setdefault(k, []).append((t1 - t0) / 1e3)
+    rows = sorted(by.items(), key=lambda kv: -sum(kv[1]))
+    lines = ["| kernel | calls | avg us (all) | % time | working launches | avg us (working) |",
+             "|---|---|---|---|---|---|"]
+    for k, d in rows[:16]:
+        w = [v for v in d if v > 10.0] or d
+        lines.append(f"| `{k}` | {len(d)} | {statistics.fmean(d):.2f} | "
+                     f"{100 * sum(d) * 1e3 / total:.2f} | {len(w)} | {statistics.fmean(w):.2f} |")
+    step = [(t0, t1) for t0, t1, k in recs
+            if k.split("<")[0] in ("sell_step", "csr_step", "bsell_step", "bsr3_step")
+            and (t1 - t0) > 10000]
+    gaps = sorted(max(0, b0 - a1) / 1e3 for (a0, a1), (b0, b1) in zip(step, step[1:]))
+    a_key = next((k for k, _ in rows if k.startswith("sell_step<double, 2,")), None)
+    a_work = [v for v in by.get(a_key, []) if v > 10.0]
+    cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d {d} -o bench -- "
+           "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline").format(d=trace_dir)
+    md = ["# Kernel trace of bench.py, 3D Poisson 128^3 fp64 (PCG + factorised SPAI, "
+          "forward + adjoint)", "", "Command (from the repository root, `export TMPDIR=/tmp`):",
+          "", "    " + cmd, f"    python bench.py --trace-summary {trace_dir}"
+          + (f" {bench_json}" if bench_json else ""), "",
+          "`sell_step<T, MODE, NT, I16, U>`: MODE 2 = A step, 4 = G^T step, 6 = G step",
+          "(1, 3, 5: their first-iteration / start-up forms, 0 = plain SpMV); NT =",
+          "non-temporal matrix stream; I16 = 16-bit column offsets; U = slots per load",
+          "batch.  \"calls\" counts every launch, including the launches of a batch that",
+          "return at once after convergence; \"working launches\" keeps those over 10 us",
+          "(the ones that did the product).", "", *lines, ""]
+    if a_work:
+        md.append(f"The A step (`{a_key}`) averages {statistics.fmean(a_work):.2f} us per "
+                  "working launch here.")
+    if bench_json:
+        rec = json.loads(open(bench_json).read().strip().splitlines()[-1])
+        md.append("bench.py's own HIP-event measurement of the same kernel over its timed steps "
+                  f"gave {rec['roofline']['avg_launch_us']:.2f} us (`roofline.avg_launch_us` of a "
+                  "bench run of the same tree).")
+    if gaps:
+        md += ["", f"Gaps between consecutive working step kernels: median "
+               f"{statistics.median(gaps):.2f} us, mean {statistics.fmean(gaps):.2f} us, 90th "
+               f"percentile {gaps[int(0.9 * len(gaps))]:.2f} us over {len(gaps)} boundaries."]
+    with open(os.path.join(ROOT, "profiles", "kernel_trace_poisson3d_128.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+    print("\n".join(lines))
+
+
+def cpu_baseline(p, w, min_seconds):
+    """The oracle on the host cores doing the benchmark's step minus the handle
+    set-up: the full forward PCG solve and the full adjoint solve on the same
+    input, repeated until at least min_seconds have passed (at most 20 times)."""
     import oracle
-    log(f"cpu oracle: forward PCG capped at {iters} iterations, {oracle.num_threads()} threads")
+    log(f"cpu oracle: forward + adjoint solves for >= {min_seconds:.0f} s, "
+        f"{oracle.num_threads()} threads")
+    its, reps = 0, 0
     t0 = time.perf_counter()
-    x, st, it, rr = oracle.pcg(p.A, p.G, p.eps, p.b, p.rtol, iters)
+    while reps < 20 and (reps == 0 or time.perf_counter() - t0 < min_seconds):
+        x, st, it, _ = oracle.pcg(p.A, p.G, p.eps, p.b, p.rtol, p.maxit)
+        _, _, st2, it2, _ = oracle.adjoint(p.A, p.G, p.eps, x, w, p.rtol, p.maxit)
+        its += it + it2
+        reps += 1
     dt = time.perf_counter() - t0
-    return {"value": it / dt, "unit": "iters/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"forward PCG on the same 128^3 input capped at {iters} iterations "
-                      f"({it} done, includes the oracle's G^T build), {dt:.1f} s"}
+    return {"value": its / dt, "unit": "iters/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{reps} x (full forward PCG solve + full adjoint solve with dL/dA) on "
+                      f"the same {round(p.A.n ** (1 / 3))}^3 input, {its} iterations in {dt:.1f} s (each solve "
+                      "includes the oracle's own G^T build)"}
 
 
 def main():
@@ -98,13 +249,26 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--size", type=int, default=128, help="grid edge of the 3D Poisson workload")
-    ap.add_argument("--cpu-iters", type=int, default=300)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum host time of the CPU-oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--spmv-reps", type=int, default=50)
     ap.add_argument("--counters-workload", action="store_true",
                     help="short run for rocprofv3 --pmc: a 256 MiB copy (calibration) and "
                          "20 forward + 20 adjoint PCG iterations on the same input")
+    ap.add_argument("--counter-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the traffic summary under profiles/ from two rocprofv3 "
+                         "--pmc runs of --counters-workload (no GPU needed)")
+    ap.add_argument("--trace-summary", nargs="+", metavar="DIR",
+                    help="write profiles/kernel_trace_poisson3d_128.md from a rocprofv3 "
+                         "--kernel-trace --stats run (and optionally a saved bench JSON line)")
     args = ap.parse_args()
+    if args.trace_summary:
+        summarize_trace(*args.trace_summary[:2])
+        return
+    if args.counter_summary:
+        summarize_counters(*args.counter_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this solver runs on a single MI355X "
               "(multi-GPU sharding is described in the design notes, not built); "
@@ -276,7 +440,7 @@ def main():
         "setup_ms": statistics.median(setup) * 1e3,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(p, args.cpu_iters)
+        result["cpu_baseline"] = cpu_baseline(p, p.w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
