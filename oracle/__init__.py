@@ -69,6 +69,12 @@ def _bind(lib):
     lib.orc_lanczos_tridiag.restype = ctypes.c_int
     lib.orc_sai_loss.argtypes = [i64, ctypes.c_int, vp, vp, vp, vp, vp, vp, dbl, vp, i32, dbl, vp]
     lib.orc_sai_loss.restype = ctypes.c_int
+    lib.orc_pcg_multi.argtypes = [i64, ctypes.c_int, vp, vp, vp, vp, vp, vp, dbl, vp, vp, i32, dbl,
+                                  i32, vp, vp, vp]
+    lib.orc_pcg_multi.restype = ctypes.c_int
+    lib.orc_adjoint_multi.argtypes = [i64, ctypes.c_int, vp, vp, vp, vp, vp, vp, dbl, vp, vp, vp,
+                                      vp, i32, dbl, i32, vp, vp, vp]
+    lib.orc_adjoint_multi.restype = ctypes.c_int
     lib.orc_num_threads.argtypes = []
     lib.orc_num_threads.restype = ctypes.c_int
     lib.orc_dot_block.argtypes = []
@@ -228,6 +234,45 @@ def kaporin_number(eigs: np.ndarray) -> float:
     eigenvalues over their geometric mean (1 for a multiple of I)."""
     e = np.asarray(eigs, dtype=np.float64)
     return float(np.mean(e) / np.exp(np.mean(np.log(e))))
+
+
+def pcg_multi(A, G, eps: float, B: np.ndarray, rtol: float, maxit: int, lib=None):
+    """k right-hand sides (columns of the n x k array B): returns (X n x k,
+    overall status, per-column iterations, relres, status)."""
+    lib = lib or load()
+    arp, aci, av = _mat(A)
+    grp, gci, gv = _mat(G)
+    B = _c(B, np.float64)
+    k = B.shape[1]
+    X = np.empty_like(B)
+    it = np.zeros(k, dtype=np.int32)
+    rr = np.zeros(k, dtype=np.float64)
+    sts = np.zeros(k, dtype=np.int32)
+    st = lib.orc_pcg_multi(A.n_block_rows, A.block_dim, _p(arp), _p(aci), _p(av), _p(grp),
+                           _p(gci), _p(gv), float(eps), _p(B), _p(X), k, float(rtol), int(maxit),
+                           _p(it), _p(rr), _p(sts))
+    return X, int(st), it, rr, sts
+
+
+def adjoint_multi(A, G, eps: float, X: np.ndarray, GX: np.ndarray, rtol: float, maxit: int,
+                  lib=None):
+    """Adjoint of k solves sharing A: returns (Lambda = dL/dB (n x k), dL/dvals
+    summed over the solves, overall status, per-column iterations, relres, status)."""
+    lib = lib or load()
+    arp, aci, av = _mat(A)
+    grp, gci, gv = _mat(G)
+    X = _c(X, np.float64)
+    GX = _c(GX, np.float64)
+    k = X.shape[1]
+    lam = np.empty_like(X)
+    gval = np.empty(av.shape[0], dtype=np.float64)
+    it = np.zeros(k, dtype=np.int32)
+    rr = np.zeros(k, dtype=np.float64)
+    sts = np.zeros(k, dtype=np.int32)
+    st = lib.orc_adjoint_multi(A.n_block_rows, A.block_dim, _p(arp), _p(aci), _p(av), _p(grp),
+                               _p(gci), _p(gv), float(eps), _p(X), _p(GX), _p(lam), _p(gval), k,
+                               float(rtol), int(maxit), _p(it), _p(rr), _p(sts))
+    return lam, gval, int(st), it, rr, sts
 
 
 def pattern_grad(A, lam: np.ndarray, x: np.ndarray, lib=None) -> np.ndarray:

@@ -347,6 +347,72 @@ int orc_adjoint(int64_t nbr, int bs,
     return st;
 }
 
+/* Several right-hand sides sharing A and G.  b and x are n x k and row-major:
+ * b[i * k + j] is entry i of right-hand side j.  Every column is its own PCG
+ * solve (the k solves share only the operators), with its own iteration count,
+ * residual and status in iters[j], relres[j], status[j].  Returns the first
+ * negative column status, else ORC_NOT_CONVERGED if any column did not
+ * converge, else ORC_OK. */
+int orc_pcg_multi(int64_t nbr, int bs,
+                  const int32_t *a_row_ptr, const int32_t *a_col, const double *a_val,
+                  const int32_t *g_row_ptr, const int32_t *g_col, const double *g_val,
+                  double eps, const double *b, double *x, int32_t k, double rtol, int32_t maxit,
+                  int32_t *iters, double *relres, int32_t *status)
+{
+    const int64_t n = nbr * bs;
+    if (nbr < 0 || bs < 1 || k < 1) return ORC_ERR_ARG;
+    const size_t vb = (size_t)(n > 0 ? n : 1) * sizeof(double);
+    double *bj = (double *)malloc(vb), *xj = (double *)malloc(vb);
+    int ret = ORC_OK;
+    if (!bj || !xj) { ret = ORC_ERR_NOMEM; goto out; }
+    for (int32_t j = 0; j < k; ++j) {
+        for (int64_t i = 0; i < n; ++i) bj[i] = b[i * k + j];
+        status[j] = orc_pcg(nbr, bs, a_row_ptr, a_col, a_val, g_row_ptr, g_col, g_val, eps, bj,
+                            xj, rtol, maxit, &iters[j], &relres[j]);
+        for (int64_t i = 0; i < n; ++i) x[i * k + j] = xj[i];
+        if (status[j] < 0 && ret >= 0) ret = status[j];
+        else if (status[j] == ORC_NOT_CONVERGED && ret == ORC_OK) ret = ORC_NOT_CONVERGED;
+    }
+out:
+    free(bj); free(xj);
+    return ret;
+}
+
+/* Adjoint of k solves X = A^-1 B sharing A, for a loss L(X) with gradient
+ * gx = dL/dX (n x k, row-major like x): column j of lam solves
+ * A^T lam_j = gx_j, dL/dB = lam, and since every solve uses the same A, its
+ * gradient is the sum over the solves of -lam_j[i] x_j[c] at every stored
+ * scalar (i, c), accumulated over j = 0 .. k-1 in that order. */
+int orc_adjoint_multi(int64_t nbr, int bs,
+                      const int32_t *a_row_ptr, const int32_t *a_col, const double *a_val,
+                      const int32_t *g_row_ptr, const int32_t *g_col, const double *g_val,
+                      double eps, const double *x, const double *gx, double *lam,
+                      double *grad_val, int32_t k, double rtol, int32_t maxit, int32_t *iters,
+                      double *relres, int32_t *status)
+{
+    const int64_t n = nbr * bs;
+    const int64_t bb = (int64_t)bs * bs;
+    if (nbr < 0 || bs < 1 || k < 1) return ORC_ERR_ARG;
+    int ret = orc_pcg_multi(nbr, bs, a_row_ptr, a_col, a_val, g_row_ptr, g_col, g_val, eps, gx,
+                            lam, k, rtol, maxit, iters, relres, status);
+    if (ret < 0) return ret;
+    (void)n;
+#pragma omp parallel for schedule(static)
+    for (int64_t I = 0; I < nbr; ++I) {
+        for (int64_t e = a_row_ptr[I]; e < a_row_ptr[I + 1]; ++e) {
+            const int64_t J = a_col[e];
+            for (int r = 0; r < bs; ++r)
+                for (int c = 0; c < bs; ++c) {
+                    double g = 0.0;
+                    for (int32_t j = 0; j < k; ++j)
+                        g = g - lam[(I * bs + r) * k + j] * x[(J * bs + c) * k + j];
+                    grad_val[e * bb + (int64_t)r * bs + c] = g;
+                }
+        }
+    }
+    return ret;
+}
+
 int orc_dot_block(void) { return ORC_DOT_BLOCK; }
 
 /* Threads the OpenMP row loops use (1 when built without OpenMP). */

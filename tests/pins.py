@@ -511,9 +511,71 @@ def pin_sai_loss(lib):
     assert np.allclose(est, np.sum((E @ W) ** 2, axis=0), rtol=1e-12), "probe terms"
 
 
+# ---------------------------------------------------------------------------
+# several right-hand sides
+# ---------------------------------------------------------------------------
+
+def pin_pcg_multi(lib):
+    """k columns solved together equal dense solves column by column; with a
+    scalar preconditioner a column that is one Laplacian eigenvector converges
+    in one iteration, a mix of four in at most five, while a random column
+    takes many; a zero column is solved at once with x = 0."""
+    N = 16
+    A = I.poisson2d(N)
+    G = scalar_factor(A.n, 0.7)
+    rng = np.random.default_rng(71)
+    B = np.zeros((A.n, 4))
+    B[:, 0] = lap2d_eig(N, 3, 5)[0]
+    for (k, l) in ((1, 1), (2, 3), (7, 7), (12, 4)):
+        B[:, 1] += lap2d_eig(N, k, l)[0] * (1 + k + l)
+    B[:, 2] = rng.standard_normal(A.n)
+    X, st, it, rr, sts = oracle.pcg_multi(A, G, 3e-3, B, 1e-12, 500, lib=lib)
+    assert st == oracle.OK and list(sts) == [0, 0, 0, 0], (st, sts)
+    assert it[0] == 1 and 2 <= it[1] <= 5 and it[2] > 20 and it[3] == 0, it
+    Xd = sla.cho_solve(sla.cho_factor(A.to_dense()), B)
+    for j in range(4):
+        assert rel(X[:, j], Xd[:, j]) <= 1e-10, ("column", j)
+    assert rr[3] == 0.0 and np.all(rr[:3] <= 1e-12)
+    p = I.make_problem(3, size=2)                      # BSR
+    Bb = rng.standard_normal((p.A.n, 3))
+    Xb, st, it, _, _ = oracle.pcg_multi(p.A, p.G, p.eps, Bb, 1e-14, 500, lib=lib)
+    assert st == oracle.OK
+    assert rel(Xb, sla.cho_solve(sla.cho_factor(p.A.to_dense()), Bb)) <= 1e-11, "bsr multi"
+
+
+def pin_adjoint_multi(lib):
+    """Loss L = sum_j <W_j, X_j> over three solves sharing A: dL/dB = A^-T W
+    (dense), and the pattern gradient's directional derivative matches central
+    differences of L along a symmetric direction on A's pattern."""
+    rng = np.random.default_rng(72)
+    p = I.make_problem(0, size=12)
+    k = 3
+    B = rng.standard_normal((p.A.n, k))
+    W = rng.standard_normal((p.A.n, k))
+    X, st, _, _, _ = oracle.pcg_multi(p.A, p.G, p.eps, B, 1e-13, 5000, lib=lib)
+    lam, gval, st2, _, _, _ = oracle.adjoint_multi(p.A, p.G, p.eps, X, W, 1e-13, 5000, lib=lib)
+    assert st == oracle.OK and st2 == oracle.OK
+    Ad = p.A.to_dense()
+    assert rel(lam, np.linalg.solve(Ad.T, W)) <= 1e-10, "dL/dB"
+    S = p.A.to_scipy().copy()
+    S.data = rng.standard_normal(S.nnz)
+    S = ((S + S.T) * 0.5).tocsr()
+    S.sort_indices()
+    assert np.array_equal(S.indices, p.A.col_idx)
+    h = 1e-6
+
+    def L(sign):
+        Ah = Ad + sign * h * S.toarray()
+        return float(np.sum(W * np.linalg.solve(Ah, B)))
+    fd = (L(+1) - L(-1)) / (2 * h)
+    an = float(gval @ S.data)
+    assert abs(fd - an) <= 1e-6 * abs(an), ("directional", fd, an)
+
+
 ALL_PINS = [
     pin_spmv_bruteforce, pin_spmv_bsr_dense, pin_spmv_eigenpairs, pin_transpose, pin_precond,
     pin_pcg_cholesky, pin_pcg_galerkin, pin_pcg_eigen, pin_pcg_cg_equivalence, pin_pcg_scipy,
     pin_pcg_edges, pin_adjoint_fd_b, pin_adjoint_fd_entries, pin_adjoint_directional,
     pin_adjoint_identities, pin_lanczos_diagonal, pin_lanczos_spectrum, pin_sai_loss,
+    pin_pcg_multi, pin_adjoint_multi,
 ]

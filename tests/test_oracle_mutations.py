@@ -59,6 +59,18 @@ MUTATIONS = [
      "        orc_spmv(nbr, bs, a_row_ptr, a_col, a_val, wj, z);\n"
      "        st = orc_precond_apply(nbr, bs, g_row_ptr, g_col, g_val, eps, z, y);\n"
      "        if (st != ORC_OK) goto out;"),
+    ("multi-RHS reads b column-major",
+     "for (int64_t i = 0; i < n; ++i) bj[i] = b[i * k + j];",
+     "for (int64_t i = 0; i < n; ++i) bj[i] = b[j * n + i];"),
+    ("multi-RHS writes every column to the first",
+     "for (int64_t i = 0; i < n; ++i) x[i * k + j] = xj[i];",
+     "for (int64_t i = 0; i < n; ++i) x[i * k] = xj[i];"),
+    ("multi-RHS adjoint gradient keeps only the last solve",
+     "g = g - lam[(I * bs + r) * k + j] * x[(J * bs + c) * k + j];",
+     "g = -lam[(I * bs + r) * k + j] * x[(J * bs + c) * k + j];"),
+    ("multi-RHS adjoint gradient pairs lambda and x of different solves",
+     "g = g - lam[(I * bs + r) * k + j] * x[(J * bs + c) * k + j];",
+     "g = g - lam[(I * bs + r) * k + j] * x[(J * bs + c) * k + (k - 1 - j)];"),
 ]
 
 
