@@ -185,6 +185,57 @@ sla_status sla_pcg_adjoint(sla_mat_t A, sla_mat_t G, double eps, const void *d_x
                            sla_solve_info *info);
 
 /*
+ * Several right-hand sides sharing A (and G).  Multi-vectors are n x k
+ * row-major device arrays in A's dtype: entry i of column c at [i * k + c],
+ * so one gathered matrix column brings in the k values of that row at once.
+ * Batched same-pattern solves are the batched use of "torch-sla"
+ * (Significance); the k solves share only the operators.
+ */
+
+/* Y = A X (sla_spmm) or Y = A^T X (sla_spmm_t, needs SLA_BUILD_TRANSPOSE) for
+ * k >= 0 columns.  Asynchronous on `stream`.  SLA_ERR_INVALID_ARG on a NULL
+ * handle, k < 0, or NULL / aliased X and Y. */
+sla_status sla_spmm(sla_mat_t A, const void *d_x, void *d_y, int32_t k, void *stream);
+sla_status sla_spmm_t(sla_mat_t A, const void *d_x, void *d_y, int32_t k, void *stream);
+
+/* Device workspace bytes for sla_pcg_solve_multi / sla_pcg_adjoint_multi
+ * with k right-hand sides (k >= 1). */
+sla_status sla_pcg_workspace_size_multi(sla_mat_t A, int32_t k, size_t *bytes);
+
+/*
+ * Solve A X = B for the k >= 1 columns of B with the preconditioner
+ * M^-1 = G G^T + eps I.  Every column is its own PCG solve with the stopping
+ * rule, statuses and results of sla_pcg_solve (column c of X equals the
+ * one-right-hand-side solve of column c of B, to rounding); the columns are
+ * advanced together, up to 8 per pass, so each product streams the matrix
+ * once for all of them.  A column that exits is frozen while the others go
+ * on.  info[k] and col_status[k] (host arrays, either may be NULL) receive
+ * each column's record and status.  Returns the first column error if any
+ * column failed (SLA_ERR_BREAKDOWN, SLA_ERR_NONFINITE), else
+ * SLA_NOT_CONVERGED if any column hit maxit, else SLA_OK; X is written for
+ * every column.  Synchronous with respect to the host (returns when done).
+ */
+sla_status sla_pcg_solve_multi(sla_mat_t A, sla_mat_t G, double eps, const void *d_b, void *d_x,
+                               int32_t k, double rtol, int32_t maxit, void *d_work,
+                               size_t work_bytes, void *stream, sla_solve_info *info,
+                               sla_status *col_status);
+
+/*
+ * Adjoint of X = A^-1 B over k solves sharing A, for a loss with gradient
+ * d_grad_x = dL/dX (n x k): d_grad_b = dL/dB solves A^T Lambda = dL/dX column
+ * by column, and d_grad_vals[nnz] = dL/dA on A's pattern, summed over the
+ * solves: -sum_c Lambda[i, c] X[j, c] at every stored scalar (i, j), in A's
+ * storage order ("torch-sla", Technical Summary, Methodology 2, with the
+ * gradients of the k uses of A added).  Statuses as sla_pcg_solve_multi; the
+ * gradient is written unless a column failed.
+ */
+sla_status sla_pcg_adjoint_multi(sla_mat_t A, sla_mat_t G, double eps, const void *d_x,
+                                 const void *d_grad_x, void *d_grad_b, void *d_grad_vals,
+                                 int32_t k, double rtol, int32_t maxit, void *d_work,
+                                 size_t work_bytes, void *stream, sla_solve_info *info,
+                                 sla_status *col_status);
+
+/*
  * Extreme Ritz values of M^-1 A from k steps of PCG: the smallest and largest
  * eigenvalues of the Lanczos tridiagonal built from h_alpha[0..k-1] and
  * h_beta[0..k-2] as recorded by sla_pcg_solve_history (host arrays).  They lie

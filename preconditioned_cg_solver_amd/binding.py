@@ -77,6 +77,13 @@ def _declare(L):
                           st),
         "sla_pcg_adjoint": ([vp, vp, dbl, vp, vp, vp, vp, dbl, i32, vp, sz, vp,
                              ctypes.POINTER(SolveInfo)], st),
+        "sla_spmm": ([vp, vp, vp, i32, vp], st),
+        "sla_spmm_t": ([vp, vp, vp, i32, vp], st),
+        "sla_pcg_workspace_size_multi": ([vp, i32, ctypes.POINTER(sz)], st),
+        "sla_pcg_solve_multi": ([vp, vp, dbl, vp, vp, i32, dbl, i32, vp, sz, vp,
+                                 ctypes.POINTER(SolveInfo), ctypes.POINTER(ctypes.c_int)], st),
+        "sla_pcg_adjoint_multi": ([vp, vp, dbl, vp, vp, vp, vp, i32, dbl, i32, vp, sz, vp,
+                                   ctypes.POINTER(SolveInfo), ctypes.POINTER(ctypes.c_int)], st),
         "sla_lanczos_extremes": ([vp, vp, i32, ctypes.POINTER(dbl), ctypes.POINTER(dbl)], st),
         "sla_sai_loss": ([vp, vp, dbl, vp, i32, dbl, vp, sz, vp, vp], st),
         "sla_pcg_solve_history": ([vp, vp, dbl, vp, vp, dbl, i32, vp, sz, vp, vp, i32, vp,
@@ -322,6 +329,94 @@ def sla_pcg_adjoint(A: Mat, G: Mat, eps: float, x: torch.Tensor, grad_x: torch.T
     if raise_on_error:
         _check(st, allow=(OK, NOT_CONVERGED))
     return grad_b, grad_vals, _info(st, si)
+
+
+# ----- several right-hand sides (n x k row-major device tensors) -----
+
+def _cols(t: torch.Tensor) -> int:
+    if t.dim() != 2 or not t.is_contiguous():
+        raise ValueError("expected a contiguous (n, k) tensor")
+    return t.shape[1]
+
+
+def sla_spmm(A: Mat, X: torch.Tensor, Y: Optional[torch.Tensor] = None,
+             stream=None) -> torch.Tensor:
+    """Y = A X for the k columns of the (n, k) tensor X."""
+    k = _cols(X)
+    if Y is None:
+        Y = torch.empty_like(X)
+    _check(lib().sla_spmm(A.handle, _ptr(X), _ptr(Y), k, _stream(stream)))
+    return Y
+
+
+def sla_spmm_t(A: Mat, X: torch.Tensor, Y: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    k = _cols(X)
+    if Y is None:
+        Y = torch.empty_like(X)
+    _check(lib().sla_spmm_t(A.handle, _ptr(X), _ptr(Y), k, _stream(stream)))
+    return Y
+
+
+def sla_pcg_workspace_size_multi(A: Mat, k: int) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().sla_pcg_workspace_size_multi(A.handle, int(k), ctypes.byref(b)))
+    return b.value
+
+
+def workspace_multi(A: Mat, k: int, device=None) -> torch.Tensor:
+    return torch.empty(max(sla_pcg_workspace_size_multi(A, k), 1), dtype=torch.uint8,
+                       device=device or A.device)
+
+
+def _multi_out(st, infos, cst, k):
+    return [_info(int(cst[c]), infos[c]) for c in range(k)]
+
+
+def sla_pcg_solve_multi(A: Mat, G: Mat, eps: float, B: torch.Tensor,
+                        X: Optional[torch.Tensor] = None, rtol: float = 1e-10, maxit: int = 1000,
+                        work: Optional[torch.Tensor] = None, stream=None,
+                        raise_on_error: bool = True):
+    """Solve A X = B for the k columns of B (n, k) together; returns X and one
+    Info per column (its own status, iterations and residual)."""
+    k = _cols(B)
+    if X is None:
+        X = torch.empty_like(B)
+    if work is None:
+        work = workspace_multi(A, k, B.device)
+    infos = (SolveInfo * k)()
+    cst = (ctypes.c_int * k)()
+    st = lib().sla_pcg_solve_multi(A.handle, G.handle, float(eps), _ptr(B), _ptr(X), k,
+                                   float(rtol), int(maxit), _ptr(work), work.numel(),
+                                   _stream(stream), infos, cst)
+    if raise_on_error:
+        _check(st, allow=(OK, NOT_CONVERGED))
+    return X, _multi_out(st, infos, cst, k)
+
+
+def sla_pcg_adjoint_multi(A: Mat, G: Mat, eps: float, X: torch.Tensor, GX: torch.Tensor,
+                          rtol: float = 1e-10, maxit: int = 1000,
+                          GB: Optional[torch.Tensor] = None,
+                          grad_vals: Optional[torch.Tensor] = None,
+                          work: Optional[torch.Tensor] = None, stream=None,
+                          raise_on_error: bool = True):
+    """Adjoint of k solves sharing A: dL/dB = A^-T dL/dX column by column and
+    dL/dA on A's pattern summed over the solves."""
+    k = _cols(X)
+    if GB is None:
+        GB = torch.empty_like(X)
+    if grad_vals is None:
+        grad_vals = torch.empty(A.nnz, dtype=A.dtype, device=X.device)
+    if work is None:
+        work = workspace_multi(A, k, X.device)
+    infos = (SolveInfo * k)()
+    cst = (ctypes.c_int * k)()
+    st = lib().sla_pcg_adjoint_multi(A.handle, G.handle, float(eps), _ptr(X), _ptr(GX), _ptr(GB),
+                                     _ptr(grad_vals), k, float(rtol), int(maxit), _ptr(work),
+                                     work.numel(), _stream(stream), infos, cst)
+    if raise_on_error:
+        _check(st, allow=(OK, NOT_CONVERGED))
+    return GB, grad_vals, _multi_out(st, infos, cst, k)
 
 
 def sla_pattern_grad(A: Mat, lam: torch.Tensor, x: torch.Tensor,

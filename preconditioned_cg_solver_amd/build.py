@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsla.so")
-SOURCES = ["setup.hip", "solver.hip", "spectrum.cpp", "api.cpp"]
+SOURCES = ["setup.hip", "solver.hip", "multi.hip", "host_util.cpp", "spectrum.cpp", "api.cpp"]
 ARCH = os.environ.get("SLA_OFFLOAD_ARCH", "gfx950")
 
 

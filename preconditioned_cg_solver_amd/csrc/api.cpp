@@ -53,14 +53,12 @@ sla_status alloc_long_scratch(sla_mat* m, MatView& v, int part_slot, int cnt_slo
   return SLA_OK;
 }
 
-// SELL-64 copies are built unless SLA_SELL=0 (then every CSR product uses
-// the LDS-tile engine).
+// Sliced copies (SELL-64, BSR sliced ELL) are built unless SLA_SELL=0 at
+// handle creation (then CSR products use the LDS-tile engine and BSR the
+// block-row engine).
 bool sell_enabled() {
-  static const bool on = [] {
-    const char* e = getenv("SLA_SELL");
-    return !(e && e[0] == '0');
-  }();
-  return on;
+  const char* e = getenv("SLA_SELL");
+  return !(e && e[0] == '0');
 }
 
 bool check(bool ok, const char* msg) {
@@ -153,8 +151,10 @@ sla_status create_common(sla_mat_t* out, int64_t nbr, int64_t nnzb, int32_t bs, 
   return SLA_OK;
 }
 
+// k = 0: one right-hand side; k >= 1: the multi-RHS solver's workspace.
 sla_status check_solve(sla_mat_t A, sla_mat_t G, double eps, const void* b, const void* x,
-                       double rtol, int32_t maxit, const void* work, size_t work_bytes) {
+                       double rtol, int32_t maxit, const void* work, size_t work_bytes,
+                       int32_t k = 0) {
   if (!check(A && G, "matrix handle is NULL")) return SLA_ERR_INVALID_ARG;
   if (!check(A->nbr == G->nbr && A->bs == G->bs && A->dtype == G->dtype,
              "A and G differ in size, block size or dtype"))
@@ -168,6 +168,12 @@ sla_status check_solve(sla_mat_t A, sla_mat_t G, double eps, const void* b, cons
   if (A->n() == 0) return SLA_OK;
   if (!check(b && x, "vector pointer is NULL")) return SLA_ERR_INVALID_ARG;
   if (!check(b != x, "x must not alias b")) return SLA_ERR_INVALID_ARG;
+  if (k > 0) {
+    if (!check(work != nullptr && work_bytes >= workspace_bytes_multi(*A, k),
+               "workspace too small"))
+      return SLA_ERR_INVALID_ARG;
+    return SLA_OK;
+  }
   if (!check(work != nullptr && work_bytes >= workspace_bytes(*A), "workspace too small"))
     return SLA_ERR_INVALID_ARG;
   const int64_t slots = (int64_t)std::max<int64_t>(A->fwd.nlong_rows, A->nnz() / kLdsCap + 1);
@@ -356,6 +362,79 @@ sla_status sla_pcg_adjoint(sla_mat_t A, sla_mat_t G, double eps, const void* d_x
   st = sla::pcg_solve(*A, *G, eps, d_grad_x, d_grad_b, rtol, maxit, d_work, work_bytes, s, info);
   if (st < 0) return st;
   sla_status gs = sla::pattern_grad(*A, d_grad_b, d_x, d_grad_vals, s);
+  if (gs != SLA_OK) return gs;
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  return st;
+}
+
+sla_status sla_spmm(sla_mat_t A, const void* d_x, void* d_y, int32_t k, void* stream) {
+  if (!A || k < 0) {
+    set_error("matrix handle is NULL or k < 0");
+    return SLA_ERR_INVALID_ARG;
+  }
+  if (A->n() > 0 && k > 0 && (!d_x || !d_y || d_x == d_y)) {
+    set_error("X and Y must be distinct non-NULL device arrays");
+    return SLA_ERR_INVALID_ARG;
+  }
+  return sla::spmm(*A, false, d_x, d_y, k, (hipStream_t)stream);
+}
+
+sla_status sla_spmm_t(sla_mat_t A, const void* d_x, void* d_y, int32_t k, void* stream) {
+  if (!A || !A->has_t || k < 0) {
+    set_error("handle is NULL, has no transpose (create with SLA_BUILD_TRANSPOSE) or k < 0");
+    return SLA_ERR_INVALID_ARG;
+  }
+  if (A->n() > 0 && k > 0 && (!d_x || !d_y || d_x == d_y)) {
+    set_error("X and Y must be distinct non-NULL device arrays");
+    return SLA_ERR_INVALID_ARG;
+  }
+  return sla::spmm(*A, true, d_x, d_y, k, (hipStream_t)stream);
+}
+
+sla_status sla_pcg_workspace_size_multi(sla_mat_t A, int32_t k, size_t* bytes) {
+  if (!A || !bytes || k < 1) {
+    set_error("NULL argument or k < 1");
+    return SLA_ERR_INVALID_ARG;
+  }
+  *bytes = workspace_bytes_multi(*A, k);
+  return SLA_OK;
+}
+
+sla_status sla_pcg_solve_multi(sla_mat_t A, sla_mat_t G, double eps, const void* d_b, void* d_x,
+                               int32_t k, double rtol, int32_t maxit, void* d_work,
+                               size_t work_bytes, void* stream, sla_solve_info* info,
+                               sla_status* col_status) {
+  if (k < 1) {
+    set_error("k must be >= 1");
+    return SLA_ERR_INVALID_ARG;
+  }
+  sla_status st = check_solve(A, G, eps, d_b, d_x, rtol, maxit, d_work, work_bytes, k);
+  if (st != SLA_OK) return st;
+  return sla::pcg_solve_multi(*A, *G, eps, d_b, d_x, k, rtol, maxit, d_work, (hipStream_t)stream,
+                              info, col_status);
+}
+
+sla_status sla_pcg_adjoint_multi(sla_mat_t A, sla_mat_t G, double eps, const void* d_x,
+                                 const void* d_grad_x, void* d_grad_b, void* d_grad_vals,
+                                 int32_t k, double rtol, int32_t maxit, void* d_work,
+                                 size_t work_bytes, void* stream, sla_solve_info* info,
+                                 sla_status* col_status) {
+  if (k < 1) {
+    set_error("k must be >= 1");
+    return SLA_ERR_INVALID_ARG;
+  }
+  sla_status st = check_solve(A, G, eps, d_grad_x, d_grad_b, rtol, maxit, d_work, work_bytes, k);
+  if (st != SLA_OK) return st;
+  if (A->n() > 0 && (!d_x || (A->nnzb > 0 && !d_grad_vals))) {
+    set_error("x or grad_vals is NULL");
+    return SLA_ERR_INVALID_ARG;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  st = sla::pcg_solve_multi(*A, *G, eps, d_grad_x, d_grad_b, k, rtol, maxit, d_work, s, info,
+                            col_status);
+  if (st < 0) return st;
+  sla_status gs = sla::pattern_grad_multi(*A, d_grad_b, d_x, k, d_grad_vals, s);
   if (gs != SLA_OK) return gs;
   hipError_t e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");

@@ -42,6 +42,8 @@ constexpr int kBsrLanes = 32;
 constexpr int kBsrTileRows = kWG / kBsrLanes;
 // Ring sizes of the per-iteration scalars kept on the device.
 constexpr int kRing = 4;
+// Right-hand sides advanced together by one pass of the multi-RHS solver.
+constexpr int kMaxRhs = 8;
 
 // Tile descriptor (CSR engine).
 //   kind 0: rows [a, b) staged through LDS, 2^c lanes per row; their
@@ -170,6 +172,25 @@ sla_status pattern_grad(const sla_mat& A, const void* lam, const void* x, void* 
                         hipStream_t s);
 sla_status sai_loss(const sla_mat& A, const sla_mat& G, double eps, const void* probes,
                     int32_t nprobe, double scale, void* work, double* out, hipStream_t s);
+
+// Several right-hand sides (multi.hip).
+size_t workspace_bytes_multi(const sla_mat& A, int k);
+sla_status spmm(const sla_mat& A, bool transpose, const void* x, void* y, int k, hipStream_t s);
+sla_status pcg_solve_multi(const sla_mat& A, const sla_mat& G, double eps, const void* b, void* x,
+                           int k, double rtol, int maxit, void* work, hipStream_t s,
+                           sla_solve_info* info, sla_status* cst);
+sla_status pattern_grad_multi(const sla_mat& A, const void* lam, const void* x, int k, void* grad,
+                              hipStream_t s);
+
+// Host helpers (host_util.cpp).
+size_t align_up(size_t v);
+int max_grid();
+int step_grid(int ntiles);
+int view_tiles(const sla_mat& m, const MatView& v);
+size_t matrix_bytes(const sla_mat& m);
+size_t mall_budget();
+hipEvent_t timing_event();
+int batch_iters();
 
 // Spectrum of the Lanczos tridiagonal (spectrum.cpp, host only).
 sla_status lanczos_extremes(const double* alpha, const double* beta, int32_t k, double* lmin,

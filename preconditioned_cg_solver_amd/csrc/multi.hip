@@ -1,0 +1,843 @@
+// Several right-hand sides sharing one A and one G: K PCG solves advanced in
+// lock step so that every product streams its matrix once for all K columns.
+//
+// Vectors are row-major n x K blocks: entry i of column c sits at i * ld + c,
+// so a gathered column index j brings in K contiguous values (one 16-64 byte
+// load) for the one matrix value read.  Every column keeps its own scalars
+// (alpha, beta, rho, ||r||) and its own exit: a column that converges or
+// breaks down is frozen (its x no longer changes) while the others go on, and
+// the solve ends when every column has exited.  Each column's arithmetic is
+// the single-right-hand-side iteration's, so column c gives the result of an
+// independent solve for b_c (the solves share only the operators).
+//
+// One iteration k is three kernels, as for one right-hand side:
+//   A step   Q = A P_k with P_k = Z + beta P_{k-1} formed on the fly (stored
+//            for owned rows) and partials of sigma_c = p_c . q_c;
+//   G^T step T = G^T R_k with R_k = R_{k-1} - alpha Q formed on the fly
+//            (stored), X += alpha P_k on owned rows, partials of ||r_c||^2;
+//   G step   Z = G T + eps R_k, partials of rho_c = r_c . z_c.
+// (With one right-hand side the x update rides in the next A step; here it
+// is applied in the G^T step, so a column that exits leaves x final.)
+//
+// Method: "Learning Sparse Approximate Inverse Preconditioners for CG Solvers
+// on GPUs" (Approach) for M^-1 = G G^T + eps I; several same-pattern systems
+// solved together is the batched use of "torch-sla" (Significance, batched
+// solves); adjoint gradients add over the solves because A is shared
+// ("torch-sla", Technical Summary, Methodology 2).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <deque>
+#include <mutex>
+
+#include "device_util.h"
+#include "internal.h"
+
+namespace sla {
+namespace {
+
+struct MState {
+  int done;  // every column has exited
+  int pad[3];
+  int exit_kind[kMaxRhs];
+  int exit_iter[kMaxRhs];
+  double bb[kMaxRhs];
+  double rr[kMaxRhs];
+  double rho[kRing][kMaxRhs];
+  double alpha[kRing][kMaxRhs];
+};
+
+enum MMode {
+  MM_PLAIN = 0,  // Y = M X
+  MM_A1 = 1,     // A step of iteration 1 (P_1 = Z_0)
+  MM_A = 2,      // A step of iteration k >= 2
+  MM_GT = 3,     // G^T step of iteration k >= 1
+  MM_G0 = 4,     // G step of the start-up (checks ||b_c||)
+  MM_G = 5       // G step of iteration k >= 1 (checks convergence)
+};
+
+template <typename T>
+struct MArgs {
+  const int32_t* rp;
+  const int32_t* ci;
+  const T* v;
+  const T* sv;
+  const int32_t* sc;
+  const int16_t* sd;
+  const int32_t* soff;
+  int nslices;
+  int ntiles;
+  int nbr;
+  int n;
+  int ld;        // row stride of the gathered / owned vectors
+  const T* in0;  // gathered: X, Z (A step), R_{k-1} (G^T step), T (G step)
+  const T* in1;  // gathered second operand: P_{k-1} (A step), Q (G^T step)
+  T* own;        // owned-row output: P_k, R_k
+  T* y;          // product output
+  const T* rv;   // R_k (G step)
+  const T* pv;   // P_k (G^T step)
+  T* xv;         // solution columns, row stride ldx
+  int ldx;
+  double eps;
+  const double* pin;  // producer partials, [npin][K]
+  int npin;
+  double* pout;  // this kernel's partials, [gridDim.x][K]
+  MState* st;
+  int k;
+  int maxit;
+  double rtol;
+};
+
+template <typename T, int K>
+struct MCoef {
+  T c[K];   // gather coefficient (beta, -alpha or 0)
+  T c2[K];  // alpha for the x update
+  bool act[K];
+};
+
+template <int K>
+__device__ __forceinline__ void block_sum_k(double (&v)[K], double* red) {
+#pragma unroll
+  for (int c = 0; c < K; ++c) v[c] = wave_sum(v[c]);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+    for (int c = 0; c < K; ++c) red[(threadIdx.x >> 6) * K + c] = v[c];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < K; ++c) {
+    double s = red[c];
+#pragma unroll
+    for (int q = 1; q < kWaves; ++q) s += red[q * K + c];
+    v[c] = s;
+  }
+}
+
+template <int K>
+__device__ __forceinline__ void sum_partials_k(const double* __restrict__ p, int np,
+                                               double (&out)[K], double* red) {
+#pragma unroll
+  for (int c = 0; c < K; ++c) out[c] = 0.0;
+  for (int i = threadIdx.x; i < np; i += kWG) {
+#pragma unroll
+    for (int c = 0; c < K; ++c) out[c] += p[(size_t)i * K + c];
+  }
+  block_sum_k<K>(out, red);
+}
+
+__device__ __forceinline__ void col_exit(MState* st, int c, int kind, int k) {
+  st->exit_kind[c] = kind;
+  st->exit_iter[c] = k;
+}
+
+// Kernel start: the done check, then every workgroup sums the producer's
+// partials in the same order and takes the same per-column decisions; the
+// lead thread records them.  Returns false when the kernel has no work.
+template <typename T, int MODE, int K>
+__device__ __forceinline__ bool mprologue(const MArgs<T>& a, MCoef<T, K>& cf, double* red,
+                                          int* s_flag) {
+#pragma unroll
+  for (int c = 0; c < K; ++c) {
+    cf.c[c] = T(0);
+    cf.c2[c] = T(0);
+    cf.act[c] = true;
+  }
+  if constexpr (MODE == MM_PLAIN) {
+    return true;
+  } else {
+    if (threadIdx.x == 0)
+      *s_flag = __hip_atomic_load(&a.st->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (*s_flag) return false;
+    const bool lead = blockIdx.x == 0 && threadIdx.x == 0;
+    const int k = a.k;
+    double s[K];
+    sum_partials_k<K>(a.pin, a.npin, s, red);
+    int live = 0;
+#pragma unroll
+    for (int c = 0; c < K; ++c) {
+      bool act;
+      if constexpr (MODE == MM_G0) {
+        const double bb = s[c];
+        int ex = EX_NONE;
+        if (!isfinite(bb)) ex = EX_NONFINITE_B;
+        else if (bb == 0.0) ex = EX_BZERO;
+        else if (a.maxit == 0) ex = EX_MAXIT0;
+        if (lead) {
+          a.st->bb[c] = bb;
+          a.st->rr[c] = bb;
+          if (ex != EX_NONE) col_exit(a.st, c, ex, 0);
+        }
+        act = ex == EX_NONE;
+      } else {
+        act = a.st->exit_kind[c] == EX_NONE;
+        if (act) {
+          if constexpr (MODE == MM_A1 || MODE == MM_A) {
+            const double rho = s[c];  // rho_{k-1}
+            if (!(rho > 0.0) || !isfinite(rho)) {
+              if (lead) col_exit(a.st, c, EX_BREAK_RHO, k);
+              act = false;
+            } else {
+              if (lead) a.st->rho[(k - 1) % kRing][c] = rho;
+              if constexpr (MODE == MM_A) cf.c[c] = T(rho / a.st->rho[(k - 2) % kRing][c]);
+            }
+          } else if constexpr (MODE == MM_GT) {
+            const double sigma = s[c];
+            if (!(sigma > 0.0) || !isfinite(sigma)) {
+              if (lead) col_exit(a.st, c, EX_BREAK_SIGMA, k);
+              act = false;
+            } else {
+              const double alpha = a.st->rho[(k - 1) % kRing][c] / sigma;
+              if (lead) a.st->alpha[k % kRing][c] = alpha;
+              cf.c[c] = T(-alpha);
+              cf.c2[c] = T(alpha);
+            }
+          } else {  // MM_G
+            const double rr = s[c];
+            const double rnorm = sqrt(rr), bnorm = sqrt(a.st->bb[c]);
+            int ex = EX_NONE;
+            if (!isfinite(rnorm)) ex = EX_BREAK_RR;
+            else if (rnorm <= a.rtol * bnorm) ex = EX_CONV;
+            else if (k == a.maxit) ex = EX_MAXIT;
+            if (lead) {
+              a.st->rr[c] = rr;
+              if (ex != EX_NONE) col_exit(a.st, c, ex, k);
+            }
+            act = ex == EX_NONE;
+          }
+        }
+      }
+      cf.act[c] = act;
+      live += act ? 1 : 0;
+    }
+    if (live == 0) {
+      if (lead) a.st->done = 1;
+      return false;
+    }
+    return true;
+  }
+}
+
+// Gathered value of column c at vector row j.
+template <typename T, int MODE, int K>
+__device__ __forceinline__ T mgat(const MArgs<T>& a, size_t base, int c, const MCoef<T, K>& cf) {
+  if constexpr (MODE == MM_A || MODE == MM_GT) return fma(cf.c[c], a.in1[base + c], a.in0[base + c]);
+  else return a.in0[base + c];
+}
+
+template <typename T, int K>
+struct MOwn {
+  T a[K], b[K], p[K], x[K];
+};
+
+template <typename T, int MODE, int K>
+__device__ __forceinline__ void mown_load(const MArgs<T>& a, int i, MOwn<T, K>& o) {
+  const size_t r = (size_t)i * a.ld;
+#pragma unroll
+  for (int c = 0; c < K; ++c) {
+    if constexpr (MODE == MM_A1) {
+      o.a[c] = a.in0[r + c];
+    } else if constexpr (MODE == MM_A) {
+      o.a[c] = a.in1[r + c];
+      o.b[c] = a.in0[r + c];
+    } else if constexpr (MODE == MM_GT) {
+      o.a[c] = a.in1[r + c];
+      o.b[c] = a.in0[r + c];
+      o.p[c] = a.pv[r + c];
+      o.x[c] = a.xv[(size_t)i * a.ldx + c];
+    } else if constexpr (MODE == MM_G0 || MODE == MM_G) {
+      o.a[c] = a.rv[r + c];
+    }
+  }
+}
+
+// Row epilogue: stores and the row's contributions to the K dot products.
+template <typename T, int MODE, int K>
+__device__ __forceinline__ void mepi(const MArgs<T>& a, int i, const T (&acc)[K],
+                                     const MCoef<T, K>& cf, const MOwn<T, K>& o,
+                                     double (&dot)[K]) {
+  const size_t r = (size_t)i * a.ld;
+#pragma unroll
+  for (int c = 0; c < K; ++c) {
+    if constexpr (MODE == MM_PLAIN) {
+      a.y[r + c] = acc[c];
+    } else if constexpr (MODE == MM_A1 || MODE == MM_A) {
+      const T pn = MODE == MM_A1 ? o.a[c] : fma(cf.c[c], o.a[c], o.b[c]);
+      a.own[r + c] = pn;
+      a.y[r + c] = acc[c];
+      dot[c] += (double)pn * (double)acc[c];
+    } else if constexpr (MODE == MM_GT) {
+      const T rn = fma(cf.c[c], o.a[c], o.b[c]);
+      a.own[r + c] = rn;
+      a.y[r + c] = acc[c];
+      if (cf.act[c]) a.xv[(size_t)i * a.ldx + c] = fma(cf.c2[c], o.p[c], o.x[c]);
+      dot[c] += (double)rn * (double)rn;
+    } else {
+      const T zv = fma(T(a.eps), o.a[c], acc[c]);
+      a.y[r + c] = zv;
+      dot[c] += (double)o.a[c] * (double)zv;
+    }
+  }
+}
+
+template <typename T, int MODE, int K>
+__device__ __forceinline__ void mfinish(const MArgs<T>& a, double (&dot)[K], double* red) {
+  if constexpr (MODE != MM_PLAIN) {
+    block_sum_k<K>(dot, red);
+    if (threadIdx.x < K) {
+      double v = dot[0];
+#pragma unroll
+      for (int c = 1; c < K; ++c)
+        if (threadIdx.x == c) v = dot[c];
+      a.pout[(size_t)blockIdx.x * K + threadIdx.x] = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// SELL-64 engine (CSR whose rows qualified for the sliced layout): one
+// wavefront per slice of 64 rows, lane l owns row 64 s + l, every value and
+// column word of a wavefront is one contiguous access; each slot gathers the
+// K entries of its column.
+// ---------------------------------------------------------------------------
+
+template <typename T, int MODE, int K, bool I16, int U>
+__global__ __launch_bounds__(kWG) void msell_step(MArgs<T> a) {
+  __shared__ double s_red[kWaves * K];
+  __shared__ int s_flag;
+  const int lane = threadIdx.x & (kSlice - 1), wv = threadIdx.x / kSlice;
+  int t0, t1, step;
+  tile_range(a.ntiles, t0, t1, step);
+  MCoef<T, K> cf;
+  if (!mprologue<T, MODE, K>(a, cf, s_red, &s_flag)) return;
+  double dot[K];
+#pragma unroll
+  for (int c = 0; c < K; ++c) dot[c] = 0.0;
+  for (int t = t0; t < t1; t += step) {
+    const int sl = t * kWaves + wv;
+    if (sl >= a.nslices) continue;
+    const int off = a.soff[sl], w = (a.soff[sl + 1] - off) / kSlice;
+    const int row = sl * kSlice + lane;
+    const bool live = row < a.n;
+    MOwn<T, K> o;
+    mown_load<T, MODE, K>(a, live ? row : 0, o);
+    T acc[K];
+#pragma unroll
+    for (int c = 0; c < K; ++c) acc[c] = T(0);
+    for (int j = 0; j < w; j += U) {
+      T vv[U];
+      int col[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        // loads past the slice end stay inside the arrays' padding tail
+        const int idx = off + (j + u) * kSlice + lane;
+        vv[u] = ld_stream<true>(a.sv + idx);
+        int raw;
+        if constexpr (I16) raw = ld_stream<true>(a.sd + idx);
+        else raw = ld_stream<true>(a.sc + idx);
+        const bool in = j + u < w;
+        if constexpr (I16) col[u] = (in && raw != kPad16) ? row + raw : -1;
+        else col[u] = in ? raw : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool ok = col[u] >= 0;
+        const size_t base = (size_t)(ok ? col[u] : 0) * a.ld;
+        const T vu = ok ? vv[u] : T(0);
+#pragma unroll
+        for (int c = 0; c < K; ++c) {
+          const T g = mgat<T, MODE, K>(a, base, c, cf);
+          acc[c] = fma(vu, ok ? g : T(0), acc[c]);
+        }
+      }
+    }
+    if (live) mepi<T, MODE, K>(a, row, acc, cf, o, dot);
+  }
+  mfinish<T, MODE, K>(a, dot, s_red);
+}
+
+// ---------------------------------------------------------------------------
+// Sliced-ELL engine for 3x3 BSR: one wavefront per slice of 21 block rows,
+// lane l owns scalar row 3 (21 s + l / 3) + l % 3 and reads its three values
+// of every block; each block gathers 3 K contiguous entries.
+// ---------------------------------------------------------------------------
+
+template <typename T, int MODE, int K, int U>
+__global__ __launch_bounds__(kWG) void mbsell_step(MArgs<T> a) {
+  __shared__ double s_red[kWaves * K];
+  __shared__ int s_flag;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int li = min(lane / 3, kBSlice - 1), r = lane - 3 * (lane / 3);
+  const bool lane_live = lane < 3 * kBSlice;
+  int t0, t1, step;
+  tile_range(a.ntiles, t0, t1, step);
+  MCoef<T, K> cf;
+  if (!mprologue<T, MODE, K>(a, cf, s_red, &s_flag)) return;
+  double dot[K];
+#pragma unroll
+  for (int c = 0; c < K; ++c) dot[c] = 0.0;
+  for (int t = t0; t < t1; t += step) {
+    const int sl = t * kWaves + wv;
+    if (sl >= a.nslices) continue;
+    const int off = a.soff[sl], w = (a.soff[sl + 1] - off) / kBSlice;
+    const int brow = sl * kBSlice + li;
+    const bool live = lane_live && brow < a.nbr;
+    const int row = 3 * brow + r;
+    MOwn<T, K> o;
+    mown_load<T, MODE, K>(a, live ? row : 0, o);
+    T acc[K];
+#pragma unroll
+    for (int c = 0; c < K; ++c) acc[c] = T(0);
+    for (int j = 0; j < w; j += U) {
+      T bv[U][3];
+      int bc[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        // loads past the slice end stay inside the arrays' padding tail
+        const int blk = off + (j + u) * kBSlice + li;
+        bc[u] = ld_stream<true>(a.sc + blk);
+#pragma unroll
+        for (int e = 0; e < 3; ++e) bv[u][e] = ld_stream<true>(a.sv + (size_t)blk * 9 + 3 * r + e);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool ok = j + u < w && bc[u] >= 0;
+#pragma unroll
+        for (int e = 0; e < 3; ++e) {
+          const size_t base = (size_t)(ok ? 3 * bc[u] + e : 0) * a.ld;
+          const T vu = ok ? bv[u][e] : T(0);
+#pragma unroll
+          for (int c = 0; c < K; ++c) {
+            const T g = mgat<T, MODE, K>(a, base, c, cf);
+            acc[c] = fma(vu, ok ? g : T(0), acc[c]);
+          }
+        }
+      }
+    }
+    if (live) mepi<T, MODE, K>(a, row, acc, cf, o, dot);
+  }
+  mfinish<T, MODE, K>(a, dot, s_red);
+}
+
+// ---------------------------------------------------------------------------
+// Row engine for every other matrix (CSR without the sliced layout, BSR
+// without it): one lane per scalar row walks the row's entries in storage
+// order.  Not tuned: long rows serialise on one lane.
+// ---------------------------------------------------------------------------
+
+template <typename T, int MODE, int K, int BS>
+__global__ __launch_bounds__(kWG) void mrow_step(MArgs<T> a) {
+  __shared__ double s_red[kWaves * K];
+  __shared__ int s_flag;
+  MCoef<T, K> cf;
+  if (!mprologue<T, MODE, K>(a, cf, s_red, &s_flag)) return;
+  double dot[K];
+#pragma unroll
+  for (int c = 0; c < K; ++c) dot[c] = 0.0;
+  for (int i = blockIdx.x * kWG + threadIdx.x; i < a.n; i += gridDim.x * kWG) {
+    MOwn<T, K> o;
+    mown_load<T, MODE, K>(a, i, o);
+    T acc[K];
+#pragma unroll
+    for (int c = 0; c < K; ++c) acc[c] = T(0);
+    const int I = BS == 1 ? i : i / 3, r = BS == 1 ? 0 : i - 3 * (i / 3);
+    const int e0 = a.rp[I], e1 = a.rp[I + 1];
+    for (int e = e0; e < e1; ++e) {
+      const int J = a.ci[e];
+#pragma unroll
+      for (int q = 0; q < BS; ++q) {
+        const T vu = BS == 1 ? a.v[e] : a.v[(size_t)e * 9 + 3 * r + q];
+        const size_t base = (size_t)(BS * J + q) * a.ld;
+#pragma unroll
+        for (int c = 0; c < K; ++c) acc[c] = fma(vu, mgat<T, MODE, K>(a, base, c, cf), acc[c]);
+      }
+    }
+    mepi<T, MODE, K>(a, i, acc, cf, o, dot);
+  }
+  mfinish<T, MODE, K>(a, dot, s_red);
+}
+
+// Start-up: R_0 = B (columns c0 .. c0 + K - 1 of the caller's n x ldb array),
+// X = 0 on the same columns, partials of ||b_c||^2.
+template <typename T, int K>
+__global__ __launch_bounds__(kWG) void minit(const T* __restrict__ b, int ldb, T* __restrict__ r0,
+                                             T* __restrict__ x, int ldx, int n,
+                                             double* __restrict__ pout) {
+  __shared__ double s_red[kWaves * K];
+  double dot[K];
+#pragma unroll
+  for (int c = 0; c < K; ++c) dot[c] = 0.0;
+  for (int i = blockIdx.x * kWG + threadIdx.x; i < n; i += gridDim.x * kWG) {
+#pragma unroll
+    for (int c = 0; c < K; ++c) {
+      const T v = b[(size_t)i * ldb + c];
+      r0[(size_t)i * K + c] = v;
+      x[(size_t)i * ldx + c] = T(0);
+      dot[c] += (double)v * (double)v;
+    }
+  }
+  block_sum_k<K>(dot, s_red);
+  if (threadIdx.x < K) {
+    double v = dot[0];
+#pragma unroll
+    for (int c = 1; c < K; ++c)
+      if (threadIdx.x == c) v = dot[c];
+    pout[(size_t)blockIdx.x * K + threadIdx.x] = v;
+  }
+}
+
+// dL/dA over k solves: g[e] = -sum_c lambda_c[row(e)] x_c[col(e)], the sum
+// taken over c = 0 .. k-1 in order (products rounded before the subtraction).
+// One wavefront per block row; its lanes stride over the row's scalars.
+template <typename T>
+__global__ __launch_bounds__(kWG) void mgrad(const int32_t* __restrict__ rp,
+                                             const int32_t* __restrict__ ci, int nbr, int bs,
+                                             const T* __restrict__ lam,
+                                             const T* __restrict__ x, int k,
+                                             T* __restrict__ g) {
+  const int lane = threadIdx.x & 63;
+  const int bb = bs * bs;
+  for (int I = blockIdx.x * kWaves + (threadIdx.x >> 6); I < nbr; I += gridDim.x * kWaves) {
+    const int e0 = rp[I] * bb, e1 = rp[I + 1] * bb;
+    for (int e = e0 + lane; e < e1; e += 64) {
+      const int kb = e / bb, w = e - kb * bb;
+      const int r = w / bs, cc = w - r * bs;
+      const size_t li = (size_t)(I * bs + r) * k, xi = (size_t)(ci[kb] * bs + cc) * k;
+      T s = T(0);
+      for (int c = 0; c < k; ++c) {
+#pragma clang fp contract(off)
+        s = s - lam[li + c] * x[xi + c];
+      }
+      g[e] = s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+
+template <typename T>
+void fill_mat(MArgs<T>& a, const sla_mat& m, const MatView& v) {
+  a.rp = v.rp;
+  a.ci = v.ci;
+  a.v = (const T*)v.v;
+  a.nbr = (int)m.nbr;
+  a.n = (int)m.n();
+  if (v.sell) {
+    a.sv = (const T*)v.sv;
+    a.sc = v.sd ? nullptr : v.sc;
+    a.sd = v.sd;
+    a.soff = v.soff;
+    a.nslices = v.nslices;
+    a.ntiles = (v.nslices + kWaves - 1) / kWaves;
+  } else {
+    a.ntiles = 0;
+  }
+}
+
+template <typename T, int MODE, int K>
+hipError_t mlaunch(const sla_mat& m, const MatView& v, const MArgs<T>& a, int grid,
+                   hipStream_t s) {
+  const dim3 g(grid), b(kWG);
+  constexpr int U = K >= 8 ? 2 : 4;
+  if (m.bs == 1 && v.sell) {
+    if (v.sd) hipLaunchKernelGGL((msell_step<T, MODE, K, true, U>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((msell_step<T, MODE, K, false, U>), g, b, 0, s, a);
+  } else if (m.bs == 3 && v.sell) {
+    hipLaunchKernelGGL((mbsell_step<T, MODE, K, U>), g, b, 0, s, a);
+  } else if (m.bs == 1) {
+    hipLaunchKernelGGL((mrow_step<T, MODE, K, 1>), g, b, 0, s, a);
+  } else {
+    hipLaunchKernelGGL((mrow_step<T, MODE, K, 3>), g, b, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+int mgrid(const sla_mat& m) {
+  const int rows = (int)std::min<int64_t>(m.n(), (int64_t)1 << 30);
+  int g = std::max(view_tiles(m, m.fwd), (rows + kWG - 1) / kWG);
+  if (m.has_t) g = std::max(g, view_tiles(m, m.tr));
+  return step_grid(g);
+}
+
+// Columns handled per pass: the largest of 8, 4, 2, 1 that fits k.
+int chunk_width(int k) { return k >= 8 ? 8 : k >= 4 ? 4 : k >= 2 ? 2 : 1; }
+
+struct MWork {
+  MState* st;
+  double* psig;
+  double* prr;
+  double* prho;
+  void* vec[7];  // P0 P1 R0 R1 Q T Z, n x K each
+};
+
+MWork mcarve(const sla_mat& A, int kw, void* work) {
+  MWork w;
+  char* p = (char*)work;
+  const size_t es = A.dtype == SLA_F64 ? 8 : 4;
+  w.st = (MState*)p;
+  p += align_up(sizeof(MState));
+  const size_t ps = align_up((size_t)max_grid() * kMaxRhs * sizeof(double));
+  w.psig = (double*)p;
+  p += ps;
+  w.prr = (double*)p;
+  p += ps;
+  w.prho = (double*)p;
+  p += ps;
+  for (int i = 0; i < 7; ++i) {
+    w.vec[i] = p;
+    p += align_up((size_t)A.n() * kw * es);
+  }
+  return w;
+}
+
+std::mutex g_mpoll_mu;
+MState* g_mhost = nullptr;  // 3 polling slots + 1 final record, pinned
+hipEvent_t g_mpoll_ev[3];
+
+sla_status mpoll_init() {
+  if (g_mhost) return SLA_OK;
+  if (hipHostMalloc((void**)&g_mhost, 4 * sizeof(MState), hipHostMallocDefault) != hipSuccess) {
+    g_mhost = nullptr;
+    set_error("hipHostMalloc of the polling slots failed");
+    return SLA_ERR_OOM;
+  }
+  for (auto& e : g_mpoll_ev) SLA_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+  return SLA_OK;
+}
+
+// One pass of K columns: b and x point at the pass's first column of the
+// caller's n x ld arrays.
+template <typename T, int K>
+sla_status mpcg_pass(const sla_mat& A, const sla_mat& G, double eps, const T* b, T* x, int ld,
+                     double rtol, int maxit, const MWork& w, hipStream_t s,
+                     sla_solve_info* info, sla_status* cst) {
+  const int n = (int)A.n();
+  T *P[2] = {(T*)w.vec[0], (T*)w.vec[1]}, *R[2] = {(T*)w.vec[2], (T*)w.vec[3]};
+  T *q = (T*)w.vec[4], *t = (T*)w.vec[5], *z = (T*)w.vec[6];
+  const int grid = std::max(mgrid(A), mgrid(G));
+  SLA_HIP(hipMemsetAsync(w.st, 0, sizeof(MState), s));
+
+  MArgs<T> aA{}, aT{}, aG{};
+  fill_mat(aA, A, A.fwd);
+  fill_mat(aT, G, G.tr);
+  fill_mat(aG, G, G.fwd);
+  for (MArgs<T>* a : {&aA, &aT, &aG}) {
+    a->st = w.st;
+    a->maxit = maxit;
+    a->rtol = rtol;
+    a->eps = eps;
+    a->ld = K;
+    a->xv = x;
+    a->ldx = ld;
+    a->npin = grid;
+  }
+  aA.pin = w.prho;
+  aA.pout = w.psig;
+  aA.in0 = z;
+  aA.y = q;
+  aT.pin = w.psig;
+  aT.pout = w.prr;
+  aT.in1 = q;
+  aT.y = t;
+  aG.pin = w.prr;
+  aG.pout = w.prho;
+  aG.in0 = t;
+  aG.y = z;
+
+  // start-up: R_0 = B, X = 0, ||b_c||^2; T = G^T R_0; Z_0 = G T + eps R_0
+  hipLaunchKernelGGL((minit<T, K>), dim3(grid), dim3(kWG), 0, s, b, ld, R[0], x, ld, n, w.prr);
+  SLA_HIP(hipGetLastError());
+  MArgs<T> a0 = aT;
+  a0.in0 = R[0];
+  SLA_HIP((mlaunch<T, MM_PLAIN, K>(G, G.tr, a0, grid, s)));
+  aG.k = 0;
+  aG.rv = R[0];
+  SLA_HIP((mlaunch<T, MM_G0, K>(G, G.fwd, aG, grid, s)));
+
+  std::unique_lock<std::mutex> lk(g_mpoll_mu);
+  sla_status pst = mpoll_init();
+  if (pst != SLA_OK) return pst;
+  std::deque<int> pend;
+  int next_slot = 0;
+  const int B = batch_iters();
+  int k = 1;
+  bool finished = false;
+  while (!finished) {
+    if (k <= maxit) {
+      const int kend = std::min(maxit, k + B - 1);
+      for (int kk = k; kk <= kend; ++kk) {
+        aA.k = kk;
+        aA.in1 = P[(kk - 1) & 1];
+        aA.own = P[kk & 1];
+        if (kk == 1) SLA_HIP((mlaunch<T, MM_A1, K>(A, A.fwd, aA, grid, s)));
+        else SLA_HIP((mlaunch<T, MM_A, K>(A, A.fwd, aA, grid, s)));
+        aT.k = kk;
+        aT.in0 = R[(kk - 1) & 1];
+        aT.own = R[kk & 1];
+        aT.pv = P[kk & 1];
+        SLA_HIP((mlaunch<T, MM_GT, K>(G, G.tr, aT, grid, s)));
+        aG.k = kk;
+        aG.rv = R[kk & 1];
+        SLA_HIP((mlaunch<T, MM_G, K>(G, G.fwd, aG, grid, s)));
+      }
+      const int slot = next_slot;
+      next_slot = (next_slot + 1) % 3;
+      SLA_HIP(hipMemcpyAsync(&g_mhost[slot], w.st, 16, hipMemcpyDeviceToHost, s));
+      SLA_HIP(hipEventRecord(g_mpoll_ev[slot], s));
+      pend.push_back(slot);
+      k = kend + 1;
+    }
+    if (pend.size() >= 2 || (k > maxit && !pend.empty())) {
+      const int slot = pend.front();
+      pend.pop_front();
+      SLA_HIP(hipEventSynchronize(g_mpoll_ev[slot]));
+      if (g_mhost[slot].done) finished = true;
+    }
+    if (k > maxit && pend.empty()) finished = true;
+  }
+  while (!pend.empty()) {
+    SLA_HIP(hipEventSynchronize(g_mpoll_ev[pend.front()]));
+    pend.pop_front();
+  }
+  MState* hs = &g_mhost[3];
+  SLA_HIP(hipMemcpyAsync(hs, w.st, sizeof(MState), hipMemcpyDeviceToHost, s));
+  SLA_HIP(hipStreamSynchronize(s));
+  const MState fin = *hs;
+  lk.unlock();
+
+  sla_status worst = SLA_OK;
+  for (int c = 0; c < K; ++c) {
+    sla_status st = SLA_OK;
+    int iters = 0, conv = 0;
+    const int e = fin.exit_iter[c];
+    switch (fin.exit_kind[c]) {
+      case EX_CONV: st = SLA_OK; iters = e; conv = 1; break;
+      case EX_BZERO: st = SLA_OK; iters = 0; conv = 1; break;
+      case EX_MAXIT: st = SLA_NOT_CONVERGED; iters = e; break;
+      case EX_MAXIT0: st = SLA_NOT_CONVERGED; iters = 0; break;
+      case EX_BREAK_SIGMA: st = SLA_ERR_BREAKDOWN; iters = e - 1; break;
+      case EX_BREAK_RHO: st = SLA_ERR_BREAKDOWN; iters = e - 1; break;
+      case EX_BREAK_RR: st = SLA_ERR_BREAKDOWN; iters = e; break;
+      case EX_NONFINITE_B: st = SLA_ERR_NONFINITE; iters = 0; break;
+      default:
+        set_error("solver finished without an exit record for a column");
+        return SLA_ERR_HIP;
+    }
+    if (cst) cst[c] = st;
+    if (info) {
+      info[c].iterations = iters;
+      info[c].converged = conv;
+      info[c].bnorm = std::sqrt(fin.bb[c]);
+      info[c].rel_residual = fin.bb[c] > 0 ? std::sqrt(fin.rr[c]) / std::sqrt(fin.bb[c])
+                                           : (fin.exit_kind[c] == EX_BZERO ? 0.0 : 1.0);
+      if (fin.exit_kind[c] == EX_MAXIT0) info[c].rel_residual = 1.0;
+    }
+    if (st < 0 && worst >= 0) worst = st;
+    else if (st == SLA_NOT_CONVERGED && worst == SLA_OK) worst = st;
+  }
+  return worst;
+}
+
+template <typename T>
+sla_status mpcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, T* x, int k,
+                     double rtol, int maxit, void* work, hipStream_t s, sla_solve_info* info,
+                     sla_status* cst) {
+  const MWork w = mcarve(A, chunk_width(k), work);
+  sla_status worst = SLA_OK;
+  for (int c0 = 0; c0 < k;) {
+    const int kw = chunk_width(k - c0);
+    sla_status st;
+    sla_solve_info* ci = info ? info + c0 : nullptr;
+    sla_status* cs = cst ? cst + c0 : nullptr;
+    switch (kw) {
+      case 8: st = mpcg_pass<T, 8>(A, G, eps, b + c0, x + c0, k, rtol, maxit, w, s, ci, cs); break;
+      case 4: st = mpcg_pass<T, 4>(A, G, eps, b + c0, x + c0, k, rtol, maxit, w, s, ci, cs); break;
+      case 2: st = mpcg_pass<T, 2>(A, G, eps, b + c0, x + c0, k, rtol, maxit, w, s, ci, cs); break;
+      default: st = mpcg_pass<T, 1>(A, G, eps, b + c0, x + c0, k, rtol, maxit, w, s, ci, cs); break;
+    }
+    if (st == SLA_ERR_HIP || st == SLA_ERR_OOM) return st;
+    if (st < 0 && worst >= 0) worst = st;
+    else if (st == SLA_NOT_CONVERGED && worst == SLA_OK) worst = st;
+    c0 += kw;
+  }
+  return worst;
+}
+
+template <typename T, int K>
+hipError_t spmm_pass(const sla_mat& A, bool transpose, const T* x, T* y, int ld, hipStream_t s) {
+  const MatView& v = transpose ? A.tr : A.fwd;
+  MArgs<T> a{};
+  fill_mat(a, A, v);
+  a.ld = ld;
+  a.in0 = x;
+  a.y = y;
+  return mlaunch<T, MM_PLAIN, K>(A, v, a, mgrid(A), s);
+}
+
+template <typename T>
+sla_status spmm_impl(const sla_mat& A, bool transpose, const T* x, T* y, int k, hipStream_t s) {
+  for (int c0 = 0; c0 < k;) {
+    const int kw = chunk_width(k - c0);
+    switch (kw) {
+      case 8: SLA_HIP((spmm_pass<T, 8>(A, transpose, x + c0, y + c0, k, s))); break;
+      case 4: SLA_HIP((spmm_pass<T, 4>(A, transpose, x + c0, y + c0, k, s))); break;
+      case 2: SLA_HIP((spmm_pass<T, 2>(A, transpose, x + c0, y + c0, k, s))); break;
+      default: SLA_HIP((spmm_pass<T, 1>(A, transpose, x + c0, y + c0, k, s))); break;
+    }
+    c0 += kw;
+  }
+  return SLA_OK;
+}
+
+}  // namespace
+
+size_t workspace_bytes_multi(const sla_mat& A, int k) {
+  const size_t es = A.dtype == SLA_F64 ? 8 : 4;
+  return align_up(sizeof(MState)) + 3 * align_up((size_t)max_grid() * kMaxRhs * sizeof(double)) +
+         7 * align_up((size_t)A.n() * chunk_width(k) * es);
+}
+
+sla_status spmm(const sla_mat& A, bool transpose, const void* x, void* y, int k, hipStream_t s) {
+  if (A.n() == 0 || k == 0) return SLA_OK;
+  if (A.dtype == SLA_F64) return spmm_impl<double>(A, transpose, (const double*)x, (double*)y, k, s);
+  return spmm_impl<float>(A, transpose, (const float*)x, (float*)y, k, s);
+}
+
+sla_status pcg_solve_multi(const sla_mat& A, const sla_mat& G, double eps, const void* b, void* x,
+                           int k, double rtol, int maxit, void* work, hipStream_t s,
+                           sla_solve_info* info, sla_status* cst) {
+  if (A.n() == 0) {
+    for (int c = 0; c < k; ++c) {
+      if (info) info[c] = sla_solve_info{0, 1, 0.0, 0.0};
+      if (cst) cst[c] = SLA_OK;
+    }
+    return SLA_OK;
+  }
+  if (A.dtype == SLA_F64)
+    return mpcg_impl<double>(A, G, eps, (const double*)b, (double*)x, k, rtol, maxit, work, s,
+                             info, cst);
+  return mpcg_impl<float>(A, G, eps, (const float*)b, (float*)x, k, rtol, maxit, work, s, info,
+                          cst);
+}
+
+sla_status pattern_grad_multi(const sla_mat& A, const void* lam, const void* x, int k, void* grad,
+                              hipStream_t s) {
+  if (A.nnzb == 0) return SLA_OK;
+  const int grid = (int)std::min<int64_t>((A.nbr + kWaves - 1) / kWaves, 65536);
+  if (A.dtype == SLA_F64)
+    hipLaunchKernelGGL(mgrad<double>, dim3(grid), dim3(kWG), 0, s, A.fwd.rp, A.fwd.ci,
+                       (int)A.nbr, (int)A.bs, (const double*)lam, (const double*)x, k,
+                       (double*)grad);
+  else
+    hipLaunchKernelGGL(mgrad<float>, dim3(grid), dim3(kWG), 0, s, A.fwd.rp, A.fwd.ci, (int)A.nbr,
+                       (int)A.bs, (const float*)lam, (const float*)x, k, (float*)grad);
+  SLA_HIP(hipGetLastError());
+  return SLA_OK;
+}
+
+}  // namespace sla

@@ -37,6 +37,7 @@
 #include <vector>
 
 #include "internal.h"
+#include "device_util.h"
 
 namespace sla {
 namespace {
@@ -95,34 +96,6 @@ struct Coef {
   T c;
   T c2;
 };
-
-// ---------------------------------------------------------------------------
-// Reductions (deterministic: fixed association order)
-// ---------------------------------------------------------------------------
-
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
-// Sum over the workgroup; every thread gets lane 0 / wave order's value.
-__device__ __forceinline__ double block_sum(double v, double* red) {
-  v = wave_sum(v);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  double s = red[0];
-#pragma unroll
-  for (int q = 1; q < kWaves; ++q) s += red[q];
-  return s;
-}
-
-__device__ __forceinline__ double sum_partials(const double* __restrict__ p, int np, double* red) {
-  double s = 0.0;
-  for (int i = threadIdx.x; i < np; i += kWG) s += p[i];
-  return block_sum(s, red);
-}
 
 __device__ __forceinline__ void take_exit(SolverState* st, int kind, int k) {
   st->exit_kind = kind;
@@ -333,24 +306,6 @@ __device__ __forceinline__ double epi(const StepArgs<T>& a, int i, T acc, const 
   }
 }
 
-// XCD-aware tile assignment: workgroups are dispatched round-robin over the
-// 8 XCDs, so workgroup b runs on XCD b % 8.  Give each XCD a contiguous eighth
-// of the tiles and let its workgroups stride through it, so neighbouring rows
-// (and the vector entries they gather) stay in one XCD's L2.
-__device__ __forceinline__ void tile_range(int ntiles, int& t0, int& t1, int& step) {
-  const int G = gridDim.x, b = blockIdx.x;
-  if (G >= 8 && (G & 7) == 0) {
-    const int x = b & 7, slot = b >> 3;
-    t0 = (int)(((long long)ntiles * x) >> 3) + slot;
-    t1 = (int)(((long long)ntiles * (x + 1)) >> 3);
-    step = G >> 3;
-  } else {
-    t0 = b;
-    t1 = ntiles;
-    step = G;
-  }
-}
-
 template <typename T>
 __device__ __forceinline__ T shfl_xor_t(T v, int m) {
   return __shfl_xor(v, m, 64);
@@ -360,17 +315,6 @@ __device__ __forceinline__ T shfl_xor_t(T v, int m) {
 #define SLA_ROW_BATCH 4
 #endif
 
-
-// Matrix streams (values, column indices, row pointers) are read once per
-// product.  With NT they are loaded non-temporally: they do not displace the
-// gathered vector entries from L2, and they are not allocated in the 256 MB
-// last-level Infinity Cache (MALL), which is then left to the operator the
-// host chose to keep resident there across iterations.
-template <bool NT, typename U>
-__device__ __forceinline__ U ld_stream(const U* p) {
-  if constexpr (NT) return __builtin_nontemporal_load(p);
-  else return *p;
-}
 
 // Software pipelining of the LDS tiles: the next tile's row pointers,
 // values and columns are loaded into registers (all loads of a thread in
@@ -975,30 +919,6 @@ __global__ __launch_bounds__(kWG) void bsr3_grad(const int32_t* __restrict__ rp,
 // Host side
 // ---------------------------------------------------------------------------
 
-constexpr size_t kAlign = 256;
-size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
-
-int max_grid() {
-  const int g = device_info().max_grid;
-  return g > 0 ? g : 2048;
-}
-
-// Grid of a step kernel over `ntiles` tiles: at most the resident capacity,
-// a multiple of 8 (one share per XCD) when large enough.
-int step_grid(int ntiles) {
-  int g = std::min(std::max(ntiles, 1), max_grid());
-  if (g >= 8) g &= ~7;
-  return std::max(g, 1);
-}
-
-// Work items of a product over one orientation: SELL slices grouped by
-// workgroup (one per wavefront), LDS tiles, or BSR block-row tiles.
-int view_tiles(const sla_mat& m, const MatView& v) {
-  if (m.bs != 1 && v.sell) return (v.nslices + kWaves - 1) / kWaves;
-  if (m.bs != 1) return (int)((m.nbr + kBsrTileRows - 1) / kBsrTileRows);
-  if (v.sell) return (v.nslices + kWaves - 1) / kWaves;
-  return v.ntiles;
-}
 
 template <typename T>
 void fill_matrix(StepArgs<T>& a, const sla_mat& m, const MatView& v, double* long_part,
@@ -1062,18 +982,6 @@ hipError_t launch_step(const sla_mat& m, const StepArgs<T>& a, int grid, hipStre
 struct MallPlan {
   bool nt_a, nt_g;
 };
-size_t matrix_bytes(const sla_mat& m) {
-  const size_t es = m.dtype == SLA_F64 ? 8 : 4;
-  return (size_t)m.nnz() * es + (size_t)m.nnzb * 4 + (size_t)(m.nbr + 1) * 4;
-}
-size_t mall_budget() {
-  static size_t b = [] {
-    const char* e = getenv("SLA_MALL_BUDGET_MB");
-    const long v = e ? atol(e) : 208;
-    return (size_t)std::max(0L, v) << 20;
-  }();
-  return b;
-}
 MallPlan mall_plan(const sla_mat& A, const sla_mat& G) {
   const size_t a = matrix_bytes(A), g = matrix_bytes(G);
   const size_t vecs = 8 * (size_t)A.n() * (A.dtype == SLA_F64 ? 8 : 4);
@@ -1112,15 +1020,6 @@ struct ProfClass {
 std::mutex g_prof_mu;
 std::atomic<int> g_prof_mask{0};
 ProfClass g_prof[4];
-
-// Events used only for timing: no system-scope fence when recorded, so the
-// bracketed kernel is not slowed by cache write-back and invalidation.
-hipEvent_t timing_event() {
-  hipEvent_t e = nullptr;
-  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) == hipSuccess) return e;
-  if (hipEventCreate(&e) == hipSuccess) return e;
-  return nullptr;
-}
 
 struct EventPair {
   hipEvent_t a, b;
@@ -1195,15 +1094,6 @@ sla_status poll_init() {
   for (auto& e : g_poll_ev) SLA_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
   g_poll_ready = true;
   return SLA_OK;
-}
-
-int batch_iters() {
-  static int b = [] {
-    const char* e = getenv("SLA_BATCH_ITERS");
-    int v = e ? atoi(e) : 16;
-    return std::max(1, std::min(v, 4096));
-  }();
-  return b;
 }
 
 struct Work {

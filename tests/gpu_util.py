@@ -73,6 +73,22 @@ def oracle_self_sensitivity(A, G, eps, b, rtol, maxit, seed=0):
     return rel(x2, x1), abs(r2 - r1) / max(abs(r1), 1e-300)
 
 
+def oracle_spread(A, G, eps, b, rtol, maxit, nsamp=6):
+    """The oracle's own spread under one-ulp perturbations of b: (fewest and
+    most iterations, largest relative change of x).  On systems whose residual
+    stagnates near rtol the stopping iteration is decided by rounding; this is
+    the yardstick for an implementation whose rounding differs."""
+    import oracle
+    x0, _, it0, _ = oracle.pcg(A, G, eps, b, rtol, maxit)
+    its, dx = [it0], 0.0
+    for s in range(nsamp):
+        b2 = b * (1.0 + 1e-16 * np.random.default_rng(s).standard_normal(b.shape))
+        x2, _, it2, _ = oracle.pcg(A, G, eps, b2, rtol, maxit)
+        its.append(it2)
+        dx = max(dx, rel(x2, x0))
+    return min(its), max(its), dx
+
+
 def copy_device_ints(ptr: int, count: int) -> np.ndarray:
     """Copy `count` int32 from a raw device pointer owned by the library."""
     out = torch.empty(count, dtype=torch.int32, device=DEV)
@@ -102,3 +118,40 @@ def _memcpy_d2d(dst: int, src: int, nbytes: int):
     torch.cuda.synchronize()
     rc = _hip.hipMemcpy(ctypes.c_void_p(dst), ctypes.c_void_p(src), nbytes, 3)
     assert rc == 0, f"hipMemcpy failed: {rc}"
+
+
+# Seeded problems shared by the GPU tests, built once per process.
+_cache = {}
+
+
+def problem(key):
+    if key not in _cache:
+        if key == "c0":
+            p = I.make_problem(0)
+        elif key == "c1":
+            p = I.make_problem(1)
+        elif key == "c2":
+            p = I.make_problem(2)
+        elif key == "c3":
+            p = I.make_problem(3)
+        elif key == "poisson2d_37":
+            p = I.make_problem(0, size=37)
+        elif key == "poisson3d_13":
+            p = I.make_problem(2, size=13)
+        elif key == "bsr_elastic_6":
+            p = I.make_problem(3, size=6)
+        elif key == "irregular_long_rows":
+            A = I.random_spd_csr(12000, np.random.default_rng(8), max_deg=6, long_rows=5,
+                                 long_deg=9000)
+            G = I.spai_factor(A, np.random.default_rng(9))
+            b = np.random.default_rng(10).standard_normal(A.n)
+            p = I.Problem("irregular_long_rows", -1, A, G, b, 3e-3, 1e-10, 5000, "dot",
+                          np.random.default_rng(11).standard_normal(A.n))
+        elif key == "powerlaw_20k":
+            p = I.make_problem(4, size=20000)
+        elif key == "heat2d_64":
+            p = I.make_problem(1, size=64)
+        else:
+            raise KeyError(key)
+        _cache[key] = p
+    return _cache[key]

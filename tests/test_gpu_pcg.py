@@ -13,43 +13,10 @@ import oracle
 from preconditioned_cg_solver_amd import autograd as AG
 from preconditioned_cg_solver_amd import binding as B
 from preconditioned_cg_solver_amd import inputs as I
-from gpu_util import DEV, create, host, iters_close, oracle_self_sensitivity, rel, say, tdev
+from gpu_util import (DEV, create, host, iters_close, oracle_self_sensitivity, problem, rel,
+                      say, tdev)
 
 pytestmark = pytest.mark.gpu
-
-_cache = {}
-
-
-def problem(key):
-    if key not in _cache:
-        if key == "c0":
-            p = I.make_problem(0)
-        elif key == "c1":
-            p = I.make_problem(1)
-        elif key == "c2":
-            p = I.make_problem(2)
-        elif key == "c3":
-            p = I.make_problem(3)
-        elif key == "poisson2d_37":
-            p = I.make_problem(0, size=37)
-        elif key == "poisson3d_13":
-            p = I.make_problem(2, size=13)
-        elif key == "bsr_elastic_6":
-            p = I.make_problem(3, size=6)
-        elif key == "irregular_long_rows":
-            A = I.random_spd_csr(12000, np.random.default_rng(8), max_deg=6, long_rows=5,
-                                 long_deg=9000)
-            G = I.spai_factor(A, np.random.default_rng(9))
-            b = np.random.default_rng(10).standard_normal(A.n)
-            p = I.Problem("irregular_long_rows", -1, A, G, b, 3e-3, 1e-10, 5000, "dot",
-                          np.random.default_rng(11).standard_normal(A.n))
-        elif key == "powerlaw_20k":
-            p = I.make_problem(4, size=20000)
-        else:
-            raise KeyError(key)
-        _cache[key] = p
-    return _cache[key]
-
 
 def handles(p, dtype="f64"):
     return create(p.A, dtype=dtype), create(p.G, transpose=True, dtype=dtype)

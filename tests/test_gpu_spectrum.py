@@ -16,30 +16,9 @@ import torch
 import oracle
 from preconditioned_cg_solver_amd import binding as B
 from preconditioned_cg_solver_amd import inputs as I
-from gpu_util import create, host, iters_close, rel, say, tdev
+from gpu_util import create, host, iters_close, problem, rel, say, tdev
 
 pytestmark = pytest.mark.gpu
-
-_cache = {}
-
-
-def problem(key):
-    if key not in _cache:
-        if key == "c0":
-            p = I.make_problem(0)
-        elif key == "poisson3d_13":
-            p = I.make_problem(2, size=13)
-        elif key == "bsr_elastic_6":
-            p = I.make_problem(3, size=6)
-        elif key == "powerlaw_20k":
-            p = I.make_problem(4, size=20000)
-        elif key == "heat2d_64":
-            p = I.make_problem(1, size=64)
-        else:
-            raise KeyError(key)
-        _cache[key] = p
-    return _cache[key]
-
 
 KEYS = ["c0", "poisson3d_13", "bsr_elastic_6", "powerlaw_20k"]
 
