@@ -55,7 +55,9 @@ enum MMode {
   MM_A = 2,      // A step of iteration k >= 2
   MM_GT = 3,     // G^T step of iteration k >= 1
   MM_G0 = 4,     // G step of the start-up (checks ||b_c||)
-  MM_G = 5       // G step of iteration k >= 1 (checks convergence)
+  MM_G = 5,      // G step of iteration k >= 1 (checks convergence)
+  MM_AU = 6,     // separate form: Q = A P_k on a stored P_k, sigma partials
+  MM_GTU = 7     // separate form: T = G^T R_k on a stored R_k
 };
 
 template <typename T>
@@ -152,6 +154,7 @@ __device__ __forceinline__ bool mprologue(const MArgs<T>& a, MCoef<T, K>& cf, do
       *s_flag = __hip_atomic_load(&a.st->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (*s_flag) return false;
+    if constexpr (MODE == MM_AU || MODE == MM_GTU) return true;
     const bool lead = blockIdx.x == 0 && threadIdx.x == 0;
     const int k = a.k;
     double s[K];
@@ -238,7 +241,7 @@ __device__ __forceinline__ void mown_load(const MArgs<T>& a, int i, MOwn<T, K>& 
   const size_t r = (size_t)i * a.ld;
 #pragma unroll
   for (int c = 0; c < K; ++c) {
-    if constexpr (MODE == MM_A1) {
+    if constexpr (MODE == MM_A1 || MODE == MM_AU) {
       o.a[c] = a.in0[r + c];
     } else if constexpr (MODE == MM_A) {
       o.a[c] = a.in1[r + c];
@@ -262,8 +265,11 @@ __device__ __forceinline__ void mepi(const MArgs<T>& a, int i, const T (&acc)[K]
   const size_t r = (size_t)i * a.ld;
 #pragma unroll
   for (int c = 0; c < K; ++c) {
-    if constexpr (MODE == MM_PLAIN) {
+    if constexpr (MODE == MM_PLAIN || MODE == MM_GTU) {
       a.y[r + c] = acc[c];
+    } else if constexpr (MODE == MM_AU) {
+      a.y[r + c] = acc[c];
+      dot[c] += (double)o.a[c] * (double)acc[c];
     } else if constexpr (MODE == MM_A1 || MODE == MM_A) {
       const T pn = MODE == MM_A1 ? o.a[c] : fma(cf.c[c], o.a[c], o.b[c]);
       a.own[r + c] = pn;
@@ -285,7 +291,7 @@ __device__ __forceinline__ void mepi(const MArgs<T>& a, int i, const T (&acc)[K]
 
 template <typename T, int MODE, int K>
 __device__ __forceinline__ void mfinish(const MArgs<T>& a, double (&dot)[K], double* red) {
-  if constexpr (MODE != MM_PLAIN) {
+  if constexpr (MODE != MM_PLAIN && MODE != MM_GTU) {
     block_sum_k<K>(dot, red);
     if (threadIdx.x < K) {
       double v = dot[0];
@@ -304,6 +310,20 @@ __device__ __forceinline__ void mfinish(const MArgs<T>& a, double (&dot)[K], dou
 // K entries of its column.
 // ---------------------------------------------------------------------------
 
+// One batch of U slots of a slice: values and decoded columns (-1 for
+// padding).  Loads past the slice end stay inside the arrays' padding tail.
+template <typename T, bool I16, int U>
+__device__ __forceinline__ void msell_batch(const MArgs<T>& a, int off, int lane, int j,
+                                            T (&v)[U], int (&raw)[U]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int idx = off + (j + u) * kSlice + lane;
+    v[u] = ld_stream<true>(a.sv + idx);
+    if constexpr (I16) raw[u] = ld_stream<true>(a.sd + idx);
+    else raw[u] = ld_stream<true>(a.sc + idx);
+  }
+}
+
 template <typename T, int MODE, int K, bool I16, int U>
 __global__ __launch_bounds__(kWG) void msell_step(MArgs<T> a) {
   __shared__ double s_red[kWaves * K];
@@ -311,50 +331,88 @@ __global__ __launch_bounds__(kWG) void msell_step(MArgs<T> a) {
   const int lane = threadIdx.x & (kSlice - 1), wv = threadIdx.x / kSlice;
   int t0, t1, step;
   tile_range(a.ntiles, t0, t1, step);
+  // Software pipeline over the wave's batches (slice by slice, U slots at a
+  // time): the matrix data of the next batch -- possibly the next slice's
+  // first -- is loaded while the current batch's gathers are in flight.
+  auto slice_of = [&](int t, int& off, int& w) {
+    const int sl = t * kWaves + wv;
+    off = 0;
+    w = -1;  // no such slice
+    if (t < t1 && sl < a.nslices) {
+      off = a.soff[sl];
+      w = (a.soff[sl + 1] - off) / kSlice;
+    }
+  };
+  int t = t0, off, w;
+  slice_of(t, off, w);
+  while (t < t1 && w < 0) {
+    t += step;
+    slice_of(t, off, w);
+  }
+  T cv[U];
+  int cr[U];
+  if (w >= 0) msell_batch<T, I16, U>(a, off, lane, 0, cv, cr);
   MCoef<T, K> cf;
   if (!mprologue<T, MODE, K>(a, cf, s_red, &s_flag)) return;
   double dot[K];
 #pragma unroll
   for (int c = 0; c < K; ++c) dot[c] = 0.0;
-  for (int t = t0; t < t1; t += step) {
-    const int sl = t * kWaves + wv;
-    if (sl >= a.nslices) continue;
-    const int off = a.soff[sl], w = (a.soff[sl + 1] - off) / kSlice;
-    const int row = sl * kSlice + lane;
-    const bool live = row < a.n;
-    MOwn<T, K> o;
-    mown_load<T, MODE, K>(a, live ? row : 0, o);
-    T acc[K];
+  int j = 0;
+  int row = (t * kWaves + wv) * kSlice + lane;
+  MOwn<T, K> o;
+  if (w >= 0) mown_load<T, MODE, K>(a, row < a.n ? row : 0, o);
+  T acc[K];
 #pragma unroll
-    for (int c = 0; c < K; ++c) acc[c] = T(0);
-    for (int j = 0; j < w; j += U) {
-      T vv[U];
-      int col[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        // loads past the slice end stay inside the arrays' padding tail
-        const int idx = off + (j + u) * kSlice + lane;
-        vv[u] = ld_stream<true>(a.sv + idx);
-        int raw;
-        if constexpr (I16) raw = ld_stream<true>(a.sd + idx);
-        else raw = ld_stream<true>(a.sc + idx);
-        const bool in = j + u < w;
-        if constexpr (I16) col[u] = (in && raw != kPad16) ? row + raw : -1;
-        else col[u] = in ? raw : -1;
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const bool ok = col[u] >= 0;
-        const size_t base = (size_t)(ok ? col[u] : 0) * a.ld;
-        const T vu = ok ? vv[u] : T(0);
-#pragma unroll
-        for (int c = 0; c < K; ++c) {
-          const T g = mgat<T, MODE, K>(a, base, c, cf);
-          acc[c] = fma(vu, ok ? g : T(0), acc[c]);
-        }
-      }
+  for (int c = 0; c < K; ++c) acc[c] = T(0);
+  while (w >= 0) {
+    // position of the next batch
+    int nt = t, nj = j + U, noff = off, nw = w;
+    if (nj >= w) {
+      nj = 0;
+      do {
+        nt += step;
+        slice_of(nt, noff, nw);
+      } while (nt < t1 && nw < 0);
     }
-    if (live) mepi<T, MODE, K>(a, row, acc, cf, o, dot);
+    // gathers of the current batch
+    T g[U][K];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int col;
+      if constexpr (I16) col = (j + u < w && cr[u] != kPad16) ? row + cr[u] : -1;
+      else col = j + u < w ? cr[u] : -1;
+      ok[u] = col >= 0;
+      const size_t base = (size_t)(ok[u] ? col : 0) * a.ld;
+#pragma unroll
+      for (int c = 0; c < K; ++c) g[u][c] = mgat<T, MODE, K>(a, base, c, cf);
+    }
+    // matrix data of the next batch
+    T nv[U];
+    int nr[U];
+    if (nw >= 0) msell_batch<T, I16, U>(a, noff, lane, nj, nv, nr);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const T vu = ok[u] ? cv[u] : T(0);
+#pragma unroll
+      for (int c = 0; c < K; ++c) acc[c] = fma(vu, ok[u] ? g[u][c] : T(0), acc[c]);
+    }
+    if (nj == 0) {
+      if (row < a.n) mepi<T, MODE, K>(a, row, acc, cf, o, dot);
+#pragma unroll
+      for (int c = 0; c < K; ++c) acc[c] = T(0);
+      row = (nt * kWaves + wv) * kSlice + lane;
+      if (nw >= 0) mown_load<T, MODE, K>(a, row < a.n ? row : 0, o);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      cv[u] = nv[u];
+      cr[u] = nr[u];
+    }
+    t = nt;
+    j = nj;
+    off = noff;
+    w = nw;
   }
   mfinish<T, MODE, K>(a, dot, s_red);
 }
@@ -458,6 +516,110 @@ __global__ __launch_bounds__(kWG) void mrow_step(MArgs<T> a) {
     mepi<T, MODE, K>(a, i, acc, cf, o, dot);
   }
   mfinish<T, MODE, K>(a, dot, s_red);
+}
+
+// Separate form of the iteration (single-gather products, vector updates
+// in streaming passes).  The n x K blocks are walked as flat arrays, two
+// consecutive entries per thread and step (one 16-byte access per operand);
+// the grid-wide step is a multiple of K, so a thread always meets the same
+// two columns.  P_k = Z + beta P_{k-1} after the rho check ...
+template <typename T, int MODE, int K>
+__global__ __launch_bounds__(kWG) void mvec_p(MArgs<T> a) {
+  __shared__ double s_red[kWaves * K];
+  __shared__ int s_flag;
+  MCoef<T, K> cf;
+  if (!mprologue<T, MODE, K>(a, cf, s_red, &s_flag)) return;
+  constexpr int E = K >= 2 ? 2 : 1;
+  const size_t total = (size_t)a.n * K;
+  const size_t stride = (size_t)gridDim.x * kWG * E;
+  const size_t first = ((size_t)blockIdx.x * kWG + threadIdx.x) * E;
+  const int c0 = (int)(first % K);
+  T beta[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    beta[e] = cf.c[0];
+#pragma unroll
+    for (int c = 1; c < K; ++c)
+      if (c0 + e == c) beta[e] = cf.c[c];
+  }
+  for (size_t f = first; f < total; f += stride) {
+    T z[E], po[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) z[e] = a.in0[f + e];
+    if constexpr (MODE == MM_A) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) po[e] = a.in1[f + e];
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if constexpr (MODE == MM_A1) a.own[f + e] = z[e];
+      else a.own[f + e] = fma(beta[e], po[e], z[e]);
+    }
+  }
+}
+
+// ... and R_k = R_{k-1} - alpha Q, X += alpha P_k with ||r_k||^2 partials
+// after the sigma check (the G^T step's prologue).
+template <typename T, int K>
+__global__ __launch_bounds__(kWG) void mvec_r(MArgs<T> a) {
+  __shared__ double s_red[kWaves * K];
+  __shared__ int s_flag;
+  MCoef<T, K> cf;
+  if (!mprologue<T, MM_GT, K>(a, cf, s_red, &s_flag)) return;
+  constexpr int E = K >= 2 ? 2 : 1;
+  const size_t total = (size_t)a.n * K;
+  const size_t stride = (size_t)gridDim.x * kWG * E;
+  const size_t first = ((size_t)blockIdx.x * kWG + threadIdx.x) * E;
+  const int c0 = (int)(first % K);
+  T nal[E], al[E];
+  bool act[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    nal[e] = cf.c[0];
+    al[e] = cf.c2[0];
+    act[e] = cf.act[0];
+#pragma unroll
+    for (int c = 1; c < K; ++c)
+      if (c0 + e == c) {
+        nal[e] = cf.c[c];
+        al[e] = cf.c2[c];
+        act[e] = cf.act[c];
+      }
+  }
+  double d[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) d[e] = 0.0;
+  for (size_t f = first; f < total; f += stride) {
+    const size_t i = f / K;
+    const size_t fx = i * a.ldx + c0;
+    T ro[E], q[E], pk[E], xo[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) ro[e] = a.in0[f + e];
+#pragma unroll
+    for (int e = 0; e < E; ++e) q[e] = a.in1[f + e];
+#pragma unroll
+    for (int e = 0; e < E; ++e) pk[e] = a.pv[f + e];
+#pragma unroll
+    for (int e = 0; e < E; ++e) xo[e] = a.xv[fx + e];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const T rn = fma(nal[e], q[e], ro[e]);
+      a.own[f + e] = rn;
+      d[e] += (double)rn * (double)rn;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (act[e]) a.xv[fx + e] = fma(al[e], pk[e], xo[e]);
+  }
+  double dot[K];
+#pragma unroll
+  for (int c = 0; c < K; ++c) {
+    dot[c] = 0.0;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (c0 + e == c) dot[c] = d[e];
+  }
+  mfinish<T, MM_GT, K>(a, dot, s_red);
 }
 
 // Start-up: R_0 = B (columns c0 .. c0 + K - 1 of the caller's n x ldb array),
@@ -564,6 +726,15 @@ int mgrid(const sla_mat& m) {
   return step_grid(g);
 }
 
+// Iteration form: products with p and r formed inside their gathers
+// (fused) or single-gather products with the p and r updates in streaming
+// passes (separate, the default: with K columns the fused form's two
+// gathered vectors per nonzero overflow L2).  SLA_MFUSION=fused|unfused.
+bool mfused() {
+  const char* e = getenv("SLA_MFUSION");
+  return e && !strcmp(e, "fused");
+}
+
 // Columns handled per pass: the largest of 8, 4, 2, 1 that fits k.
 int chunk_width(int k) { return k >= 8 ? 8 : k >= 4 ? 4 : k >= 2 ? 2 : 1; }
 
@@ -649,6 +820,12 @@ sla_status mpcg_pass(const sla_mat& A, const sla_mat& G, double eps, const T* b,
   aG.in0 = t;
   aG.y = z;
 
+  // separate form: vector passes around single-gather products
+  const bool fused = mfused();
+  MArgs<T> aV = aA, aR = aT;
+  aV.in0 = z;
+  aR.in1 = q;
+
   // start-up: R_0 = B, X = 0, ||b_c||^2; T = G^T R_0; Z_0 = G T + eps R_0
   hipLaunchKernelGGL((minit<T, K>), dim3(grid), dim3(kWG), 0, s, b, ld, R[0], x, ld, n, w.prr);
   SLA_HIP(hipGetLastError());
@@ -671,16 +848,40 @@ sla_status mpcg_pass(const sla_mat& A, const sla_mat& G, double eps, const T* b,
     if (k <= maxit) {
       const int kend = std::min(maxit, k + B - 1);
       for (int kk = k; kk <= kend; ++kk) {
-        aA.k = kk;
-        aA.in1 = P[(kk - 1) & 1];
-        aA.own = P[kk & 1];
-        if (kk == 1) SLA_HIP((mlaunch<T, MM_A1, K>(A, A.fwd, aA, grid, s)));
-        else SLA_HIP((mlaunch<T, MM_A, K>(A, A.fwd, aA, grid, s)));
-        aT.k = kk;
-        aT.in0 = R[(kk - 1) & 1];
-        aT.own = R[kk & 1];
-        aT.pv = P[kk & 1];
-        SLA_HIP((mlaunch<T, MM_GT, K>(G, G.tr, aT, grid, s)));
+        if (fused) {
+          aA.k = kk;
+          aA.in1 = P[(kk - 1) & 1];
+          aA.own = P[kk & 1];
+          if (kk == 1) SLA_HIP((mlaunch<T, MM_A1, K>(A, A.fwd, aA, grid, s)));
+          else SLA_HIP((mlaunch<T, MM_A, K>(A, A.fwd, aA, grid, s)));
+          aT.k = kk;
+          aT.in0 = R[(kk - 1) & 1];
+          aT.own = R[kk & 1];
+          aT.pv = P[kk & 1];
+          SLA_HIP((mlaunch<T, MM_GT, K>(G, G.tr, aT, grid, s)));
+        } else {
+          // P_k; Q = A P_k; R_k and X; T = G^T R_k -- one gather per product
+          aV.k = kk;
+          aV.in1 = P[(kk - 1) & 1];
+          aV.own = P[kk & 1];
+          if (kk == 1)
+            hipLaunchKernelGGL((mvec_p<T, MM_A1, K>), dim3(grid), dim3(kWG), 0, s, aV);
+          else
+            hipLaunchKernelGGL((mvec_p<T, MM_A, K>), dim3(grid), dim3(kWG), 0, s, aV);
+          SLA_HIP(hipGetLastError());
+          aA.k = kk;
+          aA.in0 = P[kk & 1];
+          SLA_HIP((mlaunch<T, MM_AU, K>(A, A.fwd, aA, grid, s)));
+          aR.k = kk;
+          aR.in0 = R[(kk - 1) & 1];
+          aR.own = R[kk & 1];
+          aR.pv = P[kk & 1];
+          hipLaunchKernelGGL((mvec_r<T, K>), dim3(grid), dim3(kWG), 0, s, aR);
+          SLA_HIP(hipGetLastError());
+          aT.k = kk;
+          aT.in0 = R[kk & 1];
+          SLA_HIP((mlaunch<T, MM_GTU, K>(G, G.tr, aT, grid, s)));
+        }
         aG.k = kk;
         aG.rv = R[kk & 1];
         SLA_HIP((mlaunch<T, MM_G, K>(G, G.fwd, aG, grid, s)));

@@ -34,6 +34,15 @@ def layout(request, monkeypatch):
     return request.param
 
 
+@pytest.fixture(params=["separate", "fused"])
+def form(request, monkeypatch):
+    """The iteration's two forms: single-gather products with separate vector
+    passes, or p and r formed inside the products' gathers."""
+    if request.param == "fused":
+        monkeypatch.setenv("SLA_MFUSION", "fused")
+    return request.param
+
+
 def rhs(n, k, seed):
     return np.random.default_rng(seed).standard_normal((n, k))
 
@@ -101,14 +110,14 @@ def check_solve(p, Bm, rtol, maxit, cache_key=None):
 
 @pytest.mark.parametrize("key", MATS)
 @pytest.mark.parametrize("k", [2, 5, 8])
-def test_solve_multi_parity(key, k, layout):
+def test_solve_multi_parity(key, k, layout, form):
     p = problem(key)
     Bm = rhs(p.A.n, k, 7)
     Bm[:, 0] = p.b
     if k > 2:
         Bm[:, 2] = 0.0            # solved at once with x = 0
         Bm[:, 1] *= 1e-3          # same iterations as an unscaled column
-    say("solve_multi", key, k, layout, p.A.n)
+    say("solve_multi", key, k, layout, form, p.A.n)
     check_solve(p, Bm, p.rtol, p.maxit, cache_key=(key, k))
 
 
@@ -130,7 +139,7 @@ def test_solve_multi_columns_exit_at_different_iterations():
     assert infos[1].iterations > 20 and infos[3].iterations > 20
 
 
-def test_solve_multi_edges():
+def test_solve_multi_edges(form):
     p = problem("c0")
     n = p.A.n
     Bm = rhs(n, 4, 9)
@@ -170,7 +179,7 @@ def test_solve_multi_fp32_heat():
 
 
 @pytest.mark.parametrize("key", ["c0", "bsr_elastic_6", "powerlaw_20k"])
-def test_adjoint_multi_parity(key, layout):
+def test_adjoint_multi_parity(key, layout, form):
     p = problem(key)
     k = 3
     Bm = rhs(p.A.n, k, 13)
