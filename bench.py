@@ -253,6 +253,9 @@ def main():
                     help="minimum host time of the CPU-oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--spmv-reps", type=int, default=50)
+    ap.add_argument("--multi-rhs", type=lambda v: [int(c) for c in v.split(",") if c],
+                    default=[4, 8], help="right-hand-side counts of the multi-RHS lines "
+                                         "(empty string: none)")
     ap.add_argument("--counters-workload", action="store_true",
                     help="short run for rocprofv3 --pmc: a 256 MiB copy (calibration) and "
                          "20 forward + 20 adjoint PCG iterations on the same input")
@@ -392,6 +395,33 @@ def main():
     del flush
     spmv_cold_s = statistics.median(cold)
 
+    # several right-hand sides on the same operators (the single solve's b as
+    # column 0, seeded N(0,1) columns after it): forward solves only
+    multi = {}
+    if args.multi_rhs:
+        A = B.sla_csr_create(a_rp, a_ci, a_v)
+        G = B.sla_csr_create(g_rp, g_ci, g_v, build_transpose=True)
+        for k in args.multi_rhs:
+            Bm = np.random.default_rng(100 + k).standard_normal((n, k))
+            Bm[:, 0] = p.b
+            Bt = torch.from_numpy(Bm).to(dev)
+            Xt = torch.empty_like(Bt)
+            wm = B.workspace_multi(A, k, dev)
+            B.sla_pcg_solve_multi(A, G, p.eps, Bt, X=Xt, rtol=p.rtol, maxit=p.maxit, work=wm)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            _, infos = B.sla_pcg_solve_multi(A, G, p.eps, Bt, X=Xt, rtol=p.rtol, maxit=p.maxit,
+                                             work=wm)
+            torch.cuda.synchronize()
+            tm = time.perf_counter() - t0
+            its = [i.iterations for i in infos]
+            multi[str(k)] = {"column_iterations": sum(its), "lockstep_iterations": max(its),
+                             "ms": tm * 1e3, "column_iters_per_s": sum(its) / tm,
+                             "vs_single_forward": (sum(its) / tm) / (fi.iterations / tts)}
+            del Bt, Xt, wm
+        A.destroy()
+        G.destroy()
+
     achieved = ab["a_step"] / a_avg_s / 1e9
     traffic = traffic_if_current()
     moved = moved_bytes_a_step(p.A, n)
@@ -438,6 +468,10 @@ def main():
                          "read-only cache flush, warm = back-to-back calls with A (183 MB) "
                          "held in the 256 MB Infinity Cache"},
         "setup_ms": statistics.median(setup) * 1e3,
+        "multi_rhs": {"note": "k right-hand sides solved together on the same A and G "
+                              "(forward solves, fp64); column-iterations per second and the "
+                              "ratio to the single-right-hand-side forward rate",
+                      **multi} if multi else None,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(p, p.w, args.cpu_seconds)
