@@ -81,7 +81,8 @@ def traffic_if_current():
         return None
 
 
-STEP_NAMES = {1: "A step, iteration 1", 2: "A step (q = A p, p and x updates)",
+STEP_NAMES = {0: "plain SpMV y = A x (matrix from HBM)",
+              1: "A step, iteration 1", 2: "A step (q = A p, p and x updates)",
               3: "G^T step, start-up", 4: "G^T step (t = G^T r, r update)",
               5: "G step, start-up", 6: "G step (z = G t + eps r)"}
 
@@ -139,9 +140,10 @@ def summarize_counters(fetch_dir, write_dir):
     md = ["# HBM traffic per launch of the PCG kernels, 3D Poisson 128^3 fp64", "",
           "Counters from two rocprofv3 runs of the benchmark's counter workload (a 256 MiB",
           "copy for calibration, then 20 forward and 20 adjoint PCG iterations on the",
-          "128^3 input).  FETCH_SIZE and WRITE_SIZE are KiB per dispatch; the copy of",
-          f"known size (256 MiB read, 256 MiB written) calibrates fetched bytes by {fs:.3f}",
-          f"and written bytes by {ws:.3f}.", "",
+          "128^3 input, then 8 plain SpMVs alternating between two copies of A so that",
+          "each streams its matrix from HBM).  FETCH_SIZE and WRITE_SIZE are KiB per",
+          "dispatch; the copy of known size (256 MiB read, 256 MiB written) calibrates",
+          f"fetched bytes by {fs:.3f} and written bytes by {ws:.3f}.", "",
           "Commands (from the repository root, `export TMPDIR=/tmp`):", "",
           "    " + cmd.format(c="FETCH_SIZE", d=fetch_dir),
           "    " + cmd.format(c="WRITE_SIZE", d=write_dir),
@@ -258,7 +260,8 @@ def main():
                                          "(empty string: none)")
     ap.add_argument("--counters-workload", action="store_true",
                     help="short run for rocprofv3 --pmc: a 256 MiB copy (calibration) and "
-                         "20 forward + 20 adjoint PCG iterations on the same input")
+                         "20 forward + 20 adjoint PCG iterations on the same input, then 8 "
+                         "SpMVs alternating between two copies of A")
     ap.add_argument("--counter-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic summary under profiles/ from two rocprofv3 "
                          "--pmc runs of --counters-workload (no GPU needed)")
@@ -272,6 +275,9 @@ def main():
     if args.counter_summary:
         summarize_counters(*args.counter_summary)
         return
+    if args.steps < 1 or args.warmup < 0:
+        print("bench.py needs --steps >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this solver runs on a single MI355X "
               "(multi-GPU sharding is described in the design notes, not built); "
@@ -314,6 +320,12 @@ def main():
         B.sla_pcg_solve(A, G, p.eps, b, x=x, rtol=p.rtol, maxit=20, work=work)
         B.sla_pcg_adjoint(A, G, p.eps, x, w, rtol=p.rtol, maxit=20, grad_b=grad_b,
                           grad_vals=grad_vals, work=work)
+        # plain SpMV streaming its matrix from HBM: two copies of A alternately
+        A2 = B.sla_csr_create(a_rp.clone(), a_ci.clone(), a_v.clone())
+        y = torch.empty_like(b)
+        for _ in range(4):
+            B.sla_spmv(A, b, y)
+            B.sla_spmv(A2, b, y)
         torch.cuda.synchronize()
         log("counters workload done")
         return
@@ -334,7 +346,7 @@ def main():
     log(f"warmup {args.warmup} step(s)")
     for _ in range(args.warmup):
         fi, ai = step()
-    log(f"forward iterations {fi.iterations}, adjoint iterations {ai.iterations}")
+        log(f"forward iterations {fi.iterations}, adjoint iterations {ai.iterations}")
 
     B.sla_reset_profile()
     B.sla_set_profiling(["a_step"])
@@ -371,29 +383,50 @@ def main():
         _, fi = B.sla_pcg_solve(A, G, p.eps, b, x=x, rtol=p.rtol, maxit=p.maxit, work=work)
         solve_t.append(time.perf_counter() - s0)
     tts = statistics.median(solve_t)
+    # SpMV of A: kernel durations from the library's own fence-free events on
+    # the launch stream (as for the roofline kernel)
     y = torch.empty_like(b)
     B.sla_spmv(A, b, y)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    e0.record()
+    B.sla_reset_profile()
+    B.sla_set_profiling(["spmv"])
     for _ in range(args.spmv_reps):
         B.sla_spmv(A, b, y)
-    e1.record()
     torch.cuda.synchronize()
-    spmv_s = e0.elapsed_time(e1) / 1e3 / args.spmv_reps
+    nw, ms_w = B.sla_get_profile("spmv")
+    spmv_s = ms_w / max(nw, 1) / 1e3
     # cold: a 1 GiB read-only pass before each call evicts A from L2 and the
     # 256 MB Infinity Cache without leaving dirty lines behind
     flush = torch.ones(128 * 1024 * 1024, dtype=torch.float64, device=dev)
     cold = []
     for _ in range(10):
-        flush.sum()
-        e0.record()
-        B.sla_spmv(A, b, y)
-        e1.record()
         torch.cuda.synchronize()
-        cold.append(e0.elapsed_time(e1) / 1e3)
+        B.sla_reset_profile()
+        flush.sum()
+        B.sla_spmv(A, b, y)          # queued right behind the flush
+        torch.cuda.synchronize()
+        nc, ms_c = B.sla_get_profile("spmv")
+        cold.append(ms_c / max(nc, 1) / 1e3)
     del flush
     spmv_cold_s = statistics.median(cold)
+    # steady streaming: two handles over separate copies of A (2 x 183 MB, more
+    # than the 256 MB Infinity Cache holds) called alternately, so each call
+    # streams its matrix from HBM while x and y stay where the previous call
+    # left them, as inside an iterative method
+    A2 = B.sla_csr_create(a_rp.clone(), a_ci.clone(), a_v.clone())
+    for _ in range(4):
+        B.sla_spmv(A, b, y)
+        B.sla_spmv(A2, b, y)
+    torch.cuda.synchronize()
+    B.sla_reset_profile()
+    for _ in range(args.spmv_reps // 2):
+        B.sla_spmv(A, b, y)
+        B.sla_spmv(A2, b, y)
+    torch.cuda.synchronize()
+    ns, ms_s = B.sla_get_profile("spmv")
+    spmv_stream_s = ms_s / max(ns, 1) / 1e3
+    B.sla_set_profiling(False)
+    A2.destroy()
 
     # several right-hand sides on the same operators (the single solve's b as
     # column 0, seeded N(0,1) columns after it): forward solves only
@@ -428,6 +461,7 @@ def main():
     iter_gbs = ab["iteration"] * fi.iterations / tts / 1e9
     spmv_gbs = ab["spmv_A"] / spmv_s / 1e9
     spmv_cold_gbs = ab["spmv_A"] / spmv_cold_s / 1e9
+    spmv_stream_gbs = ab["spmv_A"] / spmv_stream_s / 1e9
     result = {
         "metric": "PCG iters/sec + SpMV HBM GB/s (% of peak), 3D Poisson 128^3 fp64, 1 GPU",
         "value": total_iters / elapsed,
@@ -460,13 +494,18 @@ def main():
                       "us_per_iteration": tts / fi.iterations * 1e6,
                       "time_to_solution_ms": tts * 1e3},
         "spmv": {"bytes": ab["spmv_A"],
+                 "hbm_stream": {"GBps": spmv_stream_gbs, "frac": spmv_stream_gbs / HBM_PEAK_GBS,
+                                "us": spmv_stream_s * 1e6},
                  "cold": {"GBps": spmv_cold_gbs, "frac": spmv_cold_gbs / HBM_PEAK_GBS,
                           "us": spmv_cold_s * 1e6},
                  "warm": {"GBps": spmv_gbs, "frac": spmv_gbs / HBM_PEAK_GBS,
                           "us": spmv_s * 1e6},
-                 "note": "algorithmic CSR bytes; cold = median of 10 calls after a 1 GiB "
-                         "read-only cache flush, warm = back-to-back calls with A (183 MB) "
-                         "held in the 256 MB Infinity Cache"},
+                 "note": "algorithmic CSR bytes over the kernel's duration (library "
+                         "events); hbm_stream = two copies of A (2 x 183 MB) called "
+                         "alternately so each call streams its matrix from HBM with x and "
+                         "y warm; cold = median of 10 calls, each after a 1 GiB read-only "
+                         "flush of every cache (x included); warm = back-to-back calls "
+                         "with A held in the 256 MB Infinity Cache"},
         "setup_ms": statistics.median(setup) * 1e3,
         "multi_rhs": {"note": "k right-hand sides solved together on the same A and G "
                               "(forward solves, fp64); column-iterations per second and the "

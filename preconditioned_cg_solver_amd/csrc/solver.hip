@@ -34,6 +34,7 @@
 #include <cstring>
 #include <deque>
 #include <mutex>
+#include <utility>
 #include <vector>
 
 #include "internal.h"
@@ -220,7 +221,8 @@ __device__ __forceinline__ Own<T> own_load(const StepArgs<T>& a, int i) {
 #define SLA_NTS_MASK 3
 #endif
 // Output stores.  Outputs with no reuse before the next iteration (x and p
-// of the A step: bits 1 and 2 of SLA_NTS_MASK; bit 4 would add q) are stored
+// of the A step: bits 1 and 2 of SLA_NTS_MASK; bit 4 would add q, bit 8 the
+// result of a plain product) are stored
 // non-temporally, so they do not sit dirty in L2 and need no write-back at
 // the kernel boundary; outputs the next kernel consumes keep normal stores.
 template <int BIT, typename U>
@@ -233,7 +235,10 @@ __device__ __forceinline__ void st_out(U* p, U v) {
 template <typename T, int MODE>
 __device__ __forceinline__ double epi_own(const StepArgs<T>& a, int i, T acc, const Coef<T>& cf,
                                           const Own<T>& o) {
-  if constexpr (MODE == M_PLAIN || MODE == M_GTU) {
+  if constexpr (MODE == M_PLAIN) {
+    st_out<8>(a.y + i, acc);
+    return 0.0;
+  } else if constexpr (MODE == M_GTU) {
     st_out<0>(a.y + i, acc);
     return 0.0;
   } else if constexpr (MODE == M_AU) {
@@ -1020,6 +1025,7 @@ struct ProfClass {
 std::mutex g_prof_mu;
 std::atomic<int> g_prof_mask{0};
 ProfClass g_prof[4];
+std::vector<std::pair<hipEvent_t, hipEvent_t>> g_spmv_pending;  // standalone SpMV timings
 
 struct EventPair {
   hipEvent_t a, b;
@@ -1399,16 +1405,10 @@ sla_status spmv(const sla_mat& A, bool transpose, const void* x, void* y, hipStr
   }
   if (prof) {
     SLA_HIP(hipEventRecord(eb, s));
-    SLA_HIP(hipEventSynchronize(eb));
-    float ms = 0.f;
-    SLA_HIP(hipEventElapsedTime(&ms, ea, eb));
-    {
-      std::lock_guard<std::mutex> lk(g_prof_mu);
-      g_prof[3].launches += 1;
-      g_prof[3].ms += ms;
-    }
-    (void)hipEventDestroy(ea);
-    (void)hipEventDestroy(eb);
+    // read back later (prof_get / prof_reset), so that timed calls queue
+    // back to back as they do inside a solve
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_spmv_pending.push_back({ea, eb});
   }
   return SLA_OK;
 }
@@ -1517,13 +1517,30 @@ sla_status pattern_grad(const sla_mat& A, const void* lam, const void* x, void* 
 }
 
 void prof_enable(int mask) { g_prof_mask.store(mask & 15); }
+// Fold the pending standalone-SpMV event pairs into their class (waits for
+// them); caller holds g_prof_mu.
+void flush_spmv_pending() {
+  for (auto& pr : g_spmv_pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(pr.second) == hipSuccess &&
+        hipEventElapsedTime(&ms, pr.first, pr.second) == hipSuccess) {
+      g_prof[3].launches += 1;
+      g_prof[3].ms += ms;
+    }
+    (void)hipEventDestroy(pr.first);
+    (void)hipEventDestroy(pr.second);
+  }
+  g_spmv_pending.clear();
+}
 void prof_get(int cls, int64_t* launches, double* ms) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
+  flush_spmv_pending();
   if (launches) *launches = g_prof[cls].launches;
   if (ms) *ms = g_prof[cls].ms;
 }
 void prof_reset() {
   std::lock_guard<std::mutex> lk(g_prof_mu);
+  flush_spmv_pending();
   for (auto& p : g_prof) p = ProfClass{};
 }
 
