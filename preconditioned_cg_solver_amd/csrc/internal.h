@@ -173,6 +173,13 @@ sla_status pattern_grad(const sla_mat& A, const void* lam, const void* x, void* 
 sla_status sai_loss(const sla_mat& A, const sla_mat& G, double eps, const void* probes,
                     int32_t nprobe, double scale, void* work, double* out, hipStream_t s);
 
+// Small systems solved in one workgroup per right-hand side (solver.hip).
+bool small_applies(const sla_mat& A, const sla_mat& G);
+size_t small_states_bytes(int k);
+sla_status small_solve_batch(const sla_mat& A, const sla_mat& G, double eps, const void* b,
+                             void* x, int k, double rtol, int maxit, void* states,
+                             hipStream_t s, sla_solve_info* info, sla_status* cst);
+
 // Several right-hand sides (multi.hip).
 size_t workspace_bytes_multi(const sla_mat& A, int k);
 sla_status spmm(const sla_mat& A, bool transpose, const void* x, void* y, int k, hipStream_t s);

@@ -999,8 +999,10 @@ sla_status spmm_impl(const sla_mat& A, bool transpose, const T* x, T* y, int k, 
 
 size_t workspace_bytes_multi(const sla_mat& A, int k) {
   const size_t es = A.dtype == SLA_F64 ? 8 : 4;
-  return align_up(sizeof(MState)) + 3 * align_up((size_t)max_grid() * kMaxRhs * sizeof(double)) +
-         7 * align_up((size_t)A.n() * chunk_width(k) * es);
+  const size_t lockstep = align_up(sizeof(MState)) +
+                          3 * align_up((size_t)max_grid() * kMaxRhs * sizeof(double)) +
+                          7 * align_up((size_t)A.n() * chunk_width(k) * es);
+  return std::max(lockstep, small_states_bytes(k));
 }
 
 sla_status spmm(const sla_mat& A, bool transpose, const void* x, void* y, int k, hipStream_t s) {
@@ -1019,6 +1021,9 @@ sla_status pcg_solve_multi(const sla_mat& A, const sla_mat& G, double eps, const
     }
     return SLA_OK;
   }
+  // small systems: one workgroup per column, every column in one launch
+  if (small_applies(A, G))
+    return small_solve_batch(A, G, eps, b, x, k, rtol, maxit, work, s, info, cst);
   if (A.dtype == SLA_F64)
     return mpcg_impl<double>(A, G, eps, (const double*)b, (double*)x, k, rtol, maxit, work, s,
                              info, cst);

@@ -861,6 +861,190 @@ __global__ __launch_bounds__(kWG) void sai_final(const double* __restrict__ part
 }
 
 // ---------------------------------------------------------------------------
+// Whole solve in one workgroup for small systems (n <= 1024, SELL rows of at
+// most kSmallW slots in A, G and G^T): thread i owns row i and keeps its rows
+// of A, G and G^T in registers for the whole solve, the three gathered
+// vectors (p, r, t) live in LDS, every dot product is a workgroup reduction
+// in a fixed order, and the iteration loop runs inside the kernel -- one
+// launch per solve instead of three per iteration.  Same recurrences, exit
+// rules and records as the multi-kernel solver.
+// ---------------------------------------------------------------------------
+
+constexpr int kSmallN = 1024;
+constexpr int kSmallW = 8;
+constexpr int kSmallWaves = kSmallN / 64;
+
+template <typename T>
+struct SmallArgs {
+  const T* av;
+  const int32_t* ac;
+  const int16_t* ad;
+  const int32_t* ao;
+  const T* gv;
+  const int32_t* gc;
+  const int16_t* gd;
+  const int32_t* go;
+  const T* tv;
+  const int32_t* tc;
+  const int16_t* td;
+  const int32_t* to;
+  int n;
+  double eps;
+  const T* b;  // column blockIdx.x of b and x, row stride ld
+  T* x;
+  int ld;
+  double rtol;
+  int maxit;
+  SolverState* st;  // one record per column
+  double* hist_a;
+  double* hist_b;
+  int hist_len;
+};
+
+// Row i of a SELL matrix into registers (value 0 / column 0 for padding).
+template <typename T>
+__device__ __forceinline__ void small_row(const T* v, const int32_t* c, const int16_t* d,
+                                          const int32_t* soff, int i, T (&val)[kSmallW],
+                                          int (&col)[kSmallW]) {
+  const int sl = i / kSlice, l = i - sl * kSlice;
+  const int off = soff[sl], w = (soff[sl + 1] - off) / kSlice;
+#pragma unroll
+  for (int j = 0; j < kSmallW; ++j) {
+    val[j] = T(0);
+    col[j] = 0;
+    if (j < w) {
+      const int idx = off + j * kSlice + l;
+      int cc;
+      if (d) {
+        const int raw = d[idx];
+        cc = raw == kPad16 ? -1 : i + raw;
+      } else {
+        cc = c[idx];
+      }
+      if (cc >= 0) {
+        val[j] = v[idx];
+        col[j] = cc;
+      }
+    }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ T small_dot_row(const T (&val)[kSmallW], const int (&col)[kSmallW],
+                                           const T* vec) {
+  T acc = T(0);
+#pragma unroll
+  for (int j = 0; j < kSmallW; ++j) acc = fma(val[j], vec[col[j]], acc);
+  return acc;
+}
+
+__device__ __forceinline__ double small_sum(double v, double* red) {
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double s = red[0];
+#pragma unroll
+  for (int q = 1; q < kSmallWaves; ++q) s += red[q];
+  return s;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kSmallN) void small_pcg(SmallArgs<T> a) {
+  __shared__ T s_p[kSmallN], s_r[kSmallN], s_t[kSmallN];
+  __shared__ double s_red[kSmallWaves];
+  const int i = threadIdx.x;
+  const bool live = i < a.n;
+  T av[kSmallW], gv[kSmallW], tv[kSmallW];
+  int ac[kSmallW], gc[kSmallW], tc[kSmallW];
+  const int ri = live ? i : 0;
+  small_row<T>(a.av, a.ac, a.ad, a.ao, ri, av, ac);
+  small_row<T>(a.gv, a.gc, a.gd, a.go, ri, gv, gc);
+  small_row<T>(a.tv, a.tc, a.td, a.to, ri, tv, tc);
+  if (!live) {
+#pragma unroll
+    for (int j = 0; j < kSmallW; ++j) av[j] = gv[j] = tv[j] = T(0);
+  }
+  s_p[i] = T(0);
+  s_t[i] = T(0);
+  const int col = blockIdx.x;
+  const T bi = live ? a.b[(size_t)i * a.ld + col] : T(0);
+  T x = T(0), r = bi;
+  const bool lead = i == 0;
+  int kind = EX_NONE, kexit = 0;
+  const double bb = small_sum((double)bi * (double)bi, s_red);
+  double rr = bb;
+  if (!isfinite(bb)) kind = EX_NONFINITE_B;
+  else if (bb == 0.0) kind = EX_BZERO;
+  else if (a.maxit == 0) kind = EX_MAXIT0;
+  const double bnorm = sqrt(bb);
+  T z = T(0), p = T(0);
+  double rho = 0.0;
+  if (kind == EX_NONE) {
+    // z_0 = G (G^T r_0) + eps r_0, rho_0
+    s_r[i] = r;
+    __syncthreads();
+    s_t[i] = small_dot_row(tv, tc, s_r);
+    __syncthreads();
+    z = fma(T(a.eps), r, small_dot_row(gv, gc, s_t));
+    rho = small_sum((double)r * (double)z, s_red);
+    if (!(rho > 0.0) || !isfinite(rho)) {
+      kind = EX_BREAK_RHO;
+      kexit = 1;
+    }
+    p = z;
+  }
+  for (int k = 1; kind == EX_NONE && k <= a.maxit; ++k) {
+    s_p[i] = p;
+    __syncthreads();
+    const T q = small_dot_row(av, ac, s_p);
+    const double sigma = small_sum((double)p * (double)q, s_red);
+    if (!(sigma > 0.0) || !isfinite(sigma)) {
+      kind = EX_BREAK_SIGMA;
+      kexit = k;
+      break;
+    }
+    const double alpha = rho / sigma;
+    if (lead && a.hist_a && k <= a.hist_len) a.hist_a[k - 1] = alpha;
+    x = fma(T(alpha), p, x);
+    r = fma(T(-alpha), q, r);
+    rr = small_sum((double)r * (double)r, s_red);
+    const double rnorm = sqrt(rr);
+    if (!isfinite(rnorm)) kind = EX_BREAK_RR;
+    else if (rnorm <= a.rtol * bnorm) kind = EX_CONV;
+    else if (k == a.maxit) kind = EX_MAXIT;
+    if (kind != EX_NONE) {
+      kexit = k;
+      break;
+    }
+    s_r[i] = r;
+    __syncthreads();
+    s_t[i] = small_dot_row(tv, tc, s_r);
+    __syncthreads();
+    z = fma(T(a.eps), r, small_dot_row(gv, gc, s_t));
+    const double rho_new = small_sum((double)r * (double)z, s_red);
+    if (!(rho_new > 0.0) || !isfinite(rho_new)) {
+      kind = EX_BREAK_RHO;
+      kexit = k + 1;
+      break;
+    }
+    const double beta = rho_new / rho;
+    if (lead && a.hist_b && k <= a.hist_len) a.hist_b[k - 1] = beta;
+    rho = rho_new;
+    p = fma(T(beta), p, z);
+  }
+  if (live) a.x[(size_t)i * a.ld + col] = x;
+  if (lead) {
+    SolverState* st = a.st + col;
+    st->exit_kind = kind;
+    st->exit_iter = kexit;
+    st->bb = bb;
+    st->rr = rr;
+    st->done = 1;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Adjoint pattern gradient: g[k] = -lambda_row(k) * x_col(k).
 // ---------------------------------------------------------------------------
 
@@ -1136,6 +1320,37 @@ Work carve(const sla_mat& A, void* work) {
   return w;
 }
 
+// Status and record of a finished solve from its exit kind and iteration.
+sla_status exit_status(const SolverState& fin, sla_solve_info* info, int* iters_out) {
+  sla_status st = SLA_OK;
+  int iters = 0, conv = 0;
+  switch (fin.exit_kind) {
+    case EX_CONV: st = SLA_OK; iters = fin.exit_iter; conv = 1; break;
+    case EX_BZERO: st = SLA_OK; iters = 0; conv = 1; break;
+    case EX_MAXIT: st = SLA_NOT_CONVERGED; iters = fin.exit_iter; break;
+    case EX_MAXIT0: st = SLA_NOT_CONVERGED; iters = 0; break;
+    case EX_BREAK_SIGMA: st = SLA_ERR_BREAKDOWN; iters = fin.exit_iter - 1; break;
+    case EX_BREAK_RHO: st = SLA_ERR_BREAKDOWN; iters = fin.exit_iter - 1; break;
+    case EX_BREAK_RR: st = SLA_ERR_BREAKDOWN; iters = fin.exit_iter; break;
+    case EX_NONFINITE_B: st = SLA_ERR_NONFINITE; iters = 0; break;
+    default:
+      set_error("solver finished without an exit record");
+      return SLA_ERR_HIP;
+  }
+  if (st == SLA_ERR_BREAKDOWN) set_error("PCG breakdown (p.Ap <= 0, r.z <= 0 or non-finite residual)");
+  if (st == SLA_ERR_NONFINITE) set_error("right-hand side is not finite");
+  if (info) {
+    info->iterations = iters;
+    info->converged = conv;
+    info->bnorm = std::sqrt(fin.bb);
+    info->rel_residual = fin.bb > 0 ? std::sqrt(fin.rr) / std::sqrt(fin.bb)
+                                    : (fin.exit_kind == EX_BZERO ? 0.0 : 1.0);
+    if (fin.exit_kind == EX_MAXIT0) info->rel_residual = 1.0;
+  }
+  if (iters_out) *iters_out = iters;
+  return st;
+}
+
 // Fused iteration (p and r formed inside the products' gathers) when A's
 // gathers have locality -- A qualified for the SELL-64 layout (short, even,
 // banded rows) or is block sparse; otherwise separate streaming passes keep
@@ -1330,31 +1545,9 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
   const SolverState fin = *hs;
   lk.unlock();
 
-  sla_status st = SLA_OK;
-  int iters = 0, conv = 0;
-  switch (fin.exit_kind) {
-    case EX_CONV: st = SLA_OK; iters = fin.exit_iter; conv = 1; break;
-    case EX_BZERO: st = SLA_OK; iters = 0; conv = 1; break;
-    case EX_MAXIT: st = SLA_NOT_CONVERGED; iters = fin.exit_iter; break;
-    case EX_MAXIT0: st = SLA_NOT_CONVERGED; iters = 0; break;
-    case EX_BREAK_SIGMA: st = SLA_ERR_BREAKDOWN; iters = fin.exit_iter - 1; break;
-    case EX_BREAK_RHO: st = SLA_ERR_BREAKDOWN; iters = fin.exit_iter - 1; break;
-    case EX_BREAK_RR: st = SLA_ERR_BREAKDOWN; iters = fin.exit_iter; break;
-    case EX_NONFINITE_B: st = SLA_ERR_NONFINITE; iters = 0; break;
-    default:
-      set_error("solver finished without an exit record");
-      return SLA_ERR_HIP;
-  }
-  if (st == SLA_ERR_BREAKDOWN) set_error("PCG breakdown (p.Ap <= 0, r.z <= 0 or non-finite residual)");
-  if (st == SLA_ERR_NONFINITE) set_error("right-hand side is not finite");
-  if (info) {
-    info->iterations = iters;
-    info->converged = conv;
-    info->bnorm = std::sqrt(fin.bb);
-    info->rel_residual = fin.bb > 0 ? std::sqrt(fin.rr) / std::sqrt(fin.bb)
-                                    : (fin.exit_kind == EX_BZERO ? 0.0 : 1.0);
-    if (fin.exit_kind == EX_MAXIT0) info->rel_residual = 1.0;
-  }
+  int iters = 0;
+  const sla_status st = exit_status(fin, info, &iters);
+  if (st == SLA_ERR_HIP) return st;
   // profile: A / G^T launches of iterations 1..iters did work; G launches of
   // iterations < the exit iteration did work (the exit one returns early)
   rec.flush(std::max(iters, fin.exit_kind == EX_BREAK_SIGMA ? fin.exit_iter : iters),
@@ -1362,6 +1555,58 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
   return st;
 }
 
+
+// The one-workgroup solver applies when every operator has the SELL layout
+// with at most kSmallW slots per row and n <= kSmallN (SLA_SMALL=0 turns it
+// off).
+bool small_ok(const sla_mat& A, const sla_mat& G) {
+  if (const char* e = getenv("SLA_SMALL"))
+    if (e[0] == '0') return false;
+  if (A.bs != 1 || A.n() > kSmallN) return false;
+  for (const MatView* v : {&A.fwd, &G.fwd, &G.tr})
+    if (!v->sell || v->sell_w > kSmallW) return false;
+  return true;
+}
+
+template <typename T>
+sla_status small_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, T* x,
+                      double rtol, int maxit, void* work, hipStream_t s, sla_solve_info* info,
+                      double* hist_a, double* hist_b, int hist_len) {
+  Work w = carve(A, work);
+  SmallArgs<T> a{};
+  auto set = [](const MatView& v, const T*& val, const int32_t*& col, const int16_t*& d,
+                const int32_t*& off) {
+    val = (const T*)v.sv;
+    col = v.sd ? nullptr : v.sc;
+    d = v.sd;
+    off = v.soff;
+  };
+  set(A.fwd, a.av, a.ac, a.ad, a.ao);
+  set(G.fwd, a.gv, a.gc, a.gd, a.go);
+  set(G.tr, a.tv, a.tc, a.td, a.to);
+  a.n = (int)A.n();
+  a.eps = eps;
+  a.b = b;
+  a.x = x;
+  a.ld = 1;
+  a.rtol = rtol;
+  a.maxit = maxit;
+  a.st = w.st;
+  a.hist_a = hist_a;
+  a.hist_b = hist_b;
+  a.hist_len = hist_len;
+  hipLaunchKernelGGL((small_pcg<T>), dim3(1), dim3(kSmallN), 0, s, a);
+  SLA_HIP(hipGetLastError());
+  std::unique_lock<std::mutex> lk(g_poll_mu);
+  sla_status pst = poll_init();
+  if (pst != SLA_OK) return pst;
+  SolverState* hs = &g_host_state[3];
+  SLA_HIP(hipMemcpyAsync(hs, w.st, sizeof(SolverState), hipMemcpyDeviceToHost, s));
+  SLA_HIP(hipStreamSynchronize(s));
+  const SolverState fin = *hs;
+  lk.unlock();
+  return exit_status(fin, info, nullptr);
+}
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -1482,11 +1727,68 @@ sla_status pcg_solve(const sla_mat& A, const sla_mat& G, double eps, const void*
     if (info) *info = sla_solve_info{0, 1, 0.0, 0.0};
     return SLA_OK;
   }
+  if (small_ok(A, G)) {
+    if (A.dtype == SLA_F64)
+      return small_impl<double>(A, G, eps, (const double*)b, (double*)x, rtol, maxit, work, s,
+                                info, hist_a, hist_b, hist_len);
+    return small_impl<float>(A, G, eps, (const float*)b, (float*)x, rtol, maxit, work, s, info,
+                             hist_a, hist_b, hist_len);
+  }
   if (A.dtype == SLA_F64)
     return pcg_impl<double>(A, G, eps, (const double*)b, (double*)x, rtol, maxit, work, s, info,
                             hist_a, hist_b, hist_len);
   return pcg_impl<float>(A, G, eps, (const float*)b, (float*)x, rtol, maxit, work, s, info,
                          hist_a, hist_b, hist_len);
+}
+
+bool small_applies(const sla_mat& A, const sla_mat& G) { return small_ok(A, G); }
+
+size_t small_states_bytes(int k) { return align_up((size_t)k * sizeof(SolverState)); }
+
+// k independent small solves (columns of n x k row-major b and x), one
+// workgroup each, all in one launch.
+sla_status small_solve_batch(const sla_mat& A, const sla_mat& G, double eps, const void* b,
+                             void* x, int k, double rtol, int maxit, void* states,
+                             hipStream_t s, sla_solve_info* info, sla_status* cst) {
+  auto launch = [&](auto tag) -> hipError_t {
+    using T = decltype(tag);
+    SmallArgs<T> a{};
+    auto set = [](const MatView& v, const T*& val, const int32_t*& col, const int16_t*& d,
+                  const int32_t*& off) {
+      val = (const T*)v.sv;
+      col = v.sd ? nullptr : v.sc;
+      d = v.sd;
+      off = v.soff;
+    };
+    set(A.fwd, a.av, a.ac, a.ad, a.ao);
+    set(G.fwd, a.gv, a.gc, a.gd, a.go);
+    set(G.tr, a.tv, a.tc, a.td, a.to);
+    a.n = (int)A.n();
+    a.eps = eps;
+    a.b = (const T*)b;
+    a.x = (T*)x;
+    a.ld = k;
+    a.rtol = rtol;
+    a.maxit = maxit;
+    a.st = (SolverState*)states;
+    hipLaunchKernelGGL((small_pcg<T>), dim3(k), dim3(kSmallN), 0, s, a);
+    return hipGetLastError();
+  };
+  if (A.dtype == SLA_F64) SLA_HIP(launch(double(0)));
+  else SLA_HIP(launch(float(0)));
+  std::vector<SolverState> fin((size_t)k);
+  SLA_HIP(hipMemcpyAsync(fin.data(), states, (size_t)k * sizeof(SolverState),
+                         hipMemcpyDeviceToHost, s));
+  SLA_HIP(hipStreamSynchronize(s));
+  sla_status worst = SLA_OK;
+  for (int c = 0; c < k; ++c) {
+    const sla_status st = exit_status(fin[c], info ? info + c : nullptr, nullptr);
+    if (st == SLA_ERR_HIP) return st;
+    if (cst) cst[c] = st;
+    if (st < 0 && worst >= 0) worst = st;
+    else if (st == SLA_NOT_CONVERGED && worst == SLA_OK) worst = st;
+  }
+  return worst;
 }
 
 sla_status pattern_grad(const sla_mat& A, const void* lam, const void* x, void* grad,

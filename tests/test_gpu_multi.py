@@ -37,9 +37,12 @@ def layout(request, monkeypatch):
 @pytest.fixture(params=["separate", "fused"])
 def form(request, monkeypatch):
     """The iteration's two forms: single-gather products with separate vector
-    passes, or p and r formed inside the products' gathers."""
+    passes, or p and r formed inside the products' gathers.  (With the
+    default form, systems of at most 1024 rows take one workgroup per column;
+    the fused form keeps them in lock step.)"""
     if request.param == "fused":
         monkeypatch.setenv("SLA_MFUSION", "fused")
+        monkeypatch.setenv("SLA_SMALL", "0")
     return request.param
 
 

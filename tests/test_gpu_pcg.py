@@ -29,9 +29,12 @@ FORWARD = ["c0", "poisson2d_37", "poisson3d_13", "irregular_long_rows", "bsr_ela
 @pytest.fixture(params=["auto", "fused", "unfused"])
 def fusion(request, monkeypatch):
     """The iteration's two forms: p and r formed inside the products'
-    gathers, or separate vector passes (the library picks per matrix)."""
+    gathers, or separate vector passes (the library picks per matrix, and
+    solves systems of at most 1024 rows in one workgroup)."""
     if request.param != "auto":
+        # the explicit forms also keep small systems off the one-workgroup solver
         monkeypatch.setenv("SLA_FUSION", request.param)
+        monkeypatch.setenv("SLA_SMALL", "0")
     return request.param
 
 
@@ -248,5 +251,58 @@ def test_jacobi_parity(key):
     A = create(p.A)
     Dh = create(D, transpose=True)
     x, info = B.sla_pcg_solve(A, Dh, 0.0, tdev(p.b), rtol=p.rtol, maxit=p.maxit)
+    assert info.status == B.OK and iters_close(info.iterations, it)
+    assert rel(host(x), x_ref) <= 1e-8
+
+
+SMALL = {
+    "poisson2d_20": lambda: I.make_problem(0, size=20),
+    "poisson2d_32": lambda: I.make_problem(0),
+    "heat2d_31": lambda: I.make_problem(1, size=31),
+    "poisson3d_10": lambda: I.make_problem(2, size=10),
+}
+
+
+@pytest.mark.parametrize("key", list(SMALL))
+@pytest.mark.parametrize("small", ["one_workgroup", "multi_kernel"])
+def test_small_systems(key, small, monkeypatch):
+    """Systems of at most 1024 rows run in one workgroup unless SLA_SMALL=0;
+    both forms against the oracle, forward and adjoint."""
+    if small == "multi_kernel":
+        monkeypatch.setenv("SLA_SMALL", "0")
+    p = SMALL[key]()
+    assert p.A.n <= 1024
+    x_ref, st, it, _ = oracle.pcg(p.A, p.G, p.eps, p.b, p.rtol, p.maxit)
+    w = np.random.default_rng(21).standard_normal(p.A.n)
+    lam_ref, g_ref, _, it_a, _ = oracle.adjoint(p.A, p.G, p.eps, x_ref, w, p.rtol, p.maxit)
+    say("small system", key, small, p.A.n)
+    A, G = handles(p)
+    x, info = B.sla_pcg_solve(A, G, p.eps, tdev(p.b), rtol=p.rtol, maxit=p.maxit)
+    assert info.status == B.OK and iters_close(info.iterations, it), (info.iterations, it)
+    assert rel(host(x), x_ref) <= 1e-8
+    gb, gv, ainfo = B.sla_pcg_adjoint(A, G, p.eps, x, tdev(w), rtol=p.rtol, maxit=p.maxit)
+    assert iters_close(ainfo.iterations, it_a)
+    assert rel(host(gb), lam_ref) <= 1e-7 and rel(host(gv), g_ref) <= 1e-7
+    # fp32 storage
+    p32 = p.astype("f32")
+    A32, G32 = handles(p32, dtype="f32")
+    x32, info32 = B.sla_pcg_solve(A32, G32, p.eps, tdev(p32.b), rtol=1e-5, maxit=p.maxit)
+    assert info32.status in (B.OK, B.NOT_CONVERGED)
+    b64 = p32.b.astype(np.float64)
+    res = oracle.spmv(p32.A.astype(np.float64), host(x32)) - b64
+    assert np.linalg.norm(res) <= 1e-3 * np.linalg.norm(b64)
+
+
+def test_small_system_wide_rows_fall_back():
+    """Rows wider than the one-workgroup solver keeps in registers take the
+    multi-kernel path, with the same results."""
+    rng = np.random.default_rng(23)
+    A = I.random_spd_csr(900, rng, max_deg=14)
+    G = I.spai_factor(A, np.random.default_rng(24))
+    b = rng.standard_normal(A.n)
+    x_ref, st, it, _ = oracle.pcg(A, G, 3e-3, b, 1e-10, 2000)
+    say("small system with wide rows", A.n)
+    Ah, Gh = create(A), create(G, transpose=True)
+    x, info = B.sla_pcg_solve(Ah, Gh, 3e-3, tdev(b), rtol=1e-10, maxit=2000)
     assert info.status == B.OK and iters_close(info.iterations, it)
     assert rel(host(x), x_ref) <= 1e-8

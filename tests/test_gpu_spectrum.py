@@ -26,7 +26,9 @@ KEYS = ["c0", "poisson3d_13", "bsr_elastic_6", "powerlaw_20k"]
 @pytest.fixture(params=["auto", "fused", "unfused"])
 def fusion(request, monkeypatch):
     if request.param != "auto":
+        # the explicit forms also keep small systems off the one-workgroup solver
         monkeypatch.setenv("SLA_FUSION", request.param)
+        monkeypatch.setenv("SLA_SMALL", "0")
     return request.param
 
 
