@@ -42,6 +42,12 @@ constexpr int kBsrLanes = 32;
 constexpr int kBsrTileRows = kWG / kBsrLanes;
 // Ring sizes of the per-iteration scalars kept on the device.
 constexpr int kRing = 4;
+// Index of entry (r, c) of local block row li in the BSR sliced-ELL value
+// array, for the slot whose first block is slot_blk.
+__host__ __device__ inline size_t bsell_val(int slot_blk, int r, int c, int li) {
+  return (size_t)slot_blk * 9 + (size_t)(63 * c + 21 * r + li);
+}
+
 // Right-hand sides advanced together by one pass of the multi-RHS solver.
 constexpr int kMaxRhs = 8;
 
@@ -101,7 +107,10 @@ struct MatView {
   // soff[s] + 64 j + l; padding slots have column -1 and value 0.
   // For 3x3 BSR the same fields hold the block form: slice s holds block
   // rows [21 s, 21 s + 21); block slot j of local block row i sits at
-  // soff[s] + 21 j + i (9 values each, row-major), columns are block columns.
+  // soff[s] + 21 j + i (its block column in sc).  The 21 blocks of a slot
+  // keep their 189 values component-major: entry (r, c) of local block i at
+  // 9 (soff[s] + 21 j) + 63 c + 21 r + i (bsell_val), so one load per
+  // component c reads 63 consecutive values for the slice's 63 scalar rows.
   const void* sv = nullptr;
   const int32_t* sc = nullptr;   // absolute columns, or
   const int16_t* sd = nullptr;   // column - row offsets (preferred when they fit)

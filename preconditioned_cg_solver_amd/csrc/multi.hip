@@ -455,10 +455,10 @@ __global__ __launch_bounds__(kWG) void mbsell_step(MArgs<T> a) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         // loads past the slice end stay inside the arrays' padding tail
-        const int blk = off + (j + u) * kBSlice + li;
-        bc[u] = ld_stream<true>(a.sc + blk);
+        const int slot = off + (j + u) * kBSlice;
+        bc[u] = ld_stream<true>(a.sc + slot + li);
 #pragma unroll
-        for (int e = 0; e < 3; ++e) bv[u][e] = ld_stream<true>(a.sv + (size_t)blk * 9 + 3 * r + e);
+        for (int e = 0; e < 3; ++e) bv[u][e] = ld_stream<true>(a.sv + bsell_val(slot, r, e, li));
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {

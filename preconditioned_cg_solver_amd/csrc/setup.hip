@@ -414,12 +414,14 @@ __global__ void bsell_fill(const int* __restrict__ rp, const int* __restrict__ c
   const int off = soff[sl], w = (soff[sl + 1] - off) / kBSlice;
   const int kb = I < nbr ? rp[I] : 0, len = I < nbr ? rp[I + 1] - kb : 0;
   for (int j = 0; j < w; ++j) {
-    const size_t dst = (size_t)off + (size_t)j * kBSlice + li;
+    const int slot = off + j * kBSlice;
+    const size_t dst = (size_t)slot + li;
     if (j < len) {
-      for (int e = 0; e < 9; ++e) sv[dst * 9 + e] = v[(size_t)(kb + j) * 9 + e];
+      for (int e = 0; e < 9; ++e)
+        sv[bsell_val(slot, e / 3, e % 3, li)] = v[(size_t)(kb + j) * 9 + e];
       sc[dst] = ci[kb + j];
     } else {
-      for (int e = 0; e < 9; ++e) sv[dst * 9 + e] = T(0);
+      for (int e = 0; e < 9; ++e) sv[bsell_val(slot, e / 3, e % 3, li)] = T(0);
       sc[dst] = -1;
     }
   }

@@ -642,10 +642,10 @@ __global__ __launch_bounds__(kWG) void bsell_step(StepArgs<T> a) {
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int blk = hoff + u * kBSlice + li;
-      hc[u] = ld_stream<NT>(a.sc + blk);
+      const int slot = hoff + u * kBSlice;
+      hc[u] = ld_stream<NT>(a.sc + slot + li);
 #pragma unroll
-      for (int c = 0; c < 3; ++c) hv[u][c] = ld_stream<NT>(a.sv + (size_t)blk * 9 + 3 * r + c);
+      for (int c = 0; c < 3; ++c) hv[u][c] = ld_stream<NT>(a.sv + bsell_val(slot, r, c, li));
     }
   };
   if (t0 < t1) load_head(t0 * kWaves + wv);
@@ -695,10 +695,10 @@ __global__ __launch_bounds__(kWG) void bsell_step(StepArgs<T> a) {
       int bc[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int blk = off + (j + u) * kBSlice + li;
-        bc[u] = ld_stream<NT>(a.sc + blk);
+        const int slot = off + (j + u) * kBSlice;
+        bc[u] = ld_stream<NT>(a.sc + slot + li);
 #pragma unroll
-        for (int c = 0; c < 3; ++c) bv[u][c] = ld_stream<NT>(a.sv + (size_t)blk * 9 + 3 * r + c);
+        for (int c = 0; c < 3; ++c) bv[u][c] = ld_stream<NT>(a.sv + bsell_val(slot, r, c, li));
       }
       consume(bv, bc, j);
     }
@@ -1153,8 +1153,17 @@ hipError_t launch_step(const sla_mat& m, const StepArgs<T>& a, int grid, hipStre
     if (nt) hipLaunchKernelGGL((csr_step<T, MODE, true>), dim3(grid), dim3(kWG), 0, s, a);
     else hipLaunchKernelGGL((csr_step<T, MODE, false>), dim3(grid), dim3(kWG), 0, s, a);
   } else if (a.sc) {
-    if (nt) hipLaunchKernelGGL((bsell_step<T, MODE, true, 4>), dim3(grid), dim3(kWG), 0, s, a);
-    else hipLaunchKernelGGL((bsell_step<T, MODE, false, 4>), dim3(grid), dim3(kWG), 0, s, a);
+    // block slots per load round: 4 for wide block rows, else 2 (fewer
+    // registers, more waves in flight; measured on the 27-point block stencil
+    // and its block triangles)
+    const dim3 g(grid), b(kWG);
+    if (a.sell_w > 16) {
+      if (nt) hipLaunchKernelGGL((bsell_step<T, MODE, true, 4>), g, b, 0, s, a);
+      else hipLaunchKernelGGL((bsell_step<T, MODE, false, 4>), g, b, 0, s, a);
+    } else {
+      if (nt) hipLaunchKernelGGL((bsell_step<T, MODE, true, 2>), g, b, 0, s, a);
+      else hipLaunchKernelGGL((bsell_step<T, MODE, false, 2>), g, b, 0, s, a);
+    }
   } else {
     if (nt) hipLaunchKernelGGL((bsr3_step<T, MODE, true>), dim3(grid), dim3(kWG), 0, s, a);
     else hipLaunchKernelGGL((bsr3_step<T, MODE, false>), dim3(grid), dim3(kWG), 0, s, a);
