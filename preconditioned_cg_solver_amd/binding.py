@@ -157,6 +157,23 @@ class Mat:
         return self._keep[0].device
 
 
+def sla_mat_destroy(A: Mat) -> None:
+    A.destroy()
+
+
+def sla_mat_info(A: Mat) -> Tuple[int, int, int, int]:
+    """(n, nnz, block_dim, dtype code) as the library records them."""
+    n, nnz = ctypes.c_int64(), ctypes.c_int64()
+    bd, dt = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().sla_mat_info(A.handle, ctypes.byref(n), ctypes.byref(nnz), ctypes.byref(bd),
+                              ctypes.byref(dt)))
+    return n.value, nnz.value, bd.value, dt.value
+
+
+def sla_last_error() -> str:
+    return lib().sla_last_error().decode(errors="replace")
+
+
 def sla_csr_create(row_ptr: torch.Tensor, col_idx: torch.Tensor, vals: torch.Tensor,
                    build_transpose: bool = False, validate: bool = False, stream=None) -> Mat:
     n = row_ptr.numel() - 1
@@ -208,6 +225,12 @@ def sla_spmv(A: Mat, x: torch.Tensor, y: Optional[torch.Tensor] = None, stream=N
     f = lib().sla_spmv_t if transpose else lib().sla_spmv
     _check(f(A.handle, _ptr(x), _ptr(y), _stream(stream)))
     return y
+
+
+def sla_spmv_t(A: Mat, x: torch.Tensor, y: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    """y = A^T x (the handle must carry its transpose)."""
+    return sla_spmv(A, x, y, stream, transpose=True)
 
 
 def sla_pcg_workspace_size(A: Mat) -> int:

@@ -54,6 +54,12 @@ def test_null_handle_is_rejected_without_gpu(libsla):
     assert libsla.sla_last_error()
 
 
+def test_every_entry_point_has_a_binding_of_the_same_name():
+    from preconditioned_cg_solver_amd import binding
+    missing = [n for n in declared_functions() if not callable(getattr(binding, n, None))]
+    assert not missing, missing
+
+
 def test_binding_has_the_same_names():
     from preconditioned_cg_solver_amd import binding
     for name in ("sla_csr_create", "sla_bsr_create", "sla_spmv", "sla_pcg_workspace_size",
