@@ -31,7 +31,7 @@ def flags():
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
             # never emit packed fp32 arithmetic (see the design notes)
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
+            "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wextra", "-Wno-unused-function"]
 
 
 def build(verbose: bool = False) -> str:

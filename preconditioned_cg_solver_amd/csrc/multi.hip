@@ -297,7 +297,7 @@ __device__ __forceinline__ void mfinish(const MArgs<T>& a, double (&dot)[K], dou
       double v = dot[0];
 #pragma unroll
       for (int c = 1; c < K; ++c)
-        if (threadIdx.x == c) v = dot[c];
+        if ((int)threadIdx.x == c) v = dot[c];
       a.pout[(size_t)blockIdx.x * K + threadIdx.x] = v;
     }
   }
@@ -646,7 +646,7 @@ __global__ __launch_bounds__(kWG) void minit(const T* __restrict__ b, int ldb, T
     double v = dot[0];
 #pragma unroll
     for (int c = 1; c < K; ++c)
-      if (threadIdx.x == c) v = dot[c];
+      if ((int)threadIdx.x == c) v = dot[c];
     pout[(size_t)blockIdx.x * K + threadIdx.x] = v;
   }
 }

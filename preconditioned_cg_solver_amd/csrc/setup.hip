@@ -54,7 +54,7 @@ __global__ __launch_bounds__(kWG) void scan_tiles(const int* __restrict__ in, in
   __syncthreads();
   // Hillis-Steele inclusive scan of the per-thread totals (integers: exact).
   for (int off = 1; off < kWG; off <<= 1) {
-    const int add = threadIdx.x >= off ? s_t[threadIdx.x - off] : 0;
+    const int add = (int)threadIdx.x >= off ? s_t[threadIdx.x - off] : 0;
     __syncthreads();
     s_t[threadIdx.x] += add;
     __syncthreads();
@@ -301,8 +301,8 @@ __device__ __forceinline__ int row_of(const int* __restrict__ rp, int nbr, int k
 }
 
 template <typename T>
-__global__ void transpose_fill(const int* __restrict__ rp, const int* __restrict__ ci,
-                               const T* __restrict__ v, int nbr, int nnzb, int bs,
+__global__ void transpose_fill(const int* __restrict__ rp, const T* __restrict__ v, int nbr,
+                               int nnzb, int bs,
                                const int* __restrict__ order, int* __restrict__ t_ci,
                                T* __restrict__ t_v) {
   for (int p = blockIdx.x * blockDim.x + threadIdx.x; p < nnzb; p += gridDim.x * blockDim.x) {
@@ -532,10 +532,10 @@ sla_status build_transpose(const sla_mat& m, int32_t** t_rp_out, int32_t** t_ci_
   }
   if (m.dtype == SLA_F64)
     hipLaunchKernelGGL(transpose_fill<double>, dim3(grid_for(nnzb)), dim3(kWG), 0, s, m.fwd.rp,
-                       m.fwd.ci, (const double*)m.fwd.v, nbr, nnzb, bs, vin, t_ci, (double*)t_v);
+                       (const double*)m.fwd.v, nbr, nnzb, bs, vin, t_ci, (double*)t_v);
   else
     hipLaunchKernelGGL(transpose_fill<float>, dim3(grid_for(nnzb)), dim3(kWG), 0, s, m.fwd.rp,
-                       m.fwd.ci, (const float*)m.fwd.v, nbr, nnzb, bs, vin, t_ci, (float*)t_v);
+                       (const float*)m.fwd.v, nbr, nnzb, bs, vin, t_ci, (float*)t_v);
   SLA_HIP(hipGetLastError());
   SLA_HIP(hipFreeAsync(work, s));
   SLA_HIP(hipStreamSynchronize(s));
