@@ -102,6 +102,7 @@ struct MatView {
   int nlong = 0;                 // long-row chunks among the tiles
   int nlong_rows = 0;            // rows split into chunks
   int n_long_part = 0;           // partial slots needed by the long-row chunks
+  const int* long_rows = nullptr;  // row index of each of the nlong_rows long rows (CSR)
   // SELL-64 copy (owned), built once when the rows qualify: slice s holds
   // rows [64 s, 64 s + 64); slot j of its row 64 s + l sits at
   // soff[s] + 64 j + l; padding slots have column -1 and value 0.

@@ -73,6 +73,8 @@ struct MArgs {
   int ntiles;
   int nbr;
   int n;
+  const int* long_rows;  // CSR rows longer than a tile (one workgroup each)
+  int nlong;
   int ld;        // row stride of the gathered / owned vectors
   const T* in0;  // gathered: X, Z (A step), R_{k-1} (G^T step), T (G step)
   const T* in1;  // gathered second operand: P_{k-1} (A step), Q (G^T step)
@@ -483,7 +485,9 @@ __global__ __launch_bounds__(kWG) void mbsell_step(MArgs<T> a) {
 // ---------------------------------------------------------------------------
 // Row engine for every other matrix (CSR without the sliced layout, BSR
 // without it): one lane per scalar row walks the row's entries in storage
-// order.  Not tuned: long rows serialise on one lane.
+// order; CSR rows longer than a tile (kLdsCap) are taken by a whole
+// workgroup each (lanes stride over the entries, then a fixed-order
+// workgroup sum), so a hub row does not serialise on one lane.
 // ---------------------------------------------------------------------------
 
 template <typename T, int MODE, int K, int BS>
@@ -503,6 +507,7 @@ __global__ __launch_bounds__(kWG) void mrow_step(MArgs<T> a) {
     for (int c = 0; c < K; ++c) acc[c] = T(0);
     const int I = BS == 1 ? i : i / 3, r = BS == 1 ? 0 : i - 3 * (i / 3);
     const int e0 = a.rp[I], e1 = a.rp[I + 1];
+    if (BS == 1 && e1 - e0 > kLdsCap) continue;  // below
     for (int e = e0; e < e1; ++e) {
       const int J = a.ci[e];
 #pragma unroll
@@ -514,6 +519,33 @@ __global__ __launch_bounds__(kWG) void mrow_step(MArgs<T> a) {
       }
     }
     mepi<T, MODE, K>(a, i, acc, cf, o, dot);
+  }
+  if constexpr (BS == 1) {
+    for (int q = blockIdx.x; q < a.nlong; q += gridDim.x) {
+      const int i = a.long_rows[q];
+      const int e0 = a.rp[i], e1 = a.rp[i + 1];
+      T acc[K];
+#pragma unroll
+      for (int c = 0; c < K; ++c) acc[c] = T(0);
+      for (int e = e0 + threadIdx.x; e < e1; e += kWG) {
+        const T vu = a.v[e];
+        const size_t base = (size_t)a.ci[e] * a.ld;
+#pragma unroll
+        for (int c = 0; c < K; ++c) acc[c] = fma(vu, mgat<T, MODE, K>(a, base, c, cf), acc[c]);
+      }
+      double sum[K];
+#pragma unroll
+      for (int c = 0; c < K; ++c) sum[c] = (double)acc[c];
+      block_sum_k<K>(sum, s_red);
+      if (threadIdx.x == 0) {
+        MOwn<T, K> o;
+        mown_load<T, MODE, K>(a, i, o);
+        T tot[K];
+#pragma unroll
+        for (int c = 0; c < K; ++c) tot[c] = T(sum[c]);
+        mepi<T, MODE, K>(a, i, tot, cf, o, dot);
+      }
+    }
   }
   mfinish<T, MODE, K>(a, dot, s_red);
 }
@@ -689,6 +721,8 @@ void fill_mat(MArgs<T>& a, const sla_mat& m, const MatView& v) {
   a.v = (const T*)v.v;
   a.nbr = (int)m.nbr;
   a.n = (int)m.n();
+  a.long_rows = m.bs == 1 ? v.long_rows : nullptr;
+  a.nlong = m.bs == 1 && v.long_rows ? v.nlong_rows : 0;
   if (v.sell) {
     a.sv = (const T*)v.sv;
     a.sc = v.sd ? nullptr : v.sc;

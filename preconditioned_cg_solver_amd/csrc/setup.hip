@@ -154,6 +154,7 @@ struct CountEmit {
 struct WriteEmit {
   const int* rp;
   Tile* out;
+  int* lrows;  // row index of every long row, in long-row order
   int t, lr, ch;
   __device__ void lds(int a, int b, int nnz) {
     const int rows = b - a;
@@ -185,6 +186,7 @@ struct WriteEmit {
       d.pad[2] = ch;
       out[t++] = d;
     }
+    lrows[lr] = row;
     lr += 1;
     ch += nc;
   }
@@ -203,10 +205,10 @@ __global__ void tiling_count(const int* __restrict__ rp, int n, int nblk, int* _
 
 __global__ void tiling_write(const int* __restrict__ rp, int n, int nblk, const int* __restrict__ ot,
                              const int* __restrict__ ol, const int* __restrict__ oc,
-                             Tile* __restrict__ out) {
+                             Tile* __restrict__ out, int* __restrict__ lrows) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= nblk) return;
-  WriteEmit em{rp, out, ot[b], ol[b], oc[b]};
+  WriteEmit em{rp, out, lrows, ot[b], ol[b], oc[b]};
   pack_block(rp, b * kTileRows, min(n, (b + 1) * kTileRows), em);
 }
 
@@ -462,10 +464,13 @@ sla_status build_tiling(const int32_t* d_rp, int64_t n, MatView& view, void** ow
   SLA_HIP(hipMemcpyAsync(&tot[1], ol + nblk, sizeof(int), hipMemcpyDeviceToHost, s));
   SLA_HIP(hipMemcpyAsync(&tot[2], oc + nblk, sizeof(int), hipMemcpyDeviceToHost, s));
   SLA_HIP(hipStreamSynchronize(s));
+  // one allocation: the tiles, then the row index of every long row
   Tile* tiles = nullptr;
-  SLA_HIP(hipMalloc((void**)&tiles, sizeof(Tile) * (size_t)std::max(1, tot[0])));
+  SLA_HIP(hipMalloc((void**)&tiles, sizeof(Tile) * (size_t)std::max(1, tot[0]) +
+                                        sizeof(int) * (size_t)std::max(1, tot[1])));
+  int* lrows = (int*)(tiles + std::max(1, tot[0]));
   hipLaunchKernelGGL(tiling_write, dim3((nblk + 127) / 128), dim3(128), 0, s, d_rp, (int)n, nblk,
-                     (const int*)ot, (const int*)ol, (const int*)oc, tiles);
+                     (const int*)ot, (const int*)ol, (const int*)oc, tiles, lrows);
   SLA_HIP(hipGetLastError());
   SLA_HIP(hipFreeAsync(buf, s));
   SLA_HIP(hipStreamSynchronize(s));
@@ -475,6 +480,7 @@ sla_status build_tiling(const int32_t* d_rp, int64_t n, MatView& view, void** ow
   view.nlong_rows = tot[1];
   view.n_long_part = tot[2];
   view.nlong = tot[2];
+  view.long_rows = lrows;
   return SLA_OK;
 }
 
