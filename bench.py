@@ -21,6 +21,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -29,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+METRIC = "PCG iters/sec + SpMV HBM GB/s (% of peak), 3D Poisson 128^3 fp64, 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_a_step_poisson3d_128.json")
 KERNEL_SRC = os.path.join(ROOT, "preconditioned_cg_solver_amd", "csrc", "solver.hip")
 
@@ -37,15 +39,19 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(n, nnz_a, nnz_g, sv, si=4):
+def algorithmic_bytes(A, G, sv, si=4):
     """Bytes the method must move (each matrix stream once, each vector once
-    per kernel, gathers counted once), per SpMV and per fused kernel."""
-    def spmv(nnz):
-        return (sv + si) * nnz + si * (n + 1) + 2 * sv * n
-    a_step = spmv(nnz_a) + 3 * sv * n + 3 * sv * n      # SpMV(A) + p update + x update
-    gt_step = spmv(nnz_g) + 3 * sv * n                  # SpMV(G^T) + r update
-    g_step = spmv(nnz_g) + sv * n                       # SpMV(G) + eps r
-    return {"spmv_A": spmv(nnz_a), "a_step": a_step, "gt_step": gt_step, "g_step": g_step,
+    per kernel, gathers counted once), per SpMV and per fused kernel; CSR
+    counts (sv + si) bytes per nonzero, 3x3 BSR (9 sv + si) per block."""
+    n = A.n
+
+    def spmv(M):
+        per = (sv + si) * M.nnz if M.block_dim == 1 else (9 * sv + si) * M.nnzb
+        return per + si * (M.n_block_rows + 1) + 2 * sv * n
+    a_step = spmv(A) + 3 * sv * n + 3 * sv * n          # SpMV(A) + p update + x update
+    gt_step = spmv(G) + 3 * sv * n                      # SpMV(G^T) + r update
+    g_step = spmv(G) + sv * n                           # SpMV(G) + eps r
+    return {"spmv_A": spmv(A), "a_step": a_step, "gt_step": gt_step, "g_step": g_step,
             "iteration": a_step + gt_step + g_step}
 
 
@@ -60,10 +66,19 @@ def sell_slots(M):
     return int(w.sum() * 64), ns
 
 
-def moved_bytes_a_step(A, n, sv=8, col_bytes=2):
-    """Bytes the fused A step physically streams with the SELL-64 layout and
-    16-bit column offsets: values + column offsets + slice offsets, z, p_old
-    and x read, x, p_new and q written (gathers counted once)."""
+def moved_bytes_a_step(A, n, sv=8):
+    """Bytes the fused A step physically streams with the SELL-64 layout
+    (16-bit column offsets where every |col - row| fits): values + column
+    words + slice offsets, z, p_old and x read, x, p_new and q written
+    (gathers counted once); None for matrices outside that layout."""
+    import numpy as np
+    if A.block_dim != 1:
+        return None
+    lens = np.diff(A.row_ptr.astype(np.int64))
+    if lens.max(initial=0) > 32:
+        return None
+    rows = np.repeat(np.arange(A.n), lens)
+    col_bytes = 2 if np.abs(A.col_idx.astype(np.int64) - rows).max(initial=0) <= 32767 else 4
     slots, ns = sell_slots(A)
     return slots * (sv + col_bytes) + 4 * (ns + 1) + 6 * sv * n
 
@@ -165,10 +180,11 @@ def _short_kernel(nm):
     return nm if len(nm) <= 48 else nm[:45] + "..."
 
 
-def summarize_trace(trace_dir, bench_json=None):
+def summarize_trace(trace_dir, bench_json=None, trace_args="--steps 2 --warmup 1 --no-cpu-baseline"):
     """Per-kernel table of a rocprofv3 --kernel-trace --stats run of this benchmark
-    (profiles/kernel_trace_poisson3d_128.md); launches under 10 us are the
-    early-out launches of a batch that ends after convergence."""
+    (profiles/kernel_trace_<workload>.md).  A launch counts as working when it
+    runs longer than half its kernel's median launch: the others (1-5 us) are
+    the early-out launches of a batch that ends after convergence."""
     import csv
     import glob
     recs = []
@@ -183,35 +199,42 @@ def summarize_trace(trace_dir, bench_json=None):
     for t0, t1, k in recs:
         by.setdefault(k, []).append((t1 - t0) / 1e3)
     rows = sorted(by.items(), key=lambda kv: -sum(kv[1]))
+    cut = {k: 0.5 * statistics.median(d) for k, d in by.items()}
     lines = ["| kernel | calls | avg us (all) | % time | working launches | avg us (working) |",
              "|---|---|---|---|---|---|"]
     for k, d in rows[:16]:
-        w = [v for v in d if v > 10.0] or d
+        w = [v for v in d if v > cut[k]] or d
         lines.append(f"| `{k}` | {len(d)} | {statistics.fmean(d):.2f} | "
                      f"{100 * sum(d) * 1e3 / total:.2f} | {len(w)} | {statistics.fmean(w):.2f} |")
     step = [(t0, t1) for t0, t1, k in recs
             if k.split("<")[0] in ("sell_step", "csr_step", "bsell_step", "bsr3_step")
-            and (t1 - t0) > 10000]
+            and (t1 - t0) / 1e3 > cut[k]]
     gaps = sorted(max(0, b0 - a1) / 1e3 for (a0, a1), (b0, b1) in zip(step, step[1:]))
-    a_key = next((k for k, _ in rows if k.startswith("sell_step<double, 2,")), None)
-    a_work = [v for v in by.get(a_key, []) if v > 10.0]
+    a_key = next((k for k, _ in rows
+                  if re.match(r"(sell_step|bsell_step|csr_step|bsr3_step)<\w+, (2|8),", k)), None)
+    a_work = [v for v in by.get(a_key, []) if v > cut[a_key]]
     cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d {d} -o bench -- "
-           "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline").format(d=trace_dir)
-    md = ["# Kernel trace of bench.py, 3D Poisson 128^3 fp64 (PCG + factorised SPAI, "
-          "forward + adjoint)", "", "Command (from the repository root, `export TMPDIR=/tmp`):",
+           "python -u bench.py {a}").format(d=trace_dir, a=trace_args)
+    rec = json.loads(open(bench_json).read().strip().splitlines()[-1]) if bench_json else None
+    workload = rec["config"]["workload"] if rec else "poisson3d_128 (3D Poisson 128^3 fp64)"
+    name = workload.split(" ")[0] + ("_f32" if rec and rec.get("dtype") == "f32" else "")
+    md = [f"# Kernel trace of bench.py, {workload}", "",
+          "Command (from the repository root, `export TMPDIR=/tmp`):",
           "", "    " + cmd, f"    python bench.py --trace-summary {trace_dir}"
-          + (f" {bench_json}" if bench_json else ""), "",
-          "`sell_step<T, MODE, NT, I16, U>`: MODE 2 = A step, 4 = G^T step, 6 = G step",
-          "(1, 3, 5: their first-iteration / start-up forms, 0 = plain SpMV); NT =",
-          "non-temporal matrix stream; I16 = 16-bit column offsets; U = slots per load",
+          + (f" {bench_json}" if bench_json else "")
+          + (f" --trace-args '{trace_args}'" if trace_args != "--steps 2 --warmup 1 "
+             "--no-cpu-baseline" else ""), "",
+          "Step kernels `<T, MODE, ...>`: MODE 2 = A step, 4 = G^T step, 6 = G step",
+          "(1, 3, 5: their first-iteration / start-up forms, 0 = plain SpMV, 8 and 9 the",
+          "A and G^T products of the separate iteration form); for `sell_step` NT =",
+          "non-temporal matrix stream, I16 = 16-bit column offsets, U = slots per load",
           "batch.  \"calls\" counts every launch, including the launches of a batch that",
-          "return at once after convergence; \"working launches\" keeps those over 10 us",
-          "(the ones that did the product).", "", *lines, ""]
+          "return at once after convergence; \"working launches\" keeps those longer than",
+          "half the kernel's median launch (the ones that did the product).", "", *lines, ""]
     if a_work:
         md.append(f"The A step (`{a_key}`) averages {statistics.fmean(a_work):.2f} us per "
                   "working launch here.")
-    if bench_json:
-        rec = json.loads(open(bench_json).read().strip().splitlines()[-1])
+    if rec and rec["roofline"].get("avg_launch_us"):
         md.append("bench.py's own HIP-event measurement of the same kernel over its timed steps "
                   f"gave {rec['roofline']['avg_launch_us']:.2f} us (`roofline.avg_launch_us` of a "
                   "bench run of the same tree).")
@@ -219,30 +242,43 @@ def summarize_trace(trace_dir, bench_json=None):
         md += ["", f"Gaps between consecutive working step kernels: median "
                f"{statistics.median(gaps):.2f} us, mean {statistics.fmean(gaps):.2f} us, 90th "
                f"percentile {gaps[int(0.9 * len(gaps))]:.2f} us over {len(gaps)} boundaries."]
-    with open(os.path.join(ROOT, "profiles", "kernel_trace_poisson3d_128.md"), "w") as f:
+    with open(os.path.join(ROOT, "profiles", f"kernel_trace_{name}.md"), "w") as f:
         f.write("\n".join(md) + "\n")
     print("\n".join(lines))
 
 
-def cpu_baseline(p, w, min_seconds):
+def cpu_baseline(p, w, min_seconds, expected_iters):
     """The oracle on the host cores doing the benchmark's step minus the handle
     set-up: the full forward PCG solve and the full adjoint solve on the same
-    input, repeated until at least min_seconds have passed (at most 20 times)."""
+    input, repeated until at least min_seconds have passed (at most 20 times).
+    When one such pair would take more than three times min_seconds (the large
+    workloads), both solves are cut at the same iteration cap instead, sized from
+    a 3-iteration probe so that the pair takes about min_seconds: the rate is
+    then iterations per second over truncated solves, said so in the sample."""
     import oracle
     log(f"cpu oracle: forward + adjoint solves for >= {min_seconds:.0f} s, "
         f"{oracle.num_threads()} threads")
+    t0 = time.perf_counter()
+    _, _, it, _ = oracle.pcg(p.A, p.G, p.eps, p.b, p.rtol, min(3, p.maxit))
+    per_it = (time.perf_counter() - t0) / max(it, 1)
+    cap = p.maxit
+    if per_it * expected_iters > 3 * min_seconds:
+        cap = max(3, int(min_seconds / per_it / 2))
     its, reps = 0, 0
     t0 = time.perf_counter()
     while reps < 20 and (reps == 0 or time.perf_counter() - t0 < min_seconds):
-        x, st, it, _ = oracle.pcg(p.A, p.G, p.eps, p.b, p.rtol, p.maxit)
-        _, _, st2, it2, _ = oracle.adjoint(p.A, p.G, p.eps, x, w, p.rtol, p.maxit)
+        x, st, it, _ = oracle.pcg(p.A, p.G, p.eps, p.b, p.rtol, cap)
+        gx = w if w is not None else 2.0 * x      # dL/dx of <w, x>, or of sum(x^2)
+        _, _, st2, it2, _ = oracle.adjoint(p.A, p.G, p.eps, x, gx, p.rtol, cap)
         its += it + it2
         reps += 1
     dt = time.perf_counter() - t0
+    what = ("full forward PCG solve + full adjoint solve with dL/dA" if cap == p.maxit else
+            f"forward PCG solve + adjoint solve with dL/dA, each cut at {cap} iterations "
+            f"(the full pair runs {expected_iters} iterations on the GPU)")
     return {"value": its / dt, "unit": "iters/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{reps} x (full forward PCG solve + full adjoint solve with dL/dA) on "
-                      f"the same {round(p.A.n ** (1 / 3))}^3 input, {its} iterations in {dt:.1f} s (each solve "
-                      "includes the oracle's own G^T build)"}
+            "sample": f"{reps} x ({what}) on the same {p.name} input, {its} iterations in "
+                      f"{dt:.1f} s (each solve includes the oracle's own G^T build)"}
 
 
 def main():
@@ -250,7 +286,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--size", type=int, default=128, help="grid edge of the 3D Poisson workload")
+    ap.add_argument("--config", type=int, default=2, choices=range(5),
+                    help="workload: 0 2D Poisson 32^2, 1 heat 512^2, 2 3D Poisson 128^3 "
+                         "(the metric's), 3 elasticity BSR3 64^3, 4 power-law 4M")
+    ap.add_argument("--size", type=int, default=None,
+                    help="size parameter of the workload generator (grid edge; rows for 4)")
+    ap.add_argument("--dtype", default="f64", choices=("f64", "f32"))
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum host time of the CPU-oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -265,12 +306,14 @@ def main():
     ap.add_argument("--counter-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic summary under profiles/ from two rocprofv3 "
                          "--pmc runs of --counters-workload (no GPU needed)")
+    ap.add_argument("--trace-args", default="--steps 2 --warmup 1 --no-cpu-baseline",
+                    help="bench.py arguments of the traced run (for the summary's command)")
     ap.add_argument("--trace-summary", nargs="+", metavar="DIR",
-                    help="write profiles/kernel_trace_poisson3d_128.md from a rocprofv3 "
+                    help="write profiles/kernel_trace_<workload>.md from a rocprofv3 "
                          "--kernel-trace --stats run (and optionally a saved bench JSON line)")
     args = ap.parse_args()
     if args.trace_summary:
-        summarize_trace(*args.trace_summary[:2])
+        summarize_trace(*args.trace_summary[:2], trace_args=args.trace_args)
         return
     if args.counter_summary:
         summarize_counters(*args.counter_summary)
@@ -293,20 +336,35 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log("generating inputs")
-    p = I.make_problem(2, size=None if args.size == 128 else args.size)
+    p = I.make_problem(args.config, size=args.size)
+    if args.dtype == "f32":
+        p = p.astype("f32")
+    sv = 4 if args.dtype == "f32" else 8
+    tdt = torch.float32 if args.dtype == "f32" else torch.float64
     n, nnz_a, nnz_g = p.A.n, p.A.nnz, p.G.nnz
-    ab = algorithmic_bytes(n, nnz_a, nnz_g, 8)
+    ab = algorithmic_bytes(p.A, p.G, sv)
+    bs = p.A.block_dim
 
     def t(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
+    def mk(rp, ci, v, transpose=False):
+        if bs == 1:
+            return B.sla_csr_create(rp, ci, v, build_transpose=transpose)
+        return B.sla_bsr_create(rp, ci, v, block_dim=bs, build_transpose=transpose)
+
     a_rp, a_ci, a_v = t(p.A.row_ptr), t(p.A.col_idx), t(p.A.vals)
     g_rp, g_ci, g_v = t(p.G.row_ptr), t(p.G.col_idx), t(p.G.vals)
-    b, w = t(p.b), t(p.w)
+    b = t(p.b)
+    # dL/dx of the configuration's loss: <w, x> gives w, sum(x^2) gives 2x
+    w = t(p.w) if p.w is not None else None
     x = torch.empty_like(b)
     grad_b = torch.empty_like(b)
-    grad_vals = torch.empty(nnz_a, dtype=torch.float64, device=dev)
+    grad_vals = torch.empty(nnz_a, dtype=tdt, device=dev)
     work = None
+
+    def loss_grad(xv):
+        return w if w is not None else 2.0 * xv
 
     if args.counters_workload:
         src = torch.ones(32 * 1024 * 1024, dtype=torch.float64, device=dev)
@@ -314,14 +372,14 @@ def main():
         for _ in range(3):
             dst.copy_(src)                       # 256 MiB read + 256 MiB written
         torch.cuda.synchronize()
-        A = B.sla_csr_create(a_rp, a_ci, a_v)
-        G = B.sla_csr_create(g_rp, g_ci, g_v, build_transpose=True)
+        A = mk(a_rp, a_ci, a_v)
+        G = mk(g_rp, g_ci, g_v, transpose=True)
         work = B.workspace(A)
         B.sla_pcg_solve(A, G, p.eps, b, x=x, rtol=p.rtol, maxit=20, work=work)
-        B.sla_pcg_adjoint(A, G, p.eps, x, w, rtol=p.rtol, maxit=20, grad_b=grad_b,
+        B.sla_pcg_adjoint(A, G, p.eps, x, loss_grad(x), rtol=p.rtol, maxit=20, grad_b=grad_b,
                           grad_vals=grad_vals, work=work)
         # plain SpMV streaming its matrix from HBM: two copies of A alternately
-        A2 = B.sla_csr_create(a_rp.clone(), a_ci.clone(), a_v.clone())
+        A2 = mk(a_rp.clone(), a_ci.clone(), a_v.clone())
         y = torch.empty_like(b)
         for _ in range(4):
             B.sla_spmv(A, b, y)
@@ -332,12 +390,12 @@ def main():
 
     def step():
         nonlocal work
-        A = B.sla_csr_create(a_rp, a_ci, a_v)
-        G = B.sla_csr_create(g_rp, g_ci, g_v, build_transpose=True)
+        A = mk(a_rp, a_ci, a_v)
+        G = mk(g_rp, g_ci, g_v, transpose=True)
         if work is None:
             work = B.workspace(A)
         _, fi = B.sla_pcg_solve(A, G, p.eps, b, x=x, rtol=p.rtol, maxit=p.maxit, work=work)
-        _, _, ai = B.sla_pcg_adjoint(A, G, p.eps, x, w, rtol=p.rtol, maxit=p.maxit,
+        _, _, ai = B.sla_pcg_adjoint(A, G, p.eps, x, loss_grad(x), rtol=p.rtol, maxit=p.maxit,
                                      grad_b=grad_b, grad_vals=grad_vals, work=work)
         A.destroy()
         G.destroy()
@@ -364,14 +422,14 @@ def main():
     a_avg_s = a_ms / max(a_launches, 1) / 1e3
 
     # Outside the timed region: the parts of a step on their own.
-    A = B.sla_csr_create(a_rp, a_ci, a_v)
-    G = B.sla_csr_create(g_rp, g_ci, g_v, build_transpose=True)
+    A = mk(a_rp, a_ci, a_v)
+    G = mk(g_rp, g_ci, g_v, transpose=True)
     setup = []
     for _ in range(3):
         torch.cuda.synchronize()
         s0 = time.perf_counter()
-        H = B.sla_csr_create(g_rp, g_ci, g_v, build_transpose=True)
-        H2 = B.sla_csr_create(a_rp, a_ci, a_v)
+        H = mk(g_rp, g_ci, g_v, transpose=True)
+        H2 = mk(a_rp, a_ci, a_v)
         torch.cuda.synchronize()
         setup.append(time.perf_counter() - s0)
         H.destroy()
@@ -413,7 +471,7 @@ def main():
     # than the 256 MB Infinity Cache holds) called alternately, so each call
     # streams its matrix from HBM while x and y stay where the previous call
     # left them, as inside an iterative method
-    A2 = B.sla_csr_create(a_rp.clone(), a_ci.clone(), a_v.clone())
+    A2 = mk(a_rp.clone(), a_ci.clone(), a_v.clone())
     for _ in range(4):
         B.sla_spmv(A, b, y)
         B.sla_spmv(A2, b, y)
@@ -432,12 +490,12 @@ def main():
     # column 0, seeded N(0,1) columns after it): forward solves only
     multi = {}
     if args.multi_rhs:
-        A = B.sla_csr_create(a_rp, a_ci, a_v)
-        G = B.sla_csr_create(g_rp, g_ci, g_v, build_transpose=True)
+        A = mk(a_rp, a_ci, a_v)
+        G = mk(g_rp, g_ci, g_v, transpose=True)
         for k in args.multi_rhs:
             Bm = np.random.default_rng(100 + k).standard_normal((n, k))
             Bm[:, 0] = p.b
-            Bt = torch.from_numpy(Bm).to(dev)
+            Bt = torch.from_numpy(Bm).to(dev, tdt)
             Xt = torch.empty_like(Bt)
             wm = B.workspace_multi(A, k, dev)
             B.sla_pcg_solve_multi(A, G, p.eps, Bt, X=Xt, rtol=p.rtol, maxit=p.maxit, work=wm)
@@ -455,15 +513,37 @@ def main():
         A.destroy()
         G.destroy()
 
-    achieved = ab["a_step"] / a_avg_s / 1e9
-    traffic = traffic_if_current()
-    moved = moved_bytes_a_step(p.A, n)
+    # the A step's kernel: the one-workgroup solver (n <= 1024) has none of its own
+    has_a = a_launches > 0
+    achieved = ab["a_step"] / a_avg_s / 1e9 if has_a else None
+    headline = args.config == 2 and args.dtype == "f64" and n == 128 ** 3
+    traffic = traffic_if_current() if headline else None
+    moved = moved_bytes_a_step(p.A, n, sv)
+    if bs == 3:
+        a_kernel = "bsell_step<A step> (BSR sliced ELL, p = z + beta p_old formed on the fly)"
+    elif moved is not None:
+        a_kernel = ("sell_step<double, A step> (q = A p with p = z + beta p_old formed on the "
+                    "fly, x += alpha_prev p_old, p.q partials)")
+    else:
+        a_kernel = "csr_step<A product> (LDS tiles, separate p / r update passes)"
+    describe = {
+        0: "2D Poisson 5-point, 32^2 interior, CSR, PCG + factorised SPAI eps=3e-3, rtol=1e-10, "
+           "forward + adjoint of sum(x^2)",
+        1: "heat I + dt L5, 512^2, CSR, PCG + factorised SPAI eps=3e-3, rtol=1e-8, forward + "
+           "adjoint",
+        2: f"3D Poisson 7-point, {round(n ** (1 / 3))}^3 interior, fp64 CSR, PCG + factorised "
+           "SPAI eps=3e-3, rtol=1e-10, forward + adjoint",
+        3: "elasticity-like 27-point block system, 64^3 nodes x 3 dof, 3x3 BSR, PCG + "
+           "factorised SPAI eps=3e-3, rtol=1e-8, forward + adjoint",
+        4: "power-law random SPD, 4M rows, CSR, PCG + factorised SPAI eps=3e-3, rtol=1e-8, "
+           "forward + adjoint"}
     iter_gbs = ab["iteration"] * fi.iterations / tts / 1e9
     spmv_gbs = ab["spmv_A"] / spmv_s / 1e9
     spmv_cold_gbs = ab["spmv_A"] / spmv_cold_s / 1e9
     spmv_stream_gbs = ab["spmv_A"] / spmv_stream_s / 1e9
     result = {
-        "metric": "PCG iters/sec + SpMV HBM GB/s (% of peak), 3D Poisson 128^3 fp64, 1 GPU",
+        "metric": METRIC if headline else
+                  f"PCG iters/sec + SpMV HBM GB/s (% of peak), {p.name} {args.dtype}, 1 GPU",
         "value": total_iters / elapsed,
         "unit": "iters/s",
         "n_gpus": 1,
@@ -473,23 +553,22 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f64",
+        "dtype": args.dtype,
         "data": "synthetic",
-        "config": {"workload": f"poisson3d_{args.size} (3D Poisson 7-point, {args.size}^3 "
-                               "interior, fp64 CSR, PCG + factorised SPAI eps=3e-3, rtol=1e-10, "
-                               "forward + adjoint)",
+        "config": {"workload": f"{p.name} ({describe[args.config]})",
                    "n": n, "nnz_A": nnz_a, "nnz_G": nnz_g,
                    "iterations_forward": fi.iterations, "iterations_adjoint": ai.iterations,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm",
-                     "kernel": "sell_step<double, A step> (q = A p with p = z + beta p_old "
-                               "formed on the fly, x += alpha_prev p_old, p.q partials)",
+                     "kernel": a_kernel,
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": ab["a_step"],
                      "moved_bytes_per_launch": moved,
-                     "moved_GBps": moved / a_avg_s / 1e9,
-                     "avg_launch_us": a_avg_s * 1e6, "launches": a_launches},
+                     "moved_GBps": moved / a_avg_s / 1e9 if moved else None,
+                     "avg_launch_us": a_avg_s * 1e6, "launches": a_launches} if has_a else
+                    {"bound": "latency", "note": "the whole solve runs in one workgroup "
+                     "(n <= 1024): no per-step kernel to time"},
         "iteration": {"bytes": ab["iteration"], "GBps": iter_gbs, "frac": iter_gbs / HBM_PEAK_GBS,
                       "us_per_iteration": tts / fi.iterations * 1e6,
                       "time_to_solution_ms": tts * 1e3},
@@ -500,20 +579,21 @@ def main():
                           "us": spmv_cold_s * 1e6},
                  "warm": {"GBps": spmv_gbs, "frac": spmv_gbs / HBM_PEAK_GBS,
                           "us": spmv_s * 1e6},
-                 "note": "algorithmic CSR bytes over the kernel's duration (library "
-                         "events); hbm_stream = two copies of A (2 x 183 MB) called "
-                         "alternately so each call streams its matrix from HBM with x and "
+                 "note": "algorithmic bytes over the kernel's duration (library "
+                         "events); hbm_stream = two copies of A called alternately (more "
+                         "than the 256 MB Infinity Cache holds when A exceeds 128 MB), x and "
                          "y warm; cold = median of 10 calls, each after a 1 GiB read-only "
                          "flush of every cache (x included); warm = back-to-back calls "
-                         "with A held in the 256 MB Infinity Cache"},
+                         "(A held in the Infinity Cache when it fits)"},
         "setup_ms": statistics.median(setup) * 1e3,
         "multi_rhs": {"note": "k right-hand sides solved together on the same A and G "
-                              "(forward solves, fp64); column-iterations per second and the "
+                              f"(forward solves, {args.dtype}); column-iterations per second and the "
                               "ratio to the single-right-hand-side forward rate",
                       **multi} if multi else None,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(p, p.w, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(p, p.w, args.cpu_seconds,
+                                              fi.iterations + ai.iterations)
     print(json.dumps(result), flush=True)
 
 
