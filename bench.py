@@ -55,6 +55,17 @@ def algorithmic_bytes(A, G, sv, si=4):
             "iteration": a_step + gt_step + g_step}
 
 
+def fused_iteration(A):
+    """Whether the library runs the fused iteration on A (p and r formed inside
+    the products' gathers): CSR matrices in the SELL-64 layout, unless
+    SLA_FUSION overrides.  Otherwise the A kernel is the bare product q = A p
+    (with p.q) and the p, x and r updates run as separate streaming passes."""
+    e = os.environ.get("SLA_FUSION")
+    if e in ("fused", "unfused"):
+        return e == "fused"
+    return A.block_dim == 1 and sell_layout(A)
+
+
 def sell_slots(M):
     """Slots of the SELL-64 copy the library builds for short-row CSR (each
     64-row slice padded to its longest row)."""
@@ -64,6 +75,17 @@ def sell_slots(M):
     w = np.zeros(ns, np.int64)
     np.maximum.at(w, np.arange(M.n) // 64, lens)
     return int(w.sum() * 64), ns
+
+
+def sell_layout(A):
+    """Whether the library keeps a CSR matrix in the SELL-64 layout: rows of at
+    most 32 entries, slices padded by at most 25 %."""
+    import numpy as np
+    lens = np.diff(A.row_ptr.astype(np.int64))
+    if A.nnz == 0 or lens.max(initial=0) > 32:
+        return False
+    slots, _ = sell_slots(A)
+    return slots * 100 <= A.nnz * 125
 
 
 def moved_bytes_a_step(A, n, sv=8):
@@ -513,19 +535,26 @@ def main():
         A.destroy()
         G.destroy()
 
-    # the A step's kernel: the one-workgroup solver (n <= 1024) has none of its own
+    # the A step's kernel: the one-workgroup solver (n <= 1024) has none of its own;
+    # in the separate iteration form it is the bare product q = A p (p.q partials)
     has_a = a_launches > 0
-    achieved = ab["a_step"] / a_avg_s / 1e9 if has_a else None
+    fused = fused_iteration(p.A)
+    a_bytes = ab["a_step"] if fused else ab["spmv_A"]
+    achieved = a_bytes / a_avg_s / 1e9 if has_a else None
     headline = args.config == 2 and args.dtype == "f64" and n == 128 ** 3
-    traffic = traffic_if_current() if headline else None
-    moved = moved_bytes_a_step(p.A, n, sv)
-    if bs == 3:
+    traffic = traffic_if_current() if headline and fused else None
+    moved = moved_bytes_a_step(p.A, n, sv) if fused else None
+    if fused and bs == 1:
+        a_kernel = (f"sell_step<{'double' if sv == 8 else 'float'}, A step> (q = A p with "
+                    "p = z + beta p_old formed on the fly, x += alpha_prev p_old, p.q partials)")
+    elif fused:
         a_kernel = "bsell_step<A step> (BSR sliced ELL, p = z + beta p_old formed on the fly)"
-    elif moved is not None:
-        a_kernel = ("sell_step<double, A step> (q = A p with p = z + beta p_old formed on the "
-                    "fly, x += alpha_prev p_old, p.q partials)")
+    elif bs == 3:
+        a_kernel = ("bsell_step<A product> (BSR sliced ELL, q = A p and p.q; p, x and r "
+                    "updates in separate streaming passes)")
     else:
-        a_kernel = "csr_step<A product> (LDS tiles, separate p / r update passes)"
+        a_kernel = ("csr_step<A product> (LDS tiles, q = A p and p.q; p, x and r updates in "
+                    "separate streaming passes)")
     describe = {
         0: "2D Poisson 5-point, 32^2 interior, CSR, PCG + factorised SPAI eps=3e-3, rtol=1e-10, "
            "forward + adjoint of sum(x^2)",
@@ -563,7 +592,7 @@ def main():
                      "kernel": a_kernel,
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "algorithmic_bytes_per_launch": ab["a_step"],
+                     "algorithmic_bytes_per_launch": a_bytes,
                      "moved_bytes_per_launch": moved,
                      "moved_GBps": moved / a_avg_s / 1e9 if moved else None,
                      "avg_launch_us": a_avg_s * 1e6, "launches": a_launches} if has_a else

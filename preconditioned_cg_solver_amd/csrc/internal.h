@@ -31,21 +31,29 @@ constexpr int kSellMaxPadPct = 25;
 constexpr int kPad16 = -32768;
 // Padding slots allocated past the last slice (covers the widest batch).
 constexpr int kSellTail = 16 * kSlice;
-// Sliced ELLPACK for 3x3 BSR: kBSlice block rows per wavefront slice (lane l
-// owns scalar row 3 (kBSlice s + l / 3) + l % 3; lane 63 idles).
+// Sliced ELLPACK for 3x3 BSR: kBSlice block rows per wavefront slice (lane
+// l = 3 i + c takes block row 21 s + i and block component c; lane 63 idles).
+// A slot (one block of each of the slice's 21 block rows) keeps kBSlotVals
+// values, three block rows r of 64 entries (63 used, entry (r, c) of block i
+// at 64 r + 21 c + i), and kBSlotCols column entries (21 used), so every
+// load of a block row of a slot, and of a slot's columns, covers whole
+// 128-byte lines and shares none with the next load.
 constexpr int kBSlice = 21;
 constexpr int kBSellMaxWidth = 64;
-constexpr int kBSellTail = 16 * kBSlice;
+constexpr int kBSlotVals = 192;
+constexpr int kBSlotCols = 32;
+// Padding slots allocated past the last slice (covers the widest batch).
+constexpr int kBSellTail = 16;
 // BSR(3x3) engine: kBsrLanes lanes per block row, kWG / kBsrLanes block rows
 // per tile.
 constexpr int kBsrLanes = 32;
 constexpr int kBsrTileRows = kWG / kBsrLanes;
 // Ring sizes of the per-iteration scalars kept on the device.
 constexpr int kRing = 4;
-// Index of entry (r, c) of local block row li in the BSR sliced-ELL value
-// array, for the slot whose first block is slot_blk.
-__host__ __device__ inline size_t bsell_val(int slot_blk, int r, int c, int li) {
-  return (size_t)slot_blk * 9 + (size_t)(63 * c + 21 * r + li);
+// Index of entry (r, c) of local block row li of slot q in the BSR
+// sliced-ELL value array.
+__host__ __device__ inline size_t bsell_val(int q, int r, int c, int li) {
+  return (size_t)q * kBSlotVals + (size_t)(64 * r + 21 * c + li);
 }
 
 // Right-hand sides advanced together by one pass of the multi-RHS solver.
@@ -107,11 +115,10 @@ struct MatView {
   // rows [64 s, 64 s + 64); slot j of its row 64 s + l sits at
   // soff[s] + 64 j + l; padding slots have column -1 and value 0.
   // For 3x3 BSR the same fields hold the block form: slice s holds block
-  // rows [21 s, 21 s + 21); block slot j of local block row i sits at
-  // soff[s] + 21 j + i (its block column in sc).  The 21 blocks of a slot
-  // keep their 189 values component-major: entry (r, c) of local block i at
-  // 9 (soff[s] + 21 j) + 63 c + 21 r + i (bsell_val), so one load per
-  // component c reads 63 consecutive values for the slice's 63 scalar rows.
+  // rows [21 s, 21 s + 21) in slots soff[s] .. soff[s + 1] - 1 (soff counts
+  // slots); in slot q, local block row i has its block column at
+  // kBSlotCols q + i (sc absolute, -1 padding; or sd as block column minus
+  // block row, kPad16 padding) and its entry (r, c) at bsell_val(q, r, c, i).
   const void* sv = nullptr;
   const int32_t* sc = nullptr;   // absolute columns, or
   const int16_t* sd = nullptr;   // column - row offsets (preferred when they fit)

@@ -422,10 +422,11 @@ __global__ __launch_bounds__(kWG) void msell_step(MArgs<T> a) {
 // ---------------------------------------------------------------------------
 // Sliced-ELL engine for 3x3 BSR: one wavefront per slice of 21 block rows,
 // lane l owns scalar row 3 (21 s + l / 3) + l % 3 and reads its three values
-// of every block; each block gathers 3 K contiguous entries.
+// of every block (slot layout: bsell_val); each block gathers 3 K contiguous
+// entries.
 // ---------------------------------------------------------------------------
 
-template <typename T, int MODE, int K, int U>
+template <typename T, int MODE, int K, bool I16, int U>
 __global__ __launch_bounds__(kWG) void mbsell_step(MArgs<T> a) {
   __shared__ double s_red[kWaves * K];
   __shared__ int s_flag;
@@ -442,7 +443,7 @@ __global__ __launch_bounds__(kWG) void mbsell_step(MArgs<T> a) {
   for (int t = t0; t < t1; t += step) {
     const int sl = t * kWaves + wv;
     if (sl >= a.nslices) continue;
-    const int off = a.soff[sl], w = (a.soff[sl + 1] - off) / kBSlice;
+    const int off = a.soff[sl], w = a.soff[sl + 1] - off;
     const int brow = sl * kBSlice + li;
     const bool live = lane_live && brow < a.nbr;
     const int row = 3 * brow + r;
@@ -457,14 +458,16 @@ __global__ __launch_bounds__(kWG) void mbsell_step(MArgs<T> a) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         // loads past the slice end stay inside the arrays' padding tail
-        const int slot = off + (j + u) * kBSlice;
-        bc[u] = ld_stream<true>(a.sc + slot + li);
+        const int q = off + j + u;
+        const size_t ci = (size_t)q * kBSlotCols + li;
+        const int raw = I16 ? (int)ld_stream<true>(a.sd + ci) : ld_stream<true>(a.sc + ci);
+        bc[u] = j + u >= w ? -1 : I16 ? (raw == kPad16 ? -1 : brow + raw) : raw;
 #pragma unroll
-        for (int e = 0; e < 3; ++e) bv[u][e] = ld_stream<true>(a.sv + bsell_val(slot, r, e, li));
+        for (int e = 0; e < 3; ++e) bv[u][e] = ld_stream<true>(a.sv + bsell_val(q, r, e, li));
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const bool ok = j + u < w && bc[u] >= 0;
+        const bool ok = bc[u] >= 0;
 #pragma unroll
         for (int e = 0; e < 3; ++e) {
           const size_t base = (size_t)(ok ? 3 * bc[u] + e : 0) * a.ld;
@@ -744,7 +747,8 @@ hipError_t mlaunch(const sla_mat& m, const MatView& v, const MArgs<T>& a, int gr
     if (v.sd) hipLaunchKernelGGL((msell_step<T, MODE, K, true, U>), g, b, 0, s, a);
     else hipLaunchKernelGGL((msell_step<T, MODE, K, false, U>), g, b, 0, s, a);
   } else if (m.bs == 3 && v.sell) {
-    hipLaunchKernelGGL((mbsell_step<T, MODE, K, U>), g, b, 0, s, a);
+    if (v.sd) hipLaunchKernelGGL((mbsell_step<T, MODE, K, true, U>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((mbsell_step<T, MODE, K, false, U>), g, b, 0, s, a);
   } else if (m.bs == 1) {
     hipLaunchKernelGGL((mrow_step<T, MODE, K, 1>), g, b, 0, s, a);
   } else {

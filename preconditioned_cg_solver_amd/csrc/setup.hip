@@ -394,37 +394,48 @@ __global__ void sell_fill(const int* __restrict__ rp, const int* __restrict__ ci
 
 // ---- sliced ELLPACK for 3x3 BSR ----
 
-__global__ void bsell_widths(const int* __restrict__ rp, int nbr, int nslices,
-                             int* __restrict__ slots, int* __restrict__ maxw) {
+// Per slice: slots (widest block row); global: widest block row and largest
+// |block column - block row| (whether int16 offsets can hold the columns).
+__global__ void bsell_widths(const int* __restrict__ rp, const int* __restrict__ ci, int nbr,
+                             int nslices, int* __restrict__ slots, int* __restrict__ maxw,
+                             int* __restrict__ maxd) {
   const int sl = blockIdx.x * blockDim.x + threadIdx.x;
   if (sl >= nslices) return;
-  int w = 0;
+  int w = 0, dmax = 0;
   const int r1 = min(nbr, (sl + 1) * kBSlice);
-  for (int i = sl * kBSlice; i < r1; ++i) w = max(w, rp[i + 1] - rp[i]);
-  slots[sl] = w * kBSlice;
+  for (int i = sl * kBSlice; i < r1; ++i) {
+    const int kb = rp[i], ke = rp[i + 1];
+    w = max(w, ke - kb);
+    if (ke > kb) dmax = max(dmax, max(abs(ci[kb] - i), abs(ci[ke - 1] - i)));
+  }
+  slots[sl] = w;
   atomicMax(maxw, w);
+  atomicMax(maxd, dmax);
 }
 
-template <typename T>
+// Fill the slots of one block row (block rows past nbr only get padding).
+// C is the column type: int (absolute block column, -1 = padding) or short
+// (offset from the block row, kPad16 = padding).
+template <typename T, typename C>
 __global__ void bsell_fill(const int* __restrict__ rp, const int* __restrict__ ci,
                            const T* __restrict__ v, int nbr, int nslices,
                            const int* __restrict__ soff, T* __restrict__ sv,
-                           int* __restrict__ sc) {
+                           C* __restrict__ sc) {
   const int I = blockIdx.x * blockDim.x + threadIdx.x;  // block row (padded)
   if (I >= nslices * kBSlice) return;
   const int sl = I / kBSlice, li = I % kBSlice;
-  const int off = soff[sl], w = (soff[sl + 1] - off) / kBSlice;
+  const int off = soff[sl], w = soff[sl + 1] - off;
   const int kb = I < nbr ? rp[I] : 0, len = I < nbr ? rp[I + 1] - kb : 0;
+  constexpr bool rel = sizeof(C) == 2;
   for (int j = 0; j < w; ++j) {
-    const int slot = off + j * kBSlice;
-    const size_t dst = (size_t)slot + li;
+    const int q = off + j;
+    const size_t dst = (size_t)q * kBSlotCols + li;
     if (j < len) {
-      for (int e = 0; e < 9; ++e)
-        sv[bsell_val(slot, e / 3, e % 3, li)] = v[(size_t)(kb + j) * 9 + e];
-      sc[dst] = ci[kb + j];
+      for (int e = 0; e < 9; ++e) sv[bsell_val(q, e / 3, e % 3, li)] = v[(size_t)(kb + j) * 9 + e];
+      sc[dst] = (C)(rel ? ci[kb + j] - I : ci[kb + j]);
     } else {
-      for (int e = 0; e < 9; ++e) sv[bsell_val(slot, e / 3, e % 3, li)] = T(0);
-      sc[dst] = -1;
+      for (int e = 0; e < 9; ++e) sv[bsell_val(q, e / 3, e % 3, li)] = T(0);
+      sc[dst] = (C)(rel ? kPad16 : -1);
     }
   }
 }
@@ -652,49 +663,72 @@ sla_status build_bsell(MatView& view, int64_t nbr, int64_t nnzb, int32_t dtype, 
   if (nbr == 0 || nnzb == 0) return SLA_OK;
   const int nslices = (int)((nbr + kBSlice - 1) / kBSlice);
   int* buf = nullptr;
-  SLA_HIP(hipMallocAsync((void**)&buf, sizeof(int) * ((size_t)nslices + 2), s));
-  int* slots = buf;
+  SLA_HIP(hipMallocAsync((void**)&buf, sizeof(int) * ((size_t)nslices + 3), s));
+  int* slots = buf;            // nslices + 1 (last one zero)
   int* maxw = buf + nslices + 1;
-  SLA_HIP(hipMemsetAsync(buf, 0, sizeof(int) * ((size_t)nslices + 2), s));
+  int* maxd = buf + nslices + 2;
+  SLA_HIP(hipMemsetAsync(buf, 0, sizeof(int) * ((size_t)nslices + 3), s));
   hipLaunchKernelGGL(bsell_widths, dim3((nslices + 255) / 256), dim3(256), 0, s, view.rp,
-                     (int)nbr, nslices, slots, maxw);
+                     view.ci, (int)nbr, nslices, slots, maxw, maxd);
   SLA_HIP(hipGetLastError());
   int* soff = nullptr;
   SLA_HIP(hipMalloc((void**)&soff, sizeof(int) * ((size_t)nslices + 1)));
   owned3[2] = soff;
   sla_status st = exclusive_scan(slots, soff, nslices + 1, s);
   if (st != SLA_OK) return st;
-  int h[2] = {0, 0};
+  int h[3] = {0, 0, 0};
   SLA_HIP(hipMemcpyAsync(&h[0], maxw, sizeof(int), hipMemcpyDeviceToHost, s));
   SLA_HIP(hipMemcpyAsync(&h[1], soff + nslices, sizeof(int), hipMemcpyDeviceToHost, s));
+  SLA_HIP(hipMemcpyAsync(&h[2], maxd, sizeof(int), hipMemcpyDeviceToHost, s));
   SLA_HIP(hipFreeAsync(buf, s));
   SLA_HIP(hipStreamSynchronize(s));
-  const int64_t total = h[1];
-  if (h[0] > kBSellMaxWidth || total * 100 > nnzb * (100 + kSellMaxPadPct)) return SLA_OK;
-  if ((total + kBSellTail) * 9 >= (int64_t)INT32_MAX) return SLA_OK;
+  const int64_t total = h[1];  // slots
+  if (h[0] > kBSellMaxWidth || total * kBSlice * 100 > nnzb * (100 + kSellMaxPadPct))
+    return SLA_OK;
+  if ((total + kBSellTail) * kBSlotVals >= (int64_t)INT32_MAX) return SLA_OK;
   const size_t es = dtype == SLA_F64 ? 8 : 4;
+  const char* e16 = getenv("SLA_SELL16");
+  const bool rel16 = h[2] <= 32767 && !(e16 && e16[0] == '0');
+  const size_t cs = rel16 ? 2 : 4;
+  // kBSellTail padding slots past the last slice let the products load whole
+  // batches without bounds checks.
   const size_t alloc = (size_t)total + kBSellTail;
   void* sv = nullptr;
-  int* sc = nullptr;
-  SLA_HIP(hipMalloc(&sv, es * 9 * alloc));
+  void* sc = nullptr;
+  SLA_HIP(hipMalloc(&sv, es * kBSlotVals * alloc));
   owned3[0] = sv;
-  SLA_HIP(hipMalloc((void**)&sc, sizeof(int) * alloc));
+  SLA_HIP(hipMalloc(&sc, cs * kBSlotCols * alloc));
   owned3[1] = sc;
-  SLA_HIP(hipMemsetAsync((char*)sv + es * 9 * (size_t)total, 0, es * 9 * kBSellTail, s));
-  SLA_HIP(hipMemsetAsync(sc + total, 0xff, sizeof(int) * kBSellTail, s));
-  const int rows = nslices * kBSlice;
-  if (dtype == SLA_F64)
-    hipLaunchKernelGGL(bsell_fill<double>, dim3((rows + 255) / 256), dim3(256), 0, s, view.rp,
-                       view.ci, (const double*)view.v, (int)nbr, nslices, (const int*)soff,
-                       (double*)sv, sc);
+  // every entry is defined: the fill writes the 189 used values and 21 used
+  // columns of each slot, this clears the per-row and per-slot pads and the
+  // tail slots (value 0, column padding)
+  SLA_HIP(hipMemsetAsync(sv, 0, es * kBSlotVals * alloc, s));
+  if (rel16)
+    SLA_HIP(hipMemsetD16Async((hipDeviceptr_t)sc, (unsigned short)kPad16, kBSlotCols * alloc, s));
   else
-    hipLaunchKernelGGL(bsell_fill<float>, dim3((rows + 255) / 256), dim3(256), 0, s, view.rp,
-                       view.ci, (const float*)view.v, (int)nbr, nslices, (const int*)soff,
-                       (float*)sv, sc);
+    SLA_HIP(hipMemsetAsync(sc, 0xff, 4 * kBSlotCols * alloc, s));
+  const int rows = nslices * kBSlice;
+  const dim3 g((rows + 255) / 256), b(256);
+  if (dtype == SLA_F64 && rel16)
+    hipLaunchKernelGGL((bsell_fill<double, short>), g, b, 0, s, view.rp, view.ci,
+                       (const double*)view.v, (int)nbr, nslices, (const int*)soff, (double*)sv,
+                       (short*)sc);
+  else if (dtype == SLA_F64)
+    hipLaunchKernelGGL((bsell_fill<double, int>), g, b, 0, s, view.rp, view.ci,
+                       (const double*)view.v, (int)nbr, nslices, (const int*)soff, (double*)sv,
+                       (int*)sc);
+  else if (rel16)
+    hipLaunchKernelGGL((bsell_fill<float, short>), g, b, 0, s, view.rp, view.ci,
+                       (const float*)view.v, (int)nbr, nslices, (const int*)soff, (float*)sv,
+                       (short*)sc);
+  else
+    hipLaunchKernelGGL((bsell_fill<float, int>), g, b, 0, s, view.rp, view.ci,
+                       (const float*)view.v, (int)nbr, nslices, (const int*)soff, (float*)sv,
+                       (int*)sc);
   SLA_HIP(hipGetLastError());
   view.sv = sv;
-  view.sc = sc;
-  view.sd = nullptr;
+  view.sc = rel16 ? nullptr : (const int32_t*)sc;
+  view.sd = rel16 ? (const int16_t*)sc : nullptr;
   view.soff = soff;
   view.nslices = nslices;
   view.sell_w = h[0];

@@ -614,95 +614,113 @@ __global__ __launch_bounds__(kWG) void sell_step(StepArgs<T> a) {
 
 // ---------------------------------------------------------------------------
 // Sliced-ELL engine for 3x3 BSR: one wavefront per slice of 21 block rows.
-// Lane l owns scalar row 3 (21 s + l / 3) + l % 3 and, for every block slot,
-// reads that row's three values of the block (the 63 live lanes read 63
-// consecutive 24-byte row thirds) and the three gathered entries of the
-// block column; no cross-lane reduction, accumulation in (block, column)
-// order.  The next slice's first batch is prefetched across slices.
+// Lane l = 3 i + c takes local block row i and block component c: for every
+// block slot it gathers only entry c of the block column (two gathers for
+// the A and G^T steps, one otherwise, instead of six or three per lane) and
+// reads column c of the block (per block row r one load of 63 values inside
+// four aligned 128-byte lines, bsell_val), accumulating the three row
+// partials sum_slots v[r][c] x_c.
+// After the last slot the three lanes of a block row add their partials for
+// row r in component order 0, 1, 2 (two cross-lane reads per slice), and
+// lane 3 i + r runs the epilogue of scalar row 3 (21 s + i) + r.  Loads run
+// one batch of U slots ahead of the gathers, across slice boundaries.
 // ---------------------------------------------------------------------------
 
-template <typename T, int MODE, bool NT, int U>
+template <typename T, int MODE, bool NT, bool I16, int U>
 __global__ __launch_bounds__(kWG) void bsell_step(StepArgs<T> a) {
   __shared__ double s_red[kWaves];
   __shared__ int s_flag;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int li = min(lane / 3, kBSlice - 1), r = lane - 3 * (lane / 3);
+  // lane 63 mirrors lane 60 (block row 20, component 0) and stores nothing
+  const int li = min(lane / 3, kBSlice - 1), c = lane - 3 * (lane / 3);
   const bool lane_live = lane < 3 * kBSlice;
+  // lanes holding the same block row's partials, by component distance
+  const int src_prev = 3 * li + (c + 2) % 3, src_next = 3 * li + (c + 1) % 3;
   int t0, t1, step;
   tile_range(a.ntiles, t0, t1, step);
-  T hv[U][3];
-  int hc[U];
-  int hoff = 0, hw = 0;
-  auto load_head = [&](int sl) {
-    hoff = 0;
-    hw = 0;
-    if (sl < a.nslices) {
-      hoff = a.soff[sl];
-      hw = (a.soff[sl + 1] - hoff) / kBSlice;
-    }
+  // The wave's batches of U slots form one stream over its slices: the
+  // loads of the next batch (possibly the next slice's first) are issued
+  // before the current batch gathers, so one batch is always in flight.
+  T nv[U][3];
+  int nc[U];
+  int pre_sl = -1;  // slice whose first batch sits in nv, if any
+  auto load_batch = [&](int q0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int slot = hoff + u * kBSlice;
-      hc[u] = ld_stream<NT>(a.sc + slot + li);
+      // loads past the slice end stay inside the arrays' padding tail
+      const int q = q0 + u;
+      nc[u] = sell_raw<NT, I16>(a, q * kBSlotCols + li);
 #pragma unroll
-      for (int c = 0; c < 3; ++c) hv[u][c] = ld_stream<NT>(a.sv + bsell_val(slot, r, c, li));
+      for (int r = 0; r < 3; ++r) nv[u][r] = ld_stream<NT>(a.sv + bsell_val(q, r, c, li));
     }
   };
-  if (t0 < t1) load_head(t0 * kWaves + wv);
+  auto slice_of = [&](int t) { return t * kWaves + wv; };
+  if (t0 < t1 && slice_of(t0) < a.nslices) {
+    const int sl = slice_of(t0), off = a.soff[sl];
+    if (a.soff[sl + 1] > off) {
+      load_batch(off);
+      pre_sl = sl;
+    }
+  }
   Coef<T> cf;
   if (!prologue<T, MODE>(a, cf, s_red, &s_flag)) return;
   double dot = 0.0;
   for (int t = t0; t < t1; t += step) {
-    const int sl = t * kWaves + wv;
-    const int off = hoff, w = hw;
-    T cv[U][3];
-    int cc[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      cc[u] = hc[u];
-#pragma unroll
-      for (int c = 0; c < 3; ++c) cv[u][c] = hv[u][c];
-    }
-    if (t + step < t1) load_head((t + step) * kWaves + wv);
-    if (sl >= a.nslices) continue;
+    const int sl = slice_of(t);
+    if (sl >= a.nslices) break;
+    const int off = a.soff[sl], w = a.soff[sl + 1] - off;
     const int brow = sl * kBSlice + li;
     const bool live = lane_live && brow < a.nbr;
-    const int row = 3 * brow + r;
-    T acc = T(0);
-    auto consume = [&](T (&v)[U][3], int (&col)[U], int j0) {
-      T g[U][3];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const bool ok = j0 + u < w && col[u] >= 0;
-        const int base = ok ? 3 * col[u] : 0;
-#pragma unroll
-        for (int c = 0; c < 3; ++c) {
-          const T x = gat<T, MODE>(a, base + c, cf);
-          g[u][c] = ok ? x : T(0);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const bool ok = j0 + u < w && col[u] >= 0;
-#pragma unroll
-        for (int c = 0; c < 3; ++c) acc = fma(ok ? v[u][c] : T(0), g[u][c], acc);
-      }
-    };
+    const int row = 3 * brow + c;
     const Own<T> o = own_load<T, MODE>(a, live ? row : 0);
-    consume(cv, cc, 0);
-    for (int j = U; j < w; j += U) {
-      T bv[U][3];
-      int bc[U];
+    if (w > 0 && pre_sl != sl) load_batch(off);
+    // next slice with slots, for the prefetch that crosses the boundary
+    const int sl_n = t + step < t1 ? slice_of(t + step) : a.nslices;
+    const int off_n = sl_n < a.nslices ? a.soff[sl_n] : 0;
+    const bool has_n = sl_n < a.nslices && a.soff[sl_n + 1] > off_n;
+    T acc[3] = {T(0), T(0), T(0)};
+    for (int j = 0; j < w; j += U) {
+      T cv[U][3];
+      int cc[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int slot = off + (j + u) * kBSlice;
-        bc[u] = ld_stream<NT>(a.sc + slot + li);
+        cc[u] = nc[u];
 #pragma unroll
-        for (int c = 0; c < 3; ++c) bv[u][c] = ld_stream<NT>(a.sv + bsell_val(slot, r, c, li));
+        for (int r = 0; r < 3; ++r) cv[u][r] = nv[u][r];
       }
-      consume(bv, bc, j);
+      if (j + U < w) {
+        load_batch(off + j + U);
+      } else if (has_n) {
+        load_batch(off_n);
+        pre_sl = sl_n;
+      }
+      T g[U];
+      bool ok[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int bc = sell_decode<I16>(cc[u], brow, j + u < w);
+        ok[u] = bc >= 0;
+        const T x = gat<T, MODE>(a, ok[u] ? 3 * bc + c : 0, cf);
+        g[u] = ok[u] ? x : T(0);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int r = 0; r < 3; ++r) acc[r] = fma(ok[u] ? cv[u][r] : T(0), g[u], acc[r]);
+      }
     }
-    if (live) dot += epi_own<T, MODE>(a, row, acc, cf, o);
+    // row c of this block row: own partial (component c) plus those of
+    // components c - 1 and c + 1 (mod 3), read from the neighbouring lanes,
+    // added in component order
+    const T own = c == 0 ? acc[0] : (c == 1 ? acc[1] : acc[2]);
+    const T for_next = c == 0 ? acc[1] : (c == 1 ? acc[2] : acc[0]);  // row c + 1
+    const T for_prev = c == 0 ? acc[2] : (c == 1 ? acc[0] : acc[1]);  // row c - 1
+    const T from_prev = __shfl(for_next, src_prev, 64);   // component c - 1
+    const T from_next = __shfl(for_prev, src_next, 64);   // component c + 1
+    const T y = c == 0 ? (own + from_next) + from_prev
+              : c == 1 ? (from_prev + own) + from_next
+                       : (from_next + from_prev) + own;
+    if (live) dot += epi_own<T, MODE>(a, row, y, cf, o);
   }
   if constexpr (MODE != M_PLAIN && MODE != M_GZ && MODE != M_GTU) {
     const double s = block_sum(dot, s_red);
@@ -1152,17 +1170,22 @@ hipError_t launch_step(const sla_mat& m, const StepArgs<T>& a, int grid, hipStre
   } else if (m.bs == 1) {
     if (nt) hipLaunchKernelGGL((csr_step<T, MODE, true>), dim3(grid), dim3(kWG), 0, s, a);
     else hipLaunchKernelGGL((csr_step<T, MODE, false>), dim3(grid), dim3(kWG), 0, s, a);
-  } else if (a.sc) {
+  } else if (a.sc || a.sd) {
     // block slots per load round: 4 for wide block rows, else 2 (fewer
     // registers, more waves in flight; measured on the 27-point block stencil
     // and its block triangles)
     const dim3 g(grid), b(kWG);
-    if (a.sell_w > 16) {
-      if (nt) hipLaunchKernelGGL((bsell_step<T, MODE, true, 4>), g, b, 0, s, a);
-      else hipLaunchKernelGGL((bsell_step<T, MODE, false, 4>), g, b, 0, s, a);
+    const bool wide = a.sell_w > 16;
+    if (a.sd) {
+      if (nt && wide) hipLaunchKernelGGL((bsell_step<T, MODE, true, true, 4>), g, b, 0, s, a);
+      else if (nt) hipLaunchKernelGGL((bsell_step<T, MODE, true, true, 2>), g, b, 0, s, a);
+      else if (wide) hipLaunchKernelGGL((bsell_step<T, MODE, false, true, 4>), g, b, 0, s, a);
+      else hipLaunchKernelGGL((bsell_step<T, MODE, false, true, 2>), g, b, 0, s, a);
     } else {
-      if (nt) hipLaunchKernelGGL((bsell_step<T, MODE, true, 2>), g, b, 0, s, a);
-      else hipLaunchKernelGGL((bsell_step<T, MODE, false, 2>), g, b, 0, s, a);
+      if (nt && wide) hipLaunchKernelGGL((bsell_step<T, MODE, true, false, 4>), g, b, 0, s, a);
+      else if (nt) hipLaunchKernelGGL((bsell_step<T, MODE, true, false, 2>), g, b, 0, s, a);
+      else if (wide) hipLaunchKernelGGL((bsell_step<T, MODE, false, false, 4>), g, b, 0, s, a);
+      else hipLaunchKernelGGL((bsell_step<T, MODE, false, false, 2>), g, b, 0, s, a);
     }
   } else {
     if (nt) hipLaunchKernelGGL((bsr3_step<T, MODE, true>), dim3(grid), dim3(kWG), 0, s, a);
@@ -1360,17 +1383,22 @@ sla_status exit_status(const SolverState& fin, sla_solve_info* info, int* iters_
   return st;
 }
 
-// Fused iteration (p and r formed inside the products' gathers) when A's
-// gathers have locality -- A qualified for the SELL-64 layout (short, even,
-// banded rows) or is block sparse; otherwise separate streaming passes keep
-// every product at one random gather per nonzero.  SLA_FUSION=fused|unfused
-// overrides the choice.
+// Fused iteration (p and r formed inside the products' gathers) when A is a
+// CSR matrix in the SELL-64 layout (short, even, banded rows: its gathers
+// have locality and its one gather per slot costs little next to the value
+// stream).  Otherwise separate streaming passes keep every product at one
+// gather per nonzero: random gathers (irregular CSR) cost the same whether
+// or not p and r are formed in them, and a 3x3 block slot streams 9 values
+// per gathered entry, so the fused form's second gather and its three extra
+// stores cost the BSR products more than the two vector passes
+// (elasticity 64^3 x 3: 296 against 270 us per iteration).
+// SLA_FUSION=fused|unfused overrides the choice.
 bool use_fused(const sla_mat& A) {
   if (const char* e = getenv("SLA_FUSION")) {
     if (!strcmp(e, "fused")) return true;
     if (!strcmp(e, "unfused")) return false;
   }
-  return A.bs != 1 || A.fwd.sell;
+  return A.bs == 1 && A.fwd.sell;
 }
 
 template <typename T>

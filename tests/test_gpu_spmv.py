@@ -95,6 +95,49 @@ def test_spmv_fp32(name):
     assert rel(host(y), ref) <= 1e-5
 
 
+def far_bsr(m=33):
+    """Block 27-point stencil on m^3 nodes plus a coupling block between the
+    first and the last block row: block-column offsets beyond 16 bits, so the
+    sliced layout keeps absolute int32 block columns."""
+    A = I.elastic_bsr(m, I.rng_for(3, 0))
+    nbr = A.n_block_rows
+    rows = np.repeat(np.arange(nbr), np.diff(A.row_ptr))
+    blk = -0.01 * np.eye(3).reshape(9)
+    rows = np.concatenate([rows, [0, nbr - 1]])
+    cols = np.concatenate([A.col_idx, [nbr - 1, 0]])
+    vals = np.concatenate([A.vals.reshape(-1, 9), [blk, blk]])
+    order = np.lexsort((cols, rows))
+    rp = np.zeros(nbr + 1, np.int32)
+    np.cumsum(np.bincount(rows, minlength=nbr), out=rp[1:])
+    return I.SparseMatrix(nbr, 3, rp, cols[order].astype(np.int32), vals[order].reshape(-1))
+
+
+@pytest.mark.parametrize("name,force32", [("bsr_elastic_5", True), ("far_bsr_33", False),
+                                          ("bsr_G_5", True)])
+def test_bsr_int32_columns(name, force32, monkeypatch):
+    """The BSR sliced layout with absolute int32 block columns (forced, or
+    because an offset does not fit 16 bits): products both ways and, for a
+    factor, the preconditioner apply."""
+    if force32:
+        monkeypatch.setenv("SLA_SELL16", "0")
+    M = far_bsr() if name == "far_bsr_33" else (FACTORS[name]() if name in FACTORS
+                                                  else MATRICES[name]())
+    say("bsr int32 columns", name, M.n)
+    h = create(M, transpose=True)
+    x = I.spmv_test_vector(9, M.n)
+    y = B.sla_spmv(h, tdev(x))
+    yt = B.sla_spmv(h, tdev(x), transpose=True)
+    torch.cuda.synchronize()
+    assert rel(host(y), oracle.spmv(M, x)) <= 1e-13
+    trp, tci, tv = oracle.transpose(M)
+    Mt = I.SparseMatrix(M.n_block_rows, 3, trp, tci, tv)
+    assert rel(host(yt), oracle.spmv(Mt, x)) <= 1e-13
+    if name.startswith("bsr_G"):
+        z = B.sla_precond_apply(h, 3e-3, tdev(x))
+        torch.cuda.synchronize()
+        assert rel(host(z), oracle.precond_apply(M, 3e-3, x)) <= 1e-13
+
+
 def test_empty_matrix():
     say("n = 0")
     rp = torch.zeros(1, dtype=torch.int32, device=DEV)
