@@ -420,10 +420,13 @@ __global__ __launch_bounds__(kWG) void msell_step(MArgs<T> a) {
 }
 
 // ---------------------------------------------------------------------------
-// Sliced-ELL engine for 3x3 BSR: one wavefront per slice of 21 block rows,
-// lane l owns scalar row 3 (21 s + l / 3) + l % 3 and reads its three values
-// of every block (slot layout: bsell_val); each block gathers 3 K contiguous
-// entries.
+// Sliced-ELL engine for 3x3 BSR: one wavefront per slice of 21 block rows;
+// lane l = 3 i + c takes block row i and block component c.  Per slot it
+// reads column c of each block (slot layout: bsell_val) and gathers the K
+// contiguous entries of row c of the block column only, keeping the three
+// row partials of every right-hand side; after the slice the three lanes of
+// a block row add their partials in component order and lane 3 i + r runs
+// the epilogue of scalar row 3 (21 s + i) + r.
 // ---------------------------------------------------------------------------
 
 template <typename T, int MODE, int K, bool I16, int U>
@@ -431,27 +434,31 @@ __global__ __launch_bounds__(kWG) void mbsell_step(MArgs<T> a) {
   __shared__ double s_red[kWaves * K];
   __shared__ int s_flag;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int li = min(lane / 3, kBSlice - 1), r = lane - 3 * (lane / 3);
+  // lane 63 mirrors lane 60 (block row 20, component 0) and stores nothing
+  const int li = min(lane / 3, kBSlice - 1), c = lane - 3 * (lane / 3);
   const bool lane_live = lane < 3 * kBSlice;
+  const int src_prev = 3 * li + (c + 2) % 3, src_next = 3 * li + (c + 1) % 3;
   int t0, t1, step;
   tile_range(a.ntiles, t0, t1, step);
   MCoef<T, K> cf;
   if (!mprologue<T, MODE, K>(a, cf, s_red, &s_flag)) return;
   double dot[K];
 #pragma unroll
-  for (int c = 0; c < K; ++c) dot[c] = 0.0;
+  for (int k = 0; k < K; ++k) dot[k] = 0.0;
   for (int t = t0; t < t1; t += step) {
     const int sl = t * kWaves + wv;
     if (sl >= a.nslices) continue;
     const int off = a.soff[sl], w = a.soff[sl + 1] - off;
     const int brow = sl * kBSlice + li;
     const bool live = lane_live && brow < a.nbr;
-    const int row = 3 * brow + r;
+    const int row = 3 * brow + c;
     MOwn<T, K> o;
     mown_load<T, MODE, K>(a, live ? row : 0, o);
-    T acc[K];
+    T acc[3][K];
 #pragma unroll
-    for (int c = 0; c < K; ++c) acc[c] = T(0);
+    for (int r = 0; r < 3; ++r)
+#pragma unroll
+      for (int k = 0; k < K; ++k) acc[r][k] = T(0);
     for (int j = 0; j < w; j += U) {
       T bv[U][3];
       int bc[U];
@@ -463,24 +470,35 @@ __global__ __launch_bounds__(kWG) void mbsell_step(MArgs<T> a) {
         const int raw = I16 ? (int)ld_stream<true>(a.sd + ci) : ld_stream<true>(a.sc + ci);
         bc[u] = j + u >= w ? -1 : I16 ? (raw == kPad16 ? -1 : brow + raw) : raw;
 #pragma unroll
-        for (int e = 0; e < 3; ++e) bv[u][e] = ld_stream<true>(a.sv + bsell_val(q, r, e, li));
+        for (int r = 0; r < 3; ++r) bv[u][r] = ld_stream<true>(a.sv + bsell_val(q, r, c, li));
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const bool ok = bc[u] >= 0;
+        const size_t base = (size_t)(ok ? 3 * bc[u] + c : 0) * a.ld;
 #pragma unroll
-        for (int e = 0; e < 3; ++e) {
-          const size_t base = (size_t)(ok ? 3 * bc[u] + e : 0) * a.ld;
-          const T vu = ok ? bv[u][e] : T(0);
+        for (int k = 0; k < K; ++k) {
+          const T g = ok ? mgat<T, MODE, K>(a, base, k, cf) : T(0);
 #pragma unroll
-          for (int c = 0; c < K; ++c) {
-            const T g = mgat<T, MODE, K>(a, base, c, cf);
-            acc[c] = fma(vu, ok ? g : T(0), acc[c]);
-          }
+          for (int r = 0; r < 3; ++r) acc[r][k] = fma(ok ? bv[u][r] : T(0), g, acc[r][k]);
         }
       }
     }
-    if (live) mepi<T, MODE, K>(a, row, acc, cf, o, dot);
+    // row c of this block row, per right-hand side: own partial plus those of
+    // components c - 1 and c + 1 (mod 3), added in component order
+    T y[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const T own = c == 0 ? acc[0][k] : (c == 1 ? acc[1][k] : acc[2][k]);
+      const T for_next = c == 0 ? acc[1][k] : (c == 1 ? acc[2][k] : acc[0][k]);
+      const T for_prev = c == 0 ? acc[2][k] : (c == 1 ? acc[0][k] : acc[1][k]);
+      const T from_prev = __shfl(for_next, src_prev, 64);
+      const T from_next = __shfl(for_prev, src_next, 64);
+      y[k] = c == 0 ? (own + from_next) + from_prev
+           : c == 1 ? (from_prev + own) + from_next
+                    : (from_next + from_prev) + own;
+    }
+    if (live) mepi<T, MODE, K>(a, row, y, cf, o, dot);
   }
   mfinish<T, MODE, K>(a, dot, s_red);
 }
@@ -747,8 +765,11 @@ hipError_t mlaunch(const sla_mat& m, const MatView& v, const MArgs<T>& a, int gr
     if (v.sd) hipLaunchKernelGGL((msell_step<T, MODE, K, true, U>), g, b, 0, s, a);
     else hipLaunchKernelGGL((msell_step<T, MODE, K, false, U>), g, b, 0, s, a);
   } else if (m.bs == 3 && v.sell) {
-    if (v.sd) hipLaunchKernelGGL((mbsell_step<T, MODE, K, true, U>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((mbsell_step<T, MODE, K, false, U>), g, b, 0, s, a);
+    // one gathered block row per lane and slot: K entries per slot, batches
+    // of UB slots keep the three row partials per column within registers
+    constexpr int UB = K >= 4 ? 1 : 2;
+    if (v.sd) hipLaunchKernelGGL((mbsell_step<T, MODE, K, true, UB>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((mbsell_step<T, MODE, K, false, UB>), g, b, 0, s, a);
   } else if (m.bs == 1) {
     hipLaunchKernelGGL((mrow_step<T, MODE, K, 1>), g, b, 0, s, a);
   } else {
