@@ -112,6 +112,40 @@ def far_bsr(m=33):
     return I.SparseMatrix(nbr, 3, rp, cols[order].astype(np.int32), vals[order].reshape(-1))
 
 
+def bsr_empty_slices():
+    """Block stencil on 10^3 nodes with block rows 105..167 emptied: three
+    whole 21-block-row slices without a slot, between slices that have them
+    (15% slot padding, inside the sliced layout's limit)."""
+    A = I.elastic_bsr(10, I.rng_for(3, 0))
+    rows = np.repeat(np.arange(A.n_block_rows), np.diff(A.row_ptr))
+    keep = (rows < 105) | (rows > 167)
+    rp = np.zeros(A.n_block_rows + 1, np.int32)
+    np.cumsum(np.bincount(rows[keep], minlength=A.n_block_rows), out=rp[1:])
+    return I.SparseMatrix(A.n_block_rows, 3, rp, A.col_idx[keep],
+                          A.vals.reshape(-1, 9)[keep].reshape(-1))
+
+
+@pytest.mark.parametrize("force32", [False, True])
+def test_bsr_empty_slices(force32, monkeypatch):
+    """Slices with no slot among slices with slots: the products' batch
+    stream skips them and their rows still get y = 0 (both column forms)."""
+    if force32:
+        monkeypatch.setenv("SLA_SELL16", "0")
+    M = bsr_empty_slices()
+    say("bsr empty slices", "int32" if force32 else "int16")
+    h = create(M, transpose=True)
+    x = I.spmv_test_vector(9, M.n)
+    y = B.sla_spmv(h, tdev(x))
+    yt = B.sla_spmv(h, tdev(x), transpose=True)
+    torch.cuda.synchronize()
+    ref = oracle.spmv(M, x)
+    assert np.all(ref[3 * 105:3 * 168] == 0)
+    assert rel(host(y), ref) <= 1e-13
+    assert np.all(host(y)[3 * 105:3 * 168] == 0)
+    trp, tci, tv = oracle.transpose(M)
+    assert rel(host(yt), oracle.spmv(I.SparseMatrix(M.n_block_rows, 3, trp, tci, tv), x)) <= 1e-13
+
+
 @pytest.mark.parametrize("name,force32", [("bsr_elastic_5", True), ("far_bsr_33", False),
                                           ("bsr_G_5", True)])
 def test_bsr_int32_columns(name, force32, monkeypatch):
