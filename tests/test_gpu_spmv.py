@@ -224,9 +224,10 @@ def test_precond_apply(name):
 
 
 @pytest.mark.parametrize("name", ["c0_poisson2d_32", "c2_poisson3d_128", "irregular_long_rows",
-                                  "bsr_elastic_5", "empty_rows"])
+                                  "bsr_elastic_5", "empty_rows", "bsr_empty_slices",
+                                  "c3_bsr_elastic_64"])
 def test_pattern_grad_bit_exact(name):
-    M = MATRICES[name]()
+    M = bsr_empty_slices() if name == "bsr_empty_slices" else MATRICES[name]()
     lam = I.spmv_test_vector(5, M.n)
     x = I.spmv_test_vector(6, M.n)
     say("pattern grad", name)
