@@ -508,6 +508,22 @@ def main():
     B.sla_set_profiling(False)
     A2.destroy()
 
+    # dL/dA alone (launched on torch's current stream, so torch events bracket
+    # it): 10 back-to-back calls on the last adjoint's lambda and x
+    B.sla_pattern_grad(A, grad_b, x, out=grad_vals)
+    torch.cuda.synchronize()
+    ge0, ge1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ge0.record()
+    for _ in range(10):
+        B.sla_pattern_grad(A, grad_b, x, out=grad_vals)
+    ge1.record()
+    torch.cuda.synchronize()
+    grad_s = ge0.elapsed_time(ge1) / 10 / 1e3
+    if bs == 1:
+        grad_bytes = (sv + 4) * nnz_a + 4 * (n + 1) + 2 * sv * n
+    else:
+        grad_bytes = (9 * sv + 4) * p.A.nnzb + 4 * (p.A.n_block_rows + 1) + 2 * sv * n
+
     # several right-hand sides on the same operators (the single solve's b as
     # column 0, seeded N(0,1) columns after it): forward solves only
     multi = {}
@@ -614,6 +630,12 @@ def main():
                          "y warm; cold = median of 10 calls, each after a 1 GiB read-only "
                          "flush of every cache (x included); warm = back-to-back calls "
                          "(A held in the Infinity Cache when it fits)"},
+        "gradient": {"bytes": grad_bytes, "us": grad_s * 1e6,
+                     "GBps": grad_bytes / grad_s / 1e9,
+                     "frac": grad_bytes / grad_s / 1e9 / HBM_PEAK_GBS,
+                     "note": "dL/dA = -lambda_i x_j on A's pattern (sla_pattern_grad), mean "
+                             "of 10 back-to-back calls; bytes: column indices and row "
+                             "pointers read, the gradient written, lambda and x read once"},
         "setup_ms": statistics.median(setup) * 1e3,
         "multi_rhs": {"note": "k right-hand sides solved together on the same A and G "
                               f"(forward solves, {args.dtype}); column-iterations per second and the "
