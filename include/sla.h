@@ -29,6 +29,25 @@
  *    a thread-local message for the last failing call on that thread.
  *  - Nothing here falls back to the CPU: every numerical step runs in the
  *    library's HIP kernels.
+ *
+ * Environment variables (all optional; the defaults are the measured best
+ * choices and no result depends on them beyond rounding order):
+ *  - SLA_FUSION=fused|unfused: iteration form of the one-right-hand-side
+ *    solves (default: fused for CSR matrices in the sliced layout, separate
+ *    streaming passes otherwise).  SLA_MFUSION=fused: the same for the
+ *    multi-right-hand-side solves (default: separate).
+ *  - SLA_SMALL=0: no one-workgroup solve for systems of at most 1024 rows.
+ *  - SLA_SELL=0: no sliced (SELL-64 / BSR sliced-ELL) copies at create time;
+ *    SLA_SELL16=0: absolute int32 columns in them instead of 16-bit offsets.
+ *  - SLA_GRID=G (G >= 8, rounded down to a multiple of 8): workgroups of the
+ *    row-parallel kernels instead of the resident capacity.
+ *  - SLA_MALL_BUDGET_MB (default 208) and SLA_MALL_POLICY=A|G|all|none: which
+ *    operator a solve keeps resident in the 256 MB Infinity Cache (default: A
+ *    when it fits the budget, otherwise none; the rest stream non-temporally).
+ *  - SLA_BATCH_ITERS (default 16, 1..4096): iterations enqueued between two
+ *    host polls of the device exit flag.
+ * SLA_GRID is read once per device, SLA_MALL_BUDGET_MB and SLA_BATCH_ITERS
+ * once per process; the others at every handle creation or solve.
  */
 #ifndef SLA_H
 #define SLA_H
