@@ -401,8 +401,13 @@ __device__ __forceinline__ T row_sum_lds(const StepArgs<T>& a, const T* s_val, c
 
 static_assert(kTileRows == kWG, "one row pointer per thread when staging a tile");
 
+// Every step kernel must keep kWaves-wide workgroups resident four per CU
+// (the grid is sized for that, see occupancy_grid): the plain, preconditioner
+// tail and separate G^T forms would otherwise take 130+ VGPRs, fall to three
+// waves per SIMD and run a quarter of their workgroups as a second round.
 template <typename T, int MODE, bool NT>
-__global__ __launch_bounds__(kWG) void csr_step(StepArgs<T> a) {
+__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4)))
+void csr_step(StepArgs<T> a) {
   __shared__ T s_val[kLdsCap];
   __shared__ int s_col[kLdsCap];
   __shared__ int s_rp[kTileRows + 1];
