@@ -19,6 +19,12 @@
 //            (double-buffered r) and stored, and partials of ||r_k||^2;
 //   G step   z_k = G t + eps r_k, partials of rho_k = r_k . z_k.
 //
+// That fused form runs for CSR matrices in the SELL-64 layout.  BSR matrices
+// and irregular CSR take the separate form (use_fused): bare products
+// q = A p_{k-1} (with p.q) and t = G^T r_k around two streaming passes,
+// vec_p_update (p and the deferred x) and vec_r_update (r and ||r||^2),
+// so each product gathers one vector.
+//
 // Each kernel begins by summing the previous kernel's per-workgroup partials
 // in a fixed order (so every workgroup derives the same scalar) and the
 // convergence / breakdown decisions are taken on the device; the host polls
