@@ -306,6 +306,15 @@ const char *sla_last_error(void);
  * summed event time (ms) of a class since the last sla_reset_profile.
  */
 sla_status sla_set_profiling(int32_t enable);
+/*
+ * Sampling of the solver's kernel timing: events bracket only the launches of
+ * iterations k with k % every == 0 (the start-up launches, k = 0, always).
+ * every = 1 (the default) times every launch; a larger stride keeps the
+ * event packets from slowing the solve they measure.  Applies to classes
+ * 0-2; plain sla_spmv calls are always timed when class 3 is enabled.
+ * Error: SLA_ERR_INVALID_ARG if every < 1.
+ */
+sla_status sla_set_profiling_stride(int32_t every);
 sla_status sla_get_profile(int32_t kernel_class, int64_t *launches, double *total_ms);
 sla_status sla_reset_profile(void);
 

@@ -92,6 +92,7 @@ def _declare(L):
         "sla_status_string": ([st], ctypes.c_char_p),
         "sla_last_error": ([], ctypes.c_char_p),
         "sla_set_profiling": ([i32], st),
+        "sla_set_profiling_stride": ([i32], st),
         "sla_get_profile": ([i32, ctypes.POINTER(i64), ctypes.POINTER(dbl)], st),
         "sla_reset_profile": ([], st),
     }
@@ -463,6 +464,11 @@ def sla_set_profiling(enable) -> None:
         for c in enable:
             mask |= 1 << (PROFILE_CLASSES[c] if isinstance(c, str) else int(c))
     _check(lib().sla_set_profiling(int(mask)))
+
+
+def sla_set_profiling_stride(every: int) -> None:
+    """Time only the launches of iterations k with k % every == 0."""
+    _check(lib().sla_set_profiling_stride(int(every)))
 
 
 def sla_reset_profile() -> None:

@@ -508,6 +508,15 @@ sla_status sla_set_profiling(int32_t enable) {
   return SLA_OK;
 }
 
+sla_status sla_set_profiling_stride(int32_t every) {
+  if (every < 1) {
+    set_error("every must be >= 1");
+    return SLA_ERR_INVALID_ARG;
+  }
+  prof_every(every);
+  return SLA_OK;
+}
+
 sla_status sla_get_profile(int32_t kernel_class, int64_t* launches, double* total_ms) {
   if (kernel_class < 0 || kernel_class > 3) {
     set_error("kernel_class must be 0..3");

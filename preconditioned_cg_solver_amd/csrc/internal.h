@@ -222,6 +222,7 @@ sla_status lanczos_extremes(const double* alpha, const double* beta, int32_t k, 
 
 // Profiling (solver.hip).
 void prof_enable(int mask);
+void prof_every(int every);
 void prof_get(int cls, int64_t* launches, double* ms);
 void prof_reset();
 

@@ -1275,6 +1275,7 @@ struct ProfClass {
 };
 std::mutex g_prof_mu;
 std::atomic<int> g_prof_mask{0};
+std::atomic<int> g_prof_every{1};  // events on iterations k with k % every == 0
 ProfClass g_prof[4];
 std::vector<std::pair<hipEvent_t, hipEvent_t>> g_spmv_pending;  // standalone SpMV timings
 
@@ -1286,6 +1287,7 @@ struct EventPair {
 
 struct Recorder {
   int mask = 0;
+  int every = 1;
   hipStream_t s = nullptr;
   std::vector<EventPair> ev;
   std::vector<hipEvent_t> pool;
@@ -1298,8 +1300,10 @@ struct Recorder {
     }
     return pool[used++];
   }
-  hipEvent_t begin(int cls) {
-    if (!(mask & (1 << cls))) return nullptr;
+  // Events around the launch of iteration k's class-cls kernel, if that
+  // class is profiled and k is a multiple of the sampling stride.
+  hipEvent_t begin(int cls, int k) {
+    if (!(mask & (1 << cls)) || k % every != 0) return nullptr;
     hipEvent_t e = get();
     if (e) (void)hipEventRecord(e, s);
     return e;
@@ -1508,6 +1512,7 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
 
   Recorder rec;
   rec.mask = g_prof_mask.load();
+  rec.every = g_prof_every.load();
   rec.s = s;
 
   // start-up: r_0 = b, x = 0, t = G^T b, ||b||^2; z_0 = G t + eps r_0, rho_0
@@ -1515,13 +1520,13 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
   aT.in0 = b;
   aT.own = R[0];
   aT.pout = w.prr;
-  hipEvent_t e0 = rec.begin(1);
+  hipEvent_t e0 = rec.begin(1, 0);
   SLA_HIP((launch_step<T, M_GT0>(G, aT, grid, s, plan.nt_g)));
   rec.end(e0, 1, 0);
   if (!fused) aT.pout = nullptr;
   aG.k = 0;
   aG.rv = R[0];
-  e0 = rec.begin(2);
+  e0 = rec.begin(2, 0);
   SLA_HIP((launch_step<T, M_G0>(G, aG, grid, s, plan.nt_g)));
   rec.end(e0, 2, 0);
 
@@ -1545,14 +1550,14 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
           aA.k = kk;
           aA.in1 = P[(kk - 1) & 1];
           aA.own = P[kk & 1];
-          hipEvent_t ea = rec.begin(0);
+          hipEvent_t ea = rec.begin(0, kk);
           if (kk == 1) SLA_HIP((launch_step<T, M_A1>(A, aA, grid, s, plan.nt_a)));
           else SLA_HIP((launch_step<T, M_A>(A, aA, grid, s, plan.nt_a)));
           rec.end(ea, 0, kk);
           aT.k = kk;
           aT.in0 = R[(kk - 1) & 1];
           aT.own = R[kk & 1];
-          hipEvent_t et = rec.begin(1);
+          hipEvent_t et = rec.begin(1, kk);
           SLA_HIP((launch_step<T, M_GT>(G, aT, grid, s, plan.nt_g)));
           rec.end(et, 1, kk);
         } else {
@@ -1567,7 +1572,7 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
           SLA_HIP(hipGetLastError());
           aA.k = kk;
           aA.in0 = P[kk & 1];
-          hipEvent_t ea = rec.begin(0);
+          hipEvent_t ea = rec.begin(0, kk);
           SLA_HIP((launch_step<T, M_AU>(A, aA, grid, s, plan.nt_a)));
           rec.end(ea, 0, kk);
           aR.k = kk;
@@ -1577,14 +1582,14 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
           SLA_HIP(hipGetLastError());
           aT.k = kk;
           aT.in0 = R[kk & 1];
-          hipEvent_t et = rec.begin(1);
+          hipEvent_t et = rec.begin(1, kk);
           SLA_HIP((launch_step<T, M_GTU>(G, aT, grid, s, plan.nt_g)));
           rec.end(et, 1, kk);
           aG.npin = grid;  // rr partials now come from vec_r_update
         }
         aG.k = kk;
         aG.rv = R[kk & 1];
-        hipEvent_t eg = rec.begin(2);
+        hipEvent_t eg = rec.begin(2, kk);
         SLA_HIP((launch_step<T, M_G>(G, aG, grid, s, plan.nt_g)));
         rec.end(eg, 2, kk);
       }
@@ -1891,6 +1896,7 @@ sla_status pattern_grad(const sla_mat& A, const void* lam, const void* x, void* 
 }
 
 void prof_enable(int mask) { g_prof_mask.store(mask & 15); }
+void prof_every(int every) { g_prof_every.store(every < 1 ? 1 : every); }
 // Fold the pending standalone-SpMV event pairs into their class (waits for
 // them); caller holds g_prof_mu.
 void flush_spmv_pending() {

@@ -306,3 +306,29 @@ def test_small_system_wide_rows_fall_back():
     x, info = B.sla_pcg_solve(Ah, Gh, 3e-3, tdev(b), rtol=1e-10, maxit=2000)
     assert info.status == B.OK and iters_close(info.iterations, it)
     assert rel(host(x), x_ref) <= 1e-8
+
+
+@pytest.mark.parametrize("every", [1, 5])
+def test_profiling_launch_counts(every, monkeypatch):
+    """The A-step timing counts one launch per iteration that did work, or
+    one per iteration index divisible by the sampling stride."""
+    monkeypatch.setenv("SLA_SMALL", "0")
+    A = I.poisson2d(37)
+    G = I.spai_factor(A, np.random.default_rng(4))
+    b = I.spmv_test_vector(2, A.n)
+    say("profiling counts, stride", every)
+    hA, hG = create(A), create(G, transpose=True)
+    B.sla_reset_profile()
+    B.sla_set_profiling_stride(every)
+    B.sla_set_profiling(["a_step"])
+    try:
+        _, info = B.sla_pcg_solve(hA, hG, 3e-3, tdev(b), rtol=1e-10, maxit=2000)
+    finally:
+        B.sla_set_profiling(False)
+        B.sla_set_profiling_stride(1)
+    n, ms = B.sla_get_profile("a_step")
+    assert n == info.iterations // every
+    assert ms > 0.0
+    with pytest.raises(B.SlaError) as e:
+        B.sla_set_profiling_stride(0)
+    assert e.value.status == B.ERR_INVALID_ARG
