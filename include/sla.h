@@ -29,6 +29,13 @@
  *    a thread-local message for the last failing call on that thread.
  *  - Nothing here falls back to the CPU: every numerical step runs in the
  *    library's HIP kernels.
+ *  - Device memory that a handle owns (explicit transpose, sliced copies,
+ *    tiles, scratch) comes from a caching allocator in the library:
+ *    sla_mat_destroy parks the buffers in a per-device cache (up to 8 GiB;
+ *    beyond that they are freed) and later handles reuse them, so
+ *    re-creating handles every step costs no hipMalloc / hipFree.  A failed
+ *    allocation empties the cache and retries.  Cached buffers are held
+ *    until the process ends.
  *
  * Environment variables (all optional; the defaults are the measured best
  * choices and no result depends on them beyond rounding order):

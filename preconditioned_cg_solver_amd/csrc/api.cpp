@@ -36,9 +36,12 @@ std::mutex g_dev_mu;
 DeviceInfo g_dev[64];
 bool g_dev_ready[64];
 
+// Returns a handle's buffers to the cache; callers have synchronised the
+// device (destroy) or the creation stream (a failed create) first, so no
+// queued work can still use them.
 void free_owned(sla_mat* m) {
   for (void*& p : m->owned) {
-    if (p) (void)hipFree(p);
+    buf_free(p);
     p = nullptr;
   }
 }
@@ -47,8 +50,8 @@ sla_status alloc_long_scratch(sla_mat* m, MatView& v, int part_slot, int cnt_slo
                               hipStream_t s) {
   const size_t np = (size_t)std::max(1, v.n_long_part);
   const size_t nc = (size_t)std::max(1, v.nlong_rows);
-  SLA_HIP(hipMalloc(&m->owned[part_slot], np * sizeof(double)));
-  SLA_HIP(hipMalloc(&m->owned[cnt_slot], nc * sizeof(int)));
+  SLA_HIP(buf_alloc(&m->owned[part_slot], np * sizeof(double)));
+  SLA_HIP(buf_alloc(&m->owned[cnt_slot], nc * sizeof(int)));
   SLA_HIP(hipMemsetAsync(m->owned[cnt_slot], 0, nc * sizeof(int), s));
   return SLA_OK;
 }

@@ -4,11 +4,85 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdint>
 #include <cstdlib>
+#include <map>
+#include <mutex>
+#include <unordered_map>
+#include <utility>
 
 #include "internal.h"
 
 namespace sla {
+
+// Device memory a handle owns comes from a small caching allocator: a
+// destroyed handle parks its buffers in a per-device cache (up to kCacheKeep
+// bytes), and the next handle reuses a cached buffer of the same or a
+// slightly larger size.  Creating and destroying handles every step (as a
+// training loop does) then costs no hipMalloc / hipFree after the first
+// time; each of those takes tens to hundreds of microseconds and hipFree
+// synchronises the device.  A failed hipMalloc empties the cache and retries.
+namespace {
+constexpr size_t kCacheKeep = 8ull << 30;
+struct BufCache {
+  std::mutex mu;
+  std::multimap<size_t, void*> idle[64];      // size -> buffer, per device
+  std::unordered_map<void*, std::pair<int, size_t>> live;  // buffer -> device, size
+  size_t held[64] = {};
+};
+BufCache& cache() {
+  static BufCache c;
+  return c;
+}
+void drop_idle(BufCache& c, int dev) {
+  for (auto& kv : c.idle[dev]) (void)hipFree(kv.second);
+  c.idle[dev].clear();
+  c.held[dev] = 0;
+}
+}  // namespace
+
+hipError_t buf_alloc(void** p, size_t bytes) {
+  bytes = std::max<size_t>(bytes, 256);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  BufCache& c = cache();
+  std::lock_guard<std::mutex> lk(c.mu);
+  auto it = c.idle[dev].lower_bound(bytes);
+  if (it != c.idle[dev].end() && it->first <= bytes + bytes / 4) {
+    *p = it->second;
+    c.live[*p] = {dev, it->first};
+    c.held[dev] -= it->first;
+    c.idle[dev].erase(it);
+    return hipSuccess;
+  }
+  e = hipMalloc(p, bytes);
+  if (e == hipErrorOutOfMemory && !c.idle[dev].empty()) {
+    (void)hipGetLastError();
+    drop_idle(c, dev);
+    e = hipMalloc(p, bytes);
+  }
+  if (e == hipSuccess) c.live[*p] = {dev, bytes};
+  return e;
+}
+
+void buf_free(void* p) {
+  if (!p) return;
+  BufCache& c = cache();
+  std::lock_guard<std::mutex> lk(c.mu);
+  auto it = c.live.find(p);
+  if (it == c.live.end()) return;
+  const int dev = it->second.first;
+  const size_t bytes = it->second.second;
+  c.live.erase(it);
+  if (c.held[dev] + bytes > kCacheKeep) {
+    (void)hipFree(p);
+    return;
+  }
+  c.idle[dev].insert({bytes, p});
+  c.held[dev] += bytes;
+}
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }

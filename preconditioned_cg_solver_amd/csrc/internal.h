@@ -207,6 +207,10 @@ sla_status pattern_grad_multi(const sla_mat& A, const void* lam, const void* x, 
                               hipStream_t s);
 
 // Host helpers (host_util.cpp).
+// Device buffers owned by handles, from the library's caching allocator
+// (buf_free only after every queued use of the buffer has completed).
+hipError_t buf_alloc(void** p, size_t bytes);
+void buf_free(void* p);
 size_t align_up(size_t v);
 int max_grid();
 int step_grid(int ntiles);

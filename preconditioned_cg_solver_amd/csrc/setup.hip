@@ -477,7 +477,7 @@ sla_status build_tiling(const int32_t* d_rp, int64_t n, MatView& view, void** ow
   SLA_HIP(hipStreamSynchronize(s));
   // one allocation: the tiles, then the row index of every long row
   Tile* tiles = nullptr;
-  SLA_HIP(hipMalloc((void**)&tiles, sizeof(Tile) * (size_t)std::max(1, tot[0]) +
+  SLA_HIP(buf_alloc((void**)&tiles, sizeof(Tile) * (size_t)std::max(1, tot[0]) +
                                         sizeof(int) * (size_t)std::max(1, tot[1])));
   int* lrows = (int*)(tiles + std::max(1, tot[0]));
   hipLaunchKernelGGL(tiling_write, dim3((nblk + 127) / 128), dim3(128), 0, s, d_rp, (int)n, nblk,
@@ -501,9 +501,9 @@ sla_status build_transpose(const sla_mat& m, int32_t** t_rp_out, int32_t** t_ci_
   const size_t es = m.dtype == SLA_F64 ? 8 : 4;
   int32_t *t_rp = nullptr, *t_ci = nullptr;
   void* t_v = nullptr;
-  SLA_HIP(hipMalloc((void**)&t_rp, sizeof(int) * ((size_t)nbr + 1)));
-  SLA_HIP(hipMalloc((void**)&t_ci, sizeof(int) * (size_t)std::max(1, nnzb)));
-  SLA_HIP(hipMalloc(&t_v, es * (size_t)bs * bs * (size_t)std::max(1, nnzb)));
+  SLA_HIP(buf_alloc((void**)&t_rp, sizeof(int) * ((size_t)nbr + 1)));
+  SLA_HIP(buf_alloc((void**)&t_ci, sizeof(int) * (size_t)std::max(1, nnzb)));
+  SLA_HIP(buf_alloc(&t_v, es * (size_t)bs * bs * (size_t)std::max(1, nnzb)));
   *t_rp_out = t_rp;
   *t_ci_out = t_ci;
   *t_v_out = t_v;
@@ -598,7 +598,7 @@ sla_status build_sell(MatView& view, int64_t n, int64_t nnz, int32_t dtype, void
                      (int)n, nslices, slots, maxw, maxd);
   SLA_HIP(hipGetLastError());
   int* soff = nullptr;
-  SLA_HIP(hipMalloc((void**)&soff, sizeof(int) * ((size_t)nslices + 1)));
+  SLA_HIP(buf_alloc((void**)&soff, sizeof(int) * ((size_t)nslices + 1)));
   owned3[2] = soff;
   sla_status st = exclusive_scan(slots, soff, nslices + 1, s);
   if (st != SLA_OK) return st;
@@ -618,9 +618,9 @@ sla_status build_sell(MatView& view, int64_t n, int64_t nnz, int32_t dtype, void
   // kSellTail padding slots past the last slice let the products load whole
   // batches without bounds checks.
   const size_t alloc = (size_t)total + kSellTail;
-  SLA_HIP(hipMalloc(&sv, es * alloc));
+  SLA_HIP(buf_alloc(&sv, es * alloc));
   owned3[0] = sv;
-  SLA_HIP(hipMalloc(&sc, (rel16 ? 2 : 4) * alloc));
+  SLA_HIP(buf_alloc(&sc, (rel16 ? 2 : 4) * alloc));
   owned3[1] = sc;
   SLA_HIP(hipMemsetAsync((char*)sv + es * (size_t)total, 0, es * kSellTail, s));
   if (rel16)
@@ -672,7 +672,7 @@ sla_status build_bsell(MatView& view, int64_t nbr, int64_t nnzb, int32_t dtype, 
                      view.ci, (int)nbr, nslices, slots, maxw, maxd);
   SLA_HIP(hipGetLastError());
   int* soff = nullptr;
-  SLA_HIP(hipMalloc((void**)&soff, sizeof(int) * ((size_t)nslices + 1)));
+  SLA_HIP(buf_alloc((void**)&soff, sizeof(int) * ((size_t)nslices + 1)));
   owned3[2] = soff;
   sla_status st = exclusive_scan(slots, soff, nslices + 1, s);
   if (st != SLA_OK) return st;
@@ -695,9 +695,9 @@ sla_status build_bsell(MatView& view, int64_t nbr, int64_t nnzb, int32_t dtype, 
   const size_t alloc = (size_t)total + kBSellTail;
   void* sv = nullptr;
   void* sc = nullptr;
-  SLA_HIP(hipMalloc(&sv, es * kBSlotVals * alloc));
+  SLA_HIP(buf_alloc(&sv, es * kBSlotVals * alloc));
   owned3[0] = sv;
-  SLA_HIP(hipMalloc(&sc, cs * kBSlotCols * alloc));
+  SLA_HIP(buf_alloc(&sc, cs * kBSlotCols * alloc));
   owned3[1] = sc;
   // every entry is defined: the fill writes the 189 used values and 21 used
   // columns of each slot, this clears the per-row and per-slot pads and the
