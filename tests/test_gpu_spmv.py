@@ -268,3 +268,26 @@ def test_validate_rejects_bad_structure():
     with pytest.raises(B.SlaError) as e:
         B.sla_csr_create(tdev(rp), tdev(M.col_idx), tdev(M.vals))
     assert e.value.status == B.ERR_INVALID_ARG
+
+
+def test_handle_buffers_reused_across_sizes():
+    """Handles created and destroyed in turn reuse cached device buffers
+    (possibly larger than needed and holding an earlier handle's data):
+    every product and transpose still matches the oracle."""
+    seq = [("poisson3d_13", lambda: I.poisson3d(13)), ("bsr_elastic_5", lambda: FACTORS["bsr_G_5"]()),
+           ("poisson3d_13_again", lambda: I.poisson3d(13)), ("poisson2d_37", lambda: I.poisson2d(37)),
+           ("irregular_long_rows", MATRICES["irregular_long_rows"]), ("poisson2d_37_again",
+                                                                      lambda: I.poisson2d(37))]
+    for name, make in seq * 2:
+        M = make()
+        say("handle reuse", name)
+        h = create(M, transpose=True)
+        x = I.spmv_test_vector(3, M.n)
+        y = B.sla_spmv(h, tdev(x))
+        yt = B.sla_spmv(h, tdev(x), transpose=True)
+        torch.cuda.synchronize()
+        assert rel(host(y), oracle.spmv(M, x)) <= 1e-13
+        trp, tci, tv = oracle.transpose(M)
+        Mt = I.SparseMatrix(M.n_block_rows, M.block_dim, trp, tci, tv)
+        assert rel(host(yt), oracle.spmv(Mt, x)) <= 1e-13
+        h.destroy()
