@@ -349,21 +349,46 @@ __global__ void validate_rows(const int* __restrict__ rp, const int* __restrict_
 
 // Per slice: slots (widest row x 64); global: widest row and largest
 // |column - row| (to decide whether int16 offsets can hold the columns).
-__global__ void sell_widths(const int* __restrict__ rp, const int* __restrict__ ci, int n,
-                            int nslices, int* __restrict__ slots, int* __restrict__ maxw,
-                            int* __restrict__ maxd) {
-  const int sl = blockIdx.x * blockDim.x + threadIdx.x;
-  if (sl >= nslices) return;
-  int w = 0, dmax = 0;
-  const int r1 = min(n, (sl + 1) * kSlice);
-  for (int i = sl * kSlice; i < r1; ++i) {
-    const int kb = rp[i], ke = rp[i + 1];
-    w = max(w, ke - kb);
-    if (ke > kb) dmax = max(dmax, max(abs(ci[kb] - i), abs(ci[ke - 1] - i)));
+// One wavefront per slice (lane = row), wavefronts striding over the slices;
+// the maxima are reduced in the workgroup and folded in with one atomic
+// each per workgroup.
+__global__ __launch_bounds__(kWG) void sell_widths(const int* __restrict__ rp,
+                                                   const int* __restrict__ ci, int n, int nslices,
+                                                   int* __restrict__ slots,
+                                                   int* __restrict__ maxw,
+                                                   int* __restrict__ maxd) {
+  __shared__ int s_w[kWaves], s_d[kWaves];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int wmax = 0, dmax = 0;
+  for (int sl = blockIdx.x * kWaves + wv; sl < nslices; sl += gridDim.x * kWaves) {
+    const int i = sl * kSlice + lane;
+    int w = 0, d = 0;
+    if (i < n) {
+      const int kb = rp[i], ke = rp[i + 1];
+      w = ke - kb;
+      if (ke > kb) d = max(abs(ci[kb] - i), abs(ci[ke - 1] - i));
+    }
+    for (int off = 32; off >= 1; off >>= 1) {
+      w = max(w, __shfl_xor(w, off, 64));
+      d = max(d, __shfl_xor(d, off, 64));
+    }
+    if (lane == 0) slots[sl] = w * kSlice;
+    wmax = max(wmax, w);
+    dmax = max(dmax, d);
   }
-  slots[sl] = w * kSlice;
-  atomicMax(maxw, w);
-  atomicMax(maxd, dmax);
+  if (lane == 0) {
+    s_w[wv] = wmax;
+    s_d[wv] = dmax;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 1; k < kWaves; ++k) {
+      wmax = max(wmax, s_w[k]);
+      dmax = max(dmax, s_d[k]);
+    }
+    atomicMax(maxw, wmax);
+    atomicMax(maxd, dmax);
+  }
 }
 
 // Fill the SELL slots of one row (rows past n only get padding).  C is the
@@ -396,21 +421,43 @@ __global__ void sell_fill(const int* __restrict__ rp, const int* __restrict__ ci
 
 // Per slice: slots (widest block row); global: widest block row and largest
 // |block column - block row| (whether int16 offsets can hold the columns).
-__global__ void bsell_widths(const int* __restrict__ rp, const int* __restrict__ ci, int nbr,
-                             int nslices, int* __restrict__ slots, int* __restrict__ maxw,
-                             int* __restrict__ maxd) {
-  const int sl = blockIdx.x * blockDim.x + threadIdx.x;
-  if (sl >= nslices) return;
-  int w = 0, dmax = 0;
-  const int r1 = min(nbr, (sl + 1) * kBSlice);
-  for (int i = sl * kBSlice; i < r1; ++i) {
-    const int kb = rp[i], ke = rp[i + 1];
-    w = max(w, ke - kb);
-    if (ke > kb) dmax = max(dmax, max(abs(ci[kb] - i), abs(ci[ke - 1] - i)));
+// One thread per slice, threads striding over the slices; the maxima are
+// reduced in the workgroup and folded in with one atomic each per workgroup.
+__global__ __launch_bounds__(kWG) void bsell_widths(const int* __restrict__ rp,
+                                                    const int* __restrict__ ci, int nbr,
+                                                    int nslices, int* __restrict__ slots,
+                                                    int* __restrict__ maxw,
+                                                    int* __restrict__ maxd) {
+  __shared__ int s_w[kWaves], s_d[kWaves];
+  int wmax = 0, dmax = 0;
+  for (int sl = blockIdx.x * kWG + threadIdx.x; sl < nslices; sl += gridDim.x * kWG) {
+    int w = 0;
+    const int r1 = min(nbr, (sl + 1) * kBSlice);
+    for (int i = sl * kBSlice; i < r1; ++i) {
+      const int kb = rp[i], ke = rp[i + 1];
+      w = max(w, ke - kb);
+      if (ke > kb) dmax = max(dmax, max(abs(ci[kb] - i), abs(ci[ke - 1] - i)));
+    }
+    slots[sl] = w;
+    wmax = max(wmax, w);
   }
-  slots[sl] = w;
-  atomicMax(maxw, w);
-  atomicMax(maxd, dmax);
+  for (int off = 32; off >= 1; off >>= 1) {
+    wmax = max(wmax, __shfl_xor(wmax, off, 64));
+    dmax = max(dmax, __shfl_xor(dmax, off, 64));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    s_w[threadIdx.x >> 6] = wmax;
+    s_d[threadIdx.x >> 6] = dmax;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 1; k < kWaves; ++k) {
+      wmax = max(wmax, s_w[k]);
+      dmax = max(dmax, s_d[k]);
+    }
+    atomicMax(maxw, wmax);
+    atomicMax(maxd, dmax);
+  }
 }
 
 // Fill the slots of one block row (block rows past nbr only get padding).
@@ -594,8 +641,8 @@ sla_status build_sell(MatView& view, int64_t n, int64_t nnz, int32_t dtype, void
   int* maxw = buf + nslices + 1;
   int* maxd = buf + nslices + 2;
   SLA_HIP(hipMemsetAsync(buf, 0, sizeof(int) * ((size_t)nslices + 3), s));
-  hipLaunchKernelGGL(sell_widths, dim3((nslices + 255) / 256), dim3(256), 0, s, view.rp, view.ci,
-                     (int)n, nslices, slots, maxw, maxd);
+  hipLaunchKernelGGL(sell_widths, dim3(std::min(1024, (nslices + kWaves - 1) / kWaves)), dim3(kWG),
+                     0, s, view.rp, view.ci, (int)n, nslices, slots, maxw, maxd);
   SLA_HIP(hipGetLastError());
   int* soff = nullptr;
   SLA_HIP(buf_alloc((void**)&soff, sizeof(int) * ((size_t)nslices + 1)));
@@ -668,8 +715,8 @@ sla_status build_bsell(MatView& view, int64_t nbr, int64_t nnzb, int32_t dtype, 
   int* maxw = buf + nslices + 1;
   int* maxd = buf + nslices + 2;
   SLA_HIP(hipMemsetAsync(buf, 0, sizeof(int) * ((size_t)nslices + 3), s));
-  hipLaunchKernelGGL(bsell_widths, dim3((nslices + 255) / 256), dim3(256), 0, s, view.rp,
-                     view.ci, (int)nbr, nslices, slots, maxw, maxd);
+  hipLaunchKernelGGL(bsell_widths, dim3(std::min(256, (nslices + kWG - 1) / kWG)), dim3(kWG), 0,
+                     s, view.rp, view.ci, (int)nbr, nslices, slots, maxw, maxd);
   SLA_HIP(hipGetLastError());
   int* soff = nullptr;
   SLA_HIP(buf_alloc((void**)&soff, sizeof(int) * ((size_t)nslices + 1)));
