@@ -120,7 +120,10 @@ sla_status sla_bsr_create(sla_mat_t *out, int64_t n_block_rows, int64_t nnzb, in
                           const int32_t *d_brow_ptr, const int32_t *d_bcol_idx,
                           const void *d_bvals, sla_dtype dtype, uint32_t flags, void *stream);
 
-/* Release the handle and everything it owns (the borrowed arrays are untouched). */
+/* Release the handle and everything it owns (the borrowed arrays are
+ * untouched).  Waits for all work queued on the handle's device, so it may be
+ * called right after asynchronous products; the handle's buffers then go to
+ * the library's buffer cache. */
 sla_status sla_mat_destroy(sla_mat_t m);
 
 /* Sizes of a handle: scalar rows, stored scalar entries, block size, dtype. */

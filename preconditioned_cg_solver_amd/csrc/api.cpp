@@ -236,7 +236,13 @@ sla_status sla_bsr_create(sla_mat_t* out, int64_t n_block_rows, int64_t nnzb, in
 
 sla_status sla_mat_destroy(sla_mat_t m) {
   if (!m) return SLA_OK;
+  // wait for every queued use of the handle on its own device before its
+  // buffers go back to the cache
+  int cur = 0;
+  const bool switch_dev = hipGetDevice(&cur) == hipSuccess && cur != m->device;
+  if (switch_dev) (void)hipSetDevice(m->device);
   (void)hipDeviceSynchronize();
+  if (switch_dev) (void)hipSetDevice(cur);
   free_owned(m);
   delete m;
   return SLA_OK;
