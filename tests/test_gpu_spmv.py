@@ -80,7 +80,7 @@ def test_spmv_fp64(name):
 
 
 @pytest.mark.parametrize("name", ["c1_heat2d_512", "c0_poisson2d_32", "irregular_long_rows",
-                                  "bsr_elastic_5"])
+                                  "bsr_elastic_5", "c2_poisson3d_128", "c3_bsr_elastic_64"])
 def test_spmv_fp32(name):
     M = MATRICES[name]()
     M32 = M.astype(np.float32)
