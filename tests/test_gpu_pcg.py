@@ -332,3 +332,29 @@ def test_profiling_launch_counts(every, monkeypatch):
     with pytest.raises(B.SlaError) as e:
         B.sla_set_profiling_stride(0)
     assert e.value.status == B.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("env", [{"SLA_SELL16": "0", "SLA_MALL_POLICY": "none"},
+                                 {"SLA_MALL_POLICY": "none"}, {"SLA_SELL": "0"},
+                                 {"SLA_SELL16": "0", "SLA_FUSION": "fused"}])
+def test_bsr_engine_variants(env, monkeypatch):
+    """Forward and adjoint parity of the BSR system through each engine form
+    the defaults do not reach at this size: int32 block columns, matrices
+    streamed non-temporally (as when they exceed the Infinity Cache budget),
+    the block-row engine without the sliced layout, the fused iteration."""
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    p = problem("bsr_elastic_6")
+    x_ref, st, it, _ = oracle.pcg(p.A, p.G, p.eps, p.b, p.rtol, p.maxit)
+    gx_ref = I.loss_grad_weights(p, x_ref)
+    lam_ref, gv_ref, st2, it2, _ = oracle.adjoint(p.A, p.G, p.eps, x_ref, gx_ref, p.rtol, p.maxit)
+    say("bsr engine variant", env)
+    A, G = handles(p)
+    x, info = B.sla_pcg_solve(A, G, p.eps, tdev(p.b), rtol=p.rtol, maxit=p.maxit)
+    assert info.status == B.OK and iters_close(info.iterations, it)
+    assert rel(host(x), x_ref) <= 1e-8
+    gx = 2.0 * x if p.loss == "sumsq" else tdev(p.w)
+    grad_b, grad_vals, ainfo = B.sla_pcg_adjoint(A, G, p.eps, x, gx, rtol=p.rtol, maxit=p.maxit)
+    assert ainfo.status == B.OK and iters_close(ainfo.iterations, it2)
+    assert rel(host(grad_b), lam_ref) <= 1e-7
+    assert rel(host(grad_vals), gv_ref) <= 1e-7
