@@ -334,21 +334,28 @@ def test_profiling_launch_counts(every, monkeypatch):
     assert e.value.status == B.ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("env", [{"SLA_SELL16": "0", "SLA_MALL_POLICY": "none"},
-                                 {"SLA_MALL_POLICY": "none"}, {"SLA_SELL": "0"},
-                                 {"SLA_SELL16": "0", "SLA_FUSION": "fused"}])
-def test_bsr_engine_variants(env, monkeypatch):
-    """Forward and adjoint parity of the BSR system through each engine form
-    the defaults do not reach at this size: int32 block columns, matrices
-    streamed non-temporally (as when they exceed the Infinity Cache budget),
-    the block-row engine without the sliced layout, the fused iteration."""
+ENGINE_VARIANTS = [{"SLA_SELL16": "0", "SLA_MALL_POLICY": "none"}, {"SLA_MALL_POLICY": "none"},
+                   {"SLA_SELL": "0"}, {"SLA_SELL16": "0", "SLA_FUSION": "fused"},
+                   {"SLA_SELL": "0", "SLA_FUSION": "fused"},
+                   {"SLA_SELL16": "0", "SLA_FUSION": "unfused"}]
+
+
+@pytest.mark.parametrize("key", ["bsr_elastic_6", "poisson3d_13"])
+@pytest.mark.parametrize("env", ENGINE_VARIANTS)
+def test_engine_variants(key, env, monkeypatch):
+    """Forward and adjoint parity through each engine form the defaults do
+    not reach at these sizes: int32 (block) columns in the sliced layouts,
+    matrices streamed non-temporally (as when they exceed the Infinity Cache
+    budget), the tile / block-row engines without the sliced layout, and the
+    iteration form the library would not pick."""
+    monkeypatch.setenv("SLA_SMALL", "0")
     for k, v in env.items():
         monkeypatch.setenv(k, v)
-    p = problem("bsr_elastic_6")
+    p = problem(key)
     x_ref, st, it, _ = oracle.pcg(p.A, p.G, p.eps, p.b, p.rtol, p.maxit)
     gx_ref = I.loss_grad_weights(p, x_ref)
     lam_ref, gv_ref, st2, it2, _ = oracle.adjoint(p.A, p.G, p.eps, x_ref, gx_ref, p.rtol, p.maxit)
-    say("bsr engine variant", env)
+    say("engine variant", key, env)
     A, G = handles(p)
     x, info = B.sla_pcg_solve(A, G, p.eps, tdev(p.b), rtol=p.rtol, maxit=p.maxit)
     assert info.status == B.OK and iters_close(info.iterations, it)
