@@ -967,21 +967,28 @@ __device__ __forceinline__ T small_dot_row(const T (&val)[kSmallW], const int (&
   return acc;
 }
 
-__device__ __forceinline__ double small_sum(double v, double* red) {
+// Workgroup sums in a fixed order (wave sums, then the waves in order).  The
+// reductions alternate between two LDS buffers (red[0..], red[2 kSmallWaves
+// ..]), so no barrier is needed before a buffer is written: it was last read
+// two reductions earlier, and every thread has passed the barrier of the
+// reduction in between since.
+__device__ __forceinline__ double small_sum(double v, double* red, int& buf) {
+  double* rb = red + buf * 2 * kSmallWaves;
+  buf ^= 1;
   v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) rb[threadIdx.x >> 6] = v;
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  double s = red[0];
+  double s = rb[0];
 #pragma unroll
-  for (int q = 1; q < kSmallWaves; ++q) s += red[q];
+  for (int q = 1; q < kSmallWaves; ++q) s += rb[q];
   return s;
 }
 
 template <typename T>
 __global__ __launch_bounds__(kSmallN) void small_pcg(SmallArgs<T> a) {
   __shared__ T s_p[kSmallN], s_r[kSmallN], s_t[kSmallN];
-  __shared__ double s_red[kSmallWaves];
+  __shared__ double s_red[4 * kSmallWaves];  // two buffers (small_sum)
+  int rbuf = 0;
   const int i = threadIdx.x;
   const bool live = i < a.n;
   T av[kSmallW], gv[kSmallW], tv[kSmallW];
@@ -1001,7 +1008,7 @@ __global__ __launch_bounds__(kSmallN) void small_pcg(SmallArgs<T> a) {
   T x = T(0), r = bi;
   const bool lead = i == 0;
   int kind = EX_NONE, kexit = 0;
-  const double bb = small_sum((double)bi * (double)bi, s_red);
+  const double bb = small_sum((double)bi * (double)bi, s_red, rbuf);
   double rr = bb;
   if (!isfinite(bb)) kind = EX_NONFINITE_B;
   else if (bb == 0.0) kind = EX_BZERO;
@@ -1016,7 +1023,7 @@ __global__ __launch_bounds__(kSmallN) void small_pcg(SmallArgs<T> a) {
     s_t[i] = small_dot_row(tv, tc, s_r);
     __syncthreads();
     z = fma(T(a.eps), r, small_dot_row(gv, gc, s_t));
-    rho = small_sum((double)r * (double)z, s_red);
+    rho = small_sum((double)r * (double)z, s_red, rbuf);
     if (!(rho > 0.0) || !isfinite(rho)) {
       kind = EX_BREAK_RHO;
       kexit = 1;
@@ -1027,7 +1034,7 @@ __global__ __launch_bounds__(kSmallN) void small_pcg(SmallArgs<T> a) {
     s_p[i] = p;
     __syncthreads();
     const T q = small_dot_row(av, ac, s_p);
-    const double sigma = small_sum((double)p * (double)q, s_red);
+    const double sigma = small_sum((double)p * (double)q, s_red, rbuf);
     if (!(sigma > 0.0) || !isfinite(sigma)) {
       kind = EX_BREAK_SIGMA;
       kexit = k;
@@ -1037,7 +1044,7 @@ __global__ __launch_bounds__(kSmallN) void small_pcg(SmallArgs<T> a) {
     if (lead && a.hist_a && k <= a.hist_len) a.hist_a[k - 1] = alpha;
     x = fma(T(alpha), p, x);
     r = fma(T(-alpha), q, r);
-    rr = small_sum((double)r * (double)r, s_red);
+    rr = small_sum((double)r * (double)r, s_red, rbuf);
     const double rnorm = sqrt(rr);
     if (!isfinite(rnorm)) kind = EX_BREAK_RR;
     else if (rnorm <= a.rtol * bnorm) kind = EX_CONV;
@@ -1051,7 +1058,7 @@ __global__ __launch_bounds__(kSmallN) void small_pcg(SmallArgs<T> a) {
     s_t[i] = small_dot_row(tv, tc, s_r);
     __syncthreads();
     z = fma(T(a.eps), r, small_dot_row(gv, gc, s_t));
-    const double rho_new = small_sum((double)r * (double)z, s_red);
+    const double rho_new = small_sum((double)r * (double)z, s_red, rbuf);
     if (!(rho_new > 0.0) || !isfinite(rho_new)) {
       kind = EX_BREAK_RHO;
       kexit = k + 1;
