@@ -13,9 +13,26 @@ namespace sla {
 // Reductions (deterministic: fixed association order)
 // ---------------------------------------------------------------------------
 
+// A double moved between lanes by a DPP pattern (both 32-bit halves).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xf, 0xf, false);
+  return __hiloint2double(hi, lo);
+}
+
+// Sum over the 64 lanes, the same value in every lane: within each 16-lane
+// row by DPP moves (lane pairs l ^ 1, then l ^ 2, then the mirrored half of
+// the 8-lane group, then the mirrored half of the row), then across rows by
+// two cross-lane permutes (l ^ 16, l ^ 32).  Every step adds a lane pair in
+// both orders, so all lanes hold the identical sum.
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  v += dpp_f64<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f64<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f64<0x141>(v);  // row_half_mirror
+  v += dpp_f64<0x140>(v);  // row_mirror
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
   return v;
 }
 
