@@ -21,19 +21,35 @@ __device__ __forceinline__ double dpp_f64(double v) {
   return __hiloint2double(hi, lo);
 }
 
+// Sum of the two 16-lane rows of each 32-lane half (even row + odd row, in
+// that order in every lane) and of the two 32-lane halves (lower + upper):
+// the gfx950 lane swaps, with the value as both operands, return the even
+// and the odd row (the lower and the upper half) in every lane.
+__device__ __forceinline__ double rows_pair_sum(double v) {
+  const unsigned lo = (unsigned)__double2loint(v), hi = (unsigned)__double2hiint(v);
+  const auto l = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  const auto h = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  return __hiloint2double((int)h[0], (int)l[0]) + __hiloint2double((int)h[1], (int)l[1]);
+}
+__device__ __forceinline__ double halves_sum(double v) {
+  const unsigned lo = (unsigned)__double2loint(v), hi = (unsigned)__double2hiint(v);
+  const auto l = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  const auto h = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  return __hiloint2double((int)h[0], (int)l[0]) + __hiloint2double((int)h[1], (int)l[1]);
+}
+
 // Sum over the 64 lanes, the same value in every lane: within each 16-lane
 // row by DPP moves (lane pairs l ^ 1, then l ^ 2, then the mirrored half of
-// the 8-lane group, then the mirrored half of the row), then across rows by
-// two cross-lane permutes (l ^ 16, l ^ 32).  Every step adds a lane pair in
-// both orders, so all lanes hold the identical sum.
+// the 8-lane group, then the mirrored half of the row; each adds a lane pair
+// in both orders, which IEEE addition makes identical), then across rows
+// and halves by the lane swaps.  No LDS round trip.
 __device__ __forceinline__ double wave_sum(double v) {
   v += dpp_f64<0xB1>(v);   // quad_perm [1,0,3,2]
   v += dpp_f64<0x4E>(v);   // quad_perm [2,3,0,1]
   v += dpp_f64<0x141>(v);  // row_half_mirror
   v += dpp_f64<0x140>(v);  // row_mirror
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
-  return v;
+  v = rows_pair_sum(v);
+  return halves_sum(v);
 }
 
 // Sum over the workgroup; every thread gets lane 0 / wave order's value.
