@@ -53,6 +53,9 @@
  *    when it fits the budget, otherwise none; the rest stream non-temporally).
  *  - SLA_BATCH_ITERS (default 16, 1..4096): iterations enqueued between two
  *    host polls of the device exit flag.
+ *  - SLA_ORDER=0|1: locality ordering of the solves off, or on for every CSR
+ *    matrix outside the SELL layout (default: automatic, see
+ *    sla_mat_reordered).
  * SLA_GRID is read once per device, SLA_MALL_BUDGET_MB and SLA_BATCH_ITERS
  * once per process; the others at every handle creation or solve.
  */
@@ -142,6 +145,32 @@ sla_status sla_mat_transpose_arrays(sla_mat_t m, const int32_t **d_row_ptr,
 /* Number of SpMV tiles (row bins) of the handle and how many of them are long
  * rows processed by row splitting; for tests and reports. */
 sla_status sla_mat_tiling(sla_mat_t m, int32_t transpose, int64_t *n_tiles, int64_t *n_long);
+
+/*
+ * Whether one-right-hand-side solves (sla_pcg_solve, sla_pcg_solve_history,
+ * sla_pcg_adjoint) with m as A run on a locality ordering: *reordered = 1 or
+ * 0, decided when m was created.  Such a solve applies one symmetric
+ * permutation P to the whole system (P A P^T y = P b with the preconditioner
+ * P G G^T P^T + eps I, which is P M^-1 P^T, so the iterates are those of the
+ * unpermuted solve up to rounding order) and returns x = P^T y; dL/dA is
+ * still computed on A's own storage order.  P sorts the rows by decreasing
+ * length, so the most-referenced entries of the gathered vectors share cache
+ * lines, and deals them round-robin over eight contiguous row segments, so
+ * the per-XCD shares of the row-parallel kernels get the same mix of long
+ * and short rows.  It applies to CSR matrices outside the SELL layout with
+ * at least 131072 rows whose sampled stored entries lie mostly more than
+ * 32768 rows from the diagonal (random-graph-like gathers with no locality
+ * to lose); SLA_ORDER=0 turns it off and SLA_ORDER=1 applies it to every
+ * CSR matrix outside the SELL layout.  The first such solve builds P (on
+ * the device), P A P^T into A's handle and P G P^T into G's handle (G's copy
+ * is rebuilt when G is next used with another reordered A); they stay until
+ * the handles are destroyed, so the handles then hold twice their matrices'
+ * memory.  That first solve is synchronous set-up work and must not overlap
+ * other calls on the same handles.  The workspace of such an A holds two
+ * more n-vectors (sla_pcg_workspace_size includes them).  The several-
+ * right-hand-side solves do not reorder.
+ */
+sla_status sla_mat_reordered(sla_mat_t m, int32_t *reordered);
 
 /* y = A x (transpose = 0) or y = A^T x via the explicit transpose (transpose = 1).
  * d_x[n] and d_y[n] must not overlap.  Asynchronous on `stream`. */

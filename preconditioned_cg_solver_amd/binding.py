@@ -69,6 +69,7 @@ def _declare(L):
         "sla_mat_transpose_arrays": ([vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                       ctypes.POINTER(vp)], st),
         "sla_mat_tiling": ([vp, i32, ctypes.POINTER(i64), ctypes.POINTER(i64)], st),
+        "sla_mat_reordered": ([vp, ctypes.POINTER(i32)], st),
         "sla_spmv": ([vp, vp, vp, vp], st),
         "sla_spmv_t": ([vp, vp, vp, vp], st),
         "sla_pcg_workspace_size": ([vp, ctypes.POINTER(sz)], st),
@@ -209,6 +210,13 @@ def sla_mat_tiling(A: Mat, transpose: bool = False) -> Tuple[int, int]:
     nt, nl = ctypes.c_int64(), ctypes.c_int64()
     _check(lib().sla_mat_tiling(A.handle, int(transpose), ctypes.byref(nt), ctypes.byref(nl)))
     return nt.value, nl.value
+
+
+def sla_mat_reordered(A: Mat) -> bool:
+    """True when one-right-hand-side solves with A run on its locality ordering."""
+    r = ctypes.c_int32()
+    _check(lib().sla_mat_reordered(A.handle, ctypes.byref(r)))
+    return bool(r.value)
 
 
 def sla_mat_transpose_arrays(A: Mat):

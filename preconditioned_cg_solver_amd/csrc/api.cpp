@@ -29,7 +29,10 @@ enum OwnedSlot {
   O_TCI = 7,
   O_TV = 8,
   O_SELL_F = 9,   // 9, 10, 11: values, columns, slice offsets
-  O_SELL_T = 12   // 12, 13, 14
+  O_SELL_T = 12,  // 12, 13, 14
+  O_ORD_RP = 15,  // arrays of a permuted copy (15, 16, 17)
+  O_PERM = 18,
+  O_IPERM = 19
 };
 
 std::mutex g_dev_mu;
@@ -44,6 +47,13 @@ void free_owned(sla_mat* m) {
     buf_free(p);
     p = nullptr;
   }
+}
+
+// Frees a handle, its permuted copy and their buffers (same precondition).
+void destroy_handle(sla_mat* m) {
+  if (m->ord) destroy_handle(m->ord);
+  free_owned(m);
+  delete m;
 }
 
 sla_status alloc_long_scratch(sla_mat* m, MatView& v, int part_slot, int cnt_slot,
@@ -69,9 +79,32 @@ bool check(bool ok, const char* msg) {
   return ok;
 }
 
+// Whether solves with m as A run on the locality ordering: SLA_ORDER=0 never,
+// =1 for every CSR matrix outside the SELL layout, otherwise (auto) when such
+// a matrix has at least kOrderMinRows rows and at least half of
+// kOrderSamples evenly spaced stored entries lie more than kOrderNear rows
+// from the diagonal (gathers with no locality for the ordering to lose).
+sla_status decide_order(sla_mat* m, hipStream_t s) {
+  m->ord_want = false;
+  if (m->bs != 1 || m->fwd.sell || m->nbr == 0 || m->nnzb == 0) return SLA_OK;
+  const char* e = getenv("SLA_ORDER");
+  if (e && e[0] == '0') return SLA_OK;
+  if (e && e[0] == '1') {
+    m->ord_want = true;
+    return SLA_OK;
+  }
+  if (m->nbr < kOrderMinRows) return SLA_OK;
+  const int samples = (int)std::min<int64_t>(m->nnzb, kOrderSamples);
+  int far = 0;
+  sla_status st = count_far_entries(*m, samples, kOrderNear, &far, s);
+  if (st != SLA_OK) return st;
+  m->ord_want = 2 * (int64_t)far >= samples;
+  return SLA_OK;
+}
+
 sla_status create_common(sla_mat_t* out, int64_t nbr, int64_t nnzb, int32_t bs, const int32_t* rp,
                          const int32_t* ci, const void* v, sla_dtype dtype, uint32_t flags,
-                         void* stream) {
+                         void* stream, bool ordering = true) {
   if (!check(out != nullptr, "out is NULL")) return SLA_ERR_INVALID_ARG;
   *out = nullptr;
   if (!check(nbr >= 0 && nnzb >= 0, "negative size")) return SLA_ERR_INVALID_ARG;
@@ -120,6 +153,7 @@ sla_status create_common(sla_mat_t* out, int64_t nbr, int64_t nnzb, int32_t bs, 
   if (st == SLA_OK && bs == 3 && sell_enabled())
     st = build_bsell(m->fwd, nbr, nnzb, dtype, &m->owned[O_SELL_F], s);
   if (st == SLA_OK) st = alloc_long_scratch(m, m->fwd, O_LPART_F, O_LCNT_F, s);
+  if (st == SLA_OK && ordering) st = decide_order(m, s);
   if (st == SLA_OK && (flags & SLA_BUILD_TRANSPOSE)) {
     int32_t *trp = nullptr, *tci = nullptr;
     void* tv = nullptr;
@@ -152,6 +186,101 @@ sla_status create_common(sla_mat_t* out, int64_t nbr, int64_t nnzb, int32_t bs, 
   }
   *out = m;
   return SLA_OK;
+}
+
+// P M P^T as a handle of its own that owns its arrays (transpose built when
+// asked).  P is given by perm / iperm.
+sla_status make_permuted(const sla_mat& src, const int32_t* perm, const int32_t* iperm,
+                         bool transpose, sla_mat** out, hipStream_t s) {
+  int32_t *rp = nullptr, *ci = nullptr;
+  void* v = nullptr;
+  sla_status st = build_permuted(src, perm, iperm, &rp, &ci, &v, s);
+  if (st == SLA_OK)
+    st = create_common(out, src.nbr, src.nnzb, 1, rp, ci, v, (sla_dtype)src.dtype,
+                       transpose ? SLA_BUILD_TRANSPOSE : 0, s, false);
+  if (st != SLA_OK) {
+    (void)hipStreamSynchronize(s);
+    buf_free(rp);
+    buf_free(ci);
+    buf_free(v);
+    return st;
+  }
+  (*out)->owned[O_ORD_RP] = rp;
+  (*out)->owned[O_ORD_RP + 1] = ci;
+  (*out)->owned[O_ORD_RP + 2] = v;
+  return SLA_OK;
+}
+
+std::mutex g_order_mu;
+uint64_t g_order_serial = 0;
+
+// Builds, at the first solve that needs them, A's ordering with P A P^T and
+// P G P^T for that ordering (rebuilt when G was last used with another A).
+// *use = false when A's solves do not reorder.
+sla_status ensure_order(sla_mat* A, sla_mat* G, hipStream_t s, bool* use) {
+  *use = false;
+  if (!A->ord_want || A == G || A->n() == 0) return SLA_OK;
+  std::lock_guard<std::mutex> lk(g_order_mu);
+  sla_status st = SLA_OK;
+  if (!A->perm) {
+    int32_t *perm = nullptr, *iperm = nullptr;
+    st = build_order(*A, &perm, &iperm, s);
+    if (st != SLA_OK) {
+      (void)hipStreamSynchronize(s);
+      buf_free(perm);
+      buf_free(iperm);
+      return st;
+    }
+    A->owned[O_PERM] = perm;
+    A->owned[O_IPERM] = iperm;
+    A->perm = perm;
+    A->iperm = iperm;
+  }
+  if (!A->ord) {
+    if ((st = make_permuted(*A, A->perm, A->iperm, false, &A->ord, s)) != SLA_OK) return st;
+    A->ord_id = ++g_order_serial;
+  }
+  if (!G->ord || G->ord_id != A->ord_id) {
+    if (G->ord) {
+      (void)hipDeviceSynchronize();
+      destroy_handle(G->ord);
+      G->ord = nullptr;
+    }
+    if ((st = make_permuted(*G, A->perm, A->iperm, true, &G->ord, s)) != SLA_OK) return st;
+    G->ord_id = A->ord_id;
+  }
+  *use = true;
+  return SLA_OK;
+}
+
+// One-right-hand-side solve, on A's locality ordering when it has one: b
+// enters as P b, the solve runs on P A P^T and P G P^T, and x = P^T x~.
+// The permuted b and x sit after the base workspace.
+sla_status solve_any(sla_mat* A, sla_mat* G, double eps, const void* b, void* x, double rtol,
+                     int32_t maxit, void* work, size_t work_bytes, hipStream_t s,
+                     sla_solve_info* info, double* ha = nullptr, double* hb = nullptr,
+                     int32_t hl = 0) {
+  bool use = false;
+  sla_status st = ensure_order(A, G, s, &use);
+  if (st != SLA_OK) return st;
+  if (!use)
+    return sla::pcg_solve(*A, *G, eps, b, x, rtol, maxit, work, work_bytes, s, info, ha, hb, hl);
+  const size_t base = workspace_base(*A);
+  const size_t vb = align_up((size_t)A->n() * (A->dtype == SLA_F64 ? 8 : 4));
+  void* pb = (char*)work + base;
+  void* px = (char*)work + base + vb;
+  if ((st = permute_vec(A->perm, b, pb, A->n(), A->dtype, true, s)) != SLA_OK) return st;
+  if ((st = permute_vec(A->perm, nullptr, px, A->n(), A->dtype, true, s)) != SLA_OK) return st;
+  st = sla::pcg_solve(*A->ord, *G->ord, eps, pb, px, rtol, maxit, work, base, s, info, ha, hb,
+                      hl);
+  if (st == SLA_ERR_HIP || st == SLA_ERR_OOM || st == SLA_ERR_INVALID_ARG ||
+      st == SLA_ERR_UNSUPPORTED)
+    return st;
+  sla_status pst = permute_vec(A->perm, px, x, A->n(), A->dtype, false, s);
+  if (pst != SLA_OK) return pst;
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  return st;
 }
 
 // k = 0: one right-hand side; k >= 1: the multi-RHS solver's workspace.
@@ -243,8 +372,7 @@ sla_status sla_mat_destroy(sla_mat_t m) {
   if (switch_dev) (void)hipSetDevice(m->device);
   (void)hipDeviceSynchronize();
   if (switch_dev) (void)hipSetDevice(cur);
-  free_owned(m);
-  delete m;
+  destroy_handle(m);
   return SLA_OK;
 }
 
@@ -281,6 +409,15 @@ sla_status sla_mat_tiling(sla_mat_t m, int32_t transpose, int64_t* n_tiles, int6
   const MatView& v = transpose ? m->tr : m->fwd;
   if (n_tiles) *n_tiles = m->bs == 1 ? v.ntiles : (m->nbr + kBsrTileRows - 1) / kBsrTileRows;
   if (n_long) *n_long = v.nlong;
+  return SLA_OK;
+}
+
+sla_status sla_mat_reordered(sla_mat_t m, int32_t* reordered) {
+  if (!m || !reordered) {
+    set_error("NULL argument");
+    return SLA_ERR_INVALID_ARG;
+  }
+  *reordered = m->ord_want ? 1 : 0;
   return SLA_OK;
 }
 
@@ -327,7 +464,7 @@ sla_status sla_precond_apply(sla_mat_t G, double eps, const void* d_r, void* d_z
     set_error("eps must be finite and >= 0");
     return SLA_ERR_INVALID_ARG;
   }
-  if (G->n() > 0 && (!d_r || !d_z || d_r == d_z || !d_work || work_bytes < workspace_bytes(*G))) {
+  if (G->n() > 0 && (!d_r || !d_z || d_r == d_z || !d_work || work_bytes < workspace_base(*G))) {
     set_error("bad vector or workspace argument");
     return SLA_ERR_INVALID_ARG;
   }
@@ -339,8 +476,8 @@ sla_status sla_pcg_solve(sla_mat_t A, sla_mat_t G, double eps, const void* d_b, 
                          sla_solve_info* info) {
   sla_status st = check_solve(A, G, eps, d_b, d_x, rtol, maxit, d_work, work_bytes);
   if (st != SLA_OK) return st;
-  return sla::pcg_solve(*A, *G, eps, d_b, d_x, rtol, maxit, d_work, work_bytes,
-                        (hipStream_t)stream, info);
+  return solve_any(A, G, eps, d_b, d_x, rtol, maxit, d_work, work_bytes, (hipStream_t)stream,
+                   info);
 }
 
 sla_status sla_pcg_solve_history(sla_mat_t A, sla_mat_t G, double eps, const void* d_b, void* d_x,
@@ -353,8 +490,8 @@ sla_status sla_pcg_solve_history(sla_mat_t A, sla_mat_t G, double eps, const voi
     set_error("history buffers must hold hist_len doubles each");
     return SLA_ERR_INVALID_ARG;
   }
-  return sla::pcg_solve(*A, *G, eps, d_b, d_x, rtol, maxit, d_work, work_bytes,
-                        (hipStream_t)stream, info, d_alpha, d_beta, hist_len);
+  return solve_any(A, G, eps, d_b, d_x, rtol, maxit, d_work, work_bytes, (hipStream_t)stream,
+                   info, d_alpha, d_beta, hist_len);
 }
 
 sla_status sla_pcg_adjoint(sla_mat_t A, sla_mat_t G, double eps, const void* d_x,
@@ -368,7 +505,7 @@ sla_status sla_pcg_adjoint(sla_mat_t A, sla_mat_t G, double eps, const void* d_x
     return SLA_ERR_INVALID_ARG;
   }
   hipStream_t s = (hipStream_t)stream;
-  st = sla::pcg_solve(*A, *G, eps, d_grad_x, d_grad_b, rtol, maxit, d_work, work_bytes, s, info);
+  st = solve_any(A, G, eps, d_grad_x, d_grad_b, rtol, maxit, d_work, work_bytes, s, info);
   if (st < 0) return st;
   sla_status gs = sla::pattern_grad(*A, d_grad_b, d_x, d_grad_vals, s);
   if (gs != SLA_OK) return gs;

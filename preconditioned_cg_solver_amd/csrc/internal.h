@@ -20,6 +20,16 @@ constexpr int kWaves = kWG / 64;
 constexpr int kTileRows = 256;
 constexpr int kLdsCap = 2048;
 constexpr int kLongChunk = 4096;
+// Locality ordering of the solves (CSR matrices outside the SELL layout
+// with at least kOrderMinRows rows whose sampled entries lie mostly more
+// than kOrderNear rows from the diagonal): rows sorted by decreasing length
+// (lengths capped at kOrderKeyMax for the sort) and dealt over eight row
+// segments; see build_order.
+constexpr int kOrderKeyBits = 16;
+constexpr int kOrderKeyMax = (1 << kOrderKeyBits) - 1;
+constexpr int kOrderMinRows = 1 << 17;
+constexpr int kOrderNear = 1 << 15;
+constexpr int kOrderSamples = 1 << 16;
 // Sliced ELLPACK with one wavefront per slice (SELL-64): used for a CSR
 // orientation whose rows are short and of even length (at most
 // kSellMaxWidth nonzeros per row, padding at most kSellMaxPadPct percent).
@@ -139,8 +149,18 @@ struct sla_mat {
   sla::MatView fwd;
   bool has_t = false;
   sla::MatView tr;
-  // owned device memory: tiles, long-row scratch and the transpose arrays
-  void* owned[16] = {};
+  // owned device memory: tiles, long-row scratch, the transpose arrays and,
+  // for the copies below, the permuted arrays and the permutation
+  void* owned[20] = {};
+  // Locality ordering used by the solves with this handle as A (decided at
+  // creation, built at the first solve): perm maps a row of P A P^T to A's
+  // row, iperm the other way; ord is P A P^T, or for a G handle P G P^T of
+  // the A ordering numbered ord_id.
+  bool ord_want = false;
+  const int32_t* perm = nullptr;
+  const int32_t* iperm = nullptr;
+  sla_mat* ord = nullptr;
+  uint64_t ord_id = 0;
   int64_t n() const { return nbr * bs; }
   int64_t nnz() const { return nnzb * bs * bs; }
 };
@@ -175,8 +195,18 @@ sla_status build_sell(MatView& view, int64_t n, int64_t nnz, int32_t dtype, void
                       hipStream_t s);
 sla_status build_bsell(MatView& view, int64_t nbr, int64_t nnzb, int32_t dtype, void** owned3,
                        hipStream_t s);
+sla_status count_far_entries(const sla_mat& m, int samples, int near, int* far, hipStream_t s);
+sla_status build_order(const sla_mat& m, int32_t** perm, int32_t** iperm, hipStream_t s);
+sla_status build_permuted(const sla_mat& m, const int32_t* perm, const int32_t* iperm,
+                          int32_t** rp, int32_t** ci, void** v, hipStream_t s);
+// into: dst[j] = src[perm[j]]; otherwise dst[perm[j]] = src[j]; src == NULL
+// zeroes dst.
+sla_status permute_vec(const int32_t* perm, const void* src, void* dst, int64_t n, int32_t dtype,
+                       bool into, hipStream_t s);
 
-// Solver (solver.hip).
+// Solver (solver.hip).  workspace_bytes = workspace_base plus, for an A the
+// solves reorder, the two permuted vectors (b and x) after it.
+size_t workspace_base(const sla_mat& A);
 size_t workspace_bytes(const sla_mat& A);
 sla_status spmv(const sla_mat& A, bool transpose, const void* x, void* y, hipStream_t s);
 sla_status precond_apply(const sla_mat& G, double eps, const void* r, void* z, void* work,

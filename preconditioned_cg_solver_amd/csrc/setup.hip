@@ -322,6 +322,88 @@ __global__ void transpose_fill(const int* __restrict__ rp, const T* __restrict__
 }
 
 // ---------------------------------------------------------------------------
+// Locality ordering of irregular matrices: a symmetric permutation P that
+// puts high-degree rows first (so the entries most gathered share cache
+// lines) and deals them round-robin over eight contiguous row segments (one
+// per XCD share of the row-parallel kernels, so each gets the same mix).
+// ---------------------------------------------------------------------------
+
+// Sampled count of stored entries far from the diagonal: entry e_k =
+// floor(k nnz / samples) for k < samples, far when |col - row| > near.
+__global__ __launch_bounds__(kWG) void sample_far(const int* __restrict__ rp,
+                                                  const int* __restrict__ ci, int n, int nnz,
+                                                  int samples, int near, int* __restrict__ far) {
+  __shared__ int cnt;
+  if (threadIdx.x == 0) cnt = 0;
+  __syncthreads();
+  int mine = 0;
+  for (int k = blockIdx.x * kWG + threadIdx.x; k < samples; k += gridDim.x * kWG) {
+    const int e = (int)((int64_t)k * nnz / samples);
+    const int r = row_of(rp, n, e);
+    const int d = ci[e] - r;
+    mine += (d > near || d < -near) ? 1 : 0;
+  }
+  atomicAdd(&cnt, mine);
+  __syncthreads();
+  if (threadIdx.x == 0) atomicAdd(far, cnt);
+}
+
+// Sort key of row i: longer rows first (ascending keys), lengths capped.
+__global__ void order_keys(const int* __restrict__ rp, int n, int* __restrict__ keys) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+    keys[i] = kOrderKeyMax - min(rp[i + 1] - rp[i], kOrderKeyMax);
+}
+
+// Rank k of the degree order (row srt[k]) goes to segment k mod 8, position
+// floor(k / 8) inside it; segment x starts at seg.start[x].
+struct SegStarts {
+  int start[8];
+};
+__global__ void order_deal(const int* __restrict__ srt, int n, SegStarts seg,
+                           int* __restrict__ perm, int* __restrict__ iperm) {
+  for (int k = blockIdx.x * blockDim.x + threadIdx.x; k < n; k += gridDim.x * blockDim.x) {
+    const int pos = seg.start[k & 7] + (k >> 3);
+    const int o = srt[k];
+    perm[pos] = o;
+    iperm[o] = pos;
+  }
+}
+
+// Row lengths of P M P^T (slot n is 0, so the exclusive scan ends at nnz).
+__global__ void perm_lengths(const int* __restrict__ rp, const int* __restrict__ perm, int n,
+                             int* __restrict__ len) {
+  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j <= n; j += gridDim.x * blockDim.x)
+    len[j] = j < n ? rp[perm[j] + 1] - rp[perm[j]] : 0;
+}
+
+// Entry k of P M P^T: row j of the new matrix is row perm[j] of M, entries
+// in M's order, columns renamed through iperm.
+template <typename T>
+__global__ void perm_fill(const int* __restrict__ rp, const int* __restrict__ ci,
+                          const T* __restrict__ v, const int* __restrict__ nrp,
+                          const int* __restrict__ perm, const int* __restrict__ iperm, int n,
+                          int nnz, int* __restrict__ nci, T* __restrict__ nv) {
+  for (int k = blockIdx.x * blockDim.x + threadIdx.x; k < nnz; k += gridDim.x * blockDim.x) {
+    const int j = row_of(nrp, n, k);
+    const int src = rp[perm[j]] + (k - nrp[j]);
+    nci[k] = iperm[ci[src]];
+    nv[k] = v[src];
+  }
+}
+
+// dst[j] = src[perm[j]] (into the ordering) or dst[perm[j]] = src[j] (back);
+// src == nullptr writes zeros to dst[j].
+template <typename T>
+__global__ void permute_vec_k(const int* __restrict__ perm, const T* __restrict__ src,
+                              T* __restrict__ dst, int n, bool into) {
+  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < n; j += gridDim.x * blockDim.x) {
+    if (!src) dst[j] = T(0);
+    else if (into) dst[j] = src[perm[j]];
+    else dst[perm[j]] = src[j];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Validation.
 // ---------------------------------------------------------------------------
 
@@ -542,6 +624,42 @@ sla_status build_tiling(const int32_t* d_rp, int64_t n, MatView& view, void** ow
   return SLA_OK;
 }
 
+// Stable LSD radix sort of m non-negative keys below 2^bits, carrying the
+// element indices.  `work` holds radix_work_ints(m) ints; *idx_out points
+// into it and gives the element indices in ascending key order (equal keys
+// keep their input order).
+size_t radix_work_ints(int m) {
+  const size_t tiles = ((size_t)std::max(1, m) + kRadixTile - 1) / kRadixTile;
+  return 4 * (size_t)std::max(1, m) + (size_t)kRadixDigits * tiles;
+}
+
+sla_status radix_sort_indices(const int* keys, int m, int bits, int* work, const int** idx_out,
+                              hipStream_t s) {
+  const int passes = (bits + kRadixBits - 1) / kRadixBits;
+  const int ntiles = (m + kRadixTile - 1) / kRadixTile;
+  const size_t hist_n = (size_t)kRadixDigits * ntiles;
+  int *ka = work, *va = work + m, *kb = work + 2 * (size_t)m, *vb = work + 3 * (size_t)m;
+  int* hist = work + 4 * (size_t)m;
+  const int* kin = keys;
+  const int* vin = nullptr;
+  sla_status st = SLA_OK;
+  for (int p = 0; p < passes; ++p) {
+    const int shift = p * kRadixBits;
+    int* kout = (p & 1) ? kb : ka;
+    int* vout = (p & 1) ? vb : va;
+    hipLaunchKernelGGL(radix_hist, dim3(ntiles), dim3(kWG), 0, s, kin, m, shift, ntiles, hist);
+    SLA_HIP(hipGetLastError());
+    if ((st = exclusive_scan(hist, hist, (int)hist_n, s)) != SLA_OK) return st;
+    hipLaunchKernelGGL(radix_scatter, dim3(ntiles), dim3(kWG), 0, s, kin, vin, m, shift, ntiles,
+                       (const int*)hist, kout, vout);
+    SLA_HIP(hipGetLastError());
+    kin = kout;
+    vin = vout;
+  }
+  *idx_out = vin;
+  return SLA_OK;
+}
+
 sla_status build_transpose(const sla_mat& m, int32_t** t_rp_out, int32_t** t_ci_out, void** t_v_out,
                            hipStream_t s) {
   const int nbr = (int)m.nbr, nnzb = (int)m.nnzb, bs = m.bs;
@@ -572,28 +690,10 @@ sla_status build_transpose(const sla_mat& m, int32_t** t_rp_out, int32_t** t_ci_
   // stable radix sort of the column keys, carrying entry indices
   int bits = 1;
   while (bits < 31 && ((int64_t)1 << bits) < (int64_t)nbr) ++bits;
-  const int passes = (bits + kRadixBits - 1) / kRadixBits;
-  const int ntiles = (nnzb + kRadixTile - 1) / kRadixTile;
   int* work = nullptr;
-  const size_t hist_n = (size_t)kRadixDigits * ntiles;
-  SLA_HIP(hipMallocAsync((void**)&work, sizeof(int) * (4 * (size_t)nnzb + hist_n), s));
-  int *ka = work, *va = work + nnzb, *kb = work + 2 * (size_t)nnzb, *vb = work + 3 * (size_t)nnzb;
-  int* hist = work + 4 * (size_t)nnzb;
-  const int* kin = m.fwd.ci;
+  SLA_HIP(hipMallocAsync((void**)&work, sizeof(int) * radix_work_ints(nnzb), s));
   const int* vin = nullptr;
-  for (int p = 0; p < passes; ++p) {
-    const int shift = p * kRadixBits;
-    int* kout = (p & 1) ? kb : ka;
-    int* vout = (p & 1) ? vb : va;
-    hipLaunchKernelGGL(radix_hist, dim3(ntiles), dim3(kWG), 0, s, kin, nnzb, shift, ntiles, hist);
-    SLA_HIP(hipGetLastError());
-    if ((st = exclusive_scan(hist, hist, (int)hist_n, s)) != SLA_OK) return st;
-    hipLaunchKernelGGL(radix_scatter, dim3(ntiles), dim3(kWG), 0, s, kin, vin, nnzb, shift, ntiles,
-                       (const int*)hist, kout, vout);
-    SLA_HIP(hipGetLastError());
-    kin = kout;
-    vin = vout;
-  }
+  if ((st = radix_sort_indices(m.fwd.ci, nnzb, bits, work, &vin, s)) != SLA_OK) return st;
   if (m.dtype == SLA_F64)
     hipLaunchKernelGGL(transpose_fill<double>, dim3(grid_for(nnzb)), dim3(kWG), 0, s, m.fwd.rp,
                        (const double*)m.fwd.v, nbr, nnzb, bs, vin, t_ci, (double*)t_v);
@@ -780,6 +880,105 @@ sla_status build_bsell(MatView& view, int64_t nbr, int64_t nnzb, int32_t dtype, 
   view.nslices = nslices;
   view.sell_w = h[0];
   view.sell = true;
+  return SLA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Locality ordering (host side).
+// ---------------------------------------------------------------------------
+
+sla_status count_far_entries(const sla_mat& m, int samples, int near, int* far, hipStream_t s) {
+  *far = 0;
+  if (m.nnzb == 0 || samples <= 0) return SLA_OK;
+  int* d = nullptr;
+  SLA_HIP(hipMallocAsync((void**)&d, sizeof(int), s));
+  SLA_HIP(hipMemsetAsync(d, 0, sizeof(int), s));
+  hipLaunchKernelGGL(sample_far, dim3(grid_for(samples)), dim3(kWG), 0, s, m.fwd.rp, m.fwd.ci,
+                     (int)m.nbr, (int)m.nnzb, samples, near, d);
+  SLA_HIP(hipGetLastError());
+  SLA_HIP(hipMemcpyAsync(far, d, sizeof(int), hipMemcpyDeviceToHost, s));
+  SLA_HIP(hipFreeAsync(d, s));
+  SLA_HIP(hipStreamSynchronize(s));
+  return SLA_OK;
+}
+
+sla_status build_order(const sla_mat& m, int32_t** perm_out, int32_t** iperm_out,
+                       hipStream_t s) {
+  const int n = (int)m.nbr;
+  int32_t *perm = nullptr, *iperm = nullptr;
+  SLA_HIP(buf_alloc((void**)&perm, sizeof(int) * (size_t)std::max(1, n)));
+  *perm_out = perm;
+  SLA_HIP(buf_alloc((void**)&iperm, sizeof(int) * (size_t)std::max(1, n)));
+  *iperm_out = iperm;
+  if (n == 0) return SLA_OK;
+  int* keys = nullptr;
+  int* work = nullptr;
+  SLA_HIP(hipMallocAsync((void**)&keys, sizeof(int) * (size_t)n, s));
+  SLA_HIP(hipMallocAsync((void**)&work, sizeof(int) * radix_work_ints(n), s));
+  hipLaunchKernelGGL(order_keys, dim3(grid_for(n)), dim3(kWG), 0, s, m.fwd.rp, n, keys);
+  SLA_HIP(hipGetLastError());
+  const int* srt = nullptr;
+  sla_status st = radix_sort_indices(keys, n, kOrderKeyBits, work, &srt, s);
+  if (st != SLA_OK) return st;
+  SegStarts seg{};
+  int acc = 0;
+  for (int x = 0; x < 8; ++x) {
+    seg.start[x] = acc;
+    acc += x < n ? (n - x + 7) / 8 : 0;
+  }
+  hipLaunchKernelGGL(order_deal, dim3(grid_for(n)), dim3(kWG), 0, s, srt, n, seg, perm, iperm);
+  SLA_HIP(hipGetLastError());
+  SLA_HIP(hipFreeAsync(work, s));
+  SLA_HIP(hipFreeAsync(keys, s));
+  SLA_HIP(hipStreamSynchronize(s));
+  return SLA_OK;
+}
+
+sla_status build_permuted(const sla_mat& m, const int32_t* perm, const int32_t* iperm,
+                          int32_t** rp_out, int32_t** ci_out, void** v_out, hipStream_t s) {
+  const int n = (int)m.nbr, nnz = (int)m.nnzb;
+  const size_t es = m.dtype == SLA_F64 ? 8 : 4;
+  int32_t *rp = nullptr, *ci = nullptr;
+  void* v = nullptr;
+  SLA_HIP(buf_alloc((void**)&rp, sizeof(int) * ((size_t)n + 1)));
+  *rp_out = rp;
+  SLA_HIP(buf_alloc((void**)&ci, sizeof(int) * (size_t)std::max(1, nnz)));
+  *ci_out = ci;
+  SLA_HIP(buf_alloc(&v, es * (size_t)std::max(1, nnz)));
+  *v_out = v;
+  int* len = nullptr;
+  SLA_HIP(hipMallocAsync((void**)&len, sizeof(int) * ((size_t)n + 1), s));
+  hipLaunchKernelGGL(perm_lengths, dim3(grid_for((int64_t)n + 1)), dim3(kWG), 0, s, m.fwd.rp,
+                     perm, n, len);
+  SLA_HIP(hipGetLastError());
+  sla_status st = exclusive_scan(len, rp, n + 1, s);
+  if (st != SLA_OK) return st;
+  SLA_HIP(hipFreeAsync(len, s));
+  if (nnz > 0) {
+    if (m.dtype == SLA_F64)
+      hipLaunchKernelGGL(perm_fill<double>, dim3(grid_for(nnz)), dim3(kWG), 0, s, m.fwd.rp,
+                         m.fwd.ci, (const double*)m.fwd.v, (const int*)rp, perm, iperm, n, nnz,
+                         ci, (double*)v);
+    else
+      hipLaunchKernelGGL(perm_fill<float>, dim3(grid_for(nnz)), dim3(kWG), 0, s, m.fwd.rp,
+                         m.fwd.ci, (const float*)m.fwd.v, (const int*)rp, perm, iperm, n, nnz,
+                         ci, (float*)v);
+    SLA_HIP(hipGetLastError());
+  }
+  SLA_HIP(hipStreamSynchronize(s));
+  return SLA_OK;
+}
+
+sla_status permute_vec(const int32_t* perm, const void* src, void* dst, int64_t n, int32_t dtype,
+                       bool into, hipStream_t s) {
+  if (n == 0) return SLA_OK;
+  if (dtype == SLA_F64)
+    hipLaunchKernelGGL(permute_vec_k<double>, dim3(grid_for(n)), dim3(kWG), 0, s, perm,
+                       (const double*)src, (double*)dst, (int)n, into);
+  else
+    hipLaunchKernelGGL(permute_vec_k<float>, dim3(grid_for(n)), dim3(kWG), 0, s, perm,
+                       (const float*)src, (float*)dst, (int)n, into);
+  SLA_HIP(hipGetLastError());
   return SLA_OK;
 }
 

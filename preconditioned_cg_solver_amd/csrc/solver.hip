@@ -1697,10 +1697,15 @@ sla_status small_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b
 // Internal API used by api.cpp
 // ---------------------------------------------------------------------------
 
-size_t workspace_bytes(const sla_mat& A) {
+size_t workspace_base(const sla_mat& A) {
   const size_t es = A.dtype == SLA_F64 ? 8 : 4;
   return align_up(sizeof(SolverState)) + 3 * align_up(partial_slots(A) * sizeof(double)) +
          7 * align_up((size_t)A.n() * es);
+}
+
+size_t workspace_bytes(const sla_mat& A) {
+  const size_t es = A.dtype == SLA_F64 ? 8 : 4;
+  return workspace_base(A) + (A.ord_want ? 2 * align_up((size_t)A.n() * es) : 0);
 }
 
 sla_status spmv(const sla_mat& A, bool transpose, const void* x, void* y, hipStream_t s) {

@@ -64,7 +64,8 @@ def test_binding_has_the_same_names():
     from preconditioned_cg_solver_amd import binding
     for name in ("sla_csr_create", "sla_bsr_create", "sla_spmv", "sla_pcg_workspace_size",
                  "sla_pcg_solve", "sla_pcg_adjoint", "sla_precond_apply", "sla_pattern_grad",
-                 "sla_mat_tiling", "sla_mat_transpose_arrays", "sla_set_profiling",
+                 "sla_mat_tiling", "sla_mat_reordered", "sla_mat_transpose_arrays",
+                 "sla_set_profiling",
                  "sla_get_profile", "sla_reset_profile", "sla_status_string"):
         assert callable(getattr(binding, name))
 
