@@ -168,7 +168,8 @@ sla_status sla_mat_tiling(sla_mat_t m, int32_t transpose, int64_t *n_tiles, int6
  * memory.  That first solve is synchronous set-up work and must not overlap
  * other calls on the same handles.  The workspace of such an A holds two
  * more n-vectors (sla_pcg_workspace_size includes them).  The several-
- * right-hand-side solves do not reorder.
+ * right-hand-side solves keep A's own order: their row-per-thread products
+ * would meet the sorted long rows side by side in the same wavefronts.
  */
 sla_status sla_mat_reordered(sla_mat_t m, int32_t *reordered);
 

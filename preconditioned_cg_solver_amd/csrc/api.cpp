@@ -269,14 +269,14 @@ sla_status solve_any(sla_mat* A, sla_mat* G, double eps, const void* b, void* x,
   const size_t vb = align_up((size_t)A->n() * (A->dtype == SLA_F64 ? 8 : 4));
   void* pb = (char*)work + base;
   void* px = (char*)work + base + vb;
-  if ((st = permute_vec(A->perm, b, pb, A->n(), A->dtype, true, s)) != SLA_OK) return st;
-  if ((st = permute_vec(A->perm, nullptr, px, A->n(), A->dtype, true, s)) != SLA_OK) return st;
+  if ((st = permute_rows(A->perm, b, pb, A->n(), 1, A->dtype, true, s)) != SLA_OK) return st;
+  if ((st = permute_rows(A->perm, nullptr, px, A->n(), 1, A->dtype, true, s)) != SLA_OK) return st;
   st = sla::pcg_solve(*A->ord, *G->ord, eps, pb, px, rtol, maxit, work, base, s, info, ha, hb,
                       hl);
   if (st == SLA_ERR_HIP || st == SLA_ERR_OOM || st == SLA_ERR_INVALID_ARG ||
       st == SLA_ERR_UNSUPPORTED)
     return st;
-  sla_status pst = permute_vec(A->perm, px, x, A->n(), A->dtype, false, s);
+  sla_status pst = permute_rows(A->perm, px, x, A->n(), 1, A->dtype, false, s);
   if (pst != SLA_OK) return pst;
   hipError_t e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");

@@ -199,10 +199,10 @@ sla_status count_far_entries(const sla_mat& m, int samples, int near, int* far, 
 sla_status build_order(const sla_mat& m, int32_t** perm, int32_t** iperm, hipStream_t s);
 sla_status build_permuted(const sla_mat& m, const int32_t* perm, const int32_t* iperm,
                           int32_t** rp, int32_t** ci, void** v, hipStream_t s);
-// into: dst[j] = src[perm[j]]; otherwise dst[perm[j]] = src[j]; src == NULL
-// zeroes dst.
-sla_status permute_vec(const int32_t* perm, const void* src, void* dst, int64_t n, int32_t dtype,
-                       bool into, hipStream_t s);
+// Rows of n x cols row-major arrays.  into: dst row j = src row perm[j];
+// otherwise dst row perm[j] = src row j; src == NULL zeroes dst.
+sla_status permute_rows(const int32_t* perm, const void* src, void* dst, int64_t n, int cols,
+                        int32_t dtype, bool into, hipStream_t s);
 
 // Solver (solver.hip).  workspace_bytes = workspace_base plus, for an A the
 // solves reorder, the two permuted vectors (b and x) after it.

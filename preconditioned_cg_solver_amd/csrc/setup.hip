@@ -391,15 +391,20 @@ __global__ void perm_fill(const int* __restrict__ rp, const int* __restrict__ ci
   }
 }
 
-// dst[j] = src[perm[j]] (into the ordering) or dst[perm[j]] = src[j] (back);
-// src == nullptr writes zeros to dst[j].
+// Rows of n x cols row-major arrays: dst row j = src row perm[j] (into the
+// ordering) or dst row perm[j] = src row j (back); src == nullptr writes
+// zeros to dst.
 template <typename T>
-__global__ void permute_vec_k(const int* __restrict__ perm, const T* __restrict__ src,
-                              T* __restrict__ dst, int n, bool into) {
-  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < n; j += gridDim.x * blockDim.x) {
-    if (!src) dst[j] = T(0);
-    else if (into) dst[j] = src[perm[j]];
-    else dst[perm[j]] = src[j];
+__global__ void permute_rows_k(const int* __restrict__ perm, const T* __restrict__ src,
+                               T* __restrict__ dst, int n, int cols, bool into) {
+  const int64_t m = (int64_t)n * cols;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < m;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int j = (int)(e / cols), c = (int)(e - (int64_t)j * cols);
+    const int64_t o = (int64_t)perm[j] * cols + c;
+    if (!src) dst[e] = T(0);
+    else if (into) dst[e] = src[o];
+    else dst[o] = src[e];
   }
 }
 
@@ -969,15 +974,16 @@ sla_status build_permuted(const sla_mat& m, const int32_t* perm, const int32_t* 
   return SLA_OK;
 }
 
-sla_status permute_vec(const int32_t* perm, const void* src, void* dst, int64_t n, int32_t dtype,
-                       bool into, hipStream_t s) {
-  if (n == 0) return SLA_OK;
+sla_status permute_rows(const int32_t* perm, const void* src, void* dst, int64_t n, int cols,
+                        int32_t dtype, bool into, hipStream_t s) {
+  if (n == 0 || cols == 0) return SLA_OK;
+  const int g = grid_for(n * cols);
   if (dtype == SLA_F64)
-    hipLaunchKernelGGL(permute_vec_k<double>, dim3(grid_for(n)), dim3(kWG), 0, s, perm,
-                       (const double*)src, (double*)dst, (int)n, into);
+    hipLaunchKernelGGL(permute_rows_k<double>, dim3(g), dim3(kWG), 0, s, perm,
+                       (const double*)src, (double*)dst, (int)n, cols, into);
   else
-    hipLaunchKernelGGL(permute_vec_k<float>, dim3(grid_for(n)), dim3(kWG), 0, s, perm,
-                       (const float*)src, (float*)dst, (int)n, into);
+    hipLaunchKernelGGL(permute_rows_k<float>, dim3(g), dim3(kWG), 0, s, perm, (const float*)src,
+                       (float*)dst, (int)n, cols, into);
   SLA_HIP(hipGetLastError());
   return SLA_OK;
 }

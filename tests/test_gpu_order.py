@@ -177,3 +177,40 @@ def test_ordered_matches_unordered(monkeypatch):
     x1, i1 = B.sla_pcg_solve(A1, G1, p.eps, tdev(p.b), rtol=p.rtol, maxit=8)
     assert i0.iterations == i1.iterations == 8
     assert rel(host(x1), host(x0)) <= 1e-10
+
+
+@pytest.mark.parametrize("k", [3, 9])
+def test_multi_rhs_with_a_reordered_handle(k, ordered):
+    """The several-right-hand-side solves keep A's own order (their
+    row-per-thread products would meet the sorted long rows side by side in
+    the same wavefronts); on handles that reorder their one-column solves
+    they must still match the oracle (nine columns take two lock-step
+    passes)."""
+    p = problem("powerlaw_20k")
+    rng = np.random.default_rng(21)
+    Bm, W = rng.standard_normal((p.A.n, k)), rng.standard_normal((p.A.n, k))
+    Xr, _, it_r, _, _ = oracle.pcg_multi(p.A, p.G, p.eps, Bm, p.rtol, p.maxit)
+    lam_r, g_r, st_r, it2_r, _, _ = oracle.adjoint_multi(p.A, p.G, p.eps, Xr, W, p.rtol, p.maxit)
+    assert st_r == oracle.OK
+    A, G = handles(p)
+    assert B.sla_mat_reordered(A)
+    x1, _ = B.sla_pcg_solve(A, G, p.eps, tdev(Bm[:, 0].copy()), rtol=p.rtol, maxit=p.maxit)
+    say("multi-RHS on a reordered handle", k)
+    X, infos = B.sla_pcg_solve_multi(A, G, p.eps, tdev(Bm), rtol=p.rtol, maxit=p.maxit)
+    for c in range(k):
+        assert infos[c].status == B.OK
+        assert_solve_matches(p.A, p.G, p.eps, Bm[:, c], p.rtol, p.maxit, infos[c].iterations,
+                             host(X[:, c]), int(it_r[c]), Xr[:, c], strict=False,
+                             what=f"multi column {c}")
+    GB, gv, ainfos = B.sla_pcg_adjoint_multi(A, G, p.eps, X, tdev(W), rtol=p.rtol,
+                                             maxit=p.maxit)
+    assert all(i.status == B.OK for i in ainfos)
+    assert rel(host(GB), lam_r) <= 1e-7
+    assert rel(host(gv), g_r) <= 1e-7
+    # the summed gradient on A's own storage order, from the device's Lambda and X
+    lam, x = host(GB), host(X)
+    ri, cj = p.A.row_of_entry(), p.A.col_idx
+    g = np.zeros(p.A.nnz)
+    for c in range(k):
+        g = g - lam[ri, c] * x[cj, c]
+    assert np.array_equal(host(gv), g)
