@@ -147,8 +147,9 @@ sla_status sla_mat_transpose_arrays(sla_mat_t m, const int32_t **d_row_ptr,
 sla_status sla_mat_tiling(sla_mat_t m, int32_t transpose, int64_t *n_tiles, int64_t *n_long);
 
 /*
- * Whether one-right-hand-side solves (sla_pcg_solve, sla_pcg_solve_history,
- * sla_pcg_adjoint) with m as A run on a locality ordering: *reordered = 1 or
+ * Whether the solves (sla_pcg_solve, sla_pcg_solve_history, sla_pcg_adjoint
+ * and their several-right-hand-side forms) with m as A run on a locality
+ * ordering: *reordered = 1 or
  * 0, decided when m was created.  Such a solve applies one symmetric
  * permutation P to the whole system (P A P^T y = P b with the preconditioner
  * P G G^T P^T + eps I, which is P M^-1 P^T, so the iterates are those of the
@@ -168,8 +169,9 @@ sla_status sla_mat_tiling(sla_mat_t m, int32_t transpose, int64_t *n_tiles, int6
  * memory.  That first solve is synchronous set-up work and must not overlap
  * other calls on the same handles.  The workspace of such an A holds two
  * more n-vectors (sla_pcg_workspace_size includes them).  The several-
- * right-hand-side solves keep A's own order: their row-per-thread products
- * would meet the sorted long rows side by side in the same wavefronts.
+ * right-hand-side solves (sla_pcg_solve_multi, sla_pcg_adjoint_multi) use
+ * the same ordering, permuting the n x k blocks by rows; their workspace
+ * holds two more n x k blocks (sla_pcg_workspace_size_multi includes them).
  */
 sla_status sla_mat_reordered(sla_mat_t m, int32_t *reordered);
 

@@ -213,7 +213,7 @@ def sla_mat_tiling(A: Mat, transpose: bool = False) -> Tuple[int, int]:
 
 
 def sla_mat_reordered(A: Mat) -> bool:
-    """True when one-right-hand-side solves with A run on its locality ordering."""
+    """True when the solves with A run on its locality ordering."""
     r = ctypes.c_int32()
     _check(lib().sla_mat_reordered(A.handle, ctypes.byref(r)))
     return bool(r.value)

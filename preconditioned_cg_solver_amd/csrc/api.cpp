@@ -283,6 +283,33 @@ sla_status solve_any(sla_mat* A, sla_mat* G, double eps, const void* b, void* x,
   return st;
 }
 
+// Several right-hand sides, on A's locality ordering when it has one: the
+// n x k blocks are permuted by rows (P B in, X = P^T Y out), after the base
+// workspace.
+sla_status solve_multi_any(sla_mat* A, sla_mat* G, double eps, const void* b, void* x, int32_t k,
+                           double rtol, int32_t maxit, void* work, hipStream_t s,
+                           sla_solve_info* info, sla_status* cst) {
+  bool use = false;
+  sla_status st = ensure_order(A, G, s, &use);
+  if (st != SLA_OK) return st;
+  if (!use) return sla::pcg_solve_multi(*A, *G, eps, b, x, k, rtol, maxit, work, s, info, cst);
+  const size_t base = workspace_base_multi(*A, k);
+  const size_t vb = align_up((size_t)A->n() * (size_t)k * (A->dtype == SLA_F64 ? 8 : 4));
+  void* pb = (char*)work + base;
+  void* px = (char*)work + base + vb;
+  if ((st = permute_rows(A->perm, b, pb, A->n(), k, A->dtype, true, s)) != SLA_OK) return st;
+  if ((st = permute_rows(A->perm, nullptr, px, A->n(), k, A->dtype, true, s)) != SLA_OK) return st;
+  st = sla::pcg_solve_multi(*A->ord, *G->ord, eps, pb, px, k, rtol, maxit, work, s, info, cst);
+  if (st == SLA_ERR_HIP || st == SLA_ERR_OOM || st == SLA_ERR_INVALID_ARG ||
+      st == SLA_ERR_UNSUPPORTED)
+    return st;
+  sla_status pst = permute_rows(A->perm, px, x, A->n(), k, A->dtype, false, s);
+  if (pst != SLA_OK) return pst;
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  return st;
+}
+
 // k = 0: one right-hand side; k >= 1: the multi-RHS solver's workspace.
 sla_status check_solve(sla_mat_t A, sla_mat_t G, double eps, const void* b, const void* x,
                        double rtol, int32_t maxit, const void* work, size_t work_bytes,
@@ -557,8 +584,8 @@ sla_status sla_pcg_solve_multi(sla_mat_t A, sla_mat_t G, double eps, const void*
   }
   sla_status st = check_solve(A, G, eps, d_b, d_x, rtol, maxit, d_work, work_bytes, k);
   if (st != SLA_OK) return st;
-  return sla::pcg_solve_multi(*A, *G, eps, d_b, d_x, k, rtol, maxit, d_work, (hipStream_t)stream,
-                              info, col_status);
+  return solve_multi_any(A, G, eps, d_b, d_x, k, rtol, maxit, d_work, (hipStream_t)stream, info,
+                         col_status);
 }
 
 sla_status sla_pcg_adjoint_multi(sla_mat_t A, sla_mat_t G, double eps, const void* d_x,
@@ -577,8 +604,8 @@ sla_status sla_pcg_adjoint_multi(sla_mat_t A, sla_mat_t G, double eps, const voi
     return SLA_ERR_INVALID_ARG;
   }
   hipStream_t s = (hipStream_t)stream;
-  st = sla::pcg_solve_multi(*A, *G, eps, d_grad_x, d_grad_b, k, rtol, maxit, d_work, s, info,
-                            col_status);
+  st = solve_multi_any(A, G, eps, d_grad_x, d_grad_b, k, rtol, maxit, d_work, s, info,
+                       col_status);
   if (st < 0) return st;
   sla_status gs = sla::pattern_grad_multi(*A, d_grad_b, d_x, k, d_grad_vals, s);
   if (gs != SLA_OK) return gs;

@@ -227,7 +227,9 @@ sla_status small_solve_batch(const sla_mat& A, const sla_mat& G, double eps, con
                              void* x, int k, double rtol, int maxit, void* states,
                              hipStream_t s, sla_solve_info* info, sla_status* cst);
 
-// Several right-hand sides (multi.hip).
+// Several right-hand sides (multi.hip); the same split as workspace_bytes,
+// with the permuted blocks n x k.
+size_t workspace_base_multi(const sla_mat& A, int k);
 size_t workspace_bytes_multi(const sla_mat& A, int k);
 sla_status spmm(const sla_mat& A, bool transpose, const void* x, void* y, int k, hipStream_t s);
 sla_status pcg_solve_multi(const sla_mat& A, const sla_mat& G, double eps, const void* b, void* x,

@@ -70,6 +70,7 @@ struct MArgs {
   const int16_t* sd;
   const int32_t* soff;
   int nslices;
+  const Tile* tiles;  // CSR row tiles (tile engine)
   int ntiles;
   int nbr;
   int n;
@@ -504,14 +505,91 @@ __global__ __launch_bounds__(kWG) void mbsell_step(MArgs<T> a) {
 }
 
 // ---------------------------------------------------------------------------
-// Row engine for every other matrix (CSR without the sliced layout, BSR
-// without it): one lane per scalar row walks the row's entries in storage
-// order; CSR rows longer than a tile (kLdsCap) are taken by a whole
-// workgroup each (lanes stride over the entries, then a fixed-order
-// workgroup sum), so a hub row does not serialise on one lane.
+// Tile engine for CSR without the sliced layout: the row tiles of the
+// one-column engine (at most 256 rows and kLdsCap nonzeros, 2^lg lanes per
+// row), read straight from the CSR arrays.  The lanes of a row stride over
+// its entries with K partial sums each, summed across the row's lanes; no
+// LDS and no barrier per tile, so the wavefronts of a workgroup advance
+// independently.  Long-row chunks are skipped: rows longer than kLdsCap
+// are taken by a whole workgroup each (lanes stride over the entries, then
+// a fixed-order workgroup sum), so a hub row does not serialise.
 // ---------------------------------------------------------------------------
 
-template <typename T, int MODE, int K, int BS>
+template <typename T, int MODE, int K>
+__global__ __launch_bounds__(kWG) void mtile_step(MArgs<T> a) {
+  __shared__ double s_red[kWaves * K];
+  __shared__ int s_flag;
+  MCoef<T, K> cf;
+  if (!mprologue<T, MODE, K>(a, cf, s_red, &s_flag)) return;
+  double dot[K];
+#pragma unroll
+  for (int c = 0; c < K; ++c) dot[c] = 0.0;
+  const int tid = threadIdx.x;
+  int t0, t1, step;
+  tile_range(a.ntiles, t0, t1, step);
+  for (int t = t0; t < t1; t += step) {
+    const Tile d = a.tiles[t];
+    if (d.kind != kTileLds) continue;
+    const int nr = d.b - d.a, lg = d.c;
+    const int L = 1 << lg, g = tid >> lg, sub = tid & (L - 1);
+    const bool in = g < nr;
+    const int i = d.a + (in ? g : 0);
+    T acc[K];
+#pragma unroll
+    for (int c = 0; c < K; ++c) acc[c] = T(0);
+    if (in) {
+      const int e1 = a.rp[i + 1];
+      for (int e = a.rp[i] + sub; e < e1; e += L) {
+        const T vu = a.v[e];
+        const size_t base = (size_t)a.ci[e] * a.ld;
+#pragma unroll
+        for (int c = 0; c < K; ++c) acc[c] = fma(vu, mgat<T, MODE, K>(a, base, c, cf), acc[c]);
+      }
+    }
+    for (int off = L >> 1; off >= 1; off >>= 1) {
+#pragma unroll
+      for (int c = 0; c < K; ++c) acc[c] += __shfl_xor(acc[c], off, 64);
+    }
+    if (in && sub == 0) {
+      MOwn<T, K> o;
+      mown_load<T, MODE, K>(a, i, o);
+      mepi<T, MODE, K>(a, i, acc, cf, o, dot);
+    }
+  }
+  for (int q = blockIdx.x; q < a.nlong; q += gridDim.x) {
+    const int i = a.long_rows[q];
+    const int e0 = a.rp[i], e1 = a.rp[i + 1];
+    T acc[K];
+#pragma unroll
+    for (int c = 0; c < K; ++c) acc[c] = T(0);
+    for (int e = e0 + tid; e < e1; e += kWG) {
+      const T vu = a.v[e];
+      const size_t base = (size_t)a.ci[e] * a.ld;
+#pragma unroll
+      for (int c = 0; c < K; ++c) acc[c] = fma(vu, mgat<T, MODE, K>(a, base, c, cf), acc[c]);
+    }
+    double sum[K];
+#pragma unroll
+    for (int c = 0; c < K; ++c) sum[c] = (double)acc[c];
+    block_sum_k<K>(sum, s_red);
+    if (tid == 0) {
+      MOwn<T, K> o;
+      mown_load<T, MODE, K>(a, i, o);
+      T tot[K];
+#pragma unroll
+      for (int c = 0; c < K; ++c) tot[c] = T(sum[c]);
+      mepi<T, MODE, K>(a, i, tot, cf, o, dot);
+    }
+  }
+  mfinish<T, MODE, K>(a, dot, s_red);
+}
+
+// ---------------------------------------------------------------------------
+// Row engine for 3x3 BSR without the sliced layout: one lane per scalar
+// row walks its block row's entries in storage order.
+// ---------------------------------------------------------------------------
+
+template <typename T, int MODE, int K>
 __global__ __launch_bounds__(kWG) void mrow_step(MArgs<T> a) {
   __shared__ double s_red[kWaves * K];
   __shared__ int s_flag;
@@ -526,47 +604,19 @@ __global__ __launch_bounds__(kWG) void mrow_step(MArgs<T> a) {
     T acc[K];
 #pragma unroll
     for (int c = 0; c < K; ++c) acc[c] = T(0);
-    const int I = BS == 1 ? i : i / 3, r = BS == 1 ? 0 : i - 3 * (i / 3);
+    const int I = i / 3, r = i - 3 * I;
     const int e0 = a.rp[I], e1 = a.rp[I + 1];
-    if (BS == 1 && e1 - e0 > kLdsCap) continue;  // below
     for (int e = e0; e < e1; ++e) {
       const int J = a.ci[e];
 #pragma unroll
-      for (int q = 0; q < BS; ++q) {
-        const T vu = BS == 1 ? a.v[e] : a.v[(size_t)e * 9 + 3 * r + q];
-        const size_t base = (size_t)(BS * J + q) * a.ld;
+      for (int q = 0; q < 3; ++q) {
+        const T vu = a.v[(size_t)e * 9 + 3 * r + q];
+        const size_t base = (size_t)(3 * J + q) * a.ld;
 #pragma unroll
         for (int c = 0; c < K; ++c) acc[c] = fma(vu, mgat<T, MODE, K>(a, base, c, cf), acc[c]);
       }
     }
     mepi<T, MODE, K>(a, i, acc, cf, o, dot);
-  }
-  if constexpr (BS == 1) {
-    for (int q = blockIdx.x; q < a.nlong; q += gridDim.x) {
-      const int i = a.long_rows[q];
-      const int e0 = a.rp[i], e1 = a.rp[i + 1];
-      T acc[K];
-#pragma unroll
-      for (int c = 0; c < K; ++c) acc[c] = T(0);
-      for (int e = e0 + threadIdx.x; e < e1; e += kWG) {
-        const T vu = a.v[e];
-        const size_t base = (size_t)a.ci[e] * a.ld;
-#pragma unroll
-        for (int c = 0; c < K; ++c) acc[c] = fma(vu, mgat<T, MODE, K>(a, base, c, cf), acc[c]);
-      }
-      double sum[K];
-#pragma unroll
-      for (int c = 0; c < K; ++c) sum[c] = (double)acc[c];
-      block_sum_k<K>(sum, s_red);
-      if (threadIdx.x == 0) {
-        MOwn<T, K> o;
-        mown_load<T, MODE, K>(a, i, o);
-        T tot[K];
-#pragma unroll
-        for (int c = 0; c < K; ++c) tot[c] = T(sum[c]);
-        mepi<T, MODE, K>(a, i, tot, cf, o, dot);
-      }
-    }
   }
   mfinish<T, MODE, K>(a, dot, s_red);
 }
@@ -751,6 +801,9 @@ void fill_mat(MArgs<T>& a, const sla_mat& m, const MatView& v) {
     a.soff = v.soff;
     a.nslices = v.nslices;
     a.ntiles = (v.nslices + kWaves - 1) / kWaves;
+  } else if (m.bs == 1) {
+    a.tiles = v.tiles;
+    a.ntiles = v.ntiles;
   } else {
     a.ntiles = 0;
   }
@@ -771,9 +824,9 @@ hipError_t mlaunch(const sla_mat& m, const MatView& v, const MArgs<T>& a, int gr
     if (v.sd) hipLaunchKernelGGL((mbsell_step<T, MODE, K, true, UB>), g, b, 0, s, a);
     else hipLaunchKernelGGL((mbsell_step<T, MODE, K, false, UB>), g, b, 0, s, a);
   } else if (m.bs == 1) {
-    hipLaunchKernelGGL((mrow_step<T, MODE, K, 1>), g, b, 0, s, a);
+    hipLaunchKernelGGL((mtile_step<T, MODE, K>), g, b, 0, s, a);
   } else {
-    hipLaunchKernelGGL((mrow_step<T, MODE, K, 3>), g, b, 0, s, a);
+    hipLaunchKernelGGL((mrow_step<T, MODE, K>), g, b, 0, s, a);
   }
   return hipGetLastError();
 }
@@ -1056,12 +1109,18 @@ sla_status spmm_impl(const sla_mat& A, bool transpose, const T* x, T* y, int k, 
 
 }  // namespace
 
-size_t workspace_bytes_multi(const sla_mat& A, int k) {
+size_t workspace_base_multi(const sla_mat& A, int k) {
   const size_t es = A.dtype == SLA_F64 ? 8 : 4;
   const size_t lockstep = align_up(sizeof(MState)) +
                           3 * align_up((size_t)max_grid() * kMaxRhs * sizeof(double)) +
                           7 * align_up((size_t)A.n() * chunk_width(k) * es);
   return std::max(lockstep, small_states_bytes(k));
+}
+
+size_t workspace_bytes_multi(const sla_mat& A, int k) {
+  const size_t es = A.dtype == SLA_F64 ? 8 : 4;
+  return workspace_base_multi(A, k) +
+         (A.ord_want ? 2 * align_up((size_t)A.n() * (size_t)k * es) : 0);
 }
 
 sla_status spmm(const sla_mat& A, bool transpose, const void* x, void* y, int k, hipStream_t s) {

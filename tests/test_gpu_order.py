@@ -69,6 +69,11 @@ def test_workspace_holds_the_permuted_vectors(monkeypatch):
     monkeypatch.setenv("SLA_ORDER", "0")
     plain = B.sla_pcg_workspace_size(create(p.A))
     assert grown >= plain + 2 * 8 * p.A.n
+    monkeypatch.setenv("SLA_ORDER", "1")
+    grown_m = B.sla_pcg_workspace_size_multi(create(p.A), 3)
+    monkeypatch.setenv("SLA_ORDER", "0")
+    plain_m = B.sla_pcg_workspace_size_multi(create(p.A), 3)
+    assert grown_m >= plain_m + 2 * 8 * 3 * p.A.n
 
 
 @pytest.mark.parametrize("key", KEYS)
@@ -180,12 +185,10 @@ def test_ordered_matches_unordered(monkeypatch):
 
 
 @pytest.mark.parametrize("k", [3, 9])
-def test_multi_rhs_with_a_reordered_handle(k, ordered):
-    """The several-right-hand-side solves keep A's own order (their
-    row-per-thread products would meet the sorted long rows side by side in
-    the same wavefronts); on handles that reorder their one-column solves
-    they must still match the oracle (nine columns take two lock-step
-    passes)."""
+def test_ordered_multi_rhs(k, ordered):
+    """Several right-hand sides on the ordering (n x k blocks permuted by
+    rows; nine columns take two passes of the lock-step solver), after a
+    one-column solve has built the permuted copies."""
     p = problem("powerlaw_20k")
     rng = np.random.default_rng(21)
     Bm, W = rng.standard_normal((p.A.n, k)), rng.standard_normal((p.A.n, k))
@@ -195,13 +198,13 @@ def test_multi_rhs_with_a_reordered_handle(k, ordered):
     A, G = handles(p)
     assert B.sla_mat_reordered(A)
     x1, _ = B.sla_pcg_solve(A, G, p.eps, tdev(Bm[:, 0].copy()), rtol=p.rtol, maxit=p.maxit)
-    say("multi-RHS on a reordered handle", k)
+    say("ordered multi-RHS", k)
     X, infos = B.sla_pcg_solve_multi(A, G, p.eps, tdev(Bm), rtol=p.rtol, maxit=p.maxit)
     for c in range(k):
         assert infos[c].status == B.OK
         assert_solve_matches(p.A, p.G, p.eps, Bm[:, c], p.rtol, p.maxit, infos[c].iterations,
                              host(X[:, c]), int(it_r[c]), Xr[:, c], strict=False,
-                             what=f"multi column {c}")
+                             what=f"ordered multi column {c}")
     GB, gv, ainfos = B.sla_pcg_adjoint_multi(A, G, p.eps, X, tdev(W), rtol=p.rtol,
                                              maxit=p.maxit)
     assert all(i.status == B.OK for i in ainfos)
