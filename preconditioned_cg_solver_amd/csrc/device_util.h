@@ -1,6 +1,7 @@
 // Device helpers shared by the PCG kernels (single and several right-hand
 // sides): deterministic workgroup reductions, the XCD-aware assignment of
-// work items to workgroups, and streaming loads of matrix data.
+// work items to workgroups, streaming loads of matrix data and the staging
+// of CSR row tiles.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -97,6 +98,57 @@ template <bool NT, typename U>
 __device__ __forceinline__ U ld_stream(const U* p) {
   if constexpr (NT) return __builtin_nontemporal_load(p);
   else return *p;
+}
+
+// ---------------------------------------------------------------------------
+// CSR row tiles
+// ---------------------------------------------------------------------------
+
+// Software pipelining of the CSR row tiles, staged through LDS by the
+// kernels of one and of several right-hand sides (Args has the CSR arrays
+// rp, v, ci): the next tile's row pointers, values and columns are loaded
+// into registers (all loads of a thread in flight at once) while the
+// current tile does its gathers, then committed to LDS at the top of the
+// next round.
+constexpr int kPer = kLdsCap / kWG;
+template <typename T>
+struct TileRegs {
+  T v[kPer];
+  int c[kPer];
+  int rp, rp_last;
+};
+
+template <bool NT, typename T, typename Args>
+__device__ __forceinline__ void tile_load(const Args& a, const Tile& d, TileRegs<T>& R) {
+  const int nr = d.b - d.a, kb = d.d, ne = d.pad[0];
+  const int tid = threadIdx.x;
+  if (tid <= nr) R.rp = ld_stream<NT>(a.rp + d.a + tid);
+  if (tid == 0 && nr == kWG) R.rp_last = ld_stream<NT>(a.rp + d.a + kWG);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = tid + j * kWG;
+    if (e < ne) {
+      R.v[j] = ld_stream<NT>(a.v + kb + e);
+      R.c[j] = ld_stream<NT>(a.ci + kb + e);
+    }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void tile_commit(const Tile& d, const TileRegs<T>& R, T* s_val,
+                                            int* s_col, int* s_rp) {
+  const int nr = d.b - d.a, ne = d.pad[0];
+  const int tid = threadIdx.x;
+  if (tid <= nr) s_rp[tid] = R.rp;
+  if (tid == 0 && nr == kWG) s_rp[kWG] = R.rp_last;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = tid + j * kWG;
+    if (e < ne) {
+      s_val[e] = R.v[j];
+      s_col[e] = R.c[j];
+    }
+  }
 }
 
 }  // namespace sla

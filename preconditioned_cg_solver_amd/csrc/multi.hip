@@ -507,16 +507,21 @@ __global__ __launch_bounds__(kWG) void mbsell_step(MArgs<T> a) {
 // ---------------------------------------------------------------------------
 // Tile engine for CSR without the sliced layout: the row tiles of the
 // one-column engine (at most 256 rows and kLdsCap nonzeros, 2^lg lanes per
-// row), read straight from the CSR arrays.  The lanes of a row stride over
-// its entries with K partial sums each, summed across the row's lanes; no
-// LDS and no barrier per tile, so the wavefronts of a workgroup advance
-// independently.  Long-row chunks are skipped: rows longer than kLdsCap
-// are taken by a whole workgroup each (lanes stride over the entries, then
-// a fixed-order workgroup sum), so a hub row does not serialise.
+// row), staged through LDS with the next tile's matrix data loaded into
+// registers while the current tile gathers.  The lanes of a row stride over
+// its entries (for K <= 4 in batches of two, whose K-wide gathers are in
+// flight together) with K partial sums each, summed across the row's lanes.  Long-row chunks
+// are skipped: rows longer than kLdsCap are taken by a whole workgroup each
+// (lanes stride over the entries, then a fixed-order workgroup sum), so a
+// hub row does not serialise.
 // ---------------------------------------------------------------------------
 
-template <typename T, int MODE, int K>
-__global__ __launch_bounds__(kWG) void mtile_step(MArgs<T> a) {
+template <typename T, int MODE, int K, bool NT>
+__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4)))
+void mtile_step(MArgs<T> a) {
+  __shared__ T s_val[kLdsCap];
+  __shared__ int s_col[kLdsCap];
+  __shared__ int s_rp[kTileRows + 1];
   __shared__ double s_red[kWaves * K];
   __shared__ int s_flag;
   MCoef<T, K> cf;
@@ -527,34 +532,57 @@ __global__ __launch_bounds__(kWG) void mtile_step(MArgs<T> a) {
   const int tid = threadIdx.x;
   int t0, t1, step;
   tile_range(a.ntiles, t0, t1, step);
+  TileRegs<T> R;
+  Tile nxt;
+  if (t0 < t1) {
+    nxt = a.tiles[t0];
+    if (nxt.kind == kTileLds) tile_load<NT>(a, nxt, R);
+  }
   for (int t = t0; t < t1; t += step) {
-    const Tile d = a.tiles[t];
+    const Tile d = nxt;
+    if (d.kind == kTileLds) tile_commit(d, R, s_val, s_col, s_rp);
+    if (t + step < t1) {
+      nxt = a.tiles[t + step];
+      if (nxt.kind == kTileLds) tile_load<NT>(a, nxt, R);
+    }
     if (d.kind != kTileLds) continue;
-    const int nr = d.b - d.a, lg = d.c;
+    __syncthreads();
+    const int nr = d.b - d.a, lg = d.c, kb = d.d;
     const int L = 1 << lg, g = tid >> lg, sub = tid & (L - 1);
     const bool in = g < nr;
     const int i = d.a + (in ? g : 0);
+    MOwn<T, K> o;
+    if (in && sub == 0) mown_load<T, MODE, K>(a, i, o);
     T acc[K];
 #pragma unroll
     for (int c = 0; c < K; ++c) acc[c] = T(0);
     if (in) {
-      const int e1 = a.rp[i + 1];
-      for (int e = a.rp[i] + sub; e < e1; e += L) {
-        const T vu = a.v[e];
-        const size_t base = (size_t)a.ci[e] * a.ld;
+      // entries per batch: two for K <= 4, one for K = 8 (register budget)
+      constexpr int EB = K >= 8 ? 1 : 2;
+      const int e1 = s_rp[g + 1] - kb;
+      for (int e = s_rp[g] - kb + sub; e < e1; e += EB * L) {
+        T vb[EB], xb[EB][K];
 #pragma unroll
-        for (int c = 0; c < K; ++c) acc[c] = fma(vu, mgat<T, MODE, K>(a, base, c, cf), acc[c]);
+        for (int u = 0; u < EB; ++u) {
+          const bool ok = e + u * L < e1;
+          const int ee = ok ? e + u * L : e;
+          vb[u] = ok ? s_val[ee] : T(0);
+          const size_t base = (size_t)s_col[ee] * a.ld;
+#pragma unroll
+          for (int c = 0; c < K; ++c) xb[u][c] = mgat<T, MODE, K>(a, base, c, cf);
+        }
+#pragma unroll
+        for (int u = 0; u < EB; ++u)
+#pragma unroll
+          for (int c = 0; c < K; ++c) acc[c] = fma(vb[u], xb[u][c], acc[c]);
       }
     }
     for (int off = L >> 1; off >= 1; off >>= 1) {
 #pragma unroll
       for (int c = 0; c < K; ++c) acc[c] += __shfl_xor(acc[c], off, 64);
     }
-    if (in && sub == 0) {
-      MOwn<T, K> o;
-      mown_load<T, MODE, K>(a, i, o);
-      mepi<T, MODE, K>(a, i, acc, cf, o, dot);
-    }
+    if (in && sub == 0) mepi<T, MODE, K>(a, i, acc, cf, o, dot);
+    __syncthreads();
   }
   for (int q = blockIdx.x; q < a.nlong; q += gridDim.x) {
     const int i = a.long_rows[q];
@@ -824,7 +852,10 @@ hipError_t mlaunch(const sla_mat& m, const MatView& v, const MArgs<T>& a, int gr
     if (v.sd) hipLaunchKernelGGL((mbsell_step<T, MODE, K, true, UB>), g, b, 0, s, a);
     else hipLaunchKernelGGL((mbsell_step<T, MODE, K, false, UB>), g, b, 0, s, a);
   } else if (m.bs == 1) {
-    hipLaunchKernelGGL((mtile_step<T, MODE, K>), g, b, 0, s, a);
+    if (matrix_bytes(m) > mall_budget())
+      hipLaunchKernelGGL((mtile_step<T, MODE, K, true>), g, b, 0, s, a);
+    else
+      hipLaunchKernelGGL((mtile_step<T, MODE, K, false>), g, b, 0, s, a);
   } else {
     hipLaunchKernelGGL((mrow_step<T, MODE, K>), g, b, 0, s, a);
   }

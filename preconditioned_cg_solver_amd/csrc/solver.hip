@@ -327,51 +327,6 @@ __device__ __forceinline__ T shfl_xor_t(T v, int m) {
 #endif
 
 
-// Software pipelining of the LDS tiles: the next tile's row pointers,
-// values and columns are loaded into registers (all loads of a thread in
-// flight at once) while the current tile does its gathers, then committed to
-// LDS at the top of the next round.
-constexpr int kPer = kLdsCap / kWG;
-template <typename T>
-struct TileRegs {
-  T v[kPer];
-  int c[kPer];
-  int rp, rp_last;
-};
-
-template <bool NT, typename T>
-__device__ __forceinline__ void tile_load(const StepArgs<T>& a, const Tile& d, TileRegs<T>& R) {
-  const int nr = d.b - d.a, kb = d.d, ne = d.pad[0];
-  const int tid = threadIdx.x;
-  if (tid <= nr) R.rp = ld_stream<NT>(a.rp + d.a + tid);
-  if (tid == 0 && nr == kWG) R.rp_last = ld_stream<NT>(a.rp + d.a + kWG);
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int e = tid + j * kWG;
-    if (e < ne) {
-      R.v[j] = ld_stream<NT>(a.v + kb + e);
-      R.c[j] = ld_stream<NT>(a.ci + kb + e);
-    }
-  }
-}
-
-template <typename T>
-__device__ __forceinline__ void tile_commit(const Tile& d, const TileRegs<T>& R, T* s_val,
-                                            int* s_col, int* s_rp) {
-  const int nr = d.b - d.a, ne = d.pad[0];
-  const int tid = threadIdx.x;
-  if (tid <= nr) s_rp[tid] = R.rp;
-  if (tid == 0 && nr == kWG) s_rp[kWG] = R.rp_last;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int e = tid + j * kWG;
-    if (e < ne) {
-      s_val[e] = R.v[j];
-      s_col[e] = R.c[j];
-    }
-  }
-}
-
 // Sum of one row's entries [e0, e1) (stride L) from LDS: batches of
 // SLA_ROW_BATCH entries load their values and columns, then issue all the
 // gathers, then accumulate in entry order (the order is fixed, so results do
