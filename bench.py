@@ -89,17 +89,48 @@ def sell_layout(A):
     return slots * 100 <= A.nnz * 125
 
 
+def slice_offset_slots(M):
+    """Slots of the library's slice-offset form of SELL-64 (every 64-row slice
+    lists the distinct column offsets of its rows, at most 8, and slot j holds
+    offset j for each row), or None when the rows do not qualify: a row with
+    unsorted columns, a slice with more than 8 offsets, padding above 25 %, or
+    SLA_SELL_OFS=0."""
+    import numpy as np
+    if os.environ.get("SLA_SELL_OFS", "") == "0" or M.nnz == 0:
+        return None
+    lens = np.diff(M.row_ptr.astype(np.int64))
+    rows = np.repeat(np.arange(M.n), lens)
+    ci = M.col_idx.astype(np.int64)
+    d = ci - rows
+    if np.abs(d).max(initial=0) > 32767:
+        return None
+    same_row = rows[1:] == rows[:-1]
+    if np.any(ci[1:][same_row] <= ci[:-1][same_row]):
+        return None
+    per_slice = np.bincount(np.unique((rows // 64) * 65536 + (d + 32768)) // 65536,
+                            minlength=(M.n + 63) // 64)
+    if per_slice.max(initial=0) > 8:
+        return None
+    slots = int(per_slice.sum() * 64)
+    return (slots, len(per_slice)) if slots * 100 <= M.nnz * 125 else None
+
+
 def moved_bytes_a_step(A, n, sv=8):
-    """Bytes the fused A step physically streams with the SELL-64 layout
-    (16-bit column offsets where every |col - row| fits): values + column
-    words + slice offsets, z, p_old and x read, x, p_new and q written
-    (gathers counted once); None for matrices outside that layout."""
+    """Bytes the fused A step physically streams with the SELL-64 layout:
+    values + column words (16-bit offsets where every |col - row| fits; in the
+    slice-offset form one 4-byte offset per slot of a slice and a one-byte
+    mask per row instead) + slice starts, z, p_old and x read, x, p_new and q
+    written (gathers counted once); None for matrices outside that layout."""
     import numpy as np
     if A.block_dim != 1:
         return None
     lens = np.diff(A.row_ptr.astype(np.int64))
     if lens.max(initial=0) > 32:
         return None
+    ofs = slice_offset_slots(A)
+    if ofs is not None:
+        slots, ns = ofs
+        return slots * sv + (slots // 64) * 4 + ns * 64 + 4 * (ns + 1) + 6 * sv * n
     rows = np.repeat(np.arange(A.n), lens)
     col_bytes = 2 if np.abs(A.col_idx.astype(np.int64) - rows).max(initial=0) <= 32767 else 4
     slots, ns = sell_slots(A)

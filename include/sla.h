@@ -45,7 +45,12 @@
  *    multi-right-hand-side solves (default: separate).
  *  - SLA_SMALL=0: no one-workgroup solve for systems of at most 1024 rows.
  *  - SLA_SELL=0: no sliced (SELL-64 / BSR sliced-ELL) copies at create time;
- *    SLA_SELL16=0: absolute int32 columns in them instead of 16-bit offsets.
+ *    SLA_SELL16=0: absolute int32 columns in them instead of 16-bit offsets;
+ *    SLA_SELL_OFS=0: no slice-offset form (by default a CSR matrix whose
+ *    64-row slices each have at most 8 distinct column offsets over sorted
+ *    rows, as stencils do, stores one offset per slot of a slice and a
+ *    one-byte mask of present slots per row, and its one-right-hand-side
+ *    products read no per-entry column words).
  *  - SLA_GRID=G (G >= 8, rounded down to a multiple of 8): workgroups of the
  *    row-parallel kernels instead of the resident capacity.
  *  - SLA_MALL_BUDGET_MB (default 208) and SLA_MALL_POLICY=A|G|all|none: which

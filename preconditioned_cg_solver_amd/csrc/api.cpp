@@ -32,7 +32,9 @@ enum OwnedSlot {
   O_SELL_T = 12,  // 12, 13, 14
   O_ORD_RP = 15,  // arrays of a permuted copy (15, 16, 17)
   O_PERM = 18,
-  O_IPERM = 19
+  O_IPERM = 19,
+  O_SOFS_F = 20,  // slice offsets and row masks (20, 21; 22, 23)
+  O_SOFS_T = 22
 };
 
 std::mutex g_dev_mu;
@@ -149,7 +151,7 @@ sla_status create_common(sla_mat_t* out, int64_t nbr, int64_t nnzb, int32_t bs, 
   if (flags & SLA_VALIDATE) st = validate_structure(*m, s);
   if (st == SLA_OK && bs == 1) st = build_tiling(rp, nbr, m->fwd, &m->owned[O_TILES_F], s);
   if (st == SLA_OK && bs == 1 && sell_enabled())
-    st = build_sell(m->fwd, nbr, nnzb, dtype, &m->owned[O_SELL_F], s);
+    st = build_sell(m->fwd, nbr, nnzb, dtype, &m->owned[O_SELL_F], &m->owned[O_SOFS_F], s);
   if (st == SLA_OK && bs == 3 && sell_enabled())
     st = build_bsell(m->fwd, nbr, nnzb, dtype, &m->owned[O_SELL_F], s);
   if (st == SLA_OK) st = alloc_long_scratch(m, m->fwd, O_LPART_F, O_LCNT_F, s);
@@ -168,7 +170,7 @@ sla_status create_common(sla_mat_t* out, int64_t nbr, int64_t nnzb, int32_t bs, 
       m->tr.v = tv;
       if (bs == 1) st = build_tiling(trp, nbr, m->tr, &m->owned[O_TILES_T], s);
       if (st == SLA_OK && bs == 1 && sell_enabled())
-        st = build_sell(m->tr, nbr, nnzb, dtype, &m->owned[O_SELL_T], s);
+        st = build_sell(m->tr, nbr, nnzb, dtype, &m->owned[O_SELL_T], &m->owned[O_SOFS_T], s);
       if (st == SLA_OK && bs == 3 && sell_enabled())
         st = build_bsell(m->tr, nbr, nnzb, dtype, &m->owned[O_SELL_T], s);
       if (st == SLA_OK) st = alloc_long_scratch(m, m->tr, O_LPART_T, O_LCNT_T, s);

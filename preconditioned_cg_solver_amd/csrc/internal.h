@@ -41,6 +41,13 @@ constexpr int kSellMaxPadPct = 25;
 constexpr int kPad16 = -32768;
 // Padding slots allocated past the last slice (covers the widest batch).
 constexpr int kSellTail = 16 * kSlice;
+// Slice-offset form of SELL-64 (banded matrices with a repeating pattern,
+// e.g. stencils): every slice lists the distinct column offsets of its rows
+// (at most kOfsMax, ascending) and slot j of the slice holds offset j for
+// every row; a one-byte mask per row marks the slots the row has.  The
+// per-entry column words are then not read by the one-right-hand-side
+// products.
+constexpr int kOfsMax = 8;
 // Sliced ELLPACK for 3x3 BSR: kBSlice block rows per wavefront slice (lane
 // l = 3 i + c takes block row 21 s + i and block component c; lane 63 idles).
 // A slot (one block of each of the slice's 21 block rows) keeps kBSlotVals
@@ -136,6 +143,12 @@ struct MatView {
   int nslices = 0;
   int sell_w = 0;                // widest slice (slots per row)
   bool sell = false;
+  // Slice-offset form (CSR, null when the rows do not qualify): the column
+  // offset of slot j of slice s is so[soff[s] / 64 + j]; bit j of sm[row]
+  // is set when the row has that slot (the same slots hold the same values
+  // and int16 offsets in sv and sd, padding elsewhere).
+  const int32_t* so = nullptr;
+  const uint8_t* sm = nullptr;
 };
 
 }  // namespace sla
@@ -151,7 +164,7 @@ struct sla_mat {
   sla::MatView tr;
   // owned device memory: tiles, long-row scratch, the transpose arrays and,
   // for the copies below, the permuted arrays and the permutation
-  void* owned[20] = {};
+  void* owned[24] = {};
   // Locality ordering used by the solves with this handle as A (decided at
   // creation, built at the first solve): perm maps a row of P A P^T to A's
   // row, iperm the other way; ord is P A P^T, or for a G handle P G P^T of
@@ -192,7 +205,7 @@ sla_status build_transpose(const sla_mat& m, int32_t** t_rp, int32_t** t_ci, voi
                            hipStream_t s);
 sla_status validate_structure(const sla_mat& m, hipStream_t s);
 sla_status build_sell(MatView& view, int64_t n, int64_t nnz, int32_t dtype, void** owned3,
-                      hipStream_t s);
+                      void** owned_ofs2, hipStream_t s);
 sla_status build_bsell(MatView& view, int64_t nbr, int64_t nnzb, int32_t dtype, void** owned3,
                        hipStream_t s);
 sla_status count_far_entries(const sla_mat& m, int samples, int near, int* far, hipStream_t s);

@@ -17,6 +17,7 @@
 
 #include <algorithm>
 #include <cstdio>
+#include <climits>
 #include <cstdlib>
 #include <vector>
 
@@ -504,6 +505,74 @@ __global__ void sell_fill(const int* __restrict__ rp, const int* __restrict__ ci
   }
 }
 
+// ---- slice-offset form ----
+
+// Per slice (one wavefront, lane = row): the ascending union of the column
+// offsets (col - row) of its rows, by repeated wavefront minima over each
+// row's next offset.  count[s] = size of the union, or kOfsMax + 1 when it
+// is larger or a row does not list its columns in increasing order.
+__global__ __launch_bounds__(kWG) void slice_union(const int* __restrict__ rp,
+                                                   const int* __restrict__ ci, int n, int nslices,
+                                                   int* __restrict__ count,
+                                                   int* __restrict__ ofs) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  for (int sl = blockIdx.x * kWaves + wv; sl < nslices; sl += gridDim.x * kWaves) {
+    const int i = sl * kSlice + lane;
+    int k = i < n ? rp[i] : 0;
+    const int ke = i < n ? rp[i + 1] : 0;
+    int prev = INT_MIN, cnt = 0;
+    bool bad = false;
+    while (cnt <= kOfsMax) {
+      const int cur = k < ke ? ci[k] - i : INT_MAX;
+      if (k < ke && cur <= prev) bad = true;
+      int m = cur;
+      for (int off = 32; off >= 1; off >>= 1) m = min(m, __shfl_xor(m, off, 64));
+      if (m == INT_MAX) break;
+      if (cnt < kOfsMax && lane == 0) ofs[(size_t)sl * kOfsMax + cnt] = m;
+      ++cnt;
+      if (cur == m) {
+        prev = cur;
+        ++k;
+      }
+    }
+    bad = __any(bad);
+    if (lane == 0) count[sl] = bad ? kOfsMax + 1 : cnt;
+  }
+}
+
+// Fill of the slice-offset form: row i of slice s puts its entry at offset
+// ofs[s][j] into slot j (rows list their columns in increasing order, so a
+// merge walk finds them); missing slots get value 0 and kPad16.
+template <typename T>
+__global__ void sell_fill_ofs(const int* __restrict__ rp, const int* __restrict__ ci,
+                              const T* __restrict__ v, int n, int nslices,
+                              const int* __restrict__ soff, const int* __restrict__ ofs,
+                              T* __restrict__ sv, short* __restrict__ sd, int* __restrict__ so,
+                              uint8_t* __restrict__ sm) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;  // row (padded to slices)
+  if (i >= nslices * kSlice) return;
+  const int sl = i / kSlice, lane = i % kSlice;
+  const int off = soff[sl], w = (soff[sl + 1] - off) / kSlice;
+  int k = i < n ? rp[i] : 0;
+  const int ke = i < n ? rp[i + 1] : 0;
+  unsigned mask = 0;
+  for (int j = 0; j < w; ++j) {
+    const int o = ofs[(size_t)sl * kOfsMax + j];
+    const int dst = off + j * kSlice + lane;
+    if (k < ke && ci[k] - i == o) {
+      sv[dst] = v[k];
+      sd[dst] = (short)o;
+      mask |= 1u << j;
+      ++k;
+    } else {
+      sv[dst] = T(0);
+      sd[dst] = (short)kPad16;
+    }
+    if (lane == 0) so[off / kSlice + j] = o;
+  }
+  sm[i] = (uint8_t)mask;
+}
+
 // ---- sliced ELLPACK for 3x3 BSR ----
 
 // Per slice: slots (widest block row); global: widest block row and largest
@@ -735,8 +804,93 @@ sla_status validate_structure(const sla_mat& m, hipStream_t s) {
   return SLA_OK;
 }
 
+// Slice-offset form of a SELL-64 matrix whose int16 offsets fit: built when
+// every slice has at most kOfsMax distinct offsets over rows with sorted
+// columns and the padding stays within kSellMaxPadPct (SLA_SELL_OFS=0: never).
+// Returns SLA_OK with view.so == nullptr when the rows do not qualify.
+sla_status build_sell_ofs(MatView& view, int64_t n, int64_t nnz, int32_t dtype, void** owned3,
+                          void** owned_ofs2, hipStream_t s) {
+  const char* e = getenv("SLA_SELL_OFS");
+  if (e && e[0] == '0') return SLA_OK;
+  const int nslices = (int)((n + kSlice - 1) / kSlice);
+  int* cnt = nullptr;
+  int* ofs = nullptr;
+  SLA_HIP(hipMallocAsync((void**)&cnt, sizeof(int) * ((size_t)nslices + 1), s));
+  SLA_HIP(hipMallocAsync((void**)&ofs, sizeof(int) * (size_t)nslices * kOfsMax, s));
+  hipLaunchKernelGGL(slice_union, dim3(std::min(1024, (nslices + kWaves - 1) / kWaves)),
+                     dim3(kWG), 0, s, view.rp, view.ci, (int)n, nslices, cnt, ofs);
+  SLA_HIP(hipGetLastError());
+  std::vector<int> hc((size_t)nslices + 1, 0);
+  SLA_HIP(hipMemcpyAsync(hc.data(), cnt, sizeof(int) * (size_t)nslices, hipMemcpyDeviceToHost, s));
+  SLA_HIP(hipStreamSynchronize(s));
+  int64_t total = 0;
+  int wmax = 0;
+  bool ok = true;
+  for (int sl = 0; sl < nslices && ok; ++sl) {
+    ok = hc[sl] <= kOfsMax;
+    wmax = std::max(wmax, hc[sl]);
+    total += (int64_t)hc[sl] * kSlice;
+    hc[sl] *= kSlice;
+  }
+  if (!ok || total * 100 > nnz * (100 + kSellMaxPadPct)) {
+    SLA_HIP(hipFreeAsync(ofs, s));
+    SLA_HIP(hipFreeAsync(cnt, s));
+    SLA_HIP(hipStreamSynchronize(s));
+    return SLA_OK;
+  }
+  hc[nslices] = 0;
+  SLA_HIP(hipMemcpyAsync(cnt, hc.data(), sizeof(int) * ((size_t)nslices + 1),
+                         hipMemcpyHostToDevice, s));
+  // the slice offsets of the row-order layout (same size) are rewritten
+  int* soff = (int*)owned3[2];
+  sla_status st = exclusive_scan(cnt, soff, nslices + 1, s);
+  if (st != SLA_OK) return st;
+  const size_t es = dtype == SLA_F64 ? 8 : 4;
+  const size_t alloc = (size_t)total + kSellTail;
+  const size_t nslot = alloc / kSlice;
+  void* sv = nullptr;
+  void* sd = nullptr;
+  void* so = nullptr;
+  void* sm = nullptr;
+  SLA_HIP(buf_alloc(&sv, es * alloc));
+  owned3[0] = sv;
+  SLA_HIP(buf_alloc(&sd, 2 * alloc));
+  owned3[1] = sd;
+  SLA_HIP(buf_alloc(&so, sizeof(int) * nslot));
+  owned_ofs2[0] = so;
+  SLA_HIP(buf_alloc(&sm, (size_t)nslices * kSlice));
+  owned_ofs2[1] = sm;
+  SLA_HIP(hipMemsetAsync((char*)sv + es * (size_t)total, 0, es * kSellTail, s));
+  SLA_HIP(hipMemsetD16Async((hipDeviceptr_t)((short*)sd + total), (unsigned short)kPad16,
+                            kSellTail, s));
+  SLA_HIP(hipMemsetAsync(so, 0, sizeof(int) * nslot, s));
+  const int rows = nslices * kSlice;
+  const dim3 g((rows + 255) / 256), b(256);
+  if (dtype == SLA_F64)
+    hipLaunchKernelGGL(sell_fill_ofs<double>, g, b, 0, s, view.rp, view.ci,
+                       (const double*)view.v, (int)n, nslices, (const int*)soff,
+                       (const int*)ofs, (double*)sv, (short*)sd, (int*)so, (uint8_t*)sm);
+  else
+    hipLaunchKernelGGL(sell_fill_ofs<float>, g, b, 0, s, view.rp, view.ci,
+                       (const float*)view.v, (int)n, nslices, (const int*)soff,
+                       (const int*)ofs, (float*)sv, (short*)sd, (int*)so, (uint8_t*)sm);
+  SLA_HIP(hipGetLastError());
+  SLA_HIP(hipFreeAsync(ofs, s));
+  SLA_HIP(hipFreeAsync(cnt, s));
+  view.sv = sv;
+  view.sc = nullptr;
+  view.sd = (const int16_t*)sd;
+  view.soff = soff;
+  view.nslices = nslices;
+  view.sell_w = wmax;
+  view.so = (const int32_t*)so;
+  view.sm = (const uint8_t*)sm;
+  view.sell = true;
+  return SLA_OK;
+}
+
 sla_status build_sell(MatView& view, int64_t n, int64_t nnz, int32_t dtype, void** owned3,
-                      hipStream_t s) {
+                      void** owned_ofs2, hipStream_t s) {
   view.sell = false;
   if (n == 0 || nnz == 0) return SLA_OK;
   const int nslices = (int)((n + kSlice - 1) / kSlice);
@@ -765,6 +919,13 @@ sla_status build_sell(MatView& view, int64_t n, int64_t nnz, int32_t dtype, void
   const size_t es = dtype == SLA_F64 ? 8 : 4;
   const char* e16 = getenv("SLA_SELL16");
   const bool rel16 = h[2] <= 32767 && !(e16 && e16[0] == '0');
+  if (rel16) {
+    st = build_sell_ofs(view, n, nnz, dtype, owned3, owned_ofs2, s);
+    if (st != SLA_OK || view.sell) {
+      if (st == SLA_OK) SLA_HIP(hipStreamSynchronize(s));
+      return st;
+    }
+  }
   void* sv = nullptr;
   void* sc = nullptr;
   // kSellTail padding slots past the last slice let the products load whole

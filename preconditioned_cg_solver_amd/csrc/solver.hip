@@ -77,6 +77,8 @@ struct StepArgs {
   const int32_t* soff;
   int nslices;
   int sell_w;            // widest slice (slots per row)
+  const int32_t* so;     // slice-offset form: offset of each slot (null: per-entry words)
+  const uint8_t* sm;     // slice-offset form: slots present in each row
   double* long_part;
   int* long_cnt;
   const T* in0;   // gathered vector (PLAIN: x, A: z, GT0: b, GT: r_{k-1}, G: t)
@@ -487,27 +489,31 @@ __device__ __forceinline__ int sell_decode(int raw, int row, bool in) {
 
 // One batch of U slots starting at slot j of a slice: value, column and
 // gathered entry (0 for padding) for every slot.
-template <typename T, int MODE, bool NT, bool I16, int U>
+// OFS: slice-offset form, the slot's offset from the per-slot table and
+// the row's mask of present slots (`mask`).
+template <typename T, int MODE, bool NT, bool I16, int U, bool OFS>
 __device__ __forceinline__ void sell_batch(const StepArgs<T>& a, int off, int lane, int row,
-                                           int j, int w, const Coef<T>& cf, T (&v)[U],
-                                           T (&x)[U]) {
+                                           int j, int w, int mask, const Coef<T>& cf,
+                                           T (&v)[U], T (&x)[U]) {
   int raw[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int idx = off + (j + u) * kSlice + lane;
     v[u] = ld_stream<NT>(a.sv + idx);
-    raw[u] = sell_raw<NT, I16>(a, idx);
+    if constexpr (OFS) raw[u] = ld_stream<NT>(a.so + off / kSlice + j + u);
+    else raw[u] = sell_raw<NT, I16>(a, idx);
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int c = sell_decode<I16>(raw[u], row, j + u < w);
+    const int c = OFS ? (((mask >> (j + u)) & 1) ? row + raw[u] : -1)
+                      : sell_decode<I16>(raw[u], row, j + u < w);
     const T g = gat<T, MODE>(a, c >= 0 ? c : 0, cf);
     x[u] = c >= 0 ? g : T(0);
     if (c < 0) v[u] = T(0);
   }
 }
 
-template <typename T, int MODE, bool NT, bool I16, int U>
+template <typename T, int MODE, bool NT, bool I16, int U, bool OFS>
 __global__ __launch_bounds__(kWG) void sell_step(StepArgs<T> a) {
   __shared__ double s_red[kWaves];
   __shared__ int s_flag;
@@ -519,19 +525,22 @@ __global__ __launch_bounds__(kWG) void sell_step(StepArgs<T> a) {
   // slice, while the prologue sums the partials).
   T hv[U];
   int hr[U];
-  int hoff = 0, hw = 0;
+  int hoff = 0, hw = 0, hm = 0;
   auto load_head = [&](int sl) {
     hoff = 0;
     hw = 0;
+    hm = 0;
     if (sl < a.nslices) {
       hoff = a.soff[sl];
       hw = (a.soff[sl + 1] - hoff) / kSlice;
+      if constexpr (OFS) hm = ld_stream<NT>(a.sm + sl * kSlice + lane);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int idx = hoff + u * kSlice + lane;
       hv[u] = ld_stream<NT>(a.sv + idx);
-      hr[u] = sell_raw<NT, I16>(a, idx);
+      if constexpr (OFS) hr[u] = ld_stream<NT>(a.so + hoff / kSlice + u);
+      else hr[u] = sell_raw<NT, I16>(a, idx);
     }
   };
   if (t0 < t1) load_head(t0 * kWaves + wv);
@@ -540,7 +549,7 @@ __global__ __launch_bounds__(kWG) void sell_step(StepArgs<T> a) {
   double dot = 0.0;
   for (int t = t0; t < t1; t += step) {
     const int sl = t * kWaves + wv;
-    const int off = hoff, w = hw;
+    const int off = hoff, w = hw, m = hm;
     T cv[U];
     int cr[U];
 #pragma unroll
@@ -555,7 +564,7 @@ __global__ __launch_bounds__(kWG) void sell_step(StepArgs<T> a) {
     T xx[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int c = sell_decode<I16>(cr[u], row, u < w);
+      const int c = OFS ? (((m >> u) & 1) ? row + cr[u] : -1) : sell_decode<I16>(cr[u], row, u < w);
       const T g = gat<T, MODE>(a, c >= 0 ? c : 0, cf);
       xx[u] = c >= 0 ? g : T(0);
       if (c < 0) cv[u] = T(0);
@@ -566,7 +575,7 @@ __global__ __launch_bounds__(kWG) void sell_step(StepArgs<T> a) {
     for (int u = 0; u < U; ++u) acc = fma(cv[u], xx[u], acc);
     for (int j = U; j < w; j += U) {
       T vv[U], yy[U];
-      sell_batch<T, MODE, NT, I16, U>(a, off, lane, row, j, w, cf, vv, yy);
+      sell_batch<T, MODE, NT, I16, U, OFS>(a, off, lane, row, j, w, m, cf, vv, yy);
 #pragma unroll
       for (int u = 0; u < U; ++u) acc = fma(vv[u], yy[u], acc);
     }
@@ -1140,6 +1149,8 @@ void fill_matrix(StepArgs<T>& a, const sla_mat& m, const MatView& v, double* lon
     a.soff = v.soff;
     a.nslices = v.nslices;
     a.sell_w = v.sell_w;
+    a.so = v.so;
+    a.sm = v.sm;
   }
   a.nbr = (int)m.nbr;
   a.long_part = long_part;
@@ -1153,16 +1164,21 @@ hipError_t launch_step(const sla_mat& m, const StepArgs<T>& a, int grid, hipStre
     // batch of slots per load round: the slice width rounded up to 4 or 8
     const bool wide = a.sell_w > 4;
     const dim3 g(grid), b(kWG);
-    if (a.sd) {
-      if (nt && wide) hipLaunchKernelGGL((sell_step<T, MODE, true, true, 8>), g, b, 0, s, a);
-      else if (nt) hipLaunchKernelGGL((sell_step<T, MODE, true, true, 4>), g, b, 0, s, a);
-      else if (wide) hipLaunchKernelGGL((sell_step<T, MODE, false, true, 8>), g, b, 0, s, a);
-      else hipLaunchKernelGGL((sell_step<T, MODE, false, true, 4>), g, b, 0, s, a);
+    if (a.so) {
+      if (nt && wide) hipLaunchKernelGGL((sell_step<T, MODE, true, true, 8, true>), g, b, 0, s, a);
+      else if (nt) hipLaunchKernelGGL((sell_step<T, MODE, true, true, 4, true>), g, b, 0, s, a);
+      else if (wide) hipLaunchKernelGGL((sell_step<T, MODE, false, true, 8, true>), g, b, 0, s, a);
+      else hipLaunchKernelGGL((sell_step<T, MODE, false, true, 4, true>), g, b, 0, s, a);
+    } else if (a.sd) {
+      if (nt && wide) hipLaunchKernelGGL((sell_step<T, MODE, true, true, 8, false>), g, b, 0, s, a);
+      else if (nt) hipLaunchKernelGGL((sell_step<T, MODE, true, true, 4, false>), g, b, 0, s, a);
+      else if (wide) hipLaunchKernelGGL((sell_step<T, MODE, false, true, 8, false>), g, b, 0, s, a);
+      else hipLaunchKernelGGL((sell_step<T, MODE, false, true, 4, false>), g, b, 0, s, a);
     } else {
-      if (nt && wide) hipLaunchKernelGGL((sell_step<T, MODE, true, false, 8>), g, b, 0, s, a);
-      else if (nt) hipLaunchKernelGGL((sell_step<T, MODE, true, false, 4>), g, b, 0, s, a);
-      else if (wide) hipLaunchKernelGGL((sell_step<T, MODE, false, false, 8>), g, b, 0, s, a);
-      else hipLaunchKernelGGL((sell_step<T, MODE, false, false, 4>), g, b, 0, s, a);
+      if (nt && wide) hipLaunchKernelGGL((sell_step<T, MODE, true, false, 8, false>), g, b, 0, s, a);
+      else if (nt) hipLaunchKernelGGL((sell_step<T, MODE, true, false, 4, false>), g, b, 0, s, a);
+      else if (wide) hipLaunchKernelGGL((sell_step<T, MODE, false, false, 8, false>), g, b, 0, s, a);
+      else hipLaunchKernelGGL((sell_step<T, MODE, false, false, 4, false>), g, b, 0, s, a);
     }
   } else if (m.bs == 1) {
     if (nt) hipLaunchKernelGGL((csr_step<T, MODE, true>), dim3(grid), dim3(kWG), 0, s, a);

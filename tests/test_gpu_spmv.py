@@ -291,3 +291,40 @@ def test_handle_buffers_reused_across_sizes():
         Mt = I.SparseMatrix(M.n_block_rows, M.block_dim, trp, tci, tv)
         assert rel(host(yt), oracle.spmv(Mt, x)) <= 1e-13
         h.destroy()
+
+
+def unsorted_rows(m=24):
+    """2D 5-point stencil on m^2 whose rows 100..163 list their columns in
+    reverse: the slice-offset form needs sorted rows, so that slice (and the
+    matrix) keeps the per-entry offsets."""
+    A = I.poisson2d(m)
+    ci, v = A.col_idx.copy(), A.vals.copy()
+    for i in range(100, 164):
+        a, b = A.row_ptr[i], A.row_ptr[i + 1]
+        ci[a:b], v[a:b] = ci[a:b][::-1].copy(), v[a:b][::-1].copy()
+    return I.SparseMatrix(A.n, 1, A.row_ptr, ci, v)
+
+
+@pytest.mark.parametrize("name", ["poisson2d_37_ragged", "poisson3d_13_ragged", "c1_heat2d_512",
+                                  "c2_poisson3d_128", "empty_rows", "unsorted_rows"])
+def test_slice_offset_form(name, monkeypatch):
+    """The slice-offset form of SELL-64 (one offset per slot of a slice, a
+    mask of present slots per row) gives the same products, bit for bit, as
+    the per-entry int16 offsets: every row adds its entries in the same
+    order, the moved padding adding exact zeros.  Also through the explicit
+    transpose, and for rows that do not qualify (unsorted columns)."""
+    M = unsorted_rows() if name == "unsorted_rows" else MATRICES[name]()
+    x = I.spmv_test_vector(2, M.n)
+    monkeypatch.setenv("SLA_SMALL", "0")
+    check = name != "unsorted_rows"   # validation requires sorted columns
+    monkeypatch.setenv("SLA_SELL_OFS", "0")
+    A0 = create(M, transpose=True, validate=check)
+    monkeypatch.delenv("SLA_SELL_OFS")
+    A1 = create(M, transpose=True, validate=check)
+    say("slice-offset form", name)
+    y0, y1 = B.sla_spmv(A0, tdev(x)), B.sla_spmv(A1, tdev(x))
+    t0 = B.sla_spmv(A0, tdev(x), transpose=True)
+    t1 = B.sla_spmv(A1, tdev(x), transpose=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(t0, t1)
+    assert rel(host(y1), oracle.spmv(M, x)) <= 1e-13
