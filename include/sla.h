@@ -53,9 +53,13 @@
  *    products read no per-entry column words).
  *  - SLA_GRID=G (G >= 8, rounded down to a multiple of 8): workgroups of the
  *    row-parallel kernels instead of the resident capacity.
- *  - SLA_MALL_BUDGET_MB (default 208) and SLA_MALL_POLICY=A|G|all|none: which
- *    operator a solve keeps resident in the 256 MB Infinity Cache (default: A
- *    when it fits the budget, otherwise none; the rest stream non-temporally).
+ *  - SLA_MALL_BUDGET_MB (default 208) and SLA_MALL_POLICY=A|G|AG|AT|all|none:
+ *    which operators a solve keeps resident in the 256 MB Infinity Cache
+ *    (G = G and G^T, AG = A and G, AT = A and G^T).  Default: all three when
+ *    they fit the budget with eight vectors; else G and G^T when the bytes
+ *    their products stream are at least A's and fit 240 MB beside six
+ *    vectors; else A when it fits the budget; else none.  The rest stream
+ *    non-temporally.
  *  - SLA_BATCH_ITERS (default 16, 1..4096): iterations enqueued between two
  *    host polls of the device exit flag.
  *  - SLA_ORDER=0|1: locality ordering of the solves off, or on for every CSR

@@ -113,6 +113,18 @@ size_t matrix_bytes(const sla_mat& m) {
   const size_t es = m.dtype == SLA_F64 ? 8 : 4;
   return (size_t)m.nnz() * es + (size_t)m.nnzb * 4 + (size_t)(m.nbr + 1) * 4;
 }
+
+// Bytes one one-right-hand-side product streams from the matrix side of a
+// CSR orientation: the SELL-64 copy in the form the products read (values
+// and per-entry column words, or values, one offset per slot and one mask
+// byte per row in the slice-offset form), else the CSR arrays.
+size_t stream_bytes(const sla_mat& m, const MatView& v) {
+  const size_t es = m.dtype == SLA_F64 ? 8 : 4;
+  if (m.bs != 1 || !v.sell) return matrix_bytes(m);
+  const size_t slots = (size_t)v.sell_slots, ns = (size_t)v.nslices;
+  const size_t cols = v.so ? slots / 16 + ns * 64 : slots * (v.sd ? 2 : 4);
+  return slots * es + cols + 4 * (ns + 1);
+}
 size_t mall_budget() {
   static size_t b = [] {
     const char* e = getenv("SLA_MALL_BUDGET_MB");

@@ -48,6 +48,8 @@ constexpr int kSellTail = 16 * kSlice;
 // per-entry column words are then not read by the one-right-hand-side
 // products.
 constexpr int kOfsMax = 8;
+// Capacity of the MI355X last-level Infinity Cache (MALL).
+constexpr size_t kMallBytes = (size_t)256 << 20;
 // Sliced ELLPACK for 3x3 BSR: kBSlice block rows per wavefront slice (lane
 // l = 3 i + c takes block row 21 s + i and block component c; lane 63 idles).
 // A slot (one block of each of the slice's 21 block rows) keeps kBSlotVals
@@ -142,6 +144,7 @@ struct MatView {
   const int32_t* soff = nullptr;
   int nslices = 0;
   int sell_w = 0;                // widest slice (slots per row)
+  int64_t sell_slots = 0;        // stored slots (x 64 values; BSR: block slots)
   bool sell = false;
   // Slice-offset form (CSR, null when the rows do not qualify): the column
   // offset of slot j of slice s is so[soff[s] / 64 + j]; bit j of sm[row]
@@ -261,6 +264,7 @@ int max_grid();
 int step_grid(int ntiles);
 int view_tiles(const sla_mat& m, const MatView& v);
 size_t matrix_bytes(const sla_mat& m);
+size_t stream_bytes(const sla_mat& m, const MatView& v);
 size_t mall_budget();
 hipEvent_t timing_event();
 int batch_iters();

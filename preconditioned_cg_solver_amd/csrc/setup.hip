@@ -885,6 +885,7 @@ sla_status build_sell_ofs(MatView& view, int64_t n, int64_t nnz, int32_t dtype, 
   view.sell_w = wmax;
   view.so = (const int32_t*)so;
   view.sm = (const uint8_t*)sm;
+  view.sell_slots = total;
   view.sell = true;
   return SLA_OK;
 }
@@ -966,6 +967,7 @@ sla_status build_sell(MatView& view, int64_t n, int64_t nnz, int32_t dtype, void
   view.soff = soff;
   view.nslices = nslices;
   view.sell_w = h[0];
+  view.sell_slots = total;
   view.sell = true;
   return SLA_OK;
 }

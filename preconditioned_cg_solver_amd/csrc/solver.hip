@@ -1214,7 +1214,7 @@ hipError_t launch_step(const sla_mat& m, const StepArgs<T>& a, int grid, hipStre
 // nothing resident; the remaining operators are streamed non-temporally.
 // When everything fits, nothing is streamed non-temporally.
 struct MallPlan {
-  bool nt_a, nt_g;
+  bool nt_a, nt_g, nt_t;  // A, G and G^T streams non-temporal
 };
 MallPlan mall_plan(const sla_mat& A, const sla_mat& G) {
   const size_t a = matrix_bytes(A), g = matrix_bytes(G);
@@ -1222,14 +1222,23 @@ MallPlan mall_plan(const sla_mat& A, const sla_mat& G) {
   const size_t budget = mall_budget();
   const char* pol = getenv("SLA_MALL_POLICY");
   if (pol) {
-    if (!strcmp(pol, "none")) return {true, true};
-    if (!strcmp(pol, "all")) return {false, false};
-    if (!strcmp(pol, "A")) return {false, true};
-    if (!strcmp(pol, "G")) return {true, false};
+    if (!strcmp(pol, "none")) return {true, true, true};
+    if (!strcmp(pol, "all")) return {false, false, false};
+    if (!strcmp(pol, "A")) return {false, true, true};
+    if (!strcmp(pol, "G")) return {true, false, false};
+    if (!strcmp(pol, "AG")) return {false, false, true};
+    if (!strcmp(pol, "AT")) return {false, true, false};
   }
-  if (a + 2 * g + vecs <= budget) return {false, false};
-  if (a <= budget) return {false, true};
-  return {true, true};
+  if (a + 2 * g + vecs <= budget) return {false, false, false};
+  // G and G^T rather than A when their streams are the larger share and fit
+  // the 256 MB Infinity Cache beside the six vectors an iteration touches
+  // (16 MB left for partials, solver state and the rest)
+  const size_t sa = stream_bytes(A, A.fwd), sg = stream_bytes(G, G.fwd) + stream_bytes(G, G.tr);
+  const size_t live = 6 * (size_t)A.n() * (A.dtype == SLA_F64 ? 8 : 4);
+  if (A.bs == 1 && sg >= sa && sg + live <= kMallBytes - ((size_t)16 << 20))
+    return {true, false, false};
+  if (a <= budget) return {false, true, true};
+  return {true, true, true};
 }
 
 // Long-row scratch of a handle orientation lives in the handle (owned[]);
@@ -1499,7 +1508,7 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
   aT.own = R[0];
   aT.pout = w.prr;
   hipEvent_t e0 = rec.begin(1, 0);
-  SLA_HIP((launch_step<T, M_GT0>(G, aT, grid, s, plan.nt_g)));
+  SLA_HIP((launch_step<T, M_GT0>(G, aT, grid, s, plan.nt_t)));
   rec.end(e0, 1, 0);
   if (!fused) aT.pout = nullptr;
   aG.k = 0;
@@ -1536,7 +1545,7 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
           aT.in0 = R[(kk - 1) & 1];
           aT.own = R[kk & 1];
           hipEvent_t et = rec.begin(1, kk);
-          SLA_HIP((launch_step<T, M_GT>(G, aT, grid, s, plan.nt_g)));
+          SLA_HIP((launch_step<T, M_GT>(G, aT, grid, s, plan.nt_t)));
           rec.end(et, 1, kk);
         } else {
           // p and x update, q = A p, r update, t = G^T r: single gathers
@@ -1561,7 +1570,7 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
           aT.k = kk;
           aT.in0 = R[kk & 1];
           hipEvent_t et = rec.begin(1, kk);
-          SLA_HIP((launch_step<T, M_GTU>(G, aT, grid, s, plan.nt_g)));
+          SLA_HIP((launch_step<T, M_GTU>(G, aT, grid, s, plan.nt_t)));
           rec.end(et, 1, kk);
           aG.npin = grid;  // rr partials now come from vec_r_update
         }
