@@ -70,6 +70,8 @@ struct MArgs {
   const int16_t* sd;
   const int32_t* soff;
   int nslices;
+  const int32_t* so;  // slice-offset form: offset of each slot (null: per-entry words)
+  const uint8_t* sm;  // slice-offset form: slots present in each row
   const Tile* tiles;  // CSR row tiles (tile engine)
   int ntiles;
   int nbr;
@@ -315,19 +317,22 @@ __device__ __forceinline__ void mfinish(const MArgs<T>& a, double (&dot)[K], dou
 
 // One batch of U slots of a slice: values and decoded columns (-1 for
 // padding).  Loads past the slice end stay inside the arrays' padding tail.
-template <typename T, bool I16, int U>
+// OFS: the slice-offset form, one offset per slot instead of a column word
+// per entry.
+template <typename T, bool I16, int U, bool OFS>
 __device__ __forceinline__ void msell_batch(const MArgs<T>& a, int off, int lane, int j,
                                             T (&v)[U], int (&raw)[U]) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int idx = off + (j + u) * kSlice + lane;
     v[u] = ld_stream<true>(a.sv + idx);
-    if constexpr (I16) raw[u] = ld_stream<true>(a.sd + idx);
+    if constexpr (OFS) raw[u] = ld_stream<true>(a.so + off / kSlice + j + u);
+    else if constexpr (I16) raw[u] = ld_stream<true>(a.sd + idx);
     else raw[u] = ld_stream<true>(a.sc + idx);
   }
 }
 
-template <typename T, int MODE, int K, bool I16, int U>
+template <typename T, int MODE, int K, bool I16, int U, bool OFS>
 __global__ __launch_bounds__(kWG) void msell_step(MArgs<T> a) {
   __shared__ double s_red[kWaves * K];
   __shared__ int s_flag;
@@ -354,7 +359,7 @@ __global__ __launch_bounds__(kWG) void msell_step(MArgs<T> a) {
   }
   T cv[U];
   int cr[U];
-  if (w >= 0) msell_batch<T, I16, U>(a, off, lane, 0, cv, cr);
+  if (w >= 0) msell_batch<T, I16, U, OFS>(a, off, lane, 0, cv, cr);
   MCoef<T, K> cf;
   if (!mprologue<T, MODE, K>(a, cf, s_red, &s_flag)) return;
   double dot[K];
@@ -364,6 +369,9 @@ __global__ __launch_bounds__(kWG) void msell_step(MArgs<T> a) {
   int row = (t * kWaves + wv) * kSlice + lane;
   MOwn<T, K> o;
   if (w >= 0) mown_load<T, MODE, K>(a, row < a.n ? row : 0, o);
+  int msk = 0;  // slice-offset form: the row's present slots
+  if constexpr (OFS)
+    if (w >= 0) msk = a.sm[(t * kWaves + wv) * kSlice + lane];
   T acc[K];
 #pragma unroll
   for (int c = 0; c < K; ++c) acc[c] = T(0);
@@ -383,7 +391,8 @@ __global__ __launch_bounds__(kWG) void msell_step(MArgs<T> a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       int col;
-      if constexpr (I16) col = (j + u < w && cr[u] != kPad16) ? row + cr[u] : -1;
+      if constexpr (OFS) col = (j + u < w && ((msk >> (j + u)) & 1)) ? row + cr[u] : -1;
+      else if constexpr (I16) col = (j + u < w && cr[u] != kPad16) ? row + cr[u] : -1;
       else col = j + u < w ? cr[u] : -1;
       ok[u] = col >= 0;
       const size_t base = (size_t)(ok[u] ? col : 0) * a.ld;
@@ -393,7 +402,7 @@ __global__ __launch_bounds__(kWG) void msell_step(MArgs<T> a) {
     // matrix data of the next batch
     T nv[U];
     int nr[U];
-    if (nw >= 0) msell_batch<T, I16, U>(a, noff, lane, nj, nv, nr);
+    if (nw >= 0) msell_batch<T, I16, U, OFS>(a, noff, lane, nj, nv, nr);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const T vu = ok[u] ? cv[u] : T(0);
@@ -406,6 +415,8 @@ __global__ __launch_bounds__(kWG) void msell_step(MArgs<T> a) {
       for (int c = 0; c < K; ++c) acc[c] = T(0);
       row = (nt * kWaves + wv) * kSlice + lane;
       if (nw >= 0) mown_load<T, MODE, K>(a, row < a.n ? row : 0, o);
+      if constexpr (OFS)
+        if (nw >= 0) msk = a.sm[(nt * kWaves + wv) * kSlice + lane];
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -828,6 +839,8 @@ void fill_mat(MArgs<T>& a, const sla_mat& m, const MatView& v) {
     a.sd = v.sd;
     a.soff = v.soff;
     a.nslices = v.nslices;
+    a.so = v.so;
+    a.sm = v.sm;
     a.ntiles = (v.nslices + kWaves - 1) / kWaves;
   } else if (m.bs == 1) {
     a.tiles = v.tiles;
@@ -843,8 +856,9 @@ hipError_t mlaunch(const sla_mat& m, const MatView& v, const MArgs<T>& a, int gr
   const dim3 g(grid), b(kWG);
   constexpr int U = K >= 8 ? 2 : 4;
   if (m.bs == 1 && v.sell) {
-    if (v.sd) hipLaunchKernelGGL((msell_step<T, MODE, K, true, U>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((msell_step<T, MODE, K, false, U>), g, b, 0, s, a);
+    if (v.so) hipLaunchKernelGGL((msell_step<T, MODE, K, true, U, true>), g, b, 0, s, a);
+    else if (v.sd) hipLaunchKernelGGL((msell_step<T, MODE, K, true, U, false>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((msell_step<T, MODE, K, false, U, false>), g, b, 0, s, a);
   } else if (m.bs == 3 && v.sell) {
     // one gathered block row per lane and slot: K entries per slot, batches
     // of UB slots keep the three row partials per column within registers
