@@ -49,8 +49,8 @@
  *    SLA_SELL_OFS=0: no slice-offset form (by default a CSR matrix whose
  *    64-row slices each have at most 8 distinct column offsets over sorted
  *    rows, as stencils do, stores one offset per slot of a slice and a
- *    one-byte mask of present slots per row, and its one-right-hand-side
- *    products read no per-entry column words).
+ *    one-byte mask of present slots per row, and its products, for one or
+ *    several right-hand sides, read no per-entry column words).
  *  - SLA_GRID=G (G >= 8, rounded down to a multiple of 8): workgroups of the
  *    row-parallel kernels instead of the resident capacity.
  *  - SLA_MALL_BUDGET_MB (default 208) and SLA_MALL_POLICY=A|G|AG|AT|all|none:

@@ -45,8 +45,7 @@ constexpr int kSellTail = 16 * kSlice;
 // e.g. stencils): every slice lists the distinct column offsets of its rows
 // (at most kOfsMax, ascending) and slot j of the slice holds offset j for
 // every row; a one-byte mask per row marks the slots the row has.  The
-// per-entry column words are then not read by the one-right-hand-side
-// products.
+// per-entry column words are then read only by the one-workgroup solver.
 constexpr int kOfsMax = 8;
 // Capacity of the MI355X last-level Infinity Cache (MALL).
 constexpr size_t kMallBytes = (size_t)256 << 20;
