@@ -500,7 +500,10 @@ __device__ __forceinline__ void sell_batch(const StepArgs<T>& a, int off, int la
   for (int u = 0; u < U; ++u) {
     const int idx = off + (j + u) * kSlice + lane;
     v[u] = ld_stream<NT>(a.sv + idx);
-    if constexpr (OFS) raw[u] = ld_stream<NT>(a.so + off / kSlice + j + u);
+    if constexpr (OFS && MODE == M_PLAIN)
+      raw[u] = __builtin_amdgcn_readfirstlane(a.so[off / kSlice + j + u]);
+    else if constexpr (OFS)
+      raw[u] = ld_stream<NT>(a.so + off / kSlice + j + u);
     else raw[u] = sell_raw<NT, I16>(a, idx);
   }
 #pragma unroll
@@ -526,20 +529,28 @@ __global__ __launch_bounds__(kWG) void sell_step(StepArgs<T> a) {
   T hv[U];
   int hr[U];
   int hoff = 0, hw = 0, hm = 0;
+  // SCL: the plain product takes the slice's start, width and slot offsets
+  // as wavefront-uniform scalars (one wavefront per slice); measured faster
+  // there (SpMV streamed from HBM 88 -> 95% of peak on 3D Poisson 128^3)
+  // and slower in the iteration's steps, which keep vector loads.
+  constexpr bool SCL = OFS && MODE == M_PLAIN;
+  auto uni = [](int v) { return SCL ? __builtin_amdgcn_readfirstlane(v) : v; };
   auto load_head = [&](int sl) {
+    sl = uni(sl);
     hoff = 0;
     hw = 0;
     hm = 0;
     if (sl < a.nslices) {
-      hoff = a.soff[sl];
-      hw = (a.soff[sl + 1] - hoff) / kSlice;
+      hoff = uni(a.soff[sl]);
+      hw = (uni(a.soff[sl + 1]) - hoff) / kSlice;
       if constexpr (OFS) hm = ld_stream<NT>(a.sm + sl * kSlice + lane);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int idx = hoff + u * kSlice + lane;
       hv[u] = ld_stream<NT>(a.sv + idx);
-      if constexpr (OFS) hr[u] = ld_stream<NT>(a.so + hoff / kSlice + u);
+      if constexpr (SCL) hr[u] = uni(a.so[hoff / kSlice + u]);
+      else if constexpr (OFS) hr[u] = ld_stream<NT>(a.so + hoff / kSlice + u);
       else hr[u] = sell_raw<NT, I16>(a, idx);
     }
   };
