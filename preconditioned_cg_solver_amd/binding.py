@@ -127,6 +127,37 @@ def _ptr(t: Optional[torch.Tensor]):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _vec(t: torch.Tensor, A: "Mat", numel: int, name: str):
+    """Pointer of a vector argument of a call on A: a contiguous tensor on A's
+    device, in A's dtype, with exactly `numel` elements (the library reads
+    and writes that many from the raw pointer and cannot check it)."""
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype != A.dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, the matrix has {A.dtype}")
+    if t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    if torch.device(t.device) != torch.device(A.device):
+        raise ValueError(f"{name} is on {t.device}, the matrix on {A.device}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _work(work: torch.Tensor, A: "Mat"):
+    """(pointer, size in bytes) of a workspace tensor on A's device."""
+    if not getattr(work, "is_cuda", False) or not work.is_contiguous():
+        raise ValueError("the workspace must be a contiguous GPU tensor")
+    if torch.device(work.device) != torch.device(A.device):
+        raise ValueError(f"the workspace is on {work.device}, the matrix on {A.device}")
+    return ctypes.c_void_p(work.data_ptr()), work.numel() * work.element_size()
+
+
+def _pair(A: "Mat", G: "Mat"):
+    if A.n != G.n or A.dtype != G.dtype or A.block_dim != G.block_dim:
+        raise ValueError("A and G differ in size, block size or dtype")
+
+
 def _dtype_code(dt: torch.dtype) -> int:
     if dt == torch.float64:
         return SLA_F64
@@ -229,10 +260,12 @@ def sla_mat_transpose_arrays(A: Mat):
 
 def sla_spmv(A: Mat, x: torch.Tensor, y: Optional[torch.Tensor] = None, stream=None,
              transpose: bool = False) -> torch.Tensor:
+    px = _vec(x, A, A.n, "x")
     if y is None:
         y = torch.empty(A.n, dtype=A.dtype, device=x.device)
+    py = _vec(y, A, A.n, "y")
     f = lib().sla_spmv_t if transpose else lib().sla_spmv
-    _check(f(A.handle, _ptr(x), _ptr(y), _stream(stream)))
+    _check(f(A.handle, px, py, _stream(stream)))
     return y
 
 
@@ -255,12 +288,14 @@ def workspace(A: Mat, device=None) -> torch.Tensor:
 
 def sla_precond_apply(G: Mat, eps: float, r: torch.Tensor, z: Optional[torch.Tensor] = None,
                       work: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    pr = _vec(r, G, G.n, "r")
     if z is None:
         z = torch.empty_like(r)
+    pz = _vec(z, G, G.n, "z")
     if work is None:
         work = workspace(G, r.device)
-    _check(lib().sla_precond_apply(G.handle, float(eps), _ptr(r), _ptr(z), _ptr(work),
-                                   work.numel(), _stream(stream)))
+    pw, nw = _work(work, G)
+    _check(lib().sla_precond_apply(G.handle, float(eps), pr, pz, pw, nw, _stream(stream)))
     return z
 
 
@@ -280,14 +315,17 @@ def _info(status, si: SolveInfo) -> Info:
 def sla_pcg_solve(A: Mat, G: Mat, eps: float, b: torch.Tensor, x: Optional[torch.Tensor] = None,
                   rtol: float = 1e-10, maxit: int = 1000, work: Optional[torch.Tensor] = None,
                   stream=None, raise_on_error: bool = True) -> Tuple[torch.Tensor, Info]:
+    _pair(A, G)
+    pb = _vec(b, A, A.n, "b")
     if x is None:
         x = torch.empty_like(b)
+    px = _vec(x, A, A.n, "x")
     if work is None:
         work = workspace(A, b.device)
+    pw, nw = _work(work, A)
     si = SolveInfo()
-    st = lib().sla_pcg_solve(A.handle, G.handle, float(eps), _ptr(b), _ptr(x), float(rtol),
-                             int(maxit), _ptr(work), work.numel(), _stream(stream),
-                             ctypes.byref(si))
+    st = lib().sla_pcg_solve(A.handle, G.handle, float(eps), pb, px, float(rtol), int(maxit), pw,
+                             nw, _stream(stream), ctypes.byref(si))
     if raise_on_error:
         _check(st, allow=(OK, NOT_CONVERGED))
     return x, _info(st, si)
@@ -299,17 +337,20 @@ def sla_pcg_solve_history(A: Mat, G: Mat, eps: float, b: torch.Tensor,
                           raise_on_error: bool = True):
     """sla_pcg_solve that also returns the CG coefficients alpha_k (k = 1..iters)
     and beta_k = rho_k / rho_{k-1} (k = 1..iters-1) as CPU float64 tensors."""
+    _pair(A, G)
+    pb = _vec(b, A, A.n, "b")
     if x is None:
         x = torch.empty_like(b)
+    px = _vec(x, A, A.n, "x")
     if work is None:
         work = workspace(A, b.device)
+    pw, nw = _work(work, A)
     hist_a = torch.zeros(max(maxit, 1), dtype=torch.float64, device=b.device)
     hist_b = torch.zeros(max(maxit, 1), dtype=torch.float64, device=b.device)
     si = SolveInfo()
-    st = lib().sla_pcg_solve_history(A.handle, G.handle, float(eps), _ptr(b), _ptr(x),
-                                     float(rtol), int(maxit), _ptr(work), work.numel(),
-                                     _ptr(hist_a), _ptr(hist_b), int(maxit), _stream(stream),
-                                     ctypes.byref(si))
+    st = lib().sla_pcg_solve_history(A.handle, G.handle, float(eps), pb, px, float(rtol),
+                                     int(maxit), pw, nw, _ptr(hist_a), _ptr(hist_b), int(maxit),
+                                     _stream(stream), ctypes.byref(si))
     if raise_on_error:
         _check(st, allow=(OK, NOT_CONVERGED))
     k = si.iterations
@@ -332,14 +373,19 @@ def sla_sai_loss(A: Mat, G: Mat, eps: float, probes: torch.Tensor, scale: float,
                  work: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Per-probe || A M^-1 w_j / scale - w_j ||^2 for the columns w_j of the
     (n, m) device tensor `probes` (float64 device tensor of length m)."""
+    _pair(A, G)
+    if probes.dim() != 2 or probes.shape[0] != A.n:
+        raise ValueError(f"probes must be ({A.n}, m)")
     n, m = probes.shape
     pt = probes.t().contiguous()  # probe j contiguous at j * n
+    pp = _vec(pt, A, n * m, "probes")
     if work is None:
         nb = max(sla_pcg_workspace_size(A), sla_pcg_workspace_size(G), 1)
         work = torch.empty(nb, dtype=torch.uint8, device=probes.device)
+    pw, nw = _work(work, A)
     out = torch.empty(max(m, 1), dtype=torch.float64, device=probes.device)
-    st = lib().sla_sai_loss(A.handle, G.handle, float(eps), _ptr(pt), int(m), float(scale),
-                            _ptr(work), work.numel(), _ptr(out), _stream(stream))
+    st = lib().sla_sai_loss(A.handle, G.handle, float(eps), pp, int(m), float(scale), pw, nw,
+                            _ptr(out), _stream(stream))
     _check(st)
     return out[:m]
 
@@ -348,16 +394,21 @@ def sla_pcg_adjoint(A: Mat, G: Mat, eps: float, x: torch.Tensor, grad_x: torch.T
                     rtol: float = 1e-10, maxit: int = 1000, grad_b: Optional[torch.Tensor] = None,
                     grad_vals: Optional[torch.Tensor] = None, work: Optional[torch.Tensor] = None,
                     stream=None, raise_on_error: bool = True):
+    _pair(A, G)
+    px = _vec(x, A, A.n, "x")
+    pgx = _vec(grad_x, A, A.n, "grad_x")
     if grad_b is None:
         grad_b = torch.empty_like(x)
+    pgb = _vec(grad_b, A, A.n, "grad_b")
     if grad_vals is None:
         grad_vals = torch.empty(A.nnz, dtype=A.dtype, device=x.device)
+    pgv = _vec(grad_vals, A, A.nnz, "grad_vals")
     if work is None:
         work = workspace(A, x.device)
+    pw, nw = _work(work, A)
     si = SolveInfo()
-    st = lib().sla_pcg_adjoint(A.handle, G.handle, float(eps), _ptr(x), _ptr(grad_x),
-                               _ptr(grad_b), _ptr(grad_vals), float(rtol), int(maxit), _ptr(work),
-                               work.numel(), _stream(stream), ctypes.byref(si))
+    st = lib().sla_pcg_adjoint(A.handle, G.handle, float(eps), px, pgx, pgb, pgv, float(rtol),
+                               int(maxit), pw, nw, _stream(stream), ctypes.byref(si))
     if raise_on_error:
         _check(st, allow=(OK, NOT_CONVERGED))
     return grad_b, grad_vals, _info(st, si)
@@ -365,28 +416,40 @@ def sla_pcg_adjoint(A: Mat, G: Mat, eps: float, x: torch.Tensor, grad_x: torch.T
 
 # ----- several right-hand sides (n x k row-major device tensors) -----
 
-def _cols(t: torch.Tensor) -> int:
+def _cols(t: torch.Tensor, A: "Mat" = None) -> int:
     if t.dim() != 2 or not t.is_contiguous():
         raise ValueError("expected a contiguous (n, k) tensor")
+    if A is not None and t.shape[0] != A.n:
+        raise ValueError(f"expected {A.n} rows, got {t.shape[0]}")
     return t.shape[1]
+
+
+def _block(t: torch.Tensor, A: "Mat", k: int, name: str):
+    if t.dim() != 2 or tuple(t.shape) != (A.n, k):
+        raise ValueError(f"{name} must be ({A.n}, {k}), got {tuple(t.shape)}")
+    return _vec(t, A, A.n * k, name)
 
 
 def sla_spmm(A: Mat, X: torch.Tensor, Y: Optional[torch.Tensor] = None,
              stream=None) -> torch.Tensor:
     """Y = A X for the k columns of the (n, k) tensor X."""
-    k = _cols(X)
+    k = _cols(X, A)
+    px = _block(X, A, k, "X")
     if Y is None:
         Y = torch.empty_like(X)
-    _check(lib().sla_spmm(A.handle, _ptr(X), _ptr(Y), k, _stream(stream)))
+    py = _block(Y, A, k, "Y")
+    _check(lib().sla_spmm(A.handle, px, py, k, _stream(stream)))
     return Y
 
 
 def sla_spmm_t(A: Mat, X: torch.Tensor, Y: Optional[torch.Tensor] = None,
                stream=None) -> torch.Tensor:
-    k = _cols(X)
+    k = _cols(X, A)
+    px = _block(X, A, k, "X")
     if Y is None:
         Y = torch.empty_like(X)
-    _check(lib().sla_spmm_t(A.handle, _ptr(X), _ptr(Y), k, _stream(stream)))
+    py = _block(Y, A, k, "Y")
+    _check(lib().sla_spmm_t(A.handle, px, py, k, _stream(stream)))
     return Y
 
 
@@ -411,16 +474,19 @@ def sla_pcg_solve_multi(A: Mat, G: Mat, eps: float, B: torch.Tensor,
                         raise_on_error: bool = True):
     """Solve A X = B for the k columns of B (n, k) together; returns X and one
     Info per column (its own status, iterations and residual)."""
-    k = _cols(B)
+    _pair(A, G)
+    k = _cols(B, A)
+    pb = _block(B, A, k, "B")
     if X is None:
         X = torch.empty_like(B)
+    px = _block(X, A, k, "X")
     if work is None:
         work = workspace_multi(A, k, B.device)
+    pw, nw = _work(work, A)
     infos = (SolveInfo * k)()
     cst = (ctypes.c_int * k)()
-    st = lib().sla_pcg_solve_multi(A.handle, G.handle, float(eps), _ptr(B), _ptr(X), k,
-                                   float(rtol), int(maxit), _ptr(work), work.numel(),
-                                   _stream(stream), infos, cst)
+    st = lib().sla_pcg_solve_multi(A.handle, G.handle, float(eps), pb, px, k, float(rtol),
+                                   int(maxit), pw, nw, _stream(stream), infos, cst)
     if raise_on_error:
         _check(st, allow=(OK, NOT_CONVERGED))
     return X, _multi_out(st, infos, cst, k)
@@ -434,18 +500,23 @@ def sla_pcg_adjoint_multi(A: Mat, G: Mat, eps: float, X: torch.Tensor, GX: torch
                           raise_on_error: bool = True):
     """Adjoint of k solves sharing A: dL/dB = A^-T dL/dX column by column and
     dL/dA on A's pattern summed over the solves."""
-    k = _cols(X)
+    _pair(A, G)
+    k = _cols(X, A)
+    px = _block(X, A, k, "X")
+    pgx = _block(GX, A, k, "GX")
     if GB is None:
         GB = torch.empty_like(X)
+    pgb = _block(GB, A, k, "GB")
     if grad_vals is None:
         grad_vals = torch.empty(A.nnz, dtype=A.dtype, device=X.device)
+    pgv = _vec(grad_vals, A, A.nnz, "grad_vals")
     if work is None:
         work = workspace_multi(A, k, X.device)
+    pw, nw = _work(work, A)
     infos = (SolveInfo * k)()
     cst = (ctypes.c_int * k)()
-    st = lib().sla_pcg_adjoint_multi(A.handle, G.handle, float(eps), _ptr(X), _ptr(GX), _ptr(GB),
-                                     _ptr(grad_vals), k, float(rtol), int(maxit), _ptr(work),
-                                     work.numel(), _stream(stream), infos, cst)
+    st = lib().sla_pcg_adjoint_multi(A.handle, G.handle, float(eps), px, pgx, pgb, pgv, k,
+                                     float(rtol), int(maxit), pw, nw, _stream(stream), infos, cst)
     if raise_on_error:
         _check(st, allow=(OK, NOT_CONVERGED))
     return GB, grad_vals, _multi_out(st, infos, cst, k)
@@ -453,9 +524,12 @@ def sla_pcg_adjoint_multi(A: Mat, G: Mat, eps: float, X: torch.Tensor, GX: torch
 
 def sla_pattern_grad(A: Mat, lam: torch.Tensor, x: torch.Tensor,
                      out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    pl = _vec(lam, A, A.n, "lam")
+    px = _vec(x, A, A.n, "x")
     if out is None:
         out = torch.empty(A.nnz, dtype=A.dtype, device=x.device)
-    _check(lib().sla_pattern_grad(A.handle, _ptr(lam), _ptr(x), _ptr(out), _stream(stream)))
+    po = _vec(out, A, A.nnz, "out")
+    _check(lib().sla_pattern_grad(A.handle, pl, px, po, _stream(stream)))
     return out
 
 

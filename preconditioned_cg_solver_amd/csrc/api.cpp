@@ -51,9 +51,22 @@ void free_owned(sla_mat* m) {
   }
 }
 
-// Frees a handle, its permuted copy and their buffers (same precondition).
+// Waits for the asynchronous calls queued on a handle (its use events) and
+// releases the events.
+void wait_uses(sla_mat* m) {
+  std::lock_guard<std::mutex> lk(m->use_mu);
+  for (auto& u : m->uses) {
+    (void)hipEventSynchronize(u.e);
+    (void)hipEventDestroy(u.e);
+  }
+  m->uses.clear();
+}
+
+// Frees a handle, its permuted copy and their buffers once the work queued
+// on them has finished.
 void destroy_handle(sla_mat* m) {
   if (m->ord) destroy_handle(m->ord);
+  wait_uses(m);
   free_owned(m);
   delete m;
 }
@@ -244,7 +257,7 @@ sla_status ensure_order(sla_mat* A, sla_mat* G, hipStream_t s, bool* use) {
   }
   if (!G->ord || G->ord_id != A->ord_id) {
     if (G->ord) {
-      (void)hipDeviceSynchronize();
+      // the copy is used only by solves, which return when their work is done
       destroy_handle(G->ord);
       G->ord = nullptr;
     }
@@ -312,10 +325,40 @@ sla_status solve_multi_any(sla_mat* A, sla_mat* G, double eps, const void* b, vo
   return st;
 }
 
-// k = 0: one right-hand side; k >= 1: the multi-RHS solver's workspace.
 sla_status check_solve(sla_mat_t A, sla_mat_t G, double eps, const void* b, const void* x,
                        double rtol, int32_t maxit, const void* work, size_t work_bytes,
                        int32_t k = 0) {
+  return check_solve_args(A, G, eps, b, x, rtol, maxit, work, work_bytes, k, true);
+}
+
+// [p, p + pb) and [q, q + qb) overlap
+bool overlaps(const void* p, size_t pb, const void* q, size_t qb) {
+  const uintptr_t a = (uintptr_t)p, c = (uintptr_t)q;
+  return pb > 0 && qb > 0 && a < c + qb && c < a + pb;
+}
+
+// The adjoint's output lambda (= dL/db) must not share memory with x, which
+// the pattern gradient reads after the solve, or with the workspace; the
+// gradient must not share memory with lambda or x.
+sla_status check_adjoint_outputs(const sla_mat& A, int k, const void* x, const void* grad_b,
+                                 const void* grad_vals, const void* work, size_t work_bytes) {
+  const size_t es = A.dtype == SLA_F64 ? 8 : 4;
+  const size_t vb = (size_t)A.n() * (size_t)k * es, gb = (size_t)A.nnz() * es;
+  if (!check(!overlaps(grad_b, vb, x, vb), "grad_b must not overlap x")) return SLA_ERR_INVALID_ARG;
+  if (!check(!overlaps(grad_b, vb, work, work_bytes), "grad_b must not overlap the workspace"))
+    return SLA_ERR_INVALID_ARG;
+  if (!check(!overlaps(grad_vals, gb, x, vb) && !overlaps(grad_vals, gb, grad_b, vb),
+             "grad_vals must not overlap x or grad_b"))
+    return SLA_ERR_INVALID_ARG;
+  return SLA_OK;
+}
+
+}  // namespace
+
+// k = 0: one right-hand side; k >= 1: the multi-RHS solver's workspace.
+sla_status check_solve_args(const sla_mat* A, const sla_mat* G, double eps, const void* b,
+                            const void* x, double rtol, int32_t maxit, const void* work,
+                            size_t work_bytes, int32_t k, bool need_work) {
   if (!check(A && G, "matrix handle is NULL")) return SLA_ERR_INVALID_ARG;
   if (!check(A->nbr == G->nbr && A->bs == G->bs && A->dtype == G->dtype,
              "A and G differ in size, block size or dtype"))
@@ -330,21 +373,60 @@ sla_status check_solve(sla_mat_t A, sla_mat_t G, double eps, const void* b, cons
   if (!check(b && x, "vector pointer is NULL")) return SLA_ERR_INVALID_ARG;
   if (!check(b != x, "x must not alias b")) return SLA_ERR_INVALID_ARG;
   if (k > 0) {
-    if (!check(work != nullptr && work_bytes >= workspace_bytes_multi(*A, k),
-               "workspace too small"))
+    if (need_work && !check(work != nullptr && work_bytes >= workspace_bytes_multi(*A, k),
+                            "workspace too small"))
       return SLA_ERR_INVALID_ARG;
     return SLA_OK;
   }
-  if (!check(work != nullptr && work_bytes >= workspace_bytes(*A), "workspace too small"))
+  if (need_work &&
+      !check(work != nullptr && work_bytes >= workspace_bytes(*A), "workspace too small"))
     return SLA_ERR_INVALID_ARG;
-  const int64_t slots = (int64_t)std::max<int64_t>(A->fwd.nlong_rows, A->nnz() / kLdsCap + 1);
-  if (!check(G->fwd.nlong_rows <= slots && G->tr.nlong_rows <= slots,
+  // the workspace's long-row scratch is sized from A's entry count
+  const int64_t rows = long_rows_bound(*A), parts = long_part_bound(*A);
+  if (!check(G->fwd.nlong_rows <= rows && G->tr.nlong_rows <= rows &&
+                 G->fwd.n_long_part <= parts && G->tr.n_long_part <= parts,
              "G has more long rows than the workspace sized for A provides"))
     return SLA_ERR_INVALID_ARG;
   return SLA_OK;
 }
 
-}  // namespace
+sla_status use_begin(const sla_mat& m, hipStream_t s, bool scratch) {
+  if (!scratch) return SLA_OK;
+  std::lock_guard<std::mutex> lk(m.use_mu);
+  for (const auto& u : m.uses)
+    if (u.scratch && u.s != s) SLA_HIP(hipStreamWaitEvent(s, u.e, 0));
+  return SLA_OK;
+}
+
+sla_status use_end(const sla_mat& m, hipStream_t s, bool scratch) {
+  std::lock_guard<std::mutex> lk(m.use_mu);
+  sla_mat::Use* u = nullptr;
+  for (auto& v : m.uses)
+    if (v.s == s) u = &v;
+  if (!u) {
+    hipEvent_t e = nullptr;
+    SLA_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+    m.uses.push_back({s, e, false});
+    u = &m.uses.back();
+  }
+  u->scratch = u->scratch || scratch;
+  SLA_HIP(hipEventRecord(u->e, s));
+  return SLA_OK;
+}
+
+// Runs an asynchronous call on handle m (and m2, if given) between the use
+// log's begin and end: the call waits for m's own long-row scratch on other
+// streams when it uses it, and records the stream's event on both handles.
+template <typename F>
+sla_status async_call(const sla_mat& m, const sla_mat* m2, hipStream_t s, bool scratch, F&& f) {
+  sla_status st = use_begin(m, s, scratch);
+  if (st != SLA_OK) return st;
+  st = f();
+  if (st != SLA_OK) return st;
+  st = use_end(m, s, scratch);
+  if (st == SLA_OK && m2 && m2 != &m) st = use_end(*m2, s, false);
+  return st;
+}
 
 void set_error(const std::string& msg) { g_last_error = msg; }
 
@@ -394,13 +476,9 @@ sla_status sla_bsr_create(sla_mat_t* out, int64_t n_block_rows, int64_t nnzb, in
 
 sla_status sla_mat_destroy(sla_mat_t m) {
   if (!m) return SLA_OK;
-  // wait for every queued use of the handle on its own device before its
-  // buffers go back to the cache
-  int cur = 0;
-  const bool switch_dev = hipGetDevice(&cur) == hipSuccess && cur != m->device;
-  if (switch_dev) (void)hipSetDevice(m->device);
-  (void)hipDeviceSynchronize();
-  if (switch_dev) (void)hipSetDevice(cur);
+  // waits for the handle's queued asynchronous calls (their events) before
+  // its buffers go back to the cache; solves and creation have already
+  // finished when they return
   destroy_handle(m);
   return SLA_OK;
 }
@@ -459,7 +537,9 @@ sla_status sla_spmv(sla_mat_t A, const void* d_x, void* d_y, void* stream) {
     set_error("x and y must be distinct non-NULL device vectors");
     return SLA_ERR_INVALID_ARG;
   }
-  return sla::spmv(*A, false, d_x, d_y, (hipStream_t)stream);
+  hipStream_t s = (hipStream_t)stream;
+  return async_call(*A, nullptr, s, A->fwd.nlong > 0,
+                    [&] { return sla::spmv(*A, false, d_x, d_y, s); });
 }
 
 sla_status sla_spmv_t(sla_mat_t A, const void* d_x, void* d_y, void* stream) {
@@ -471,7 +551,9 @@ sla_status sla_spmv_t(sla_mat_t A, const void* d_x, void* d_y, void* stream) {
     set_error("x and y must be distinct non-NULL device vectors");
     return SLA_ERR_INVALID_ARG;
   }
-  return sla::spmv(*A, true, d_x, d_y, (hipStream_t)stream);
+  hipStream_t s = (hipStream_t)stream;
+  return async_call(*A, nullptr, s, A->tr.nlong > 0,
+                    [&] { return sla::spmv(*A, true, d_x, d_y, s); });
 }
 
 sla_status sla_pcg_workspace_size(sla_mat_t A, size_t* bytes) {
@@ -497,7 +579,10 @@ sla_status sla_precond_apply(sla_mat_t G, double eps, const void* d_r, void* d_z
     set_error("bad vector or workspace argument");
     return SLA_ERR_INVALID_ARG;
   }
-  return sla::precond_apply(*G, eps, d_r, d_z, d_work, work_bytes, (hipStream_t)stream);
+  hipStream_t s = (hipStream_t)stream;
+  return async_call(*G, nullptr, s, false, [&] {
+    return sla::precond_apply(*G, eps, d_r, d_z, d_work, work_bytes, s);
+  });
 }
 
 sla_status sla_pcg_solve(sla_mat_t A, sla_mat_t G, double eps, const void* d_b, void* d_x,
@@ -533,6 +618,9 @@ sla_status sla_pcg_adjoint(sla_mat_t A, sla_mat_t G, double eps, const void* d_x
     set_error("x or grad_vals is NULL");
     return SLA_ERR_INVALID_ARG;
   }
+  if ((st = check_adjoint_outputs(*A, 1, d_x, d_grad_b, d_grad_vals, d_work, work_bytes)) !=
+      SLA_OK)
+    return st;
   hipStream_t s = (hipStream_t)stream;
   st = solve_any(A, G, eps, d_grad_x, d_grad_b, rtol, maxit, d_work, work_bytes, s, info);
   if (st < 0) return st;
@@ -552,7 +640,8 @@ sla_status sla_spmm(sla_mat_t A, const void* d_x, void* d_y, int32_t k, void* st
     set_error("X and Y must be distinct non-NULL device arrays");
     return SLA_ERR_INVALID_ARG;
   }
-  return sla::spmm(*A, false, d_x, d_y, k, (hipStream_t)stream);
+  hipStream_t s = (hipStream_t)stream;
+  return async_call(*A, nullptr, s, false, [&] { return sla::spmm(*A, false, d_x, d_y, k, s); });
 }
 
 sla_status sla_spmm_t(sla_mat_t A, const void* d_x, void* d_y, int32_t k, void* stream) {
@@ -564,7 +653,8 @@ sla_status sla_spmm_t(sla_mat_t A, const void* d_x, void* d_y, int32_t k, void* 
     set_error("X and Y must be distinct non-NULL device arrays");
     return SLA_ERR_INVALID_ARG;
   }
-  return sla::spmm(*A, true, d_x, d_y, k, (hipStream_t)stream);
+  hipStream_t s = (hipStream_t)stream;
+  return async_call(*A, nullptr, s, false, [&] { return sla::spmm(*A, true, d_x, d_y, k, s); });
 }
 
 sla_status sla_pcg_workspace_size_multi(sla_mat_t A, int32_t k, size_t* bytes) {
@@ -605,6 +695,9 @@ sla_status sla_pcg_adjoint_multi(sla_mat_t A, sla_mat_t G, double eps, const voi
     set_error("x or grad_vals is NULL");
     return SLA_ERR_INVALID_ARG;
   }
+  if ((st = check_adjoint_outputs(*A, k, d_x, d_grad_b, d_grad_vals, d_work, work_bytes)) !=
+      SLA_OK)
+    return st;
   hipStream_t s = (hipStream_t)stream;
   st = solve_multi_any(A, G, eps, d_grad_x, d_grad_b, k, rtol, maxit, d_work, s, info,
                        col_status);
@@ -646,7 +739,10 @@ sla_status sla_sai_loss(sla_mat_t A, sla_mat_t G, double eps, const void* d_prob
     set_error("bad probe, output or workspace argument");
     return SLA_ERR_INVALID_ARG;
   }
-  return sla::sai_loss(*A, *G, eps, d_probes, nprobe, scale, d_work, d_out, (hipStream_t)stream);
+  hipStream_t s = (hipStream_t)stream;
+  return async_call(*A, G, s, false, [&] {
+    return sla::sai_loss(*A, *G, eps, d_probes, nprobe, scale, d_work, d_out, s);
+  });
 }
 
 sla_status sla_pattern_grad(sla_mat_t A, const void* d_lambda, const void* d_x,
@@ -659,7 +755,9 @@ sla_status sla_pattern_grad(sla_mat_t A, const void* d_lambda, const void* d_x,
     set_error("NULL vector");
     return SLA_ERR_INVALID_ARG;
   }
-  return sla::pattern_grad(*A, d_lambda, d_x, d_grad_vals, (hipStream_t)stream);
+  hipStream_t s = (hipStream_t)stream;
+  return async_call(*A, nullptr, s, false,
+                    [&] { return sla::pattern_grad(*A, d_lambda, d_x, d_grad_vals, s); });
 }
 
 const char* sla_status_string(sla_status st) {

@@ -8,8 +8,10 @@
 #include <cstdlib>
 #include <map>
 #include <mutex>
+#include <new>
 #include <unordered_map>
 #include <utility>
+#include <vector>
 
 #include "internal.h"
 
@@ -82,6 +84,75 @@ void buf_free(void* p) {
   }
   c.idle[dev].insert({bytes, p});
   c.held[dev] += bytes;
+}
+
+// Polling records: a solve copies its 16-byte exit flag into pinned host
+// memory once per batch of iterations and waits on an event; each running
+// solve holds a record of its own, so solves on different streams or threads
+// proceed independently.  Records return to a per-device pool and are reused.
+namespace {
+struct PollPool {
+  std::mutex mu;
+  std::vector<PollSlot*> idle[64];
+};
+PollPool& poll_pool() {
+  static PollPool p;
+  return p;
+}
+int current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  return dev;
+}
+}  // namespace
+
+sla_status poll_create(PollSlot** out) {
+  *out = nullptr;
+  PollSlot* p = new (std::nothrow) PollSlot();
+  if (!p) {
+    set_error("host allocation failed");
+    return SLA_ERR_OOM;
+  }
+  p->device = current_device();
+  if (hipHostMalloc(&p->host, kPollBytes, hipHostMallocDefault) != hipSuccess) {
+    (void)hipGetLastError();
+    delete p;
+    set_error("hipHostMalloc of a polling record failed");
+    return SLA_ERR_OOM;
+  }
+  for (auto& e : p->ev) {
+    const hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+    if (r != hipSuccess) {
+      for (auto& f : p->ev)
+        if (f) (void)hipEventDestroy(f);
+      (void)hipHostFree(p->host);
+      delete p;
+      return hip_fail(r, "hipEventCreateWithFlags");
+    }
+  }
+  *out = p;
+  return SLA_OK;
+}
+
+sla_status poll_acquire(PollSlot** out) {
+  const int dev = current_device();
+  PollPool& pp = poll_pool();
+  {
+    std::lock_guard<std::mutex> lk(pp.mu);
+    if (!pp.idle[dev].empty()) {
+      *out = pp.idle[dev].back();
+      pp.idle[dev].pop_back();
+      return SLA_OK;
+    }
+  }
+  return poll_create(out);
+}
+
+void poll_release(PollSlot* p) {
+  if (!p) return;
+  PollPool& pp = poll_pool();
+  std::lock_guard<std::mutex> lk(pp.mu);
+  pp.idle[p->device >= 0 && p->device < 64 ? p->device : 0].push_back(p);
 }
 
 constexpr size_t kAlign = 256;

@@ -5,8 +5,11 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <mutex>
 #include <string>
+#include <vector>
 
+#include "bounds.h"
 #include "sla.h"
 
 namespace sla {
@@ -176,6 +179,19 @@ struct sla_mat {
   const int32_t* iperm = nullptr;
   sla_mat* ord = nullptr;
   uint64_t ord_id = 0;
+  // Asynchronous calls on the handle (products, preconditioner apply,
+  // pattern gradient, SAI loss) record an event on their stream after their
+  // launches; sla_mat_destroy waits on these instead of the whole device.
+  // `scratch` marks streams whose last call used the handle's own long-row
+  // scratch (the standalone products): a later call on another stream that
+  // uses it waits for that event first.
+  struct Use {
+    hipStream_t s;
+    hipEvent_t e;
+    bool scratch;
+  };
+  mutable std::mutex use_mu;
+  mutable std::vector<Use> uses;
   int64_t n() const { return nbr * bs; }
   int64_t nnz() const { return nnzb * bs * bs; }
 };
@@ -219,21 +235,77 @@ sla_status build_permuted(const sla_mat& m, const int32_t* perm, const int32_t* 
 sla_status permute_rows(const int32_t* perm, const void* src, void* dst, int64_t n, int cols,
                         int32_t dtype, bool into, hipStream_t s);
 
+// Long-row scratch of a product: per-chunk partial sums and one integer
+// ticket per long row (the chunk that takes the last ticket sums the row and
+// resets its ticket to 0).  The standalone products use the handle's own
+// (long_scratch_of); the solves, the preconditioner apply and the SAI loss
+// carve theirs from the caller's workspace, so calls on different streams
+// never share tickets.
+struct LongScratch {
+  double* part;
+  int* cnt;
+};
+LongScratch long_scratch_of(const sla_mat& m, bool transpose);
+// Bounds on the long rows and chunks of any matrix with at most A's stored
+// entries (the workspace sizes its long-row scratch by them).
+int64_t long_rows_bound(const sla_mat& A);
+int64_t long_part_bound(const sla_mat& A);
+
+// Event log of a handle's asynchronous calls (api.cpp): use_begin before
+// enqueueing work on s (waits for the handle's scratch on other streams
+// when `scratch`), use_end after it (records the stream's event).
+sla_status use_begin(const sla_mat& m, hipStream_t s, bool scratch);
+sla_status use_end(const sla_mat& m, hipStream_t s, bool scratch);
+
+// Pinned host records a running solve polls (host_util.cpp): kPollBytes of
+// pinned memory and three events.  poll_acquire takes one from a pool
+// (allocating when every pooled slot is in use); poll_create makes a slot
+// outside the pool.
+constexpr size_t kPollBytes = 4096;
+struct PollSlot {
+  void* host = nullptr;
+  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+  int device = -1;
+};
+sla_status poll_create(PollSlot** out);
+sla_status poll_acquire(PollSlot** out);
+void poll_release(PollSlot* p);
+// Holds a pooled slot for the lifetime of a solve.
+struct PollLease {
+  PollSlot* p = nullptr;
+  PollLease() = default;
+  PollLease(const PollLease&) = delete;
+  PollLease& operator=(const PollLease&) = delete;
+  ~PollLease() {
+    if (p) poll_release(p);
+  }
+};
+
 // Solver (solver.hip).  workspace_bytes = workspace_base plus, for an A the
 // solves reorder, the two permuted vectors (b and x) after it.
 size_t workspace_base(const sla_mat& A);
 size_t workspace_bytes(const sla_mat& A);
-sla_status spmv(const sla_mat& A, bool transpose, const void* x, void* y, hipStream_t s);
+// y = A x (or A^T x) with the given long-row scratch (NULL: the handle's).
+sla_status spmv(const sla_mat& A, bool transpose, const void* x, void* y, hipStream_t s,
+                const LongScratch* ls = nullptr);
 sla_status precond_apply(const sla_mat& G, double eps, const void* r, void* z, void* work,
                          size_t work_bytes, hipStream_t s);
+// slot: the polling record to use (NULL: one from the pool); quiet: record
+// no profiling events (the no-allocation entry point).
 sla_status pcg_solve(const sla_mat& A, const sla_mat& G, double eps, const void* b, void* x,
                      double rtol, int32_t maxit, void* work, size_t work_bytes, hipStream_t s,
                      sla_solve_info* info, double* hist_a = nullptr, double* hist_b = nullptr,
-                     int32_t hist_len = 0);
+                     int32_t hist_len = 0, PollSlot* slot = nullptr, bool quiet = false);
 sla_status pattern_grad(const sla_mat& A, const void* lam, const void* x, void* grad,
                         hipStream_t s);
 sla_status sai_loss(const sla_mat& A, const sla_mat& G, double eps, const void* probes,
                     int32_t nprobe, double scale, void* work, double* out, hipStream_t s);
+// Argument checks shared by the solve entry points (api.cpp): k = 0 for one
+// right-hand side, k >= 1 for the multi-RHS workspace; need_work = false
+// skips the workspace check (the no-allocation entry point).
+sla_status check_solve_args(const sla_mat* A, const sla_mat* G, double eps, const void* b,
+                            const void* x, double rtol, int32_t maxit, const void* work,
+                            size_t work_bytes, int32_t k, bool need_work);
 
 // Small systems solved in one workgroup per right-hand side (solver.hip).
 bool small_applies(const sla_mat& A, const sla_mat& G);

@@ -923,20 +923,7 @@ MWork mcarve(const sla_mat& A, int kw, void* work) {
   return w;
 }
 
-std::mutex g_mpoll_mu;
-MState* g_mhost = nullptr;  // 3 polling slots + 1 final record, pinned
-hipEvent_t g_mpoll_ev[3];
-
-sla_status mpoll_init() {
-  if (g_mhost) return SLA_OK;
-  if (hipHostMalloc((void**)&g_mhost, 4 * sizeof(MState), hipHostMallocDefault) != hipSuccess) {
-    g_mhost = nullptr;
-    set_error("hipHostMalloc of the polling slots failed");
-    return SLA_ERR_OOM;
-  }
-  for (auto& e : g_mpoll_ev) SLA_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
-  return SLA_OK;
-}
+static_assert(4 * sizeof(MState) <= kPollBytes, "polling record too small");
 
 // One pass of K columns: b and x point at the pass's first column of the
 // caller's n x ld arrays.
@@ -993,9 +980,11 @@ sla_status mpcg_pass(const sla_mat& A, const sla_mat& G, double eps, const T* b,
   aG.rv = R[0];
   SLA_HIP((mlaunch<T, MM_G0, K>(G, G.fwd, aG, grid, s)));
 
-  std::unique_lock<std::mutex> lk(g_mpoll_mu);
-  sla_status pst = mpoll_init();
+  PollLease lease;
+  sla_status pst = poll_acquire(&lease.p);
   if (pst != SLA_OK) return pst;
+  MState* mhost = (MState*)lease.p->host;
+  hipEvent_t* mev = lease.p->ev;
   std::deque<int> pend;
   int next_slot = 0;
   const int B = batch_iters();
@@ -1045,28 +1034,27 @@ sla_status mpcg_pass(const sla_mat& A, const sla_mat& G, double eps, const T* b,
       }
       const int slot = next_slot;
       next_slot = (next_slot + 1) % 3;
-      SLA_HIP(hipMemcpyAsync(&g_mhost[slot], w.st, 16, hipMemcpyDeviceToHost, s));
-      SLA_HIP(hipEventRecord(g_mpoll_ev[slot], s));
+      SLA_HIP(hipMemcpyAsync(&mhost[slot], w.st, 16, hipMemcpyDeviceToHost, s));
+      SLA_HIP(hipEventRecord(mev[slot], s));
       pend.push_back(slot);
       k = kend + 1;
     }
     if (pend.size() >= 2 || (k > maxit && !pend.empty())) {
       const int slot = pend.front();
       pend.pop_front();
-      SLA_HIP(hipEventSynchronize(g_mpoll_ev[slot]));
-      if (g_mhost[slot].done) finished = true;
+      SLA_HIP(hipEventSynchronize(mev[slot]));
+      if (mhost[slot].done) finished = true;
     }
     if (k > maxit && pend.empty()) finished = true;
   }
   while (!pend.empty()) {
-    SLA_HIP(hipEventSynchronize(g_mpoll_ev[pend.front()]));
+    SLA_HIP(hipEventSynchronize(mev[pend.front()]));
     pend.pop_front();
   }
-  MState* hs = &g_mhost[3];
+  MState* hs = &mhost[3];
   SLA_HIP(hipMemcpyAsync(hs, w.st, sizeof(MState), hipMemcpyDeviceToHost, s));
   SLA_HIP(hipStreamSynchronize(s));
   const MState fin = *hs;
-  lk.unlock();
 
   sla_status worst = SLA_OK;
   for (int c = 0; c < K; ++c) {

@@ -832,7 +832,8 @@ sla_status build_sell_ofs(MatView& view, int64_t n, int64_t nnz, int32_t dtype, 
     total += (int64_t)hc[sl] * kSlice;
     hc[sl] *= kSlice;
   }
-  if (!ok || total * 100 > nnz * (100 + kSellMaxPadPct)) {
+  if (!ok || total * 100 > nnz * (100 + kSellMaxPadPct) ||
+      !sliced_layout_fits(nslices, wmax, kSlice, kSellTail)) {
     SLA_HIP(hipFreeAsync(ofs, s));
     SLA_HIP(hipFreeAsync(cnt, s));
     SLA_HIP(hipStreamSynchronize(s));
@@ -915,6 +916,9 @@ sla_status build_sell(MatView& view, int64_t n, int64_t nnz, int32_t dtype, void
   SLA_HIP(hipMemcpyAsync(&h[2], maxd, sizeof(int), hipMemcpyDeviceToHost, s));
   SLA_HIP(hipFreeAsync(buf, s));
   SLA_HIP(hipStreamSynchronize(s));
+  // the slot counts were summed in int32: only a layout whose largest
+  // possible size fits int32 has an exact total
+  if (!sliced_layout_fits(nslices, h[0], kSlice, kSellTail)) return SLA_OK;
   const int64_t total = h[1];
   if (h[0] > kSellMaxWidth || total * 100 > nnz * (100 + kSellMaxPadPct)) return SLA_OK;
   const size_t es = dtype == SLA_F64 ? 8 : 4;
@@ -997,6 +1001,7 @@ sla_status build_bsell(MatView& view, int64_t nbr, int64_t nnzb, int32_t dtype, 
   SLA_HIP(hipMemcpyAsync(&h[2], maxd, sizeof(int), hipMemcpyDeviceToHost, s));
   SLA_HIP(hipFreeAsync(buf, s));
   SLA_HIP(hipStreamSynchronize(s));
+  if (!sliced_layout_fits(nslices, h[0], kBSlotVals, kBSellTail * kBSlotVals)) return SLA_OK;
   const int64_t total = h[1];  // slots
   if (h[0] > kBSellMaxWidth || total * kBSlice * 100 > nnzb * (100 + kSellMaxPadPct))
     return SLA_OK;

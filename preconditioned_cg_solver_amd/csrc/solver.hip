@@ -38,7 +38,6 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
-#include <deque>
 #include <mutex>
 #include <utility>
 #include <vector>
@@ -1252,20 +1251,6 @@ MallPlan mall_plan(const sla_mat& A, const sla_mat& G) {
   return {true, true, true};
 }
 
-// Long-row scratch of a handle orientation lives in the handle (owned[]);
-// slots: see api.cpp (make_long_scratch).
-struct LongScratch {
-  double* part;
-  int* cnt;
-};
-LongScratch long_scratch(const sla_mat& m, bool transpose) {
-  LongScratch ls{nullptr, nullptr};
-  const int base = transpose ? 4 : 2;
-  ls.part = (double*)m.owned[base];
-  ls.cnt = (int*)m.owned[base + 1];
-  return ls;
-}
-
 // ----- profiling -----
 struct ProfClass {
   int64_t launches = 0;
@@ -1337,26 +1322,12 @@ struct Recorder {
   }
 };
 
-// ----- pinned host polling slots -----
-std::mutex g_poll_mu;
-SolverState* g_host_state = nullptr;
-hipEvent_t g_poll_ev[3];
-bool g_poll_ready = false;
-
-sla_status poll_init() {
-  if (g_poll_ready) return SLA_OK;
-  if (hipHostMalloc((void**)&g_host_state, 4 * sizeof(SolverState), hipHostMallocDefault) !=
-      hipSuccess) {
-    set_error("hipHostMalloc of the polling slots failed");
-    return SLA_ERR_OOM;
-  }
-  for (auto& e : g_poll_ev) SLA_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
-  g_poll_ready = true;
-  return SLA_OK;
-}
+static_assert(4 * sizeof(SolverState) <= kPollBytes, "polling record too small");
 
 struct Work {
   SolverState* st;
+  int* lcnt;      // long-row tickets (zeroed with the state)
+  double* lpart;  // long-row chunk partials
   double* psig;
   double* prr;
   double* prho;
@@ -1364,10 +1335,17 @@ struct Work {
 };
 
 size_t partial_slots(const sla_mat& A) {
-  const int64_t lr_bound = std::max<int64_t>(A.fwd.nlong_rows, A.nnz() / kLdsCap + 1);
-  return (size_t)max_grid() + (size_t)lr_bound;
+  return (size_t)max_grid() + (size_t)long_rows_bound(A);
 }
 
+// Bytes from the start of the workspace that must be zero when a solve or
+// a preconditioner apply starts: the state and the long-row tickets.
+size_t zeroed_bytes(const sla_mat& A) {
+  return align_up(sizeof(SolverState)) + align_up((size_t)long_rows_bound(A) * sizeof(int));
+}
+
+// Workspace layout: state, long-row tickets, long-row partials, the three
+// reduction partial arrays, seven n-vectors.
 Work carve(const sla_mat& A, void* work) {
   Work w;
   char* p = (char*)work;
@@ -1375,6 +1353,10 @@ Work carve(const sla_mat& A, void* work) {
   const size_t n = (size_t)A.n();
   w.st = (SolverState*)p;
   p += align_up(sizeof(SolverState));
+  w.lcnt = (int*)p;
+  p += align_up((size_t)long_rows_bound(A) * sizeof(int));
+  w.lpart = (double*)p;
+  p += align_up((size_t)long_part_bound(A) * sizeof(double));
   const size_t ps = align_up(partial_slots(A) * sizeof(double));
   w.psig = (double*)p;
   p += ps;
@@ -1441,19 +1423,20 @@ bool use_fused(const sla_mat& A) {
 template <typename T>
 sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, T* x, double rtol,
                     int maxit, void* work, hipStream_t s, sla_solve_info* info, double* hist_a,
-                    double* hist_b, int hist_len) {
+                    double* hist_b, int hist_len, PollSlot* slot, bool quiet) {
   const int n = (int)A.n();
   Work w = carve(A, work);
   T *P[2] = {(T*)w.vec[0], (T*)w.vec[1]}, *R[2] = {(T*)w.vec[2], (T*)w.vec[3]};
   T *q = (T*)w.vec[4], *t = (T*)w.vec[5], *z = (T*)w.vec[6];
-  const LongScratch lsA = long_scratch(A, false), lsG = long_scratch(G, false),
-                    lsT = long_scratch(G, true);
+  // the three products run one after another on s, so they share one
+  // long-row scratch (every ticket is back at 0 when a product ends)
+  const LongScratch lsA{w.lpart, w.lcnt}, lsG = lsA, lsT = lsA;
   const int ntA = view_tiles(A, A.fwd), ntG = view_tiles(G, G.fwd), ntT = view_tiles(G, G.tr);
   const int grid = step_grid(std::max(ntA, std::max(ntG, ntT)));
   const int npA = grid + A.fwd.nlong_rows, npG = grid + G.fwd.nlong_rows,
             npT = grid + G.tr.nlong_rows;
 
-  SLA_HIP(hipMemsetAsync(w.st, 0, sizeof(SolverState), s));
+  SLA_HIP(hipMemsetAsync(w.st, 0, zeroed_bytes(A), s));
   const MallPlan plan = mall_plan(A, G);
   const bool fused = use_fused(A);
 
@@ -1509,7 +1492,7 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
   }
 
   Recorder rec;
-  rec.mask = g_prof_mask.load();
+  rec.mask = quiet ? 0 : g_prof_mask.load();
   rec.every = g_prof_every.load();
   rec.s = s;
 
@@ -1528,14 +1511,10 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
   SLA_HIP((launch_step<T, M_G0>(G, aG, grid, s, plan.nt_g)));
   rec.end(e0, 2, 0);
 
-  std::unique_lock<std::mutex> lk(g_poll_mu);
-  sla_status pst = poll_init();
-  if (pst != SLA_OK) return pst;
-  struct Pending {
-    int slot;
-    int kend;
-  };
-  std::deque<Pending> pend;
+  // exit-flag copies in flight: a ring of at most two pending batches
+  SolverState* hst = (SolverState*)slot->host;
+  int pend[3];
+  int npend = 0, pfirst = 0;
   int next_slot = 0;
   const int B = batch_iters();
   int k = 1;
@@ -1591,34 +1570,36 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
         SLA_HIP((launch_step<T, M_G>(G, aG, grid, s, plan.nt_g)));
         rec.end(eg, 2, kk);
       }
-      const int slot = next_slot;
+      const int ps = next_slot;
       next_slot = (next_slot + 1) % 3;
-      SLA_HIP(hipMemcpyAsync(&g_host_state[slot], w.st, 16, hipMemcpyDeviceToHost, s));
-      SLA_HIP(hipEventRecord(g_poll_ev[slot], s));
-      pend.push_back({slot, kend});
+      SLA_HIP(hipMemcpyAsync(&hst[ps], w.st, 16, hipMemcpyDeviceToHost, s));
+      SLA_HIP(hipEventRecord(slot->ev[ps], s));
+      pend[(pfirst + npend) % 3] = ps;
+      ++npend;
       k = kend + 1;
     }
-    if (pend.size() >= 2 || (k > maxit && !pend.empty())) {
-      const Pending p = pend.front();
-      pend.pop_front();
-      SLA_HIP(hipEventSynchronize(g_poll_ev[p.slot]));
-      if (g_host_state[p.slot].done) finished = true;
+    if (npend >= 2 || (k > maxit && npend > 0)) {
+      const int ps = pend[pfirst];
+      pfirst = (pfirst + 1) % 3;
+      --npend;
+      SLA_HIP(hipEventSynchronize(slot->ev[ps]));
+      if (hst[ps].done) finished = true;
     }
-    if (k > maxit && pend.empty()) finished = true;
+    if (k > maxit && npend == 0) finished = true;
   }
-  while (!pend.empty()) {
-    SLA_HIP(hipEventSynchronize(g_poll_ev[pend.front().slot]));
-    pend.pop_front();
+  while (npend > 0) {
+    SLA_HIP(hipEventSynchronize(slot->ev[pend[pfirst]]));
+    pfirst = (pfirst + 1) % 3;
+    --npend;
   }
   hipLaunchKernelGGL(finalize_x<T>, dim3(std::max(1, std::min((n + kWG - 1) / kWG, 4096))),
                      dim3(kWG), 0, s, (const SolverState*)w.st, x, (const T*)P[0],
                      (const T*)P[1], n);
   SLA_HIP(hipGetLastError());
-  SolverState* hs = &g_host_state[3];
+  SolverState* hs = &hst[3];
   SLA_HIP(hipMemcpyAsync(hs, w.st, sizeof(SolverState), hipMemcpyDeviceToHost, s));
   SLA_HIP(hipStreamSynchronize(s));
   const SolverState fin = *hs;
-  lk.unlock();
 
   int iters = 0;
   const sla_status st = exit_status(fin, info, &iters);
@@ -1646,7 +1627,7 @@ bool small_ok(const sla_mat& A, const sla_mat& G) {
 template <typename T>
 sla_status small_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, T* x,
                       double rtol, int maxit, void* work, hipStream_t s, sla_solve_info* info,
-                      double* hist_a, double* hist_b, int hist_len) {
+                      double* hist_a, double* hist_b, int hist_len, PollSlot* slot) {
   Work w = carve(A, work);
   SmallArgs<T> a{};
   auto set = [](const MatView& v, const T*& val, const int32_t*& col, const int16_t*& d,
@@ -1672,14 +1653,10 @@ sla_status small_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b
   a.hist_len = hist_len;
   hipLaunchKernelGGL((small_pcg<T>), dim3(1), dim3(kSmallN), 0, s, a);
   SLA_HIP(hipGetLastError());
-  std::unique_lock<std::mutex> lk(g_poll_mu);
-  sla_status pst = poll_init();
-  if (pst != SLA_OK) return pst;
-  SolverState* hs = &g_host_state[3];
+  SolverState* hs = (SolverState*)slot->host + 3;
   SLA_HIP(hipMemcpyAsync(hs, w.st, sizeof(SolverState), hipMemcpyDeviceToHost, s));
   SLA_HIP(hipStreamSynchronize(s));
   const SolverState fin = *hs;
-  lk.unlock();
   return exit_status(fin, info, nullptr);
 }
 }  // namespace
@@ -1688,10 +1665,26 @@ sla_status small_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b
 // Internal API used by api.cpp
 // ---------------------------------------------------------------------------
 
+LongScratch long_scratch_of(const sla_mat& m, bool transpose) {
+  // slots of the handle's owned[] array (see api.cpp)
+  const int base = transpose ? 4 : 2;
+  return LongScratch{(double*)m.owned[base], (int*)m.owned[base + 1]};
+}
+
+// A row longer than kLdsCap holds more than kLdsCap of the nnz entries, and
+// splits into at most len / kLongChunk + 1 chunks.
+int64_t long_rows_bound(const sla_mat& A) {
+  return std::max<int64_t>(std::max(A.fwd.nlong_rows, A.tr.nlong_rows), A.nnz() / kLdsCap + 1);
+}
+int64_t long_part_bound(const sla_mat& A) {
+  return std::max<int64_t>(std::max(A.fwd.n_long_part, A.tr.n_long_part),
+                           A.nnz() / kLongChunk + long_rows_bound(A) + 1);
+}
+
 size_t workspace_base(const sla_mat& A) {
   const size_t es = A.dtype == SLA_F64 ? 8 : 4;
-  return align_up(sizeof(SolverState)) + 3 * align_up(partial_slots(A) * sizeof(double)) +
-         7 * align_up((size_t)A.n() * es);
+  return zeroed_bytes(A) + align_up((size_t)long_part_bound(A) * sizeof(double)) +
+         3 * align_up(partial_slots(A) * sizeof(double)) + 7 * align_up((size_t)A.n() * es);
 }
 
 size_t workspace_bytes(const sla_mat& A) {
@@ -1699,7 +1692,8 @@ size_t workspace_bytes(const sla_mat& A) {
   return workspace_base(A) + (A.ord_want ? 2 * align_up((size_t)A.n() * es) : 0);
 }
 
-sla_status spmv(const sla_mat& A, bool transpose, const void* x, void* y, hipStream_t s) {
+sla_status spmv(const sla_mat& A, bool transpose, const void* x, void* y, hipStream_t s,
+                const LongScratch* scratch) {
   const MatView& v = transpose ? A.tr : A.fwd;
   if (A.n() == 0) return SLA_OK;
   hipEvent_t ea = nullptr, eb = nullptr;
@@ -1713,7 +1707,7 @@ sla_status spmv(const sla_mat& A, bool transpose, const void* x, void* y, hipStr
     }
     SLA_HIP(hipEventRecord(ea, s));
   }
-  const LongScratch ls = long_scratch(A, transpose);
+  const LongScratch ls = scratch ? *scratch : long_scratch_of(A, transpose);
   const bool nt = matrix_bytes(A) > mall_budget();
   if (A.dtype == SLA_F64) {
     StepArgs<double> a{};
@@ -1738,12 +1732,12 @@ sla_status spmv(const sla_mat& A, bool transpose, const void* x, void* y, hipStr
   return SLA_OK;
 }
 
-// z = G (G^T r) + eps r with t = G^T r in caller-provided memory.
+// z = G (G^T r) + eps r with t = G^T r in caller-provided memory; both
+// products use the long-row scratch ls (tickets at zero).
 static sla_status precond_into(const sla_mat& G, double eps, const void* r, void* t, void* z,
-                               hipStream_t s) {
-  sla_status st = spmv(G, true, r, t, s);
+                               const LongScratch& ls, hipStream_t s) {
+  sla_status st = spmv(G, true, r, t, s, &ls);
   if (st != SLA_OK) return st;
-  const LongScratch ls = long_scratch(G, false);
   const bool nt = matrix_bytes(G) > mall_budget();
   if (G.dtype == SLA_F64) {
     StepArgs<double> a{};
@@ -1769,22 +1763,28 @@ sla_status precond_apply(const sla_mat& G, double eps, const void* r, void* z, v
                          size_t, hipStream_t s) {
   if (G.n() == 0) return SLA_OK;
   Work w = carve(G, work);
-  return precond_into(G, eps, r, w.vec[5], z, s);
+  SLA_HIP(hipMemsetAsync(w.st, 0, zeroed_bytes(G), s));
+  return precond_into(G, eps, r, w.vec[5], z, LongScratch{w.lpart, w.lcnt}, s);
 }
 
 sla_status sai_loss(const sla_mat& A, const sla_mat& G, double eps, const void* probes,
                     int32_t nprobe, double scale, void* work, double* out, hipStream_t s) {
   const int64_t n = A.n();
   if (nprobe == 0) return SLA_OK;
-  Work w = carve(A, work);
+  // the workspace holds max(workspace_bytes(A), workspace_bytes(G)): carve
+  // it for the operator with more entries, whose long-row bounds cover both
+  const sla_mat& big = A.nnz() >= G.nnz() ? A : G;
+  Work w = carve(big, work);
+  SLA_HIP(hipMemsetAsync(w.st, 0, zeroed_bytes(big), s));
+  const LongScratch ls{w.lpart, w.lcnt};
   const size_t es = A.dtype == SLA_F64 ? 8 : 4;
   const int grid = (int)std::min<int64_t>(max_grid(), std::max<int64_t>(1, (n + kWG - 1) / kWG));
   for (int32_t j = 0; j < nprobe; ++j) {
     const void* wj = (const char*)probes + (size_t)j * (size_t)n * es;
     if (n > 0) {
-      sla_status st = precond_into(G, eps, wj, w.vec[5], w.vec[0], s);
+      sla_status st = precond_into(G, eps, wj, w.vec[5], w.vec[0], ls, s);
       if (st != SLA_OK) return st;
-      st = spmv(A, false, w.vec[0], w.vec[1], s);
+      st = spmv(A, false, w.vec[0], w.vec[1], s, &ls);
       if (st != SLA_OK) return st;
     }
     if (A.dtype == SLA_F64)
@@ -1802,23 +1802,30 @@ sla_status sai_loss(const sla_mat& A, const sla_mat& G, double eps, const void* 
 
 sla_status pcg_solve(const sla_mat& A, const sla_mat& G, double eps, const void* b, void* x,
                      double rtol, int32_t maxit, void* work, size_t, hipStream_t s,
-                     sla_solve_info* info, double* hist_a, double* hist_b, int32_t hist_len) {
+                     sla_solve_info* info, double* hist_a, double* hist_b, int32_t hist_len,
+                     PollSlot* slot, bool quiet) {
   if (A.n() == 0) {
     if (info) *info = sla_solve_info{0, 1, 0.0, 0.0};
     return SLA_OK;
   }
+  PollLease lease;
+  if (!slot) {
+    sla_status st = poll_acquire(&lease.p);
+    if (st != SLA_OK) return st;
+    slot = lease.p;
+  }
   if (small_ok(A, G)) {
     if (A.dtype == SLA_F64)
       return small_impl<double>(A, G, eps, (const double*)b, (double*)x, rtol, maxit, work, s,
-                                info, hist_a, hist_b, hist_len);
+                                info, hist_a, hist_b, hist_len, slot);
     return small_impl<float>(A, G, eps, (const float*)b, (float*)x, rtol, maxit, work, s, info,
-                             hist_a, hist_b, hist_len);
+                             hist_a, hist_b, hist_len, slot);
   }
   if (A.dtype == SLA_F64)
     return pcg_impl<double>(A, G, eps, (const double*)b, (double*)x, rtol, maxit, work, s, info,
-                            hist_a, hist_b, hist_len);
+                            hist_a, hist_b, hist_len, slot, quiet);
   return pcg_impl<float>(A, G, eps, (const float*)b, (float*)x, rtol, maxit, work, s, info,
-                         hist_a, hist_b, hist_len);
+                         hist_a, hist_b, hist_len, slot, quiet);
 }
 
 bool small_applies(const sla_mat& A, const sla_mat& G) { return small_ok(A, G); }

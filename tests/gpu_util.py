@@ -73,21 +73,38 @@ def oracle_self_sensitivity(A, G, eps, b, rtol, maxit, seed=0):
     return rel(x2, x1), abs(r2 - r1) / max(abs(r1), 1e-300)
 
 
+# Cases that passed through the oracle-spread reading rather than the fixed
+# gates; conftest prints them at the end of the run.
+FALLBACKS = []
+
+
 def assert_solve_matches(A, G, eps, b, rtol, maxit, it_g, x_g, it_r, x_r, strict, what=""):
     """The GPU solve against the oracle's: iterations within 2% and x within
     1e-8.  Where strict is False (the test matrices beyond the benchmark
-    workloads), a solve outside those gates must lie within the oracle's own
-    spread under one-ulp perturbations of b (plus one iteration, ten times
-    its change of x): on systems whose residual stagnates near rtol the
-    stopping iteration is decided by rounding, and any change of summation
-    order moves it."""
+    workloads), a gate that fails is re-taken against the oracle's own spread
+    under one-ulp perturbations of b -- but only when that spread is itself
+    wider than the fixed gate: on systems whose residual stagnates near rtol
+    the stopping iteration is decided by rounding, and any change of
+    summation order moves it.  The iteration count must then lie within the
+    oracle's range (+-1) and x within ten times its largest change.  Every
+    case that takes this route is printed and recorded in FALLBACKS."""
     err = rel(x_g, x_r)
-    if iters_close(it_g, it_r) and err <= 1e-8:
+    it_ok, x_ok = iters_close(it_g, it_r), err <= 1e-8
+    if it_ok and x_ok:
         return
     assert not strict, (what, "iterations", it_g, it_r, "x", err)
     lo, hi, dx = oracle_spread(A, G, eps, b, rtol, maxit)
-    assert lo - 1 <= it_g <= hi + 1, (what, "iterations", it_g, it_r, (lo, hi))
-    assert err <= max(1e-8, 10 * dx), (what, "x", err, dx)
+    wide_it = not (iters_close(lo, it_r) and iters_close(hi, it_r))
+    wide_x = dx > 1e-8
+    rec = dict(what=what, it_gpu=it_g, it_ref=it_r, spread=(lo, hi), x_err=err, x_spread=dx)
+    if not it_ok:
+        assert wide_it, (what, "iterations outside 2% while the oracle's spread is inside it", rec)
+        assert lo - 1 <= it_g <= hi + 1, (what, "iterations outside the oracle's spread", rec)
+    if not x_ok:
+        assert wide_x, (what, "x outside 1e-8 while the oracle's spread is inside it", rec)
+        assert err <= 10 * dx, (what, "x outside ten times the oracle's spread", rec)
+    FALLBACKS.append(rec)
+    print("[fallback]", rec, flush=True)
 
 
 def oracle_spread(A, G, eps, b, rtol, maxit, nsamp=6):

@@ -572,10 +572,44 @@ def pin_adjoint_multi(lib):
     assert abs(fd - an) <= 1e-6 * abs(an), ("directional", fd, an)
 
 
+# ---------------------------------------------------------------------------
+# Kaporin's condition number (dense, small systems)
+# ---------------------------------------------------------------------------
+
+def pin_kaporin(lib, kaporin=None):
+    """Kaporin's number of an SPD operator, (trace / n) / det^(1/n): 1 for any
+    multiple of I, (a + b) / (2 sqrt(a b)) for two eigenvalues (1.25 for
+    diag(1, 4)), unchanged by scaling, at least 1 (AM-GM), and on the
+    preconditioned Poisson operator M^-1 A equal to the same ratio formed from
+    the trace and log-determinant of the dense product (no eigenvalues)."""
+    kap = kaporin or oracle.kaporin_number
+    for c in (1.0, 0.3, 7.5):
+        assert abs(kap(np.full(5, c)) - 1.0) <= 1e-15, ("multiple of I", c)
+    assert abs(kap(np.array([1.0, 4.0])) - 1.25) <= 1e-15, "diag(1, 4)"
+    rng = np.random.default_rng(81)
+    for _ in range(4):
+        a, b = rng.uniform(0.1, 10.0, 2)
+        assert abs(kap(np.array([a, b])) - (a + b) / (2 * math.sqrt(a * b))) <= 1e-14, "two"
+    e = rng.uniform(0.01, 3.0, 17)
+    assert abs(kap(123.0 * e) - kap(e)) <= 1e-13 * kap(e), "scale invariance"
+    assert kap(e) >= 1.0, "AM-GM"
+    p = I.make_problem(0, size=5)                      # n = 25
+    Ad = p.A.to_dense()
+    Gd = p.G.to_dense()
+    Minv = Gd @ Gd.T + p.eps * np.eye(p.A.n)
+    S = Minv @ Ad
+    _, logdet_m = np.linalg.slogdet(Minv)
+    _, logdet_a = np.linalg.slogdet(Ad)
+    n = p.A.n
+    ref = (np.trace(S) / n) / math.exp((logdet_m + logdet_a) / n)
+    got = kap(oracle.dense_spectrum(p.A, p.G, p.eps))
+    assert abs(got - ref) <= 1e-10 * ref, ("trace / det form", got, ref)
+
+
 ALL_PINS = [
     pin_spmv_bruteforce, pin_spmv_bsr_dense, pin_spmv_eigenpairs, pin_transpose, pin_precond,
     pin_pcg_cholesky, pin_pcg_galerkin, pin_pcg_eigen, pin_pcg_cg_equivalence, pin_pcg_scipy,
     pin_pcg_edges, pin_adjoint_fd_b, pin_adjoint_fd_entries, pin_adjoint_directional,
     pin_adjoint_identities, pin_lanczos_diagonal, pin_lanczos_spectrum, pin_sai_loss,
-    pin_pcg_multi, pin_adjoint_multi,
+    pin_pcg_multi, pin_adjoint_multi, pin_kaporin,
 ]

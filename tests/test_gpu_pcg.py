@@ -5,6 +5,8 @@ the memory property of the adjoint.
 Gates: solution ||x_gpu - x_ref|| / ||x_ref|| <= 1e-8, iteration count within
 2 % (at least 1), adjoint gradients dL/db and dL/dA within 1e-7 relative.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -187,9 +189,22 @@ def test_invalid_arguments():
         B.sla_pcg_solve(A, G, p.eps, b, work=small)
     assert e.value.status == B.ERR_INVALID_ARG
     other = create(problem("poisson2d_37").G, transpose=True)
-    with pytest.raises(B.SlaError) as e:
-        B.sla_pcg_solve(A, other, p.eps, b)
-    assert e.value.status == B.ERR_INVALID_ARG
+    with pytest.raises(ValueError):
+        B.sla_pcg_solve(A, other, p.eps, b)      # the binding's check
+    # the library's own check, through the raw C ABI
+    x = torch.empty_like(b)
+    work = B.workspace(A)
+    si = B.SolveInfo()
+    st = B.lib().sla_pcg_solve(A.handle, other.handle, p.eps, B._ptr(b), B._ptr(x), 1e-10, 10,
+                               B._ptr(work), work.numel(), None, ctypes.byref(si))
+    assert st == B.ERR_INVALID_ARG
+    # lambda (grad_b) may not share memory with x in the adjoint
+    x, _ = B.sla_pcg_solve(A, G, p.eps, b, rtol=p.rtol, maxit=p.maxit)
+    gv = torch.empty(p.A.nnz, dtype=torch.float64, device=DEV)
+    st = B.lib().sla_pcg_adjoint(A.handle, G.handle, p.eps, B._ptr(x), B._ptr(b), B._ptr(x),
+                                 B._ptr(gv), 1e-10, 10, B._ptr(work), work.numel(), None,
+                                 ctypes.byref(si))
+    assert st == B.ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("key", ["c0", "irregular_long_rows", "bsr_elastic_6", "powerlaw_20k"])

@@ -2,6 +2,7 @@
 at least one pin catches each of them.  The shipped oracle is never modified."""
 import os
 
+import numpy as np
 import pytest
 
 import oracle
@@ -92,3 +93,28 @@ def test_pins_catch_planted_mistake(tmp_path, name, old, new):
         except Exception as e:  # a crash of the mutant is also a catch
             caught.append(f"{pin.__name__} ({type(e).__name__})")
     assert caught, f"no pin caught: {name}"
+
+
+# Plausible mistakes in Kaporin's number (a numpy function of the oracle
+# package, so the mutants are Python functions rather than copies of oracle.c).
+KAPORIN_MUTANTS = [
+    ("harmonic instead of geometric mean",
+     lambda e: float(np.mean(e) * np.mean(1.0 / np.asarray(e)))),
+    ("ratio inverted",
+     lambda e: float(np.exp(np.mean(np.log(e))) / np.mean(e))),
+    ("sum instead of mean in the numerator",
+     lambda e: float(np.sum(e) / np.exp(np.mean(np.log(e))))),
+    ("log of the geometric mean used without exp",
+     lambda e: float(np.mean(e) / np.mean(np.log(e)))),
+    ("extreme-eigenvalue ratio",
+     lambda e: float(np.max(e) / np.min(e))),
+    ("square root of the ratio",
+     lambda e: float(np.sqrt(np.mean(e) / np.exp(np.mean(np.log(e)))))),
+]
+
+
+@pytest.mark.parametrize("name,fn", KAPORIN_MUTANTS, ids=[m[0] for m in KAPORIN_MUTANTS])
+def test_kaporin_pin_catches_planted_mistake(name, fn):
+    with pytest.raises(AssertionError):
+        with np.errstate(all="ignore"):
+            pins.pin_kaporin(oracle.load(), kaporin=fn)
