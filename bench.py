@@ -32,8 +32,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "PCG iters/sec + SpMV HBM GB/s (% of peak), 3D Poisson 128^3 fp64, 1 GPU"
 PROF_EVERY = 7
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_a_step_poisson3d_128.json")
-KERNEL_SRC = os.path.join(ROOT, "preconditioned_cg_solver_amd", "csrc", "solver.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "preconditioned_cg_solver_amd", "csrc", f)
+               for f in ("solver.hip", "multi.hip", "device_util.h")]
 
 
 def log(*a):
@@ -137,47 +137,96 @@ def moved_bytes_a_step(A, n, sv=8):
     return slots * (sv + col_bytes) + 4 * (ns + 1) + 6 * sv * n
 
 
-def traffic_if_current():
-    """HBM bytes per A-step launch from the committed rocprofv3 counter runs,
-    if they were taken on the current kernel source; else None."""
+def kernel_source_sha() -> str:
+    """SHA-256 over the sources of the counted kernels (the counters of a
+    workload are only used while these are unchanged)."""
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+
+
+def traffic_if_current(workload: str):
+    """Per-kernel HBM bytes per launch of a workload from the committed
+    rocprofv3 counter runs, if they were taken on the current kernel sources;
+    else None."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))
-        src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-        if rec.get("kernel_source_sha256") != src:
+        rec = json.load(open(traffic_file(workload)))
+        if rec.get("kernel_source_sha256") != kernel_source_sha():
             return None
-        return rec.get("bytes_per_launch")
+        return rec
     except (OSError, ValueError):
         return None
+
+
+def kernel_bytes(rec, pattern):
+    """Counter bytes per launch of the first kernel whose key matches the regex
+    `pattern` in a traffic record (None if no kernel matches)."""
+    if not rec:
+        return None
+    for k, v in rec["kernels"].items():
+        if re.match(pattern, k):
+            return v["bytes"]
+    return None
 
 
 STEP_NAMES = {0: "plain SpMV y = A x (matrix from HBM)",
               1: "A step, iteration 1", 2: "A step (q = A p, p and x updates)",
               3: "G^T step, start-up", 4: "G^T step (t = G^T r, r update)",
-              5: "G step, start-up", 6: "G step (z = G t + eps r)"}
+              5: "G step, start-up", 6: "G step (z = G t + eps r)",
+              7: "preconditioner tail (z = G t + eps r, no solver state)",
+              8: "A product (separate form: q = A p, p.q)",
+              9: "G^T product (separate form: t = G^T r)"}
+MSTEP_NAMES = {0: "Y = M X (products of several vectors)", 1: "A step, iteration 1",
+               2: "A step", 3: "G^T step", 4: "G step, start-up", 5: "G step",
+               6: "A product (separate form)", 7: "G^T product (separate form)"}
 
 
 def _counter_rows(run_dir):
     import csv
     import glob
-    import re
     out = {}
     for path in sorted(glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"),
                                  recursive=True)):
         for r in csv.DictReader(open(path)):
-            nm = r["Kernel_Name"].replace("void ", "").replace("sla::(anonymous namespace)::", "")
-            nm = nm.replace("sla::", "")
-            m = re.match(r"([\w:]+)(<[^>]*>)?", nm)
-            key = (m.group(1) + (m.group(2) or "")) if m else nm[:48]
+            key = _kernel_key(r["Kernel_Name"])
             out.setdefault(key, []).append((float(r["Counter_Value"]), int(r.get("Grid_Size", 0))))
     return out
 
 
-def summarize_counters(fetch_dir, write_dir):
-    """Turn the two rocprofv3 --pmc runs of --counters-workload (FETCH_SIZE, then
-    WRITE_SIZE, KiB per dispatch) into the traffic summary and the A-step record
-    that the benchmark reports; the 256 MiB copy calibrates both counters."""
-    import re
+def _kernel_key(nm):
+    nm = nm.replace("void ", "").replace("sla::(anonymous namespace)::", "").replace("sla::", "")
+    m = re.match(r"([\w:]+)(<[^>]*>)?", nm)
+    return (m.group(1) + (m.group(2) or "")) if m else nm[:48]
+
+
+def _describe(key):
+    m = re.match(r"(sell_step|csr_step|bsell_step|bsr3_step)<\w+, (\d+)", key)
+    if m:
+        return STEP_NAMES.get(int(m.group(2)), m.group(2))
+    m = re.match(r"(msell_step|mbsell_step|mtile_step|mrow_step)<\w+, (\d+), (\d+)", key)
+    if m:
+        return f"{MSTEP_NAMES.get(int(m.group(2)), m.group(2))}, K = {m.group(3)}"
+    return {"vec_p_update": "p and x update pass", "vec_r_update": "r update pass, ||r||^2",
+            "csr_grad": "dL/dA on the CSR pattern", "bsr3_grad": "dL/dA on the BSR pattern",
+            "finalize_x": "last x update", "mvec_p": "P and X update pass (K columns)",
+            "mvec_r": "R update pass (K columns)", "mgrad": "summed dL/dA (K columns)",
+            "minit": "start-up (K columns)"}.get(key.split("<")[0], "")
+
+
+def summarize_counters(fetch_dir, write_dir, l2_dir=None, workload="poisson3d_128",
+                       run_args="--counters-workload", out_dir=None):
+    """Turn the rocprofv3 --pmc runs of --counters-workload (FETCH_SIZE, then
+    WRITE_SIZE, KiB per dispatch; optionally TCC_HIT_sum and TCC_MISS_sum) into
+    the per-kernel traffic summary profiles/traffic_<workload>.md and the record
+    profiles/traffic_<workload>.json that the benchmark reads; the 256 MiB copy
+    calibrates both byte counters."""
     fetch, write = _counter_rows(fetch_dir), _counter_rows(write_dir)
+    l2 = _counter_rows(l2_dir) if l2_dir else {}
     copy_kib = 256 * 1024.0
 
     def calib(rows):
@@ -185,44 +234,71 @@ def summarize_counters(fetch_dir, write_dir):
         big = [v for v in vals if v > 0.25 * copy_kib]
         return copy_kib / statistics.median(big)
     fs, ws = calib(fetch), calib(write)
-    src_sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-    lines = ["| kernel | step | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB (scaled) "
-             "| written MB | total MB |", "|---|---|---|---|---|---|---|---|"]
-    a_rec = None
-    for k in sorted(fetch):
-        m = re.match(r"(sell_step|csr_step|bsell_step|bsr3_step)<double, (\d+),", k)
-        if not m or k not in write:
+    kernels = {}
+    for k in fetch:
+        if k not in write or "copyBuffer" in k or "elementwise" in k.lower() or k.startswith("at::"):
             continue
-        mode = int(m.group(2))
         fk = statistics.fmean(v for v, _ in fetch[k])
         wk = statistics.fmean(v for v, _ in write[k])
-        rb, wb = fk * 1024 * fs, wk * 1024 * ws
-        lines.append(f"| `{k}` | {STEP_NAMES.get(mode, mode)} | {len(fetch[k])} | {fk:,.1f} | "
-                     f"{wk:,.1f} | {rb / 1e6:.1f} | {wb / 1e6:.1f} | {(rb + wb) / 1e6:.1f} |")
-        if mode == 2:
-            a_rec = {"kernel": k, "workload": "poisson3d_128 fp64", "kernel_source_sha256": src_sha,
-                     "fetch_scale": fs, "write_scale": ws, "fetch_kib_raw": fk,
-                     "write_kib_raw": wk, "fetch_bytes": rb, "write_bytes": wb,
-                     "bytes_per_launch": rb + wb, "launches_averaged": len(fetch[k])}
-    cmd = "rocprofv3 --pmc {c} --output-format csv -d {d} -o pmc -- python -u bench.py " \
-          "--counters-workload"
-    md = ["# HBM traffic per launch of the PCG kernels, 3D Poisson 128^3 fp64", "",
-          "Counters from two rocprofv3 runs of the benchmark's counter workload (a 256 MiB",
-          "copy for calibration, then 20 forward and 20 adjoint PCG iterations on the",
-          "128^3 input, then 8 plain SpMVs alternating between two copies of A so that",
-          "each streams its matrix from HBM).  FETCH_SIZE and WRITE_SIZE are KiB per",
-          "dispatch; the copy of known size (256 MiB read, 256 MiB written) calibrates",
-          f"fetched bytes by {fs:.3f} and written bytes by {ws:.3f}.", "",
-          "Commands (from the repository root, `export TMPDIR=/tmp`):", "",
-          "    " + cmd.format(c="FETCH_SIZE", d=fetch_dir),
-          "    " + cmd.format(c="WRITE_SIZE", d=write_dir),
-          f"    python bench.py --counter-summary {fetch_dir} {write_dir}", "", *lines, "",
-          f"Kernel source: preconditioned_cg_solver_amd/csrc/solver.hip sha256 {src_sha}.", ""]
-    with open(os.path.join(ROOT, "profiles", "traffic_poisson3d_128.md"), "w") as f:
+        rec = {"dispatches": len(fetch[k]), "fetch_kib_raw": fk, "write_kib_raw": wk,
+               "fetch_bytes": fk * 1024 * fs, "write_bytes": wk * 1024 * ws}
+        rec["bytes"] = rec["fetch_bytes"] + rec["write_bytes"]
+        kernels[k] = rec
+    # L2 (TCC) hit rate: the HIT and MISS runs record one row per counter and dispatch
+    if l2:
+        import csv
+        import glob
+        hm = {}
+        for path in glob.glob(os.path.join(l2_dir, "**", "*counter_collection.csv"),
+                              recursive=True):
+            for r in csv.DictReader(open(path)):
+                k = _kernel_key(r["Kernel_Name"])
+                d = hm.setdefault(k, {"hit": 0.0, "miss": 0.0})
+                name = r.get("Counter_Name", "")
+                if "HIT" in name:
+                    d["hit"] += float(r["Counter_Value"])
+                elif "MISS" in name:
+                    d["miss"] += float(r["Counter_Value"])
+        for k, d in hm.items():
+            if k in kernels and d["hit"] + d["miss"] > 0:
+                kernels[k]["l2_hit_rate"] = d["hit"] / (d["hit"] + d["miss"])
+    src_sha = kernel_source_sha()
+    lines = ["| kernel | role | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB (scaled) "
+             "| written MB | total MB | L2 hit |", "|---|---|---|---|---|---|---|---|---|"]
+    for k, r in sorted(kernels.items(), key=lambda kv: -kv[1]["bytes"] * kv[1]["dispatches"]):
+        if r["bytes"] < 1e5:
+            continue
+        hit = f"{100 * r['l2_hit_rate']:.1f}%" if "l2_hit_rate" in r else "-"
+        lines.append(f"| `{k}` | {_describe(k)} | {r['dispatches']} | {r['fetch_kib_raw']:,.1f} | "
+                     f"{r['write_kib_raw']:,.1f} | {r['fetch_bytes'] / 1e6:.1f} | "
+                     f"{r['write_bytes'] / 1e6:.1f} | {r['bytes'] / 1e6:.1f} | {hit} |")
+    cmd = ("timeout -s KILL 300 rocprofv3 --pmc {c} --output-format csv -d {d} -o pmc -- "
+           f"python -u bench.py {run_args}")
+    cmds = ["    " + cmd.format(c="FETCH_SIZE", d=fetch_dir),
+            "    " + cmd.format(c="WRITE_SIZE", d=write_dir)]
+    if l2_dir:
+        cmds.append("    " + cmd.format(c="TCC_HIT_sum TCC_MISS_sum", d=l2_dir))
+    md = [f"# HBM traffic per launch of the PCG kernels, {workload}", "",
+          "Counters from rocprofv3 --pmc runs of the benchmark's counter workload: a 256 MiB",
+          "copy for calibration, then 20 forward and 20 adjoint PCG iterations (with dL/dA),",
+          "20 lock-step iterations of each several-right-hand-side count, and 8 plain SpMVs",
+          "alternating between two copies of A so that each streams its matrix from HBM.",
+          "FETCH_SIZE and WRITE_SIZE are KiB per dispatch (averaged over the dispatches of",
+          "each kernel); the copy of known size (256 MiB read, 256 MiB written) calibrates",
+          f"fetched bytes by {fs:.3f} and written bytes by {ws:.3f}.  FETCH_SIZE counts what",
+          "L2 fetches from the memory side, so Infinity Cache hits are included: an upper",
+          "bound on HBM reads.  L2 hit = TCC_HIT / (TCC_HIT + TCC_MISS) where taken.", "",
+          "Commands (from the repository root, `export TMPDIR=/tmp`):", "", *cmds,
+          f"    python bench.py --counter-summary {fetch_dir} {write_dir}"
+          + (f" --l2-dir {l2_dir}" if l2_dir else "")
+          + f" --workload-name {workload} --counters-args '{run_args}'", "", *lines, "",
+          "Kernel sources (solver.hip, multi.hip, device_util.h) sha256 " + src_sha + ".", ""]
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    with open(os.path.join(out_dir, f"traffic_{workload}.md"), "w") as f:
         f.write("\n".join(md))
-    if a_rec is not None:
-        with open(TRAFFIC_FILE, "w") as f:
-            json.dump(a_rec, f, indent=1)
+    with open(os.path.join(out_dir, f"traffic_{workload}.json"), "w") as f:
+        json.dump({"workload": workload, "kernel_source_sha256": src_sha, "fetch_scale": fs,
+                   "write_scale": ws, "kernels": kernels}, f, indent=1)
     print("\n".join(lines))
 
 
@@ -301,6 +377,19 @@ def summarize_trace(trace_dir, bench_json=None, trace_args="--steps 2 --warmup 1
     print("\n".join(lines))
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(p, w, min_seconds, expected_iters):
     """The oracle on the host cores doing the benchmark's step minus the handle
     set-up: the full forward PCG solve and the full adjoint solve on the same
@@ -308,10 +397,13 @@ def cpu_baseline(p, w, min_seconds, expected_iters):
     When one such pair would take more than three times min_seconds (the large
     workloads), both solves are cut at the same iteration cap instead, sized from
     a 3-iteration probe so that the pair takes about min_seconds: the rate is
-    then iterations per second over truncated solves, said so in the sample."""
+    then iterations per second over truncated solves, said so in the sample.
+    Then the same oracle on ONE thread pinned to one core of the affinity mask:
+    a forward solve cut at the iteration count that takes about min_seconds / 2
+    (the oracle's results are bitwise the same for any thread count)."""
     import oracle
-    log(f"cpu oracle: forward + adjoint solves for >= {min_seconds:.0f} s, "
-        f"{oracle.num_threads()} threads")
+    threads = oracle.num_threads()
+    log(f"cpu oracle: forward + adjoint solves for >= {min_seconds:.0f} s, {threads} threads")
     t0 = time.perf_counter()
     _, _, it, _ = oracle.pcg(p.A, p.G, p.eps, p.b, p.rtol, min(3, p.maxit))
     per_it = (time.perf_counter() - t0) / max(it, 1)
@@ -330,9 +422,34 @@ def cpu_baseline(p, w, min_seconds, expected_iters):
     what = ("full forward PCG solve + full adjoint solve with dL/dA" if cap == p.maxit else
             f"forward PCG solve + adjoint solve with dL/dA, each cut at {cap} iterations "
             f"(the full pair runs {expected_iters} iterations on the GPU)")
-    return {"value": its / dt, "unit": "iters/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{reps} x ({what}) on the same {p.name} input, {its} iterations in "
-                      f"{dt:.1f} s (each solve includes the oracle's own G^T build)"}
+    out = {"value": its / dt, "unit": "iters/s", "cores": threads, "kind": "oracle",
+           "cpu_model": cpu_model(),
+           "sample": f"{reps} x ({what}) on the same {p.name} input, {its} iterations in "
+                     f"{dt:.1f} s (each solve includes the oracle's own G^T build)"}
+    # serial leg: one OpenMP thread, this thread pinned to one core
+    mask = os.sched_getaffinity(0)
+    core = min(mask)
+    try:
+        os.sched_setaffinity(0, {core})
+        oracle.set_num_threads(1)
+        log(f"cpu oracle: serial forward solve, 1 thread pinned to core {core}")
+        t0 = time.perf_counter()
+        _, _, it, _ = oracle.pcg(p.A, p.G, p.eps, p.b, p.rtol, min(3, p.maxit))
+        per_it1 = (time.perf_counter() - t0) / max(it, 1)
+        cap1 = max(3, min(p.maxit, int(0.5 * min_seconds / per_it1)))
+        t0 = time.perf_counter()
+        _, _, it1, _ = oracle.pcg(p.A, p.G, p.eps, p.b, p.rtol, cap1)
+        dt1 = time.perf_counter() - t0
+    finally:
+        oracle.set_num_threads(threads)
+        os.sched_setaffinity(0, mask)
+    out["serial_1core"] = {
+        "value": it1 / dt1, "unit": "iters/s", "cores": 1,
+        "sample": f"forward PCG solve cut at {cap1} iterations ({it1} run) on the same "
+                  f"{p.name} input in {dt1:.1f} s, one thread pinned to core {core} "
+                  f"(including the oracle's own G^T build)"}
+    out["affinity_cores"] = len(mask)
+    return out
 
 
 def main():
@@ -360,6 +477,12 @@ def main():
     ap.add_argument("--counter-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic summary under profiles/ from two rocprofv3 "
                          "--pmc runs of --counters-workload (no GPU needed)")
+    ap.add_argument("--l2-dir", default=None,
+                    help="with --counter-summary: a third run with TCC_HIT_sum TCC_MISS_sum")
+    ap.add_argument("--workload-name", default="poisson3d_128",
+                    help="with --counter-summary: the workload the runs measured")
+    ap.add_argument("--counters-args", default="--counters-workload",
+                    help="with --counter-summary: bench.py arguments of the counted runs")
     ap.add_argument("--trace-args", default="--steps 2 --warmup 1 --no-cpu-baseline",
                     help="bench.py arguments of the traced run (for the summary's command)")
     ap.add_argument("--trace-summary", nargs="+", metavar="DIR",
@@ -370,7 +493,8 @@ def main():
         summarize_trace(*args.trace_summary[:2], trace_args=args.trace_args)
         return
     if args.counter_summary:
-        summarize_counters(*args.counter_summary)
+        summarize_counters(*args.counter_summary, l2_dir=args.l2_dir,
+                           workload=args.workload_name, run_args=args.counters_args)
         return
     if args.steps < 1 or args.warmup < 0:
         print("bench.py needs --steps >= 1 and --warmup >= 0", file=sys.stderr)
@@ -432,6 +556,12 @@ def main():
         B.sla_pcg_solve(A, G, p.eps, b, x=x, rtol=p.rtol, maxit=20, work=work)
         B.sla_pcg_adjoint(A, G, p.eps, x, loss_grad(x), rtol=p.rtol, maxit=20, grad_b=grad_b,
                           grad_vals=grad_vals, work=work)
+        for k in args.multi_rhs:
+            Bt = torch.from_numpy(np.random.default_rng(100 + k).standard_normal((n, k))).to(
+                dev, tdt)
+            B.sla_pcg_solve_multi(A, G, p.eps, Bt, rtol=p.rtol, maxit=20,
+                                  work=B.workspace_multi(A, k, dev))
+            del Bt
         # plain SpMV streaming its matrix from HBM: two copies of A alternately
         A2 = mk(a_rp.clone(), a_ci.clone(), a_v.clone())
         y = torch.empty_like(b)
@@ -596,7 +726,30 @@ def main():
     a_bytes = ab["a_step"] if fused else ab["spmv_A"]
     achieved = a_bytes / a_avg_s / 1e9 if has_a else None
     headline = args.config == 2 and args.dtype == "f64" and n == 128 ** 3
-    traffic = traffic_if_current() if headline and fused else None
+    workload = p.name + ("_f32" if args.dtype == "f32" else "")
+    tr = traffic_if_current(workload)
+    a_mode, gt_mode = (2, 4) if fused else (8, 9)
+    step_re = r"(sell_step|csr_step|bsell_step|bsr3_step)<\w+, {}[,>]"
+    traffic = kernel_bytes(tr, step_re.format(a_mode)) if has_a else None
+    physical = None
+    if tr:
+        it_kernels = [step_re.format(a_mode), step_re.format(gt_mode), step_re.format(6)]
+        if not fused:
+            it_kernels += [r"vec_p_update<\w+, 2>", r"vec_r_update<"]
+        parts = [kernel_bytes(tr, k) for k in it_kernels]
+        sp = kernel_bytes(tr, step_re.format(0))
+        it_bytes = sum(parts) if all(v is not None for v in parts) else None
+        physical = {
+            "source": f"profiles/traffic_{workload}.md (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                      "calibrated; Infinity Cache hits count as fetched)",
+            "a_step": {"bytes": traffic, "GBps": traffic / a_avg_s / 1e9,
+                       "frac": traffic / a_avg_s / 1e9 / HBM_PEAK_GBS} if traffic and has_a
+                      else None,
+            "spmv_hbm_stream": {"bytes": sp, "GBps": sp / spmv_stream_s / 1e9,
+                                "frac": sp / spmv_stream_s / 1e9 / HBM_PEAK_GBS} if sp else None,
+            "iteration": {"bytes": it_bytes, "GBps": it_bytes * fi.iterations / tts / 1e9,
+                          "frac": it_bytes * fi.iterations / tts / 1e9 / HBM_PEAK_GBS}
+                         if it_bytes else None}
     moved = moved_bytes_a_step(p.A, n, sv) if fused else None
     if fused and bs == 1:
         a_kernel = (f"sell_step<{'double' if sv == 8 else 'float'}, A step> (q = A p with "
@@ -675,6 +828,7 @@ def main():
                      "note": "dL/dA = -lambda_i x_j on A's pattern (sla_pattern_grad), mean "
                              "of 10 back-to-back calls; bytes: column indices and row "
                              "pointers read, the gradient written, lambda and x read once"},
+        "physical": physical,
         "setup_ms": statistics.median(setup) * 1e3,
         "multi_rhs": {"note": "k right-hand sides solved together on the same A and G "
                               f"(forward solves, {args.dtype}); column-iterations per second and the "

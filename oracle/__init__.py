@@ -17,11 +17,18 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
+# The same source built with multiply-adds contracted to FMA instructions.
+# Not a second oracle: the parity tests use it only to measure how far the
+# oracle's own stopping iteration moves under rounding changes of the kind a
+# GPU makes (fused multiply-adds).
+LIB_CONTRACTED = os.path.join(HERE, "liboracle_contracted.so")
+CONTRACTED_FLAGS = ("-mfma", "-ffp-contract=fast")
 
 OK, NOT_CONVERGED, ERR_ARG, ERR_BREAKDOWN, ERR_NONFINITE, ERR_NOMEM = 0, 1, -1, -3, -4, -6
 
 _lock = threading.Lock()
 _lib = None
+_lib_contracted = None
 
 
 def build(src: str = SRC, out: str = LIB, extra_flags: Tuple[str, ...] = ()) -> str:
@@ -42,6 +49,18 @@ def load(path: Optional[str] = None):
                 build()
             _lib = _bind(ctypes.CDLL(LIB))
         return _lib
+
+
+def load_contracted():
+    """The oracle built with contracted multiply-adds (see LIB_CONTRACTED)."""
+    global _lib_contracted
+    with _lock:
+        if _lib_contracted is None:
+            if (not os.path.exists(LIB_CONTRACTED)
+                    or os.path.getmtime(LIB_CONTRACTED) < os.path.getmtime(SRC)):
+                build(out=LIB_CONTRACTED, extra_flags=CONTRACTED_FLAGS)
+            _lib_contracted = _bind(ctypes.CDLL(LIB_CONTRACTED))
+        return _lib_contracted
 
 
 def _bind(lib):
@@ -77,6 +96,8 @@ def _bind(lib):
     lib.orc_adjoint_multi.restype = ctypes.c_int
     lib.orc_num_threads.argtypes = []
     lib.orc_num_threads.restype = ctypes.c_int
+    lib.orc_set_num_threads.argtypes = [ctypes.c_int]
+    lib.orc_set_num_threads.restype = None
     lib.orc_dot_block.argtypes = []
     lib.orc_dot_block.restype = ctypes.c_int
     return lib
@@ -96,6 +117,12 @@ def _mat(M):
 
 def num_threads(lib=None) -> int:
     return int((lib or load()).orc_num_threads())
+
+
+def set_num_threads(t: int, lib=None) -> None:
+    """Threads of the oracle's OpenMP loops for the calling thread's later
+    calls (timing only: results do not depend on it)."""
+    (lib or load()).orc_set_num_threads(int(t))
 
 
 def spmv(M, x: np.ndarray, lib=None) -> np.ndarray:

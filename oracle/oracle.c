@@ -415,10 +415,13 @@ int orc_adjoint_multi(int64_t nbr, int bs,
 
 int orc_dot_block(void) { return ORC_DOT_BLOCK; }
 
-/* Threads the OpenMP row loops use (1 when built without OpenMP). */
+/* Threads the OpenMP row loops use (1 when built without OpenMP), and a
+ * setter for timing runs (results are bitwise the same for any count). */
 #ifdef _OPENMP
 #include <omp.h>
 int orc_num_threads(void) { return omp_get_max_threads(); }
+void orc_set_num_threads(int t) { omp_set_num_threads(t > 0 ? t : 1); }
 #else
 int orc_num_threads(void) { return 1; }
+void orc_set_num_threads(int t) { (void)t; }
 #endif

@@ -12,7 +12,18 @@ Only the oracle and the seeded input generator run here.  Stored per solve
     ulp (b * (1 + 1e-16 g), g ~ N(0, 1) seeded), its iterations and the
     relative change of x over the whole vector and over the sampled rows;
   - SHA-256 digests of the inputs, so the test can tell that it regenerated
-    the same system.
+    the same system;
+  - the same solves by the oracle's source built with contracted multiply-
+    adds (oracle.load_contracted; parts forward_contracted and
+    adjoint_contracted): status, iterations, residual and the relative
+    difference of the sampled rows from the plain build's.  On this system
+    the stopping iteration depends on that rounding; the parity test takes
+    the contracted count as the yardstick for a GPU that fuses its
+    multiply-adds.
+
+Parts can be run one at a time (e.g. `... make_powerlaw_golden.py
+adjoint_contracted`); a part reuses the stored results of the others when
+the input digests match.
 
 Run from the repository root:  python tests/golden/make_powerlaw_golden.py
 """
@@ -75,6 +86,17 @@ def record(p, rhs, rows, what):
     }
 
 
+def record_contracted(p, rhs, rows, plain, what):
+    t0 = time.time()
+    x, st, it, rr = oracle.pcg(p.A, p.G, p.eps, rhs, p.rtol, p.maxit, lib=oracle.load_contracted())
+    ref = np.asarray(plain["samples"])
+    print(f"[golden] {what} contracted: status {st}, {it} iterations, relres {rr:.3e}, "
+          f"{time.time() - t0:.0f} s", flush=True)
+    return {"status": int(st), "iterations": int(it), "rel_residual": float(rr),
+            "rel_change_samples": rel(x[rows], ref), "rel_change_norm":
+            abs(float(np.linalg.norm(x)) - plain["norm"]) / plain["norm"]}
+
+
 def main():
     t0 = time.time()
     p = I.make_problem(4)
@@ -92,11 +114,12 @@ def main():
                     "b": digest(p.b), "w": digest(p.w)},
         "rows": [int(r) for r in rows],
     }
-    parts = sys.argv[1:] or ["forward", "adjoint"]
+    parts = sys.argv[1:] or ["forward", "adjoint", "forward_contracted", "adjoint_contracted"]
+    names = ("forward", "adjoint", "forward_contracted", "adjoint_contracted")
     if os.path.exists(OUT):
         old = json.load(open(OUT))
         if old.get("digests") == out["digests"]:
-            for k in ("forward", "adjoint"):
+            for k in names:
                 if k in old and k not in parts:
                     out[k] = old[k]
     if "forward" in parts:
@@ -104,6 +127,10 @@ def main():
     if "adjoint" in parts:
         # L = <w, x>: the adjoint solve's right-hand side is dL/dx = w
         out["adjoint"] = record(p, p.w, rows, "adjoint")
+    if "forward_contracted" in parts:
+        out["forward_contracted"] = record_contracted(p, p.b, rows, out["forward"], "forward")
+    if "adjoint_contracted" in parts:
+        out["adjoint_contracted"] = record_contracted(p, p.w, rows, out["adjoint"], "adjoint")
     with open(OUT, "w") as f:
         json.dump(out, f, indent=1)
     print(f"[golden] wrote {OUT} in {time.time() - t0:.0f} s", flush=True)

@@ -78,49 +78,89 @@ def oracle_self_sensitivity(A, G, eps, b, rtol, maxit, seed=0):
 FALLBACKS = []
 
 
+def iters_gate(k_ref: int) -> int:
+    """Half-width of the fixed iteration gate: 2% of the oracle's count, at
+    least one iteration."""
+    return max(1, math.ceil(0.02 * k_ref))
+
+
+def assert_iterations_match(A, G, eps, b, rtol, maxit, it_g, it_r, strict, what="", rec=None):
+    """The GPU's iteration count against the oracle's: within 2% (at least
+    1).  Where strict is False (the test matrices beyond the benchmark
+    workloads) and that fails, the gate is re-taken against the oracle's own
+    spread (oracle_spread) -- but only when that spread is at least as wide as
+    the fixed gate, i.e. when rounding alone moves the oracle's stopping
+    iteration as far as 2% would allow: then the count must lie within the
+    spread, +-1.  Every case that takes this route is printed and recorded
+    in FALLBACKS."""
+    if iters_close(it_g, it_r):
+        return None
+    assert not strict, (what, "iterations", it_g, it_r)
+    lo, hi, dx = oracle_spread(A, G, eps, b, rtol, maxit)
+    r = dict(what=what, it_gpu=it_g, it_ref=it_r, spread=(lo, hi), x_spread=dx)
+    if rec:
+        r.update(rec)
+    assert hi - lo >= iters_gate(it_r), (what, "iterations outside 2% while the oracle's "
+                                         "rounding spread is narrower than that", r)
+    assert lo - 1 <= it_g <= hi + 1, (what, "iterations outside the oracle's spread", r)
+    FALLBACKS.append(r)
+    print("[fallback]", r, flush=True)
+    return dx
+
+
 def assert_solve_matches(A, G, eps, b, rtol, maxit, it_g, x_g, it_r, x_r, strict, what=""):
     """The GPU solve against the oracle's: iterations within 2% and x within
-    1e-8.  Where strict is False (the test matrices beyond the benchmark
-    workloads), a gate that fails is re-taken against the oracle's own spread
-    under one-ulp perturbations of b -- but only when that spread is itself
-    wider than the fixed gate: on systems whose residual stagnates near rtol
-    the stopping iteration is decided by rounding, and any change of
-    summation order moves it.  The iteration count must then lie within the
-    oracle's range (+-1) and x within ten times its largest change.  Every
-    case that takes this route is printed and recorded in FALLBACKS."""
+    1e-8.  Where strict is False, a gate that fails is re-taken against the
+    oracle's own rounding spread, and only when that spread is itself at
+    least as wide as the fixed gate (assert_iterations_match): on systems
+    whose residual stagnates near rtol the stopping iteration is decided by
+    rounding, and any change of summation order or contraction moves it.  x
+    may then differ by up to ten times the oracle's own largest change (and
+    only if that change exceeds 1e-8)."""
     err = rel(x_g, x_r)
-    it_ok, x_ok = iters_close(it_g, it_r), err <= 1e-8
-    if it_ok and x_ok:
+    dx = assert_iterations_match(A, G, eps, b, rtol, maxit, it_g, it_r, strict, what,
+                                 dict(x_err=err))
+    if err <= 1e-8:
         return
-    assert not strict, (what, "iterations", it_g, it_r, "x", err)
-    lo, hi, dx = oracle_spread(A, G, eps, b, rtol, maxit)
-    wide_it = not (iters_close(lo, it_r) and iters_close(hi, it_r))
-    wide_x = dx > 1e-8
-    rec = dict(what=what, it_gpu=it_g, it_ref=it_r, spread=(lo, hi), x_err=err, x_spread=dx)
-    if not it_ok:
-        assert wide_it, (what, "iterations outside 2% while the oracle's spread is inside it", rec)
-        assert lo - 1 <= it_g <= hi + 1, (what, "iterations outside the oracle's spread", rec)
-    if not x_ok:
-        assert wide_x, (what, "x outside 1e-8 while the oracle's spread is inside it", rec)
-        assert err <= 10 * dx, (what, "x outside ten times the oracle's spread", rec)
-    FALLBACKS.append(rec)
-    print("[fallback]", rec, flush=True)
+    assert not strict, (what, "x", err)
+    if dx is None:
+        _, _, dx = oracle_spread(A, G, eps, b, rtol, maxit)
+    r = dict(what=what, it_gpu=it_g, it_ref=it_r, x_err=err, x_spread=dx)
+    assert dx > 1e-8, (what, "x outside 1e-8 while the oracle's spread is inside it", r)
+    assert err <= 10 * dx, (what, "x outside ten times the oracle's spread", r)
+    FALLBACKS.append(r)
+    print("[fallback]", r, flush=True)
+
+
+_spread_cache = {}
 
 
 def oracle_spread(A, G, eps, b, rtol, maxit, nsamp=6):
-    """The oracle's own spread under one-ulp perturbations of b: (fewest and
-    most iterations, largest relative change of x).  On systems whose residual
-    stagnates near rtol the stopping iteration is decided by rounding; this is
-    the yardstick for an implementation whose rounding differs."""
+    """The oracle's own spread under rounding changes: (fewest and most
+    iterations, largest relative change of x) over its solves of b and of
+    nsamp one-ulp perturbations of b (b (1 + 1e-16 g), g seeded), each by
+    the plain build and by the same source built with contracted
+    multiply-adds (oracle.load_contracted).  On systems whose residual
+    stagnates near rtol the stopping iteration is decided by rounding; this
+    is the yardstick for an implementation whose rounding differs."""
     import oracle
-    x0, _, it0, _ = oracle.pcg(A, G, eps, b, rtol, maxit)
+    key = (id(A), id(G), float(eps), hash(np.ascontiguousarray(b).tobytes()), float(rtol),
+           int(maxit), nsamp)
+    if key in _spread_cache:
+        return _spread_cache[key]
+    libs = (oracle.load(), oracle.load_contracted())
+    x0, _, it0, _ = oracle.pcg(A, G, eps, b, rtol, maxit, lib=libs[0])
     its, dx = [it0], 0.0
-    for s in range(nsamp):
-        b2 = b * (1.0 + 1e-16 * np.random.default_rng(s).standard_normal(b.shape))
-        x2, _, it2, _ = oracle.pcg(A, G, eps, b2, rtol, maxit)
-        its.append(it2)
-        dx = max(dx, rel(x2, x0))
-    return min(its), max(its), dx
+    for s in range(-1, nsamp):
+        b2 = b if s < 0 else b * (1.0 + 1e-16 * np.random.default_rng(s).standard_normal(b.shape))
+        for lib in libs:
+            if s < 0 and lib is libs[0]:
+                continue
+            x2, _, it2, _ = oracle.pcg(A, G, eps, b2, rtol, maxit, lib=lib)
+            its.append(it2)
+            dx = max(dx, rel(x2, x0))
+    _spread_cache[key] = (min(its), max(its), dx)
+    return _spread_cache[key]
 
 
 def copy_device_ints(ptr: int, count: int) -> np.ndarray:

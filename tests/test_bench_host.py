@@ -62,3 +62,46 @@ def test_moved_bytes_of_the_slice_offset_form(monkeypatch):
     monkeypatch.setenv("SLA_SELL_OFS", "0")
     assert bench.moved_bytes_a_step(A, n) - (slots * 8 + slots // 64 * 4 + ns * 64
                                              + 4 * (ns + 1) + 6 * 8 * n) > 25e6
+
+
+def _fake_counter_run(d, counter, rows):
+    """A rocprofv3 counter_collection.csv with the given (kernel, value) rows."""
+    import csv
+    os.makedirs(d / "host", exist_ok=True)
+    with open(d / "host" / "pmc_counter_collection.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"])
+        for i, (k, v) in enumerate(rows):
+            w.writerow([i, k, 256, counter, v])
+
+
+def test_counter_summary_calibrates_by_the_copy(tmp_path):
+    """Per-kernel bytes = mean counter KiB per dispatch x 1024 x the factor that
+    makes the 256 MiB copy read and write 256 MiB; the L2 hit rate is
+    HIT / (HIT + MISS) summed over the dispatches."""
+    copy = "void at::native::copyBuffer<double>(...)"
+    step = "void sla::(anonymous namespace)::sell_step<double, 2, true, true, 8, true>(...)"
+    fetch, write, l2 = tmp_path / "f", tmp_path / "w", tmp_path / "l2"
+    # the copy reads 2x and writes 3x what the counters report; the step's two
+    # dispatches report 1000 and 3000 KiB fetched, 10 and 30 KiB written
+    _fake_counter_run(fetch, "FETCH_SIZE", [(copy, 128 * 1024.0), (step, 1000.0), (step, 3000.0)])
+    _fake_counter_run(write, "WRITE_SIZE", [(copy, 256 * 1024.0 / 3), (step, 10.0), (step, 30.0)])
+    import csv
+    os.makedirs(l2 / "host")
+    with open(l2 / "host" / "pmc_counter_collection.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"])
+        w.writerows([[0, step, 256, "TCC_HIT_sum", 30], [0, step, 256, "TCC_MISS_sum", 70],
+                     [1, step, 256, "TCC_HIT_sum", 10], [1, step, 256, "TCC_MISS_sum", 90]])
+    bench.summarize_counters(str(fetch), str(write), str(l2), workload="fake", out_dir=tmp_path)
+    import json
+    rec = json.load(open(tmp_path / "traffic_fake.json"))
+    assert rec["fetch_scale"] == pytest.approx(2.0) and rec["write_scale"] == pytest.approx(3.0)
+    k = rec["kernels"]["sell_step<double, 2, true, true, 8, true>"]
+    assert k["dispatches"] == 2
+    assert k["fetch_bytes"] == pytest.approx(2000.0 * 1024 * 2.0)
+    assert k["write_bytes"] == pytest.approx(20.0 * 1024 * 3.0)
+    assert k["l2_hit_rate"] == pytest.approx(0.2)
+    assert bench.kernel_bytes(rec, r"sell_step<\w+, 2[,>]") == pytest.approx(k["bytes"])
+    assert bench.kernel_bytes(rec, r"sell_step<\w+, 4[,>]") is None
+    assert "A step" in open(tmp_path / "traffic_fake.md").read()

@@ -208,3 +208,25 @@ def test_adjoint_multi_parity(key, layout, form):
     for c in range(k):
         g = g - lam[ri, c] * x[cj, c]
     assert np.array_equal(host(gv), g)
+
+
+@pytest.mark.parametrize("k", [4, 8])
+def test_solve_multi_full_size_poisson3d_128(k):
+    """The benchmark's several-right-hand-side lines at their size: 3D Poisson
+    128^3 (n = 2,097,152), columns N(0, 1) from seed 100 + k with the single
+    solve's b as column 0, every column against the oracle's solve of it
+    under the fixed gates (x within 1e-8, iterations within 2%)."""
+    p = problem("c2")
+    Bm = np.random.default_rng(100 + k).standard_normal((p.A.n, k))
+    Bm[:, 0] = p.b
+    say("solve_multi full size 128^3", k)
+    A, G = create(p.A, validate=False), create(p.G, transpose=True, validate=False)
+    X, infos = B.sla_pcg_solve_multi(A, G, p.eps, tdev(Bm), rtol=p.rtol, maxit=p.maxit)
+    Xg = host(X)
+    Xr, st_r, it_r, _, sts_r = oracle.pcg_multi(p.A, p.G, p.eps, Bm, p.rtol, p.maxit)
+    assert st_r == oracle.OK
+    for c in range(k):
+        say("  column", c, "iterations gpu", infos[c].iterations, "oracle", int(it_r[c]))
+        assert infos[c].status == B.OK and infos[c].converged
+        assert iters_close(infos[c].iterations, int(it_r[c])), (c, infos[c].iterations, it_r[c])
+        assert rel(Xg[:, c], Xr[:, c]) <= 1e-8, (c, rel(Xg[:, c], Xr[:, c]))
