@@ -133,9 +133,14 @@ sla_status sla_bsr_create(sla_mat_t *out, int64_t n_block_rows, int64_t nnzb, in
                           const void *d_bvals, sla_dtype dtype, uint32_t flags, void *stream);
 
 /* Release the handle and everything it owns (the borrowed arrays are
- * untouched).  Waits for all work queued on the handle's device, so it may be
- * called right after asynchronous products; the handle's buffers then go to
- * the library's buffer cache. */
+ * untouched).  Waits for the asynchronous calls queued on the handle (the
+ * products, preconditioner apply, pattern gradient and SAI loss record an
+ * event on their stream), not for the rest of the device, so it may be
+ * called right after them; the handle's buffers then go to the library's
+ * buffer cache.  Handles may be used from several streams and threads at
+ * once, except that the first solve with a reordered A (sla_mat_reordered)
+ * builds the permuted copies and must not overlap other calls on the same
+ * handles. */
 sla_status sla_mat_destroy(sla_mat_t m);
 
 /* Sizes of a handle: scalar rows, stored scalar entries, block size, dtype. */
@@ -341,6 +346,38 @@ sla_status sla_sai_loss(sla_mat_t A, sla_mat_t G, double eps, const void *d_prob
  */
 sla_status sla_pattern_grad(sla_mat_t A, const void *d_lambda, const void *d_x,
                             void *d_grad_vals, void *stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ *
+ * sla_init() prepares the CURRENT device once: it resolves the device
+ * address of the library's fixed solver scratch (32 MiB, a static device
+ * array that every device the library runs on holds until the process
+ * ends) and reserves a pinned polling record.  It may allocate (pinned
+ * host memory, events) and must run outside the allocation-free region.
+ * Idempotent; SLA_ERR_HIP if the device cannot be queried.
+ *
+ * sla_pcg_solve_noalloc() is sla_pcg_solve with its workspace taken from
+ * that scratch: it calls no hipMalloc, hipFree, hipHostMalloc or other
+ * allocating routine.  Same arguments (minus the workspace), iteration,
+ * stopping rule, statuses and results as sla_pcg_solve, except that it
+ * always runs in A's own row order (no locality ordering, which would build
+ * permuted copies; results agree to rounding) and records no profiling
+ * events.  A and G must belong to the current device.  Errors:
+ * SLA_ERR_INVALID_ARG if sla_init() has not run on the current device or
+ * the system's workspace (sla_pcg_workspace_size without the ordering's two
+ * extra vectors) exceeds 32 MiB -- about 500k rows in fp64 -- plus every
+ * error of sla_pcg_solve.  All calls on one device share the one scratch
+ * array, which keeps the last call's contents (the solve clears what must
+ * start at zero); the library serialises calls from different host threads
+ * on the same device, so overlapping calls wait rather than race.
+ * Synchronous like sla_pcg_solve.
+ */
+sla_status sla_init(void);
+sla_status sla_pcg_solve_noalloc(sla_mat_t A, sla_mat_t G, double eps, const void *d_b,
+                                 void *d_x, double rtol, int32_t maxit, void *stream,
+                                 sla_solve_info *info);
 
 /* Human-readable name of a status, and the calling thread's last error text. */
 const char *sla_status_string(sla_status st);

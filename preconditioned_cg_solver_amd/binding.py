@@ -90,6 +90,9 @@ def _declare(L):
         "sla_pcg_solve_history": ([vp, vp, dbl, vp, vp, dbl, i32, vp, sz, vp, vp, i32, vp,
                                    ctypes.POINTER(SolveInfo)], st),
         "sla_pattern_grad": ([vp, vp, vp, vp, vp], st),
+        "sla_init": ([], st),
+        "sla_pcg_solve_noalloc": ([vp, vp, dbl, vp, vp, dbl, i32, vp, ctypes.POINTER(SolveInfo)],
+                                  st),
         "sla_status_string": ([st], ctypes.c_char_p),
         "sla_last_error": ([], ctypes.c_char_p),
         "sla_set_profiling": ([i32], st),
@@ -329,6 +332,28 @@ def sla_pcg_solve(A: Mat, G: Mat, eps: float, b: torch.Tensor, x: Optional[torch
     if raise_on_error:
         _check(st, allow=(OK, NOT_CONVERGED))
     return x, _info(st, si)
+
+
+def sla_init() -> None:
+    """Prepare the current device for sla_pcg_solve_noalloc (resolves the
+    library's fixed scratch and reserves a polling record; may allocate)."""
+    _check(lib().sla_init())
+
+
+def sla_pcg_solve_noalloc(A: Mat, G: Mat, eps: float, b: torch.Tensor, x: torch.Tensor,
+                          rtol: float = 1e-10, maxit: int = 1000, stream=None,
+                          raise_on_error: bool = True) -> Info:
+    """sla_pcg_solve with the library's fixed scratch as workspace: allocates
+    nothing (x is the caller's output tensor).  Needs sla_init() first."""
+    _pair(A, G)
+    pb = _vec(b, A, A.n, "b")
+    px = _vec(x, A, A.n, "x")
+    si = SolveInfo()
+    st = lib().sla_pcg_solve_noalloc(A.handle, G.handle, float(eps), pb, px, float(rtol),
+                                     int(maxit), _stream(stream), ctypes.byref(si))
+    if raise_on_error:
+        _check(st, allow=(OK, NOT_CONVERGED))
+    return _info(st, si)
 
 
 def sla_pcg_solve_history(A: Mat, G: Mat, eps: float, b: torch.Tensor,
