@@ -137,13 +137,12 @@ def moved_bytes_a_step(A, n, sv=8):
     return slots * (sv + col_bytes) + 4 * (ns + 1) + 6 * sv * n
 
 
-def kernel_source_sha() -> str:
-    """SHA-256 over the sources of the counted kernels (the counters of a
-    workload are only used while these are unchanged)."""
-    h = hashlib.sha256()
-    for f in KERNEL_SRCS:
-        h.update(open(f, "rb").read())
-    return h.hexdigest()
+def kernel_source_shas() -> dict:
+    """SHA-256 of each source of the counted kernels: the counters of a kernel
+    are used only while its own source file and the shared device helpers
+    are unchanged."""
+    return {os.path.basename(f): hashlib.sha256(open(f, "rb").read()).hexdigest()
+            for f in KERNEL_SRCS}
 
 
 def traffic_file(workload: str) -> str:
@@ -152,15 +151,19 @@ def traffic_file(workload: str) -> str:
 
 def traffic_if_current(workload: str):
     """Per-kernel HBM bytes per launch of a workload from the committed
-    rocprofv3 counter runs, if they were taken on the current kernel sources;
-    else None."""
+    rocprofv3 counter runs, keeping only the kernels whose sources are
+    unchanged since the counters were taken; None if there are none."""
     try:
         rec = json.load(open(traffic_file(workload)))
-        if rec.get("kernel_source_sha256") != kernel_source_sha():
-            return None
-        return rec
     except (OSError, ValueError):
         return None
+    now, then = kernel_source_shas(), rec.get("kernel_source_sha256", {})
+    if not isinstance(then, dict) or now.get("device_util.h") != then.get("device_util.h"):
+        return None
+    keep = {k: v for k, v in rec["kernels"].items()
+            if now.get(v.get("source")) is not None
+            and now.get(v.get("source")) == then.get(v.get("source"))}
+    return dict(rec, kernels=keep) if keep else None
 
 
 def kernel_bytes(rec, pattern):
@@ -174,6 +177,10 @@ def kernel_bytes(rec, pattern):
     return None
 
 
+def kernel_source(key: str) -> str:
+    """Source file of a counted kernel of this library."""
+    return "multi.hip" if key.startswith(("msell", "mbsell", "mtile", "mrow", "mvec", "minit",
+                                          "mgrad")) else "solver.hip"
 STEP_NAMES = {0: "plain SpMV y = A x (matrix from HBM)",
               1: "A step, iteration 1", 2: "A step (q = A p, p and x updates)",
               3: "G^T step, start-up", 4: "G^T step (t = G^T r, r update)",
@@ -241,7 +248,8 @@ def summarize_counters(fetch_dir, write_dir, l2_dir=None, workload="poisson3d_12
         fk = statistics.fmean(v for v, _ in fetch[k])
         wk = statistics.fmean(v for v, _ in write[k])
         rec = {"dispatches": len(fetch[k]), "fetch_kib_raw": fk, "write_kib_raw": wk,
-               "fetch_bytes": fk * 1024 * fs, "write_bytes": wk * 1024 * ws}
+               "fetch_bytes": fk * 1024 * fs, "write_bytes": wk * 1024 * ws,
+               "source": kernel_source(k)}
         rec["bytes"] = rec["fetch_bytes"] + rec["write_bytes"]
         kernels[k] = rec
     # L2 (TCC) hit rate: the HIT and MISS runs record one row per counter and dispatch
@@ -262,7 +270,7 @@ def summarize_counters(fetch_dir, write_dir, l2_dir=None, workload="poisson3d_12
         for k, d in hm.items():
             if k in kernels and d["hit"] + d["miss"] > 0:
                 kernels[k]["l2_hit_rate"] = d["hit"] / (d["hit"] + d["miss"])
-    src_sha = kernel_source_sha()
+    src_sha = kernel_source_shas()
     lines = ["| kernel | role | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB (scaled) "
              "| written MB | total MB | L2 hit |", "|---|---|---|---|---|---|---|---|---|"]
     for k, r in sorted(kernels.items(), key=lambda kv: -kv[1]["bytes"] * kv[1]["dispatches"]):
@@ -292,7 +300,8 @@ def summarize_counters(fetch_dir, write_dir, l2_dir=None, workload="poisson3d_12
           f"    python bench.py --counter-summary {fetch_dir} {write_dir}"
           + (f" --l2-dir {l2_dir}" if l2_dir else "")
           + f" --workload-name {workload} --counters-args '{run_args}'", "", *lines, "",
-          "Kernel sources (solver.hip, multi.hip, device_util.h) sha256 " + src_sha + ".", ""]
+          "Kernel sources (sha256): " + ", ".join(f"{f} {h}" for f, h in src_sha.items()) + ".",
+          ""]
     out_dir = out_dir or os.path.join(ROOT, "profiles")
     with open(os.path.join(out_dir, f"traffic_{workload}.md"), "w") as f:
         f.write("\n".join(md))

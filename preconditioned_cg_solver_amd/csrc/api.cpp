@@ -167,6 +167,7 @@ sla_status create_common(sla_mat_t* out, int64_t nbr, int64_t nnzb, int32_t bs, 
     st = build_sell(m->fwd, nbr, nnzb, dtype, &m->owned[O_SELL_F], &m->owned[O_SOFS_F], s);
   if (st == SLA_OK && bs == 3 && sell_enabled())
     st = build_bsell(m->fwd, nbr, nnzb, dtype, &m->owned[O_SELL_F], s);
+  if (st == SLA_OK && bs == 3) st = max_row_length(rp, nbr, &m->fwd.max_row, s);
   if (st == SLA_OK) st = alloc_long_scratch(m, m->fwd, O_LPART_F, O_LCNT_F, s);
   if (st == SLA_OK && ordering) st = decide_order(m, s);
   if (st == SLA_OK && (flags & SLA_BUILD_TRANSPOSE)) {

@@ -131,6 +131,7 @@ struct MatView {
   int nlong = 0;                 // long-row chunks among the tiles
   int nlong_rows = 0;            // rows split into chunks
   int n_long_part = 0;           // partial slots needed by the long-row chunks
+  int max_row = -1;              // longest row in blocks (BSR; -1 = not computed)
   const int* long_rows = nullptr;  // row index of each of the nlong_rows long rows (CSR)
   // SELL-64 copy (owned), built once when the rows qualify: slice s holds
   // rows [64 s, 64 s + 64); slot j of its row 64 s + l sits at
@@ -222,6 +223,7 @@ sla_status build_tiling(const int32_t* d_rp, int64_t n, MatView& view, void** ow
 sla_status build_transpose(const sla_mat& m, int32_t** t_rp, int32_t** t_ci, void** t_v,
                            hipStream_t s);
 sla_status validate_structure(const sla_mat& m, hipStream_t s);
+sla_status max_row_length(const int32_t* d_rp, int64_t nbr, int* out, hipStream_t s);
 sla_status build_sell(MatView& view, int64_t n, int64_t nnz, int32_t dtype, void** owned3,
                       void** owned_ofs2, hipStream_t s);
 sla_status build_bsell(MatView& view, int64_t nbr, int64_t nnzb, int32_t dtype, void** owned3,

@@ -643,6 +643,22 @@ __global__ void bsell_fill(const int* __restrict__ rp, const int* __restrict__ c
   }
 }
 
+// Longest row (in stored entries or blocks) of a CSR / BSR row pointer array.
+__global__ __launch_bounds__(kWG) void row_len_max(const int* __restrict__ rp, int nbr,
+                                                   int* __restrict__ out) {
+  __shared__ int s_m[kWaves];
+  int m = 0;
+  for (int i = blockIdx.x * kWG + threadIdx.x; i < nbr; i += gridDim.x * kWG)
+    m = max(m, rp[i + 1] - rp[i]);
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, __shfl_xor(m, off, 64));
+  if ((threadIdx.x & 63) == 0) s_m[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 1; k < kWaves; ++k) m = max(m, s_m[k]);
+    atomicMax(out, m);
+  }
+}
+
 int grid_for(int64_t work, int per_block = kWG) {
   const int64_t g = (work + per_block - 1) / per_block;
   return (int)std::max<int64_t>(1, std::min<int64_t>(g, 65536));
@@ -776,6 +792,21 @@ sla_status build_transpose(const sla_mat& m, int32_t** t_rp_out, int32_t** t_ci_
                        (const float*)m.fwd.v, nbr, nnzb, bs, vin, t_ci, (float*)t_v);
   SLA_HIP(hipGetLastError());
   SLA_HIP(hipFreeAsync(work, s));
+  SLA_HIP(hipStreamSynchronize(s));
+  return SLA_OK;
+}
+
+sla_status max_row_length(const int32_t* d_rp, int64_t nbr, int* out, hipStream_t s) {
+  *out = 0;
+  if (nbr == 0) return SLA_OK;
+  int* d = nullptr;
+  SLA_HIP(hipMallocAsync((void**)&d, sizeof(int), s));
+  SLA_HIP(hipMemsetAsync(d, 0, sizeof(int), s));
+  hipLaunchKernelGGL(row_len_max, dim3(std::min(grid_for(nbr), 1024)), dim3(kWG), 0, s, d_rp,
+                     (int)nbr, d);
+  SLA_HIP(hipGetLastError());
+  SLA_HIP(hipMemcpyAsync(out, d, sizeof(int), hipMemcpyDeviceToHost, s));
+  SLA_HIP(hipFreeAsync(d, s));
   SLA_HIP(hipStreamSynchronize(s));
   return SLA_OK;
 }

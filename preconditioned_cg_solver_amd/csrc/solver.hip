@@ -1094,20 +1094,74 @@ __global__ __launch_bounds__(kWG) void csr_grad(const int32_t* __restrict__ rp,
   }
 }
 
+// BSR: a tile of kBsrTileRows block rows owns one contiguous range of the
+// gradient (9 entries per block, storage order).  Each thread forms the three
+// entries of one block row r of one block (-lambda_{3I+r} times the block
+// column's three x entries: one column load, three contiguous gathers) into
+// LDS, then the workgroup streams the tile's range out with 16-byte
+// non-temporal stores, the odd entries at either end alone.  The output is
+// written once and never read here, and a gradient larger than the Infinity
+// Cache would otherwise cycle through it.  (Elasticity 64^3 x 3, 494 MB
+// written: 112 us; with one scalar entry per thread and round, computing its
+// block from the entry index, 158-176 us.)
+constexpr int kGradMaxBlocks = 27;  // blocks per block row the LDS tile holds
 template <typename T>
 __global__ __launch_bounds__(kWG) void bsr3_grad(const int32_t* __restrict__ rp,
                                                  const int32_t* __restrict__ ci, int nbr,
                                                  int ntiles, const T* __restrict__ lam,
                                                  const T* __restrict__ x, T* __restrict__ g) {
-  // A tile of kBsrTileRows block rows owns one contiguous range of the
-  // gradient (9 entries per block, storage order), streamed by the whole
-  // workgroup with coalesced stores; an entry's block row is its position
-  // among the tile's row pointers.  Four entries per thread and round keep
-  // four independent column -> gather -> store chains in flight.  (Entry
-  // indices fit int: the handle limits 9 nnzb below 2^31.)  The output is
-  // stored non-temporally: nothing here reads it again, and a gradient larger
-  // than the Infinity Cache would otherwise cycle through it (elasticity
-  // 64^3 x 3: 229 -> 156 us).
+  using V2 = T __attribute__((ext_vector_type(2)));
+  constexpr int kMax = 9 * kGradMaxBlocks * kBsrTileRows + 2;
+  __shared__ T s_g[kMax];
+  int t0, t1, step;
+  tile_range(ntiles, t0, t1, step);
+  for (int t = t0; t < t1; t += step) {
+    const int I0 = t * kBsrTileRows;
+    int rr[kBsrTileRows + 1];
+#pragma unroll
+    for (int j = 0; j <= kBsrTileRows; ++j) rr[j] = rp[min(I0 + j, nbr)];
+    const int b0 = rr[0], b1 = rr[kBsrTileRows];
+    // (Entry indices fit int: the handle limits 9 nnzb below 2^31.)
+    const int e0 = 9 * b0, e1 = 9 * b1, ea = e0 & ~1;
+    // the host sends tiles with more blocks than the LDS holds to the
+    // streaming path below
+    for (int q = threadIdx.x; q < 3 * (b1 - b0); q += kWG) {
+      const int kb = b0 + q / 3, r = q - 3 * (q / 3);
+      int li = 0;
+#pragma unroll
+      for (int j = 1; j < kBsrTileRows; ++j) li += kb >= rr[j] ? 1 : 0;
+      const T l = lam[3 * (I0 + li) + r];
+      const int J = ci[kb];
+      const T x0 = x[3 * J], x1 = x[3 * J + 1], x2 = x[3 * J + 2];
+      T* d = s_g + (9 * kb + 3 * r - ea);
+      d[0] = -(l * x0);
+      d[1] = -(l * x1);
+      d[2] = -(l * x2);
+    }
+    __syncthreads();
+    for (int e = ea + 2 * (int)threadIdx.x; e < e1; e += 2 * kWG) {
+      if (e >= e0 && e + 1 < e1) {
+        V2 v;
+        v.x = s_g[e - ea];
+        v.y = s_g[e - ea + 1];
+        __builtin_nontemporal_store(v, (V2*)(g + e));
+      } else {
+        if (e >= e0) __builtin_nontemporal_store(s_g[e - ea], g + e);
+        if (e + 1 < e1) __builtin_nontemporal_store(s_g[e - ea + 1], g + e + 1);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// The same product for BSR tiles of any width, one scalar entry per thread
+// and round (used when some block row holds more than kGradMaxBlocks blocks).
+template <typename T>
+__global__ __launch_bounds__(kWG) void bsr3_grad_wide(const int32_t* __restrict__ rp,
+                                                      const int32_t* __restrict__ ci, int nbr,
+                                                      int ntiles, const T* __restrict__ lam,
+                                                      const T* __restrict__ x,
+                                                      T* __restrict__ g) {
   constexpr int B = 4;
   int t0, t1, step;
   tile_range(ntiles, t0, t1, step);
@@ -1894,12 +1948,17 @@ sla_status pattern_grad(const sla_mat& A, const void* lam, const void* x, void* 
   } else {
     const int nt = (int)((A.nbr + kBsrTileRows - 1) / kBsrTileRows);
     const int grid = step_grid(nt);
+    // the LDS-staged kernel holds tiles whose block rows have at most
+    // kGradMaxBlocks blocks
+    const bool staged = A.fwd.max_row >= 0 && A.fwd.max_row <= kGradMaxBlocks;
     if (A.dtype == SLA_F64)
-      hipLaunchKernelGGL(bsr3_grad<double>, dim3(grid), dim3(kWG), 0, s, A.fwd.rp, A.fwd.ci,
-                         (int)A.nbr, nt, (const double*)lam, (const double*)x, (double*)grad);
+      hipLaunchKernelGGL(staged ? bsr3_grad<double> : bsr3_grad_wide<double>, dim3(grid),
+                         dim3(kWG), 0, s, A.fwd.rp, A.fwd.ci, (int)A.nbr, nt,
+                         (const double*)lam, (const double*)x, (double*)grad);
     else
-      hipLaunchKernelGGL(bsr3_grad<float>, dim3(grid), dim3(kWG), 0, s, A.fwd.rp, A.fwd.ci,
-                         (int)A.nbr, nt, (const float*)lam, (const float*)x, (float*)grad);
+      hipLaunchKernelGGL(staged ? bsr3_grad<float> : bsr3_grad_wide<float>, dim3(grid),
+                         dim3(kWG), 0, s, A.fwd.rp, A.fwd.ci, (int)A.nbr, nt,
+                         (const float*)lam, (const float*)x, (float*)grad);
   }
   SLA_HIP(hipGetLastError());
   return SLA_OK;

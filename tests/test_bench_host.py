@@ -102,6 +102,7 @@ def test_counter_summary_calibrates_by_the_copy(tmp_path):
     assert k["fetch_bytes"] == pytest.approx(2000.0 * 1024 * 2.0)
     assert k["write_bytes"] == pytest.approx(20.0 * 1024 * 3.0)
     assert k["l2_hit_rate"] == pytest.approx(0.2)
+    assert k["source"] == "solver.hip"
     assert bench.kernel_bytes(rec, r"sell_step<\w+, 2[,>]") == pytest.approx(k["bytes"])
     assert bench.kernel_bytes(rec, r"sell_step<\w+, 4[,>]") is None
     assert "A step" in open(tmp_path / "traffic_fake.md").read()

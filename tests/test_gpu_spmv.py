@@ -112,6 +112,17 @@ def far_bsr(m=33):
     return I.SparseMatrix(nbr, 3, rp, cols[order].astype(np.int32), vals[order].reshape(-1))
 
 
+def bsr_wide_rows(nbr=500, seed=12):
+    """Random 3x3-block pattern with 0 to 60 blocks per block row: rows wider
+    than the 27 blocks the LDS-staged pattern-gradient tile holds."""
+    rng = np.random.default_rng(seed)
+    cols = [np.sort(rng.choice(nbr, size=rng.integers(0, 61), replace=False)) for _ in range(nbr)]
+    rp = np.zeros(nbr + 1, np.int32)
+    np.cumsum([len(c) for c in cols], out=rp[1:])
+    ci = np.concatenate(cols).astype(np.int32)
+    return I.SparseMatrix(nbr, 3, rp, ci, rng.standard_normal(9 * len(ci)))
+
+
 def bsr_empty_slices():
     """Block stencil on 10^3 nodes with block rows 105..167 emptied: three
     whole 21-block-row slices without a slot, between slices that have them
@@ -225,9 +236,10 @@ def test_precond_apply(name):
 
 @pytest.mark.parametrize("name", ["c0_poisson2d_32", "c2_poisson3d_128", "irregular_long_rows",
                                   "bsr_elastic_5", "empty_rows", "bsr_empty_slices",
-                                  "c3_bsr_elastic_64"])
+                                  "bsr_wide_rows", "c3_bsr_elastic_64"])
 def test_pattern_grad_bit_exact(name):
-    M = bsr_empty_slices() if name == "bsr_empty_slices" else MATRICES[name]()
+    M = {"bsr_empty_slices": bsr_empty_slices, "bsr_wide_rows": bsr_wide_rows}.get(
+        name, MATRICES.get(name))()
     lam = I.spmv_test_vector(5, M.n)
     x = I.spmv_test_vector(6, M.n)
     say("pattern grad", name)
