@@ -50,6 +50,9 @@ constexpr int kSellTail = 16 * kSlice;
 // every row; a one-byte mask per row marks the slots the row has.  The
 // per-entry column words are then read only by the one-workgroup solver.
 constexpr int kOfsMax = 8;
+// Halo of the windowed slice-offset engine: slot offsets within +-kWinHalo
+// rows are read from the workgroup's LDS window of the gathered vector.
+constexpr int kWinHalo = 128;
 // Capacity of the MI355X last-level Infinity Cache (MALL).
 constexpr size_t kMallBytes = (size_t)256 << 20;
 // Sliced ELLPACK for 3x3 BSR: kBSlice block rows per wavefront slice (lane

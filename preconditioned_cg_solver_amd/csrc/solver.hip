@@ -597,6 +597,123 @@ __global__ __launch_bounds__(kWG) void sell_step(StepArgs<T> a) {
   }
 }
 
+// Slice-offset form with a window in LDS: a workgroup takes kWaves
+// consecutive slices (a tile of R = 256 rows) and first writes the gathered
+// vector's value (z + beta p_old, r - alpha q, ... as gat() forms it) for
+// every row of [the tile's first row - kWinHalo, its last row + kWinHalo]
+// into LDS, each row once and with coalesced loads; a slot whose offset lies
+// within the halo (the slice-offset form gives every slot one offset for the
+// whole slice, so the test is wavefront-uniform) then reads LDS, and only
+// the far offsets gather from memory.  On the 3D 7-point stencil that serves
+// the offsets 0, +-1 and +-128 of every slice from LDS and leaves the two
+// +-16,384 planes to the caches.  The next tile's window entries and each
+// wavefront's next slice head (its first U values and offsets, and its row
+// masks) are loaded into registers while the current tile computes.  Every
+// row adds its slots in the same order and with the same values as
+// sell_step, so the results are bit-identical to it.
+template <typename T, int MODE, bool NT, int U>
+__global__ __launch_bounds__(kWG) void sell_win_step(StepArgs<T> a) {
+  constexpr int R = kWaves * kSlice;
+  constexpr int WN = R + 2 * kWinHalo;
+  constexpr int PER = (WN + kWG - 1) / kWG;
+  constexpr bool TWO = MODE == M_A || MODE == M_GT;  // gat() reads in0 and in1
+  __shared__ T gs[WN];
+  __shared__ double s_red[kWaves];
+  __shared__ int s_flag;
+  const int lane = threadIdx.x & (kSlice - 1), wv = threadIdx.x / kSlice;
+  int t0, t1, step;
+  tile_range(a.ntiles, t0, t1, step);
+  // next tile: raw window entries and this wavefront's slice head
+  T w0[PER], w1[PER];
+  T hv[U];
+  int hr[U];
+  int hoff = 0, hw = 0, hm = 0;
+  auto fetch = [&](int t) {
+    const int wb = t * R - kWinHalo;
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int i = threadIdx.x + p * kWG, r = wb + i;
+      const bool in = i < WN && r >= 0 && r < a.n;
+      w0[p] = in ? a.in0[r] : T(0);
+      if constexpr (TWO) w1[p] = in ? a.in1[r] : T(0);
+    }
+    const int sl = t * kWaves + wv;
+    hoff = 0;
+    hw = 0;
+    hm = 0;
+    if (sl < a.nslices) {
+      hoff = a.soff[sl];
+      hw = (a.soff[sl + 1] - hoff) / kSlice;
+      hm = ld_stream<NT>(a.sm + sl * kSlice + lane);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      hv[u] = ld_stream<NT>(a.sv + hoff + u * kSlice + lane);
+      hr[u] = ld_stream<NT>(a.so + hoff / kSlice + u);
+    }
+  };
+  if (t0 < t1) fetch(t0);
+  Coef<T> cf;
+  if (!prologue<T, MODE>(a, cf, s_red, &s_flag)) return;
+  double dot = 0.0;
+  for (int t = t0; t < t1; t += step) {
+    const int wb = t * R - kWinHalo;
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int i = threadIdx.x + p * kWG;
+      if (i < WN) {
+        if constexpr (TWO) gs[i] = fma(cf.c, w1[p], w0[p]);
+        else gs[i] = w0[p];
+      }
+    }
+    const int off = hoff, w = hw, m = hm;
+    T cv[U];
+    int cr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      cv[u] = hv[u];
+      cr[u] = hr[u];
+    }
+    __syncthreads();
+    if (t + step < t1) fetch(t + step);
+    const int sl = t * kWaves + wv;
+    if (sl < a.nslices) {
+      const int row = sl * kSlice + lane;
+      const bool live = row < a.nbr;
+      const Own<T> o = own_load<T, MODE>(a, live ? row : 0);
+      T acc = T(0);
+      for (int j = 0; j < w; j += U) {
+        if (j > 0) {
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            cv[u] = ld_stream<NT>(a.sv + off + (j + u) * kSlice + lane);
+            cr[u] = ld_stream<NT>(a.so + off / kSlice + j + u);
+          }
+        }
+        T x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const bool ok = (m >> (j + u)) & 1;
+          const int c = ok ? row + cr[u] : row;
+          T g;
+          if (cr[u] >= -kWinHalo && cr[u] <= kWinHalo) g = gs[c - wb];
+          else g = gat<T, MODE>(a, c, cf);
+          x[u] = ok ? g : T(0);
+          if (!ok) cv[u] = T(0);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc = fma(cv[u], x[u], acc);
+      }
+      if (live) dot += epi_own<T, MODE>(a, row, acc, cf, o);
+    }
+    __syncthreads();
+  }
+  if constexpr (MODE != M_PLAIN && MODE != M_GZ && MODE != M_GTU) {
+    const double sd = block_sum(dot, s_red);
+    if (threadIdx.x == 0) a.pout[blockIdx.x] = sd;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Sliced-ELL engine for 3x3 BSR: one wavefront per slice of 21 block rows.
 // Lane l = 3 i + c takes local block row i and block component c: for every
@@ -1221,14 +1338,31 @@ void fill_matrix(StepArgs<T>& a, const sla_mat& m, const MatView& v, double* lon
   a.long_cnt = long_cnt;
 }
 
+// The windowed slice-offset engine (sell_win_step): SLA_WIN=1 (default) for
+// the A steps, 2 for every step of the iteration, 0 never (read once per
+// solve).
+int win_level() {
+  const char* e = getenv("SLA_WIN");
+  return e ? atoi(e) : 1;
+}
+bool win_applies(int mode, int level) {
+  if (mode == M_PLAIN || level <= 0) return false;
+  return level >= 2 || mode == M_A || mode == M_A1 || mode == M_AU;
+}
+
 template <typename T, int MODE>
 hipError_t launch_step(const sla_mat& m, const StepArgs<T>& a, int grid, hipStream_t s,
-                       bool nt) {
+                       bool nt, int win = 0) {
   if (m.bs == 1 && (a.sd || a.sc)) {
     // batch of slots per load round: the slice width rounded up to 4 or 8
     const bool wide = a.sell_w > 4;
     const dim3 g(grid), b(kWG);
-    if (a.so) {
+    if (a.so && win_applies(MODE, win)) {
+      if (nt && wide) hipLaunchKernelGGL((sell_win_step<T, MODE, true, 8>), g, b, 0, s, a);
+      else if (nt) hipLaunchKernelGGL((sell_win_step<T, MODE, true, 4>), g, b, 0, s, a);
+      else if (wide) hipLaunchKernelGGL((sell_win_step<T, MODE, false, 8>), g, b, 0, s, a);
+      else hipLaunchKernelGGL((sell_win_step<T, MODE, false, 4>), g, b, 0, s, a);
+    } else if (a.so) {
       if (nt && wide) hipLaunchKernelGGL((sell_step<T, MODE, true, true, 8, true>), g, b, 0, s, a);
       else if (nt) hipLaunchKernelGGL((sell_step<T, MODE, true, true, 4, true>), g, b, 0, s, a);
       else if (wide) hipLaunchKernelGGL((sell_step<T, MODE, false, true, 8, true>), g, b, 0, s, a);
@@ -1493,6 +1627,7 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
   SLA_HIP(hipMemsetAsync(w.st, 0, zeroed_bytes(A), s));
   const MallPlan plan = mall_plan(A, G);
   const bool fused = use_fused(A);
+  const int win = win_level();
 
   StepArgs<T> aA{}, aT{}, aG{};
   fill_matrix(aA, A, A.fwd, lsA.part, lsA.cnt);
@@ -1556,13 +1691,13 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
   aT.own = R[0];
   aT.pout = w.prr;
   hipEvent_t e0 = rec.begin(1, 0);
-  SLA_HIP((launch_step<T, M_GT0>(G, aT, grid, s, plan.nt_t)));
+  SLA_HIP((launch_step<T, M_GT0>(G, aT, grid, s, plan.nt_t, win)));
   rec.end(e0, 1, 0);
   if (!fused) aT.pout = nullptr;
   aG.k = 0;
   aG.rv = R[0];
   e0 = rec.begin(2, 0);
-  SLA_HIP((launch_step<T, M_G0>(G, aG, grid, s, plan.nt_g)));
+  SLA_HIP((launch_step<T, M_G0>(G, aG, grid, s, plan.nt_g, win)));
   rec.end(e0, 2, 0);
 
   // exit-flag copies in flight: a ring of at most two pending batches
@@ -1582,14 +1717,14 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
           aA.in1 = P[(kk - 1) & 1];
           aA.own = P[kk & 1];
           hipEvent_t ea = rec.begin(0, kk);
-          if (kk == 1) SLA_HIP((launch_step<T, M_A1>(A, aA, grid, s, plan.nt_a)));
-          else SLA_HIP((launch_step<T, M_A>(A, aA, grid, s, plan.nt_a)));
+          if (kk == 1) SLA_HIP((launch_step<T, M_A1>(A, aA, grid, s, plan.nt_a, win)));
+          else SLA_HIP((launch_step<T, M_A>(A, aA, grid, s, plan.nt_a, win)));
           rec.end(ea, 0, kk);
           aT.k = kk;
           aT.in0 = R[(kk - 1) & 1];
           aT.own = R[kk & 1];
           hipEvent_t et = rec.begin(1, kk);
-          SLA_HIP((launch_step<T, M_GT>(G, aT, grid, s, plan.nt_t)));
+          SLA_HIP((launch_step<T, M_GT>(G, aT, grid, s, plan.nt_t, win)));
           rec.end(et, 1, kk);
         } else {
           // p and x update, q = A p, r update, t = G^T r: single gathers
@@ -1604,7 +1739,7 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
           aA.k = kk;
           aA.in0 = P[kk & 1];
           hipEvent_t ea = rec.begin(0, kk);
-          SLA_HIP((launch_step<T, M_AU>(A, aA, grid, s, plan.nt_a)));
+          SLA_HIP((launch_step<T, M_AU>(A, aA, grid, s, plan.nt_a, win)));
           rec.end(ea, 0, kk);
           aR.k = kk;
           aR.in0 = R[(kk - 1) & 1];
@@ -1614,14 +1749,14 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
           aT.k = kk;
           aT.in0 = R[kk & 1];
           hipEvent_t et = rec.begin(1, kk);
-          SLA_HIP((launch_step<T, M_GTU>(G, aT, grid, s, plan.nt_t)));
+          SLA_HIP((launch_step<T, M_GTU>(G, aT, grid, s, plan.nt_t, win)));
           rec.end(et, 1, kk);
           aG.npin = grid;  // rr partials now come from vec_r_update
         }
         aG.k = kk;
         aG.rv = R[kk & 1];
         hipEvent_t eg = rec.begin(2, kk);
-        SLA_HIP((launch_step<T, M_G>(G, aG, grid, s, plan.nt_g)));
+        SLA_HIP((launch_step<T, M_G>(G, aG, grid, s, plan.nt_g, win)));
         rec.end(eg, 2, kk);
       }
       const int ps = next_slot;

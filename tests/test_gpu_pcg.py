@@ -385,3 +385,27 @@ def test_engine_variants(key, env, monkeypatch):
     assert ainfo.status == B.OK and iters_close(ainfo.iterations, it2)
     assert rel(host(grad_b), lam_ref) <= 1e-7
     assert rel(host(grad_vals), gv_ref) <= 1e-7
+
+
+@pytest.mark.parametrize("key", ["poisson3d_13", "heat2d_64", "poisson2d_37", "c2"])
+def test_window_engine_bit_identical(key, fusion, monkeypatch):
+    """The windowed slice-offset engine (an LDS window of the gathered vector
+    serves the slots within 128 rows) solves bit-identically to the plain
+    slice-offset engine, on the A steps only (default) and on every step,
+    and matches the oracle."""
+    if fusion != "auto" and key == "c2":
+        pytest.skip("full-size configs run in the library's own choice only")
+    p = problem(key)
+    monkeypatch.setenv("SLA_SMALL", "0")
+    x_ref, _, it_ref, _ = oracle.pcg(p.A, p.G, p.eps, p.b, p.rtol, p.maxit)
+    outs = []
+    for level in ("0", "1", "2"):
+        monkeypatch.setenv("SLA_WIN", level)
+        say("window engine", key, fusion, "level", level)
+        A, G = handles(p)
+        x, info = B.sla_pcg_solve(A, G, p.eps, tdev(p.b), rtol=p.rtol, maxit=p.maxit)
+        assert info.status == B.OK
+        outs.append((host(x), info.iterations))
+    for x, it in outs[1:]:
+        assert it == outs[0][1] and np.array_equal(x, outs[0][0])
+    assert iters_close(outs[0][1], it_ref) and rel(outs[0][0], x_ref) <= 1e-8
