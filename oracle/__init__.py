@@ -23,12 +23,18 @@ LIB = os.path.join(HERE, "liboracle.so")
 # GPU makes (fused multiply-adds).
 LIB_CONTRACTED = os.path.join(HERE, "liboracle_contracted.so")
 CONTRACTED_FLAGS = ("-mfma", "-ffp-contract=fast")
+# The same source with rows longer than 2,048 entries summed in 4,096-entry
+# chunks (ORC_ROW_CHUNK in oracle.c): likewise only a yardstick for how far
+# the stopping iteration moves with the summation order of very long rows.
+LIB_CHUNKED = os.path.join(HERE, "liboracle_chunked.so")
+CHUNKED_FLAGS = ("-DORC_ROW_CHUNK=4096",)
 
 OK, NOT_CONVERGED, ERR_ARG, ERR_BREAKDOWN, ERR_NONFINITE, ERR_NOMEM = 0, 1, -1, -3, -4, -6
 
 _lock = threading.Lock()
 _lib = None
 _lib_contracted = None
+_lib_chunked = None
 
 
 def build(src: str = SRC, out: str = LIB, extra_flags: Tuple[str, ...] = ()) -> str:
@@ -61,6 +67,18 @@ def load_contracted():
                 build(out=LIB_CONTRACTED, extra_flags=CONTRACTED_FLAGS)
             _lib_contracted = _bind(ctypes.CDLL(LIB_CONTRACTED))
         return _lib_contracted
+
+
+def load_chunked():
+    """The oracle built with chunked sums of very long rows (see LIB_CHUNKED)."""
+    global _lib_chunked
+    with _lock:
+        if _lib_chunked is None:
+            if (not os.path.exists(LIB_CHUNKED)
+                    or os.path.getmtime(LIB_CHUNKED) < os.path.getmtime(SRC)):
+                build(out=LIB_CHUNKED, extra_flags=CHUNKED_FLAGS)
+            _lib_chunked = _bind(ctypes.CDLL(LIB_CHUNKED))
+        return _lib_chunked
 
 
 def _bind(lib):

@@ -60,6 +60,17 @@ enum {
     ORC_ERR_NOMEM = -6
 };
 
+/* Summation order of long rows.  0 (the oracle): every row sum starts at
+ * 0.0 and adds val*x in storage order.  A build with ORC_ROW_CHUNK = c > 0
+ * instead sums each row longer than c / 2 entries in consecutive chunks of c
+ * entries (each from 0.0, in storage order) and adds the chunk sums in
+ * order: another valid rounding order of the same sum, used only to measure
+ * how far the solver's stopping iteration moves with the summation order on
+ * systems with very long rows. */
+#ifndef ORC_ROW_CHUNK
+#define ORC_ROW_CHUNK 0
+#endif
+
 /* y = A x.  Row sums start at 0.0 and add val*x in storage order
  * (the definition of a sparse matrix-vector product). */
 void orc_spmv(int64_t nbr, int bs, const int32_t *row_ptr, const int32_t *col,
@@ -68,15 +79,21 @@ void orc_spmv(int64_t nbr, int bs, const int32_t *row_ptr, const int32_t *col,
     const int64_t bb = (int64_t)bs * bs;
 #pragma omp parallel for schedule(static)
     for (int64_t I = 0; I < nbr; ++I) {
+        const int64_t kb = row_ptr[I], ke = row_ptr[I + 1];
+        const int chunked = ORC_ROW_CHUNK > 0 && 2 * (ke - kb) > (int64_t)ORC_ROW_CHUNK;
         for (int r = 0; r < bs; ++r) {
-            double s = 0.0;
-            for (int64_t k = row_ptr[I]; k < row_ptr[I + 1]; ++k) {
+            double s = 0.0, done = 0.0;
+            for (int64_t k = kb; k < ke; ++k) {
+                if (chunked && k > kb && (k - kb) % (ORC_ROW_CHUNK > 0 ? ORC_ROW_CHUNK : 1) == 0) {
+                    done += s;
+                    s = 0.0;
+                }
                 const int64_t J = col[k];
                 const double *blk = val + k * bb + (int64_t)r * bs;
                 for (int c = 0; c < bs; ++c)
                     s += blk[c] * x[J * bs + c];
             }
-            y[I * bs + r] = s;
+            y[I * bs + r] = chunked ? done + s : s;
         }
     }
 }

@@ -13,13 +13,16 @@ Only the oracle and the seeded input generator run here.  Stored per solve
     relative change of x over the whole vector and over the sampled rows;
   - SHA-256 digests of the inputs, so the test can tell that it regenerated
     the same system;
-  - the same solves by the oracle's source built with contracted multiply-
-    adds (oracle.load_contracted; parts forward_contracted and
-    adjoint_contracted): status, iterations, residual and the relative
-    difference of the sampled rows from the plain build's.  On this system
-    the stopping iteration depends on that rounding; the parity test takes
-    the contracted count as the yardstick for a GPU that fuses its
-    multiply-adds.
+  - the same solves by two other builds of the oracle's source, each a
+    different valid rounding of the same arithmetic: contracted multiply-adds
+    (oracle.load_contracted; parts forward_contracted, adjoint_contracted)
+    and rows longer than 2,048 entries summed in 4,096-entry chunks
+    (oracle.load_chunked; parts forward_chunked, adjoint_chunked): status,
+    iterations, residual and the relative difference of the sampled rows
+    from the plain build's.  On this system (hub rows of up to a million
+    entries, kappa ~ 1e8) the stopping iteration moves with the summation
+    order of the long rows; the parity test's iteration gate spans the
+    builds' counts.
 
 Parts can be run one at a time (e.g. `... make_powerlaw_golden.py
 adjoint_contracted`); a part reuses the stored results of the others when
@@ -86,11 +89,11 @@ def record(p, rhs, rows, what):
     }
 
 
-def record_contracted(p, rhs, rows, plain, what):
+def record_variant(p, rhs, rows, plain, what, lib, name):
     t0 = time.time()
-    x, st, it, rr = oracle.pcg(p.A, p.G, p.eps, rhs, p.rtol, p.maxit, lib=oracle.load_contracted())
+    x, st, it, rr = oracle.pcg(p.A, p.G, p.eps, rhs, p.rtol, p.maxit, lib=lib)
     ref = np.asarray(plain["samples"])
-    print(f"[golden] {what} contracted: status {st}, {it} iterations, relres {rr:.3e}, "
+    print(f"[golden] {what} {name}: status {st}, {it} iterations, relres {rr:.3e}, "
           f"{time.time() - t0:.0f} s", flush=True)
     return {"status": int(st), "iterations": int(it), "rel_residual": float(rr),
             "rel_change_samples": rel(x[rows], ref), "rel_change_norm":
@@ -114,8 +117,10 @@ def main():
                     "b": digest(p.b), "w": digest(p.w)},
         "rows": [int(r) for r in rows],
     }
-    parts = sys.argv[1:] or ["forward", "adjoint", "forward_contracted", "adjoint_contracted"]
-    names = ("forward", "adjoint", "forward_contracted", "adjoint_contracted")
+    parts = sys.argv[1:] or ["forward", "adjoint", "forward_contracted", "adjoint_contracted",
+                             "forward_chunked", "adjoint_chunked"]
+    names = ("forward", "adjoint", "forward_contracted", "adjoint_contracted", "forward_chunked",
+             "adjoint_chunked")
     if os.path.exists(OUT):
         old = json.load(open(OUT))
         if old.get("digests") == out["digests"]:
@@ -127,10 +132,10 @@ def main():
     if "adjoint" in parts:
         # L = <w, x>: the adjoint solve's right-hand side is dL/dx = w
         out["adjoint"] = record(p, p.w, rows, "adjoint")
-    if "forward_contracted" in parts:
-        out["forward_contracted"] = record_contracted(p, p.b, rows, out["forward"], "forward")
-    if "adjoint_contracted" in parts:
-        out["adjoint_contracted"] = record_contracted(p, p.w, rows, out["adjoint"], "adjoint")
+    for part, rhs in (("forward", p.b), ("adjoint", p.w)):
+        for name, load in (("contracted", oracle.load_contracted), ("chunked", oracle.load_chunked)):
+            if f"{part}_{name}" in parts:
+                out[f"{part}_{name}"] = record_variant(p, rhs, rows, out[part], part, load(), name)
     with open(OUT, "w") as f:
         json.dump(out, f, indent=1)
     print(f"[golden] wrote {OUT} in {time.time() - t0:.0f} s", flush=True)
