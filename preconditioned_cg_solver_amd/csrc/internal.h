@@ -82,6 +82,11 @@ __host__ __device__ inline size_t bsell_val(int q, int r, int c, int li) {
 
 // Right-hand sides advanced together by one pass of the multi-RHS solver.
 constexpr int kMaxRhs = 8;
+// A pass of 8 columns over a SELL matrix whose stored entries reach further
+// than kFarRows rows from the diagonal runs as two passes of 4: the 64-byte
+// rows gathered at both far ends, 2 x kFarRows rows apart, then no longer
+// stay in an XCD's 4 MB L2 beside the rows in flight.
+constexpr int kFarRows = 8192;
 
 // Tile descriptor (CSR engine).
 //   kind 0: rows [a, b) staged through LDS, 2^c lanes per row; their
@@ -135,6 +140,7 @@ struct MatView {
   int nlong_rows = 0;            // rows split into chunks
   int n_long_part = 0;           // partial slots needed by the long-row chunks
   int max_row = -1;              // longest row in blocks (BSR; -1 = not computed)
+  int max_dist = -1;             // largest |col - row| (CSR in the SELL layout; -1 = unknown)
   const int* long_rows = nullptr;  // row index of each of the nlong_rows long rows (CSR)
   // SELL-64 copy (owned), built once when the rows qualify: slice s holds
   // rows [64 s, 64 s + 64); slot j of its row 64 s + l sits at

@@ -764,6 +764,18 @@ __global__ __launch_bounds__(kWG) void mvec_r(MArgs<T> a) {
   mfinish<T, MM_GT, K>(a, dot, s_red);
 }
 
+// Columns of a pass: the n x kw block src into columns [0, kw) of the n x ld
+// array dst (which points at the pass's first column).
+template <typename T>
+__global__ __launch_bounds__(kWG) void mcopy_cols(const T* __restrict__ src, int kw,
+                                                  T* __restrict__ dst, int ld, int n) {
+  const size_t m = (size_t)n * kw;
+  for (size_t f = blockIdx.x * (size_t)kWG + threadIdx.x; f < m; f += (size_t)gridDim.x * kWG) {
+    const size_t i = f / kw;
+    dst[i * ld + (f - i * kw)] = src[f];
+  }
+}
+
 // Start-up: R_0 = B (columns c0 .. c0 + K - 1 of the caller's n x ldb array),
 // X = 0 on the same columns, partials of ||b_c||^2.
 template <typename T, int K>
@@ -892,8 +904,16 @@ bool mfused() {
   return e && !strcmp(e, "fused");
 }
 
-// Columns handled per pass: the largest of 8, 4, 2, 1 that fits k.
-int chunk_width(int k) { return k >= 8 ? 8 : k >= 4 ? 4 : k >= 2 ? 2 : 1; }
+// Columns handled per pass: the largest of 8, 4, 2, 1 that fits k, with
+// passes of 4 instead of 8 on a SELL matrix reaching further than kFarRows
+// from its diagonal (3D Poisson 128^3: 8-column products ran 2.3x the time
+// of 4-column ones, so two passes of 4 beat one of 8 by 10%; 2D heat 512^2,
+// whose rows reach 512 rows out, keeps passes of 8).
+int chunk_width(const sla_mat& A, int k) {
+  const bool far = A.bs == 1 && A.fwd.sell && A.fwd.max_dist > kFarRows;
+  if (k >= 8 && !far) return 8;
+  return k >= 4 ? 4 : k >= 2 ? 2 : 1;
+}
 
 struct MWork {
   MState* st;
@@ -901,9 +921,10 @@ struct MWork {
   double* prr;
   double* prho;
   void* vec[7];  // P0 P1 R0 R1 Q T Z, n x K each
+  void* xblk;    // the pass's X, n x K (only when k is cut into several passes)
 };
 
-MWork mcarve(const sla_mat& A, int kw, void* work) {
+MWork mcarve(const sla_mat& A, int kw, bool xblk, void* work) {
   MWork w;
   char* p = (char*)work;
   const size_t es = A.dtype == SLA_F64 ? 8 : 4;
@@ -920,6 +941,7 @@ MWork mcarve(const sla_mat& A, int kw, void* work) {
     w.vec[i] = p;
     p += align_up((size_t)A.n() * kw * es);
   }
+  w.xblk = xblk ? p : nullptr;
   return w;
 }
 
@@ -928,8 +950,8 @@ static_assert(4 * sizeof(MState) <= kPollBytes, "polling record too small");
 // One pass of K columns: b and x point at the pass's first column of the
 // caller's n x ld arrays.
 template <typename T, int K>
-sla_status mpcg_pass(const sla_mat& A, const sla_mat& G, double eps, const T* b, T* x, int ld,
-                     double rtol, int maxit, const MWork& w, hipStream_t s,
+sla_status mpcg_pass(const sla_mat& A, const sla_mat& G, double eps, const T* b, int ldb, T* x,
+                     int ldx, double rtol, int maxit, const MWork& w, hipStream_t s,
                      sla_solve_info* info, sla_status* cst) {
   const int n = (int)A.n();
   T *P[2] = {(T*)w.vec[0], (T*)w.vec[1]}, *R[2] = {(T*)w.vec[2], (T*)w.vec[3]};
@@ -948,7 +970,7 @@ sla_status mpcg_pass(const sla_mat& A, const sla_mat& G, double eps, const T* b,
     a->eps = eps;
     a->ld = K;
     a->xv = x;
-    a->ldx = ld;
+    a->ldx = ldx;
     a->npin = grid;
   }
   aA.pin = w.prho;
@@ -971,7 +993,7 @@ sla_status mpcg_pass(const sla_mat& A, const sla_mat& G, double eps, const T* b,
   aR.in1 = q;
 
   // start-up: R_0 = B, X = 0, ||b_c||^2; T = G^T R_0; Z_0 = G T + eps R_0
-  hipLaunchKernelGGL((minit<T, K>), dim3(grid), dim3(kWG), 0, s, b, ld, R[0], x, ld, n, w.prr);
+  hipLaunchKernelGGL((minit<T, K>), dim3(grid), dim3(kWG), 0, s, b, ldb, R[0], x, ldx, n, w.prr);
   SLA_HIP(hipGetLastError());
   MArgs<T> a0 = aT;
   a0.in0 = R[0];
@@ -1093,24 +1115,39 @@ template <typename T>
 sla_status mpcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, T* x, int k,
                      double rtol, int maxit, void* work, hipStream_t s, sla_solve_info* info,
                      sla_status* cst) {
-  const MWork w = mcarve(A, chunk_width(k), work);
+  const int kw0 = chunk_width(A, k);
+  // several passes: each pass keeps its X columns contiguous in the
+  // workspace (the per-iteration X update then streams whole rows) and
+  // copies them into the caller's n x k array when it ends
+  const bool staged = kw0 < k;
+  const MWork w = mcarve(A, kw0, staged, work);
   sla_status worst = SLA_OK;
   for (int c0 = 0; c0 < k;) {
-    const int kw = chunk_width(k - c0);
+    const int kw = chunk_width(A, k - c0);
     sla_status st;
     sla_solve_info* ci = info ? info + c0 : nullptr;
     sla_status* cs = cst ? cst + c0 : nullptr;
+    T* xp = staged ? (T*)w.xblk : x + c0;
+    const int ldx = staged ? kw : k;
     switch (kw) {
-      case 8: st = mpcg_pass<T, 8>(A, G, eps, b + c0, x + c0, k, rtol, maxit, w, s, ci, cs); break;
-      case 4: st = mpcg_pass<T, 4>(A, G, eps, b + c0, x + c0, k, rtol, maxit, w, s, ci, cs); break;
-      case 2: st = mpcg_pass<T, 2>(A, G, eps, b + c0, x + c0, k, rtol, maxit, w, s, ci, cs); break;
-      default: st = mpcg_pass<T, 1>(A, G, eps, b + c0, x + c0, k, rtol, maxit, w, s, ci, cs); break;
+      case 8: st = mpcg_pass<T, 8>(A, G, eps, b + c0, k, xp, ldx, rtol, maxit, w, s, ci, cs); break;
+      case 4: st = mpcg_pass<T, 4>(A, G, eps, b + c0, k, xp, ldx, rtol, maxit, w, s, ci, cs); break;
+      case 2: st = mpcg_pass<T, 2>(A, G, eps, b + c0, k, xp, ldx, rtol, maxit, w, s, ci, cs); break;
+      default: st = mpcg_pass<T, 1>(A, G, eps, b + c0, k, xp, ldx, rtol, maxit, w, s, ci, cs); break;
     }
     if (st == SLA_ERR_HIP || st == SLA_ERR_OOM) return st;
+    if (staged) {
+      const size_t m = (size_t)A.n() * kw;
+      const int g = (int)std::min<size_t>((m + kWG - 1) / kWG, 65536);
+      hipLaunchKernelGGL(mcopy_cols<T>, dim3(g), dim3(kWG), 0, s, (const T*)w.xblk, kw, x + c0, k,
+                         (int)A.n());
+      SLA_HIP(hipGetLastError());
+    }
     if (st < 0 && worst >= 0) worst = st;
     else if (st == SLA_NOT_CONVERGED && worst == SLA_OK) worst = st;
     c0 += kw;
   }
+  if (staged) SLA_HIP(hipStreamSynchronize(s));
   return worst;
 }
 
@@ -1128,7 +1165,7 @@ hipError_t spmm_pass(const sla_mat& A, bool transpose, const T* x, T* y, int ld,
 template <typename T>
 sla_status spmm_impl(const sla_mat& A, bool transpose, const T* x, T* y, int k, hipStream_t s) {
   for (int c0 = 0; c0 < k;) {
-    const int kw = chunk_width(k - c0);
+    const int kw = chunk_width(A, k - c0);
     switch (kw) {
       case 8: SLA_HIP((spmm_pass<T, 8>(A, transpose, x + c0, y + c0, k, s))); break;
       case 4: SLA_HIP((spmm_pass<T, 4>(A, transpose, x + c0, y + c0, k, s))); break;
@@ -1144,9 +1181,10 @@ sla_status spmm_impl(const sla_mat& A, bool transpose, const T* x, T* y, int k, 
 
 size_t workspace_base_multi(const sla_mat& A, int k) {
   const size_t es = A.dtype == SLA_F64 ? 8 : 4;
+  const int kw = chunk_width(A, k);
   const size_t lockstep = align_up(sizeof(MState)) +
                           3 * align_up((size_t)max_grid() * kMaxRhs * sizeof(double)) +
-                          7 * align_up((size_t)A.n() * chunk_width(k) * es);
+                          (kw < k ? 8 : 7) * align_up((size_t)A.n() * kw * es);
   return std::max(lockstep, small_states_bytes(k));
 }
 

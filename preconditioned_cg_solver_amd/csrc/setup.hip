@@ -952,6 +952,7 @@ sla_status build_sell(MatView& view, int64_t n, int64_t nnz, int32_t dtype, void
   if (!sliced_layout_fits(nslices, h[0], kSlice, kSellTail)) return SLA_OK;
   const int64_t total = h[1];
   if (h[0] > kSellMaxWidth || total * 100 > nnz * (100 + kSellMaxPadPct)) return SLA_OK;
+  view.max_dist = h[2];
   const size_t es = dtype == SLA_F64 ? 8 : 4;
   const char* e16 = getenv("SLA_SELL16");
   const bool rel16 = h[2] <= 32767 && !(e16 && e16[0] == '0');

@@ -225,6 +225,8 @@ def problem(key):
             p = I.make_problem(4, size=20000)
         elif key == "heat2d_64":
             p = I.make_problem(1, size=64)
+        elif key == "poisson3d_92":
+            p = I.make_problem(2, size=92)
         else:
             raise KeyError(key)
         _cache[key] = p

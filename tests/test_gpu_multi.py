@@ -230,3 +230,24 @@ def test_solve_multi_full_size_poisson3d_128(k):
         assert infos[c].status == B.OK and infos[c].converged
         assert iters_close(infos[c].iterations, int(it_r[c])), (c, infos[c].iterations, it_r[c])
         assert rel(Xg[:, c], Xr[:, c]) <= 1e-8, (c, rel(Xg[:, c], Xr[:, c]))
+
+
+@pytest.mark.parametrize("k", [5, 11])
+def test_solve_multi_passes_on_a_far_reaching_matrix(k):
+    """3D Poisson 92^3 reaches 8,464 rows from its diagonal, so its columns
+    run in passes of at most 4 with each pass's X kept in the workspace
+    (k = 5: 4 + 1, k = 11: 4 + 4 + 2 + 1); every column against the oracle's
+    solve of it, and the adjoint's dL/dB and summed dL/dA."""
+    p = problem("poisson3d_92")
+    Bm = rhs(p.A.n, k, 31)
+    say("solve_multi passes, far-reaching matrix", k, p.A.n)
+    Xg, infos = check_solve(p, Bm, p.rtol, p.maxit)
+    W = rhs(p.A.n, k, 32)
+    A, G = create(p.A, validate=False), create(p.G, transpose=True, validate=False)
+    GB, gv, ainfos = B.sla_pcg_adjoint_multi(A, G, p.eps, tdev(Xg), tdev(W), rtol=p.rtol,
+                                             maxit=p.maxit)
+    Xr, _, _, _, _ = oracle.pcg_multi(p.A, p.G, p.eps, Bm, p.rtol, p.maxit)
+    lam, gval, st, _, _, _ = oracle.adjoint_multi(p.A, p.G, p.eps, Xr, W, p.rtol, p.maxit)
+    assert st == oracle.OK
+    assert rel(host(GB), lam) <= 1e-7
+    assert rel(host(gv), gval) <= 1e-7
