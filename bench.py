@@ -212,7 +212,7 @@ def _kernel_key(nm):
 
 
 def _describe(key):
-    m = re.match(r"(sell_step|csr_step|bsell_step|bsr3_step)<\w+, (\d+)", key)
+    m = re.match(r"(sell_step|sell_win_step|csr_step|bsell_step|bsr3_step)<\w+, (\d+)", key)
     if m:
         return STEP_NAMES.get(int(m.group(2)), m.group(2))
     m = re.match(r"(msell_step|mbsell_step|mtile_step|mrow_step)<\w+, (\d+), (\d+)", key)
@@ -346,11 +346,13 @@ def summarize_trace(trace_dir, bench_json=None, trace_args="--steps 2 --warmup 1
         lines.append(f"| `{k}` | {len(d)} | {statistics.fmean(d):.2f} | "
                      f"{100 * sum(d) * 1e3 / total:.2f} | {len(w)} | {statistics.fmean(w):.2f} |")
     step = [(t0, t1) for t0, t1, k in recs
-            if k.split("<")[0] in ("sell_step", "csr_step", "bsell_step", "bsr3_step")
+            if k.split("<")[0] in ("sell_step", "sell_win_step", "csr_step", "bsell_step",
+                                   "bsr3_step")
             and (t1 - t0) / 1e3 > cut[k]]
     gaps = sorted(max(0, b0 - a1) / 1e3 for (a0, a1), (b0, b1) in zip(step, step[1:]))
     a_key = next((k for k, _ in rows
-                  if re.match(r"(sell_step|bsell_step|csr_step|bsr3_step)<\w+, (2|8),", k)), None)
+                  if re.match(r"(sell_win_step|sell_step|bsell_step|csr_step|bsr3_step)<\w+, (2|8),",
+                              k)), None)
     a_work = [v for v in by.get(a_key, []) if v > cut[a_key]]
     cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d {d} -o bench -- "
            "python -u bench.py {a}").format(d=trace_dir, a=trace_args)
@@ -413,12 +415,19 @@ def cpu_baseline(p, w, min_seconds, expected_iters):
     import oracle
     threads = oracle.num_threads()
     log(f"cpu oracle: forward + adjoint solves for >= {min_seconds:.0f} s, {threads} threads")
-    t0 = time.perf_counter()
-    _, _, it, _ = oracle.pcg(p.A, p.G, p.eps, p.b, p.rtol, min(3, p.maxit))
-    per_it = (time.perf_counter() - t0) / max(it, 1)
+    # per-iteration cost from two short probes (3 and 6 iterations), so the
+    # fixed cost of a solve (the oracle's own G^T build) is not counted per
+    # iteration
+    probe = []
+    for m in (3, 6):
+        t0 = time.perf_counter()
+        oracle.pcg(p.A, p.G, p.eps, p.b, p.rtol, min(m, p.maxit))
+        probe.append(time.perf_counter() - t0)
+    per_it = max((probe[1] - probe[0]) / 3, 1e-9)
+    fixed = max(probe[0] - 3 * per_it, 0.0)
     cap = p.maxit
-    if per_it * expected_iters > 3 * min_seconds:
-        cap = max(3, int(min_seconds / per_it / 2))
+    if 2 * fixed + per_it * expected_iters > 3 * min_seconds:
+        cap = max(3, int((min_seconds / 2 - fixed) / per_it))
     its, reps = 0, 0
     t0 = time.perf_counter()
     while reps < 20 and (reps == 0 or time.perf_counter() - t0 < min_seconds):
@@ -738,7 +747,7 @@ def main():
     workload = p.name + ("_f32" if args.dtype == "f32" else "")
     tr = traffic_if_current(workload)
     a_mode, gt_mode = (2, 4) if fused else (8, 9)
-    step_re = r"(sell_step|csr_step|bsell_step|bsr3_step)<\w+, {}[,>]"
+    step_re = r"(sell_win_step|sell_step|csr_step|bsell_step|bsr3_step)<\w+, {}[,>]"
     traffic = kernel_bytes(tr, step_re.format(a_mode)) if has_a else None
     physical = None
     if tr:
@@ -760,7 +769,12 @@ def main():
                           "frac": it_bytes * fi.iterations / tts / 1e9 / HBM_PEAK_GBS}
                          if it_bytes else None}
     moved = moved_bytes_a_step(p.A, n, sv) if fused else None
-    if fused and bs == 1:
+    if fused and bs == 1 and slice_offset_slots(p.A) is not None and \
+            os.environ.get("SLA_WIN", "1") != "0":
+        a_kernel = (f"sell_win_step<{'double' if sv == 8 else 'float'}, A step> (q = A p with "
+                    "p = z + beta p_old formed on the fly, near slots from an LDS window, "
+                    "x += alpha_prev p_old, p.q partials)")
+    elif fused and bs == 1:
         a_kernel = (f"sell_step<{'double' if sv == 8 else 'float'}, A step> (q = A p with "
                     "p = z + beta p_old formed on the fly, x += alpha_prev p_old, p.q partials)")
     elif fused:
