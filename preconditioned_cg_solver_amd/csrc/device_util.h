@@ -66,8 +66,20 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
 }
 
 __device__ __forceinline__ double sum_partials(const double* __restrict__ p, int np, double* red) {
+  // each thread adds p[tid], p[tid + kWG], ... in index order; the loads of
+  // eight strides are issued together (one memory round trip per eight
+  // instead of one per partial: the partials were written by every XCD and
+  // miss this XCD's L2 the first time)
   double s = 0.0;
-  for (int i = threadIdx.x; i < np; i += kWG) s += p[i];
+  int i = threadIdx.x;
+  for (; i + 7 * kWG < np; i += 8 * kWG) {
+    double v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[i + u * kWG];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; i < np; i += kWG) s += p[i];
   return block_sum(s, red);
 }
 

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <cmath>
 #include <cstdlib>
 #include <map>
 #include <mutex>
@@ -171,6 +172,14 @@ int step_grid(int ntiles) {
   return std::max(g, 1);
 }
 
+// Grid of a product that reads no partials: one work item per workgroup, up
+// to kWideGrid times the resident capacity, a multiple of 8.
+int wide_grid(int ntiles) {
+  int g = std::min(std::max(ntiles, 1), kWideGrid * max_grid());
+  if (g >= 8) g &= ~7;
+  return std::max(g, 1);
+}
+
 // Work items of a product over one orientation: SELL slices grouped by
 // workgroup (one per wavefront), LDS tiles, or BSR block-row tiles.
 int view_tiles(const sla_mat& m, const MatView& v) {
@@ -213,13 +222,36 @@ hipEvent_t timing_event() {
   return nullptr;
 }
 
-int batch_iters() {
-  static int b = [] {
+// Iterations per host-polled batch.  Two batches are queued at a time and
+// the device decides when to stop, so after the converging iteration up to
+// about two batches of launches still run (each returns at once but costs
+// its dispatch: a few microseconds for a grid over every CU).  A batch of
+// about 0.8 ms keeps the device busy while the host waits on the previous
+// batch and queues the next one, and bounds that tail on short solves of big
+// matrices (the elasticity system converges in a few dozen iterations of
+// ~0.25 ms).  `iter_us` is the caller's estimate of one iteration;
+// SLA_BATCH_ITERS overrides.
+int batch_iters(double iter_us) {
+  static const int env = [] {
     const char* e = getenv("SLA_BATCH_ITERS");
-    int v = e ? atoi(e) : 16;
-    return std::max(1, std::min(v, 4096));
+    return e ? std::max(1, std::min(atoi(e), 4096)) : 0;
   }();
-  return b;
+  if (env > 0) return env;
+  const double b = std::ceil(800.0 / std::max(iter_us, 1.0));
+  return (int)std::max(2.0, std::min(b, 16.0));
+}
+
+// Rough duration of one iteration over A and G with k right-hand sides
+// (us): the value and index streams of A, G and G^T once and ten vector
+// passes of n entries per column at 5 TB/s, plus 3 us per kernel launch.
+// Only the batch size depends on it.
+double iteration_estimate_us(const sla_mat& A, const sla_mat& G, int elem_bytes, int k,
+                             int launches) {
+  auto stream = [&](const sla_mat& m) {
+    return (double)m.nnz() * elem_bytes + (double)m.nnzb * 4.0;
+  };
+  const double bytes = stream(A) + 2.0 * stream(G) + 10.0 * (double)A.n() * elem_bytes * k;
+  return bytes / 5.0e6 + 3.0 * launches;
 }
 
 }  // namespace sla

@@ -343,13 +343,19 @@ hipError_t buf_alloc(void** p, size_t bytes);
 void buf_free(void* p);
 size_t align_up(size_t v);
 int max_grid();
+// Separate iteration form on BSR: products on up to kWideGrid x the
+// resident grid.
+constexpr int kWideGrid = 4;
+int wide_grid(int ntiles);
 int step_grid(int ntiles);
 int view_tiles(const sla_mat& m, const MatView& v);
 size_t matrix_bytes(const sla_mat& m);
 size_t stream_bytes(const sla_mat& m, const MatView& v);
 size_t mall_budget();
 hipEvent_t timing_event();
-int batch_iters();
+int batch_iters(double iter_us);
+double iteration_estimate_us(const sla_mat& A, const sla_mat& G, int elem_bytes, int k,
+                             int launches);
 
 // Spectrum of the Lanczos tridiagonal (spectrum.cpp, host only).
 sla_status lanczos_extremes(const double* alpha, const double* beta, int32_t k, double* lmin,

@@ -128,7 +128,22 @@ __device__ __forceinline__ void sum_partials_k(const double* __restrict__ p, int
                                                double (&out)[K], double* red) {
 #pragma unroll
   for (int c = 0; c < K; ++c) out[c] = 0.0;
-  for (int i = threadIdx.x; i < np; i += kWG) {
+  // in index order per thread; the loads of 16 / K strides (at least one)
+  // are issued together
+  constexpr int S = K >= 16 ? 1 : 16 / K;
+  int i = threadIdx.x;
+  for (; i + (S - 1) * kWG < np; i += S * kWG) {
+    double v[S][K];
+#pragma unroll
+    for (int u = 0; u < S; ++u)
+#pragma unroll
+      for (int c = 0; c < K; ++c) v[u][c] = p[(size_t)(i + u * kWG) * K + c];
+#pragma unroll
+    for (int u = 0; u < S; ++u)
+#pragma unroll
+      for (int c = 0; c < K; ++c) out[c] += v[u][c];
+  }
+  for (; i < np; i += kWG) {
 #pragma unroll
     for (int c = 0; c < K; ++c) out[c] += p[(size_t)i * K + c];
   }
@@ -1009,7 +1024,7 @@ sla_status mpcg_pass(const sla_mat& A, const sla_mat& G, double eps, const T* b,
   hipEvent_t* mev = lease.p->ev;
   std::deque<int> pend;
   int next_slot = 0;
-  const int B = batch_iters();
+  const int B = batch_iters(iteration_estimate_us(A, G, (int)sizeof(T), K, fused ? 3 : 5));
   int k = 1;
   bool finished = false;
   while (!finished) {

@@ -906,7 +906,30 @@ __global__ __launch_bounds__(kWG) void vec_p_update(StepArgs<T> a) {
   __shared__ int s_flag;
   Coef<T> cf;
   if (!prologue<T, MODE>(a, cf, s_red, &s_flag)) return;
-  for (int i = blockIdx.x * kWG + threadIdx.x; i < a.n; i += gridDim.x * kWG) {
+  // four grid strides per round, all loads issued before the stores
+  const int stride = gridDim.x * kWG;
+  int i = blockIdx.x * kWG + threadIdx.x;
+  for (; i + 3 * stride < a.n; i += 4 * stride) {
+    T z[4], po[4], xv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      z[u] = a.in0[i + u * stride];
+      if constexpr (MODE != M_A1) {
+        po[u] = a.in1[i + u * stride];
+        xv[u] = a.xv[i + u * stride];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if constexpr (MODE == M_A1) {
+        st_out<2>(a.own + i + u * stride, z[u]);
+      } else {
+        st_out<2>(a.own + i + u * stride, fma(cf.c, po[u], z[u]));
+        st_out<1>(a.xv + i + u * stride, fma(cf.c2, po[u], xv[u]));
+      }
+    }
+  }
+  for (; i < a.n; i += stride) {
     if constexpr (MODE == M_A1) {
       st_out<2>(a.own + i, a.in0[i]);
     } else {
@@ -918,7 +941,8 @@ __global__ __launch_bounds__(kWG) void vec_p_update(StepArgs<T> a) {
 }
 
 // r_k = r_{k-1} - alpha_k q and ||r_k||^2 partials; the prologue is the G^T
-// step's (sigma, alpha_k, breakdown).
+// step's (sigma, alpha_k, breakdown).  Each thread adds its entries in index
+// order.
 template <typename T>
 __global__ __launch_bounds__(kWG) void vec_r_update(StepArgs<T> a) {
   __shared__ double s_red[kWaves];
@@ -926,7 +950,23 @@ __global__ __launch_bounds__(kWG) void vec_r_update(StepArgs<T> a) {
   Coef<T> cf;
   if (!prologue<T, M_GT>(a, cf, s_red, &s_flag)) return;
   double dot = 0.0;
-  for (int i = blockIdx.x * kWG + threadIdx.x; i < a.n; i += gridDim.x * kWG) {
+  const int stride = gridDim.x * kWG;
+  int i = blockIdx.x * kWG + threadIdx.x;
+  for (; i + 3 * stride < a.n; i += 4 * stride) {
+    T ro[4], q[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      ro[u] = a.in0[i + u * stride];
+      q[u] = a.in1[i + u * stride];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const T rn = fma(cf.c, q[u], ro[u]);
+      a.own[i + u * stride] = rn;
+      dot += (double)rn * (double)rn;
+    }
+  }
+  for (; i < a.n; i += stride) {
     const T rn = fma(cf.c, a.in1[i], a.in0[i]);
     a.own[i] = rn;
     dot += (double)rn * (double)rn;
@@ -1382,20 +1422,21 @@ hipError_t launch_step(const sla_mat& m, const StepArgs<T>& a, int grid, hipStre
     if (nt) hipLaunchKernelGGL((csr_step<T, MODE, true>), dim3(grid), dim3(kWG), 0, s, a);
     else hipLaunchKernelGGL((csr_step<T, MODE, false>), dim3(grid), dim3(kWG), 0, s, a);
   } else if (a.sc || a.sd) {
-    // block slots per load round: 4 for wide block rows, else 2 (fewer
-    // registers, more waves in flight; measured on the 27-point block stencil
-    // and its block triangles)
+    // block slots per load round: 3 for wide block rows, else 2 (fewer
+    // registers, more waves in flight, and no partial last round on the
+    // 27-slot rows of the 27-point block stencil and the 14-slot rows of its
+    // block triangles; 2, 3, 4 and 6 measured there)
     const dim3 g(grid), b(kWG);
     const bool wide = a.sell_w > 16;
     if (a.sd) {
-      if (nt && wide) hipLaunchKernelGGL((bsell_step<T, MODE, true, true, 4>), g, b, 0, s, a);
+      if (nt && wide) hipLaunchKernelGGL((bsell_step<T, MODE, true, true, 3>), g, b, 0, s, a);
       else if (nt) hipLaunchKernelGGL((bsell_step<T, MODE, true, true, 2>), g, b, 0, s, a);
-      else if (wide) hipLaunchKernelGGL((bsell_step<T, MODE, false, true, 4>), g, b, 0, s, a);
+      else if (wide) hipLaunchKernelGGL((bsell_step<T, MODE, false, true, 3>), g, b, 0, s, a);
       else hipLaunchKernelGGL((bsell_step<T, MODE, false, true, 2>), g, b, 0, s, a);
     } else {
-      if (nt && wide) hipLaunchKernelGGL((bsell_step<T, MODE, true, false, 4>), g, b, 0, s, a);
+      if (nt && wide) hipLaunchKernelGGL((bsell_step<T, MODE, true, false, 3>), g, b, 0, s, a);
       else if (nt) hipLaunchKernelGGL((bsell_step<T, MODE, true, false, 2>), g, b, 0, s, a);
-      else if (wide) hipLaunchKernelGGL((bsell_step<T, MODE, false, false, 4>), g, b, 0, s, a);
+      else if (wide) hipLaunchKernelGGL((bsell_step<T, MODE, false, false, 3>), g, b, 0, s, a);
       else hipLaunchKernelGGL((bsell_step<T, MODE, false, false, 2>), g, b, 0, s, a);
     }
   } else {
@@ -1523,7 +1564,7 @@ struct Work {
 };
 
 size_t partial_slots(const sla_mat& A) {
-  return (size_t)max_grid() + (size_t)long_rows_bound(A);
+  return (size_t)kWideGrid * max_grid() + (size_t)long_rows_bound(A);
 }
 
 // Bytes from the start of the workspace that must be zero when a solve or
@@ -1620,13 +1661,26 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
   // long-row scratch (every ticket is back at 0 when a product ends)
   const LongScratch lsA{w.lpart, w.lcnt}, lsG = lsA, lsT = lsA;
   const int ntA = view_tiles(A, A.fwd), ntG = view_tiles(G, G.fwd), ntT = view_tiles(G, G.tr);
-  const int grid = step_grid(std::max(ntA, std::max(ntG, ntT)));
+  const bool fused = use_fused(A);
+  // Fused form: every kernel sums the previous one's per-workgroup partials
+  // in its prologue, so all run on the resident-capacity grid.  Separate
+  // form on BSR: the bare products read no partials and run one work item
+  // per workgroup (up to kWideGrid times that grid; the dispatcher then
+  // balances the last round; elasticity 64^3 x 3: A product 101 -> 94 us),
+  // while the vector passes, which sum the products' partials, keep the
+  // resident grid.  CSR keeps the resident grid throughout: on the
+  // power-law system the gain was 2%, and the grid sets the partial sums'
+  // rounding order, which moves that ill-conditioned system's stopping
+  // iteration by a few percent.
+  const bool wide = !fused && A.bs > 1;
+  const int grid = wide ? wide_grid(std::max(ntA, std::max(ntG, ntT)))
+                        : step_grid(std::max(ntA, std::max(ntG, ntT)));
+  const int gridV = wide ? std::min(grid, max_grid()) : grid;
   const int npA = grid + A.fwd.nlong_rows, npG = grid + G.fwd.nlong_rows,
             npT = grid + G.tr.nlong_rows;
 
   SLA_HIP(hipMemsetAsync(w.st, 0, zeroed_bytes(A), s));
   const MallPlan plan = mall_plan(A, G);
-  const bool fused = use_fused(A);
   const int win = win_level();
 
   StepArgs<T> aA{}, aT{}, aG{};
@@ -1705,7 +1759,7 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
   int pend[3];
   int npend = 0, pfirst = 0;
   int next_slot = 0;
-  const int B = batch_iters();
+  const int B = batch_iters(iteration_estimate_us(A, G, (int)sizeof(T), 1, fused ? 3 : 5));
   int k = 1;
   bool finished = false;
   while (!finished) {
@@ -1732,9 +1786,9 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
           aV.in1 = P[(kk - 1) & 1];
           aV.own = P[kk & 1];
           if (kk == 1)
-            hipLaunchKernelGGL((vec_p_update<T, M_A1>), dim3(grid), dim3(kWG), 0, s, aV);
+            hipLaunchKernelGGL((vec_p_update<T, M_A1>), dim3(gridV), dim3(kWG), 0, s, aV);
           else
-            hipLaunchKernelGGL((vec_p_update<T, M_A>), dim3(grid), dim3(kWG), 0, s, aV);
+            hipLaunchKernelGGL((vec_p_update<T, M_A>), dim3(gridV), dim3(kWG), 0, s, aV);
           SLA_HIP(hipGetLastError());
           aA.k = kk;
           aA.in0 = P[kk & 1];
@@ -1744,14 +1798,14 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
           aR.k = kk;
           aR.in0 = R[(kk - 1) & 1];
           aR.own = R[kk & 1];
-          hipLaunchKernelGGL((vec_r_update<T>), dim3(grid), dim3(kWG), 0, s, aR);
+          hipLaunchKernelGGL((vec_r_update<T>), dim3(gridV), dim3(kWG), 0, s, aR);
           SLA_HIP(hipGetLastError());
           aT.k = kk;
           aT.in0 = R[kk & 1];
           hipEvent_t et = rec.begin(1, kk);
           SLA_HIP((launch_step<T, M_GTU>(G, aT, grid, s, plan.nt_t, win)));
           rec.end(et, 1, kk);
-          aG.npin = grid;  // rr partials now come from vec_r_update
+          aG.npin = gridV;  // rr partials now come from vec_r_update
         }
         aG.k = kk;
         aG.rv = R[kk & 1];
