@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "PCG iters/sec + SpMV HBM GB/s (% of peak), 3D Poisson 128^3 fp64, 1 GPU"
-PROF_EVERY = 7
+PROF_EVERY = 23
 KERNEL_SRCS = [os.path.join(ROOT, "preconditioned_cg_solver_amd", "csrc", f)
                for f in ("solver.hip", "multi.hip", "device_util.h")]
 
@@ -609,9 +609,10 @@ def main():
         log(f"forward iterations {fi.iterations}, adjoint iterations {ai.iterations}")
 
     # the A step's duration, live over the timed steps: events bracket the A
-    # step of every PROF_EVERY-th iteration (a stride coprime with the
-    # 16-iteration host batches, so samples rotate through batch positions);
-    # bracketing every launch would slow the measured solve by ~3%
+    # step of every PROF_EVERY-th iteration (a prime stride, so samples rotate
+    # through the positions within the host's batches); each bracketed launch
+    # leaves a ~4.5 us gap on either side in the queue, so every launch
+    # bracketed would slow the measured solve by ~8%, every 23rd by ~0.4%
     B.sla_reset_profile()
     B.sla_set_profiling_stride(PROF_EVERY)
     B.sla_set_profiling(["a_step"])

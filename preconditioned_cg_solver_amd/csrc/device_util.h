@@ -10,6 +10,18 @@
 
 namespace sla {
 
+// The host-mapped polling record of a batch of iterations, written by the
+// lead thread of the batch's last G step once its prologue has decided: system-scope
+// vector stores, the iteration index last (release), which the host waits
+// for.  Only this kernel writes the record after the host cleared it.
+__device__ __forceinline__ void post_poll(SolverState* p, int done, int k, double rr,
+                                          double bb) {
+  __hip_atomic_store(&p->done, done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  __hip_atomic_store(&p->rr, rr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  __hip_atomic_store(&p->bb, bb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  __hip_atomic_store(&p->exit_iter, k, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 // ---------------------------------------------------------------------------
 // Reductions (deterministic: fixed association order)
 // ---------------------------------------------------------------------------
@@ -69,17 +81,16 @@ __device__ __forceinline__ double sum_partials(const double* __restrict__ p, int
   // each thread adds p[tid], p[tid + kWG], ... in index order; the loads of
   // eight strides are issued together (one memory round trip per eight
   // instead of one per partial: the partials were written by every XCD and
-  // miss this XCD's L2 the first time)
+  // miss this XCD's L2 the first time).  Past the end a thread adds 0.0,
+  // which leaves its sum unchanged.
   double s = 0.0;
-  int i = threadIdx.x;
-  for (; i + 7 * kWG < np; i += 8 * kWG) {
+  for (int i = threadIdx.x; i < np; i += 8 * kWG) {
     double v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = p[i + u * kWG];
+    for (int u = 0; u < 8; ++u) v[u] = i + u * kWG < np ? p[i + u * kWG] : 0.0;
 #pragma unroll
     for (int u = 0; u < 8; ++u) s += v[u];
   }
-  for (; i < np; i += kWG) s += p[i];
   return block_sum(s, red);
 }
 

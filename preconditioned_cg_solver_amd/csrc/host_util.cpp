@@ -121,6 +121,13 @@ sla_status poll_create(PollSlot** out) {
     set_error("hipHostMalloc of a polling record failed");
     return SLA_ERR_OOM;
   }
+  if (hipHostGetDevicePointer(&p->dev, p->host, 0) != hipSuccess || !p->dev) {
+    (void)hipGetLastError();
+    (void)hipHostFree(p->host);
+    delete p;
+    set_error("hipHostGetDevicePointer of a polling record failed");
+    return SLA_ERR_HIP;
+  }
   for (auto& e : p->ev) {
     const hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableTiming);
     if (r != hipSuccess) {
@@ -239,6 +246,37 @@ int batch_iters(double iter_us) {
   if (env > 0) return env;
   const double b = std::ceil(800.0 / std::max(iter_us, 1.0));
   return (int)std::max(2.0, std::min(b, 16.0));
+}
+
+// Waits until the batch ending at iteration kend has filled its polling
+// record and copies the record to *out.  The host spins on the mapped
+// record: no event, whose barrier packet would stall the queue at every
+// batch.  If the stream drains without the record (a launch failed), the
+// device's done flag is read instead and reported as done.
+hipError_t wait_poll(const SolverState* rec, int kend, hipStream_t s, const int* dev_done,
+                     SolverState* out) {
+  const volatile SolverState* r = rec;
+  for (unsigned spins = 1; r->exit_iter != kend; ++spins) {
+    if ((spins & 4095) == 0) {
+      const hipError_t q = hipStreamQuery(s);
+      if (q == hipErrorNotReady) continue;
+      __atomic_thread_fence(__ATOMIC_ACQUIRE);
+      if (r->exit_iter == kend) break;
+      if (q != hipSuccess) return q;
+      int done = 0;
+      const hipError_t e = hipMemcpy(&done, dev_done, sizeof(int), hipMemcpyDeviceToHost);
+      out->done = 1;  // nothing left to wait for
+      out->exit_iter = kend;
+      return e;
+    }
+    __builtin_ia32_pause();
+  }
+  __atomic_thread_fence(__ATOMIC_ACQUIRE);
+  out->done = r->done;
+  out->exit_iter = r->exit_iter;
+  out->rr = r->rr;
+  out->bb = r->bb;
+  return hipSuccess;
 }
 
 // Rough duration of one iteration over A and G with k right-hand sides

@@ -10,6 +10,7 @@
 #include <vector>
 
 #include "bounds.h"
+#include "planner.h"
 #include "sla.h"
 
 namespace sla {
@@ -275,6 +276,7 @@ sla_status use_end(const sla_mat& m, hipStream_t s, bool scratch);
 constexpr size_t kPollBytes = 4096;
 struct PollSlot {
   void* host = nullptr;
+  void* dev = nullptr;  // the same pinned record as the device addresses it
   hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
   int device = -1;
 };
@@ -354,6 +356,8 @@ size_t stream_bytes(const sla_mat& m, const MatView& v);
 size_t mall_budget();
 hipEvent_t timing_event();
 int batch_iters(double iter_us);
+hipError_t wait_poll(const SolverState* rec, int kend, hipStream_t s, const int* dev_done,
+                     SolverState* out);
 double iteration_estimate_us(const sla_mat& A, const sla_mat& G, int elem_bytes, int k,
                              int launches);
 

@@ -29,7 +29,6 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
-#include <deque>
 #include <mutex>
 
 #include "device_util.h"
@@ -92,6 +91,10 @@ struct MArgs {
   int npin;
   double* pout;  // this kernel's partials, [gridDim.x][K]
   MState* st;
+  // G step of a batch's last iteration: the host-mapped polling record it
+  // fills (done, iteration, the largest ||r_c||^2 / ||b_c||^2 of the
+  // columns still iterating, 1); null otherwise
+  SolverState* poll;
   int k;
   int maxit;
   double rtol;
@@ -129,23 +132,19 @@ __device__ __forceinline__ void sum_partials_k(const double* __restrict__ p, int
 #pragma unroll
   for (int c = 0; c < K; ++c) out[c] = 0.0;
   // in index order per thread; the loads of 16 / K strides (at least one)
-  // are issued together
+  // are issued together, and past the end a thread adds 0.0
   constexpr int S = K >= 16 ? 1 : 16 / K;
-  int i = threadIdx.x;
-  for (; i + (S - 1) * kWG < np; i += S * kWG) {
+  for (int i = threadIdx.x; i < np; i += S * kWG) {
     double v[S][K];
 #pragma unroll
     for (int u = 0; u < S; ++u)
 #pragma unroll
-      for (int c = 0; c < K; ++c) v[u][c] = p[(size_t)(i + u * kWG) * K + c];
+      for (int c = 0; c < K; ++c)
+        v[u][c] = i + u * kWG < np ? p[(size_t)(i + u * kWG) * K + c] : 0.0;
 #pragma unroll
     for (int u = 0; u < S; ++u)
 #pragma unroll
       for (int c = 0; c < K; ++c) out[c] += v[u][c];
-  }
-  for (; i < np; i += kWG) {
-#pragma unroll
-    for (int c = 0; c < K; ++c) out[c] += p[(size_t)i * K + c];
   }
   block_sum_k<K>(out, red);
 }
@@ -173,9 +172,14 @@ __device__ __forceinline__ bool mprologue(const MArgs<T>& a, MCoef<T, K>& cf, do
     if (threadIdx.x == 0)
       *s_flag = __hip_atomic_load(&a.st->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    if (*s_flag) return false;
-    if constexpr (MODE == MM_AU || MODE == MM_GTU) return true;
     const bool lead = blockIdx.x == 0 && threadIdx.x == 0;
+    if (*s_flag) {
+      if constexpr (MODE == MM_G) {
+        if (a.poll && lead) post_poll(a.poll, 1, a.k, 0.0, 0.0);
+      }
+      return false;
+    }
+    if constexpr (MODE == MM_AU || MODE == MM_GTU) return true;
     const int k = a.k;
     double s[K];
     sum_partials_k<K>(a.pin, a.npin, s, red);
@@ -235,6 +239,15 @@ __device__ __forceinline__ bool mprologue(const MArgs<T>& a, MCoef<T, K>& cf, do
       }
       cf.act[c] = act;
       live += act ? 1 : 0;
+    }
+    if constexpr (MODE == MM_G) {
+      if (a.poll && lead) {
+        double worst = 0.0;
+#pragma unroll
+        for (int c = 0; c < K; ++c)
+          if (cf.act[c] && a.st->bb[c] > 0.0) worst = fmax(worst, s[c] / a.st->bb[c]);
+        post_poll(a.poll, live == 0, k, worst, 1.0);
+      }
     }
     if (live == 0) {
       if (lead) a.st->done = 1;
@@ -1020,16 +1033,26 @@ sla_status mpcg_pass(const sla_mat& A, const sla_mat& G, double eps, const T* b,
   PollLease lease;
   sla_status pst = poll_acquire(&lease.p);
   if (pst != SLA_OK) return pst;
+  // polling records in slots 0..2 (as in the one-column driver), the final
+  // state after them
+  static_assert(sizeof(SolverState) <= sizeof(MState), "record layout");
+  SolverState* rec = (SolverState*)lease.p->host;
+  SolverState* drec = (SolverState*)lease.p->dev;
   MState* mhost = (MState*)lease.p->host;
-  hipEvent_t* mev = lease.p->ev;
-  std::deque<int> pend;
+  int pend[3], pend_k[3];
+  int npend = 0, pfirst = 0;
   int next_slot = 0;
-  const int B = batch_iters(iteration_estimate_us(A, G, (int)sizeof(T), K, fused ? 3 : 5));
+  BatchPlanner plan_b(batch_iters(iteration_estimate_us(A, G, (int)sizeof(T), K, fused ? 3 : 5)),
+                      rtol);
   int k = 1;
   bool finished = false;
   while (!finished) {
-    if (k <= maxit) {
-      const int kend = std::min(maxit, k + B - 1);
+    const int want = k <= maxit ? plan_b.next(k) : 0;
+    if (k <= maxit && npend < 2 && (want > 0 || npend == 0)) {
+      const int kend = std::min(maxit, k + std::max(want, plan_b.restart()) - 1);
+      const int ps = next_slot;
+      next_slot = (next_slot + 1) % 3;
+      ((volatile SolverState*)&rec[ps])->exit_iter = -1;
       for (int kk = k; kk <= kend; ++kk) {
         if (fused) {
           aA.k = kk;
@@ -1067,27 +1090,30 @@ sla_status mpcg_pass(const sla_mat& A, const sla_mat& G, double eps, const T* b,
         }
         aG.k = kk;
         aG.rv = R[kk & 1];
+        aG.poll = kk == kend ? drec + ps : nullptr;
         SLA_HIP((mlaunch<T, MM_G, K>(G, G.fwd, aG, grid, s)));
       }
-      const int slot = next_slot;
-      next_slot = (next_slot + 1) % 3;
-      SLA_HIP(hipMemcpyAsync(&mhost[slot], w.st, 16, hipMemcpyDeviceToHost, s));
-      SLA_HIP(hipEventRecord(mev[slot], s));
-      pend.push_back(slot);
+      aG.poll = nullptr;
+      pend[(pfirst + npend) % 3] = ps;
+      pend_k[(pfirst + npend) % 3] = kend;
+      ++npend;
       k = kend + 1;
+      continue;
     }
-    if (pend.size() >= 2 || (k > maxit && !pend.empty())) {
-      const int slot = pend.front();
-      pend.pop_front();
-      SLA_HIP(hipEventSynchronize(mev[slot]));
-      if (mhost[slot].done) finished = true;
+    if (npend > 0) {
+      const int ps = pend[pfirst], kb = pend_k[pfirst];
+      pfirst = (pfirst + 1) % 3;
+      --npend;
+      SolverState r{};
+      SLA_HIP(wait_poll(&rec[ps], kb, s, &w.st->done, &r));
+      if (r.done) finished = true;
+      else plan_b.observe(r.exit_iter, r.rr, r.bb);
+      continue;
     }
-    if (k > maxit && pend.empty()) finished = true;
+    finished = true;  // k > maxit and nothing queued
   }
-  while (!pend.empty()) {
-    SLA_HIP(hipEventSynchronize(mev[pend.front()]));
-    pend.pop_front();
-  }
+  // batches still queued return at once; the stream synchronization below
+  // waits for them
   MState* hs = &mhost[3];
   SLA_HIP(hipMemcpyAsync(hs, w.st, sizeof(MState), hipMemcpyDeviceToHost, s));
   SLA_HIP(hipStreamSynchronize(s));

@@ -91,6 +91,9 @@ struct StepArgs {
   int npin;
   double* pout;       // partials written: [gridDim.x] workgroups then long rows
   SolverState* st;
+  // G step of a batch's last iteration: the host-mapped polling record it
+  // fills (done flag, iteration, ||r||^2, ||b||^2); null otherwise
+  SolverState* poll;
   int k;
   int maxit;
   double rtol;
@@ -127,7 +130,12 @@ __device__ __forceinline__ bool prologue(const StepArgs<T>& a, Coef<T>& cf, doub
     if (threadIdx.x == 0) *s_flag = __hip_atomic_load(&a.st->done, __ATOMIC_RELAXED,
                                                       __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    if (*s_flag) return false;
+    if (*s_flag) {
+      if constexpr (MODE == M_G) {
+        if (a.poll && blockIdx.x == 0 && threadIdx.x == 0) post_poll(a.poll, 1, a.k, 0.0, 0.0);
+      }
+      return false;
+    }
     if constexpr (MODE == M_AU || MODE == M_GTU) return true;
     const bool lead = blockIdx.x == 0 && threadIdx.x == 0;
     const int k = a.k;
@@ -187,6 +195,7 @@ __device__ __forceinline__ bool prologue(const StepArgs<T>& a, Coef<T>& cf, doub
       if (lead) {
         a.st->rr = rr;
         if (ex != EX_NONE) take_exit(a.st, ex, k);
+        if (a.poll) post_poll(a.poll, ex != EX_NONE, k, rr, a.st->bb);
       }
       return ex == EX_NONE;
     }
@@ -906,36 +915,31 @@ __global__ __launch_bounds__(kWG) void vec_p_update(StepArgs<T> a) {
   __shared__ int s_flag;
   Coef<T> cf;
   if (!prologue<T, MODE>(a, cf, s_red, &s_flag)) return;
-  // four grid strides per round, all loads issued before the stores
+  // four grid strides per round (predicated past n), all loads issued
+  // before the stores
   const int stride = gridDim.x * kWG;
-  int i = blockIdx.x * kWG + threadIdx.x;
-  for (; i + 3 * stride < a.n; i += 4 * stride) {
+  for (long long i = blockIdx.x * kWG + threadIdx.x; i < a.n; i += 4LL * stride) {
     T z[4], po[4], xv[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      z[u] = a.in0[i + u * stride];
+      const long long e = i + (long long)u * stride;
+      const bool in = e < a.n;
+      z[u] = in ? a.in0[e] : T(0);
       if constexpr (MODE != M_A1) {
-        po[u] = a.in1[i + u * stride];
-        xv[u] = a.xv[i + u * stride];
+        po[u] = in ? a.in1[e] : T(0);
+        xv[u] = in ? a.xv[e] : T(0);
       }
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
+      const long long e = i + (long long)u * stride;
+      if (e >= a.n) break;
       if constexpr (MODE == M_A1) {
-        st_out<2>(a.own + i + u * stride, z[u]);
+        st_out<2>(a.own + e, z[u]);
       } else {
-        st_out<2>(a.own + i + u * stride, fma(cf.c, po[u], z[u]));
-        st_out<1>(a.xv + i + u * stride, fma(cf.c2, po[u], xv[u]));
+        st_out<2>(a.own + e, fma(cf.c, po[u], z[u]));
+        st_out<1>(a.xv + e, fma(cf.c2, po[u], xv[u]));
       }
-    }
-  }
-  for (; i < a.n; i += stride) {
-    if constexpr (MODE == M_A1) {
-      st_out<2>(a.own + i, a.in0[i]);
-    } else {
-      const T po = a.in1[i];
-      st_out<2>(a.own + i, fma(cf.c, po, a.in0[i]));
-      st_out<1>(a.xv + i, fma(cf.c2, po, a.xv[i]));
     }
   }
 }
@@ -951,25 +955,22 @@ __global__ __launch_bounds__(kWG) void vec_r_update(StepArgs<T> a) {
   if (!prologue<T, M_GT>(a, cf, s_red, &s_flag)) return;
   double dot = 0.0;
   const int stride = gridDim.x * kWG;
-  int i = blockIdx.x * kWG + threadIdx.x;
-  for (; i + 3 * stride < a.n; i += 4 * stride) {
+  for (long long i = blockIdx.x * kWG + threadIdx.x; i < a.n; i += 4LL * stride) {
     T ro[4], q[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      ro[u] = a.in0[i + u * stride];
-      q[u] = a.in1[i + u * stride];
+      const long long e = i + (long long)u * stride;
+      ro[u] = e < a.n ? a.in0[e] : T(0);
+      q[u] = e < a.n ? a.in1[e] : T(0);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
+      const long long e = i + (long long)u * stride;
+      if (e >= a.n) break;
       const T rn = fma(cf.c, q[u], ro[u]);
-      a.own[i + u * stride] = rn;
+      a.own[e] = rn;
       dot += (double)rn * (double)rn;
     }
-  }
-  for (; i < a.n; i += stride) {
-    const T rn = fma(cf.c, a.in1[i], a.in0[i]);
-    a.own[i] = rn;
-    dot += (double)rn * (double)rn;
   }
   const double s = block_sum(dot, s_red);
   if (threadIdx.x == 0) a.pout[blockIdx.x] = s;
@@ -1428,7 +1429,15 @@ hipError_t launch_step(const sla_mat& m, const StepArgs<T>& a, int grid, hipStre
     // block triangles; 2, 3, 4 and 6 measured there)
     const dim3 g(grid), b(kWG);
     const bool wide = a.sell_w > 16;
-    if (a.sd) {
+    const char* ue = getenv(wide ? "SLA_BSELL_UW" : "SLA_BSELL_UN");
+    const int uo = ue ? atoi(ue) : 0;
+    if (a.sd && nt && uo == 7) {
+      hipLaunchKernelGGL((bsell_step<T, MODE, true, true, 7>), g, b, 0, s, a);
+    } else if (a.sd && nt && uo == 14) {
+      hipLaunchKernelGGL((bsell_step<T, MODE, true, true, 14>), g, b, 0, s, a);
+    } else if (a.sd && nt && uo == 9) {
+      hipLaunchKernelGGL((bsell_step<T, MODE, true, true, 9>), g, b, 0, s, a);
+    } else if (a.sd) {
       if (nt && wide) hipLaunchKernelGGL((bsell_step<T, MODE, true, true, 3>), g, b, 0, s, a);
       else if (nt) hipLaunchKernelGGL((bsell_step<T, MODE, true, true, 2>), g, b, 0, s, a);
       else if (wide) hipLaunchKernelGGL((bsell_step<T, MODE, false, true, 3>), g, b, 0, s, a);
@@ -1754,17 +1763,24 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
   SLA_HIP((launch_step<T, M_G0>(G, aG, grid, s, plan.nt_g, win)));
   rec.end(e0, 2, 0);
 
-  // exit-flag copies in flight: a ring of at most two pending batches
+  // Batches of iterations, at most two queued; the G step of a batch's last
+  // iteration fills that batch's host-mapped polling record.
   SolverState* hst = (SolverState*)slot->host;
-  int pend[3];
+  SolverState* dpoll = (SolverState*)slot->dev;
+  int pend[3], pend_k[3];
   int npend = 0, pfirst = 0;
   int next_slot = 0;
-  const int B = batch_iters(iteration_estimate_us(A, G, (int)sizeof(T), 1, fused ? 3 : 5));
+  BatchPlanner plan_b(batch_iters(iteration_estimate_us(A, G, (int)sizeof(T), 1, fused ? 3 : 5)),
+                      rtol);
   int k = 1;
   bool finished = false;
   while (!finished) {
-    if (k <= maxit) {
-      const int kend = std::min(maxit, k + B - 1);
+    const int want = k <= maxit ? plan_b.next(k) : 0;
+    if (k <= maxit && npend < 2 && (want > 0 || npend == 0)) {
+      const int kend = std::min(maxit, k + std::max(want, plan_b.restart()) - 1);
+      const int ps = next_slot;
+      next_slot = (next_slot + 1) % 3;
+      ((volatile SolverState*)&hst[ps])->exit_iter = -1;
       for (int kk = k; kk <= kend; ++kk) {
         if (fused) {
           aA.k = kk;
@@ -1809,32 +1825,32 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
         }
         aG.k = kk;
         aG.rv = R[kk & 1];
+        aG.poll = kk == kend ? dpoll + ps : nullptr;
         hipEvent_t eg = rec.begin(2, kk);
         SLA_HIP((launch_step<T, M_G>(G, aG, grid, s, plan.nt_g, win)));
         rec.end(eg, 2, kk);
       }
-      const int ps = next_slot;
-      next_slot = (next_slot + 1) % 3;
-      SLA_HIP(hipMemcpyAsync(&hst[ps], w.st, 16, hipMemcpyDeviceToHost, s));
-      SLA_HIP(hipEventRecord(slot->ev[ps], s));
+      aG.poll = nullptr;
       pend[(pfirst + npend) % 3] = ps;
+      pend_k[(pfirst + npend) % 3] = kend;
       ++npend;
       k = kend + 1;
+      continue;
     }
-    if (npend >= 2 || (k > maxit && npend > 0)) {
-      const int ps = pend[pfirst];
+    if (npend > 0) {
+      const int ps = pend[pfirst], kb = pend_k[pfirst];
       pfirst = (pfirst + 1) % 3;
       --npend;
-      SLA_HIP(hipEventSynchronize(slot->ev[ps]));
-      if (hst[ps].done) finished = true;
+      SolverState r{};
+      SLA_HIP(wait_poll(&hst[ps], kb, s, &w.st->done, &r));
+      if (r.done) finished = true;
+      else plan_b.observe(r.exit_iter, r.rr, r.bb);
+      continue;
     }
-    if (k > maxit && npend == 0) finished = true;
+    finished = true;  // k > maxit and nothing queued
   }
-  while (npend > 0) {
-    SLA_HIP(hipEventSynchronize(slot->ev[pend[pfirst]]));
-    pfirst = (pfirst + 1) % 3;
-    --npend;
-  }
+  // batches still queued return at once; the stream synchronization below
+  // waits for them
   hipLaunchKernelGGL(finalize_x<T>, dim3(std::max(1, std::min((n + kWG - 1) / kWG, 4096))),
                      dim3(kWG), 0, s, (const SolverState*)w.st, x, (const T*)P[0],
                      (const T*)P[1], n);
@@ -1952,18 +1968,21 @@ sla_status spmv(const sla_mat& A, bool transpose, const void* x, void* y, hipStr
   }
   const LongScratch ls = scratch ? *scratch : long_scratch_of(A, transpose);
   const bool nt = matrix_bytes(A) > mall_budget();
+  // the plain product reads no partials: BSR takes one work item per
+  // workgroup, as in the separate iteration form
+  auto grid_of = [&](int ntiles) { return A.bs > 1 ? wide_grid(ntiles) : step_grid(ntiles); };
   if (A.dtype == SLA_F64) {
     StepArgs<double> a{};
     fill_matrix(a, A, v, ls.part, ls.cnt);
     a.in0 = (const double*)x;
     a.y = (double*)y;
-    SLA_HIP((launch_step<double, M_PLAIN>(A, a, step_grid(a.ntiles), s, nt)));
+    SLA_HIP((launch_step<double, M_PLAIN>(A, a, grid_of(a.ntiles), s, nt)));
   } else {
     StepArgs<float> a{};
     fill_matrix(a, A, v, ls.part, ls.cnt);
     a.in0 = (const float*)x;
     a.y = (float*)y;
-    SLA_HIP((launch_step<float, M_PLAIN>(A, a, step_grid(a.ntiles), s, nt)));
+    SLA_HIP((launch_step<float, M_PLAIN>(A, a, grid_of(a.ntiles), s, nt)));
   }
   if (prof) {
     SLA_HIP(hipEventRecord(eb, s));
