@@ -1257,44 +1257,76 @@ __global__ __launch_bounds__(kWG) void csr_grad(const int32_t* __restrict__ rp,
 // entries of one block row r of one block (-lambda_{3I+r} times the block
 // column's three x entries: one column load, three contiguous gathers) into
 // LDS, then the workgroup streams the tile's range out with 16-byte
-// non-temporal stores, the odd entries at either end alone.  The output is
-// written once and never read here, and a gradient larger than the Infinity
-// Cache would otherwise cycle through it.  (Elasticity 64^3 x 3, 494 MB
-// written: 112 us; with one scalar entry per thread and round, computing its
-// block from the entry index, 158-176 us.)
+// non-temporal stores from the 128-byte line boundary below the range (each
+// wavefront's store covers whole lines), the odd entries at either end
+// alone.  The output is written once and never read here, and a gradient
+// larger than the Infinity Cache would otherwise cycle through it.
+// (Elasticity 64^3 x 3, 494 MB written, on the per-tile grid: 108 us; with
+// the stores starting at the tile's first entry 116 us, with plain stores
+// 188 us, with one scalar entry per thread and round, computing its block
+// from the entry index, 162 us; a fill of the same size takes 80 us.)
 constexpr int kGradMaxBlocks = 27;  // blocks per block row the LDS tile holds
-template <typename T>
+template <typename T, int TR>
 __global__ __launch_bounds__(kWG) void bsr3_grad(const int32_t* __restrict__ rp,
                                                  const int32_t* __restrict__ ci, int nbr,
                                                  int ntiles, const T* __restrict__ lam,
                                                  const T* __restrict__ x, T* __restrict__ g) {
   using V2 = T __attribute__((ext_vector_type(2)));
-  constexpr int kMax = 9 * kGradMaxBlocks * kBsrTileRows + 2;
+  constexpr int kMax = 9 * kGradMaxBlocks * TR + 128 / (int)sizeof(T);
+  // (block, row) items per thread: all of a tile's loads are issued together
+  constexpr int QU = (3 * kGradMaxBlocks * TR + kWG - 1) / kWG;
   __shared__ T s_g[kMax];
   int t0, t1, step;
   tile_range(ntiles, t0, t1, step);
+  int rr[TR + 1];
+  auto load_rows = [&](int t, int (&d)[TR + 1]) {
+#pragma unroll
+    for (int j = 0; j <= TR; ++j) d[j] = rp[min(t * TR + j, nbr)];
+  };
+  if (t0 < t1) load_rows(t0, rr);
   for (int t = t0; t < t1; t += step) {
-    const int I0 = t * kBsrTileRows;
-    int rr[kBsrTileRows + 1];
-#pragma unroll
-    for (int j = 0; j <= kBsrTileRows; ++j) rr[j] = rp[min(I0 + j, nbr)];
-    const int b0 = rr[0], b1 = rr[kBsrTileRows];
-    // (Entry indices fit int: the handle limits 9 nnzb below 2^31.)
-    const int e0 = 9 * b0, e1 = 9 * b1, ea = e0 & ~1;
+    const int I0 = t * TR;
+    const int b0 = rr[0], b1 = rr[TR];
+    // (Entry indices fit int: the handle limits 9 nnzb below 2^31.)  The
+    // stores start at the 128-byte line below the tile's first entry, so
+    // that each wavefront's 16-byte-per-lane store covers whole lines.
+    const int e0 = 9 * b0, e1 = 9 * b1, ea = e0 & ~(128 / (int)sizeof(T) - 1);
     // the host sends tiles with more blocks than the LDS holds to the
-    // streaming path below
-    for (int q = threadIdx.x; q < 3 * (b1 - b0); q += kWG) {
-      const int kb = b0 + q / 3, r = q - 3 * (q / 3);
-      int li = 0;
+    // streaming kernel below
+    const int nq = 3 * (b1 - b0);
+    int kbv[QU], rv[QU], jv[QU];
+    T lv[QU];
 #pragma unroll
-      for (int j = 1; j < kBsrTileRows; ++j) li += kb >= rr[j] ? 1 : 0;
-      const T l = lam[3 * (I0 + li) + r];
-      const int J = ci[kb];
-      const T x0 = x[3 * J], x1 = x[3 * J + 1], x2 = x[3 * J + 2];
-      T* d = s_g + (9 * kb + 3 * r - ea);
-      d[0] = -(l * x0);
-      d[1] = -(l * x1);
-      d[2] = -(l * x2);
+    for (int u = 0; u < QU; ++u) {
+      const int q = (int)threadIdx.x + u * kWG;
+      kbv[u] = b0 + q / 3;
+      rv[u] = q - 3 * (q / 3);
+      if (q < nq) {
+        int li = 0;
+#pragma unroll
+        for (int j = 1; j < TR; ++j) li += kbv[u] >= rr[j] ? 1 : 0;
+        lv[u] = lam[3 * (I0 + li) + rv[u]];
+        jv[u] = ci[kbv[u]];
+      }
+    }
+    // the next tile's row pointers stay in flight through this tile
+    int rn[TR + 1];
+    if (t + step < t1) load_rows(t + step, rn);
+    T xv[QU][3];
+#pragma unroll
+    for (int u = 0; u < QU; ++u) {
+      if ((int)threadIdx.x + u * kWG < nq) {
+#pragma unroll
+        for (int c = 0; c < 3; ++c) xv[u][c] = x[3 * jv[u] + c];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < QU; ++u) {
+      if ((int)threadIdx.x + u * kWG < nq) {
+        T* d = s_g + (9 * kbv[u] + 3 * rv[u] - ea);
+#pragma unroll
+        for (int c = 0; c < 3; ++c) d[c] = -(lv[u] * xv[u][c]);
+      }
     }
     __syncthreads();
     for (int e = ea + 2 * (int)threadIdx.x; e < e1; e += 2 * kWG) {
@@ -1304,11 +1336,15 @@ __global__ __launch_bounds__(kWG) void bsr3_grad(const int32_t* __restrict__ rp,
         v.y = s_g[e - ea + 1];
         __builtin_nontemporal_store(v, (V2*)(g + e));
       } else {
-        if (e >= e0) __builtin_nontemporal_store(s_g[e - ea], g + e);
-        if (e + 1 < e1) __builtin_nontemporal_store(s_g[e - ea + 1], g + e + 1);
+        if (e >= e0 && e < e1) __builtin_nontemporal_store(s_g[e - ea], g + e);
+        if (e + 1 >= e0 && e + 1 < e1) __builtin_nontemporal_store(s_g[e - ea + 1], g + e + 1);
       }
     }
     __syncthreads();
+    if (t + step < t1) {
+#pragma unroll
+      for (int j = 0; j <= TR; ++j) rr[j] = rn[j];
+    }
   }
 }
 
@@ -1429,15 +1465,7 @@ hipError_t launch_step(const sla_mat& m, const StepArgs<T>& a, int grid, hipStre
     // block triangles; 2, 3, 4 and 6 measured there)
     const dim3 g(grid), b(kWG);
     const bool wide = a.sell_w > 16;
-    const char* ue = getenv(wide ? "SLA_BSELL_UW" : "SLA_BSELL_UN");
-    const int uo = ue ? atoi(ue) : 0;
-    if (a.sd && nt && uo == 7) {
-      hipLaunchKernelGGL((bsell_step<T, MODE, true, true, 7>), g, b, 0, s, a);
-    } else if (a.sd && nt && uo == 14) {
-      hipLaunchKernelGGL((bsell_step<T, MODE, true, true, 14>), g, b, 0, s, a);
-    } else if (a.sd && nt && uo == 9) {
-      hipLaunchKernelGGL((bsell_step<T, MODE, true, true, 9>), g, b, 0, s, a);
-    } else if (a.sd) {
+    if (a.sd) {
       if (nt && wide) hipLaunchKernelGGL((bsell_step<T, MODE, true, true, 3>), g, b, 0, s, a);
       else if (nt) hipLaunchKernelGGL((bsell_step<T, MODE, true, true, 2>), g, b, 0, s, a);
       else if (wide) hipLaunchKernelGGL((bsell_step<T, MODE, false, true, 3>), g, b, 0, s, a);
@@ -2143,8 +2171,10 @@ sla_status small_solve_batch(const sla_mat& A, const sla_mat& G, double eps, con
 sla_status pattern_grad(const sla_mat& A, const void* lam, const void* x, void* grad,
                         hipStream_t s) {
   if (A.nnzb == 0) return SLA_OK;
+  // an elementwise product over the stored entries: no partials, so one
+  // work item per workgroup where the tiles allow it
   if (A.bs == 1) {
-    const int grid = step_grid(A.fwd.ntiles);
+    const int grid = wide_grid(A.fwd.ntiles);
     if (A.dtype == SLA_F64)
       hipLaunchKernelGGL(csr_grad<double>, dim3(grid), dim3(kWG), 0, s, A.fwd.rp, A.fwd.ci,
                          A.fwd.tiles, A.fwd.ntiles, (const double*)lam, (const double*)x,
@@ -2154,19 +2184,20 @@ sla_status pattern_grad(const sla_mat& A, const void* lam, const void* x, void* 
                          A.fwd.tiles, A.fwd.ntiles, (const float*)lam, (const float*)x,
                          (float*)grad);
   } else {
-    const int nt = (int)((A.nbr + kBsrTileRows - 1) / kBsrTileRows);
-    const int grid = step_grid(nt);
     // the LDS-staged kernel holds tiles whose block rows have at most
     // kGradMaxBlocks blocks
     const bool staged = A.fwd.max_row >= 0 && A.fwd.max_row <= kGradMaxBlocks;
-    if (A.dtype == SLA_F64)
-      hipLaunchKernelGGL(staged ? bsr3_grad<double> : bsr3_grad_wide<double>, dim3(grid),
-                         dim3(kWG), 0, s, A.fwd.rp, A.fwd.ci, (int)A.nbr, nt,
+    const int nt = (int)((A.nbr + kBsrTileRows - 1) / kBsrTileRows);
+    const int grid = wide_grid(nt);
+    if (A.dtype == SLA_F64) {
+      auto kern = staged ? bsr3_grad<double, kBsrTileRows> : bsr3_grad_wide<double>;
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(kWG), 0, s, A.fwd.rp, A.fwd.ci, (int)A.nbr, nt,
                          (const double*)lam, (const double*)x, (double*)grad);
-    else
-      hipLaunchKernelGGL(staged ? bsr3_grad<float> : bsr3_grad_wide<float>, dim3(grid),
-                         dim3(kWG), 0, s, A.fwd.rp, A.fwd.ci, (int)A.nbr, nt,
+    } else {
+      auto kern = staged ? bsr3_grad<float, kBsrTileRows> : bsr3_grad_wide<float>;
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(kWG), 0, s, A.fwd.rp, A.fwd.ci, (int)A.nbr, nt,
                          (const float*)lam, (const float*)x, (float*)grad);
+    }
   }
   SLA_HIP(hipGetLastError());
   return SLA_OK;
