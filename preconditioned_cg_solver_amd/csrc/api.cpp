@@ -49,6 +49,7 @@ void free_owned(sla_mat* m) {
     buf_free(p);
     p = nullptr;
   }
+  free_colblocks(m);
 }
 
 // Waits for the asynchronous calls queued on a handle (its use events) and
@@ -170,6 +171,7 @@ sla_status create_common(sla_mat_t* out, int64_t nbr, int64_t nnzb, int32_t bs, 
   if (st == SLA_OK && bs == 3) st = max_row_length(rp, nbr, &m->fwd.max_row, s);
   if (st == SLA_OK) st = alloc_long_scratch(m, m->fwd, O_LPART_F, O_LCNT_F, s);
   if (st == SLA_OK && ordering) st = decide_order(m, s);
+  m->cb_want = ordering && colblocks_wanted(*m);
   if (st == SLA_OK && (flags & SLA_BUILD_TRANSPOSE)) {
     int32_t *trp = nullptr, *tci = nullptr;
     void* tv = nullptr;
@@ -224,7 +226,8 @@ sla_status make_permuted(const sla_mat& src, const int32_t* perm, const int32_t*
   (*out)->owned[O_ORD_RP] = rp;
   (*out)->owned[O_ORD_RP + 1] = ci;
   (*out)->owned[O_ORD_RP + 2] = v;
-  return SLA_OK;
+  // the solves' products on the ordering run on column blocks
+  return src.cb_want ? build_colblocks(*out, s) : SLA_OK;
 }
 
 std::mutex g_order_mu;

@@ -167,6 +167,25 @@ struct MatView {
   const uint8_t* sm = nullptr;
 };
 
+// Column-block copy of a CSR operator (random-graph matrices on their
+// locality ordering): its entries split by column into kColBlocks blocks of
+// equal column ranges, each a CSR matrix over all rows with the LDS-tile
+// layout.  A product runs block b on the workgroups b, b + kColBlocks, ...
+// (round-robin dispatch puts them on XCD b), so block b gathers only from
+// its eighth of the vector, which that XCD's L2 can hold; the eight
+// per-block results of a row are then added in block order.
+constexpr int kColBlocks = 8;
+struct ColBlockSet {
+  MatView blk[kColBlocks];
+  int lrow_off[kColBlocks];   // block's long rows in the shared ticket array
+  int lpart_off[kColBlocks];  // block's chunk partials in the shared array
+};
+struct ColBlocks {
+  ColBlockSet fwd, tr;
+  bool has_tr = false;
+  std::vector<void*> owned;
+};
+
 }  // namespace sla
 
 struct sla_mat {
@@ -178,6 +197,10 @@ struct sla_mat {
   sla::MatView fwd;
   bool has_t = false;
   sla::MatView tr;
+  // column-block copies (built with the locality ordering's copies when
+  // cb_want, decided at creation)
+  sla::ColBlocks* cb = nullptr;
+  bool cb_want = false;
   // owned device memory: tiles, long-row scratch, the transpose arrays and,
   // for the copies below, the permuted arrays and the permutation
   void* owned[24] = {};
@@ -230,6 +253,11 @@ int occupancy_grid(int cus);
 // Setup (setup.hip).
 sla_status build_tiling(const int32_t* d_rp, int64_t n, MatView& view, void** owned_tiles,
                         hipStream_t s);
+// Column-block copies of m's forward view (and of its transpose when m has
+// one); SLA_COLBLK=0 leaves m->cb null.
+sla_status build_colblocks(sla_mat* m, hipStream_t s);
+void free_colblocks(sla_mat* m);
+bool colblocks_wanted(const sla_mat& A);
 sla_status build_transpose(const sla_mat& m, int32_t** t_rp, int32_t** t_ci, void** t_v,
                            hipStream_t s);
 sla_status validate_structure(const sla_mat& m, hipStream_t s);

@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <new>
 #include <cstdio>
 #include <climits>
 #include <cstdlib>
@@ -748,6 +749,178 @@ sla_status radix_sort_indices(const int* keys, int m, int bits, int* work, const
   }
   *idx_out = vin;
   return SLA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Column-block copies.  Entries are sorted stably by their column block
+// (col / seg), which lays the eight blocks out one after another, each in
+// row order with the rows' own entry order; each block's row pointer is then
+// found by binary search over the sorted entries' rows.
+// ---------------------------------------------------------------------------
+
+namespace {
+
+__global__ void cb_keys(const int* __restrict__ ci, int nnz, int seg, int* __restrict__ keys) {
+  for (int k = blockIdx.x * blockDim.x + threadIdx.x; k < nnz; k += gridDim.x * blockDim.x)
+    keys[k] = ci[k] / seg;
+}
+
+// per-block entry counts (integer atomics on a workgroup's LDS histogram)
+__global__ __launch_bounds__(kWG) void cb_count(const int* __restrict__ keys, int nnz,
+                                                int* __restrict__ cnt) {
+  __shared__ int h[kColBlocks];
+  if (threadIdx.x < kColBlocks) h[threadIdx.x] = 0;
+  __syncthreads();
+  for (int k = blockIdx.x * blockDim.x + threadIdx.x; k < nnz; k += gridDim.x * blockDim.x)
+    atomicAdd(&h[keys[k]], 1);
+  __syncthreads();
+  if (threadIdx.x < kColBlocks && h[threadIdx.x]) atomicAdd(&cnt[threadIdx.x], h[threadIdx.x]);
+}
+
+// sorted entry k: its column, value and row
+template <typename T>
+__global__ void cb_gather(const int* __restrict__ rp, int n, const int* __restrict__ ci,
+                          const T* __restrict__ v, const int* __restrict__ idx, int nnz,
+                          int* __restrict__ oci, T* __restrict__ ov, int* __restrict__ orow) {
+  for (int k = blockIdx.x * blockDim.x + threadIdx.x; k < nnz; k += gridDim.x * blockDim.x) {
+    const int src = idx[k];
+    oci[k] = ci[src];
+    ov[k] = v[src];
+    orow[k] = row_of(rp, n, src);
+  }
+}
+
+// row pointer of block b, relative to the block's first entry: the first
+// sorted entry of the block whose row is >= r
+__global__ void cb_rowptr(const int* __restrict__ orow, const int* __restrict__ bstart, int n,
+                          int* __restrict__ rpb) {
+  const int64_t m = (int64_t)kColBlocks * (n + 1);
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < m;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int b = (int)(e / (n + 1)), r = (int)(e - (int64_t)b * (n + 1));
+    int lo = bstart[b], hi = bstart[b + 1];
+    const int first = lo;
+    while (lo < hi) {
+      const int mid = lo + ((hi - lo) >> 1);
+      if (orow[mid] < r) lo = mid + 1;
+      else hi = mid;
+    }
+    rpb[e] = lo - first;
+  }
+}
+
+}  // namespace
+
+// One view split into kColBlocks column blocks (arrays owned by `cb`).
+sla_status split_view(const sla_mat& m, const MatView& v, ColBlocks* cb, ColBlockSet* out,
+                      hipStream_t s) {
+  const int n = (int)m.nbr, nnz = (int)m.nnzb;
+  const size_t es = m.dtype == SLA_F64 ? 8 : 4;
+  const int seg = std::max(1, (n + kColBlocks - 1) / kColBlocks);
+  int *oci = nullptr, *rpb = nullptr;
+  void* ov = nullptr;
+  SLA_HIP(buf_alloc((void**)&oci, sizeof(int) * (size_t)std::max(1, nnz)));
+  cb->owned.push_back(oci);
+  SLA_HIP(buf_alloc(&ov, es * (size_t)std::max(1, nnz)));
+  cb->owned.push_back(ov);
+  SLA_HIP(buf_alloc((void**)&rpb, sizeof(int) * (size_t)kColBlocks * ((size_t)n + 1)));
+  cb->owned.push_back(rpb);
+  int* tmp = nullptr;  // keys, block counts and starts, rows, radix work
+  const size_t ntmp = 2 * (size_t)std::max(1, nnz) + 2 * kColBlocks + 2 + radix_work_ints(nnz);
+  SLA_HIP(hipMallocAsync((void**)&tmp, sizeof(int) * ntmp, s));
+  int* keys = tmp;
+  int* orow = keys + std::max(1, nnz);
+  int* cnt = orow + std::max(1, nnz);
+  int* bstart = cnt + kColBlocks;
+  int* work = bstart + kColBlocks + 2;
+  SLA_HIP(hipMemsetAsync(cnt, 0, sizeof(int) * kColBlocks, s));
+  int hb[kColBlocks + 1] = {0};
+  if (nnz > 0) {
+    hipLaunchKernelGGL(cb_keys, dim3(grid_for(nnz)), dim3(kWG), 0, s, v.ci, nnz, seg, keys);
+    hipLaunchKernelGGL(cb_count, dim3(std::min(grid_for(nnz), 2048)), dim3(kWG), 0, s,
+                       (const int*)keys, nnz, cnt);
+    SLA_HIP(hipGetLastError());
+    const int* idx = nullptr;
+    sla_status st = radix_sort_indices(keys, nnz, 3, work, &idx, s);
+    if (st != SLA_OK) return st;
+    if (m.dtype == SLA_F64)
+      hipLaunchKernelGGL(cb_gather<double>, dim3(grid_for(nnz)), dim3(kWG), 0, s, v.rp, n, v.ci,
+                         (const double*)v.v, idx, nnz, oci, (double*)ov, orow);
+    else
+      hipLaunchKernelGGL(cb_gather<float>, dim3(grid_for(nnz)), dim3(kWG), 0, s, v.rp, n, v.ci,
+                         (const float*)v.v, idx, nnz, oci, (float*)ov, orow);
+    SLA_HIP(hipGetLastError());
+    int hc[kColBlocks];
+    SLA_HIP(hipMemcpyAsync(hc, cnt, sizeof(hc), hipMemcpyDeviceToHost, s));
+    SLA_HIP(hipStreamSynchronize(s));
+    for (int b = 0; b < kColBlocks; ++b) hb[b + 1] = hb[b] + hc[b];
+    if (hb[kColBlocks] != nnz) {
+      (void)hipFreeAsync(tmp, s);
+      set_error("column-block split lost entries");
+      return SLA_ERR_HIP;
+    }
+  }
+  SLA_HIP(hipMemcpyAsync(bstart, hb, sizeof(hb), hipMemcpyHostToDevice, s));
+  hipLaunchKernelGGL(cb_rowptr, dim3(grid_for((int64_t)kColBlocks * (n + 1))), dim3(kWG), 0, s,
+                     (const int*)orow, (const int*)bstart, n, rpb);
+  SLA_HIP(hipGetLastError());
+  SLA_HIP(hipStreamSynchronize(s));
+  SLA_HIP(hipFreeAsync(tmp, s));
+  int lrows = 0, lparts = 0;
+  for (int b = 0; b < kColBlocks; ++b) {
+    MatView& bv = out->blk[b];
+    bv = MatView{};
+    bv.rp = rpb + (size_t)b * ((size_t)n + 1);
+    bv.ci = oci + hb[b];
+    bv.v = (const char*)ov + es * (size_t)hb[b];
+    void* tiles = nullptr;
+    sla_status st = build_tiling(bv.rp, n, bv, &tiles, s);
+    if (tiles) cb->owned.push_back(tiles);
+    if (st != SLA_OK) return st;
+    out->lrow_off[b] = lrows;
+    out->lpart_off[b] = lparts;
+    lrows += bv.nlong_rows;
+    lparts += bv.n_long_part;
+  }
+  // the blocks' long rows share the workspace's long-row scratch, sized
+  // for the operator's (see long_rows_bound / long_part_bound)
+  if (lrows > long_rows_bound(m) || lparts > long_part_bound(m)) {
+    set_error("column-block long rows exceed the long-row scratch");
+    return SLA_ERR_HIP;
+  }
+  return SLA_OK;
+}
+
+void free_colblocks(sla_mat* m) {
+  if (!m->cb) return;
+  for (void* p : m->cb->owned) buf_free(p);
+  delete m->cb;
+  m->cb = nullptr;
+}
+
+bool colblocks_wanted(const sla_mat& A) {
+  const char* e = getenv("SLA_COLBLK");
+  return A.bs == 1 && !(e && e[0] == '0');
+}
+
+sla_status build_colblocks(sla_mat* m, hipStream_t s) {
+  if (m->cb || m->bs != 1 || m->n() == 0) return SLA_OK;
+  ColBlocks* cb = new (std::nothrow) ColBlocks();
+  if (!cb) {
+    set_error("host allocation failed");
+    return SLA_ERR_OOM;
+  }
+  m->cb = cb;
+  sla_status st = split_view(*m, m->fwd, cb, &cb->fwd, s);
+  if (st == SLA_OK && m->has_t) {
+    st = split_view(*m, m->tr, cb, &cb->tr, s);
+    cb->has_tr = st == SLA_OK;
+  }
+  if (st != SLA_OK) {
+    (void)hipStreamSynchronize(s);
+    free_colblocks(m);
+  }
+  return st;
 }
 
 sla_status build_transpose(const sla_mat& m, int32_t** t_rp_out, int32_t** t_ci_out, void** t_v_out,

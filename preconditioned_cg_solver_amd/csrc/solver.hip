@@ -376,20 +376,24 @@ static_assert(kTileRows == kWG, "one row pointer per thread when staging a tile"
 // (the grid is sized for that, see occupancy_grid): the plain, preconditioner
 // tail and separate G^T forms would otherwise take 130+ VGPRs, fall to three
 // waves per SIMD and run a quarter of their workgroups as a second round.
+// LDS of the tile engine.
+template <typename T>
+struct CsrLds {
+  T val[kLdsCap];
+  int col[kLdsCap];
+  int rp[kTileRows + 1];
+};
+
+// The tile engine's work for one workgroup: tiles t0, t0 + step, ... < t1
+// of the view in `a`; returns the workgroup's share of the step's dot
+// product.  `nwg` is the number of workgroups the partials array starts
+// with (long rows' dot products follow them).
 template <typename T, int MODE, bool NT>
-__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4)))
-void csr_step(StepArgs<T> a) {
-  __shared__ T s_val[kLdsCap];
-  __shared__ int s_col[kLdsCap];
-  __shared__ int s_rp[kTileRows + 1];
-  __shared__ double s_red[kWaves];
-  __shared__ int s_flag;
-  Coef<T> cf;
-  if (!prologue<T, MODE>(a, cf, s_red, &s_flag)) return;
+__device__ __forceinline__ double csr_tiles(const StepArgs<T>& a, const Coef<T>& cf, int t0,
+                                            int t1, int step, int nwg, CsrLds<T>& L,
+                                            double* s_red, int* s_flag) {
   const int tid = threadIdx.x;
   double dot = 0.0;
-  int t0, t1, step;
-  tile_range(a.ntiles, t0, t1, step);
   TileRegs<T> R;
   Tile nxt;
   if (t0 < t1) {
@@ -399,18 +403,18 @@ void csr_step(StepArgs<T> a) {
   for (int t = t0; t < t1; t += step) {
     const Tile d = nxt;
     if (d.kind == kTileLds) {
-      tile_commit(d, R, s_val, s_col, s_rp);
+      tile_commit(d, R, L.val, L.col, L.rp);
       if (t + step < t1) {
         nxt = a.tiles[t + step];
         if (nxt.kind == kTileLds) tile_load<NT>(a, nxt, R);
       }
       __syncthreads();
       const int r0 = d.a, nr = d.b - d.a, lg = d.c, kb = d.d;
-      const int L = 1 << lg, g = tid >> lg, sub = tid & (L - 1);
+      const int W = 1 << lg, g = tid >> lg, sub = tid & (W - 1);
       T acc = T(0);
-      if (g < nr) acc = row_sum_lds<T, MODE>(a, s_val, s_col, s_rp[g] - kb + sub, s_rp[g + 1] - kb,
-                                             L, cf);
-      for (int off = L >> 1; off >= 1; off >>= 1) acc += shfl_xor_t(acc, off);
+      if (g < nr) acc = row_sum_lds<T, MODE>(a, L.val, L.col, L.rp[g] - kb + sub, L.rp[g + 1] - kb,
+                                             W, cf);
+      for (int off = W >> 1; off >= 1; off >>= 1) acc += shfl_xor_t(acc, off);
       if (g < nr && sub == 0) dot += epi<T, MODE>(a, r0 + g, acc, cf);
       __syncthreads();
     } else {
@@ -441,10 +445,10 @@ void csr_step(StepArgs<T> a) {
           __hip_atomic_store(&a.long_part[d.d], cs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           __threadfence();
           const int ticket = atomicAdd(&a.long_cnt[lr], 1);
-          s_flag = (ticket == nch - 1);
+          *s_flag = (ticket == nch - 1);
         }
         __syncthreads();
-        finish = s_flag;
+        finish = *s_flag;
         __syncthreads();
         if (finish && tid == 0) {
           __threadfence();
@@ -459,7 +463,7 @@ void csr_step(StepArgs<T> a) {
       }
       if (finish && tid == 0) {
         const double c = epi<T, MODE>(a, d.a, T(total), cf);
-        if (a.pout) a.pout[gridDim.x + lr] = c;
+        if (a.pout) a.pout[nwg + lr] = c;
       }
       if (t + step < t1) {
         nxt = a.tiles[t + step];
@@ -467,9 +471,82 @@ void csr_step(StepArgs<T> a) {
       }
     }
   }
+  return dot;
+}
+
+template <typename T, int MODE, bool NT>
+__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4)))
+void csr_step(StepArgs<T> a) {
+  __shared__ CsrLds<T> L;
+  __shared__ double s_red[kWaves];
+  __shared__ int s_flag;
+  Coef<T> cf;
+  if (!prologue<T, MODE>(a, cf, s_red, &s_flag)) return;
+  int t0, t1, step;
+  tile_range(a.ntiles, t0, t1, step);
+  const double dot = csr_tiles<T, MODE, NT>(a, cf, t0, t1, step, gridDim.x, L, s_red, &s_flag);
   if constexpr (MODE != M_PLAIN && MODE != M_GZ && MODE != M_GTU) {
     const double s = block_sum(dot, s_red);
-    if (tid == 0) a.pout[blockIdx.x] = s;
+    if (threadIdx.x == 0) a.pout[blockIdx.x] = s;
+  }
+}
+
+// Column-block product (y_b = A_b x for every block b of a ColBlockSet):
+// workgroup w takes block w % kColBlocks (round-robin dispatch places the
+// workgroups of one block on one XCD) and that block's tiles w /
+// kColBlocks, w / kColBlocks + gridDim.x / kColBlocks, ...; the result of
+// block b goes to part + b n.  The gathered vector is the plain in0 (the
+// separate iteration form's stored p, r or t).  With `st` set the launch
+// returns at once after the solve's exit.
+template <typename T>
+struct BlockArgs {
+  StepArgs<T> blk[kColBlocks];
+  const SolverState* st;
+};
+static_assert(sizeof(BlockArgs<double>) <= 4096, "kernel arguments must fit 4 KiB");
+
+template <typename T, bool NT>
+__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(4)))
+void csr_blk_step(BlockArgs<T> ba) {
+  __shared__ CsrLds<T> L;
+  __shared__ double s_red[kWaves];
+  __shared__ int s_flag;
+  if (ba.st) {
+    if (threadIdx.x == 0)
+      s_flag = __hip_atomic_load(&ba.st->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (s_flag) return;
+  }
+  const int b = blockIdx.x % kColBlocks, nwg = gridDim.x / kColBlocks;
+  const StepArgs<T>& a = ba.blk[b];
+  const Coef<T> cf{T(0), T(0)};
+  (void)csr_tiles<T, M_PLAIN, NT>(a, cf, blockIdx.x / kColBlocks, a.ntiles, nwg, nwg, L, s_red,
+                                  &s_flag);
+}
+
+// The eight block results of every row (block b's at part + b stride)
+// added in block order, then the
+// step's own row epilogue (q and p.q; t; z = G t + eps r and r.z; or y).
+template <typename T, int MODE>
+__global__ __launch_bounds__(kWG) void blk_reduce(StepArgs<T> a, const T* __restrict__ part,
+                                                  size_t stride) {
+  __shared__ double s_red[kWaves];
+  __shared__ int s_flag;
+  Coef<T> cf;
+  if (!prologue<T, MODE>(a, cf, s_red, &s_flag)) return;
+  double dot = 0.0;
+  for (int i = blockIdx.x * kWG + threadIdx.x; i < a.n; i += gridDim.x * kWG) {
+    T v[kColBlocks];
+#pragma unroll
+    for (int b = 0; b < kColBlocks; ++b) v[b] = part[b * stride + i];
+    T acc = v[0];
+#pragma unroll
+    for (int b = 1; b < kColBlocks; ++b) acc += v[b];
+    dot += epi<T, MODE>(a, i, acc, cf);
+  }
+  if constexpr (MODE != M_PLAIN && MODE != M_GZ && MODE != M_GTU) {
+    const double s = block_sum(dot, s_red);
+    if (threadIdx.x == 0) a.pout[blockIdx.x] = s;
   }
 }
 
@@ -1598,6 +1675,7 @@ struct Work {
   double* prr;
   double* prho;
   void* vec[7];  // P0 P1 R0 R1 q t z
+  void* cbpart;  // column-block results of one product (kColBlocks n-vectors), or null
 };
 
 size_t partial_slots(const sla_mat& A) {
@@ -1610,8 +1688,17 @@ size_t zeroed_bytes(const sla_mat& A) {
   return align_up(sizeof(SolverState)) + align_up((size_t)long_rows_bound(A) * sizeof(int));
 }
 
+// Column-block results of one product: kColBlocks n-vectors, reserved for a
+// handle whose solves run on column blocks (decided at creation, so the
+// original handle and its ordered copy agree on the layout).
+size_t colblock_bytes(const sla_mat& A) {
+  if (A.bs != 1 || !((A.ord_want && A.cb_want) || A.cb)) return 0;
+  const size_t es = A.dtype == SLA_F64 ? 8 : 4;
+  return (size_t)kColBlocks * align_up((size_t)A.n() * es);
+}
+
 // Workspace layout: state, long-row tickets, long-row partials, the three
-// reduction partial arrays, seven n-vectors.
+// reduction partial arrays, seven n-vectors, column-block results.
 Work carve(const sla_mat& A, void* work) {
   Work w;
   char* p = (char*)work;
@@ -1634,6 +1721,7 @@ Work carve(const sla_mat& A, void* work) {
     w.vec[i] = p;
     p += align_up(n * es);
   }
+  w.cbpart = colblock_bytes(A) ? (void*)p : nullptr;
   return w;
 }
 
@@ -1666,6 +1754,13 @@ sla_status exit_status(const SolverState& fin, sla_solve_info* info, int* iters_
   }
   if (iters_out) *iters_out = iters;
   return st;
+}
+
+template <typename T>
+hipError_t launch_blk(const BlockArgs<T>& ba, int grid, hipStream_t s, bool nt) {
+  if (nt) hipLaunchKernelGGL((csr_blk_step<T, true>), dim3(grid), dim3(kWG), 0, s, ba);
+  else hipLaunchKernelGGL((csr_blk_step<T, false>), dim3(grid), dim3(kWG), 0, s, ba);
+  return hipGetLastError();
 }
 
 // Fused iteration (p and r formed inside the products' gathers) when A is a
@@ -1713,8 +1808,12 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
   const int grid = wide ? wide_grid(std::max(ntA, std::max(ntG, ntT)))
                         : step_grid(std::max(ntA, std::max(ntG, ntT)));
   const int gridV = wide ? std::min(grid, max_grid()) : grid;
-  const int npA = grid + A.fwd.nlong_rows, npG = grid + G.fwd.nlong_rows,
-            npT = grid + G.tr.nlong_rows;
+  // separate form on column blocks (random-graph CSR on its ordering): each
+  // product is a column-block pass and a reduction whose epilogue and
+  // partials are the step's own
+  const bool blk = !fused && A.cb && G.cb && G.cb->has_tr && w.cbpart;
+  const int npA = grid + (blk ? 0 : A.fwd.nlong_rows), npG = grid + (blk ? 0 : G.fwd.nlong_rows),
+            npT = grid + (blk ? 0 : G.tr.nlong_rows);
 
   SLA_HIP(hipMemsetAsync(w.st, 0, zeroed_bytes(A), s));
   const MallPlan plan = mall_plan(A, G);
@@ -1754,6 +1853,26 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
   aG.in0 = t;
   aG.y = z;
 
+  BlockArgs<T> bA{}, bT{}, bG{};
+  int gridB = kColBlocks;
+  const size_t cbstride = align_up((size_t)n * sizeof(T)) / sizeof(T);
+  if (blk) {
+    auto set_blocks = [&](BlockArgs<T>& ba, const sla_mat& m, const ColBlockSet& cs,
+                          const T* in) {
+      for (int c = 0; c < kColBlocks; ++c) {
+        StepArgs<T>& a = ba.blk[c];
+        fill_matrix(a, m, cs.blk[c], w.lpart + cs.lpart_off[c], w.lcnt + cs.lrow_off[c]);
+        a.in0 = in;
+        a.y = (T*)w.cbpart + (size_t)c * cbstride;
+        gridB = std::max(gridB, kColBlocks * std::min(a.ntiles, kWideGrid * max_grid() / kColBlocks));
+      }
+      ba.st = w.st;
+    };
+    set_blocks(bA, A, A.cb->fwd, nullptr);
+    set_blocks(bT, G, G.cb->tr, nullptr);
+    set_blocks(bG, G, G.cb->fwd, t);
+  }
+
   // unfused iteration: vector passes (p/x update, r update) around
   // single-gather products
   StepArgs<T> aV = aA, aR = aT;
@@ -1782,13 +1901,28 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
   aT.own = R[0];
   aT.pout = w.prr;
   hipEvent_t e0 = rec.begin(1, 0);
-  SLA_HIP((launch_step<T, M_GT0>(G, aT, grid, s, plan.nt_t, win)));
+  if (blk) {
+    for (auto& a : bT.blk) a.in0 = b;
+    SLA_HIP(launch_blk(bT, gridB, s, plan.nt_t));
+    hipLaunchKernelGGL((blk_reduce<T, M_GT0>), dim3(grid), dim3(kWG), 0, s, aT,
+                       (const T*)w.cbpart, cbstride);
+    SLA_HIP(hipGetLastError());
+  } else {
+    SLA_HIP((launch_step<T, M_GT0>(G, aT, grid, s, plan.nt_t, win)));
+  }
   rec.end(e0, 1, 0);
   if (!fused) aT.pout = nullptr;
   aG.k = 0;
   aG.rv = R[0];
   e0 = rec.begin(2, 0);
-  SLA_HIP((launch_step<T, M_G0>(G, aG, grid, s, plan.nt_g, win)));
+  if (blk) {
+    SLA_HIP(launch_blk(bG, gridB, s, plan.nt_g));
+    hipLaunchKernelGGL((blk_reduce<T, M_G0>), dim3(grid), dim3(kWG), 0, s, aG,
+                       (const T*)w.cbpart, cbstride);
+    SLA_HIP(hipGetLastError());
+  } else {
+    SLA_HIP((launch_step<T, M_G0>(G, aG, grid, s, plan.nt_g, win)));
+  }
   rec.end(e0, 2, 0);
 
   // Batches of iterations, at most two queued; the G step of a batch's last
@@ -1837,7 +1971,15 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
           aA.k = kk;
           aA.in0 = P[kk & 1];
           hipEvent_t ea = rec.begin(0, kk);
-          SLA_HIP((launch_step<T, M_AU>(A, aA, grid, s, plan.nt_a, win)));
+          if (blk) {
+            for (auto& a : bA.blk) a.in0 = P[kk & 1];
+            SLA_HIP(launch_blk(bA, gridB, s, plan.nt_a));
+            hipLaunchKernelGGL((blk_reduce<T, M_AU>), dim3(grid), dim3(kWG), 0, s, aA,
+                               (const T*)w.cbpart, cbstride);
+            SLA_HIP(hipGetLastError());
+          } else {
+            SLA_HIP((launch_step<T, M_AU>(A, aA, grid, s, plan.nt_a, win)));
+          }
           rec.end(ea, 0, kk);
           aR.k = kk;
           aR.in0 = R[(kk - 1) & 1];
@@ -1847,7 +1989,15 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
           aT.k = kk;
           aT.in0 = R[kk & 1];
           hipEvent_t et = rec.begin(1, kk);
-          SLA_HIP((launch_step<T, M_GTU>(G, aT, grid, s, plan.nt_t, win)));
+          if (blk) {
+            for (auto& a : bT.blk) a.in0 = R[kk & 1];
+            SLA_HIP(launch_blk(bT, gridB, s, plan.nt_t));
+            hipLaunchKernelGGL((blk_reduce<T, M_GTU>), dim3(grid), dim3(kWG), 0, s, aT,
+                               (const T*)w.cbpart, cbstride);
+            SLA_HIP(hipGetLastError());
+          } else {
+            SLA_HIP((launch_step<T, M_GTU>(G, aT, grid, s, plan.nt_t, win)));
+          }
           rec.end(et, 1, kk);
           aG.npin = gridV;  // rr partials now come from vec_r_update
         }
@@ -1855,7 +2005,14 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
         aG.rv = R[kk & 1];
         aG.poll = kk == kend ? dpoll + ps : nullptr;
         hipEvent_t eg = rec.begin(2, kk);
-        SLA_HIP((launch_step<T, M_G>(G, aG, grid, s, plan.nt_g, win)));
+        if (blk) {
+          SLA_HIP(launch_blk(bG, gridB, s, plan.nt_g));
+          hipLaunchKernelGGL((blk_reduce<T, M_G>), dim3(grid), dim3(kWG), 0, s, aG,
+                             (const T*)w.cbpart, cbstride);
+          SLA_HIP(hipGetLastError());
+        } else {
+          SLA_HIP((launch_step<T, M_G>(G, aG, grid, s, plan.nt_g, win)));
+        }
         rec.end(eg, 2, kk);
       }
       aG.poll = nullptr;
@@ -1971,7 +2128,8 @@ int64_t long_part_bound(const sla_mat& A) {
 size_t workspace_base(const sla_mat& A) {
   const size_t es = A.dtype == SLA_F64 ? 8 : 4;
   return zeroed_bytes(A) + align_up((size_t)long_part_bound(A) * sizeof(double)) +
-         3 * align_up(partial_slots(A) * sizeof(double)) + 7 * align_up((size_t)A.n() * es);
+         3 * align_up(partial_slots(A) * sizeof(double)) + 7 * align_up((size_t)A.n() * es) +
+         colblock_bytes(A);
 }
 
 size_t workspace_bytes(const sla_mat& A) {
