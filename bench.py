@@ -193,15 +193,35 @@ MSTEP_NAMES = {0: "Y = M X (products of several vectors)", 1: "A step, iteration
                6: "A product (separate form)", 7: "G^T product (separate form)"}
 
 
+def _pair_blocks(keys):
+    """Column-block products run as csr_blk_step (the same kernel for every
+    step) followed by blk_reduce<T, MODE>: name each csr_blk_step launch by
+    the mode of the reduction that follows it, csr_blk_step<T, MODE>."""
+    out = list(keys)
+    for i, k in enumerate(out):
+        if not k.startswith("csr_blk_step"):
+            continue
+        nxt = next((n for n in out[i + 1:] if n.startswith("blk_reduce<")), None)
+        m = re.match(r"blk_reduce<(\w+), (\d+)>", nxt or "")
+        if m:
+            out[i] = f"csr_blk_step<{m.group(1)}, {m.group(2)}>"
+    return out
+
+
 def _counter_rows(run_dir):
     import csv
     import glob
-    out = {}
+    rows = []
     for path in sorted(glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"),
                                  recursive=True)):
         for r in csv.DictReader(open(path)):
-            key = _kernel_key(r["Kernel_Name"])
-            out.setdefault(key, []).append((float(r["Counter_Value"]), int(r.get("Grid_Size", 0))))
+            rows.append((int(r.get("Dispatch_Id", 0) or 0), _kernel_key(r["Kernel_Name"]),
+                         float(r["Counter_Value"]), int(r.get("Grid_Size", 0))))
+    rows.sort(key=lambda t: t[0])
+    keys = _pair_blocks([k for _, k, _, _ in rows])
+    out = {}
+    for key, (_, _, v, g) in zip(keys, rows):
+        out.setdefault(key, []).append((v, g))
     return out
 
 
@@ -215,6 +235,13 @@ def _describe(key):
     m = re.match(r"(sell_step|sell_win_step|csr_step|bsell_step|bsr3_step)<\w+, (\d+)", key)
     if m:
         return STEP_NAMES.get(int(m.group(2)), m.group(2))
+    m = re.match(r"csr_blk_step<\w+, (\d+)>", key)
+    if m:
+        return "column blocks of the " + STEP_NAMES.get(int(m.group(1)), m.group(1))
+    m = re.match(r"blk_reduce<\w+, (\d+)>", key)
+    if m:
+        return ("sum of the 8 column-block results, epilogue of the "
+                + STEP_NAMES.get(int(m.group(1)), m.group(1)))
     m = re.match(r"(msell_step|mbsell_step|mtile_step|mrow_step)<\w+, (\d+), (\d+)", key)
     if m:
         return f"{MSTEP_NAMES.get(int(m.group(2)), m.group(2))}, K = {m.group(3)}"
@@ -333,6 +360,7 @@ def summarize_trace(trace_dir, bench_json=None, trace_args="--steps 2 --warmup 1
             t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
             recs.append((t0, t1, _short_kernel(r["Kernel_Name"])))
     recs.sort()
+    recs = [(t0, t1, k) for (t0, t1, _), k in zip(recs, _pair_blocks([k for _, _, k in recs]))]
     total = sum(t1 - t0 for t0, t1, _ in recs)
     by = {}
     for t0, t1, k in recs:
@@ -347,13 +375,22 @@ def summarize_trace(trace_dir, bench_json=None, trace_args="--steps 2 --warmup 1
                      f"{100 * sum(d) * 1e3 / total:.2f} | {len(w)} | {statistics.fmean(w):.2f} |")
     step = [(t0, t1) for t0, t1, k in recs
             if k.split("<")[0] in ("sell_step", "sell_win_step", "csr_step", "bsell_step",
-                                   "bsr3_step")
+                                   "bsr3_step", "csr_blk_step", "blk_reduce")
             and (t1 - t0) / 1e3 > cut[k]]
     gaps = sorted(max(0, b0 - a1) / 1e3 for (a0, a1), (b0, b1) in zip(step, step[1:]))
     a_key = next((k for k, _ in rows
                   if re.match(r"(sell_win_step|sell_step|bsell_step|csr_step|bsr3_step)<\w+, (2|8),",
                               k)), None)
     a_work = [v for v in by.get(a_key, []) if v > cut[a_key]]
+    blk_key = next((k for k, _ in rows if re.match(r"csr_blk_step<\w+, 8>", k)), None)
+    if blk_key:
+        # the A product on column blocks: each working csr_blk_step<T, 8> launch
+        # plus the reduction launched right after it
+        red = blk_key.replace("csr_blk_step", "blk_reduce")
+        a_key = f"{blk_key} + {red}"
+        a_work = [(a1 - a0 + b1 - b0) / 1e3
+                  for (a0, a1, ka), (b0, b1, kb) in zip(recs, recs[1:])
+                  if ka == blk_key and kb == red and (a1 - a0) / 1e3 > cut[blk_key]]
     cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d {d} -o bench -- "
            "python -u bench.py {a}").format(d=trace_dir, a=trace_args)
     rec = json.loads(open(bench_json).read().strip().splitlines()[-1]) if bench_json else None
@@ -633,6 +670,10 @@ def main():
     # Outside the timed region: the parts of a step on their own.
     A = mk(a_rp, a_ci, a_v)
     G = mk(g_rp, g_ci, g_v, transpose=True)
+    # the separate form's products on A's locality ordering run on column
+    # blocks unless SLA_COLBLK=0
+    colblk = (B.sla_mat_reordered(A) and not fused_iteration(p.A)
+              and os.environ.get("SLA_COLBLK", "1") != "0")
     setup = []
     for _ in range(3):
         torch.cuda.synchronize()
@@ -749,13 +790,22 @@ def main():
     tr = traffic_if_current(workload)
     a_mode, gt_mode = (2, 4) if fused else (8, 9)
     step_re = r"(sell_win_step|sell_step|csr_step|bsell_step|bsr3_step)<\w+, {}[,>]"
-    traffic = kernel_bytes(tr, step_re.format(a_mode)) if has_a else None
+
+    def step_bytes(mode):
+        """Counter bytes of one step: its kernel, or on column blocks the
+        block pass plus the reduction."""
+        one = kernel_bytes(tr, step_re.format(mode))
+        if one is not None:
+            return one
+        bp = kernel_bytes(tr, rf"csr_blk_step<\w+, {mode}>")
+        br = kernel_bytes(tr, rf"blk_reduce<\w+, {mode}>")
+        return bp + br if bp is not None and br is not None else None
+    traffic = step_bytes(a_mode) if has_a else None
     physical = None
     if tr:
-        it_kernels = [step_re.format(a_mode), step_re.format(gt_mode), step_re.format(6)]
+        parts = [step_bytes(a_mode), step_bytes(gt_mode), step_bytes(6)]
         if not fused:
-            it_kernels += [r"vec_p_update<\w+, 2>", r"vec_r_update<"]
-        parts = [kernel_bytes(tr, k) for k in it_kernels]
+            parts += [kernel_bytes(tr, k) for k in (r"vec_p_update<\w+, 2>", r"vec_r_update<")]
         sp = kernel_bytes(tr, step_re.format(0))
         it_bytes = sum(parts) if all(v is not None for v in parts) else None
         physical = {
@@ -783,6 +833,10 @@ def main():
     elif bs == 3:
         a_kernel = ("bsell_step<A product> (BSR sliced ELL, q = A p and p.q; p, x and r "
                     "updates in separate streaming passes)")
+    elif colblk:
+        a_kernel = ("csr_blk_step + blk_reduce<A product> (column blocks on the locality "
+                    "ordering: q = A p per block of columns, the 8 results added with p.q; p, x "
+                    "and r updates in separate streaming passes)")
     else:
         a_kernel = ("csr_step<A product> (LDS tiles, q = A p and p.q; p, x and r updates in "
                     "separate streaming passes)")

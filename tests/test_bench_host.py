@@ -106,3 +106,19 @@ def test_counter_summary_calibrates_by_the_copy(tmp_path):
     assert bench.kernel_bytes(rec, r"sell_step<\w+, 2[,>]") == pytest.approx(k["bytes"])
     assert bench.kernel_bytes(rec, r"sell_step<\w+, 4[,>]") is None
     assert "A step" in open(tmp_path / "traffic_fake.md").read()
+
+
+def test_column_block_launches_take_their_reduction_mode():
+    """The column-block pass is one kernel for every step; the summaries name
+    each launch by the reduction launched after it."""
+    keys = ["vec_p_update<double, 2>", "csr_blk_step<double, true>", "blk_reduce<double, 8>",
+            "vec_r_update<double>", "csr_blk_step<double, true>", "blk_reduce<double, 9>",
+            "csr_blk_step<double, false>", "blk_reduce<double, 6>", "csr_blk_step<double, true>"]
+    out = bench._pair_blocks(keys)
+    assert out[1] == "csr_blk_step<double, 8>"
+    assert out[4] == "csr_blk_step<double, 9>"
+    assert out[6] == "csr_blk_step<double, 6>"
+    assert out[8] == "csr_blk_step<double, true>"  # no reduction after it: unchanged
+    assert out[0] == keys[0] and out[2] == keys[2]
+    assert bench._describe("csr_blk_step<double, 8>").startswith("column blocks of the A product")
+    assert "G step" in bench._describe("blk_reduce<double, 6>")

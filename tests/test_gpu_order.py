@@ -216,3 +216,38 @@ def test_ordered_multi_rhs(k, ordered):
     for c in range(k):
         g = g - lam[ri, c] * x[cj, c]
     assert np.array_equal(host(gv), g)
+
+
+@pytest.mark.parametrize("colblk", ["1", "0"])
+def test_column_blocks_against_the_oracle(colblk, ordered, monkeypatch):
+    """The separate form's products on the ordering run on column blocks
+    (SLA_COLBLK=0 keeps the row tiles): both against the oracle's solve, the
+    prefix iterates element by element, and the column-block solve run twice
+    bitwise identical."""
+    monkeypatch.setenv("SLA_COLBLK", colblk)
+    p = problem("powerlaw_20k")
+    x_ref, st, it, _ = oracle.pcg(p.A, p.G, p.eps, p.b, p.rtol, p.maxit)
+    assert st == oracle.OK
+    A, G = handles(p)
+    say("column blocks", colblk, "oracle iterations", it)
+    x, info = B.sla_pcg_solve(A, G, p.eps, tdev(p.b), rtol=p.rtol, maxit=p.maxit)
+    say("  gpu iterations", info.iterations)
+    assert info.status == B.OK and info.rel_residual <= p.rtol
+    assert_solve_matches(p.A, p.G, p.eps, p.b, p.rtol, p.maxit, info.iterations, host(x), it,
+                         x_ref, strict=False, what=f"column blocks {colblk}")
+    x2, info2 = B.sla_pcg_solve(A, G, p.eps, tdev(p.b), rtol=p.rtol, maxit=p.maxit)
+    assert info2.iterations == info.iterations and torch.equal(x, x2)
+    x3_ref, _, _, rr3 = oracle.pcg(p.A, p.G, p.eps, p.b, p.rtol, 3)
+    x3, info3 = B.sla_pcg_solve(A, G, p.eps, tdev(p.b), rtol=p.rtol, maxit=3)
+    assert rel(host(x3), x3_ref) <= 1e-10
+    assert abs(info3.rel_residual - rr3) <= 1e-8 * rr3
+
+
+def test_workspace_holds_the_column_block_results(monkeypatch):
+    p = problem("powerlaw_20k")
+    monkeypatch.setenv("SLA_ORDER", "1")
+    monkeypatch.setenv("SLA_COLBLK", "1")
+    with_blocks = B.sla_pcg_workspace_size(create(p.A))
+    monkeypatch.setenv("SLA_COLBLK", "0")
+    without = B.sla_pcg_workspace_size(create(p.A))
+    assert with_blocks >= without + 8 * 8 * p.A.n
