@@ -425,6 +425,37 @@ def summarize_trace(trace_dir, bench_json=None, trace_args="--steps 2 --warmup 1
     print("\n".join(lines))
 
 
+def summarize_markers(trace_dir, log_path=None, name="powerlaw_20k",
+                      run="-m preconditioned_cg_solver_amd.studies trace"):
+    """profiles/marker_trace_<name>.md from a rocprofv3 --marker-trace
+    --kernel-trace run with SLA_TRACE=1: each roctx range of the library, its
+    duration and the kernels inside it, and the run's [sla] stderr lines."""
+    import csv
+    import glob
+    mk = [r for path in glob.glob(os.path.join(trace_dir, "**", "*marker_api_trace.csv"),
+                                  recursive=True) for r in csv.DictReader(open(path))]
+    kr = [r for path in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"),
+                                  recursive=True) for r in csv.DictReader(open(path))]
+    kt = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in kr)
+    lines = [f"# roctx ranges of the library (SLA_TRACE=1), {name}", "",
+             "Commands (from the repository root, `export TMPDIR=/tmp`):", "",
+             f"    SLA_TRACE=1 rocprofv3 --marker-trace --kernel-trace --output-format csv -d "
+             f"{trace_dir} -o tr -- python -u {run} > LOG 2>&1",
+             f"    python bench.py --marker-summary {trace_dir} LOG", "",
+             "| range | duration ms | kernels inside | kernel time ms |", "|---|---|---|---|"]
+    for r in sorted(mk, key=lambda r: int(r["Start_Timestamp"])):
+        t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        ins = [(a, b) for a, b in kt if a >= t0 and b <= t1]
+        lines.append(f"| `{r['Function']}` | {(t1 - t0) / 1e6:.3f} | {len(ins)} | "
+                     f"{sum(b - a for a, b in ins) / 1e6:.3f} |")
+    if log_path:
+        lines += ["", "stderr lines of the same run:", ""]
+        lines += ["    " + l.rstrip() for l in open(log_path) if l.startswith("[sla]")]
+    with open(os.path.join(ROOT, "profiles", f"marker_trace_{name}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def cpu_model() -> str:
     """The host CPU's model name (from /proc/cpuinfo)."""
     try:
@@ -540,10 +571,16 @@ def main():
                     help="with --counter-summary: bench.py arguments of the counted runs")
     ap.add_argument("--trace-args", default="--steps 2 --warmup 1 --no-cpu-baseline",
                     help="bench.py arguments of the traced run (for the summary's command)")
+    ap.add_argument("--marker-summary", nargs="+", metavar="DIR",
+                    help="write profiles/marker_trace_powerlaw_20k.md from a rocprofv3 "
+                         "--marker-trace run of the trace study (DIR [LOG])")
     ap.add_argument("--trace-summary", nargs="+", metavar="DIR",
                     help="write profiles/kernel_trace_<workload>.md from a rocprofv3 "
                          "--kernel-trace --stats run (and optionally a saved bench JSON line)")
     args = ap.parse_args()
+    if args.marker_summary:
+        summarize_markers(*args.marker_summary[:2])
+        return
     if args.trace_summary:
         summarize_trace(*args.trace_summary[:2], trace_args=args.trace_args)
         return

@@ -60,13 +60,25 @@
  *    their products stream are at least A's and fit 240 MB beside six
  *    vectors; else A when it fits the budget; else none.  The rest stream
  *    non-temporally.
- *  - SLA_BATCH_ITERS (default 16, 1..4096): iterations enqueued between two
- *    host polls of the device exit flag.
+ *  - SLA_BATCH_ITERS (1..4096): the full batch of iterations enqueued
+ *    between two host polls of the device's record (default: sized from an
+ *    estimate of one iteration to last about 0.8 ms, 2..16; the last
+ *    batches of a solve are shortened to the predicted stopping iteration).
  *  - SLA_ORDER=0|1: locality ordering of the solves off, or on for every CSR
  *    matrix outside the SELL layout (default: automatic, see
  *    sla_mat_reordered).
- * SLA_GRID is read once per device, SLA_MALL_BUDGET_MB and SLA_BATCH_ITERS
- * once per process; the others at every handle creation or solve.
+ *  - SLA_COLBLK=0: the separate iteration form on a locality ordering keeps
+ *    the row tiles instead of splitting each operator into 8 column blocks
+ *    (read at handle creation).
+ *  - SLA_WIN=0|1|2: the windowed slice-offset engine off, for the A steps
+ *    (default), or for every step.
+ *  - SLA_TRACE=1: roctx ranges around handle creation, the locality
+ *    ordering, solves, adjoint solves and the pattern gradient (seen by
+ *    rocprofv3 --marker-trace; the roctx library is opened at run time),
+ *    and one line per call on stderr with n, iterations, relative residual,
+ *    status and wall time.
+ * SLA_GRID is read once per device, SLA_MALL_BUDGET_MB, SLA_BATCH_ITERS and
+ * SLA_TRACE once per process; the others at every handle creation or solve.
  */
 #ifndef SLA_H
 #define SLA_H

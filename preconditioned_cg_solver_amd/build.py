@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsla.so")
 SOURCES = ["setup.hip", "solver.hip", "multi.hip", "noalloc.hip", "host_util.cpp", "spectrum.cpp",
-           "api.cpp"]
+           "trace.cpp", "api.cpp"]
 ARCH = os.environ.get("SLA_OFFLOAD_ARCH", "gfx950")
 
 
@@ -60,7 +60,7 @@ def build(verbose: bool = False) -> str:
     if failed:
         raise RuntimeError("hipcc failed:\n" + "\n".join(f"--- {s}\n{o}" for s, o in failed))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, "-ldl"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
     return LIB

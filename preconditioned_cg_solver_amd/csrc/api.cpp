@@ -241,6 +241,7 @@ sla_status ensure_order(sla_mat* A, sla_mat* G, hipStream_t s, bool* use) {
   if (!A->ord_want || A == G || A->n() == 0) return SLA_OK;
   std::lock_guard<std::mutex> lk(g_order_mu);
   sla_status st = SLA_OK;
+  TraceRange tr("locality ordering");
   if (!A->perm) {
     int32_t *perm = nullptr, *iperm = nullptr;
     st = build_order(*A, &perm, &iperm, s);
@@ -468,14 +469,21 @@ extern "C" {
 sla_status sla_csr_create(sla_mat_t* out, int64_t n, int64_t nnz, const int32_t* d_row_ptr,
                           const int32_t* d_col_idx, const void* d_vals, sla_dtype dtype,
                           uint32_t flags, void* stream) {
-  return create_common(out, n, nnz, 1, d_row_ptr, d_col_idx, d_vals, dtype, flags, stream);
+  TraceRange tr("sla_csr_create");
+  const sla_status st = create_common(out, n, nnz, 1, d_row_ptr, d_col_idx, d_vals, dtype, flags,
+                                      stream);
+  trace_solve(tr, "sla_csr_create", n, nullptr, st);
+  return st;
 }
 
 sla_status sla_bsr_create(sla_mat_t* out, int64_t n_block_rows, int64_t nnzb, int32_t block_dim,
                           const int32_t* d_brow_ptr, const int32_t* d_bcol_idx,
                           const void* d_bvals, sla_dtype dtype, uint32_t flags, void* stream) {
-  return create_common(out, n_block_rows, nnzb, block_dim, d_brow_ptr, d_bcol_idx, d_bvals, dtype,
-                       flags, stream);
+  TraceRange tr("sla_bsr_create");
+  const sla_status st = create_common(out, n_block_rows, nnzb, block_dim, d_brow_ptr, d_bcol_idx,
+                                      d_bvals, dtype, flags, stream);
+  trace_solve(tr, "sla_bsr_create", n_block_rows * block_dim, nullptr, st);
+  return st;
 }
 
 sla_status sla_mat_destroy(sla_mat_t m) {
@@ -594,8 +602,10 @@ sla_status sla_pcg_solve(sla_mat_t A, sla_mat_t G, double eps, const void* d_b, 
                          sla_solve_info* info) {
   sla_status st = check_solve(A, G, eps, d_b, d_x, rtol, maxit, d_work, work_bytes);
   if (st != SLA_OK) return st;
-  return solve_any(A, G, eps, d_b, d_x, rtol, maxit, d_work, work_bytes, (hipStream_t)stream,
-                   info);
+  TraceRange tr("sla_pcg_solve");
+  st = solve_any(A, G, eps, d_b, d_x, rtol, maxit, d_work, work_bytes, (hipStream_t)stream, info);
+  trace_solve(tr, "sla_pcg_solve", A->n(), info, st);
+  return st;
 }
 
 sla_status sla_pcg_solve_history(sla_mat_t A, sla_mat_t G, double eps, const void* d_b, void* d_x,
@@ -626,12 +636,21 @@ sla_status sla_pcg_adjoint(sla_mat_t A, sla_mat_t G, double eps, const void* d_x
       SLA_OK)
     return st;
   hipStream_t s = (hipStream_t)stream;
+  TraceRange tr("sla_pcg_adjoint");
   st = solve_any(A, G, eps, d_grad_x, d_grad_b, rtol, maxit, d_work, work_bytes, s, info);
-  if (st < 0) return st;
-  sla_status gs = sla::pattern_grad(*A, d_grad_b, d_x, d_grad_vals, s);
+  if (st < 0) {
+    trace_solve(tr, "sla_pcg_adjoint", A->n(), info, st);
+    return st;
+  }
+  sla_status gs;
+  {
+    TraceRange tg("sla_pattern_grad");
+    gs = sla::pattern_grad(*A, d_grad_b, d_x, d_grad_vals, s);
+  }
   if (gs != SLA_OK) return gs;
   hipError_t e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  trace_solve(tr, "sla_pcg_adjoint", A->n(), info, st);
   return st;
 }
 
@@ -680,8 +699,11 @@ sla_status sla_pcg_solve_multi(sla_mat_t A, sla_mat_t G, double eps, const void*
   }
   sla_status st = check_solve(A, G, eps, d_b, d_x, rtol, maxit, d_work, work_bytes, k);
   if (st != SLA_OK) return st;
-  return solve_multi_any(A, G, eps, d_b, d_x, k, rtol, maxit, d_work, (hipStream_t)stream, info,
-                         col_status);
+  TraceRange tr("sla_pcg_solve_multi");
+  st = solve_multi_any(A, G, eps, d_b, d_x, k, rtol, maxit, d_work, (hipStream_t)stream, info,
+                       col_status);
+  trace_solve(tr, "sla_pcg_solve_multi", A->n() * k, nullptr, st);
+  return st;
 }
 
 sla_status sla_pcg_adjoint_multi(sla_mat_t A, sla_mat_t G, double eps, const void* d_x,

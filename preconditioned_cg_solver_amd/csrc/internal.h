@@ -384,6 +384,21 @@ size_t stream_bytes(const sla_mat& m, const MatView& v);
 size_t mall_budget();
 hipEvent_t timing_event();
 int batch_iters(double iter_us);
+// Tracing (trace.cpp, SLA_TRACE=1): a roctx range for the lifetime of a
+// TraceRange, and one stderr line per solve.
+bool trace_on();
+class TraceRange {
+ public:
+  explicit TraceRange(const char* name);
+  ~TraceRange();
+  double elapsed_ms() const;
+
+ private:
+  bool on_;
+  double t0_;
+};
+void trace_solve(const TraceRange& r, const char* what, int64_t n, const sla_solve_info* info,
+                 sla_status st);
 hipError_t wait_poll(const SolverState* rec, int kend, hipStream_t s, const int* dev_done,
                      SolverState* out);
 double iteration_estimate_us(const sla_mat& A, const sla_mat& G, int elem_bytes, int k,

@@ -15,8 +15,15 @@
   || A M^-1 / s - I ||_F^2 / n estimated with Rademacher probes, s being the
   mean absolute stored entry of A.
 
-Usage: ``python -m preconditioned_cg_solver_amd.studies jacobi|quality [--configs 0,1,2,3]``
-Prints one JSON line per configuration.
+* ``trace``: one forward and one adjoint solve (with dL/dA) of a power-law
+  SPD system of ``--rows`` rows (default 20,000) on its locality ordering:
+  the run to record with ``SLA_TRACE=1`` under ``rocprofv3 --marker-trace``,
+  which shows the library's phases (handle creation, the ordering, the
+  solves, the pattern gradient) around their kernels.
+
+Usage: ``python -m preconditioned_cg_solver_amd.studies jacobi|quality|trace
+[--configs 0,1,2,3] [--rows N]``.  jacobi and quality print one JSON line per
+configuration.
 """
 from __future__ import annotations
 
@@ -106,16 +113,44 @@ def quality(configs, nprobe=16):
             h.destroy()
 
 
+def trace_run(rows: int):
+    """One forward and one adjoint solve of a seeded power-law SPD system
+    (16 random neighbours per row, Zipf 2.1 column weights, factorised SPAI
+    eps = 3e-3), forced onto its locality ordering."""
+    import os
+    os.environ.setdefault("SLA_ORDER", "1")
+    rng = np.random.default_rng([20, rows])
+    A = I.powerlaw_spd(rows, rng)
+    G = I.spai_factor(A, rng)
+    b = rng.standard_normal(rows)
+    dev = torch.device("cuda:0")
+
+    def mk(M, transpose=False):
+        return B.sla_csr_create(torch.as_tensor(M.row_ptr.astype(np.int32), device=dev),
+                                torch.as_tensor(M.col_idx.astype(np.int32), device=dev),
+                                torch.as_tensor(M.vals, device=dev), build_transpose=transpose)
+    Ah, Gh = mk(A), mk(G, transpose=True)
+    bt = torch.as_tensor(b, device=dev)
+    x, info = B.sla_pcg_solve(Ah, Gh, 3e-3, bt, rtol=1e-8, maxit=2000)
+    _, _, ainfo = B.sla_pcg_adjoint(Ah, Gh, 3e-3, x, bt, rtol=1e-8, maxit=2000)
+    print(json.dumps({"rows": rows, "nnz": int(A.nnz), "reordered": B.sla_mat_reordered(Ah),
+                      "iterations": info.iterations, "adjoint_iterations": ainfo.iterations}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("study", choices=["jacobi", "quality"])
+    ap.add_argument("study", choices=["jacobi", "quality", "trace"])
     ap.add_argument("--configs", default="0,1,2,3")
+    ap.add_argument("--rows", type=int, default=20000)
     args = ap.parse_args()
     configs = [int(c) for c in args.configs.split(",")]
     if args.study == "jacobi":
         jacobi(configs)
-    else:
+    elif args.study == "quality":
         quality(configs)
+    else:
+        trace_run(args.rows)
 
 
 if __name__ == "__main__":
