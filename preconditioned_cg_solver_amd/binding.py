@@ -44,15 +44,23 @@ _lib = None
 _lock = threading.Lock()
 
 
+def lib_path() -> str:
+    """libsla.so, or with SLA_DEBUG=1 the bounds-checking build libsla_debug.so."""
+    if os.environ.get("SLA_DEBUG") == "1":
+        return os.path.join(PKG, "libsla_debug.so")
+    return LIB_PATH
+
+
 def lib():
-    """Load libsla.so (raises if it has not been built)."""
+    """Load the library (raises if it has not been built)."""
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(LIB_PATH):
-                raise ImportError(f"{LIB_PATH} is missing: build it with "
+            path = lib_path()
+            if not os.path.exists(path):
+                raise ImportError(f"{path} is missing: build it with "
                                   "preconditioned_cg_solver_amd.build.build()")
-            _lib = _declare(ctypes.CDLL(LIB_PATH))
+            _lib = _declare(ctypes.CDLL(path))
         return _lib
 
 

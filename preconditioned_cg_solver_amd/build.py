@@ -15,6 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsla.so")
+LIB_DEBUG = os.path.join(PKG, "libsla_debug.so")
 SOURCES = ["setup.hip", "solver.hip", "multi.hip", "noalloc.hip", "host_util.cpp", "spectrum.cpp",
            "trace.cpp", "api.cpp"]
 ARCH = os.environ.get("SLA_OFFLOAD_ARCH", "gfx950")
@@ -35,16 +36,20 @@ def flags():
             "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wextra", "-Wno-unused-function"]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source to an object, then link libsla.so (always rebuilds)."""
-    objdir = os.path.join(PKG, "_build")
+def build(verbose: bool = False, debug: bool = False) -> str:
+    """Compile every source to an object, then link libsla.so (always rebuilds).
+    debug=True builds libsla_debug.so with SLA_DEBUG defined: every gathered
+    column index is checked against the vector length on the device, and a
+    solve that saw one out of range returns SLA_ERR_INVALID_ARG."""
+    objdir = os.path.join(PKG, "_build_debug" if debug else "_build")
     os.makedirs(objdir, exist_ok=True)
     objs = []
     procs = []
     for src in SOURCES:
         obj = os.path.join(objdir, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [hipcc(), *flags(), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc(), *flags(), *(["-DSLA_DEBUG=1"] if debug else []), *lang, "-c",
+               os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
@@ -59,13 +64,13 @@ def build(verbose: bool = False) -> str:
             print(out)
     if failed:
         raise RuntimeError("hipcc failed:\n" + "\n".join(f"--- {s}\n{o}" for s, o in failed))
-    tmp = LIB + ".tmp"
+    out = LIB_DEBUG if debug else LIB
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, "-ldl"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    build(verbose="-v" in sys.argv)
-    print(LIB)
+    print(build(verbose="-v" in sys.argv, debug="--debug" in sys.argv))

@@ -109,7 +109,7 @@ struct SolverState {
   int done;        // set once an exit condition is met
   int exit_kind;   // ExitKind
   int exit_iter;   // iteration index at which the exit was taken
-  int pad0;
+  int dbg_bad;     // debug builds: gathered columns found out of range
   double rr;       // last ||r||^2
   double bb;       // ||b||^2
   double rho[kRing];    // rho_k = r_k . z_k at slot k % kRing

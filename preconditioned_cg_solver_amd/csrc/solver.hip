@@ -100,6 +100,9 @@ struct StepArgs {
   double* hist_a;  // optional coefficient history: alpha_k at [k-1],
   double* hist_b;  // beta_k = rho_k / rho_{k-1} at [k-1], for k <= hist_len
   int hist_len;
+#ifdef SLA_DEBUG
+  int dbg_shrink;  // gathered columns must lie below n - dbg_shrink
+#endif
 };
 
 template <typename T>
@@ -202,9 +205,19 @@ __device__ __forceinline__ bool prologue(const StepArgs<T>& a, Coef<T>& cf, doub
   }
 }
 
-// Value of the gathered vector at column j.
+// Value of the gathered vector at column j.  Debug builds (SLA_DEBUG) check
+// j against the vector length (less dbg_shrink, which a test sets from the
+// host to force the check on valid input): an offender is counted in the
+// solve's state and entry 0 is read instead, and the host turns the count
+// into SLA_ERR_INVALID_ARG.
 template <typename T, int MODE>
 __device__ __forceinline__ T gat(const StepArgs<T>& a, int j, const Coef<T>& cf) {
+#ifdef SLA_DEBUG
+  if (j < 0 || j >= a.n - a.dbg_shrink) {
+    if (a.st) atomicAdd(&a.st->dbg_bad, 1);
+    j = 0;
+  }
+#endif
   if constexpr (MODE == M_A || MODE == M_GT) return fma(cf.c, a.in1[j], a.in0[j]);
   else return a.in0[j];
 }
@@ -780,10 +793,11 @@ __global__ __launch_bounds__(kWG) void sell_win_step(StepArgs<T> a) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const bool ok = (m >> (j + u)) & 1;
-          const int c = ok ? row + cr[u] : row;
+          // a row without this slot (padding rows of the last slice
+          // included) reads its own window entry or entry 0, never past n
           T g;
-          if (cr[u] >= -kWinHalo && cr[u] <= kWinHalo) g = gs[c - wb];
-          else g = gat<T, MODE>(a, c, cf);
+          if (cr[u] >= -kWinHalo && cr[u] <= kWinHalo) g = gs[(ok ? row + cr[u] : row) - wb];
+          else g = gat<T, MODE>(a, ok ? row + cr[u] : 0, cf);
           x[u] = ok ? g : T(0);
           if (!ok) cv[u] = T(0);
         }
@@ -1468,6 +1482,15 @@ __global__ __launch_bounds__(kWG) void bsr3_grad_wide(const int32_t* __restrict_
 // ---------------------------------------------------------------------------
 
 
+#ifdef SLA_DEBUG
+// Debug builds: SLA_DEBUG_SHRINK=k makes the gather check reject the last k
+// columns too (valid input), so tests can reach the error path safely.
+int debug_shrink() {
+  const char* e = getenv("SLA_DEBUG_SHRINK");
+  return e ? std::max(0, atoi(e)) : 0;
+}
+#endif
+
 template <typename T>
 void fill_matrix(StepArgs<T>& a, const sla_mat& m, const MatView& v, double* long_part,
                  int* long_cnt) {
@@ -1490,6 +1513,9 @@ void fill_matrix(StepArgs<T>& a, const sla_mat& m, const MatView& v, double* lon
   a.nbr = (int)m.nbr;
   a.long_part = long_part;
   a.long_cnt = long_cnt;
+#ifdef SLA_DEBUG
+  a.dbg_shrink = debug_shrink();
+#endif
 }
 
 // The windowed slice-offset engine (sell_win_step): SLA_WIN=1 (default) for
@@ -1863,6 +1889,9 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
         StepArgs<T>& a = ba.blk[c];
         fill_matrix(a, m, cs.blk[c], w.lpart + cs.lpart_off[c], w.lcnt + cs.lrow_off[c]);
         a.in0 = in;
+#ifdef SLA_DEBUG
+        a.st = w.st;  // the gather check's count (the pass itself reads no state)
+#endif
         a.y = (T*)w.cbpart + (size_t)c * cbstride;
         gridB = std::max(gridB, kColBlocks * std::min(a.ntiles, kWideGrid * max_grid() / kColBlocks));
       }
@@ -2044,6 +2073,14 @@ sla_status pcg_impl(const sla_mat& A, const sla_mat& G, double eps, const T* b, 
   SLA_HIP(hipMemcpyAsync(hs, w.st, sizeof(SolverState), hipMemcpyDeviceToHost, s));
   SLA_HIP(hipStreamSynchronize(s));
   const SolverState fin = *hs;
+#ifdef SLA_DEBUG
+  if (fin.dbg_bad) {
+    char msg[96];
+    snprintf(msg, sizeof msg, "debug build: %d gathered column indices out of range", fin.dbg_bad);
+    set_error(msg);
+    return SLA_ERR_INVALID_ARG;
+  }
+#endif
 
   int iters = 0;
   const sla_status st = exit_status(fin, info, &iters);
