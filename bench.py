@@ -283,17 +283,26 @@ def summarize_counters(fetch_dir, write_dir, l2_dir=None, workload="poisson3d_12
     if l2:
         import csv
         import glob
-        hm = {}
+        rows = []
         for path in glob.glob(os.path.join(l2_dir, "**", "*counter_collection.csv"),
                               recursive=True):
             for r in csv.DictReader(open(path)):
-                k = _kernel_key(r["Kernel_Name"])
-                d = hm.setdefault(k, {"hit": 0.0, "miss": 0.0})
-                name = r.get("Counter_Name", "")
-                if "HIT" in name:
-                    d["hit"] += float(r["Counter_Value"])
-                elif "MISS" in name:
-                    d["miss"] += float(r["Counter_Value"])
+                rows.append((int(r.get("Dispatch_Id", 0) or 0), _kernel_key(r["Kernel_Name"]),
+                             r.get("Counter_Name", ""), float(r["Counter_Value"])))
+        # one key per dispatch (two counter rows each), column-block passes
+        # named by their reduction as for the byte counters
+        ids = sorted({d for d, _, _, _ in rows})
+        first = {}
+        for d, k, _, _ in rows:
+            first.setdefault(d, k)
+        named = dict(zip(ids, _pair_blocks([first[d] for d in ids])))
+        hm = {}
+        for d_id, _, name, v in rows:
+            d = hm.setdefault(named[d_id], {"hit": 0.0, "miss": 0.0})
+            if "HIT" in name:
+                d["hit"] += v
+            elif "MISS" in name:
+                d["miss"] += v
         for k, d in hm.items():
             if k in kernels and d["hit"] + d["miss"] > 0:
                 kernels[k]["l2_hit_rate"] = d["hit"] / (d["hit"] + d["miss"])
