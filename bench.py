@@ -335,7 +335,7 @@ def summarize_counters(fetch_dir, write_dir, l2_dir=None, workload="poisson3d_12
           "Commands (from the repository root, `export TMPDIR=/tmp`):", "", *cmds,
           f"    python bench.py --counter-summary {fetch_dir} {write_dir}"
           + (f" --l2-dir {l2_dir}" if l2_dir else "")
-          + f" --workload-name {workload} --counters-args '{run_args}'", "", *lines, "",
+          + f" --workload-name {workload} --counters-args='{run_args}'", "", *lines, "",
           "Kernel sources (sha256): " + ", ".join(f"{f} {h}" for f, h in src_sha.items()) + ".",
           ""]
     out_dir = out_dir or os.path.join(ROOT, "profiles")
@@ -409,7 +409,7 @@ def summarize_trace(trace_dir, bench_json=None, trace_args="--steps 2 --warmup 1
           "Command (from the repository root, `export TMPDIR=/tmp`):",
           "", "    " + cmd, f"    python bench.py --trace-summary {trace_dir}"
           + (f" {bench_json}" if bench_json else "")
-          + (f" --trace-args '{trace_args}'" if trace_args != "--steps 2 --warmup 1 "
+          + (f" --trace-args='{trace_args}'" if trace_args != "--steps 2 --warmup 1 "
              "--no-cpu-baseline" else ""), "",
           "Step kernels `<T, MODE, ...>`: MODE 2 = A step, 4 = G^T step, 6 = G step",
           "(1, 3, 5: their first-iteration / start-up forms, 0 = plain SpMV, 8 and 9 the",
