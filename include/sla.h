@@ -90,7 +90,10 @@
 extern "C" {
 #endif
 
-typedef enum { SLA_F64 = 0, SLA_F32 = 1 } sla_dtype;
+/* SLA_DTYPE_RANGE_ makes every non-negative int32 a value of the type, so a
+ * caller's out-of-range dtype reaches the library's check (and is rejected
+ * with SLA_ERR_INVALID_ARG) instead of being an invalid enum value. */
+typedef enum { SLA_F64 = 0, SLA_F32 = 1, SLA_DTYPE_RANGE_ = 0x7fffffff } sla_dtype;
 
 typedef enum {
     SLA_OK = 0,
