@@ -251,3 +251,24 @@ def test_workspace_holds_the_column_block_results(monkeypatch):
     monkeypatch.setenv("SLA_COLBLK", "0")
     without = B.sla_pcg_workspace_size(create(p.A))
     assert with_blocks >= without + 8 * 8 * p.A.n
+
+
+@pytest.mark.parametrize("colblk", ["1", "0"])
+def test_column_blocks_fp32(colblk, ordered, monkeypatch):
+    """fp32 storage and products on the ordering (fp64 scalars), with and
+    without column blocks: the first iterates against the oracle's fp64 ones
+    at fp32 accuracy, the converged solve against the fp64 solution."""
+    monkeypatch.setenv("SLA_COLBLK", colblk)
+    p = problem("powerlaw_20k")
+    p32 = p.astype("f32")
+    A = create(p32.A, dtype="f32")
+    G = create(p32.G, transpose=True, dtype="f32")
+    assert B.sla_mat_reordered(A)
+    x3_ref, _, _, _ = oracle.pcg(p.A, p.G, p.eps, p.b, p.rtol, 3)
+    x3, info3 = B.sla_pcg_solve(A, G, p.eps, tdev(p32.b), rtol=p.rtol, maxit=3)
+    assert info3.iterations == 3 and rel(host(x3), x3_ref) <= 1e-5
+    x_ref, st, it, _ = oracle.pcg(p.A, p.G, p.eps, p.b, p.rtol, p.maxit)
+    x, info = B.sla_pcg_solve(A, G, p.eps, tdev(p32.b), rtol=p.rtol, maxit=p.maxit)
+    say("column blocks fp32", colblk, "iterations", info.iterations, "oracle fp64", it)
+    assert info.status in (B.OK, B.NOT_CONVERGED)
+    assert rel(host(x), x_ref) <= 1e-3
