@@ -43,6 +43,9 @@
  *    solves (default: fused for CSR matrices in the sliced layout, separate
  *    streaming passes otherwise).  SLA_MFUSION=fused: the same for the
  *    multi-right-hand-side solves (default: separate).
+ *  - SLA_MCHUNK=1|2|4|8: most columns a multi-right-hand-side pass takes
+ *    (default: 8, or 4 for a sliced CSR matrix reaching far from its
+ *    diagonal).
  *  - SLA_SMALL=0: no one-workgroup solve for systems of at most 1024 rows.
  *  - SLA_SELL=0: no sliced (SELL-64 / BSR sliced-ELL) copies at create time;
  *    SLA_SELL16=0: absolute int32 columns in them instead of 16-bit offsets;
@@ -77,8 +80,9 @@
  *    rocprofv3 --marker-trace; the roctx library is opened at run time),
  *    and one line per call on stderr with n, iterations, relative residual,
  *    status and wall time.
- * SLA_GRID is read once per device, SLA_MALL_BUDGET_MB, SLA_BATCH_ITERS and
- * SLA_TRACE once per process; the others at every handle creation or solve.
+ * SLA_GRID is read once per device, SLA_MALL_BUDGET_MB, SLA_BATCH_ITERS,
+ * SLA_MCHUNK and SLA_TRACE once per process; the others at every handle
+ * creation or solve.
  */
 #ifndef SLA_H
 #define SLA_H

@@ -894,6 +894,8 @@ template <typename T, int MODE, int K>
 hipError_t mlaunch(const sla_mat& m, const MatView& v, const MArgs<T>& a, int grid,
                    hipStream_t s) {
   const dim3 g(grid), b(kWG);
+  // slots per load batch (measured on 3D Poisson 128^3 and 2D heat 512^2:
+  // 8 and 6 slots at K = 4, 3 and 4 at K = 8 gave no consistent gain)
   constexpr int U = K >= 8 ? 2 : 4;
   if (m.bs == 1 && v.sell) {
     if (v.so) hipLaunchKernelGGL((msell_step<T, MODE, K, true, U, true>), g, b, 0, s, a);
@@ -923,6 +925,19 @@ int mgrid(const sla_mat& m) {
   return step_grid(g);
 }
 
+// Grid of the lock-step solve's kernels.  With a sliced CSR A, half the
+// resident capacity (two workgroups per CU): fewer slices in flight per XCD
+// keep the gathered K-wide rows of the products' operands in its L2
+// (3D Poisson 128^3, 4 columns: 275 us per lock-step iteration against
+// 286 us with four per CU; 2D heat 512^2: 48 against 50 us, 8 columns 86
+// against 99 us).  Other layouts keep the resident grid (3x3 BSR with 4
+// columns ran 35% slower at half).
+int solve_grid(const sla_mat& A, const sla_mat& G) {
+  int g = std::max(mgrid(A), mgrid(G));
+  if (A.bs == 1 && A.fwd.sell && g >= 16) g = std::max(8, std::min(g, max_grid() / 2) & ~7);
+  return g;
+}
+
 // Iteration form: products with p and r formed inside their gathers
 // (fused) or single-gather products with the p and r updates in streaming
 // passes (separate, the default: with K columns the fused form's two
@@ -934,13 +949,28 @@ bool mfused() {
 
 // Columns handled per pass: the largest of 8, 4, 2, 1 that fits k, with
 // passes of 4 instead of 8 on a SELL matrix reaching further than kFarRows
-// from its diagonal (3D Poisson 128^3: 8-column products ran 2.3x the time
-// of 4-column ones, so two passes of 4 beat one of 8 by 10%; 2D heat 512^2,
-// whose rows reach 512 rows out, keeps passes of 8).
+// from its diagonal (3D Poisson 128^3 on the half grid: 600 us per
+// 8-column lock-step iteration against 2 x 275 us for two passes of 4, and
+// 620 us on the resident grid; 2D heat 512^2, whose rows reach 512 rows
+// out, keeps passes of 8).
+// SLA_MCHUNK=1|2|4|8 replaces the rule by a fixed cap (read once per
+// process: the workspace size depends on it).
+int chunk_cap() {
+  static const int cap = [] {
+    const char* e = getenv("SLA_MCHUNK");
+    const int v = e ? atoi(e) : 0;
+    return v == 1 || v == 2 || v == 4 || v == 8 ? v : 0;
+  }();
+  return cap;
+}
+
 int chunk_width(const sla_mat& A, int k) {
+  const int cap = chunk_cap();
   const bool far = A.bs == 1 && A.fwd.sell && A.fwd.max_dist > kFarRows;
-  if (k >= 8 && !far) return 8;
-  return k >= 4 ? 4 : k >= 2 ? 2 : 1;
+  const int lim = cap ? cap : far ? 4 : 8;
+  if (k >= 8 && lim >= 8) return 8;
+  if (k >= 4 && lim >= 4) return 4;
+  return k >= 2 && lim >= 2 ? 2 : 1;
 }
 
 struct MWork {
@@ -984,7 +1014,7 @@ sla_status mpcg_pass(const sla_mat& A, const sla_mat& G, double eps, const T* b,
   const int n = (int)A.n();
   T *P[2] = {(T*)w.vec[0], (T*)w.vec[1]}, *R[2] = {(T*)w.vec[2], (T*)w.vec[3]};
   T *q = (T*)w.vec[4], *t = (T*)w.vec[5], *z = (T*)w.vec[6];
-  const int grid = std::max(mgrid(A), mgrid(G));
+  const int grid = solve_grid(A, G);
   SLA_HIP(hipMemsetAsync(w.st, 0, sizeof(MState), s));
 
   MArgs<T> aA{}, aT{}, aG{};
