@@ -716,7 +716,12 @@ __global__ __launch_bounds__(kWG) void sell_win_step(StepArgs<T> a) {
   constexpr int WN = R + 2 * kWinHalo;
   constexpr int PER = (WN + kWG - 1) / kWG;
   constexpr bool TWO = MODE == M_A || MODE == M_GT;  // gat() reads in0 and in1
+  // A and G^T steps: the tile's own rows take their two operands (z and
+  // p_old, r and q) from the window loads, kept in LDS, instead of reading
+  // them from memory a second time
+  constexpr bool OWNW = MODE == M_A || MODE == M_GT;
   __shared__ T gs[WN];
+  __shared__ T gz[OWNW ? R : 1], gq[OWNW ? R : 1];
   __shared__ double s_red[kWaves];
   __shared__ int s_flag;
   const int lane = threadIdx.x & (kSlice - 1), wv = threadIdx.x / kSlice;
@@ -763,6 +768,13 @@ __global__ __launch_bounds__(kWG) void sell_win_step(StepArgs<T> a) {
       if (i < WN) {
         if constexpr (TWO) gs[i] = fma(cf.c, w1[p], w0[p]);
         else gs[i] = w0[p];
+        if constexpr (OWNW) {
+          const int k = i - kWinHalo;
+          if (k >= 0 && k < R) {
+            gz[k] = w0[p];
+            gq[k] = w1[p];
+          }
+        }
       }
     }
     const int off = hoff, w = hw, m = hm;
@@ -779,7 +791,14 @@ __global__ __launch_bounds__(kWG) void sell_win_step(StepArgs<T> a) {
     if (sl < a.nslices) {
       const int row = sl * kSlice + lane;
       const bool live = row < a.nbr;
-      const Own<T> o = own_load<T, MODE>(a, live ? row : 0);
+      Own<T> o{T(0), T(0), T(0)};
+      if constexpr (OWNW) {
+        o.a = gq[threadIdx.x];
+        o.b = gz[threadIdx.x];
+        if constexpr (MODE == M_A) o.c = a.xv[live ? row : 0];
+      } else {
+        o = own_load<T, MODE>(a, live ? row : 0);
+      }
       T acc = T(0);
       for (int j = 0; j < w; j += U) {
         if (j > 0) {
