@@ -77,7 +77,8 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
   return s;
 }
 
-__device__ __forceinline__ double sum_partials(const double* __restrict__ p, int np, double* red) {
+// This thread's share of a sum of partials, before the workgroup sum.
+__device__ __forceinline__ double partial_share(const double* __restrict__ p, int np) {
   // each thread adds p[tid], p[tid + kWG], ... in index order; the loads of
   // eight strides are issued together (one memory round trip per eight
   // instead of one per partial: the partials were written by every XCD and
@@ -91,7 +92,11 @@ __device__ __forceinline__ double sum_partials(const double* __restrict__ p, int
 #pragma unroll
     for (int u = 0; u < 8; ++u) s += v[u];
   }
-  return block_sum(s, red);
+  return s;
+}
+
+__device__ __forceinline__ double sum_partials(const double* __restrict__ p, int np, double* red) {
+  return block_sum(partial_share(p, np), red);
 }
 
 // XCD-aware tile assignment: workgroups are dispatched round-robin over the

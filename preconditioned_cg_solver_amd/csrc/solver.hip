@@ -130,6 +130,22 @@ __device__ __forceinline__ bool prologue(const StepArgs<T>& a, Coef<T>& cf, doub
   if constexpr (MODE == M_PLAIN || MODE == M_GZ) {
     return true;
   } else {
+    constexpr bool SUMS = MODE != M_AU && MODE != M_GTU && MODE != M_GT0;
+    const int k = a.k;
+    // Every load the prologue needs is issued before its first wait: this
+    // thread's share of the partials, the state scalars written by earlier
+    // kernels and the exit flag, so that they cost one memory round trip
+    // rather than three in a row.  Loaded but unused when the solve is done.
+    double part = 0.0, s0 = 0.0, s1 = 0.0;
+    if constexpr (SUMS) part = partial_share(a.pin, a.npin);
+    if constexpr (MODE == M_A) {
+      s0 = a.st->rho[(k - 2) % kRing];    // rho_{k-2}
+      s1 = a.st->alpha[(k - 1) % kRing];  // alpha_{k-1}
+    } else if constexpr (MODE == M_GT) {
+      s0 = a.st->rho[(k - 1) % kRing];    // rho_{k-1}
+    } else if constexpr (MODE == M_G) {
+      s0 = a.st->bb;
+    }
     if (threadIdx.x == 0) *s_flag = __hip_atomic_load(&a.st->done, __ATOMIC_RELAXED,
                                                       __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
@@ -139,11 +155,10 @@ __device__ __forceinline__ bool prologue(const StepArgs<T>& a, Coef<T>& cf, doub
       }
       return false;
     }
-    if constexpr (MODE == M_AU || MODE == M_GTU) return true;
+    if constexpr (!SUMS) return true;
     const bool lead = blockIdx.x == 0 && threadIdx.x == 0;
-    const int k = a.k;
     if constexpr (MODE == M_A1 || MODE == M_A) {
-      const double rho = sum_partials(a.pin, a.npin, red);  // rho_{k-1}
+      const double rho = block_sum(part, red);  // rho_{k-1}
       const bool bad = !(rho > 0.0) || !isfinite(rho);
       if (lead) {
         if (bad) take_exit(a.st, EX_BREAK_RHO, k);
@@ -151,16 +166,16 @@ __device__ __forceinline__ bool prologue(const StepArgs<T>& a, Coef<T>& cf, doub
       }
       if (bad) return false;
       if constexpr (MODE == M_A) {
-        const double beta = rho / a.st->rho[(k - 2) % kRing];
-        cf.c = T(beta);                               // beta_{k-1}
-        cf.c2 = T(a.st->alpha[(k - 1) % kRing]);      // alpha_{k-1}
+        const double beta = rho / s0;
+        cf.c = T(beta);   // beta_{k-1}
+        cf.c2 = T(s1);    // alpha_{k-1}
         if (lead && a.hist_b && k - 1 <= a.hist_len) a.hist_b[k - 2] = beta;
       }
       return true;
     } else if constexpr (MODE == M_GT) {
-      const double sigma = sum_partials(a.pin, a.npin, red);
+      const double sigma = block_sum(part, red);
       const bool bad = !(sigma > 0.0) || !isfinite(sigma);
-      const double alpha = a.st->rho[(k - 1) % kRing] / sigma;
+      const double alpha = s0 / sigma;
       if (lead) {
         if (bad) {
           take_exit(a.st, EX_BREAK_SIGMA, k);
@@ -173,10 +188,8 @@ __device__ __forceinline__ bool prologue(const StepArgs<T>& a, Coef<T>& cf, doub
       if (bad) return false;
       cf.c = T(-alpha);
       return true;
-    } else if constexpr (MODE == M_GT0) {
-      return true;
     } else if constexpr (MODE == M_G0) {
-      const double bb = sum_partials(a.pin, a.npin, red);
+      const double bb = block_sum(part, red);
       int ex = EX_NONE;
       if (!isfinite(bb)) ex = EX_NONFINITE_B;
       else if (bb == 0.0) ex = EX_BZERO;
@@ -188,9 +201,9 @@ __device__ __forceinline__ bool prologue(const StepArgs<T>& a, Coef<T>& cf, doub
       }
       return ex == EX_NONE;
     } else {  // M_G
-      const double rr = sum_partials(a.pin, a.npin, red);
+      const double rr = block_sum(part, red);
       const double rnorm = sqrt(rr);
-      const double bnorm = sqrt(a.st->bb);
+      const double bnorm = sqrt(s0);
       int ex = EX_NONE;
       if (!isfinite(rnorm)) ex = EX_BREAK_RR;
       else if (rnorm <= a.rtol * bnorm) ex = EX_CONV;
@@ -198,7 +211,7 @@ __device__ __forceinline__ bool prologue(const StepArgs<T>& a, Coef<T>& cf, doub
       if (lead) {
         a.st->rr = rr;
         if (ex != EX_NONE) take_exit(a.st, ex, k);
-        if (a.poll) post_poll(a.poll, ex != EX_NONE, k, rr, a.st->bb);
+        if (a.poll) post_poll(a.poll, ex != EX_NONE, k, rr, s0);
       }
       return ex == EX_NONE;
     }
