@@ -126,9 +126,11 @@ __device__ __forceinline__ void block_sum_k(double (&v)[K], double* red) {
   }
 }
 
+// This thread's share of K interleaved sums of partials (before the
+// workgroup sum).
 template <int K>
-__device__ __forceinline__ void sum_partials_k(const double* __restrict__ p, int np,
-                                               double (&out)[K], double* red) {
+__device__ __forceinline__ void partial_share_k(const double* __restrict__ p, int np,
+                                                double (&out)[K]) {
 #pragma unroll
   for (int c = 0; c < K; ++c) out[c] = 0.0;
   // in index order per thread; the loads of 16 / K strides (at least one)
@@ -146,7 +148,6 @@ __device__ __forceinline__ void sum_partials_k(const double* __restrict__ p, int
 #pragma unroll
       for (int c = 0; c < K; ++c) out[c] += v[u][c];
   }
-  block_sum_k<K>(out, red);
 }
 
 __device__ __forceinline__ void col_exit(MState* st, int c, int kind, int k) {
@@ -169,6 +170,33 @@ __device__ __forceinline__ bool mprologue(const MArgs<T>& a, MCoef<T, K>& cf, do
   if constexpr (MODE == MM_PLAIN) {
     return true;
   } else {
+    constexpr bool SUMS = MODE != MM_AU && MODE != MM_GTU;
+    const int k = a.k;
+    // Every load the decisions need is issued before the first wait: this
+    // thread's share of the partials, each column's exit kind and state
+    // scalar (written by earlier kernels) and the done flag: one memory
+    // round trip rather than three in a row.  Unused when the solve is done.
+    double s[K];
+    int ek[K];
+    double s0[K];
+#pragma unroll
+    for (int c = 0; c < K; ++c) {
+      s[c] = 0.0;
+      ek[c] = EX_NONE;
+      s0[c] = 0.0;
+    }
+    if constexpr (SUMS) {
+      partial_share_k<K>(a.pin, a.npin, s);
+      if constexpr (MODE != MM_G0) {
+#pragma unroll
+        for (int c = 0; c < K; ++c) {
+          ek[c] = a.st->exit_kind[c];
+          if constexpr (MODE == MM_A) s0[c] = a.st->rho[(k - 2) % kRing][c];
+          else if constexpr (MODE == MM_GT) s0[c] = a.st->rho[(k - 1) % kRing][c];
+          else if constexpr (MODE == MM_G) s0[c] = a.st->bb[c];
+        }
+      }
+    }
     if (threadIdx.x == 0)
       *s_flag = __hip_atomic_load(&a.st->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
@@ -179,10 +207,8 @@ __device__ __forceinline__ bool mprologue(const MArgs<T>& a, MCoef<T, K>& cf, do
       }
       return false;
     }
-    if constexpr (MODE == MM_AU || MODE == MM_GTU) return true;
-    const int k = a.k;
-    double s[K];
-    sum_partials_k<K>(a.pin, a.npin, s, red);
+    if constexpr (!SUMS) return true;
+    block_sum_k<K>(s, red);
     int live = 0;
 #pragma unroll
     for (int c = 0; c < K; ++c) {
@@ -200,7 +226,7 @@ __device__ __forceinline__ bool mprologue(const MArgs<T>& a, MCoef<T, K>& cf, do
         }
         act = ex == EX_NONE;
       } else {
-        act = a.st->exit_kind[c] == EX_NONE;
+        act = ek[c] == EX_NONE;
         if (act) {
           if constexpr (MODE == MM_A1 || MODE == MM_A) {
             const double rho = s[c];  // rho_{k-1}
@@ -209,7 +235,7 @@ __device__ __forceinline__ bool mprologue(const MArgs<T>& a, MCoef<T, K>& cf, do
               act = false;
             } else {
               if (lead) a.st->rho[(k - 1) % kRing][c] = rho;
-              if constexpr (MODE == MM_A) cf.c[c] = T(rho / a.st->rho[(k - 2) % kRing][c]);
+              if constexpr (MODE == MM_A) cf.c[c] = T(rho / s0[c]);
             }
           } else if constexpr (MODE == MM_GT) {
             const double sigma = s[c];
@@ -217,14 +243,14 @@ __device__ __forceinline__ bool mprologue(const MArgs<T>& a, MCoef<T, K>& cf, do
               if (lead) col_exit(a.st, c, EX_BREAK_SIGMA, k);
               act = false;
             } else {
-              const double alpha = a.st->rho[(k - 1) % kRing][c] / sigma;
+              const double alpha = s0[c] / sigma;
               if (lead) a.st->alpha[k % kRing][c] = alpha;
               cf.c[c] = T(-alpha);
               cf.c2[c] = T(alpha);
             }
           } else {  // MM_G
             const double rr = s[c];
-            const double rnorm = sqrt(rr), bnorm = sqrt(a.st->bb[c]);
+            const double rnorm = sqrt(rr), bnorm = sqrt(s0[c]);
             int ex = EX_NONE;
             if (!isfinite(rnorm)) ex = EX_BREAK_RR;
             else if (rnorm <= a.rtol * bnorm) ex = EX_CONV;
