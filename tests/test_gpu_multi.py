@@ -211,15 +211,17 @@ def test_adjoint_multi_parity(key, layout, form):
 
 
 @pytest.mark.parametrize("k", [4, 8])
-def test_solve_multi_full_size_poisson3d_128(k):
+@pytest.mark.parametrize("key", ["c2", "c1", "c3"])
+def test_solve_multi_full_size(key, k):
     """The benchmark's several-right-hand-side lines at their size: 3D Poisson
-    128^3 (n = 2,097,152), columns N(0, 1) from seed 100 + k with the single
+    128^3 (n = 2,097,152), heat 512^2 (n = 262,144) and the elasticity BSR3
+    system (n = 786,432), columns N(0, 1) from seed 100 + k with the single
     solve's b as column 0, every column against the oracle's solve of it
     under the fixed gates (x within 1e-8, iterations within 2%)."""
-    p = problem("c2")
+    p = problem(key)
     Bm = np.random.default_rng(100 + k).standard_normal((p.A.n, k))
     Bm[:, 0] = p.b
-    say("solve_multi full size 128^3", k)
+    say("solve_multi full size", key, p.A.n, k)
     A, G = create(p.A, validate=False), create(p.G, transpose=True, validate=False)
     X, infos = B.sla_pcg_solve_multi(A, G, p.eps, tdev(Bm), rtol=p.rtol, maxit=p.maxit)
     Xg = host(X)
