@@ -613,8 +613,8 @@ __device__ __forceinline__ void sell_batch(const StepArgs<T>& a, int off, int la
     v[u] = ld_stream<NT>(a.sv + idx);
     if constexpr (OFS && MODE == M_PLAIN)
       raw[u] = __builtin_amdgcn_readfirstlane(a.so[off / kSlice + j + u]);
-    else if constexpr (OFS)
-      raw[u] = ld_stream<NT>(a.so + off / kSlice + j + u);
+    else if constexpr (OFS)  // slice-uniform: kept in a scalar register
+      raw[u] = __builtin_amdgcn_readfirstlane(ld_stream<NT>(a.so + off / kSlice + j + u));
     else raw[u] = sell_raw<NT, I16>(a, idx);
   }
 #pragma unroll
@@ -677,7 +677,7 @@ __global__ __launch_bounds__(kWG) void sell_step(StepArgs<T> a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       cv[u] = hv[u];
-      cr[u] = hr[u];
+      cr[u] = OFS ? __builtin_amdgcn_readfirstlane(hr[u]) : hr[u];
     }
     if (t + step < t1) load_head((t + step) * kWaves + wv);
     if (sl >= a.nslices) continue;
@@ -792,11 +792,13 @@ __global__ __launch_bounds__(kWG) void sell_win_step(StepArgs<T> a) {
     }
     const int off = hoff, w = hw, m = hm;
     T cv[U];
+    // a slot's offset is the same for every row of the slice: held in a
+    // scalar register, the near / far test below is a uniform branch
     int cr[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       cv[u] = hv[u];
-      cr[u] = hr[u];
+      cr[u] = __builtin_amdgcn_readfirstlane(hr[u]);
     }
     __syncthreads();
     if (t + step < t1) fetch(t + step);
@@ -818,7 +820,7 @@ __global__ __launch_bounds__(kWG) void sell_win_step(StepArgs<T> a) {
 #pragma unroll
           for (int u = 0; u < U; ++u) {
             cv[u] = ld_stream<NT>(a.sv + off + (j + u) * kSlice + lane);
-            cr[u] = ld_stream<NT>(a.so + off / kSlice + j + u);
+            cr[u] = __builtin_amdgcn_readfirstlane(ld_stream<NT>(a.so + off / kSlice + j + u));
           }
         }
         T x[U];
